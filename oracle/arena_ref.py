@@ -1,0 +1,96 @@
+"""Reference model of the fixed-slot expert arena's slot policy (test infrastructure only).
+
+Sources: "Strata on a Mac (Apple Silicon, Metal)", section "Status" (an expert
+cache of 64 slots) and "What you need" (keep the most-used experts in an arena,
+read the rest when a token needs them; a "no free slot" failure is reported);
+"Strata" README (ro99/strata), "Architecture" / Residency (routed experts leased
+into device memory per decode step through an LRU cache). The pages measure
+eviction order as a small effect, so one plain deterministic LRU is used:
+
+1. walk the requested ids in the given order and keep first occurrences;
+2. more distinct ids than slots, or an id outside [0, E): fail, state unchanged;
+3. every requested expert already resident is a hit and gets stamp = call number;
+4. each miss, in first-occurrence order, takes the lowest-numbered empty slot,
+   else evicts the resident expert with the smallest stamp among those not
+   requested in this call (ties to the lower slot); the newcomer gets the
+   current stamp and is reported as a fill (expert, slot);
+5. the call number grows by one per successful call.
+
+Parity: pinned by a hand-worked sequence and by invariants in
+tests/test_arena_model.py.
+"""
+
+from __future__ import annotations
+
+OK, EINVAL, ENOSLOT = 0, -1, -2
+
+
+class ArenaModel:
+    def __init__(self, E: int, S: int, blob_bytes: int = 0):
+        if E <= 0 or S <= 0:
+            raise ValueError("E and S must be positive")
+        self.E, self.S, self.blob_bytes = E, S, blob_bytes
+        self.reset()
+
+    def reset(self):
+        self.slot_of = [-1] * self.E  # expert -> slot (-1 absent)
+        self.expert_in = [-1] * self.S  # slot -> expert (-1 empty)
+        self.stamp = [0] * self.S
+        self.calls = 0
+        self.stats = dict(hits=0, misses=0, evictions=0, fills=0, h2d_bytes=0)
+
+    def place(self, expert: int, slot: int) -> int:
+        """Set-up placement: the caller has put ``expert``'s data in ``slot``."""
+        if not (0 <= expert < self.E and 0 <= slot < self.S):
+            return EINVAL
+        old = self.expert_in[slot]
+        if old >= 0:
+            self.slot_of[old] = -1
+        prev = self.slot_of[expert]
+        if prev >= 0:
+            self.expert_in[prev] = -1
+        self.expert_in[slot] = expert
+        self.slot_of[expert] = slot
+        self.stamp[slot] = 0
+        return OK
+
+    def map_slots(self, ids):
+        """Returns (status, slots per input entry, fills [(expert, slot)])."""
+        ids = [int(e) for e in ids]
+        if any(not 0 <= e < self.E for e in ids):
+            return EINVAL, None, None
+        distinct = []
+        for e in ids:
+            if e not in distinct:
+                distinct.append(e)
+        if len(distinct) > self.S:
+            return ENOSLOT, None, None
+        self.calls += 1
+        now = self.calls
+        requested = set(distinct)
+        misses = []
+        for e in distinct:
+            s = self.slot_of[e]
+            if s >= 0:
+                self.stamp[s] = now
+                self.stats["hits"] += 1
+            else:
+                misses.append(e)
+        fills = []
+        for e in misses:
+            empty = [s for s in range(self.S) if self.expert_in[s] < 0]
+            if empty:
+                s = empty[0]
+            else:
+                cands = [s for s in range(self.S) if self.expert_in[s] not in requested]
+                s = min(cands, key=lambda c: (self.stamp[c], c))
+                self.slot_of[self.expert_in[s]] = -1
+                self.stats["evictions"] += 1
+            self.expert_in[s] = e
+            self.slot_of[e] = s
+            self.stamp[s] = now
+            fills.append((e, s))
+            self.stats["misses"] += 1
+            self.stats["fills"] += 1
+            self.stats["h2d_bytes"] += self.blob_bytes
+        return OK, [self.slot_of[e] for e in ids], fills

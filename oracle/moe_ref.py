@@ -1,0 +1,229 @@
+"""fp64 CPU oracle of the int4 routed-expert MoE layer (test infrastructure only).
+
+What the layer computes, written as plain definitions in float64. Sources:
+
+* "Strata on a Mac (Apple Silicon, Metal)", section "Switches": the router is a
+  GEMV producing one logit per expert, dispatched before a separate top-k
+  routing step (``moe_route``); "Status": the 64-slot expert cache;
+* "Strata" README (ro99/strata), "Models" table and "Architecture" / Kernels:
+  4-bit grouped integer experts executed W4A16 (4-bit weights, 16-bit
+  activations), checked against a CPU reference implementation;
+* "How these numbers are measured", section "Fidelity": paged output must equal
+  fully-resident output.
+
+Where the pages leave a step open the plain reading is used (each is named at
+the function): softmax over all experts, selection on logits with ties to the
+lower expert id, no renormalisation of the selected weights, symmetric
+two's-complement int4 with one fp16 scale per 32 consecutive inputs of a row,
+SwiGLU with SiLU on the gate projection, an always-on shared expert of weight
+1, and a combine summed in rank order.
+
+Parity pins (tests/test_oracle_pins.py): router logits against exact rational
+arithmetic; selection against brute-force rank counting; softmax against closed
+forms; int4 decoding against hand-written bytes; dequantisation against an
+element-by-element construction; the FFN against a closed form for an
+identity-like expert (SiLU from torch); the layer against zero input,
+linearity, permutation and relabelling invariances and the dense (K = E)
+mixture. Parity unpinned: none of the pages prints a numeric example of this
+layer, so no value here is pinned to a published number.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------- formats
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bfloat16 bit patterns (uint16) to float64 exactly."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(a: np.ndarray) -> np.ndarray:
+    return np.asarray(a, dtype=np.float16).astype(np.float64)
+
+
+def unpack_int4(packed: np.ndarray, cols: int) -> np.ndarray:
+    """Decode row-major packed int4 codes to int64 values in [-8, 7].
+
+    Element j of a row is byte j // 2; even j uses the low nibble, odd j the
+    high nibble; each nibble is two's complement (symmetric quantisation, no
+    zero point).
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    if p.shape[-1] * 2 != cols:
+        raise ValueError("packed row length does not match cols")
+    out = np.empty(p.shape[:-1] + (cols,), dtype=np.int64)
+    lo = (p & 0x0F).astype(np.int64)
+    hi = (p >> 4).astype(np.int64)
+    out[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+    out[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return out
+
+
+def dequantize(packed: np.ndarray, scales: np.ndarray, cols: int, g: int = 32) -> np.ndarray:
+    """W[n, j] = q[n, j] * s[n, j // g] in float64 (exact: 4-bit times 11-bit significands)."""
+    q = unpack_int4(packed, cols).astype(np.float64)
+    s = f16_to_f64(scales)
+    if s.shape[-1] * g != cols:
+        raise ValueError("scale count does not match cols / g")
+    return q * np.repeat(s, g, axis=-1)
+
+
+# ---------------------------------------------------------------- router
+
+
+def _f32_round_exact(terms: list[float]) -> np.float32:
+    """The float32 nearest (ties to even) to the exact sum of float64 ``terms``.
+
+    ``math.fsum`` returns the float64 nearest to the exact sum. Rounding that to
+    float32 equals rounding the exact sum to float32 except when the float64
+    result sits exactly halfway between two float32 neighbours; then the sign
+    of the exact residual (again from fsum, which keeps the sign of an exact
+    value) decides.
+    """
+    s = math.fsum(terms)
+    f = np.float32(s)
+    if not np.isfinite(f):
+        raise FloatingPointError("router logit overflows float32")
+    fd = float(f)
+    if fd == s:
+        return f
+    if fd < s:
+        lo, hi = f, np.nextafter(f, np.float32(np.inf))
+    else:
+        lo, hi = np.nextafter(f, np.float32(-np.inf)), f
+    mid = (float(lo) + float(hi)) / 2.0  # exact in float64
+    if s != mid:
+        return f
+    r = math.fsum(list(terms) + [-s])
+    if r > 0:
+        return hi
+    if r < 0:
+        return lo
+    return f  # exact tie: numpy's conversion already rounded to even
+
+
+def router_logits(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """l[t, e] = float32 rounding of the exact sum_h x[t, h] * Wr[e, h].
+
+    The router GEMV of "Strata on a Mac", section "Switches". x is bf16, Wr is
+    float32; each product is exact in float64 (8 + 24 significant bits), and the
+    sum is rounded once, to the float32 nearest the exact value.
+    """
+    x = bf16_bits_to_f64(x_bits)
+    w = np.asarray(w_router, dtype=np.float32).astype(np.float64)
+    T, H = x.shape
+    E = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("router weight width must equal hidden size")
+    out = np.empty((T, E), dtype=np.float32)
+    for t in range(T):
+        prods = x[t][None, :] * w  # exact products
+        for e in range(E):
+            out[t, e] = _f32_round_exact(prods[e].tolist())
+    return out
+
+
+def select_topk(logits: np.ndarray, K: int) -> np.ndarray:
+    """ids[t, :] = the K experts with the largest logits, in rank order.
+
+    The total order is (logit descending, expert id ascending): equal logits go
+    to the lower id, and -0.0 equals +0.0. Selection is on logits, which ranks
+    exactly like the softmax probabilities since softmax is strictly increasing.
+    """
+    l = np.asarray(logits, dtype=np.float32)
+    if not np.all(np.isfinite(l)):
+        raise ValueError("router logits must be finite")
+    T, E = l.shape
+    if not 1 <= K <= E:
+        raise ValueError("need 1 <= K <= E")
+    ids = np.empty((T, K), dtype=np.int32)
+    for t in range(T):
+        row = [float(v) for v in l[t]]
+        order = sorted(range(E), key=lambda e: (-row[e], e))
+        ids[t] = order[:K]
+    return ids
+
+
+def softmax_weights(logits: np.ndarray, ids: np.ndarray, renorm: bool = False) -> np.ndarray:
+    """w[t, k] = softmax(l[t, :])[ids[t, k]] in float64.
+
+    The probabilities are over all E experts (softmax, then top-k). By default
+    the selected probabilities are used as they are; ``renorm`` divides them by
+    their sum over the K selected experts.
+    """
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    T, K = ids.shape
+    w = np.empty((T, K), dtype=np.float64)
+    for t in range(T):
+        m = l[t].max()
+        ex = np.exp(l[t] - m)
+        z = math.fsum(ex.tolist())
+        w[t] = ex[ids[t]] / z
+        if renorm:
+            w[t] = w[t] / math.fsum(w[t].tolist())
+    return w
+
+
+def route(logits: np.ndarray, K: int, renorm: bool = False):
+    ids = select_topk(logits, K)
+    return ids, softmax_weights(logits, ids, renorm)
+
+
+# ---------------------------------------------------------------- experts
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z * sigmoid(z)
+
+
+class Expert:
+    """One int4 expert held as fp64 matrices: gate [I, H], up [I, H], down [H, I]."""
+
+    def __init__(self, tensors: dict, H: int, I: int, g: int = 32):
+        self.H, self.I = H, I
+        self.Wg = dequantize(tensors["qg"], tensors["sg"], H, g)
+        self.Wu = dequantize(tensors["qu"], tensors["su"], H, g)
+        self.Wd = dequantize(tensors["qd"], tensors["sd"], I, g)
+        if self.Wg.shape != (I, H) or self.Wu.shape != (I, H) or self.Wd.shape != (H, I):
+            raise ValueError("expert tensor shapes do not match (H, I)")
+
+    def __call__(self, x: np.ndarray) -> np.ndarray:
+        """SwiGLU FFN: down( silu(gate(x)) * up(x) ) for x of shape [..., H]."""
+        g = x @ self.Wg.T
+        u = x @ self.Wu.T
+        return (silu(g) * u) @ self.Wd.T
+
+
+def moe_layer(x_bits, experts, K, logits=None, w_router=None, shared=None, renorm=False):
+    """The whole layer for T tokens.
+
+    ``experts`` maps an expert id to an ``Expert`` (a dict or a callable, so
+    callers can build only the experts routing selects). Either ``logits``
+    [T, E] or ``w_router`` [E, H] is given. Returns (y fp64 [T, H], ids, w, l).
+
+    y[t] = shared(x[t]) + sum_{k=0..K-1} w[t, k] * expert_{ids[t, k]}(x[t]),
+    accumulated in rank order.
+    """
+    x = bf16_bits_to_f64(x_bits)
+    if logits is None:
+        logits = router_logits(x_bits, w_router)
+    ids, w = route(logits, K, renorm)
+    get = experts if callable(experts) else experts.__getitem__
+    T, H = x.shape
+    y = np.zeros((T, H), dtype=np.float64)
+    for t in range(T):
+        acc = shared(x[t]) if shared is not None else np.zeros(H)
+        for k in range(K):
+            acc = acc + w[t, k] * get(int(ids[t, k]))(x[t])
+        y[t] = acc
+    return y, ids, w, np.asarray(logits, dtype=np.float32)

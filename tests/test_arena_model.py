@@ -1,0 +1,91 @@
+"""Pins of the arena slot-policy model: a hand-worked sequence and invariants (CPU only)."""
+
+import os
+
+import numpy as np
+
+from oracle.arena_ref import ENOSLOT, OK, ArenaModel
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_sequence():
+    steps, stats = [], None
+    with open(os.path.join(GOLDEN, "arena_lru_sequence.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            if line.startswith("stats"):
+                stats = [int(v) for v in line.split()[1:]]
+                continue
+            req, st, slots, fills = [p.strip() for p in line.split("|")]
+            steps.append(
+                (
+                    [int(v) for v in req.split()],
+                    int(st),
+                    None if slots == "-" else [int(v) for v in slots.split()],
+                    [] if fills == "-" else [tuple(int(v) for v in f.split(":")) for f in fills.split()],
+                )
+            )
+    return steps, stats
+
+
+def test_hand_worked_sequence():
+    steps, stats = load_sequence()
+    a = ArenaModel(E=4, S=2, blob_bytes=100)
+    for req, st, slots, fills in steps:
+        got_st, got_slots, got_fills = a.map_slots(req)
+        assert got_st == st, req
+        if st == OK:
+            assert got_slots == slots, req
+            assert got_fills == fills, req
+    assert [a.stats[k] for k in ("hits", "misses", "evictions", "fills")] == stats
+    assert a.stats["h2d_bytes"] == 100 * stats[3]
+
+
+def check_consistent(a):
+    for e in range(a.E):
+        s = a.slot_of[e]
+        if s >= 0:
+            assert a.expert_in[s] == e
+    for s in range(a.S):
+        e = a.expert_in[s]
+        if e >= 0:
+            assert a.slot_of[e] == s
+
+
+def test_invariants_random_stream():
+    rng = np.random.default_rng(0)
+    for E, S, n in ((16, 4, 3), (256, 64, 6), (8, 8, 8), (32, 5, 5)):
+        a = ArenaModel(E, S)
+        distinct_total = 0
+        for _ in range(300):
+            ids = rng.integers(0, E, size=int(rng.integers(1, n + 1))).tolist()
+            before = list(a.expert_in)
+            st, slots, fills = a.map_slots(ids)
+            distinct = list(dict.fromkeys(ids))
+            if len(distinct) > S:
+                assert st == ENOSLOT and a.expert_in == before
+                continue
+            assert st == OK
+            distinct_total += len(distinct)
+            for e, s in zip(ids, slots):
+                assert a.expert_in[s] == e  # every requested expert is resident where reported
+            assert len({a.slot_of[e] for e in distinct}) == len(distinct)
+            missed = [e for e in distinct if e not in before]
+            assert [f[0] for f in fills] == missed  # fills are exactly the misses, in order
+            for e, s in fills:
+                assert before[s] == -1 or before[s] not in distinct  # never evicts a same-call request
+            check_consistent(a)
+        assert a.stats["hits"] + a.stats["misses"] == distinct_total
+
+
+def test_lowest_empty_slot_first_and_place():
+    a = ArenaModel(E=10, S=4)
+    assert a.place(7, 2) == OK
+    st, slots, fills = a.map_slots([3, 7, 5])
+    assert slots == [0, 2, 1] and fills == [(3, 0), (5, 1)]
+    assert a.place(3, 3) == OK  # moving an expert empties its old slot
+    assert a.slot_of[3] == 3 and a.expert_in[0] == -1
+    st, slots, fills = a.map_slots([9])
+    assert fills == [(9, 0)]

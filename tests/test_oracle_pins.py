@@ -1,0 +1,295 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test pins one step of the layer to exact arithmetic, a closed form, a
+brute-force count, a hand-written fixture, or an invariant, so that a dropped
+term, a wrong sign or index or a transposed operand in the oracle fails here.
+"""
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from synth import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ helpers (test-side)
+
+
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    """Pack int codes [-8, 7] into the interchange nibble format (even index -> low nibble)."""
+    c = (np.asarray(codes, dtype=np.int64) & 0xF).astype(np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def nearest_f32(fr: Fraction) -> np.float32:
+    """Nearest float32 to an exact rational, ties to the even significand."""
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - fr), int(np.float32(c).view(np.uint32)) & 1))
+
+
+def bits_of(v: np.ndarray) -> np.ndarray:
+    return gen.bf16_bits_from_f32(np.asarray(v, dtype=np.float32))
+
+
+def identity_expert(H, I, sg, su, sd, g=32):
+    """Gate/up rows i < H are unit vectors e_i, down rows j pick h_j; one scale per matrix."""
+    qg = np.zeros((I, H), dtype=np.int64)
+    qg[np.arange(min(I, H)), np.arange(min(I, H))] = 1
+    qd = np.zeros((H, I), dtype=np.int64)
+    qd[np.arange(min(I, H)), np.arange(min(I, H))] = 1
+    return {
+        "qg": pack_codes(qg),
+        "qu": pack_codes(qg),
+        "qd": pack_codes(qd),
+        "sg": np.full((I, H // g), sg, dtype=np.float16),
+        "su": np.full((I, H // g), su, dtype=np.float16),
+        "sd": np.full((H, I // g), sd, dtype=np.float16),
+    }
+
+
+# ------------------------------------------------------------------ int4 format
+
+
+def test_int4_golden_bytes():
+    rows = 0
+    with open(os.path.join(GOLDEN, "int4_nibbles.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            hexpart, codepart = line.split("|")
+            packed = np.array([int(b, 16) for b in hexpart.split()], dtype=np.uint8)
+            want = [int(c) for c in codepart.split()]
+            got = R.unpack_int4(packed[None, :], 2 * packed.size)[0].tolist()
+            assert got == want, (hexpart, got, want)
+            rows += 1
+    assert rows >= 5
+
+
+def test_dequant_element_by_element():
+    rng = np.random.default_rng(7)
+    rows, cols, g = 3, 96, 32
+    codes = rng.integers(-8, 8, size=(rows, cols))
+    scales = rng.uniform(0.005, 0.02, size=(rows, cols // g)).astype(np.float16)
+    W = R.dequantize(pack_codes(codes), scales, cols, g)
+    for n in range(rows):
+        for j in range(cols):
+            assert W[n, j] == float(codes[n, j]) * float(scales[n, j // g])
+
+
+def test_pack_roundtrip_every_code():
+    codes = np.array([[(j % 16) - 8 for j in range(64)]])
+    assert R.unpack_int4(pack_codes(codes), 64).tolist() == codes.tolist()
+
+
+# ------------------------------------------------------------------ router logits
+
+
+def exact_logits(x_bits, w):
+    x = R.bf16_bits_to_f64(x_bits)
+    T, E = x.shape[0], w.shape[0]
+    out = np.empty((T, E), dtype=np.float32)
+    for t in range(T):
+        for e in range(E):
+            fr = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[t], w[e].astype(np.float64))), Fraction(0))
+            out[t, e] = nearest_f32(fr)
+    return out
+
+
+def test_router_logits_exact_random():
+    rng = np.random.default_rng(11)
+    x_bits = bits_of(rng.standard_normal((3, 48)))
+    w = (rng.standard_normal((5, 48)) * 0.02).astype(np.float32)
+    got = R.router_logits(x_bits, w)
+    assert np.array_equal(got.view(np.uint32), exact_logits(x_bits, w).view(np.uint32))
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_router_logits_double_rounding_midpoint(sign):
+    # exact sum = 1 + 2^-24 + 2^-80: just above the float32 midpoint between 1 and 1 + 2^-23.
+    # Its float64 rounding is exactly that midpoint, which ties-to-even would send to 1.0.
+    x_bits = bits_of([[sign, sign, sign * 2.0**-40]])
+    w = np.array([[1.0, 2.0**-24, 2.0**-40]], dtype=np.float32)
+    got = R.router_logits(x_bits, w)[0, 0]
+    assert got == np.float32(sign * (1.0 + 2.0**-23))
+    assert got == exact_logits(x_bits, w)[0, 0]
+
+
+def test_router_logits_exact_tie_goes_even():
+    x_bits = bits_of([[1.0, 1.0]])
+    w = np.array([[1.0, 2.0**-24]], dtype=np.float32)  # exactly the midpoint: even neighbour is 1.0
+    assert R.router_logits(x_bits, w)[0, 0] == np.float32(1.0)
+    w = np.array([[1.0 + 2.0**-23, 2.0**-24]], dtype=np.float32)  # midpoint above an odd significand
+    assert R.router_logits(x_bits, w)[0, 0] == np.float32(1.0 + 2.0**-22)
+
+
+# ------------------------------------------------------------------ selection
+
+
+def brute_force_ids(row, K):
+    E = len(row)
+    rank = [sum(1 for f in range(E) if row[f] > row[e] or (row[f] == row[e] and f < e)) for e in range(E)]
+    ids = [None] * K
+    for e in range(E):
+        if rank[e] < K:
+            ids[rank[e]] = e
+    return ids
+
+
+def test_select_exhaustive_with_ties():
+    values = [0.0, -0.0, 1.0, -1.5]
+    E = 6
+    n = 0
+    for row in itertools.product(values, repeat=E):
+        l = np.array([row], dtype=np.float32)
+        for K in (1, 3, E):
+            assert R.select_topk(l, K)[0].tolist() == brute_force_ids(row, K)
+            n += 1
+    assert n == 3 * 4**E
+
+
+def test_select_random_large():
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal((20, 256)).astype(np.float32)
+    l[:, 10] = l[:, 200]  # exact ties across the board
+    for t in range(20):
+        assert R.select_topk(l[t : t + 1], 8)[0].tolist() == brute_force_ids(l[t].tolist(), 8)
+
+
+def test_select_rejects_non_finite():
+    with pytest.raises(ValueError):
+        R.select_topk(np.array([[0.0, np.nan]], dtype=np.float32), 1)
+
+
+# ------------------------------------------------------------------ softmax weights
+
+
+def test_softmax_equal_logits():
+    for E, K in ((8, 2), (256, 8), (5, 5)):
+        ids, w = R.route(np.full((1, E), 0.37, dtype=np.float32), K)
+        assert ids[0].tolist() == list(range(K))
+        assert np.allclose(w, 1.0 / E, rtol=0, atol=1e-15)
+
+
+def test_softmax_two_value_closed_form():
+    E, delta = 16, 1.75
+    l = np.zeros((1, E), dtype=np.float32)
+    l[0, 9] = delta
+    ids, w = R.route(l, 3)
+    assert ids[0].tolist() == [9, 0, 1]
+    p_top = 1.0 / (1.0 + (E - 1) * math.exp(-delta))
+    p_rest = math.exp(-delta) * p_top
+    assert abs(w[0, 0] - p_top) < 1e-15 and abs(w[0, 1] - p_rest) < 1e-15 and abs(w[0, 2] - p_rest) < 1e-15
+
+
+def test_softmax_renorm():
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((4, 32)).astype(np.float32)
+    ids, w = R.route(l, 32, renorm=True)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-15)
+    ids, w = R.route(l, 4, renorm=True)
+    _, wp = R.route(l, 4, renorm=False)
+    assert np.allclose(w, wp / wp.sum(1, keepdims=True), atol=1e-15)
+    assert np.all(wp.sum(1) < 1.0)
+
+
+# ------------------------------------------------------------------ expert FFN and layer
+
+
+def test_identity_expert_closed_form():
+    H, I = 256, 512
+    sg, su, sd = np.float16(2.0), np.float16(0.5), np.float16(0.25)
+    ex = R.Expert(identity_expert(H, I, sg, su, sd), H, I)
+    rng = np.random.default_rng(9)
+    x = R.bf16_bits_to_f64(bits_of(rng.standard_normal((4, H))))
+    xt = torch.from_numpy(x)
+    want = (float(sd) * float(su) * xt * torch.nn.functional.silu(float(sg) * xt)).numpy()
+    got = ex(x)
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-300)
+    # the single-expert layer (E = K = 1) has routing weight exactly 1
+    y, ids, w, _ = R.moe_layer(bits_of(x), {0: ex}, 1, logits=np.zeros((4, 1), dtype=np.float32))
+    assert ids.tolist() == [[0]] * 4 and np.all(w == 1.0)
+    assert np.allclose(y, want, rtol=1e-14, atol=1e-300)
+
+
+def tiny_experts(seed, E, H, I):
+    return {e: R.Expert(gen.expert_tensors(seed, 0, e, H, I), H, I) for e in range(E)}
+
+
+def test_zero_activation_gives_zero():
+    T, H, E, K, I = 4, 256, 8, 2, 512
+    experts = tiny_experts(1, E, H, I)
+    wr = gen.router_weight(1, 0, E, H)
+    y, ids, w, l = R.moe_layer(np.zeros((T, H), dtype=np.uint16), experts, K, w_router=wr)
+    assert np.all(l == 0.0)
+    assert ids.tolist() == [[0, 1]] * T
+    assert np.all(w == 1.0 / E)
+    assert np.all(y == 0.0)
+
+
+def test_shared_expert_term():
+    H, I, E = 256, 512, 4
+    shared = R.Expert(identity_expert(H, I, np.float16(1.0), np.float16(1.0), np.float16(1.0)), H, I)
+    zero = {"qg": np.zeros((I, H // 2), np.uint8), "qu": np.zeros((I, H // 2), np.uint8),
+            "qd": np.zeros((H, I // 2), np.uint8), "sg": np.ones((I, H // 32), np.float16),
+            "su": np.ones((I, H // 32), np.float16), "sd": np.ones((H, I // 32), np.float16)}
+    experts = {e: R.Expert(zero, H, I) for e in range(E)}
+    rng = np.random.default_rng(2)
+    xb = bits_of(rng.standard_normal((3, H)))
+    x = R.bf16_bits_to_f64(xb)
+    y, *_ = R.moe_layer(xb, experts, 2, logits=rng.standard_normal((3, E)).astype(np.float32), shared=shared)
+    want = (torch.from_numpy(x) * torch.nn.functional.silu(torch.from_numpy(x))).numpy()
+    assert np.allclose(y, want, rtol=1e-14, atol=1e-300)
+
+
+def test_linearity_in_down_scales():
+    T, H, E, K, I = 3, 256, 8, 2, 512
+    rng = np.random.default_rng(4)
+    xb = bits_of(rng.standard_normal((T, H)))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ts = {e: gen.expert_tensors(6, 0, e, H, I) for e in range(E)}
+    y1, *_ = R.moe_layer(xb, {e: R.Expert(ts[e], H, I) for e in range(E)}, K, logits=logits)
+    ts2 = {e: dict(ts[e], sd=(ts[e]["sd"].astype(np.float32) * 2).astype(np.float16)) for e in range(E)}
+    y2, *_ = R.moe_layer(xb, {e: R.Expert(ts2[e], H, I) for e in range(E)}, K, logits=logits)
+    assert np.array_equal(y2, 2.0 * y1)
+
+
+def test_token_permutation_and_expert_relabelling():
+    T, H, E, K, I = 5, 256, 8, 3, 512
+    rng = np.random.default_rng(8)
+    xb = bits_of(rng.standard_normal((T, H)))
+    wr = gen.router_weight(2, 0, E, H)
+    experts = tiny_experts(3, E, H, I)
+    y, ids, w, _ = R.moe_layer(xb, experts, K, w_router=wr)
+    perm = rng.permutation(T)
+    yp, *_ = R.moe_layer(xb[perm], experts, K, w_router=wr)
+    assert np.array_equal(yp, y[perm])
+    sigma = rng.permutation(E)  # new id sigma[e] for old expert e
+    wr2 = np.empty_like(wr)
+    wr2[sigma] = wr
+    experts2 = {int(sigma[e]): experts[e] for e in range(E)}
+    y2, ids2, w2, _ = R.moe_layer(xb, experts2, K, w_router=wr2)
+    assert np.array_equal(ids2, sigma[ids])
+    assert np.array_equal(w2, w)
+    assert np.allclose(y2, y, rtol=1e-13, atol=1e-15)
+
+
+def test_dense_limit_is_softmax_mixture():
+    T, H, E, I = 3, 256, 6, 512
+    rng = np.random.default_rng(12)
+    xb = bits_of(rng.standard_normal((T, H)))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    experts = tiny_experts(4, E, H, I)
+    y, ids, w, _ = R.moe_layer(xb, experts, E, logits=logits)
+    p = torch.softmax(torch.from_numpy(logits.astype(np.float64)), dim=1).numpy()
+    x = R.bf16_bits_to_f64(xb)
+    want = sum(p[:, e : e + 1] * experts[e](x) for e in range(E))
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-14)
