@@ -1,0 +1,194 @@
+/*
+ * moe.h -- C ABI of the int4 routed-expert MoE layer for MI355X (gfx950).
+ *
+ * One MoE layer of a decode or prefill step: router logits, softmax + top-k
+ * routing, resolution of the chosen experts through a fixed-slot expert arena,
+ * a SwiGLU expert FFN whose int4 group-32 weights (fp16 scales) are
+ * dequantised inside the kernels, and a routing-weighted combine.
+ *
+ * Sources (web pages on the "Strata" engines):
+ *  - "Strata on a Mac (Apple Silicon, Metal)", "Switches": a router GEMV and a
+ *    separate top-k routing dispatch (moe_route); "Status": an expert cache of
+ *    64 slots; "What you need": an arena that keeps experts and reads the rest
+ *    as each token needs them, one contiguous read per expert, and a
+ *    "no free slot" failure;
+ *  - "Strata" README (ro99/strata), "Models": 4-bit grouped integer experts run
+ *    W4A16; "Architecture": a public C interface, routed experts leased into
+ *    device memory per decode step through an LRU cache; the execution rules:
+ *    top-k and precision never change silently, exact-or-explicit-failure;
+ *  - "How these numbers are measured", "Fidelity": paged output equals the
+ *    fully-resident output bit for bit.
+ *
+ * Conventions for every call:
+ *  - Return value: MOE_OK (0) or a negative moe_status; moe_strerror() names it.
+ *    No C++ exception crosses this interface.
+ *  - Argument errors are detected before anything is enqueued. GPU work is
+ *    enqueued on the stream given (a hipStream_t passed as moe_stream_t; NULL
+ *    is the default stream) and runs asynchronously; a failed launch returns
+ *    MOE_EHIP.
+ *  - The caller owns every device buffer, pinned host buffer, stream and
+ *    event. The library owns only the host metadata of an arena. Borrowed
+ *    pointers must stay valid until the work using them has completed.
+ *  - Shapes: T tokens, H hidden size, E routed experts, K experts per token,
+ *    I expert intermediate size, g the quantisation group (only g = 32).
+ *    H and I must be multiples of 32; 1 <= K <= min(E, 32); E <= 1024.
+ *    A shape the kernels do not cover returns MOE_EUNSUP; there is no slower
+ *    fallback path.
+ *  - Calls on distinct streams are reentrant. An arena is single-threaded.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+typedef void* moe_event_t;  /* a hipEvent_t */
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,  /* bad argument: NULL pointer, size, id out of range */
+  MOE_ENOSLOT = -2, /* more distinct experts requested than the arena has slots */
+  MOE_ENOTRES = -3, /* an expert was used that is not resident (device status word) */
+  MOE_EHIP = -4,    /* a HIP runtime call or kernel launch failed */
+  MOE_EUNSUP = -5,  /* shape or option outside what the kernels cover */
+  MOE_EWS = -6      /* workspace missing or smaller than moe_ffn_workspace_bytes() */
+};
+
+enum moe_flags {
+  MOE_ROUTE_RENORM = 1u << 0,  /* moe_route: divide the K selected weights by their sum */
+  MOE_FORCE_GEMV = 1u << 8,    /* moe_expert_ffn: use the per-expert GEMV path whatever T is */
+  MOE_FORCE_GROUPED = 1u << 9  /* moe_expert_ffn: use the expert-grouped MFMA GEMM path */
+};
+
+const char* moe_strerror(int status);
+int moe_version(void); /* 100 * major + minor */
+
+/* ------------------------------------------------------------------ experts
+ * An expert is one contiguous blob in device memory ("one read per expert
+ * instead of three": "Strata on a Mac", What you need): the int4 codes and the
+ * fp16 group scales of gate [I x H], up [I x H] and down [H x I]. Its internal
+ * layout belongs to the library; build it with moe_pack_expert().
+ */
+
+/* Bytes of one expert blob; 0 on an unsupported shape. */
+size_t moe_blob_bytes(int H, int I, int g);
+/* Slot stride: moe_blob_bytes rounded up to 4096. Slots of an arena and the
+ * expert-major host source are laid out with this stride. */
+size_t moe_slot_stride(int H, int I, int g);
+
+/* Pack one expert (all pointers host memory) into blob_out (host, at least
+ * moe_blob_bytes bytes). Inputs use the plain interchange format:
+ *   qg, qu: uint8 [I][H/2]; qd: uint8 [H][I/2]. Row-major int4 codes; element j
+ *           of a row is byte j/2, even j in the low nibble; each nibble is a
+ *           two's-complement value in [-8, 7] (symmetric, no zero point).
+ *   sg, su: fp16 bit patterns [I][H/g]; sd: fp16 bit patterns [H][I/g]; one
+ *           scale per g consecutive elements of a row.
+ * The dequantised weight is W[n][j] = q[n][j] * s[n][j/g]. Pure host code. */
+int moe_pack_expert(const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, const uint16_t* sg,
+                    const uint16_t* su, const uint16_t* sd, int H, int I, int g, void* blob_out);
+
+/* ------------------------------------------------------------------ routing
+ * moe_route: router logits, then softmax + top-k ("Strata on a Mac", Switches:
+ * router GEMV then moe_route).
+ *   x        device bf16 [T][H] (bit patterns); read only when w_router != NULL.
+ *   w_router device fp32 [E][H], or NULL when the logits are supplied.
+ *   logits   device fp32 [T][E]. With w_router: written,
+ *            logits[t][e] = fp32(sum_h x[t][h] * w_router[e][h]) accumulated in
+ *            fp64 (exact products) and rounded once. Without: read.
+ *   ids      device int32 [T][K], out: the K experts with the largest logits in
+ *            rank order; equal logits rank the lower id first; -0.0 == +0.0.
+ *            Logits must be finite.
+ *   w        device fp32 [T][K], out: w[t][k] = softmax(logits[t][:])[ids[t][k]]
+ *            over all E experts; with MOE_ROUTE_RENORM divided by sum_k w[t][k].
+ * Deterministic: the same inputs give the same bits on every run. */
+int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K,
+              unsigned flags, int32_t* ids, float* w, moe_stream_t stream);
+
+/* ------------------------------------------------------------------ expert FFN
+ * moe_expert_ffn: y[t] = shared(x[t]) + sum_{k=0..K-1} w[t][k] * FFN_{ids[t][k]}(x[t])
+ * with FFN(x) = Wd (silu(Wg x) * (Wu x)), silu(z) = z / (1 + e^-z), the terms
+ * added in rank order, fp32 accumulation and one bf16 rounding (nearest even)
+ * of y. Expert e's blob is at slots + slot_table[e] * stride.
+ *   x          device bf16 [T][H].
+ *   ids, w     device [T][K] as written by moe_route.
+ *   slot_table device int32 [E]; -1 marks an expert that is not resident.
+ *   slots      device base of the slot array; stride = moe_slot_stride().
+ *   shared_blob device blob of an always-on shared expert (weight 1), or NULL.
+ *   y          device bf16 [T][H], out.
+ *   ws         device workspace of ws_bytes >= moe_ffn_workspace_bytes(); its
+ *              contents need no initialisation.
+ *   dev_status device int32, written only on error: MOE_ENOTRES when a used
+ *              expert has slot_table[e] < 0, MOE_EINVAL when an id is outside
+ *              [0, E). The caller zeroes it and checks it after the stream
+ *              completes; a layer that flags an error has unspecified y.
+ *   flags      MOE_FORCE_GEMV / MOE_FORCE_GROUPED select a path; by default the
+ *              GEMV path serves T <= 32 and the grouped MFMA path larger T.
+ * The reduction order depends only on (T, K, E, flags), never on slot
+ * addresses or on which experts are resident, so a paged run gives the same
+ * bits as a fully-resident one. */
+size_t moe_ffn_workspace_bytes(int T, int H, int I, int E, int K, int has_shared, unsigned flags);
+int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K,
+                   int g, const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
+                   uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
+                   moe_stream_t stream);
+
+/* ------------------------------------------------------------------ expert arena
+ * A fixed-slot expert arena for one layer ("Strata on a Mac", Status: the
+ * expert cache at 64 slots; "Strata" README, Architecture: an LRU lease per
+ * decode step). Slot policy, deterministic:
+ *   1. the requested ids are walked in order and de-duplicated;
+ *   2. more distinct ids than slots -> MOE_ENOSLOT, an id outside [0, E) ->
+ *      MOE_EINVAL; either way the arena is unchanged;
+ *   3. a resident expert is a hit and is stamped with the call number;
+ *   4. each miss, in first-occurrence order, takes the lowest empty slot, else
+ *      evicts the expert with the oldest stamp among those not requested in
+ *      this call (ties to the lower slot), and becomes a fill {expert, slot};
+ *   5. the call number grows by one per successful call.
+ */
+typedef struct moe_arena moe_arena; /* opaque; host metadata only */
+typedef struct {
+  int32_t expert, slot;
+} moe_fill;
+typedef struct {
+  uint64_t hits, misses, evictions, fills, h2d_bytes;
+} moe_arena_stats;
+
+/* Create an arena of S slots for E experts.
+ *   slots_dev      device, S * stride bytes (caller-owned), or NULL;
+ *   slot_table_dev device int32 [E] (caller-owned), or NULL; its contents are
+ *                  the caller's until arena_fill_async updates entries;
+ *   host_src       pinned host memory, E * stride bytes, expert-major blobs
+ *                  (caller-owned), or NULL.
+ * With any of the three NULL the arena keeps book only and arena_fill_async
+ * fails with MOE_EINVAL. An empty arena holds no expert. */
+int arena_create(int E, int S, size_t blob_bytes, size_t stride, void* slots_dev, int32_t* slot_table_dev,
+                 const void* host_src, moe_arena** out);
+/* Resolve n requested ids (host int32) to slots (host int32 [n], out) and the
+ * fills the misses need (host moe_fill, capacity n, out; count in *n_fills).
+ * Precondition: no GPU work still reads a slot that may be evicted. */
+int arena_map_slots(moe_arena* a, const int32_t* ids, int n, int32_t* slots, moe_fill* fills, int* n_fills);
+/* Enqueue on `side`: one hipMemcpyAsync per fill (host_src + expert * stride ->
+ * slots_dev + slot * stride, blob_bytes), then the slot_table_dev updates
+ * (table[evicted] = -1, table[filled] = slot), then hipEventRecord(done) when
+ * done != NULL. The compute stream must wait on `done` before using the
+ * slots. Fills must come from the last arena_map_slots call. */
+int arena_fill_async(moe_arena* a, const moe_fill* fills, int n_fills, moe_stream_t side, moe_event_t done);
+/* Set-up placement: the caller has put expert's blob into slot (no copy, no
+ * table write). An expert placed elsewhere before is moved. */
+int arena_place(moe_arena* a, int expert, int slot);
+/* Host view of the current placement: slot_of[E] (-1 when absent). */
+int arena_slot_table(const moe_arena* a, int32_t* slot_of);
+int arena_reset(moe_arena* a); /* empty every slot, zero the stamps and the stats */
+int arena_stats(const moe_arena* a, moe_arena_stats* out);
+void arena_destroy(moe_arena* a);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

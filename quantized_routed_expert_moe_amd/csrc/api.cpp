@@ -1,0 +1,107 @@
+// C-ABI entry points: argument checks and dispatch to the HIP kernels.
+//
+// Exact or explicit failure ("Strata" README, execution rules: exact mode
+// completes the exact computation or reports a failure; top-k and precision are
+// never changed silently): every unsupported shape returns MOE_EUNSUP and no
+// call falls back to another computation.
+#include "moe_internal.h"
+
+namespace {
+
+bool ffn_uses_grouped(int T, unsigned flags) {
+  if (flags & MOE_FORCE_GEMV) return false;
+  if (flags & MOE_FORCE_GROUPED) return true;
+  return T > moe::kGemvMaxT;
+}
+
+bool gemv_shape_ok(int T, int H, int I, int K) {
+  // register-resident code slices: gate/up up to 16 groups per slice, down up to 16
+  return T <= moe::kGemvMaxT && K <= moe::kMaxK && H <= 16 * 16 * moe::kGroup && I <= 16 * 8 * moe::kGroup;
+}
+
+}  // namespace
+
+extern "C" const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK:
+      return "ok";
+    case MOE_EINVAL:
+      return "invalid argument";
+    case MOE_ENOSLOT:
+      return "no free slot: more distinct experts requested than the arena has slots";
+    case MOE_ENOTRES:
+      return "an expert used by the layer is not resident in the arena";
+    case MOE_EHIP:
+      return "HIP runtime call or kernel launch failed";
+    case MOE_EUNSUP:
+      return "shape or option not supported by the kernels";
+    case MOE_EWS:
+      return "workspace missing or too small";
+    default:
+      return "unknown status";
+  }
+}
+
+extern "C" int moe_version(void) { return 100; }
+
+extern "C" int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K,
+                         unsigned flags, int32_t* ids, float* w, moe_stream_t stream) {
+  if (T < 0 || E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return MOE_EINVAL;
+  if (flags & ~(unsigned)MOE_ROUTE_RENORM) return MOE_EINVAL;
+  if (E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
+  if (w_router) {
+    if (!x || H <= 0) return MOE_EINVAL;
+    if (H % moe::kGroup) return MOE_EUNSUP;
+  }
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w_router && moe::launch_router_gemv(x, w_router, logits, T, H, E, s) != hipSuccess) return MOE_EHIP;
+  if (moe::launch_route_select(logits, T, E, K, flags, ids, w, s) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
+extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int I, int E, int K, int has_shared, unsigned flags) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0) return 0;
+  if (ffn_uses_grouped(T, flags)) return moe::grouped_workspace_bytes(T, H, I, E, K, has_shared);
+  return moe::gemv_workspace_bytes(T, H, I, K, has_shared);
+}
+
+extern "C" int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E,
+                              int K, int g, const int32_t* slot_table, const void* slots, size_t stride,
+                              const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
+                              int32_t* dev_status, unsigned flags, moe_stream_t stream) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
+  if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED)) return MOE_EINVAL;
+  if ((flags & MOE_FORCE_GEMV) && (flags & MOE_FORCE_GROUPED)) return MOE_EINVAL;
+  if (!moe::shape_ok(H, I, g) || E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !w || !slot_table || !slots || !y || !dev_status) return MOE_EINVAL;
+  const size_t blob = moe_blob_bytes(H, I, g);
+  if (stride < blob || stride % 256) return MOE_EINVAL;
+  const bool grouped = ffn_uses_grouped(T, flags);
+  if (!grouped && !gemv_shape_ok(T, H, I, K)) return MOE_EUNSUP;
+  const size_t need = moe_ffn_workspace_bytes(T, H, I, E, K, shared_blob != nullptr, flags);
+  if (need == 0) return MOE_EUNSUP;
+  if (!ws || ws_bytes < need) return MOE_EWS;
+  moe::FfnArgs a;
+  a.x = x;
+  a.ids = ids;
+  a.w = w;
+  a.T = T;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.K = K;
+  a.slot_table = slot_table;
+  a.slots = static_cast<const uint8_t*>(slots);
+  a.stride = stride;
+  a.shared_blob = static_cast<const uint8_t*>(shared_blob);
+  a.y = y;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.ws_bytes = ws_bytes;
+  a.status = dev_status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err = grouped ? moe::launch_ffn_grouped(a, s) : moe::launch_ffn_gemv(a, s);
+  if (err == hipErrorNotSupported) return MOE_EUNSUP;
+  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}

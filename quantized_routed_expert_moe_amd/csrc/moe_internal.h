@@ -1,0 +1,78 @@
+// Internal declarations shared by the host entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 32;      // int4 quantisation group along the reduced dimension
+constexpr int kScaleBlock = 16; // rows per scale block in the blob
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kGemvMaxT = 32;   // default path choice: GEMV for T <= 32, grouped MFMA above
+
+// Blob layout of one expert (all offsets in bytes from the blob start).
+//   codes of gate, up, down, then scales of gate, up, down.
+// Codes of a matrix with N rows and C reduced columns (G = C / 32 groups):
+//   [G][N][16 bytes]; the 16 bytes of (group j, row n) hold the 32 codes of
+//   columns 32j .. 32j+31 as four dwords; dword d covers columns c0 = 32j + 8d
+//   .. c0+7 with nibble i (bits 4i..4i+3) = column c0 + 2i for i < 4 and
+//   c0 + 2(i-4) + 1 for i >= 4; each nibble is the offset-binary code u = q + 8.
+// Scales: [N/16][G][16] fp16, scale of (row n, group j) at ((n/16)*G + j)*16 + n%16.
+struct BlobLayout {
+  size_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales, bytes;
+};
+
+__host__ __device__ inline BlobLayout blob_layout(int H, int I) {
+  BlobLayout L;
+  const size_t mat_codes = (size_t)H * I / 2;
+  const size_t mat_scales = (size_t)H * I / kGroup * 2;
+  L.gate_codes = 0;
+  L.up_codes = mat_codes;
+  L.down_codes = 2 * mat_codes;
+  L.gate_scales = 3 * mat_codes;
+  L.up_scales = L.gate_scales + mat_scales;
+  L.down_scales = L.up_scales + mat_scales;
+  L.bytes = L.down_scales + mat_scales;
+  return L;
+}
+
+__host__ __device__ inline bool shape_ok(int H, int I, int g) {
+  return g == kGroup && H >= kGroup && I >= kGroup && H % kGroup == 0 && I % kGroup == 0 && H <= 65536 &&
+         I <= 65536;
+}
+
+// ---- launchers (return a hipError_t) ----
+hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H, int E,
+                              hipStream_t s);
+hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigned flags, int32_t* ids,
+                               float* w, hipStream_t s);
+
+struct FfnArgs {
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* w;
+  int T, H, I, E, K;
+  const int32_t* slot_table;
+  const uint8_t* slots;
+  size_t stride;
+  const uint8_t* shared_blob;
+  uint16_t* y;
+  uint8_t* ws;
+  size_t ws_bytes;
+  int32_t* status;
+};
+
+size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared);
+hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);
+
+size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
+hipError_t launch_ffn_grouped(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_table_update(int32_t* table, const int32_t* idx, const int32_t* val, int n, hipStream_t s);
+
+}  // namespace moe

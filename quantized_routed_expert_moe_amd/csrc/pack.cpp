@@ -1,0 +1,68 @@
+// Expert blob packing (host code): plain int4 interchange format -> device blob layout.
+//
+// The blob keeps one expert's three matrices in one contiguous allocation, the
+// "one read per expert instead of three" layout of "Strata on a Mac" (What you
+// need). Inside it, codes are stored group-major ([G][N][16 bytes]) so that a
+// kernel reading one group of consecutive rows touches one contiguous run, the
+// nibbles are in offset binary (u = q + 8) and interleaved so that one shift and
+// one mask turn a code dword into bf16 pairs of consecutive columns, and scales
+// are blocked by 16 rows. The layout is documented in moe_internal.h.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+// Source dword v holds 8 consecutive codes c0..c7 (byte b = codes 2b, 2b+1 in
+// its low/high nibble, two's complement). Result: low nibbles of the 4 bytes
+// (codes c0, c2, c4, c6) in nibbles 0..3, high nibbles (c1, c3, c5, c7) in
+// nibbles 4..7, each converted to offset binary by flipping bit 3.
+inline uint32_t interleave_dword(uint32_t v) {
+  uint32_t lo = v & 0x0F0F0F0Fu;
+  uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+  lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+  lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+  hi = (hi | (hi >> 4)) & 0x00FF00FFu;
+  hi = (hi | (hi >> 8)) & 0x0000FFFFu;
+  return (lo | (hi << 16)) ^ 0x88888888u;
+}
+
+void pack_matrix(const uint8_t* q, const uint16_t* s, int N, int C, uint8_t* codes, uint16_t* scales) {
+  const int G = C / moe::kGroup;
+  const size_t row_bytes = (size_t)C / 2;
+  for (int n = 0; n < N; ++n) {
+    const uint8_t* row = q + (size_t)n * row_bytes;
+    for (int j = 0; j < G; ++j) {
+      uint32_t src[4], dst[4];
+      memcpy(src, row + (size_t)j * 16, 16);
+      for (int d = 0; d < 4; ++d) dst[d] = interleave_dword(src[d]);
+      memcpy(codes + ((size_t)j * N + n) * 16, dst, 16);
+      scales[((size_t)(n / moe::kScaleBlock) * G + j) * moe::kScaleBlock + n % moe::kScaleBlock] =
+          s[(size_t)n * G + j];
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" size_t moe_blob_bytes(int H, int I, int g) {
+  if (!moe::shape_ok(H, I, g)) return 0;
+  return moe::blob_layout(H, I).bytes;
+}
+
+extern "C" size_t moe_slot_stride(int H, int I, int g) {
+  const size_t b = moe_blob_bytes(H, I, g);
+  return (b + 4095) / 4096 * 4096;
+}
+
+extern "C" int moe_pack_expert(const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, const uint16_t* sg,
+                               const uint16_t* su, const uint16_t* sd, int H, int I, int g, void* blob_out) {
+  if (!qg || !qu || !qd || !sg || !su || !sd || !blob_out) return MOE_EINVAL;
+  if (!moe::shape_ok(H, I, g)) return MOE_EUNSUP;
+  const moe::BlobLayout L = moe::blob_layout(H, I);
+  uint8_t* b = static_cast<uint8_t*>(blob_out);
+  pack_matrix(qg, sg, I, H, b + L.gate_codes, reinterpret_cast<uint16_t*>(b + L.gate_scales));
+  pack_matrix(qu, su, I, H, b + L.up_codes, reinterpret_cast<uint16_t*>(b + L.up_scales));
+  pack_matrix(qd, sd, H, I, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
+  return MOE_OK;
+}

@@ -1,0 +1,127 @@
+"""Device-side set-up for the layer: pack seeded experts into arenas and run a layer.
+
+Harness code only: input generation comes from ``synth``, packing from the C
+library (``moe_pack_expert``), and torch is used for device memory, copies and
+streams. Nothing here computes any part of the layer.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from synth import gen
+
+from . import lib
+
+
+def pack_expert(seed: int, layer: int, expert: int, H: int, I: int, g: int = 32) -> np.ndarray:
+    """Seeded expert -> host blob (uint8, one slot stride long, zero padded)."""
+    t = gen.expert_tensors(seed, layer, expert, H, I, g)
+    out = np.zeros(lib.moe_slot_stride(H, I, g), dtype=np.uint8)
+    lib.moe_pack_expert(
+        t["qg"], t["qu"], t["qd"], t["sg"].view(np.uint16), t["su"].view(np.uint16), t["sd"].view(np.uint16),
+        H, I, g, out,
+    )
+    return out
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def placeholder_blob_fill(slots: torch.Tensor) -> None:
+    """Fill unused slots with a valid all-zero-code expert (nibbles 0x8 = q 0)."""
+    slots.fill_(0x88)
+
+
+@dataclasses.dataclass
+class DeviceLayer:
+    w: gen.Workload
+    layer: int
+    x: torch.Tensor  # bf16 [T, H]
+    wr: torch.Tensor | None  # fp32 [E, H] or None (logits supplied)
+    logits: torch.Tensor  # fp32 [T, E]
+    slots: torch.Tensor  # uint8 [S * stride]
+    table: torch.Tensor  # int32 [E]
+    shared: torch.Tensor | None  # uint8 [stride]
+    arena: lib.Arena
+    stride: int
+
+
+def make_layer(w: gen.Workload, layer: int, device, slots: int | None = None, experts=None, place_seed=None,
+               logits: np.ndarray | None = None, x_bits: np.ndarray | None = None, fill_unused=True) -> DeviceLayer:
+    """Build one layer on ``device``.
+
+    ``experts``: the expert ids to pack and place (default: all E). They go to
+    slots given by a seeded random permutation when ``place_seed`` is set, else
+    to slots 0, 1, ... in order. Other slots hold the zero-code placeholder.
+    """
+    T, H, E, I = w.T, w.H, w.E, w.I
+    S = slots if slots is not None else E
+    stride = lib.moe_slot_stride(H, I, w.g)
+    xb = x_bits if x_bits is not None else gen.activations_bf16(w.seed, layer, T, H)
+    x = bf16_tensor(xb, device)
+    if w.router == "gemv":
+        wr = torch.from_numpy(gen.router_weight(w.seed, layer, E, H)).to(device)
+        lg = torch.empty(T, E, dtype=torch.float32, device=device)
+    else:
+        wr = None
+        if logits is None:
+            logits = {"normal": gen.normal_logits, "zipf": gen.zipf_logits}[w.router](w.seed, layer, T, E)
+        lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).to(device)
+    sl = torch.empty(S * stride, dtype=torch.uint8, device=device)
+    if fill_unused:
+        placeholder_blob_fill(sl)
+    table = torch.full((E,), -1, dtype=torch.int32, device=device)
+    arena = lib.Arena(E, S, lib.moe_blob_bytes(H, I, w.g), stride, sl, table, None)
+    ex = list(range(E)) if experts is None else list(experts)
+    if len(ex) > S:
+        raise ValueError("more experts than slots")
+    if place_seed is not None:
+        order = np.random.default_rng(place_seed).permutation(S)[: len(ex)]
+    else:
+        order = np.arange(len(ex))
+    host_table = np.full(E, -1, dtype=np.int32)
+    for e, s in zip(ex, order):
+        blob = pack_expert(w.seed, layer, int(e), H, I, w.g)
+        sl[int(s) * stride : (int(s) + 1) * stride].copy_(torch.from_numpy(blob), non_blocking=False)
+        arena.place(int(e), int(s))
+        host_table[int(e)] = int(s)
+    table.copy_(torch.from_numpy(host_table))
+    shared = None
+    if w.shared:
+        shared = torch.from_numpy(pack_expert(w.seed, layer, gen.SHARED_EXPERT, H, I, w.g)).to(device)
+    return DeviceLayer(w, layer, x, wr, lg, sl, table, shared, arena, stride)
+
+
+class LayerRunner:
+    """Route + expert FFN of one layer with preallocated outputs and workspace."""
+
+    def __init__(self, w: gen.Workload, device, flags: int = 0):
+        self.w, self.flags = w, flags
+        T, H, E, K, I = w.T, w.H, w.E, w.K, w.I
+        self.ids = torch.empty(T, K, dtype=torch.int32, device=device)
+        self.wts = torch.empty(T, K, dtype=torch.float32, device=device)
+        self.y = torch.empty(T, H, dtype=torch.bfloat16, device=device)
+        self.ws_bytes = lib.moe_ffn_workspace_bytes(T, H, I, E, K, w.shared, flags)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def route(self, L: DeviceLayer, stream=None, renorm=False):
+        w = self.w
+        lib.moe_route(L.x, L.wr, L.logits, w.T, w.H, w.E, w.K, lib.MOE_ROUTE_RENORM if renorm else 0, self.ids,
+                      self.wts, stream)
+
+    def ffn(self, L: DeviceLayer, stream=None, y=None):
+        w = self.w
+        lib.moe_expert_ffn(L.x, self.ids, self.wts, w.T, w.H, w.I, w.E, w.K, w.g, L.table, L.slots, L.stride,
+                           L.shared, self.y if y is None else y, self.ws, self.ws_bytes, self.status, self.flags,
+                           stream)
+
+    def __call__(self, L: DeviceLayer, stream=None):
+        self.route(L, stream)
+        self.ffn(L, stream)
+        return self.y

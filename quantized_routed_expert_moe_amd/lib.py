@@ -1,0 +1,245 @@
+"""ctypes binding of ``libmoe.so`` (include/moe.h): argument marshalling only.
+
+Every function keeps the C name and argument order. Device buffers may be
+passed as torch tensors (their ``data_ptr()`` is used) or as integer addresses;
+streams and events as ``torch.cuda.Stream`` / ``torch.cuda.Event`` or raw
+handles. Each call raises ``MoeError`` on a negative status. Nothing here
+computes any part of the layer, and a missing library is an error, never a
+reason to compute elsewhere.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOSLOT, MOE_ENOTRES, MOE_EHIP, MOE_EUNSUP, MOE_EWS = 0, -1, -2, -3, -4, -5, -6
+MOE_ROUTE_RENORM = 1 << 0
+MOE_FORCE_GEMV = 1 << 8
+MOE_FORCE_GROUPED = 1 << 9
+
+# every symbol include/moe.h declares
+EXPORTS = (
+    "moe_strerror",
+    "moe_version",
+    "moe_blob_bytes",
+    "moe_slot_stride",
+    "moe_pack_expert",
+    "moe_route",
+    "moe_ffn_workspace_bytes",
+    "moe_expert_ffn",
+    "arena_create",
+    "arena_map_slots",
+    "arena_fill_async",
+    "arena_place",
+    "arena_slot_table",
+    "arena_reset",
+    "arena_stats",
+    "arena_destroy",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_strerror(status)} ({status})")
+
+
+class moe_fill(ctypes.Structure):
+    _fields_ = [("expert", ctypes.c_int32), ("slot", ctypes.c_int32)]
+
+
+class moe_arena_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("hits", "misses", "evictions", "fills", "h2d_bytes")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+
+def load(path: str | None = None):
+    """Load libmoe.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(p)
+    sig = {
+        "moe_strerror": (ctypes.c_char_p, [_I]),
+        "moe_version": (_I, []),
+        "moe_blob_bytes": (_SZ, [_I, _I, _I]),
+        "moe_slot_stride": (_SZ, [_I, _I, _I]),
+        "moe_pack_expert": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+        "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P]),
+        "moe_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, ctypes.c_uint]),
+        "moe_expert_ffn": (
+            _I,
+            [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P, _P, _SZ, _P, ctypes.c_uint, _P],
+        ),
+        "arena_create": (_I, [_I, _I, _SZ, _SZ, _P, _P, _P, ctypes.POINTER(_P)]),
+        "arena_map_slots": (_I, [_P, _P, _I, _P, _P, ctypes.POINTER(_I)]),
+        "arena_fill_async": (_I, [_P, _P, _I, _P, _P]),
+        "arena_place": (_I, [_P, _I, _I]),
+        "arena_slot_table": (_I, [_P, _P]),
+        "arena_reset": (_I, [_P]),
+        "arena_stats": (_I, [_P, ctypes.POINTER(moe_arena_stats)]),
+        "arena_destroy": (None, [_P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _strerror(status: int) -> str:
+    return load().moe_strerror(status).decode()
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):  # numpy array
+        return x.ctypes.data
+    return int(x)
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def _event(e) -> int | None:
+    if e is None:
+        return None
+    if hasattr(e, "cuda_event"):
+        return e.cuda_event
+    return int(e)
+
+
+def _check(status: int, what: str) -> int:
+    if status < 0:
+        raise MoeError(status, what)
+    return status
+
+
+def moe_version() -> int:
+    return load().moe_version()
+
+
+def moe_blob_bytes(H: int, I: int, g: int = 32) -> int:
+    return load().moe_blob_bytes(H, I, g)
+
+
+def moe_slot_stride(H: int, I: int, g: int = 32) -> int:
+    return load().moe_slot_stride(H, I, g)
+
+
+def moe_pack_expert(qg, qu, qd, sg, su, sd, H, I, g, blob_out) -> None:
+    """Host arrays in the plain interchange format -> host blob (numpy uint8)."""
+    _check(
+        load().moe_pack_expert(_ptr(qg), _ptr(qu), _ptr(qd), _ptr(sg), _ptr(su), _ptr(sd), H, I, g, _ptr(blob_out)),
+        "moe_pack_expert",
+    )
+
+
+def moe_route(x, w_router, logits, T, H, E, K, flags, ids, w, stream=None) -> None:
+    _check(
+        load().moe_route(_ptr(x), _ptr(w_router), _ptr(logits), T, H, E, K, flags, _ptr(ids), _ptr(w), _stream(stream)),
+        "moe_route",
+    )
+
+
+def moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, flags=0) -> int:
+    return load().moe_ffn_workspace_bytes(T, H, I, E, K, int(bool(has_shared)), flags)
+
+
+def moe_expert_ffn(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                   dev_status, flags=0, stream=None) -> None:
+    _check(
+        load().moe_expert_ffn(
+            _ptr(x), _ptr(ids), _ptr(w), T, H, I, E, K, g, _ptr(slot_table), _ptr(slots), stride,
+            _ptr(shared_blob), _ptr(y), _ptr(ws), ws_bytes, _ptr(dev_status), flags, _stream(stream),
+        ),
+        "moe_expert_ffn",
+    )
+
+
+class Arena:
+    """Owner of one ``moe_arena`` handle (the C object holds host metadata only)."""
+
+    def __init__(self, E, S, blob_bytes, stride, slots_dev=None, slot_table_dev=None, host_src=None):
+        h = _P()
+        _check(
+            load().arena_create(E, S, blob_bytes, stride, _ptr(slots_dev), _ptr(slot_table_dev), _ptr(host_src),
+                                ctypes.byref(h)),
+            "arena_create",
+        )
+        self.handle = h.value
+        self.E, self.S = E, S
+        # keep borrowed buffers alive as long as the arena
+        self._keep = (slots_dev, slot_table_dev, host_src)
+
+    def map_slots(self, ids):
+        """ids: host int sequence -> (slots list, fills list of (expert, slot)); raises on MOE_ENOSLOT."""
+        n = len(ids)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in ids])
+        slots = (ctypes.c_int32 * max(n, 1))()
+        fills = (moe_fill * max(n, 1))()
+        nf = _I(0)
+        _check(load().arena_map_slots(self.handle, arr, n, slots, fills, ctypes.byref(nf)), "arena_map_slots")
+        self._last_fills = fills
+        self._last_nf = nf.value
+        return list(slots[:n]), [(fills[i].expert, fills[i].slot) for i in range(nf.value)]
+
+    def map_slots_status(self, ids) -> int:
+        """Like map_slots but returns the raw status instead of raising."""
+        n = len(ids)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in ids])
+        slots = (ctypes.c_int32 * max(n, 1))()
+        fills = (moe_fill * max(n, 1))()
+        nf = _I(0)
+        return load().arena_map_slots(self.handle, arr, n, slots, fills, ctypes.byref(nf))
+
+    def fill_async(self, side=None, done=None) -> None:
+        """Enqueue the fills of the last map_slots call on ``side``; record ``done``."""
+        _check(
+            load().arena_fill_async(self.handle, self._last_fills, self._last_nf, _stream(side), _event(done)),
+            "arena_fill_async",
+        )
+
+    def place(self, expert: int, slot: int) -> None:
+        _check(load().arena_place(self.handle, expert, slot), "arena_place")
+
+    def slot_table(self):
+        out = (ctypes.c_int32 * self.E)()
+        _check(load().arena_slot_table(self.handle, out), "arena_slot_table")
+        return list(out)
+
+    def reset(self) -> None:
+        _check(load().arena_reset(self.handle), "arena_reset")
+
+    def stats(self) -> dict:
+        st = moe_arena_stats()
+        _check(load().arena_stats(self.handle, ctypes.byref(st)), "arena_stats")
+        return {n: getattr(st, n) for n, _ in moe_arena_stats._fields_}
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.arena_destroy(self.handle)
+            self.handle = None

@@ -1,0 +1,307 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: expert ids bit-exact; routing weights within 1e-5; layer outputs
+max|y - y_ref| <= 2e-2 * rms(y_ref) (bf16 output, fp32 accumulation); paged
+and fully-resident runs bitwise equal.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from quantized_routed_expert_moe_amd import harness, lib
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def y_f64(y):
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+class OracleExperts:
+    """Oracle experts built on demand from the seeded generator (never from the GPU)."""
+
+    def __init__(self, w, layer):
+        self.w, self.layer, self.cache = w, layer, {}
+
+    def __call__(self, e):
+        if e not in self.cache:
+            self.cache[e] = R.Expert(gen.expert_tensors(self.w.seed, self.layer, e, self.w.H, self.w.I), self.w.H,
+                                     self.w.I)
+        return self.cache[e]
+
+
+def oracle_layer(w, layer, x_bits, logits=None, renorm=False):
+    wr = gen.router_weight(w.seed, layer, w.E, w.H) if w.router == "gemv" else None
+    shared = None
+    if w.shared:
+        shared = R.Expert(gen.expert_tensors(w.seed, layer, gen.SHARED_EXPERT, w.H, w.I), w.H, w.I)
+    return R.moe_layer(x_bits, OracleExperts(w, layer), w.K, logits=logits, w_router=wr, shared=shared,
+                       renorm=renorm)
+
+
+def check_close(y_gpu, y_ref, what):
+    err = np.abs(y_gpu - y_ref).max()
+    rms = np.sqrt(np.mean(y_ref**2))
+    say(f"{what}: max|err| = {err:.3e}, rms(ref) = {rms:.3e}, ratio = {err / rms if rms else float('nan'):.3e}")
+    if rms == 0:
+        assert err == 0
+    else:
+        assert err <= TOL * rms
+
+
+def small(name, **kw):
+    return gen.Workload(name, **kw)
+
+
+# ------------------------------------------------------------------ routing
+
+
+@pytest.mark.parametrize("wname,layers", [("tiny_t4_h256_e8_k2", [0]), ("decode_t1_h4096_e256_k8_i1536_x48", [0, 1, 47])])
+def test_route_gemv_matches_oracle(wname, layers):
+    w = gen.WORKLOADS[wname]
+    run = harness.LayerRunner(w, DEV)
+    for layer in layers:
+        say(f"route {wname} layer {layer}")
+        xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
+        wr = gen.router_weight(w.seed, layer, w.E, w.H)
+        x = harness.bf16_tensor(xb, DEV)
+        wr_d = torch.from_numpy(wr).to(DEV)
+        lg = torch.empty(w.T, w.E, dtype=torch.float32, device=DEV)
+        lib.moe_route(x, wr_d, lg, w.T, w.H, w.E, w.K, 0, run.ids, run.wts)
+        torch.cuda.synchronize()
+        l_ref = R.router_logits(xb, wr)
+        l_gpu = lg.cpu().numpy()
+        ulp = np.abs(l_gpu.view(np.int32).astype(np.int64) - l_ref.view(np.int32).astype(np.int64))
+        say(f"  logits differing from the correctly rounded value: {(ulp > 0).sum()} of {ulp.size}, max {ulp.max()} ulp")
+        assert ulp.max() <= 1
+        ids_ref, w_ref = R.route(l_ref, w.K)
+        assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
+        assert np.abs(run.wts.cpu().numpy() - w_ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("T,E,K,kind", [(16, 128, 8, "zipf"), (9940, 256, 8, "normal"), (7, 1024, 32, "normal"),
+                                        (5, 3, 3, "normal"), (64, 64, 1, "normal")])
+def test_route_logits_in(T, E, K, kind):
+    say(f"route logits-in T={T} E={E} K={K} {kind}")
+    lg = (gen.zipf_logits if kind == "zipf" else gen.normal_logits)(11, 0, T, E)
+    d = torch.from_numpy(lg).to(DEV)
+    ids = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    for renorm in (False, True):
+        lib.moe_route(None, None, d, T, 0, E, K, lib.MOE_ROUTE_RENORM if renorm else 0, ids, wts)
+        torch.cuda.synchronize()
+        ids_ref, w_ref = R.route(lg, K, renorm)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.abs(wts.cpu().numpy() - w_ref).max() <= 1e-5
+
+
+def test_route_ties_and_signed_zero():
+    E, K = 70, 9
+    rows = [np.zeros(E), -np.zeros(E), np.where(np.arange(E) % 3 == 0, 1.0, -0.0), np.full(E, -2.5),
+            np.where(np.arange(E) > 60, 4.0, 0.0)]
+    lg = np.array(rows, dtype=np.float32)
+    T = lg.shape[0]
+    d = torch.from_numpy(lg).to(DEV)
+    ids = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    lib.moe_route(None, None, d, T, 0, E, K, 0, ids, wts)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = R.route(lg, K)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(wts.cpu().numpy() - w_ref).max() <= 1e-6
+
+
+# ------------------------------------------------------------------ expert FFN vs oracle
+
+
+def ffn_case(w, layer, flags=0, slots=None, place_seed=None, only_routed=False):
+    say(f"ffn {w.name} layer {layer} flags={flags}")
+    xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
+    logits = None
+    if w.router != "gemv":
+        logits = {"normal": gen.normal_logits, "zipf": gen.zipf_logits}[w.router](w.seed, layer, w.T, w.E)
+    y_ref, ids_ref, w_ref, l_ref = oracle_layer(w, layer, xb, logits=logits)
+    experts = sorted(set(ids_ref.ravel().tolist())) if only_routed else None
+    L = harness.make_layer(w, layer, DEV, slots=slots, experts=experts, place_seed=place_seed, logits=logits,
+                           x_bits=xb)
+    run = harness.LayerRunner(w, DEV, flags)
+    run(L)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
+    check_close(y_f64(run.y), y_ref, f"  {w.name} layer {layer}")
+    return L, run
+
+
+def test_ffn_tiny():
+    w = gen.WORKLOADS["tiny_t4_h256_e8_k2"]
+    ffn_case(w, 0)
+    ffn_case(w, 0, place_seed=3)
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_ffn_decode_full_size(layer):
+    w = gen.WORKLOADS["decode_t1_h4096_e256_k8_i1536_x48"]
+    ffn_case(w, layer, slots=64, place_seed=100 + layer, only_routed=True)
+
+
+def test_ffn_batched_zipf_full_layer():
+    w = gen.WORKLOADS["batched_t16_h2048_e128_k8_i768_zipf"]
+    ffn_case(w, 0, only_routed=True)
+
+
+def test_ffn_paged_shape_with_shared_expert():
+    w = gen.WORKLOADS["paged_t1_h4096_e256s1_k6_i2048_x43"]
+    w1 = gen.Workload("paged_one_layer", 1, w.H, w.E, w.K, w.I, 1, 64, "normal", w.seed, shared=True)
+    ffn_case(w1, 0, slots=64, place_seed=7, only_routed=True)
+
+
+@pytest.mark.parametrize(
+    "w",
+    [
+        # ragged: down groups (3) fewer than slices, several token chunks, odd T
+        gen.Workload("ragged_t7_h1024_e16_k3_i96", 7, 1024, 16, 3, 96, 1, 16, "gemv", 21),
+        gen.Workload("ragged_t32_h512_e40_k5_i160_shared", 32, 512, 40, 5, 160, 1, 40, "normal", 22, shared=True),
+        gen.Workload("ragged_t3_h8192_e4_k4_i64", 3, 8192, 4, 4, 64, 1, 4, "zipf", 23),
+        gen.Workload("ragged_t2_h96_e6_k6_i4096", 2, 96, 6, 6, 4096, 1, 6, "normal", 24),
+    ],
+    ids=lambda w: w.name,
+)
+def test_ffn_ragged_shapes(w):
+    ffn_case(w, 0, flags=lib.MOE_FORCE_GEMV)
+
+
+# ------------------------------------------------------------------ edge cases and errors
+
+
+def test_zero_tokens_is_a_noop():
+    w = gen.WORKLOADS["tiny_t4_h256_e8_k2"]
+    L = harness.make_layer(w, 0, DEV)
+    y = torch.full((1, w.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    run = harness.LayerRunner(w, DEV)
+    lib.moe_route(L.x, L.wr, L.logits, 0, w.H, w.E, w.K, 0, run.ids, run.wts)
+    lib.moe_expert_ffn(L.x, run.ids, run.wts, 0, w.H, w.I, w.E, w.K, 32, L.table, L.slots, L.stride, None, y,
+                       run.ws, run.ws_bytes, run.status)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_zero_activation_gives_exact_zero():
+    w = gen.WORKLOADS["tiny_t4_h256_e8_k2"]
+    L = harness.make_layer(w, 0, DEV, x_bits=np.zeros((w.T, w.H), np.uint16))
+    run = harness.LayerRunner(w, DEV)
+    run(L)
+    torch.cuda.synchronize()
+    assert run.ids.cpu().numpy().tolist() == [[0, 1]] * w.T
+    assert np.all(run.wts.cpu().numpy() == np.float32(1.0 / w.E))
+    assert torch.all(run.y.float() == 0.0)
+
+
+def test_not_resident_and_bad_id_set_status():
+    w = gen.WORKLOADS["tiny_t4_h256_e8_k2"]
+    L = harness.make_layer(w, 0, DEV)
+    run = harness.LayerRunner(w, DEV)
+    run.route(L)
+    e0 = int(run.ids[0, 0].item())
+    L.table[e0] = -1
+    run.ffn(L)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == lib.MOE_ENOTRES
+    run.status.zero_()
+    run.ids[1, 1] = w.E  # out of range
+    run.ffn(L)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) in (lib.MOE_EINVAL, lib.MOE_ENOTRES)
+
+
+def test_argument_errors_return_status():
+    w = gen.WORKLOADS["tiny_t4_h256_e8_k2"]
+    L = harness.make_layer(w, 0, DEV)
+    run = harness.LayerRunner(w, DEV)
+    with pytest.raises(lib.MoeError) as e:
+        lib.moe_expert_ffn(L.x, run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 32, L.table, L.slots, L.stride, None,
+                           run.y, run.ws, 16, run.status)
+    assert e.value.status == lib.MOE_EWS
+    with pytest.raises(lib.MoeError) as e:
+        lib.moe_route(L.x, L.wr, L.logits, w.T, w.H, w.E, w.E + 1, 0, run.ids, run.wts)
+    assert e.value.status == lib.MOE_EINVAL
+    with pytest.raises(lib.MoeError) as e:
+        lib.moe_expert_ffn(L.x, run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 64, L.table, L.slots, L.stride, None,
+                           run.y, run.ws, run.ws_bytes, run.status)
+    assert e.value.status == lib.MOE_EUNSUP
+
+
+# ------------------------------------------------------------------ fidelity: paged == resident, bitwise
+
+
+def test_resident_layout_invariance_bitwise():
+    """Same layer under the identity map, a permuted map and a routed-only arena: identical bits."""
+    w = gen.Workload("fid_t5_h1024_e32_k4_i256_shared", 5, 1024, 32, 4, 256, 1, 32, "gemv", 31, shared=True)
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    outs = []
+    for slots, place_seed, only in ((None, None, False), (None, 5, False), (64, 9, True)):
+        L0 = harness.make_layer(w, 0, DEV, x_bits=xb)
+        run = harness.LayerRunner(w, DEV)
+        run.route(L0)
+        routed = sorted(set(run.ids.cpu().numpy().ravel().tolist())) if only else None
+        L = harness.make_layer(w, 0, DEV, slots=slots, experts=routed, place_seed=place_seed, x_bits=xb)
+        for _ in range(2):  # run twice: same bits
+            run(L)
+            torch.cuda.synchronize()
+            assert int(run.status.item()) == 0
+            outs.append(run.y.view(torch.int16).cpu().numpy().copy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_paged_equals_resident_at_budget_top_k():
+    """Decode steps through an arena with S = K slots (maximum paging pressure) filled by
+    arena_fill_async from pinned host memory: every step bitwise equal to the resident run."""
+    w = gen.Workload("paged_t1_h1024_e32s1_k4_i512", 1, 1024, 32, 4, 512, 2, 4, "locality", 41, shared=True)
+    steps = 24
+    lg = gen.locality_logits(w.seed, w.layers, steps, w.E, w.K)
+    stride = lib.moe_slot_stride(w.H, w.I)
+    blob = lib.moe_blob_bytes(w.H, w.I)
+    comp = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    run = harness.LayerRunner(w, DEV)
+    y_res = torch.empty_like(run.y)
+    for layer in range(w.layers):
+        host = torch.empty(w.E * stride, dtype=torch.uint8, pin_memory=True)
+        for e in range(w.E):
+            host[e * stride : (e + 1) * stride].copy_(torch.from_numpy(harness.pack_expert(w.seed, layer, e, w.H, w.I)))
+        resident = harness.make_layer(w, layer, DEV, logits=lg[0, layer][None, :])
+        slots = torch.empty(w.K * stride, dtype=torch.uint8, device=DEV)
+        table = torch.full((w.E,), -1, dtype=torch.int32, device=DEV)
+        arena = lib.Arena(w.E, w.K, blob, stride, slots, table, host)
+        ids_h = torch.empty(w.K, dtype=torch.int32, pin_memory=True)
+        done = torch.cuda.Event()
+        for s in range(steps):
+            resident.logits.copy_(torch.from_numpy(lg[s, layer][None, :]))
+            run.route(resident)
+            ids_h.copy_(run.ids.view(-1), non_blocking=True)
+            comp.synchronize()  # the per-layer hand-shake: read the router's choice
+            _, fills = arena.map_slots(ids_h.tolist())
+            arena.fill_async(side, done)
+            comp.wait_event(done)
+            run.ffn(harness.DeviceLayer(w, layer, resident.x, None, resident.logits, slots, table, resident.shared,
+                                        arena, stride))
+            run.ffn(resident, y=y_res)
+            torch.cuda.synchronize()
+            assert int(run.status.item()) == 0
+            assert torch.equal(run.y.view(torch.int16), y_res.view(torch.int16)), (layer, s)
+        st = arena.stats()
+        say(f"  layer {layer}: hits {st['hits']} misses {st['misses']} evictions {st['evictions']}")
+        assert st["misses"] > 0 and st["hits"] + st["misses"] == steps * w.K
