@@ -51,7 +51,7 @@ extern "C" int moe_route(const uint16_t* x, const float* w_router, float* logits
   if (E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
   if (w_router) {
     if (!x || H <= 0) return MOE_EINVAL;
-    if (H % moe::kGroup) return MOE_EUNSUP;
+    if (H % moe::kGroup || H > 8192) return MOE_EUNSUP;
   }
   if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -101,7 +101,13 @@ extern "C" int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float
   a.ws_bytes = ws_bytes;
   a.status = dev_status;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = grouped ? moe::launch_ffn_grouped(a, s) : moe::launch_ffn_gemv(a, s);
+  hipError_t err;
+  if (grouped)
+    err = moe::launch_ffn_grouped(a, s);
+  else if (moe::decode1_supported(T, H, I, K, shared_blob != nullptr))
+    err = moe::launch_ffn_decode1(a, s);
+  else
+    err = moe::launch_ffn_gemv(a, s);
   if (err == hipErrorNotSupported) return MOE_EUNSUP;
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -17,10 +17,9 @@
 //   LDS and h = silu(g) * u is written in fp32.
 // Kernel 2 (down + combine): item = (unit, 32 rows of H). The same scheme in
 //   fp32 (h is fp32): P = sum_c u_c h_c, sum_c q_c h_c = P - 8 * sum_c h_c.
-//   Each item writes o rows for its pairs; the last item of a row block to
-//   arrive (an agent-scope acquire/release counter) adds, for every token,
-//   the shared expert's o and then w[t][k] * o[t][k] for k = 0..K-1 in rank
-//   order, rounds once to bf16 and resets the counter.
+//   Each item writes fp32 o rows for its pairs.
+// Kernel 3 (combine): y[t] = o_shared[t] + sum_{k=0..K-1} w[t][k] * o[t][k],
+//   added in rank order and rounded once to bf16.
 // No floating-point atomics: the reduction order depends only on (T, K, E).
 #include "moe_internal.h"
 
@@ -39,7 +38,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ workspace
 struct GemvWs {
-  size_t h_off, o_off, cnt_off, bytes;
+  size_t h_off, o_off, bytes;
 };
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -49,8 +48,7 @@ __host__ __device__ inline GemvWs gemv_ws(int T, int H, int I, int K, int has_sh
   GemvWs w;
   w.h_off = 0;
   w.o_off = align256(w.h_off + pairs * I * sizeof(float));
-  w.cnt_off = align256(w.o_off + pairs * H * sizeof(float));
-  w.bytes = align256(w.cnt_off + (size_t)(H / kRowsDN) * sizeof(uint32_t));
+  w.bytes = align256(w.o_off + pairs * H * sizeof(float));
   return w;
 }
 
@@ -214,10 +212,6 @@ __global__ void __launch_bounds__(kThreads) ffn_gateup_kernel(FfnArgs a) {
   const bool has_shared = a.shared_blob != nullptr;
   const GemvWs W = gemv_ws(T, H, I, K, has_shared);
   float* hws = reinterpret_cast<float*>(a.ws + W.h_off);
-  if (blockIdx.x == 0) {  // arrival counters of the down kernel start at zero
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + W.cnt_off);
-    for (int i = tid; i < H / kRowsDN; i += kThreads) cnt[i] = 0;
-  }
   build_plan(L.plan, a.ids, T, K, a.E, has_shared, a.status);
   const int n_rb = I / kRowsGU;
   const int n_items = L.plan.n_units * n_rb;
@@ -337,7 +331,6 @@ __global__ void __launch_bounds__(kThreads) ffn_gateup_kernel(FfnArgs a) {
 struct DnLds {
   PlanLds plan;
   float red[kTB][kSlicesDN][kRowsDN];
-  int last;
   // followed by: h chunk fp32 [kTB][I], group sums fp32 [kTB][Gd]
 };
 
@@ -355,7 +348,6 @@ __global__ void __launch_bounds__(kThreads) ffn_down_kernel(FfnArgs a) {
   const GemvWs W = gemv_ws(T, H, I, K, has_shared);
   const float* hws = reinterpret_cast<const float*>(a.ws + W.h_off);
   float* ows = reinterpret_cast<float*>(a.ws + W.o_off);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + W.cnt_off);
   build_plan(L.plan, a.ids, T, K, a.E, has_shared, a.status);
   const int n_rb = H / kRowsDN;
   const int n_units = L.plan.n_units;
@@ -453,27 +445,23 @@ __global__ void __launch_bounds__(kThreads) ffn_down_kernel(FfnArgs a) {
       }
       __syncthreads();
     }
-    // arrival: the last unit of this row block combines it
-    __threadfence();
     __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&cnt[rb], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      L.last = (old == (uint32_t)(n_units - 1));
-    }
-    __syncthreads();
-    if (L.last) {
-      __threadfence();
-      for (int idx = tid; idx < T * kRowsDN; idx += kThreads) {
-        const int t = idx / kRowsDN, rr = idx % kRowsDN;
-        const size_t col = (size_t)rb * kRowsDN + rr;
-        float acc = has_shared ? ows[(size_t)(T * K + t) * H + col] : 0.0f;
-        for (int k = 0; k < K; ++k)
-          acc = fmaf(a.w[t * K + k], ows[(size_t)(t * K + k) * H + col], acc);
-        a.y[(size_t)t * H + col] = __builtin_bit_cast(uint16_t, (__bf16)acc);
-      }
-      if (tid == 0) cnt[rb] = 0;
-    }
-    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ combine
+__global__ void __launch_bounds__(kThreads) ffn_combine_kernel(FfnArgs a) {
+  const int H = a.H, T = a.T, K = a.K;
+  const bool has_shared = a.shared_blob != nullptr;
+  const GemvWs W = gemv_ws(T, H, a.I, K, has_shared);
+  const float* ows = reinterpret_cast<const float*>(a.ws + W.o_off);
+  const size_t total = (size_t)T * H;
+  for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += (size_t)gridDim.x * kThreads) {
+    const int t = (int)(idx / H);
+    const size_t col = idx % H;
+    float acc = has_shared ? ows[(size_t)(T * K + t) * H + col] : 0.0f;
+    for (int k = 0; k < K; ++k) acc = fmaf(a.w[t * K + k], ows[(size_t)(t * K + k) * H + col], acc);
+    a.y[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc);
   }
 }
 
@@ -545,6 +533,14 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s) {
       default:
         return hipErrorInvalidValue;
     }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const size_t total = (size_t)a.T * a.H;
+    const size_t blocks = (total + kThreads - 1) / kThreads;
+    const int grid = blocks < 2048 ? (int)blocks : 2048;
+    hipLaunchKernelGGL(ffn_combine_kernel, dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
 }

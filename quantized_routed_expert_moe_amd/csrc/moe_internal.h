@@ -70,6 +70,10 @@ struct FfnArgs {
 size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared);
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);
 
+// single-token decode kernels (a specialisation of the GEMV path)
+bool decode1_supported(int T, int H, int I, int K, bool has_shared);
+hipError_t launch_ffn_decode1(const FfnArgs& a, hipStream_t s);
+
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
 hipError_t launch_ffn_grouped(const FfnArgs& a, hipStream_t s);
 

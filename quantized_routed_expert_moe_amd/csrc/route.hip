@@ -14,40 +14,57 @@ constexpr int kRouterTok = 4;  // tokens per router wave (one router row is read
 __device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// One wave per (expert, block of kRouterTok tokens). Each lane accumulates its
-// columns h = 4*lane + 256*i in order in fp64 (the bf16 x fp32 products are
-// exact in fp64), then a fixed butterfly sums the 64 lanes; one rounding to
-// fp32 at the end. The reduction order is fixed, so the bits are reproducible.
-__global__ void __launch_bounds__(64) router_gemv_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wr,
-                                                         float* __restrict__ logits, int T, int H, int E) {
+// One workgroup (4 waves) per (expert, block of kRouterTok tokens). Wave w
+// covers the contiguous quarter [w*H/4, (w+1)*H/4) of the row; lane l takes
+// columns 4l + 256i of it, all loads issued before any arithmetic. Each lane
+// accumulates its columns in order in fp64 (bf16 x fp32 products are exact in
+// fp64), a fixed butterfly sums the lanes, and the four wave sums are added in
+// wave order; one rounding to fp32 at the end. The order is fixed, so the bits
+// are reproducible.
+constexpr int kRouterMaxIt = 8;  // columns per lane = 4 * kRouterMaxIt -> H <= 8192
+
+__global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                          float* __restrict__ logits, int T, int H, int E) {
+  __shared__ double part[4][kRouterTok];
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * kRouterTok;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = H / 4;
+  const int h0 = wave * q;
   const float* w = wr + (size_t)e * H;
-  double acc[kRouterTok];
+  float4 wv[kRouterMaxIt];
+  uint2 xv[kRouterTok][kRouterMaxIt];
 #pragma unroll
-  for (int i = 0; i < kRouterTok; ++i) acc[i] = 0.0;
-  for (int h = 4 * lane; h < H; h += 256) {
-    const float4 wv = *reinterpret_cast<const float4*>(w + h);
+  for (int i = 0; i < kRouterMaxIt; ++i) {
+    const int h = 4 * lane + 256 * i;
+    if (h < q) {
+      wv[i] = *reinterpret_cast<const float4*>(w + h0 + h);
 #pragma unroll
-    for (int i = 0; i < kRouterTok; ++i) {
-      if (t0 + i < T) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + i) * H + h);
-        double a = acc[i];
-        a = fma((double)bf16_lo(xv.x), (double)wv.x, a);
-        a = fma((double)bf16_hi(xv.x), (double)wv.y, a);
-        a = fma((double)bf16_lo(xv.y), (double)wv.z, a);
-        a = fma((double)bf16_hi(xv.y), (double)wv.w, a);
-        acc[i] = a;
-      }
+      for (int tt = 0; tt < kRouterTok; ++tt)
+        if (t0 + tt < T) xv[tt][i] = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + tt) * H + h0 + h);
     }
   }
 #pragma unroll
-  for (int i = 0; i < kRouterTok; ++i) {
-    double a = acc[i];
+  for (int tt = 0; tt < kRouterTok; ++tt) {
+    double a = 0.0;
+#pragma unroll
+    for (int i = 0; i < kRouterMaxIt; ++i) {
+      if (4 * lane + 256 * i < q && t0 + tt < T) {
+        a = fma((double)bf16_lo(xv[tt][i].x), (double)wv[i].x, a);
+        a = fma((double)bf16_hi(xv[tt][i].x), (double)wv[i].y, a);
+        a = fma((double)bf16_lo(xv[tt][i].y), (double)wv[i].z, a);
+        a = fma((double)bf16_hi(xv[tt][i].y), (double)wv[i].w, a);
+      }
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
-    if (lane == 0 && t0 + i < T) logits[(size_t)(t0 + i) * E + e] = (float)a;
+    if (lane == 0) part[wave][tt] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x < kRouterTok && t0 + (int)threadIdx.x < T) {
+    const int tt = threadIdx.x;
+    const double s = ((part[0][tt] + part[1][tt]) + part[2][tt]) + part[3][tt];
+    logits[(size_t)(t0 + tt) * E + e] = (float)s;
   }
 }
 
@@ -148,7 +165,7 @@ __global__ void __launch_bounds__(64) table_update_kernel(int32_t* table, TableU
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H, int E,
                               hipStream_t s) {
   dim3 grid(E, (T + kRouterTok - 1) / kRouterTok);
-  hipLaunchKernelGGL(router_gemv_kernel, grid, dim3(64), 0, s, x, wr, logits, T, H, E);
+  hipLaunchKernelGGL(router_gemv_kernel, grid, dim3(256), 0, s, x, wr, logits, T, H, E);
   return hipGetLastError();
 }
 

@@ -128,6 +128,8 @@ def _event(e) -> int | None:
     if e is None:
         return None
     if hasattr(e, "cuda_event"):
+        if not e.cuda_event:  # torch creates the HIP event on its first record
+            raise ValueError("the event has no HIP event yet: record it once before passing it")
         return e.cuda_event
     return int(e)
 

@@ -288,6 +288,7 @@ def test_paged_equals_resident_at_budget_top_k():
         arena = lib.Arena(w.E, w.K, blob, stride, slots, table, host)
         ids_h = torch.empty(w.K, dtype=torch.int32, pin_memory=True)
         done = torch.cuda.Event()
+        done.record(side)  # creates the HIP event
         for s in range(steps):
             resident.logits.copy_(torch.from_numpy(lg[s, layer][None, :]))
             run.route(resident)
