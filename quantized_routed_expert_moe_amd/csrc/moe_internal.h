@@ -75,6 +75,7 @@ bool decode1_supported(int T, int H, int I, int K, bool has_shared);
 hipError_t launch_ffn_decode1(const FfnArgs& a, hipStream_t s);
 
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
+bool grouped_shape_ok(int H, int I);
 hipError_t launch_ffn_grouped(const FfnArgs& a, hipStream_t s);
 
 hipError_t launch_table_update(int32_t* table, const int32_t* idx, const int32_t* val, int n, hipStream_t s);

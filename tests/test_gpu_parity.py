@@ -1,8 +1,11 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
-Bars: expert ids bit-exact; routing weights within 1e-5; layer outputs
-max|y - y_ref| <= 2e-2 * rms(y_ref) (bf16 output, fp32 accumulation); paged
-and fully-resident runs bitwise equal.
+Bars: expert ids bit-exact; routing weights within 1e-5; layer outputs within
+2e-2 * rms(y_ref) of the fp64 oracle beyond the output format's own rounding,
+i.e. |y - y_ref| <= 2e-2 * rms(y_ref) + ulp_bf16(y_ref) / 2 elementwise (the
+layer's outputs are heavy-tailed, max|y| / rms up to ~12, so rounding the exact
+result to bf16 alone can exceed 2e-2 * rms); paged and fully-resident runs
+bitwise equal.
 """
 
 import sys
@@ -51,14 +54,23 @@ def oracle_layer(w, layer, x_bits, logits=None, renorm=False):
                        renorm=renorm)
 
 
+def bf16_half_ulp(y):
+    """Half the bf16 spacing at each value: the rounding any bf16 output of it carries."""
+    a = np.abs(y)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 8), 0.0)
+
+
 def check_close(y_gpu, y_ref, what):
-    err = np.abs(y_gpu - y_ref).max()
+    d = np.abs(y_gpu - y_ref)
     rms = np.sqrt(np.mean(y_ref**2))
-    say(f"{what}: max|err| = {err:.3e}, rms(ref) = {rms:.3e}, ratio = {err / rms if rms else float('nan'):.3e}")
+    beyond = np.max(d - bf16_half_ulp(y_ref))
+    say(f"{what}: max|err| / rms = {d.max() / rms if rms else float('nan'):.3e}, beyond the bf16 half-ulp "
+        f"{beyond / rms if rms else float('nan'):.3e}, max|y_ref| / rms = {np.abs(y_ref).max() / rms if rms else 0:.1f}")
     if rms == 0:
-        assert err == 0
+        assert d.max() == 0
     else:
-        assert err <= TOL * rms
+        assert beyond <= TOL * rms
 
 
 def small(name, **kw):
@@ -306,3 +318,70 @@ def test_paged_equals_resident_at_budget_top_k():
         st = arena.stats()
         say(f"  layer {layer}: hits {st['hits']} misses {st['misses']} evictions {st['evictions']}")
         assert st["misses"] > 0 and st["hits"] + st["misses"] == steps * w.K
+
+
+# ------------------------------------------------------------------ grouped (prefill) path
+
+
+@pytest.mark.parametrize(
+    "w",
+    [
+        gen.Workload("grouped_t300_h512_e16_k4_i256", 300, 512, 16, 4, 256, 1, 16, "normal", 51),
+        gen.Workload("grouped_t77_h1024_e40_k6_i192_shared", 77, 1024, 40, 6, 192, 1, 40, "zipf", 52, shared=True),
+        gen.Workload("grouped_t33_h256_e8_k2_i512", 33, 256, 8, 2, 512, 1, 8, "gemv", 53),
+        gen.Workload("grouped_t5_h384_e3_k3_i128", 5, 384, 3, 3, 128, 1, 3, "normal", 54),
+    ],
+    ids=lambda w: w.name,
+)
+def test_grouped_matches_oracle(w):
+    flags = lib.MOE_FORCE_GROUPED if w.T <= 32 else 0
+    L, run = ffn_case(w, 0, flags=flags, place_seed=2)
+    first = run.y.view(torch.int16).clone()
+    run(L)  # same inputs again: identical bits although the pair scatter uses atomics
+    torch.cuda.synchronize()
+    assert torch.equal(run.y.view(torch.int16), first)
+
+
+def test_grouped_prefill_full_size_sampled_tokens():
+    """Prefill at full size (9940 tokens, 256 experts, top-8): sampled tokens vs the oracle."""
+    w = gen.WORKLOADS["prefill_t9940_h4096_e256_k8_i1536"]
+    say("packing 256 experts for the prefill layer")
+    logits = gen.normal_logits(w.seed, 0, w.T, w.E)
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    L = harness.make_layer(w, 0, DEV, logits=logits, x_bits=xb, place_seed=4)
+    run = harness.LayerRunner(w, DEV)
+    run(L)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    ids_ref, w_ref = R.route(logits, w.K)
+    assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
+    counts = np.bincount(ids_ref.ravel(), minlength=w.E)
+    say(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}")
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(w.T, size=10, replace=False))
+    sample = np.concatenate([sample, [0, w.T - 1]])
+    experts = OracleExperts(w, 0)
+    y_ref, *_ = R.moe_layer(xb[sample], experts, w.K, logits=logits[sample])
+    y = y_f64(run.y)
+    check_close(y[sample], y_ref, "  prefill sampled tokens")
+    # the whole output is finite and the layer is deterministic
+    assert np.isfinite(y).all()
+    first = run.y.view(torch.int16).clone()
+    run.ffn(L)
+    torch.cuda.synchronize()
+    assert torch.equal(run.y.view(torch.int16), first)
+
+
+def test_grouped_equals_gemv_path_within_tolerance():
+    """The two paths are separate kernels; on a shape both serve they agree to the oracle's bar."""
+    w = gen.Workload("both_t24_h512_e12_k3_i256", 24, 512, 12, 3, 256, 1, 12, "normal", 55, shared=True)
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    logits = gen.normal_logits(w.seed, 0, w.T, w.E)
+    y_ref, *_ = oracle_layer(w, 0, xb, logits=logits)
+    L = harness.make_layer(w, 0, DEV, logits=logits, x_bits=xb)
+    for flags in (lib.MOE_FORCE_GEMV, lib.MOE_FORCE_GROUPED):
+        run = harness.LayerRunner(w, DEV, flags)
+        run(L)
+        torch.cuda.synchronize()
+        assert int(run.status.item()) == 0
+        check_close(y_f64(run.y), y_ref, f"  flags {flags}")
