@@ -1,12 +1,18 @@
 """Benchmark of the int4 routed-expert MoE layer on one MI355X.
 
-Default workload: single-token decode through 48 MoE layers (hidden 4096, 256
+Headline workload: single-token decode through 48 MoE layers (hidden 4096, 256
 experts, top-8, intermediate 1536, int4 group-32 experts with fp16 scales, fp32
-router, a 64-slot arena per layer with a seeded random expert-to-slot map and
+router, one 64-slot arena per layer with a seeded random expert-to-slot map and
 every routed expert resident). One step = one token through all 48 layers:
 per layer moe_route (router GEMV + softmax top-k) and moe_expert_ffn (int4
-SwiGLU experts + combine). Inputs are seeded synthetic tensors already resident
-in HBM. Prints one JSON line.
+SwiGLU experts + combine), replayed as one HIP graph. Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.
+
+Further workloads, reported in the same JSON line under "workloads":
+prefill of 9,940 tokens through one layer (expert-grouped MFMA path) and
+batched decode of 16 tokens with Zipf-skewed routing (rotating over distinct
+layer weight sets so the 256 MB last-level cache cannot hold them).
+Prints one JSON line on stdout; progress goes to stderr.
 """
 
 from __future__ import annotations
@@ -20,8 +26,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
-BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
 def parse():
@@ -30,9 +36,12 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=48)
+    p.add_argument("--legs", default="decode,prefill,batched", help="comma list of decode,prefill,batched")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-layers", type=int, default=3, help="layers in the oracle's timed sample")
-    p.add_argument("--graph", type=int, default=1, help="replay the layer stack as a HIP graph (1) or eagerly (0)")
+    p.add_argument("--cpu-layers", type=int, default=3, help="decode layers in the oracle's timed sample")
+    p.add_argument("--graph", type=int, default=1, help="replay the decode layer stack as a HIP graph")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="first run one plain device-to-device copy of this many MiB (counter calibration for profiles)")
     return p.parse_args()
 
 
@@ -40,8 +49,36 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_decode_stack(w, layers, dev):
-    import numpy as np
+def ev():
+    import torch
+
+    return torch.cuda.Event(enable_timing=True)
+
+
+def stage_times(calls, stream, reps=1):
+    """Mean duration (us) of each named call over reps, from HIP events recorded on `stream`."""
+    import torch
+
+    acc = {}
+    for _ in range(reps):
+        marks = []
+        with torch.cuda.stream(stream):
+            for name, f in calls:
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                f()
+                e1.record(stream)
+                marks.append((name, e0, e1))
+        torch.cuda.synchronize()
+        for name, e0, e1 in marks:
+            acc.setdefault(name, []).append(e0.elapsed_time(e1) * 1e3)
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+# ------------------------------------------------------------------ decode (headline)
+
+
+def build_decode_stack(w, dev):
     import torch
 
     from quantized_routed_expert_moe_amd import harness, lib
@@ -51,85 +88,40 @@ def build_decode_stack(w, layers, dev):
     run = harness.LayerRunner(w, dev)
     t0 = time.time()
     lg = torch.empty(w.T, w.E, dtype=torch.float32, device=dev)
-    for layer in range(layers):
+    for layer in range(w.layers):
         xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
-        # routing first (set-up only): the routed experts are the ones placed in the arena
+        # set-up only: route first, then place the routed experts in the layer's arena
         x = harness.bf16_tensor(xb, dev)
         wr = torch.from_numpy(gen.router_weight(w.seed, layer, w.E, w.H)).to(dev)
         lib.moe_route(x, wr, lg, w.T, w.H, w.E, w.K, 0, run.ids, run.wts)
         routed = sorted(set(run.ids.cpu().numpy().ravel().tolist()))
-        L = harness.make_layer(w, layer, dev, slots=w.slots, experts=routed, place_seed=1000 + layer, x_bits=xb)
-        stacks.append(L)
-        if layer % 8 == 7:
-            log(f"  packed layers 0..{layer} ({time.time() - t0:.1f} s)")
+        stacks.append(harness.make_layer(w, layer, dev, slots=w.slots, experts=routed, place_seed=1000 + layer,
+                                         x_bits=xb))
+        if layer % 16 == 15:
+            log(f"  decode: packed layers 0..{layer} ({time.time() - t0:.1f} s)")
     torch.cuda.synchronize()
     return stacks
 
 
-def cpu_baseline(w, n_layers):
-    """The oracle, as it stands, on the first n_layers layers of the same workload."""
-    import numpy as np
-
-    from oracle import moe_ref as R
-    from synth import gen
-
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    t_total = 0.0
-    for layer in range(n_layers):
-        xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
-        wr = gen.router_weight(w.seed, layer, w.E, w.H)
-        tensors = {}
-
-        def experts(e, layer=layer, tensors=tensors):
-            return R.Expert(tensors.setdefault(e, gen.expert_tensors(w.seed, layer, e, w.H, w.I)), w.H, w.I)
-
-        # input generation is outside the timed region: draw the routed experts first
-        ids = R.select_topk(R.router_logits(xb, wr), w.K)
-        for e in set(ids.ravel().tolist()):
-            tensors[e] = gen.expert_tensors(w.seed, layer, e, w.H, w.I)
-        t = time.perf_counter()
-        R.moe_layer(xb, experts, w.K, w_router=wr)
-        t_total += time.perf_counter() - t
-    per_layer = t_total / n_layers
-    return {
-        "value": 1.0 / (per_layer * w.layers),
-        "unit": "tokens/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{n_layers} of {w.layers} layers (1 token each), fp64 NumPy oracle; "
-        f"{per_layer:.2f} s per layer, scaled to a {w.layers}-layer token",
-    }
-
-
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU path)",
-              file=sys.stderr)
-        sys.exit(2)
+def decode_leg(a, dev):
     import numpy as np
     import torch
 
     from quantized_routed_expert_moe_amd import harness, lib
     from synth import gen
 
-    lib.load()
-    dev = "cuda:0"
     base = gen.WORKLOADS["decode_t1_h4096_e256_k8_i1536_x48"]
     w = gen.Workload(base.name, base.T, base.H, base.E, base.K, base.I, a.layers, base.slots, base.router, base.seed)
-    log(f"building {w.layers} layers of {w.name}")
-    stacks = build_decode_stack(w, w.layers, dev)
+    log(f"decode: building {w.layers} layers of {w.name}")
+    stacks = build_decode_stack(w, dev)
     run = harness.LayerRunner(w, dev)
     stream = torch.cuda.Stream()
     blob = lib.moe_blob_bytes(w.H, w.I)
-    bytes_router = w.E * w.H * 4 + w.T * w.H * 2 + w.T * w.E * 4
-    bytes_ffn = w.K * blob + w.T * w.H * 2 * 2  # routed experts + x read + y write
-    bytes_layer = bytes_router + bytes_ffn
+    mat_bytes = w.H * w.I // 2 + w.H * w.I // 32 * 2  # codes + fp16 scales of one matrix
+    bytes_router = w.E * w.H * 4 + w.T * w.H * 2 + w.T * w.E * 4 + w.T * w.K * 8
+    bytes_gate_up = w.K * 2 * mat_bytes + w.T * w.H * 2 + w.T * w.K * w.I * 4  # experts + x + h
+    bytes_down = w.K * mat_bytes + w.T * w.K * w.I * 4 + w.T * w.H * 2  # experts + h + y
+    bytes_layer = bytes_router + w.K * blob + w.T * w.H * 2 * 2
 
     def step():
         for L in stacks:
@@ -148,52 +140,231 @@ def main():
         with torch.cuda.graph(graph, stream=stream):
             step()
         stream.synchronize()
+        y_graph = run.y.clone()
+        with torch.cuda.stream(stream):
+            step()
+        stream.synchronize()
+        if not torch.equal(run.y.view(torch.int16), y_graph.view(torch.int16)):
+            raise RuntimeError("graph replay output differs from the eager output")
 
-    # timed region: exactly K steps, synchronised on both sides
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
     t0 = time.perf_counter()
-    ev0.record(stream)
+    e0.record(stream)
     with torch.cuda.stream(stream):
         for _ in range(a.steps):
             if graph is not None:
                 graph.replay()
             else:
                 step()
-    ev1.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / a.steps
-    tok_s = 1000.0 / ms_step
+    ms_step = e0.elapsed_time(e1) / a.steps
 
-    # per-call durations with HIP events on the launch stream (diagnostics and roofline)
-    n_probe = min(len(stacks), 48)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(n_probe)]
+    # per-stage durations with HIP events on the launch stream, every layer, 3 passes
+    t = {"route": [], "gate_up": [], "down": []}
+    for _ in range(3):
+        for L in stacks:
+            st = stage_times([("route", lambda L=L: run.route(L, stream)),
+                              ("gate_up", lambda L=L: run.ffn(L, stream, stage="gate_up")),
+                              ("down", lambda L=L: run.ffn(L, stream, stage="down"))], stream)
+            for k in t:
+                t[k].append(st[k])
+    us = {k: float(np.mean(v)) for k, v in t.items()}
+    gu_gbs = bytes_gate_up / (us["gate_up"] * 1e-6) / 1e9
+    dn_gbs = bytes_down / (us["down"] * 1e-6) / 1e9
+    layer_gbs = bytes_layer * w.layers / (ms_step * 1e-3) / 1e9
+    return w, {
+        "tok_s": 1000.0 / ms_step,
+        "ms_step": ms_step,
+        "wall": wall,
+        "graph": graph is not None,
+        "layer_gbs": layer_gbs,
+        "us": us,
+        "bytes": {"router": bytes_router, "gate_up": bytes_gate_up, "down": bytes_down, "layer": bytes_layer},
+        "gu_gbs": gu_gbs,
+        "dn_gbs": dn_gbs,
+    }
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def prefill_leg(a, dev):
+    import torch
+
+    from quantized_routed_expert_moe_amd import harness
+    from synth import gen
+
+    w = gen.WORKLOADS["prefill_t9940_h4096_e256_k8_i1536"]
+    log(f"prefill: packing {w.E} experts for {w.name}")
+    t0 = time.time()
+    L = harness.make_layer(w, 0, dev, place_seed=4)
+    log(f"  prefill: packed ({time.time() - t0:.1f} s)")
+    run = harness.LayerRunner(w, dev)
+    stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for L, (e0, e1, e2) in zip(stacks[:n_probe], evs):
-            e0.record(stream)
-            run.route(L, stream)
-            e1.record(stream)
-            run.ffn(L, stream)
-            e2.record(stream)
+        for _ in range(2):
+            run(L, stream)
+    stream.synchronize()
+    if int(run.status.item()) != 0:
+        raise RuntimeError(f"device status {int(run.status.item())}")
+    reps = 5
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            run(L, stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    t_route = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in evs])) * 1e3
-    t_ffn = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in evs])) * 1e3
-    achieved = bytes_ffn / (t_ffn * 1e-6) / 1e9
+    ms = e0.elapsed_time(e1) / reps
+    st = stage_times([("route", lambda: run.route(L, stream)),
+                      ("gate_up", lambda: run.ffn(L, stream, stage="gate_up")),
+                      ("down", lambda: run.ffn(L, stream, stage="down"))], stream, reps=3)
+    P = w.T * w.K
+    fl_gu = 2.0 * P * w.H * 2 * w.I
+    fl_dn = 2.0 * P * w.I * w.H
+    return w, {
+        "tok_s": w.T / (ms * 1e-3),
+        "ms_layer": ms,
+        "us": st,
+        "tflops_layer": (fl_gu + fl_dn) / (ms * 1e-3) / 1e12,
+        "tflops_gate_up": fl_gu / (st["gate_up"] * 1e-6) / 1e12,
+        "tflops_down": fl_dn / (st["down"] * 1e-6) / 1e12,
+        "flops": fl_gu + fl_dn,
+    }
 
+
+# ------------------------------------------------------------------ batched decode
+
+
+def batched_leg(a, dev, n_sets=16):
+    import numpy as np
+    import torch
+
+    from quantized_routed_expert_moe_amd import harness
+    from synth import gen
+
+    w = gen.WORKLOADS["batched_t16_h2048_e128_k8_i768_zipf"]
+    log(f"batched: packing {n_sets} distinct layer weight sets of {w.name}")
+    t0 = time.time()
+    sets = []
+    for layer in range(n_sets):
+        lg = gen.zipf_logits(w.seed, layer, w.T, w.E)
+        top = np.argsort(-lg, axis=1, kind="stable")[:, : w.K]  # set-up only: which experts to pack
+        experts = sorted(set(top.ravel().tolist()))
+        sets.append(harness.make_layer(w, layer, dev, experts=experts, place_seed=layer, logits=lg))
+    log(f"  batched: packed ({time.time() - t0:.1f} s)")
+    run = harness.LayerRunner(w, dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for L in sets:
+            run(L, stream)
+    stream.synchronize()
+    if int(run.status.item()) != 0:
+        raise RuntimeError(f"device status {int(run.status.item())}")
+    distinct = []
+    for L in sets:
+        run.route(L, stream)
+        stream.synchronize()
+        distinct.append(len(set(run.ids.cpu().numpy().ravel().tolist())))
+    reps = 10
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            for L in sets:
+                run(L, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_layer = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+    blob = harness.lib.moe_blob_bytes(w.H, w.I)
+    bytes_layer = float(np.mean(distinct)) * blob + w.T * w.E * 4 + 2 * w.T * w.H * 2
+    return w, {
+        "tok_s": w.T / (us_layer * 1e-6),
+        "us_layer": us_layer,
+        "distinct_experts": float(np.mean(distinct)),
+        "hbm_gbs": bytes_layer / (us_layer * 1e-6) / 1e9,
+        "bytes_layer": bytes_layer,
+    }
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+
+def cpu_baseline(w, n_layers):
+    """The oracle, as it stands, on the first n_layers decode layers of the headline workload."""
+    from oracle import moe_ref as R
+    from synth import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    t_total = 0.0
+    for layer in range(n_layers):
+        xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
+        wr = gen.router_weight(w.seed, layer, w.E, w.H)
+        tensors = {}
+        ids = R.select_topk(R.router_logits(xb, wr), w.K)
+        for e in set(ids.ravel().tolist()):  # input generation stays outside the timed region
+            tensors[e] = gen.expert_tensors(w.seed, layer, e, w.H, w.I)
+
+        def experts(e, layer=layer, tensors=tensors):
+            return R.Expert(tensors[e], w.H, w.I)
+
+        t = time.perf_counter()
+        R.moe_layer(xb, experts, w.K, w_router=wr)
+        t_total += time.perf_counter() - t
+    per_layer = t_total / n_layers
+    return {
+        "value": round(1.0 / (per_layer * w.layers), 5),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n_layers} of the {w.layers} decode layers (1 token each, fp64 NumPy oracle incl. "
+        f"dequantisation); {per_layer:.2f} s per layer, scaled to one {w.layers}-layer token",
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from quantized_routed_expert_moe_amd import lib
+
+    lib.load()
+    dev = "cuda:0"
+    legs = set(a.legs.split(","))
+    if a.copy_probe_mib:
+        src = torch.empty(a.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written")
+        del src, dst
+    w, d = decode_leg(a, dev)
     out = {
-        "metric": "MoE-layer decode tokens/s (48 layers per token) + achieved HBM GB/s",
-        "value": round(tok_s, 2),
+        "metric": "MoE-layer decode tokens/s (one token through 48 layers) + achieved HBM GB/s",
+        "value": round(d["tok_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(d["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights (fp16 group scales), bf16 activations, fp32 accumulate",
+        "dtype": "int4 weights + fp16 group scales, bf16 activations, fp32 accumulate",
         "data": "synthetic (seeded)",
         "config": {
             "workload": w.name,
@@ -205,22 +376,60 @@ def main():
             "intermediate": w.I,
             "group": w.g,
             "arena_slots": w.slots,
-            "hip_graph": bool(graph is not None),
+            "hip_graph": d["graph"],
         },
-        "hbm_gbs_layer": round(bytes_layer * w.layers / (ms_step * 1e-3) / 1e9, 1),
-        "hbm_frac_layer": round(bytes_layer * w.layers / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "per_layer_us": {"route": round(t_route, 2), "expert_ffn": round(t_ffn, 2), "step_avg": round(ms_step * 1e3 / w.layers, 2)},
+        "hbm_gbs": round(d["layer_gbs"], 1),
+        "hbm_frac": round(d["layer_gbs"] / HBM_PEAK_GBS, 4),
+        "per_layer_us": {k: round(v, 2) for k, v in d["us"].items()} | {"step_avg": round(d["ms_step"] * 1e3 / w.layers, 2)},
         "roofline": {
-            "kernel": "moe_expert_ffn (gate/up + down/combine)",
+            "kernel": "dec_gateup_kernel (moe_ffn_gate_up, single-token path)",
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": round(d["gu_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": round(d["gu_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": None,
+            "bytes_per_launch": d["bytes"]["gate_up"],
         },
-        "wall_s_timed": round(wall, 4),
+        "roofline_down": {
+            "kernel": "dec_down_kernel (moe_ffn_down, single-token path)",
+            "bound": "hbm",
+            "achieved": round(d["dn_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(d["dn_gbs"] / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": d["bytes"]["down"],
+        },
+        "wall_s_timed": round(d["wall"], 4),
+        "workloads": {},
     }
+    torch.cuda.empty_cache()
+    if "prefill" in legs:
+        wp, p = prefill_leg(a, dev)
+        out["workloads"]["prefill"] = {
+            "workload": wp.name,
+            "tokens_per_s": round(p["tok_s"], 1),
+            "ms_per_layer": round(p["ms_layer"], 3),
+            "stage_us": {k: round(v, 1) for k, v in p["us"].items()},
+            "tflops": round(p["tflops_layer"], 1),
+            "mfma_frac_layer": round(p["tflops_layer"] / BF16_PEAK_TFLOPS, 4),
+            "roofline_gate_up": {"bound": "mfma", "achieved": round(p["tflops_gate_up"], 1), "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(p["tflops_gate_up"] / BF16_PEAK_TFLOPS, 4)},
+            "roofline_down": {"bound": "mfma", "achieved": round(p["tflops_down"], 1), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(p["tflops_down"] / BF16_PEAK_TFLOPS, 4)},
+            "useful_flops_per_layer": p["flops"],
+        }
+        torch.cuda.empty_cache()
+    if "batched" in legs:
+        wb, b = batched_leg(a, dev)
+        out["workloads"]["batched"] = {
+            "workload": wb.name,
+            "tokens_per_s_per_layer": round(b["tok_s"], 1),
+            "us_per_layer": round(b["us_layer"], 2),
+            "distinct_experts_per_layer": round(b["distinct_experts"], 2),
+            "hbm_gbs": round(b["hbm_gbs"], 1),
+            "hbm_frac": round(b["hbm_gbs"] / HBM_PEAK_GBS, 4),
+        }
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, min(a.cpu_layers, w.layers))

@@ -132,6 +132,19 @@ int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, in
  * addresses or on which experts are resident, so a paged run gives the same
  * bits as a fully-resident one. */
 size_t moe_ffn_workspace_bytes(int T, int H, int I, int E, int K, int has_shared, unsigned flags);
+/* The two stages of moe_expert_ffn, with the same arguments, for callers that
+ * time or schedule them separately: moe_ffn_gate_up computes h = silu(Wg x) *
+ * (Wu x) of every (token, expert) pair into ws (y is not touched);
+ * moe_ffn_down then applies Wd and the combine and writes y. They must run in
+ * this order on one stream with the same arguments and workspace.
+ * moe_expert_ffn(...) is exactly moe_ffn_gate_up(...) then moe_ffn_down(...). */
+int moe_ffn_gate_up(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K,
+                    int g, const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
+                    uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
+                    moe_stream_t stream);
+int moe_ffn_down(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K, int g,
+                 const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob, uint16_t* y,
+                 void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags, moe_stream_t stream);
 int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K,
                    int g, const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
                    uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,

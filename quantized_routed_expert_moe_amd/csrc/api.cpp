@@ -66,10 +66,14 @@ extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int I, int E, int K, int
   return moe::gemv_workspace_bytes(T, H, I, K, has_shared);
 }
 
-extern "C" int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E,
-                              int K, int g, const int32_t* slot_table, const void* slots, size_t stride,
-                              const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
-                              int32_t* dev_status, unsigned flags, moe_stream_t stream) {
+namespace {
+
+// Shared argument checks and dispatch of one stage (0 = gate/up, 1 = down +
+// combine, 2 = both) of the expert FFN.
+int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K, int g,
+                     const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
+                     uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
+                     moe_stream_t stream, int stage) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
   if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED)) return MOE_EINVAL;
   if ((flags & MOE_FORCE_GEMV) && (flags & MOE_FORCE_GROUPED)) return MOE_EINVAL;
@@ -80,6 +84,7 @@ extern "C" int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float
   if (stride < blob || stride % 256) return MOE_EINVAL;
   const bool grouped = ffn_uses_grouped(T, flags);
   if (!grouped && !gemv_shape_ok(T, H, I, K)) return MOE_EUNSUP;
+  if (grouped && !moe::grouped_shape_ok(H, I)) return MOE_EUNSUP;
   const size_t need = moe_ffn_workspace_bytes(T, H, I, E, K, shared_blob != nullptr, flags);
   if (need == 0) return MOE_EUNSUP;
   if (!ws || ws_bytes < need) return MOE_EWS;
@@ -101,13 +106,44 @@ extern "C" int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float
   a.ws_bytes = ws_bytes;
   a.status = dev_status;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err;
-  if (grouped)
-    err = moe::launch_ffn_grouped(a, s);
-  else if (moe::decode1_supported(T, H, I, K, shared_blob != nullptr))
-    err = moe::launch_ffn_decode1(a, s);
-  else
-    err = moe::launch_ffn_gemv(a, s);
-  if (err == hipErrorNotSupported) return MOE_EUNSUP;
-  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+  const bool dec1 = !grouped && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
+  for (int st = 0; st < 2; ++st) {
+    if (stage != 2 && stage != st) continue;
+    hipError_t err;
+    if (grouped)
+      err = moe::launch_ffn_grouped(a, st, s);
+    else if (dec1)
+      err = moe::launch_ffn_decode1(a, st, s);
+    else
+      err = moe::launch_ffn_gemv(a, st, s);
+    if (err == hipErrorNotSupported) return MOE_EUNSUP;
+    if (err != hipSuccess) return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E,
+                              int K, int g, const int32_t* slot_table, const void* slots, size_t stride,
+                              const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
+                              int32_t* dev_status, unsigned flags, moe_stream_t stream) {
+  return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                          dev_status, flags, stream, 2);
+}
+
+extern "C" int moe_ffn_gate_up(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E,
+                               int K, int g, const int32_t* slot_table, const void* slots, size_t stride,
+                               const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
+                               int32_t* dev_status, unsigned flags, moe_stream_t stream) {
+  return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                          dev_status, flags, stream, 0);
+}
+
+extern "C" int moe_ffn_down(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E,
+                            int K, int g, const int32_t* slot_table, const void* slots, size_t stride,
+                            const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status,
+                            unsigned flags, moe_stream_t stream) {
+  return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                          dev_status, flags, stream, 1);
 }

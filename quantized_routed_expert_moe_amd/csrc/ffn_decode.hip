@@ -359,10 +359,10 @@ bool decode1_supported(int T, int H, int I, int K, bool has_shared) {
   return T == 1 && G <= 4 * 4 * 8 && Gd % 8 == 0 && dec_down_cpl(n_units, Gd) <= 16;
 }
 
-hipError_t launch_ffn_decode1(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
   const bool has_shared = a.shared_blob != nullptr;
   const int n_units = a.K + (has_shared ? 1 : 0);
-  {
+  if (stage == 0) {
     const int G = a.H / kGroup;
     const int GW = (G + kWaves - 1) / kWaves;
     const int gpl = (GW + 3) / 4;
@@ -379,8 +379,7 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, hipStream_t s) {
     else if (gpl <= 4) GU(4);
     else GU(8);
 #undef GU
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
   {
     const int Gd = a.I / kGroup;

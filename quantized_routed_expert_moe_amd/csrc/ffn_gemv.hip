@@ -482,12 +482,12 @@ size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared) {
   return gemv_ws(T, H, I, K, has_shared).bytes;
 }
 
-hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_gemv(const FfnArgs& a, int stage, hipStream_t s) {
   const bool has_shared = a.shared_blob != nullptr;
   const int max_units = (a.T == 1 ? a.K : (a.T * a.K < a.E ? a.T * a.K : a.E)) + (has_shared ? 1 : 0);
   const int tbc = a.T == 1 ? 1 : kTB;  // tokens per chunk: a single token needs no chunk registers
   // gate/up
-  {
+  if (stage == 0) {
     const int G = a.H / kGroup;
     const int gps = pow2_at_least((G + kSlicesGU - 1) / kSlicesGU);
     const size_t lds = align256(sizeof(GuLds)) + (size_t)kTB * a.H * 2 + (size_t)kTB * G * 4;
@@ -508,8 +508,7 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s) {
       default:
         return hipErrorInvalidValue;
     }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
   // down + combine
   {

@@ -383,15 +383,17 @@ size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared
   return grouped_ws(T, H, I, E, K, has_shared).bytes;
 }
 
-hipError_t launch_ffn_grouped(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   if (!grouped_shape_ok(a.H, a.I)) return hipErrorNotSupported;
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
-  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(W.max_mt * (a.I / 64)), dim3(kGThreads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e;
+  if (stage == 0) {
+    hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(W.max_mt * (a.I / 64)), dim3(kGThreads), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(W.max_mt * (a.H / kBN)), dim3(kGThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t n4 = (size_t)a.T * a.H / 4;

@@ -67,16 +67,18 @@ struct FfnArgs {
   int32_t* status;
 };
 
+// Each path launches in two stages: stage 0 = gate/up (h into the workspace),
+// stage 1 = down + combine (y).
 size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared);
-hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_gemv(const FfnArgs& a, int stage, hipStream_t s);
 
 // single-token decode kernels (a specialisation of the GEMV path)
 bool decode1_supported(int T, int H, int I, int K, bool has_shared);
-hipError_t launch_ffn_decode1(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s);
 
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
 bool grouped_shape_ok(int H, int I);
-hipError_t launch_ffn_grouped(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s);
 
 hipError_t launch_table_update(int32_t* table, const int32_t* idx, const int32_t* val, int n, hipStream_t s);
 

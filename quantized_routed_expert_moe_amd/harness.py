@@ -115,11 +115,12 @@ class LayerRunner:
         lib.moe_route(L.x, L.wr, L.logits, w.T, w.H, w.E, w.K, lib.MOE_ROUTE_RENORM if renorm else 0, self.ids,
                       self.wts, stream)
 
-    def ffn(self, L: DeviceLayer, stream=None, y=None):
+    def ffn(self, L: DeviceLayer, stream=None, y=None, stage="both"):
+        """Expert FFN of the layer: stage "both", "gate_up" or "down"."""
         w = self.w
-        lib.moe_expert_ffn(L.x, self.ids, self.wts, w.T, w.H, w.I, w.E, w.K, w.g, L.table, L.slots, L.stride,
-                           L.shared, self.y if y is None else y, self.ws, self.ws_bytes, self.status, self.flags,
-                           stream)
+        fn = {"both": lib.moe_expert_ffn, "gate_up": lib.moe_ffn_gate_up, "down": lib.moe_ffn_down}[stage]
+        fn(L.x, self.ids, self.wts, w.T, w.H, w.I, w.E, w.K, w.g, L.table, L.slots, L.stride, L.shared,
+           self.y if y is None else y, self.ws, self.ws_bytes, self.status, self.flags, stream)
 
     def __call__(self, L: DeviceLayer, stream=None):
         self.route(L, stream)

@@ -31,6 +31,8 @@ EXPORTS = (
     "moe_route",
     "moe_ffn_workspace_bytes",
     "moe_expert_ffn",
+    "moe_ffn_gate_up",
+    "moe_ffn_down",
     "arena_create",
     "arena_map_slots",
     "arena_fill_async",
@@ -80,6 +82,14 @@ def load(path: str | None = None):
         "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P]),
         "moe_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, ctypes.c_uint]),
         "moe_expert_ffn": (
+            _I,
+            [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P, _P, _SZ, _P, ctypes.c_uint, _P],
+        ),
+        "moe_ffn_gate_up": (
+            _I,
+            [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P, _P, _SZ, _P, ctypes.c_uint, _P],
+        ),
+        "moe_ffn_down": (
             _I,
             [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P, _P, _SZ, _P, ctypes.c_uint, _P],
         ),
@@ -171,15 +181,33 @@ def moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, flags=0) -> int:
     return load().moe_ffn_workspace_bytes(T, H, I, E, K, int(bool(has_shared)), flags)
 
 
-def moe_expert_ffn(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
-                   dev_status, flags=0, stream=None) -> None:
+def _ffn_call(name, x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+              dev_status, flags, stream):
     _check(
-        load().moe_expert_ffn(
+        getattr(load(), name)(
             _ptr(x), _ptr(ids), _ptr(w), T, H, I, E, K, g, _ptr(slot_table), _ptr(slots), stride,
             _ptr(shared_blob), _ptr(y), _ptr(ws), ws_bytes, _ptr(dev_status), flags, _stream(stream),
         ),
-        "moe_expert_ffn",
+        name,
     )
+
+
+def moe_expert_ffn(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                   dev_status, flags=0, stream=None) -> None:
+    _ffn_call("moe_expert_ffn", x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws,
+              ws_bytes, dev_status, flags, stream)
+
+
+def moe_ffn_gate_up(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                    dev_status, flags=0, stream=None) -> None:
+    _ffn_call("moe_ffn_gate_up", x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws,
+              ws_bytes, dev_status, flags, stream)
+
+
+def moe_ffn_down(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                 dev_status, flags=0, stream=None) -> None:
+    _ffn_call("moe_ffn_down", x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws,
+              ws_bytes, dev_status, flags, stream)
 
 
 class Arena:
