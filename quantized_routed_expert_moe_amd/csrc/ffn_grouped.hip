@@ -10,20 +10,26 @@
 //      unit's blob address, and the scatter of pair indices into segments.
 //      The order of pairs inside a segment does not matter: every output row
 //      of an MFMA tile depends on its own A row only.
-//   2. gate/up GEMM: tile = 128 pair rows x (64 gate + 64 up) weight rows,
-//      K = H in steps of 64. A rows are gathered from x; B holds the int4 codes
-//      q themselves, exact in bf16; both are staged in LDS and double
-//      buffered. Each 32-wide K step is one quantisation group: one
-//      v_mfma_f32_16x16x32_bf16 per 16x16 block gives the exact partial
-//      sum_k x q in fp32, which is multiplied by the group's fp16 scale and
-//      added to the fp32 accumulator. No rounding of the weights at all. The
-//      tile's columns interleave gate and up in blocks of 16, so each lane
-//      holds matching g and u and writes h = silu(g) * u as bf16 (the A
-//      operand of the next GEMM).
-//   3. down GEMM: A = h rows, B = down codes, same group scaling; o is written
-//      in fp32 at the pair's own index.
-//   4. combine: y[t] = o_shared[t] + sum_k w[t][k] * o[t][k] in rank order,
+//   2. convert: x (bf16) -> fp16 in the workspace. bf16 carries 8 significant
+//      bits, so every |x| in [2^-17, 65504] converts exactly; smaller values
+//      round to the fp16 subnormal grid (absolute error <= 2^-25), and a
+//      value that would overflow fp16 sets MOE_EUNSUP in the status word
+//      rather than being clamped.
+//   3. gate/up GEMM: tile = 128 pair rows x (64 gate + 64 up) weight rows,
+//      K = H in steps of 64 (two quantisation groups). A rows are gathered
+//      from the fp16 x; B = fp16(q * s) is formed in registers from the int4
+//      codes with packed fp16 arithmetic (q exact, one rounding of the
+//      product: relative error <= 2^-12) and staged in LDS; both double
+//      buffered. v_mfma_f32_16x16x32_f16 with fp32 accumulation. The tile's
+//      columns interleave gate and up in blocks of 16, so each lane holds
+//      matching g and u and writes h = silu(g) * u in fp16 (the next A
+//      operand; overflow sets the status word).
+//   4. down GEMM: A = h rows, B = fp16(q * s) of the down matrix; o is
+//      written in fp32 at the pair's own index.
+//   5. combine: y[t] = o_shared[t] + sum_k w[t][k] * o[t][k] in rank order,
 //      fp32, rounded once to bf16.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -34,7 +40,8 @@ constexpr int kGThreads = 256;
 constexpr int kRowE = kBK + 8;  // LDS row length in bf16 (16 bytes of padding)
 constexpr int kPlanThreads = 1024;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct TileDesc {
@@ -42,7 +49,7 @@ struct TileDesc {
 };
 
 struct GroupedWs {
-  size_t n_mt, tiles, ublob, sorted, h, o, bytes;
+  size_t n_mt, tiles, ublob, unit_mt0, sorted, xh, h, o, bytes;
   int max_units, max_mt;
 };
 
@@ -54,11 +61,13 @@ __host__ __device__ inline GroupedWs grouped_ws(int T, int H, int I, int E, int 
   const size_t PA = P + (has_shared ? T : 0);
   w.max_units = (int)((P < (size_t)E ? P : (size_t)E) + (has_shared ? 1 : 0));
   w.max_mt = (int)((PA + kBM - 1) / kBM) + w.max_units;
-  w.n_mt = 0;
+  w.n_mt = 0;  // int n_mt, int n_units
   w.tiles = al256(w.n_mt + 16);
   w.ublob = al256(w.tiles + (size_t)w.max_mt * sizeof(TileDesc));
-  w.sorted = al256(w.ublob + (size_t)w.max_units * sizeof(void*));
-  w.h = al256(w.sorted + PA * sizeof(int32_t));
+  w.unit_mt0 = al256(w.ublob + (size_t)w.max_units * sizeof(void*));
+  w.sorted = al256(w.unit_mt0 + ((size_t)w.max_units + 1) * sizeof(int32_t));
+  w.xh = al256(w.sorted + PA * sizeof(int32_t));
+  w.h = al256(w.xh + (size_t)T * H * 2);
   w.o = al256(w.h + PA * (size_t)I * 2);
   w.bytes = al256(w.o + PA * (size_t)H * 4);
   return w;
@@ -103,6 +112,7 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
   int* n_mt = reinterpret_cast<int*>(a.ws + W.n_mt);
   TileDesc* tiles = reinterpret_cast<TileDesc*>(a.ws + W.tiles);
   const uint8_t** ublob = reinterpret_cast<const uint8_t**>(a.ws + W.ublob);
+  int32_t* unit_mt0 = reinterpret_cast<int32_t*>(a.ws + W.unit_mt0);
   int32_t* sorted = reinterpret_cast<int32_t*>(a.ws + W.sorted);
   const int tid = threadIdx.x;
   const int P = T * K;
@@ -133,6 +143,7 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
       const int slot = a.slot_table[tid];
       if (slot < 0) *a.status = MOE_ENOTRES;
       ublob[uidx] = slot < 0 ? nullptr : a.slots + (size_t)slot * a.stride;
+      unit_mt0[uidx] = shared_mt + mt0;
       for (int m = 0; m < mt_here; ++m) {
         const int rows = c - m * kBM < kBM ? c - m * kBM : kBM;
         tiles[shared_mt + mt0 + m] = TileDesc{uidx, row0 + m * kBM, rows, 0};
@@ -140,15 +151,21 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
     }
   }
   if (has_shared) {
-    if (tid == 0) ublob[0] = a.shared_blob;
+    if (tid == 0) {
+      ublob[0] = a.shared_blob;
+      unit_mt0[0] = 0;
+    }
     for (int m = tid; m < shared_mt; m += kPlanThreads) {
       const int rows = T - m * kBM < kBM ? T - m * kBM : kBM;
       tiles[m] = TileDesc{0, m * kBM, rows, 0};
     }
     for (int t = tid; t < T; t += kPlanThreads) sorted[t] = P + t;
   }
-  if (tid == 0) *n_mt = shared_mt + total;
-  (void)n_units;
+  if (tid == 0) {
+    n_mt[0] = shared_mt + total;
+    n_mt[1] = n_units;
+    unit_mt0[n_units] = shared_mt + total;
+  }
   __syncthreads();
   for (int p = tid; p < P; p += kPlanThreads) {
     const int e = a.ids[p];
@@ -161,45 +178,82 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-// 32 codes of one (row, group) -> the 32 integer codes q = u - 8 as bf16 (exact),
-// in column order.
-__device__ inline void codes_to_bf16(uint4 codes, uint32_t out[16]) {
+// 32 codes of one (row, group) times the group's scale -> 32 fp16 values of
+// fp16(q * s), column order. Nibble pair p of a code dword (bits 4p and 4p+16)
+// holds columns 2p and 2p+1; OR-ing it under the fp16 pattern 0x6400 gives
+// 1024 + u exactly, one packed add of -1032 gives q, one packed multiply by s
+// rounds q * s once to nearest even.
+__device__ inline void dequant_f16(uint4 codes, _Float16 sc, uint32_t out[16]) {
   const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+  const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 s2 = {sc, sc};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = cw[d] & 0x0F0F0F0Fu;
-    const uint32_t hi = (cw[d] >> 4) & 0x0F0F0F0Fu;
-    // columns 8d + {0..7}: lo.b0, lo.b2, hi.b0, hi.b2, lo.b1, lo.b3, hi.b1, hi.b3
-    const float v0 = (float)(lo & 0xFF) - 8.0f;
-    const float v1 = (float)((lo >> 16) & 0xFF) - 8.0f;
-    const float v2 = (float)(hi & 0xFF) - 8.0f;
-    const float v3 = (float)((hi >> 16) & 0xFF) - 8.0f;
-    const float v4 = (float)((lo >> 8) & 0xFF) - 8.0f;
-    const float v5 = (float)(lo >> 24) - 8.0f;
-    const float v6 = (float)((hi >> 8) & 0xFF) - 8.0f;
-    const float v7 = (float)(hi >> 24) - 8.0f;
-    out[4 * d + 0] = pack_bf16x2(v0, v1);
-    out[4 * d + 1] = pack_bf16x2(v2, v3);
-    out[4 * d + 2] = pack_bf16x2(v4, v5);
-    out[4 * d + 3] = pack_bf16x2(v6, v7);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t m = ((cw[d] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
+      const f16x2 q = __builtin_bit_cast(f16x2, m) + off;
+      out[4 * d + p] = __builtin_bit_cast(uint32_t, q * s2);
+    }
   }
+}
+
+__global__ void __launch_bounds__(256) to_f16_kernel(FfnArgs a) {
+  const bool has_shared = a.shared_blob != nullptr;
+  const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
+  uint32_t* xh = reinterpret_cast<uint32_t*>(a.ws + W.xh);
+  const size_t n2 = (size_t)a.T * a.H / 2;
+  const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.x);
+  bool bad = false;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n2; i += (size_t)gridDim.x * 256) {
+    const uint32_t v = xb[i];
+    const float lo = __uint_as_float(v << 16), hi = __uint_as_float(v & 0xFFFF0000u);
+    bad |= !(fabsf(lo) < 65520.0f) || !(fabsf(hi) < 65520.0f);
+    const f16x2 h = {(_Float16)lo, (_Float16)hi};
+    xh[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  if (bad) *a.status = MOE_EUNSUP;
 }
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // MODE 0: gate/up with SwiGLU epilogue (writes h in segment order).
 // MODE 1: down (writes o at the pair's index).
+//
+// Block -> tile: the n_mt * n_nt tiles are ordered (unit, N-tile, M-tile) and
+// cut into 8 contiguous ranges, one per XCD (blocks are dispatched to XCDs
+// round-robin by block id), so the M-tiles of one unit that share a weight
+// N-tile run back to back on one XCD and meet its weight bytes in that XCD's
+// L2. Global loads run two K-stages ahead of the MFMAs (two register sets),
+// and LDS is double buffered, so one barrier per stage.
 template <int MODE>
-__global__ void __launch_bounds__(kGThreads) grouped_gemm_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   __shared__ __align__(16) uint16_t As[2][kBM][kRowE];
   __shared__ __align__(16) uint16_t Bs[2][kBN][kRowE];
-  __shared__ float Ss[2][kBK / kGroup][kBN];
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(T, H, I, a.E, K, has_shared);
   const int n_nt = MODE == 0 ? I / 64 : H / kBN;
-  const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
-  if (mt >= *reinterpret_cast<const int*>(a.ws + W.n_mt)) return;
+  const int* cnts = reinterpret_cast<const int*>(a.ws + W.n_mt);
+  const int n_mt = cnts[0], n_units = cnts[1];
+  const int N = n_mt * n_nt;
+  const int chunk = (N + 7) / 8;
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  if (jx >= chunk) return;
+  const int t = xcd * chunk + jx;
+  if (t >= N) return;
+  const int32_t* unit_mt0 = reinterpret_cast<const int32_t*>(a.ws + W.unit_mt0);
+  int lo = 0, hi = n_units - 1;  // last unit whose first tile index <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (unit_mt0[mid] * n_nt <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int m_first = unit_mt0[lo], m_cnt = unit_mt0[lo + 1] - m_first;
+  const int rr = t - m_first * n_nt;
+  const int nt = rr / m_cnt, mt = m_first + rr % m_cnt;
   const TileDesc td = reinterpret_cast<const TileDesc*>(a.ws + W.tiles)[mt];
   const uint8_t* blob = reinterpret_cast<const uint8_t* const*>(a.ws + W.ublob)[td.unit];
   const int32_t* sorted = reinterpret_cast<const int32_t*>(a.ws + W.sorted);
@@ -213,20 +267,20 @@ __global__ void __launch_bounds__(kGThreads) grouped_gemm_kernel(FfnArgs a) {
   const int Nmat = MODE == 0 ? I : H;  // rows of the weight matrix
   const BlobLayout BL = blob_layout(H, I);
 
-  // A loader: thread -> (row ar, 32-element half ah)
+  // A loader: thread -> (row ar, 32-element half ah) of the 128 x 64 stage
   const int ar = tid >> 1, ah = tid & 1;
   const bool a_ok = ar < td.rows && blob != nullptr;
   const uint16_t* a_src = nullptr;
   if (a_ok) {
     if (MODE == 0) {
       const int p = sorted[td.row0 + ar];
-      const int t = p < P ? p / K : p - P;
-      a_src = a.x + (size_t)t * H;
+      const int tok = p < P ? p / K : p - P;
+      a_src = reinterpret_cast<const uint16_t*>(a.ws + W.xh) + (size_t)tok * H + 32 * ah;
     } else {
-      a_src = hws + (size_t)(td.row0 + ar) * I;
+      a_src = hws + (size_t)(td.row0 + ar) * I + 32 * ah;
     }
   }
-  // B loader: thread -> (tile column bc, group-in-stage bg)
+  // B loader: thread -> (tile column bc, group bg of the stage's two)
   const int bc = tid & (kBN - 1), bg = tid >> 7;
   int brow;  // weight row
   size_t bcodes, bscales;
@@ -240,34 +294,38 @@ __global__ void __launch_bounds__(kGThreads) grouped_gemm_kernel(FfnArgs a) {
     bcodes = BL.down_codes;
     bscales = BL.down_scales;
   }
+  const uint8_t* bsrc = blob ? blob + bcodes + (size_t)brow * 16 : nullptr;
+  const uint8_t* ssrc =
+      blob ? blob + bscales + ((size_t)(brow / kScaleBlock) * G * kScaleBlock + brow % kScaleBlock) * 2 : nullptr;
 
-  uint4 ra[4];
-  uint4 rb;
-  _Float16 rs;
-  auto gload = [&](int k0) {
+  uint4 ra[2][4];
+  uint4 rb[2];
+  _Float16 rs[2];
+  auto gload = [&](auto SET, int st) {
+    constexpr int q = decltype(SET)::value;
+    const int k0 = st * kBK;
     if (a_ok) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ra[v] = reinterpret_cast<const uint4*>(a_src + k0 + 32 * ah)[v];
+      for (int v = 0; v < 4; ++v) ra[q][v] = reinterpret_cast<const uint4*>(a_src + k0)[v];
     } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ra[v] = make_uint4(0u, 0u, 0u, 0u);
+      for (int v = 0; v < 4; ++v) ra[q][v] = make_uint4(0u, 0u, 0u, 0u);
     }
     if (blob) {
       const int j = k0 / kGroup + bg;
-      rb = *reinterpret_cast<const uint4*>(blob + bcodes + ((size_t)j * Nmat + brow) * 16);
-      rs = *reinterpret_cast<const _Float16*>(
-          blob + bscales + (((size_t)(brow / kScaleBlock) * G + j) * kScaleBlock + brow % kScaleBlock) * 2);
+      rb[q] = *reinterpret_cast<const uint4*>(bsrc + (size_t)j * Nmat * 16);
+      rs[q] = *reinterpret_cast<const _Float16*>(ssrc + (size_t)j * kScaleBlock * 2);
     } else {
-      rb = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-      rs = (_Float16)0.0f;
+      rb[q] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+      rs[q] = (_Float16)0.0f;
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](auto SET, int buf) {
+    constexpr int q = decltype(SET)::value;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) reinterpret_cast<uint4*>(&As[buf][ar][32 * ah])[v] = ra[v];
+    for (int v = 0; v < 4; ++v) reinterpret_cast<uint4*>(&As[buf][ar][32 * ah])[v] = ra[q][v];
     uint32_t deq[16];
-    codes_to_bf16(rb, deq);
-    Ss[buf][bg][bc] = (float)rs;
+    dequant_f16(rb[q], rs[q], deq);
 #pragma unroll
     for (int v = 0; v < 4; ++v)
       reinterpret_cast<uint4*>(&Bs[buf][bc][32 * bg])[v] = make_uint4(deq[4 * v], deq[4 * v + 1], deq[4 * v + 2], deq[4 * v + 3]);
@@ -279,38 +337,41 @@ __global__ void __launch_bounds__(kGThreads) grouped_gemm_kernel(FfnArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int n_st = Kd / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int st = 0; st < n_st; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < n_st) gload((st + 1) * kBK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
-      bf16x8 fa[4], fb[4];
       const int kk = ks * 32 + 8 * (lane >> 4);
+      f16x8 fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * 64 + i * 16 + (lane & 15)][kk]);
+      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const f16x8*>(&As[buf][wm * 64 + i * 16 + (lane & 15)][kk]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * 64 + j * 16 + (lane & 15)][kk]);
-      float sc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[j] = Ss[buf][ks][wn * 64 + j * 16 + (lane & 15)];
+      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const f16x8*>(&Bs[buf][wn * 64 + j * 16 + (lane & 15)][kk]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // exact group partial sum_k a q, then the group's scale in fp32
-          const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(sc[j], part[v], acc[i][j][v]);
-        }
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (st + 1 < n_st) sstore(buf ^ 1);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int n_st = Kd / kBK;
+  gload(S0{}, 0);
+  if (n_st > 1) gload(S1{}, 1);
+  sstore(S0{}, 0);
+  __syncthreads();
+  // stage st lives in register set st % 2 and LDS buffer st % 2
+  for (int st = 0; st < n_st; st += 2) {
+    if (st + 2 < n_st) gload(S0{}, st + 2);
+    compute(0);
+    if (st + 1 < n_st) sstore(S1{}, 1);
     __syncthreads();
+    if (st + 1 < n_st) {
+      if (st + 3 < n_st) gload(S1{}, st + 3);
+      compute(1);
+      if (st + 2 < n_st) sstore(S0{}, 0);
+      __syncthreads();
+    }
   }
 
   // epilogue: lane holds D[row = 4*(lane/16) + v][col = lane%16] of each 16x16 block
@@ -326,7 +387,8 @@ __global__ void __launch_bounds__(kGThreads) grouped_gemm_kernel(FfnArgs a) {
           if (row < td.rows) {
             const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
             const float hv = blob ? silu(g) * u : 0.0f;
-            hws[(size_t)(td.row0 + row) * I + col_i] = __builtin_bit_cast(uint16_t, (__bf16)hv);
+            if (!(fabsf(hv) < 65520.0f)) *a.status = MOE_EUNSUP;  // h does not fit the fp16 operand
+            hws[(size_t)(td.row0 + row) * I + col_i] = __builtin_bit_cast(uint16_t, (_Float16)hv);
           }
         }
       }
@@ -375,6 +437,8 @@ __global__ void __launch_bounds__(256) grouped_combine_kernel(FfnArgs a) {
   }
 }
 
+inline int round8(int v) { return (v + 7) / 8 * 8; }
+
 }  // namespace
 
 bool grouped_shape_ok(int H, int I) { return H % kBN == 0 && I % 64 == 0 && H % kBK == 0; }
@@ -391,10 +455,14 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   if (stage == 0) {
     hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(W.max_mt * (a.I / 64)), dim3(kGThreads), 0, s, a);
+    const size_t n2 = (size_t)a.T * a.H / 2;
+    const size_t cb = (n2 + 255) / 256;
+    hipLaunchKernelGGL(to_f16_kernel, dim3(cb < 4096 ? (int)cb : 4096), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(round8(W.max_mt * (a.I / 64))), dim3(kGThreads), 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(W.max_mt * (a.H / kBN)), dim3(kGThreads), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(round8(W.max_mt * (a.H / kBN))), dim3(kGThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t n4 = (size_t)a.T * a.H / 4;
   const size_t blocks = (n4 + 255) / 256;
