@@ -36,7 +36,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=48)
-    p.add_argument("--legs", default="decode,prefill,batched", help="comma list of decode,prefill,batched")
+    p.add_argument("--legs", default="decode,prefill,batched,paged",
+                   help="comma list of decode,prefill,batched,paged")
+    p.add_argument("--paged-steps", type=int, default=64, help="measured tokens of the paged decode workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=3, help="decode layers in the oracle's timed sample")
     p.add_argument("--graph", type=int, default=1, help="replay the decode layer stack as a HIP graph")
@@ -290,6 +292,118 @@ def batched_leg(a, dev, n_sets=16):
     }
 
 
+# ------------------------------------------------------------------ paged decode
+
+
+def paged_leg(a, dev):
+    """Paged single-token decode through 43 layers with 64-slot arenas filled from pinned host memory.
+
+    Every layer's arena draws its misses from one pinned, expert-major host copy
+    of 256 experts (one weight set shared by the layers, so the host copy fits in
+    3.6 GB; arena keys stay per layer, so every miss is a real 14 MB copy). Per
+    layer and token: moe_route on logits with temporal locality, the ids come
+    back to the host (the hand-shake), arena_map_slots, arena_fill_async on a
+    side stream, the compute stream waits on its event, then moe_expert_ffn
+    (six routed experts plus the shared expert).
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    from quantized_routed_expert_moe_amd import harness, lib
+    from synth import gen
+
+    w = gen.WORKLOADS["paged_t1_h4096_e256s1_k6_i2048_x43"]
+    warm = 16
+    steps = warm + a.paged_steps
+    stride = lib.moe_slot_stride(w.H, w.I)
+    blob = lib.moe_blob_bytes(w.H, w.I)
+    log(f"paged: packing {w.E} experts into pinned host memory ({w.E * stride / 2**30:.1f} GiB)")
+    t0 = time.time()
+    host = torch.empty(w.E * stride, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy()
+
+    def put(e):
+        hv[e * stride : (e + 1) * stride] = harness.pack_expert(w.seed, 0, e, w.H, w.I)
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(put, range(w.E)))
+    shared = torch.from_numpy(harness.pack_expert(w.seed, 0, gen.SHARED_EXPERT, w.H, w.I)).to(dev)
+    resident = host.to(dev)  # all 256 experts, identity slot map: the fully-resident comparison
+    resident_table = torch.arange(w.E, dtype=torch.int32, device=dev)
+    log(f"  paged: packed ({time.time() - t0:.1f} s)")
+    lg = torch.from_numpy(gen.locality_logits(w.seed, w.layers, steps, w.E, w.K)).to(dev)  # [steps, layers, E]
+    xs = [harness.bf16_tensor(gen.activations_bf16(w.seed, l, 1, w.H), dev) for l in range(w.layers)]
+    layers = []
+    for l in range(w.layers):
+        sl = torch.empty(w.slots * stride, dtype=torch.uint8, device=dev)
+        tb = torch.full((w.E,), -1, dtype=torch.int32, device=dev)
+        layers.append((sl, tb, lib.Arena(w.E, w.slots, blob, stride, sl, tb, host)))
+    run = harness.LayerRunner(w, dev)
+    comp = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    done.record(side)
+    ids_h = torch.empty(w.K, dtype=torch.int32, pin_memory=True)
+    y_res = torch.empty_like(run.y)
+
+    def layer_step(s, l, check=False):
+        sl, tb, ar = layers[l]
+        lib.moe_route(None, None, lg[s, l], 1, 0, w.E, w.K, 0, run.ids, run.wts)
+        ids_h.copy_(run.ids.view(-1), non_blocking=True)
+        comp.synchronize()  # hand-shake: the router's choice on the host
+        ar.map_slots(ids_h.tolist())
+        ar.fill_async(side, done)
+        comp.wait_event(done)
+        lib.moe_expert_ffn(xs[l], run.ids, run.wts, 1, w.H, w.I, w.E, w.K, 32, tb, sl, stride, shared, run.y,
+                           run.ws, run.ws_bytes, run.status)
+        if check:
+            lib.moe_expert_ffn(xs[l], run.ids, run.wts, 1, w.H, w.I, w.E, w.K, 32, resident_table, resident,
+                               stride, shared, y_res, run.ws, run.ws_bytes, run.status)
+            torch.cuda.synchronize()
+            return torch.equal(run.y.view(torch.int16), y_res.view(torch.int16))
+        return True
+
+    for s in range(warm):
+        for l in range(w.layers):
+            layer_step(s, l)
+    torch.cuda.synchronize()
+    st0 = [ar.stats() for _, _, ar in layers]
+    t0 = time.perf_counter()
+    for s in range(warm, steps):
+        for l in range(w.layers):
+            layer_step(s, l)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st1 = [ar.stats() for _, _, ar in layers]
+    if int(run.status.item()) != 0:
+        raise RuntimeError(f"device status {int(run.status.item())}")
+    d = {k: sum(b[k] - a_[k] for a_, b in zip(st0, st1)) for k in st0[0]}
+    # fidelity: one more token, every layer's paged output against the fully-resident one
+    identical = all(layer_step(steps - 1, l, check=True) for l in range(w.layers))
+    # pinned host -> device copy rate for context
+    probe_dev = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    probe_host = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(3):
+        probe_dev.copy_(probe_host, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d_peak = 3 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    n_tok = steps - warm
+    return w, {
+        "tok_s": n_tok / dt,
+        "ms_per_token": dt * 1e3 / n_tok,
+        "hit_rate": d["hits"] / max(1, d["hits"] + d["misses"]),
+        "misses_per_layer_step": d["misses"] / (n_tok * w.layers),
+        "h2d_gbs": d["h2d_bytes"] / dt / 1e9,
+        "h2d_peak_gbs": h2d_peak,
+        "identical": identical,
+    }
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 
@@ -429,6 +543,20 @@ def main():
             "distinct_experts_per_layer": round(b["distinct_experts"], 2),
             "hbm_gbs": round(b["hbm_gbs"], 1),
             "hbm_frac": round(b["hbm_gbs"] / HBM_PEAK_GBS, 4),
+        }
+    if "paged" in legs:
+        torch.cuda.empty_cache()
+        wq, q = paged_leg(a, dev)
+        out["workloads"]["paged"] = {
+            "workload": wq.name,
+            "tokens_per_s": round(q["tok_s"], 2),
+            "ms_per_token": round(q["ms_per_token"], 3),
+            "hit_rate": round(q["hit_rate"], 4),
+            "misses_per_layer_step": round(q["misses_per_layer_step"], 3),
+            "h2d_gbs": round(q["h2d_gbs"], 2),
+            "h2d_pinned_copy_gbs": round(q["h2d_peak_gbs"], 2),
+            "bit_identical_to_resident": q["identical"],
+            "host_weight_sets": 1,
         }
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
