@@ -2,25 +2,44 @@
 //
 // One token routes to K experts (plus an optional always-on shared expert);
 // the layer streams K (+1) int4 expert blobs once ("Strata" README, Models:
-// 4-bit grouped integer experts run W4A16). Two kernels, each built so that no
-// workgroup barrier stands between issuing the weight loads and using them (a
-// barrier waits for every outstanding load): every wave stages the slice of
-// x or h it needs into its own LDS region, and the only barrier comes after
-// the last weight byte has been consumed.
+// 4-bit grouped integer experts run W4A16). Two kernels, both shaped for
+// streaming: many small workgroups (each reads 24-36 KB of codes, about six
+// workgroups per CU), every weight load of a wave issued up front in the
+// order the steps consume them, and straight-line code between loads and
+// use, so each step waits only for its own loads while later ones are still
+// in flight. No workgroup barrier stands between the loads and their use (a
+// barrier waits for every outstanding load): each wave stages the slice of x
+// or h it needs in its own LDS region.
 //
-// dec_gateup: work item = (unit, 16 rows of I); wave w owns the contiguous
-//   quarter of the groups [w*GW, (w+1)*GW). Lane (row r, phase p) reads groups
-//   w*GW + 4i + p of its row in gate and up. Codes become bf16 pairs (16 + u,
-//   u = q + 8 the stored nibble, exact in bf16) reduced against x with v_dot2;
-//   sum_c q_c x_c = D - 24 * sum_c x_c per group, times the group's fp16 scale.
-//   Phases then waves are summed in a fixed order; h = silu(g) * u in fp32.
-// dec_down: work item = 8 rows of H for all units at once, so the combine needs
-//   no further kernel. The flattened (unit, group) columns are split into four
-//   contiguous ranges, one per wave; at step i the 8 phases of a wave read
-//   columns 8i .. 8i+7 of its range, which belong to one unit (groups per unit
-//   are a multiple of 8). P = sum_c u_c h_c in fp32, sum_c q_c h_c = P - 8 *
-//   sum_c h_c. Per-unit sums go over phases, then waves, in a fixed order, and
+// Arithmetic (both kernels). Activations become fp16 pairs; a code dword w
+// (8 offset-binary nibbles u = q + 8, see the blob layout) gives four fp16
+// pairs with one AND-OR each (two also need w >> 8):
+//   A pairs (nibbles at bits 0..3 / 16..19 of w or w >> 8): 0x6400 | u = 1024 + u = q + 1032
+//   B pairs (nibbles at bits 4..7 / 20..23):                 0x5400 | 16u = 64 + u = q + 72
+// all exact. v_dot2_f32_f16 multiplies them with the activation pairs of the
+// same columns (A pairs cover columns 8d + {0,1,4,5} of dword d, B pairs
+// 8d + {2,3,6,7}) and accumulates in fp32, so per group
+//   sum_c q_c a_c = D - (1032 * A_sum + 72 * B_sum)
+// with A_sum / B_sum the sums of the fp16 activations over those columns,
+// computed once per group when the activations are staged. The group's fp16
+// scale multiplies that in fp32. Activations that do not fit fp16 (|v| >=
+// 65520) set MOE_EUNSUP in the status word; bf16 x converts exactly for
+// |x| in [2^-17, 65504].
+//
+// dec_gateup: one workgroup per (unit, 8 rows of I); wave w owns the
+//   contiguous quarter of the groups [w*GW, (w+1)*GW). Lane (row r of 8,
+//   phase p of 8) takes groups w*GW + 8i + p of its row in gate and up: per
+//   step a wave reads eight 128-byte lines per matrix. Phases then waves are
+//   summed in a fixed order; h = silu(g) * u is stored as fp16.
+// dec_down: one workgroup per 4 rows of H for all units at once, so the
+//   combine needs no further kernel. The flattened (unit, group) columns are
+//   split into four contiguous ranges, one per wave; at step i lane (row r of
+//   4, phase p of 16) takes column 16i + p of its wave's range; the 16
+//   columns of a step belong to one unit (groups per unit are a multiple of
+//   16). Per-unit sums go over phases, then waves, in a fixed order, and
 //   y = o_shared + sum_k w[k] * o_k in rank order, rounded once to bf16.
+// Workgroups are dealt to the 8 XCDs in contiguous runs of items, so the
+// workgroups that share a 16-row block of the blob run in one L2.
 // No atomics and no data-dependent reduction order: results depend only on
 // the inputs, never on slot addresses.
 #include "moe_internal.h"
@@ -30,22 +49,54 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr int kXcds = 8;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-__device__ inline uint32_t nib_pair(uint32_t w, int p) {
-  const uint32_t sh = p == 0 ? (w << 3) : (w >> (4 * p - 3));
-  return (sh & 0x00780078u) | 0x41804180u;  // bf16 pair (16 + u_lo, 16 + u_hi)
+__device__ inline float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
-__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+// d + the 8 codes of w times the activation pairs x0..x3 of the same columns.
+__device__ inline float code_dot(uint32_t w, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, float d) {
+  const uint32_t w8 = w >> 8;
+  d = dot2h((w & 0x000F000Fu) | 0x64006400u, x0, d);   // columns +0, +1
+  d = dot2h((w & 0x00F000F0u) | 0x54005400u, x1, d);   // +2, +3
+  d = dot2h((w8 & 0x000F000Fu) | 0x64006400u, x2, d);  // +4, +5
+  d = dot2h((w8 & 0x00F000F0u) | 0x54005400u, x3, d);  // +6, +7
+  return d;
 }
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
-__device__ inline float bf16_sum2(uint32_t v) {
-  return __uint_as_float(v << 16) + __uint_as_float(v & 0xFFFF0000u);
+// Cross-lane sums without the LDS crossbar. Each is a fixed instruction
+// sequence, so the result depends only on the data; lanes may differ in the
+// order of their additions, and callers read the lane they document.
+template <int ROR>  // t + t of the lane ROR places over in its row of 16
+__device__ inline float dpp_add(float t) {
+  return t + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t), 0x120 + ROR, 0xF, 0xF, false));
 }
+template <int X>  // t + t of lane ^ X (X = 1 or 2), same bits on both lanes
+__device__ inline float quad_xor_add(float t) {
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return t + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t), ctrl, 0xF, 0xF, false));
+}
+__device__ inline float sum_rows(float t) {  // t summed over lanes l, l^16, l^32, l^48 (same bits on all four)
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  t = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// fp16 bits of the fp32 value v (round to nearest even); *bad set when it overflows.
+__device__ inline uint32_t to_f16_bits(float v, bool* bad) {
+  const _Float16 h = (_Float16)v;
+  const uint32_t b = __builtin_bit_cast(uint16_t, h);
+  if ((b & 0x7FFFu) == 0x7C00u) *bad = true;
+  return b;
+}
+
+__device__ inline float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
+__device__ inline float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 
 // Blob of unit u (u = 0 is the shared expert when present) or nullptr with the
 // status word set.
@@ -69,272 +120,324 @@ __device__ inline int unit_pair(int u, int K, bool has_shared) {
   return (has_shared && u == 0) ? K : u - (has_shared ? 1 : 0);
 }
 
+// Item of workgroup bid when items are dealt to the XCDs in contiguous runs
+// (workgroups are dispatched to XCD bid % 8).
+__device__ inline int xcd_item(int bid, int n_items) {
+  return n_items % kXcds == 0 ? (bid % kXcds) * (n_items / kXcds) + bid / kXcds : bid;
+}
+
 // ------------------------------------------------------------------ gate/up
-// GPL = groups per lane = ceil(GW / 4) with GW = ceil(G / 4) groups per wave.
+// GPL = groups per lane = ceil(GW / 8) with GW = ceil(G / 4) groups per wave.
 template <int GPL>
 __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
-  // LDS per wave: x slice [GW*16] dwords (bf16 pairs) + group sums [GW]
+  // LDS per wave: x slice as fp16 pairs [GW][16] dwords + group corrections [GW]
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float part[2][kWaves][16];
+  __shared__ float part[2][kWaves][8];
   const int H = a.H, I = a.I, K = a.K;
   const int G = H / kGroup;
   const int GW = (G + kWaves - 1) / kWaves;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, p = lane >> 4;
-  uint32_t* xs = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * (GW * 16 + GW);
-  float* Xs = reinterpret_cast<float*>(xs + GW * 16);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 7, p = lane >> 3;
+  uint32_t* xs = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * (GW * 17);
+  float* Cs = reinterpret_cast<float*>(xs + GW * 16);
   const int j0 = wave * GW;
   const int gw_here = G - j0 < GW ? (G - j0 > 0 ? G - j0 : 0) : GW;  // groups this wave really owns
   const bool has_shared = a.shared_blob != nullptr;
-  const int n_units = K + (has_shared ? 1 : 0);
-  const int n_rb = I / 16;
-  const int n_items = n_units * n_rb;
+  const int n_hb = I / 8;
+  const int item = xcd_item(blockIdx.x, (K + (has_shared ? 1 : 0)) * n_hb);
+  const int u = item / n_hb, hb = item % n_hb;
+  // 1. this wave's slice of x: uint4 q (8 bf16) of the slice = columns 8q .. 8q+7
+  //    (issued before the two dependent loads that find the unit's blob)
+  uint4 xv[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    int q = j0 * 4 + lane * 2 + v;
+    q = q < G * 4 ? q : G * 4 - 1;
+    xv[v] = reinterpret_cast<const uint4*>(a.x)[q];
+  }
+  const uint8_t* blob = dec_unit_blob(a, u, has_shared);
+  const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
-  float* hws = reinterpret_cast<float*>(a.ws);  // h [pair][I]; routed pair k, shared pair K
-  bool staged = false;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int u = item / n_rb, rb = item % n_rb;
-    const uint8_t* blob = dec_unit_blob(a, u, has_shared);
-    const int n = rb * 16 + r;
-    uint4 xv[2];
-    if (!staged) {  // this wave's slice of x: 32 bytes per lane, issued before the weights
+  const int n = hb * 8 + r;
+  // 2. codes and scale dwords of every step, in step order
+  uint4 cg[GPL], cu[GPL];
+  uint32_t sgw[GPL], suw[GPL];
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const int q = lane * 2 + v;  // uint4 index within the slice (8 bf16 each)
-        xv[v] = q < gw_here * 4 ? reinterpret_cast<const uint4*>(a.x + (size_t)j0 * kGroup)[q]
-                                : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < GPL; ++i) {
+    const int jl = 8 * i + p;
+    int j = j0 + (jl < gw_here ? jl : gw_here - 1);
+    j = j < 0 ? 0 : (j < G ? j : G - 1);
+    const size_t co = code_off(n, j, G, kRowBlockGU);  // 8 rows x 8 groups: 1 KB contiguous per wave
+    cg[i] = *reinterpret_cast<const uint4*>(src + BL.gate_codes + co);
+    cu[i] = *reinterpret_cast<const uint4*>(src + BL.up_codes + co);
+    const size_t sd = scale_off(n, j, G, kRowBlockGU) >> 2;  // dword holding the scale
+    sgw[i] = reinterpret_cast<const uint32_t*>(src + BL.gate_scales)[sd];
+    suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before x is used
+  // 3. x -> fp16 pairs, group corrections, into LDS (lanes 2m, 2m+1 hold group m)
+  bool bad = false;
+  {
+    const bool live = lane * 2 < gw_here * 4;
+    uint32_t xh[8];
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const uint32_t d[4] = {xv[v].x, xv[v].y, xv[v].z, xv[v].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t lo = to_f16_bits(__uint_as_float(d[c] << 16), &bad);
+        const uint32_t hi = to_f16_bits(__uint_as_float(d[c] & 0xFFFF0000u), &bad);
+        const uint32_t pr = live ? (lo | (hi << 16)) : 0u;
+        xh[4 * v + c] = pr;
+        const float s2 = f16_lo(pr) + f16_hi(pr);
+        if (c & 1) sb += s2;
+        else sa += s2;
       }
     }
-    uint4 cg[GPL], cu[GPL];
-    _Float16 sgh[GPL], suh[GPL];
-    if (blob) {
-#pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const int jl = 4 * i + p;
-        const int j = j0 + (jl < gw_here ? jl : (gw_here > 0 ? gw_here - 1 : 0));
-        const int jj = j < G ? j : G - 1;
-        const size_t co = ((size_t)jj * I + n) * 16;
-        cg[i] = *reinterpret_cast<const uint4*>(blob + BL.gate_codes + co);
-        cu[i] = *reinterpret_cast<const uint4*>(blob + BL.up_codes + co);
-        const size_t so = (((size_t)(n / kScaleBlock) * G + jj) * kScaleBlock + n % kScaleBlock) * 2;
-        sgh[i] = *reinterpret_cast<const _Float16*>(blob + BL.gate_scales + so);
-        suh[i] = *reinterpret_cast<const _Float16*>(blob + BL.up_scales + so);
-      }
+    bad = bad && live;
+    const float sa_t = quad_xor_add<1>(sa);  // same bits on both lanes of the pair
+    const float sb_t = quad_xor_add<1>(sb);
+    if (lane * 2 < GW * 4) {
+      reinterpret_cast<uint4*>(xs)[lane * 2] = make_uint4(xh[0], xh[1], xh[2], xh[3]);
+      reinterpret_cast<uint4*>(xs)[lane * 2 + 1] = make_uint4(xh[4], xh[5], xh[6], xh[7]);
+      if ((lane & 1) == 0) Cs[lane >> 1] = fmaf(1032.0f, sa_t, 72.0f * sb_t);
     }
-    if (!staged) {
-      // lane pair (2m, 2m+1) holds group m of the slice: its sum in a fixed order
-      float s = 0.0f;
+    __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
+  }
+  // 4. the steps; the LDS operands of step i+1 are read during step i
+  float ag = 0.0f, au = 0.0f;
+  const int sh = (r & 1) * 16;
+  uint4 xn[4];
+  float Cn;
+  {
+    const int jc = p < gw_here ? p : 0;
+    const uint4* xq = reinterpret_cast<const uint4*>(xs + jc * 16);
+    xn[0] = xq[0], xn[1] = xq[1], xn[2] = xq[2], xn[3] = xq[3];
+    Cn = Cs[jc];
+  }
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        s += bf16_sum2(xv[v].x);
-        s += bf16_sum2(xv[v].y);
-        s += bf16_sum2(xv[v].z);
-        s += bf16_sum2(xv[v].w);
-      }
-      const float s_odd = __shfl_xor(s, 1, 64);
-      if (lane * 2 < gw_here * 4) {
-        reinterpret_cast<uint4*>(xs)[lane * 2] = xv[0];
-        reinterpret_cast<uint4*>(xs)[lane * 2 + 1] = xv[1];
-        if ((lane & 1) == 0) Xs[lane >> 1] = s + s_odd;
-      }
-      __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
-      staged = true;
+  for (int i = 0; i < GPL; ++i) {
+    const uint4 x0 = xn[0], x1 = xn[1], x2 = xn[2], x3 = xn[3];
+    const float C = Cn;
+    if (i + 1 < GPL) {
+      const int jl = 8 * (i + 1) + p;
+      const int jc = jl < gw_here ? jl : 0;
+      const uint4* xq = reinterpret_cast<const uint4*>(xs + jc * 16);
+      xn[0] = xq[0], xn[1] = xq[1], xn[2] = xq[2], xn[3] = xq[3];
+      Cn = Cs[jc];
     }
-    float ag = 0.0f, au = 0.0f;
-    if (blob) {
+    const bool ok = blob != nullptr && 8 * i + p < gw_here;
+    float dg = 0.0f, du = 0.0f;
+    dg = code_dot(cg[i].x, x0.x, x0.y, x0.z, x0.w, dg);
+    du = code_dot(cu[i].x, x0.x, x0.y, x0.z, x0.w, du);
+    dg = code_dot(cg[i].y, x1.x, x1.y, x1.z, x1.w, dg);
+    du = code_dot(cu[i].y, x1.x, x1.y, x1.z, x1.w, du);
+    dg = code_dot(cg[i].z, x2.x, x2.y, x2.z, x2.w, dg);
+    du = code_dot(cu[i].z, x2.x, x2.y, x2.z, x2.w, du);
+    dg = code_dot(cg[i].w, x3.x, x3.y, x3.z, x3.w, dg);
+    du = code_dot(cu[i].w, x3.x, x3.y, x3.z, x3.w, du);
+    const float sg = ok ? f16_lo(sgw[i] >> sh) : 0.0f;
+    const float su = ok ? f16_lo(suw[i] >> sh) : 0.0f;
+    ag = fmaf(sg, dg - C, ag);
+    au = fmaf(su, du - C, au);
+    // step i is computed here: no later LDS read moves above it and no step's
+    // operands are read more than one step ahead (register pressure)
+    asm volatile("" : "+v"(ag), "+v"(au)::"memory");
+  }
+  if (bad) *a.status = MOE_EUNSUP;
+  // 5. phases (lane bits 3..5), read from lanes 0..7, then the four waves in order
+  ag = sum_rows(dpp_add<8>(ag));
+  au = sum_rows(dpp_add<8>(au));
+  if (p == 0) {
+    part[0][wave][r] = ag;
+    part[1][wave][r] = au;
+  }
+  __syncthreads();
+  if (tid < 8) {
+    float g = 0.0f, uu = 0.0f;
 #pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const int jl = 4 * i + p;
-        const bool ok = jl < gw_here;
-        const int jc = ok ? jl : 0;
-        const uint4* xq = reinterpret_cast<const uint4*>(xs + jc * 16);
-        const uint4 x0 = xq[0], x1 = xq[1], x2 = xq[2], x3 = xq[3];
-        const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                 x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-        const uint32_t gw[4] = {cg[i].x, cg[i].y, cg[i].z, cg[i].w};
-        const uint32_t uw[4] = {cu[i].x, cu[i].y, cu[i].z, cu[i].w};
-        float dg = 0.0f, du = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            dg = dot2(nib_pair(gw[d], q), xw[4 * d + q], dg);
-            du = dot2(nib_pair(uw[d], q), xw[4 * d + q], du);
-          }
-        }
-        const float X = Xs[jc];
-        const float sg = ok ? (float)sgh[i] : 0.0f;
-        const float su = ok ? (float)suh[i] : 0.0f;
-        ag = fmaf(sg, fmaf(-24.0f, X, dg), ag);
-        au = fmaf(su, fmaf(-24.0f, X, du), au);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      g += part[0][w][tid];
+      uu += part[1][w][tid];
     }
-    // phases (lane bits 4..5) in a fixed butterfly, then the four waves in order
-    ag += __shfl_xor(ag, 16, 64);
-    au += __shfl_xor(au, 16, 64);
-    ag += __shfl_xor(ag, 32, 64);
-    au += __shfl_xor(au, 32, 64);
-    if (p == 0) {
-      part[0][wave][r] = ag;
-      part[1][wave][r] = au;
-    }
-    __syncthreads();
-    if (tid < 16) {
-      float g = 0.0f, uu = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        g += part[0][w][tid];
-        uu += part[1][w][tid];
-      }
-      hws[(size_t)unit_pair(u, K, has_shared) * I + rb * 16 + tid] = blob ? silu(g) * uu : 0.0f;
-    }
-    __syncthreads();
+    const float hv = blob ? silu(g) * uu : 0.0f;
+    if (!(fabsf(hv) < 65520.0f)) *a.status = MOE_EUNSUP;  // h does not fit fp16
+    reinterpret_cast<_Float16*>(a.ws)[(size_t)unit_pair(u, K, has_shared) * I + hb * 8 + tid] = (_Float16)hv;
   }
 }
 
 // ------------------------------------------------------------------ down + combine
-// CPL = columns per lane; a wave owns CW = 8 * CPL consecutive columns.
+// CPL = columns per lane; a wave owns CW = 16 * CPL consecutive columns.
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
-  // LDS per wave: h slice [CW][32] floats + column sums [CW]
+  // LDS per wave: h slice as fp16 pairs [CW][16] dwords + column corrections [CW]
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kMaxUnits = kMaxK + 1;
-  __shared__ float part[kWaves][kMaxUnits][8];
-  __shared__ const uint8_t* ublob[kMaxUnits];
+  constexpr int CW = 16 * CPL;
+  __shared__ float part[kWaves][kMaxUnits][4];
+  __shared__ float wsh[kMaxK];
   const int H = a.H, I = a.I, K = a.K;
   const int Gd = I / kGroup;
   const bool has_shared = a.shared_blob != nullptr;
   const int n_units = K + (has_shared ? 1 : 0);
   const int C = n_units * Gd;
-  constexpr int CW = 8 * CPL;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 7, p = lane >> 3;
-  float* hs = reinterpret_cast<float*>(smem) + (size_t)wave * (CW * 32 + CW);
-  float* hsum = hs + CW * 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 3, p = lane >> 2;
+  uint32_t* hs = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * (CW * 17);
+  float* Cc = reinterpret_cast<float*>(hs + CW * 16);
   const int c0 = wave * CW;
-  const float* hws = reinterpret_cast<const float*>(a.ws);
+  const uint4* h4 = reinterpret_cast<const uint4*>(a.ws);  // h: fp16 [pair][I]
   const BlobLayout BL = blob_layout(H, I);
-  if (tid < n_units) ublob[tid] = dec_unit_blob(a, tid, has_shared);
-  for (int q = tid; q < kWaves * kMaxUnits * 8; q += kThreads) (&part[0][0][0])[q] = 0.0f;
-  __syncthreads();  // before any weight load is issued
-  const int n_rb = H / 8;
-  bool staged = false;
-  for (int rb = blockIdx.x; rb < n_rb; rb += gridDim.x) {
-    const int n = rb * 8 + r;
-    // this wave's h slice: float4 q of the slice is column c0 + q/8, floats 4*(q%8) .. +3
-    float4 hv[CPL];
-    if (!staged) {
+  const int qb = xcd_item(blockIdx.x, H / 4);
+  const int n = qb * 4 + r;
+  // the routing weights, loaded first and kept in LDS for the combine
+  const float wk = (wave == 0 && lane < K) ? a.w[lane] : 0.0f;
+  // 1. this wave's h slice: uint4 q = lane + 64m = column c0 + q/4, halves 8*(q%4) .. +7;
+  //    (unit, group) of the lane's column advance by 16 columns per m. Issued first:
+  //    it does not depend on the unit slots.
+  uint4 hv[CPL];
+  {
+    int cu = c0 + lane / 4;
+    cu = cu < C ? cu : C - 1;
+    int hu = cu / Gd, hj = cu % Gd;
 #pragma unroll
-      for (int m = 0; m < CPL; ++m) {
-        const int q = lane + 64 * m;
-        const int c = c0 + q / 8;
-        if (c < C) {
-          const int u = c / Gd, j = c % Gd;
-          hv[m] = reinterpret_cast<const float4*>(hws + (size_t)unit_pair(u, K, has_shared) * I + j * kGroup)[q % 8];
-        } else {
-          hv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
+    for (int m = 0; m < CPL; ++m) {
+      const int uu = hu < n_units ? hu : n_units - 1;
+      const int jj = hu < n_units ? hj : Gd - 1;
+      hv[m] = h4[((size_t)unit_pair(uu, K, has_shared) * I + jj * kGroup) / 8 + lane % 4];
+      hj += 16;  // Gd is a multiple of 16: at most one wrap
+      const int w1 = hj >= Gd;
+      hj -= w1 ? Gd : 0;
+      hu += w1;
     }
-    uint4 cd[CPL];
-    _Float16 sdh[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = c0 + 8 * i + p;
-      const int cc = c < C ? c : C - 1;
-      const int u = cc / Gd, j = cc % Gd;
-      const uint8_t* blob = ublob[u];
-      if (blob) {
-        cd[i] = *reinterpret_cast<const uint4*>(blob + BL.down_codes + ((size_t)j * H + n) * 16);
-        const size_t so = (((size_t)(n / kScaleBlock) * Gd + j) * kScaleBlock + n % kScaleBlock) * 2;
-        sdh[i] = *reinterpret_cast<const _Float16*>(blob + BL.down_scales + so);
+  }
+  // unit slots (two dependent loads): lane u of every wave holds unit u's slot,
+  // -1 when it cannot be used (the status word says why); the shared expert
+  // (unit 0 when present) is marked 0 and read from shared_blob
+  int my_slot = -1;
+  if (lane < n_units) {
+    const int k = has_shared ? lane - 1 : lane;
+    if (k < 0) {
+      my_slot = 0;
+    } else {
+      const int e = a.ids[k];
+      if (e < 0 || e >= a.E) {
+        *a.status = MOE_EINVAL;
       } else {
-        cd[i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        sdh[i] = (_Float16)0.0f;
+        my_slot = a.slot_table[e];
+        if (my_slot < 0) *a.status = MOE_ENOTRES;
       }
     }
-    if (!staged) {
-#pragma unroll
-      for (int m = 0; m < CPL; ++m) {
-        const int q = lane + 64 * m;
-        reinterpret_cast<float4*>(hs)[q] = hv[m];
-        // lanes 8t .. 8t+7 hold one column: sum its 32 floats in a fixed order
-        float s = ((hv[m].x + hv[m].y) + hv[m].z) + hv[m].w;
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64);
-        if ((lane & 7) == 0) hsum[q / 8] = s;
-      }
-      __builtin_amdgcn_wave_barrier();
-      staged = true;
-    }
-    float acc = 0.0f;
-    int cur = -1;
+  }
+  // this wave's entries of the partial sums start at zero (only this wave writes them)
+  for (int q = lane; q < kMaxUnits * 4; q += 64) (&part[wave][0][0])[q] = 0.0f;
+  // 2. codes and scale dwords of every step; a step is one unit for all lanes
+  bool uok[CPL];
+  int ustep[CPL];  // unit of step i (>= n_units past the last column)
+  uint4 cd[CPL];
+  uint32_t sdw[CPL];
+  {
+    int us = c0 / Gd, js = c0 % Gd;  // unit and group of the step's first column (wave-uniform)
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const int cl = 8 * i + p;  // column within the wave's range
-      const int ustep = (c0 + 8 * i) / Gd;  // one unit for the whole step (Gd % 8 == 0)
-      if (c0 + 8 * i < C) {
-        if (ustep != cur) {
-          if (cur >= 0) {
-            float t = acc;
-            t += __shfl_xor(t, 8, 64);
-            t += __shfl_xor(t, 16, 64);
-            t += __shfl_xor(t, 32, 64);
-            if (p == 0) part[wave][cur][r] = t;
-          }
-          acc = 0.0f;
-          cur = ustep;
+      ustep[i] = us;
+      const int uc = us < n_units ? us : n_units - 1;
+      const int jc = us < n_units ? js : Gd - 16;
+      const int sl = __builtin_amdgcn_readlane(my_slot, uc);
+      uok[i] = sl >= 0;
+      const uint8_t* src = (has_shared && uc == 0) ? a.shared_blob : a.slots + (size_t)(sl > 0 ? sl : 0) * a.stride;
+      const int j = jc + p;
+      // 4 rows x 16 groups: 1 KB of contiguous codes per wave
+      cd[i] = *reinterpret_cast<const uint4*>(src + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
+      sdw[i] = reinterpret_cast<const uint32_t*>(src + BL.down_scales)[scale_off(n, j, Gd, kRowBlockDN) >> 2];
+      js += 16;
+      if (js >= Gd) {
+        js -= Gd;
+        ++us;
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before h is used
+  if (wave == 0 && lane < K) wsh[lane] = wk;
+  // 3. h slice into LDS with its column corrections (lanes 4t .. 4t+3 hold one column)
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int q = lane + 64 * m;
+    const bool live = c0 + q / 4 < C;
+    const uint32_t d[4] = {live ? hv[m].x : 0u, live ? hv[m].y : 0u, live ? hv[m].z : 0u, live ? hv[m].w : 0u};
+    float sa = (f16_lo(d[0]) + f16_hi(d[0])) + (f16_lo(d[2]) + f16_hi(d[2]));
+    float sb = (f16_lo(d[1]) + f16_hi(d[1])) + (f16_lo(d[3]) + f16_hi(d[3]));
+    sa = quad_xor_add<2>(quad_xor_add<1>(sa));  // same bits on the column's four lanes
+    sb = quad_xor_add<2>(quad_xor_add<1>(sb));
+    reinterpret_cast<uint4*>(hs)[q] = make_uint4(d[0], d[1], d[2], d[3]);
+    if ((lane & 3) == 0) Cc[q / 4] = fmaf(1032.0f, sa, 72.0f * sb);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // 4. the steps; the LDS operands of step i+1 are read during step i
+  const int sh = (r & 1) * 16;
+  float acc = 0.0f;
+  int cur = -1;
+  uint4 hn[4];
+  float Cn;
+  {
+    const uint4* hq = reinterpret_cast<const uint4*>(hs + p * 16);
+    hn[0] = hq[0], hn[1] = hq[1], hn[2] = hq[2], hn[3] = hq[3];
+    Cn = Cc[p];
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int cs = c0 + 16 * i;
+    const uint4 h0 = hn[0], h1 = hn[1], h2 = hn[2], h3 = hn[3];
+    const float Ccol = Cn;
+    if (i + 1 < CPL) {
+      const uint4* hq = reinterpret_cast<const uint4*>(hs + (16 * (i + 1) + p) * 16);
+      hn[0] = hq[0], hn[1] = hq[1], hn[2] = hq[2], hn[3] = hq[3];
+      Cn = Cc[16 * (i + 1) + p];
+    }
+    if (cs < C) {  // uniform across the wave
+      const int us = ustep[i];
+      if (us != cur) {
+        if (cur >= 0) {
+          const float t = sum_rows(dpp_add<8>(dpp_add<4>(acc)));  // phases (lane bits 2..5), read from lanes 0..3
+          if (p == 0) part[wave][cur][r] = t;
         }
-        const float* hc = hs + cl * 32;
-        const uint32_t cw[4] = {cd[i].x, cd[i].y, cd[i].z, cd[i].w};
-        float P = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float4 h0 = reinterpret_cast<const float4*>(hc + 8 * d)[0];
-          const float4 h1 = reinterpret_cast<const float4*>(hc + 8 * d)[1];
-          const uint32_t lo = cw[d] & 0x0F0F0F0Fu;
-          const uint32_t hi = (cw[d] >> 4) & 0x0F0F0F0Fu;
-          // lo bytes hold columns +0, +4, +1, +5 of the dword; hi bytes +2, +6, +3, +7
-          P = fmaf((float)(lo & 0xFF), h0.x, P);
-          P = fmaf((float)((lo >> 8) & 0xFF), h1.x, P);
-          P = fmaf((float)((lo >> 16) & 0xFF), h0.y, P);
-          P = fmaf((float)(lo >> 24), h1.y, P);
-          P = fmaf((float)(hi & 0xFF), h0.z, P);
-          P = fmaf((float)((hi >> 8) & 0xFF), h1.z, P);
-          P = fmaf((float)((hi >> 16) & 0xFF), h0.w, P);
-          P = fmaf((float)(hi >> 24), h1.w, P);
-        }
-        acc = fmaf((float)sdh[i], fmaf(-8.0f, hsum[cl], P), acc);
+        acc = 0.0f;
+        cur = us;
       }
+      float P = 0.0f;
+      P = code_dot(cd[i].x, h0.x, h0.y, h0.z, h0.w, P);
+      P = code_dot(cd[i].y, h1.x, h1.y, h1.z, h1.w, P);
+      P = code_dot(cd[i].z, h2.x, h2.y, h2.z, h2.w, P);
+      P = code_dot(cd[i].w, h3.x, h3.y, h3.z, h3.w, P);
+      const float s = uok[i] ? f16_lo(sdw[i] >> sh) : 0.0f;
+      acc = fmaf(s, P - Ccol, acc);
     }
-    if (cur >= 0) {
-      float t = acc;
-      t += __shfl_xor(t, 8, 64);
-      t += __shfl_xor(t, 16, 64);
-      t += __shfl_xor(t, 32, 64);
-      if (p == 0) part[wave][cur][r] = t;
-    }
-    __syncthreads();
-    if (tid < 8) {
-      float y = 0.0f;
-      const int base = has_shared ? 1 : 0;
-      if (has_shared) {
-        float o = 0.0f;
+    asm volatile("" : "+v"(acc)::"memory");  // as in dec_gateup: one step of operands ahead
+  }
+  if (cur >= 0) {
+    const float t = sum_rows(dpp_add<8>(dpp_add<4>(acc)));
+    if (p == 0) part[wave][cur][r] = t;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    float y = 0.0f;
+    const int base = has_shared ? 1 : 0;
+    if (has_shared) {
+      float o = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) o += part[w][0][tid];
-        y = o;
-      }
-      for (int k = 0; k < K; ++k) {
-        float o = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) o += part[w][base + k][tid];
-        y = fmaf(a.w[k], o, y);
-      }
-      a.y[(size_t)rb * 8 + tid] = __builtin_bit_cast(uint16_t, (__bf16)y);
+      for (int w = 0; w < kWaves; ++w) o += part[w][0][tid];
+      y = o;
     }
-    __syncthreads();
-    // the next row block rewrites exactly the entries this one wrote, so no re-zeroing
+    for (int k = 0; k < K; ++k) {
+      float o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) o += part[w][base + k][tid];
+      y = fmaf(wsh[k], o, y);
+    }
+    a.y[(size_t)qb * 4 + tid] = __builtin_bit_cast(uint16_t, (__bf16)y);
   }
 }
 
@@ -345,18 +448,18 @@ inline void set_lds_limit(const void* fn, size_t lds) {
 inline int dec_down_cpl(int n_units, int Gd) {
   const int C = n_units * Gd;
   const int per_wave = (C + kWaves - 1) / kWaves;
-  return (per_wave + 7) / 8;
+  return (per_wave + 15) / 16;
 }
 
-inline int round_cpl(int cpl) { return cpl <= 4 ? 4 : cpl <= 8 ? 8 : cpl <= 12 ? 12 : 16; }
+inline int round_cpl(int cpl) { return cpl <= 2 ? 2 : cpl <= 4 ? 4 : cpl <= 6 ? 6 : 8; }
 
 }  // namespace
 
 bool decode1_supported(int T, int H, int I, int K, bool has_shared) {
   const int n_units = K + (has_shared ? 1 : 0);
   const int G = H / kGroup, Gd = I / kGroup;
-  // gate/up: at most 8 groups per lane; down: whole steps of 8 columns per unit, at most 16 per lane
-  return T == 1 && G <= 4 * 4 * 8 && Gd % 8 == 0 && dec_down_cpl(n_units, Gd) <= 16;
+  // gate/up: at most 4 groups per lane; down: whole steps of 16 columns per unit, at most 8 per lane
+  return T == 1 && G <= 4 * 8 * 4 && Gd % 16 == 0 && H % 4 == 0 && dec_down_cpl(n_units, Gd) <= 8;
 }
 
 hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
@@ -365,10 +468,9 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
   if (stage == 0) {
     const int G = a.H / kGroup;
     const int GW = (G + kWaves - 1) / kWaves;
-    const int gpl = (GW + 3) / 4;
-    const size_t lds = (size_t)kWaves * (GW * 16 + GW) * 4;
-    const int items = n_units * (a.I / 16);
-    const int grid = items < 4096 ? items : 4096;
+    const int gpl = (GW + 7) / 8;
+    const size_t lds = (size_t)kWaves * GW * 17 * 4;
+    const int grid = n_units * (a.I / 8);
 #define GU(N)                                                                                       \
   do {                                                                                              \
     set_lds_limit(reinterpret_cast<const void*>(&dec_gateup_kernel<N>), lds);                       \
@@ -376,26 +478,24 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
   } while (0)
     if (gpl <= 1) GU(1);
     else if (gpl <= 2) GU(2);
-    else if (gpl <= 4) GU(4);
-    else GU(8);
+    else GU(4);
 #undef GU
     return hipGetLastError();
   }
   {
     const int Gd = a.I / kGroup;
     const int cpl = round_cpl(dec_down_cpl(n_units, Gd));
-    const size_t lds = (size_t)kWaves * (8 * cpl * 32 + 8 * cpl) * 4;
-    const int n_rb = a.H / 8;
-    const int grid = n_rb < 4096 ? n_rb : 4096;
+    const size_t lds = (size_t)kWaves * 16 * cpl * 17 * 4;
+    const int grid = a.H / 4;
 #define DN(N)                                                                                       \
   do {                                                                                              \
     set_lds_limit(reinterpret_cast<const void*>(&dec_down_kernel<N>), lds);                         \
     hipLaunchKernelGGL((dec_down_kernel<N>), dim3(grid), dim3(kThreads), lds, s, a);                \
   } while (0)
-    if (cpl == 4) DN(4);
-    else if (cpl == 8) DN(8);
-    else if (cpl == 12) DN(12);
-    else DN(16);
+    if (cpl == 2) DN(2);
+    else if (cpl == 4) DN(4);
+    else if (cpl == 6) DN(6);
+    else DN(8);
 #undef DN
     return hipGetLastError();
   }

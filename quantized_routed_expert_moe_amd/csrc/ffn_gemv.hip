@@ -234,10 +234,10 @@ __global__ void __launch_bounds__(kThreads) ffn_gateup_kernel(FfnArgs a) {
     for (int i = 0; i < GPS; ++i) {
       const int jr = sl + kSlicesGU * i;
       const int j = jr < G ? jr : G - 1;  // out-of-range slices reload the last group, scaled by 0 below
-      const size_t co = ((size_t)j * I + n) * 16;
+      const size_t co = code_off(n, j, G, kRowBlockGU);
       cg[i] = *reinterpret_cast<const uint4*>(blob + BL.gate_codes + co);
       cu[i] = *reinterpret_cast<const uint4*>(blob + BL.up_codes + co);
-      const size_t so = (((size_t)(n / kScaleBlock) * G + j) * kScaleBlock + n % kScaleBlock) * 2;
+      const size_t so = scale_off(n, j, G, kRowBlockGU);
       sgh[i] = *reinterpret_cast<const _Float16*>(blob + BL.gate_scales + so);
       suh[i] = *reinterpret_cast<const _Float16*>(blob + BL.up_scales + so);
     }
@@ -366,8 +366,8 @@ __global__ void __launch_bounds__(kThreads) ffn_down_kernel(FfnArgs a) {
       for (int i = 0; i < GPS; ++i) {
         const int jr = sl + kSlicesDN * i;
         const int j = jr < Gd ? jr : Gd - 1;
-        cd[i] = *reinterpret_cast<const uint4*>(blob + BL.down_codes + ((size_t)j * H + n) * 16);
-        const size_t so = (((size_t)(n / kScaleBlock) * Gd + j) * kScaleBlock + n % kScaleBlock) * 2;
+        cd[i] = *reinterpret_cast<const uint4*>(blob + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
+        const size_t so = scale_off(n, j, Gd, kRowBlockDN);
         sdh[i] = *reinterpret_cast<const _Float16*>(blob + BL.down_scales + so);
       }
     } else {  // expert not resident (status already set): o = 0 for its pairs

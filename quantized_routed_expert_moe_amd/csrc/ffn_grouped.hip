@@ -264,7 +264,6 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int Kd = MODE == 0 ? H : I;  // reduced dimension
   const int G = Kd / kGroup;
-  const int Nmat = MODE == 0 ? I : H;  // rows of the weight matrix
   const BlobLayout BL = blob_layout(H, I);
 
   // A loader: thread -> (row ar, 32-element half ah) of the 128 x 64 stage
@@ -294,9 +293,10 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
     bcodes = BL.down_codes;
     bscales = BL.down_scales;
   }
-  const uint8_t* bsrc = blob ? blob + bcodes + (size_t)brow * 16 : nullptr;
-  const uint8_t* ssrc =
-      blob ? blob + bscales + ((size_t)(brow / kScaleBlock) * G * kScaleBlock + brow % kScaleBlock) * 2 : nullptr;
+  // group j of this row: code chunk at bsrc + j * R * 16 bytes, scale at ssrc + j * R * 2 bytes
+  const int R = MODE == 0 ? kRowBlockGU : kRowBlockDN;
+  const uint8_t* bsrc = blob ? blob + bcodes + code_off(brow, 0, G, R) : nullptr;
+  const uint8_t* ssrc = blob ? blob + bscales + scale_off(brow, 0, G, R) : nullptr;
 
   uint4 ra[2][4];
   uint4 rb[2];
@@ -313,8 +313,8 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
     }
     if (blob) {
       const int j = k0 / kGroup + bg;
-      rb[q] = *reinterpret_cast<const uint4*>(bsrc + (size_t)j * Nmat * 16);
-      rs[q] = *reinterpret_cast<const _Float16*>(ssrc + (size_t)j * kScaleBlock * 2);
+      rb[q] = *reinterpret_cast<const uint4*>(bsrc + (size_t)j * R * 16);
+      rs[q] = *reinterpret_cast<const _Float16*>(ssrc + (size_t)j * R * 2);
     } else {
       rb[q] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
       rs[q] = (_Float16)0.0f;

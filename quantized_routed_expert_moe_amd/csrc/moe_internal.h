@@ -10,19 +10,24 @@
 namespace moe {
 
 constexpr int kGroup = 32;      // int4 quantisation group along the reduced dimension
-constexpr int kScaleBlock = 16; // rows per scale block in the blob
+constexpr int kRowBlockGU = 8;  // rows per block of the gate and up matrices in the blob
+constexpr int kRowBlockDN = 4;  // rows per block of the down matrix in the blob
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int kGemvMaxT = 32;   // default path choice: GEMV for T <= 32, grouped MFMA above
 
 // Blob layout of one expert (all offsets in bytes from the blob start).
 //   codes of gate, up, down, then scales of gate, up, down.
-// Codes of a matrix with N rows and C reduced columns (G = C / 32 groups):
-//   [G][N][16 bytes]; the 16 bytes of (group j, row n) hold the 32 codes of
-//   columns 32j .. 32j+31 as four dwords; dword d covers columns c0 = 32j + 8d
-//   .. c0+7 with nibble i (bits 4i..4i+3) = column c0 + 2i for i < 4 and
+// Codes of a matrix with N rows and C reduced columns (G = C / 32 groups), in
+//   blocks of R rows (R = 8 for gate and up, 4 for down): [N/R][G][R][16 bytes];
+//   the 16-byte chunk of (row n, group j) is chunk ((n/R)*G + j)*R + n%R, so a
+//   block of R rows is one contiguous run and 1 KB of it covers R rows of
+//   64/R consecutive groups (one wave-wide load). The chunk holds the 32 codes
+//   of columns 32j .. 32j+31 as four dwords; dword d covers columns c0 = 32j +
+//   8d .. c0+7 with nibble i (bits 4i..4i+3) = column c0 + 2i for i < 4 and
 //   c0 + 2(i-4) + 1 for i >= 4; each nibble is the offset-binary code u = q + 8.
-// Scales: [N/16][G][16] fp16, scale of (row n, group j) at ((n/16)*G + j)*16 + n%16.
+// Scales: [N/R][G][R] fp16, scale of (row n, group j) at ((n/R)*G + j)*R + n%R
+//   (the same index as the code chunk).
 struct BlobLayout {
   size_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales, bytes;
 };
@@ -40,6 +45,14 @@ __host__ __device__ inline BlobLayout blob_layout(int H, int I) {
   L.bytes = L.down_scales + mat_scales;
   return L;
 }
+
+// Byte offset of the code chunk / the scale of (row n, group j) within a matrix
+// of G groups stored in blocks of R rows.
+__host__ __device__ inline size_t chunk_index(int n, int j, int G, int R) {
+  return ((size_t)(n / R) * G + j) * R + n % R;
+}
+__host__ __device__ inline size_t code_off(int n, int j, int G, int R) { return chunk_index(n, j, G, R) * 16; }
+__host__ __device__ inline size_t scale_off(int n, int j, int G, int R) { return chunk_index(n, j, G, R) * 2; }
 
 __host__ __device__ inline bool shape_ok(int H, int I, int g) {
   return g == kGroup && H >= kGroup && I >= kGroup && H % kGroup == 0 && I % kGroup == 0 && H <= 65536 &&

@@ -2,11 +2,12 @@
 //
 // The blob keeps one expert's three matrices in one contiguous allocation, the
 // "one read per expert instead of three" layout of "Strata on a Mac" (What you
-// need). Inside it, codes are stored group-major ([G][N][16 bytes]) so that a
-// kernel reading one group of consecutive rows touches one contiguous run, the
+// need). Inside it, codes and scales are blocked by rows ([N/R][G][R][16
+// bytes], R = 8 for gate/up and 4 for down) so that a kernel walking the
+// groups of a row block reads one contiguous run, the
 // nibbles are in offset binary (u = q + 8) and interleaved so that one shift and
-// one mask turn a code dword into bf16 pairs of consecutive columns, and scales
-// are blocked by 16 rows. The layout is documented in moe_internal.h.
+// one mask turn a code dword into 16-bit pairs of consecutive columns. The
+// layout is documented in moe_internal.h.
 #include <string.h>
 
 #include "moe_internal.h"
@@ -27,7 +28,7 @@ inline uint32_t interleave_dword(uint32_t v) {
   return (lo | (hi << 16)) ^ 0x88888888u;
 }
 
-void pack_matrix(const uint8_t* q, const uint16_t* s, int N, int C, uint8_t* codes, uint16_t* scales) {
+void pack_matrix(const uint8_t* q, const uint16_t* s, int N, int C, int R, uint8_t* codes, uint16_t* scales) {
   const int G = C / moe::kGroup;
   const size_t row_bytes = (size_t)C / 2;
   for (int n = 0; n < N; ++n) {
@@ -36,9 +37,8 @@ void pack_matrix(const uint8_t* q, const uint16_t* s, int N, int C, uint8_t* cod
       uint32_t src[4], dst[4];
       memcpy(src, row + (size_t)j * 16, 16);
       for (int d = 0; d < 4; ++d) dst[d] = interleave_dword(src[d]);
-      memcpy(codes + ((size_t)j * N + n) * 16, dst, 16);
-      scales[((size_t)(n / moe::kScaleBlock) * G + j) * moe::kScaleBlock + n % moe::kScaleBlock] =
-          s[(size_t)n * G + j];
+      memcpy(codes + moe::code_off(n, j, G, R), dst, 16);
+      scales[moe::chunk_index(n, j, G, R)] = s[(size_t)n * G + j];
     }
   }
 }
@@ -61,8 +61,8 @@ extern "C" int moe_pack_expert(const uint8_t* qg, const uint8_t* qu, const uint8
   if (!moe::shape_ok(H, I, g)) return MOE_EUNSUP;
   const moe::BlobLayout L = moe::blob_layout(H, I);
   uint8_t* b = static_cast<uint8_t*>(blob_out);
-  pack_matrix(qg, sg, I, H, b + L.gate_codes, reinterpret_cast<uint16_t*>(b + L.gate_scales));
-  pack_matrix(qu, su, I, H, b + L.up_codes, reinterpret_cast<uint16_t*>(b + L.up_scales));
-  pack_matrix(qd, sd, H, I, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
+  pack_matrix(qg, sg, I, H, moe::kRowBlockGU, b + L.gate_codes, reinterpret_cast<uint16_t*>(b + L.gate_scales));
+  pack_matrix(qu, su, I, H, moe::kRowBlockGU, b + L.up_codes, reinterpret_cast<uint16_t*>(b + L.up_scales));
+  pack_matrix(qd, sd, H, I, moe::kRowBlockDN, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
   return MOE_OK;
 }

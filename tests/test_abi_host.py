@@ -45,10 +45,13 @@ def test_strerror_and_sizes():
     assert lib.moe_blob_bytes(4000 + 16, 1536, 32) == 0  # H not a multiple of 32
 
 
-def decode_blob_matrix(blob, off_codes, off_scales, N, C):
-    """Independent reader of the documented blob layout -> (codes int [N][C], scales f16 [N][C/32])."""
+def decode_blob_matrix(blob, off_codes, off_scales, N, C, R):
+    """Independent reader of the documented blob layout (blocks of R rows) ->
+    (codes int [N][C], scales f16 [N][C/32])."""
     G = C // 32
-    codes = np.frombuffer(blob, dtype=np.uint32, count=G * N * 4, offset=off_codes).reshape(G, N, 4)
+    # [N/R][G][R rows][4 dwords] -> [G][N][4]
+    codes = np.frombuffer(blob, dtype=np.uint32, count=G * N * 4, offset=off_codes).reshape(N // R, G, R, 4)
+    codes = codes.transpose(1, 0, 2, 3).reshape(G, N, 4)
     q = np.empty((N, C), dtype=np.int64)
     for d in range(4):
         w = codes[:, :, d]  # [G][N]
@@ -56,7 +59,7 @@ def decode_blob_matrix(blob, off_codes, off_scales, N, C):
             col = 8 * d + (2 * i if i < 4 else 2 * (i - 4) + 1)
             u = (w >> (4 * i)) & 0xF
             q[:, col::32] = (u.astype(np.int64) - 8).T
-    sc = np.frombuffer(blob, dtype=np.float16, count=N * G, offset=off_scales).reshape(N // 16, G, 16)
+    sc = np.frombuffer(blob, dtype=np.float16, count=N * G, offset=off_scales).reshape(N // R, G, R)
     s = sc.transpose(0, 2, 1).reshape(N, G)
     return q, s
 
@@ -77,10 +80,11 @@ def test_pack_layout_roundtrip(H, I):
     lib.moe_pack_expert(t["qg"], t["qu"], t["qd"], t["sg"].view(np.uint16), t["su"].view(np.uint16),
                         t["sd"].view(np.uint16), H, I, 32, blob)
     mc, ms = H * I // 2, H * I // 16
-    offs = [(0, 3 * mc, I, H, "qg", "sg"), (mc, 3 * mc + ms, I, H, "qu", "su"),
-            (2 * mc, 3 * mc + 2 * ms, H, I, "qd", "sd")]
-    for oc, os_, N, C, qk, sk in offs:
-        q, s = decode_blob_matrix(blob.tobytes(), oc, os_, N, C)
+    # gate and up in blocks of 8 rows, down in blocks of 4
+    offs = [(0, 3 * mc, I, H, 8, "qg", "sg"), (mc, 3 * mc + ms, I, H, 8, "qu", "su"),
+            (2 * mc, 3 * mc + 2 * ms, H, I, 4, "qd", "sd")]
+    for oc, os_, N, C, R, qk, sk in offs:
+        q, s = decode_blob_matrix(blob.tobytes(), oc, os_, N, C, R)
         assert np.array_equal(q, unpack_plain(t[qk], C))
         assert np.array_equal(s.view(np.uint16), t[sk].view(np.uint16))
     assert not blob[3 * mc + 3 * ms :].any()  # padding stays zero
