@@ -121,14 +121,13 @@ def decode_leg(a, dev):
     blob = lib.moe_blob_bytes(w.H, w.I)
     mat_bytes = w.H * w.I // 2 + w.H * w.I // 32 * 2  # codes + fp16 scales of one matrix
     bytes_router = w.E * w.H * 4 + w.T * w.H * 2 + w.T * w.E * 4 + w.T * w.K * 8
-    bytes_gate_up = w.K * 2 * mat_bytes + w.T * w.H * 2 + w.T * w.K * w.I * 4  # experts + x + h
-    bytes_down = w.K * mat_bytes + w.T * w.K * w.I * 4 + w.T * w.H * 2  # experts + h + y
+    bytes_gate_up = w.K * 2 * mat_bytes + w.T * w.H * 2 + w.T * w.K * w.I * 2  # experts + x + h (fp16)
+    bytes_down = w.K * mat_bytes + w.T * w.K * w.I * 2 + w.T * w.H * 2  # experts + h (fp16) + y
     bytes_layer = bytes_router + w.K * blob + w.T * w.H * 2 * 2
 
-    def step():
+    def step():  # one token through the layer stack: moe_layer per layer
         for L in stacks:
-            run.route(L, stream)
-            run.ffn(L, stream)
+            run.layer(L, stream)
 
     with torch.cuda.stream(stream):
         for _ in range(a.warmup):

@@ -43,6 +43,7 @@
 // No atomics and no data-dependent reduction order: results depend only on
 // the inputs, never on slot addresses.
 #include "moe_internal.h"
+#include "wave_ops.h"
 
 namespace moe {
 namespace {
@@ -68,25 +69,6 @@ __device__ inline float code_dot(uint32_t w, uint32_t x0, uint32_t x1, uint32_t 
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Cross-lane sums without the LDS crossbar. Each is a fixed instruction
-// sequence, so the result depends only on the data; lanes may differ in the
-// order of their additions, and callers read the lane they document.
-template <int ROR>  // t + t of the lane ROR places over in its row of 16
-__device__ inline float dpp_add(float t) {
-  return t + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t), 0x120 + ROR, 0xF, 0xF, false));
-}
-template <int X>  // t + t of lane ^ X (X = 1 or 2), same bits on both lanes
-__device__ inline float quad_xor_add(float t) {
-  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-  return t + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t), ctrl, 0xF, 0xF, false));
-}
-__device__ inline float sum_rows(float t) {  // t summed over lanes l, l^16, l^32, l^48 (same bits on all four)
-  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-  t = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-}
-
 // fp16 bits of the fp32 value v (round to nearest even); *bad set when it overflows.
 __device__ inline uint32_t to_f16_bits(float v, bool* bad) {
   const _Float16 h = (_Float16)v;
@@ -99,11 +81,11 @@ __device__ inline float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(_F
 __device__ inline float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 
 // Blob of unit u (u = 0 is the shared expert when present) or nullptr with the
-// status word set.
-__device__ inline const uint8_t* dec_unit_blob(const FfnArgs& a, int u, bool has_shared) {
+// status word set; ids = the token's routed experts in rank order.
+__device__ inline const uint8_t* dec_unit_blob(const FfnArgs& a, int u, bool has_shared, const int32_t* ids) {
   const int k = has_shared ? u - 1 : u;
   if (k < 0) return a.shared_blob;
-  const int e = a.ids[k];
+  const int e = ids[k];
   if (e < 0 || e >= a.E) {
     *a.status = MOE_EINVAL;
     return nullptr;
@@ -128,11 +110,14 @@ __device__ inline int xcd_item(int bid, int n_items) {
 
 // ------------------------------------------------------------------ gate/up
 // GPL = groups per lane = ceil(GW / 8) with GW = ceil(G / 4) groups per wave.
-template <int GPL>
+// SEL: the workgroup first selects the token's experts from a.logits (wave 0,
+// wave_select, bit-identical to moe_route); workgroup 0 writes them out.
+template <int GPL, bool SEL>
 __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
   // LDS per wave: x slice as fp16 pairs [GW][16] dwords + group corrections [GW]
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float part[2][kWaves][8];
+  __shared__ int32_t sel_id[kMaxK];
   const int H = a.H, I = a.I, K = a.K;
   const int G = H / kGroup;
   const int GW = (G + kWaves - 1) / kWaves;
@@ -156,7 +141,24 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
     q = q < G * 4 ? q : G * 4 - 1;
     xv[v] = reinterpret_cast<const uint4*>(a.x)[q];
   }
-  const uint8_t* blob = dec_unit_blob(a, u, has_shared);
+  const int32_t* ids = a.ids;
+  if constexpr (SEL) {
+    if (wave == 0) {
+      int32_t id;
+      float wt;
+      wave_select<kFusedSelectMaxE / 64>(a.logits, a.E, K, a.route_flags, lane, id, wt);
+      if (lane < K) {
+        sel_id[lane] = id;
+        if (blockIdx.x == 0) {
+          a.ids_out[lane] = id;
+          a.w_out[lane] = wt;
+        }
+      }
+    }
+    __syncthreads();
+    ids = sel_id;
+  }
+  const uint8_t* blob = dec_unit_blob(a, u, has_shared, ids);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
   const int n = hb * 8 + r;
@@ -473,8 +475,13 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
     const int grid = n_units * (a.I / 8);
 #define GU(N)                                                                                       \
   do {                                                                                              \
-    set_lds_limit(reinterpret_cast<const void*>(&dec_gateup_kernel<N>), lds);                       \
-    hipLaunchKernelGGL((dec_gateup_kernel<N>), dim3(grid), dim3(kThreads), lds, s, a);              \
+    if (a.logits) {                                                                                 \
+      set_lds_limit(reinterpret_cast<const void*>(&dec_gateup_kernel<N, true>), lds);               \
+      hipLaunchKernelGGL((dec_gateup_kernel<N, true>), dim3(grid), dim3(kThreads), lds, s, a);      \
+    } else {                                                                                        \
+      set_lds_limit(reinterpret_cast<const void*>(&dec_gateup_kernel<N, false>), lds);              \
+      hipLaunchKernelGGL((dec_gateup_kernel<N, false>), dim3(grid), dim3(kThreads), lds, s, a);     \
+    }                                                                                               \
   } while (0)
     if (gpl <= 1) GU(1);
     else if (gpl <= 2) GU(2);

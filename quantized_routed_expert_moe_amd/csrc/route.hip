@@ -5,6 +5,7 @@
 // Softmax and the tie rule (equal logits -> lower id) follow the plain reading
 // of a softmax top-k router.
 #include "moe_internal.h"
+#include "wave_ops.h"
 
 namespace moe {
 namespace {
@@ -18,8 +19,8 @@ __device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0
 // covers the contiguous quarter [w*H/4, (w+1)*H/4) of the row; lane l takes
 // columns 4l + 256i of it, all loads issued before any arithmetic. Each lane
 // accumulates its columns in order in fp64 (bf16 x fp32 products are exact in
-// fp64), a fixed butterfly sums the lanes, and the four wave sums are added in
-// wave order; one rounding to fp32 at the end. The order is fixed, so the bits
+// fp64), a fixed sequence of DPP and permlane additions sums the lanes, and the
+// four wave sums are added in wave order; one rounding to fp32 at the end. The order is fixed, so the bits
 // are reproducible.
 constexpr int kRouterMaxIt = 8;  // columns per lane = 4 * kRouterMaxIt -> H <= 8192
 
@@ -56,8 +57,7 @@ __global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __rest
         a = fma((double)bf16_hi(xv[tt][i].y), (double)wv[i].w, a);
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
+    a = wave_sum_f64(a);
     if (lane == 0) part[wave][tt] = a;
   }
   __syncthreads();
@@ -68,83 +68,19 @@ __global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __rest
   }
 }
 
-// Total order key: larger key = higher logit, then lower id. -0.0 is folded into +0.0.
-__device__ inline uint64_t route_key(float l, int e) {
-  const uint32_t u = __float_as_uint(l + 0.0f);
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ inline float key_logit(uint64_t k) {
-  const uint32_t ord = (uint32_t)(k >> 32);
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
-
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-// One wave per token. Lane l holds the keys of experts l, l+64, ... sorted
-// descending in registers; K rounds of a butterfly max across the wave each
-// pick the next expert in rank order and pop it from its owner lane.
+// One wave per token (the selection is wave_select, shared with the fused decode path).
 template <int EPL>
 __global__ void __launch_bounds__(64) route_select_kernel(const float* __restrict__ logits, int T, int E, int K,
                                                           unsigned flags, int32_t* __restrict__ ids,
                                                           float* __restrict__ w) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
-  const float* l = logits + (size_t)t * E;
-  uint64_t key[EPL];
-  float lg[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    lg[i] = e < E ? l[e] : 0.0f;
-    key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
-  }
-  // local descending sort (odd-even transposition, EPL <= 16)
-#pragma unroll
-  for (int r = 0; r < EPL; ++r) {
-#pragma unroll
-    for (int i = (r & 1); i + 1 < EPL; i += 2) {
-      const uint64_t a = key[i], b = key[i + 1];
-      key[i] = a > b ? a : b;
-      key[i + 1] = a > b ? b : a;
-    }
-  }
-  uint64_t mine_best = 0;  // lane k keeps the winner of rank k
-  for (int k = 0; k < K; ++k) {
-    const uint64_t best = wave_max_u64(key[0]);
-    if (key[0] == best) {
-#pragma unroll
-      for (int i = 0; i + 1 < EPL; ++i) key[i] = key[i + 1];
-      key[EPL - 1] = 0;
-    }
-    if (lane == k) mine_best = best;
-  }
-  const float m = key_logit(__shfl(mine_best, 0, 64));
-  float part = 0.0f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i < E) part += expf(lg[i] - m);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-  float wk = 0.0f;
-  if (lane < K) wk = expf(key_logit(mine_best) - m) / part;
-  if (flags & MOE_ROUTE_RENORM) {
-    float s = lane < K ? wk : 0.0f;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    wk = wk / s;
-  }
+  int32_t id;
+  float wt;
+  wave_select<EPL>(logits + (size_t)t * E, E, K, flags, lane, id, wt);
   if (lane < K) {
-    ids[(size_t)t * K + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(mine_best & 0xFFFFFFFFu));
-    w[(size_t)t * K + lane] = wk;
+    ids[(size_t)t * K + lane] = id;
+    w[(size_t)t * K + lane] = wt;
   }
 }
 

@@ -1,0 +1,164 @@
+// Wave-level helpers shared by the routing and FFN kernels: cross-lane sums
+// and maxima, and the top-k selection of one token.
+//
+// Cross-lane moves avoid the LDS crossbar: DPP rotations inside a row of 16
+// lanes and the gfx950 permlane swaps between rows. Every helper is a fixed
+// instruction sequence, so its result depends only on the data.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+template <int ROR>  // the value of the lane ROR places over in this lane's row of 16
+__device__ inline uint32_t ror_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + ROR, 0xF, 0xF, false);
+}
+template <int ROR>
+__device__ inline uint64_t ror_u64(uint64_t v) {
+  return ((uint64_t)ror_u32<ROR>((uint32_t)(v >> 32)) << 32) | ror_u32<ROR>((uint32_t)v);
+}
+// (this lane's v, v of lane ^ 16) and (v, v of lane ^ 32), in some order per lane
+__device__ inline void swap16_u64(uint64_t v, uint64_t& a, uint64_t& b) {
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+  a = ((uint64_t)hi[0] << 32) | lo[0];
+  b = ((uint64_t)hi[1] << 32) | lo[1];
+}
+__device__ inline void swap32_u64(uint64_t v, uint64_t& a, uint64_t& b) {
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+  a = ((uint64_t)hi[0] << 32) | lo[0];
+  b = ((uint64_t)hi[1] << 32) | lo[1];
+}
+__device__ inline double as_f64(uint64_t v) { return __builtin_bit_cast(double, v); }
+__device__ inline uint64_t as_u64(double v) { return __builtin_bit_cast(uint64_t, v); }
+
+// Sum over the 64 lanes in a fixed sequence of additions; lane 0's result is the one to use.
+__device__ inline double wave_sum_f64(double a) {
+  a += as_f64(ror_u64<1>(as_u64(a)));
+  a += as_f64(ror_u64<2>(as_u64(a)));
+  a += as_f64(ror_u64<4>(as_u64(a)));
+  a += as_f64(ror_u64<8>(as_u64(a)));
+  uint64_t x, y;
+  swap16_u64(as_u64(a), x, y);
+  a = as_f64(x) + as_f64(y);
+  swap32_u64(as_u64(a), x, y);
+  return as_f64(x) + as_f64(y);
+}
+
+// Sum over the 64 lanes in a fixed sequence of additions, lane 0's bits on every lane.
+__device__ inline float wave_sum_f32(float a) {
+  a += __uint_as_float(ror_u32<1>(__float_as_uint(a)));
+  a += __uint_as_float(ror_u32<2>(__float_as_uint(a)));
+  a += __uint_as_float(ror_u32<4>(__float_as_uint(a)));
+  a += __uint_as_float(ror_u32<8>(__float_as_uint(a)));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  a = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  a = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane(__float_as_uint(a)));
+}
+
+// The maximum over the 64 lanes, on every lane.
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o = ror_u64<1>(v);
+  v = o > v ? o : v;
+  o = ror_u64<2>(v);
+  v = o > v ? o : v;
+  o = ror_u64<4>(v);
+  v = o > v ? o : v;
+  o = ror_u64<8>(v);
+  v = o > v ? o : v;
+  uint64_t x, y;
+  swap16_u64(v, x, y);
+  v = x > y ? x : y;
+  swap32_u64(v, x, y);
+  return x > y ? x : y;
+}
+
+// t + t of the lane ROR places over in its row of 16 (lanes may differ in association order)
+template <int ROR>
+__device__ inline float dpp_add(float t) {
+  return t + __uint_as_float(ror_u32<ROR>(__float_as_uint(t)));
+}
+// t + t of lane ^ X (X = 1 or 2): the same bits on both lanes
+template <int X>
+__device__ inline float quad_xor_add(float t) {
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return t + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t), ctrl, 0xF, 0xF, false));
+}
+// t summed over lanes l, l ^ 16, l ^ 32, l ^ 48: the same bits on all four
+__device__ inline float sum_rows(float t) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  t = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// Total order key of (logit, expert): larger key = higher logit, then lower id.
+// -0.0 is folded into +0.0. Every real key is > 0.
+__device__ inline uint64_t route_key(float l, int e) {
+  const uint32_t u = __float_as_uint(l + 0.0f);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ inline float key_logit(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ inline int32_t key_id(uint64_t k) { return (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu)); }
+
+// Softmax top-k of one token's E logits l[0..E) by one whole wave (E <= 64 * EPL,
+// K <= 64). Lane k < K gets rank k: its expert id and its weight
+// softmax(l)[id] (divided by the sum of the K weights with MOE_ROUTE_RENORM).
+// Lane l holds the keys of experts l, l+64, ... sorted descending in
+// registers; K rounds of a wave-wide maximum each take the next expert in rank
+// order from its owner lane.
+template <int EPL>
+__device__ inline void wave_select(const float* __restrict__ l, int E, int K, unsigned flags, int lane, int32_t& id,
+                                   float& wt) {
+  uint64_t key[EPL];
+  float lg[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    lg[i] = e < E ? l[e] : 0.0f;
+    key[i] = e < E ? route_key(lg[i], e) : 0ull;
+  }
+  // local descending sort (odd-even transposition)
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) {
+#pragma unroll
+    for (int i = (r & 1); i + 1 < EPL; i += 2) {
+      const uint64_t a = key[i], b = key[i + 1];
+      key[i] = a > b ? a : b;
+      key[i + 1] = a > b ? b : a;
+    }
+  }
+  uint64_t mine = 0;  // lane k keeps the winner of rank k
+  for (int k = 0; k < K; ++k) {
+    const uint64_t best = wave_max_u64(key[0]);
+    if (key[0] == best) {
+#pragma unroll
+      for (int i = 0; i + 1 < EPL; ++i) key[i] = key[i + 1];
+      key[EPL - 1] = 0;
+    }
+    if (lane == k) mine = best;
+  }
+  const uint32_t top_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mine >> 32));
+  const uint32_t top_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mine);
+  const float m = key_logit(((uint64_t)top_hi << 32) | top_lo);  // the largest logit (rank 0, lane 0)
+  float part = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + 64 * i < E) part += expf(lg[i] - m);
+  part = wave_sum_f32(part);
+  float w = 0.0f;
+  if (lane < K) w = expf(key_logit(mine) - m) / part;
+  if (flags & MOE_ROUTE_RENORM) w = w / wave_sum_f32(lane < K ? w : 0.0f);
+  id = key_id(mine);
+  wt = w;
+}
+
+}  // namespace moe

@@ -122,6 +122,13 @@ class LayerRunner:
         fn(L.x, self.ids, self.wts, w.T, w.H, w.I, w.E, w.K, w.g, L.table, L.slots, L.stride, L.shared,
            self.y if y is None else y, self.ws, self.ws_bytes, self.status, self.flags, stream)
 
+    def layer(self, L: DeviceLayer, stream=None, renorm=False):
+        """The whole layer in one call (moe_layer): same results as route() then ffn()."""
+        w = self.w
+        lib.moe_layer(L.x, L.wr, L.logits, w.T, w.H, w.I, w.E, w.K, w.g, lib.MOE_ROUTE_RENORM if renorm else 0,
+                      self.ids, self.wts, L.table, L.slots, L.stride, L.shared, self.y, self.ws, self.ws_bytes,
+                      self.status, self.flags, stream)
+
     def __call__(self, L: DeviceLayer, stream=None):
         self.route(L, stream)
         self.ffn(L, stream)

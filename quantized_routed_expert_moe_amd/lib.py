@@ -33,6 +33,7 @@ EXPORTS = (
     "moe_expert_ffn",
     "moe_ffn_gate_up",
     "moe_ffn_down",
+    "moe_layer",
     "arena_create",
     "arena_map_slots",
     "arena_fill_async",
@@ -92,6 +93,11 @@ def load(path: str | None = None):
         "moe_ffn_down": (
             _I,
             [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P, _P, _SZ, _P, ctypes.c_uint, _P],
+        ),
+        "moe_layer": (
+            _I,
+            [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P, _P, _SZ, _P, _P, _P, _SZ, _P,
+             ctypes.c_uint, _P],
         ),
         "arena_create": (_I, [_I, _I, _SZ, _SZ, _P, _P, _P, ctypes.POINTER(_P)]),
         "arena_map_slots": (_I, [_P, _P, _I, _P, _P, ctypes.POINTER(_I)]),
@@ -208,6 +214,18 @@ def moe_ffn_down(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_
                  dev_status, flags=0, stream=None) -> None:
     _ffn_call("moe_ffn_down", x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws,
               ws_bytes, dev_status, flags, stream)
+
+
+def moe_layer(x, w_router, logits, T, H, I, E, K, g, route_flags, ids, w, slot_table, slots, stride, shared_blob,
+              y, ws, ws_bytes, dev_status, ffn_flags=0, stream=None) -> None:
+    _check(
+        load().moe_layer(
+            _ptr(x), _ptr(w_router), _ptr(logits), T, H, I, E, K, g, route_flags, _ptr(ids), _ptr(w),
+            _ptr(slot_table), _ptr(slots), stride, _ptr(shared_blob), _ptr(y), _ptr(ws), ws_bytes,
+            _ptr(dev_status), ffn_flags, _stream(stream),
+        ),
+        "moe_layer",
+    )
 
 
 class Arena:

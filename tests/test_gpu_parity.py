@@ -195,6 +195,79 @@ def test_ffn_ragged_shapes(w):
     ffn_case(w, 0, flags=lib.MOE_FORCE_GEMV)
 
 
+# ------------------------------------------------------------------ whole layer (moe_layer)
+
+
+@pytest.mark.parametrize(
+    "w,renorm",
+    [
+        (gen.WORKLOADS["decode_t1_h4096_e256_k8_i1536_x48"], False),
+        (gen.Workload("paged_shape_t1_shared_logits_in", 1, 4096, 256, 6, 2048, 1, 64, "normal", 5, shared=True),
+         True),
+        (gen.Workload("dec_t1_h256_e64_k4_i512", 1, 256, 64, 4, 512, 1, 64, "gemv", 31), True),
+        (gen.Workload("dec_t1_h512_e256_k32_i512_shared", 1, 512, 256, 32, 512, 1, 256, "gemv", 32, shared=True),
+         False),
+        # more experts than the fused selection covers: moe_layer runs the two calls in turn
+        (gen.Workload("dec_t1_h256_e512_k8_i512", 1, 256, 512, 8, 512, 1, 512, "normal", 33), False),
+        # several tokens: the two calls in turn
+        (gen.Workload("t5_h256_e64_k4_i512", 5, 256, 64, 4, 512, 1, 64, "gemv", 34), False),
+    ],
+    ids=lambda v: v.name if hasattr(v, "name") else f"renorm{int(v)}",
+)
+def test_layer_equals_route_then_ffn_bitwise(w, renorm):
+    """moe_layer (selection fused into the first FFN kernel for one token) gives the
+    bits of moe_route followed by moe_expert_ffn: logits, ids, w and y."""
+    layer = 3
+    say(f"moe_layer {w.name} renorm={renorm}")
+    xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
+    logits = None
+    if w.router != "gemv":
+        logits = gen.normal_logits(w.seed, layer, w.T, w.E)
+        l_ref = logits
+    else:
+        l_ref = R.router_logits(xb, gen.router_weight(w.seed, layer, w.E, w.H))
+    ids_ref, _ = R.route(l_ref, w.K, renorm)
+    experts = sorted(set(ids_ref.ravel().tolist()))
+    L = harness.make_layer(w, layer, DEV, slots=max(len(experts), min(w.E, 64)), experts=experts, place_seed=9,
+                           logits=logits, x_bits=xb)
+    run = harness.LayerRunner(w, DEV)
+    run.route(L, renorm=renorm)
+    run.ffn(L)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    y1, ids1, w1, lg1 = run.y.clone(), run.ids.clone(), run.wts.clone(), L.logits.clone()
+    y2 = torch.empty_like(run.y)
+    ids2 = torch.full_like(run.ids, -7)
+    w2 = torch.full_like(run.wts, -7.0)
+    lg2 = L.logits if L.wr is None else torch.full_like(L.logits, -7.0)
+    lib.moe_layer(L.x, L.wr, lg2, w.T, w.H, w.I, w.E, w.K, w.g, lib.MOE_ROUTE_RENORM if renorm else 0, ids2, w2,
+                  L.table, L.slots, L.stride, L.shared, y2, run.ws, run.ws_bytes, run.status)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    assert torch.equal(lg2.view(torch.int32), lg1.view(torch.int32))
+    assert torch.equal(ids2, ids1)
+    assert np.array_equal(ids2.cpu().numpy(), ids_ref)
+    assert torch.equal(w2.view(torch.int32), w1.view(torch.int32))
+    assert torch.equal(y2.view(torch.int16), y1.view(torch.int16))
+
+
+def test_layer_decode_matches_oracle():
+    w = gen.WORKLOADS["decode_t1_h4096_e256_k8_i1536_x48"]
+    layer = 11
+    xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
+    y_ref, ids_ref, w_ref, _ = oracle_layer(w, layer, xb)
+    L = harness.make_layer(w, layer, DEV, slots=64, experts=sorted(set(ids_ref.ravel().tolist())), place_seed=4,
+                           x_bits=xb)
+    run = harness.LayerRunner(w, DEV)
+    lib.moe_layer(L.x, L.wr, L.logits, w.T, w.H, w.I, w.E, w.K, w.g, 0, run.ids, run.wts, L.table, L.slots,
+                  L.stride, L.shared, run.y, run.ws, run.ws_bytes, run.status)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
+    assert np.abs(run.wts.cpu().numpy() - w_ref).max() <= 1e-5
+    check_close(y_f64(run.y), y_ref, "  moe_layer decode layer 11")
+
+
 # ------------------------------------------------------------------ edge cases and errors
 
 
