@@ -125,7 +125,7 @@ def decode_leg(a, dev):
     bytes_down = w.K * mat_bytes + w.T * w.K * w.I * 2 + w.T * w.H * 2  # experts + h (fp16) + y
     bytes_layer = bytes_router + w.K * blob + w.T * w.H * 2 * 2
 
-    def step():  # one token through the layer stack: moe_layer per layer
+    def step():  # one token through the layer stack: one moe_layer call per layer
         for L in stacks:
             run.layer(L, stream)
 

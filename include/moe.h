@@ -152,18 +152,12 @@ int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T,
 
 /* ------------------------------------------------------------------ whole layer
  * moe_layer: moe_route(x, w_router, logits, T, H, E, K, route_flags, ids, w)
- * then moe_expert_ffn(x, ids, w, ..., ffn_flags) in one call, with the same
- * arguments, the same checks and the same results bit for bit; ids and w are
- * outputs ("Strata on a Mac", Switches: the router GEMV and moe_route run
- * before the expert FFN; there the fused router + moe_route dispatch hands the
- * logits to the last threadgroup through a device counter). Here no workgroup
- * waits for another: for one token on the single-token decode kernels with
- * E <= 256, every workgroup of the first FFN kernel selects the experts from
- * the logits itself (the same selection code as moe_route) and workgroup 0
- * writes ids and w, which saves the separate selection launch; other shapes
- * run the two calls in turn. For a resident arena: a paged caller needs ids on
- * the host before the FFN and uses moe_route, arena_map_slots and
- * arena_fill_async, then moe_expert_ffn. */
+ * then moe_expert_ffn(x, ids, w, ..., ffn_flags) in one call on one stream,
+ * with the same arguments, checks and results ("Strata on a Mac", Switches:
+ * the router GEMV and moe_route run before the expert FFN); ids and w are
+ * outputs. A route error returns before the FFN is enqueued. For a resident
+ * arena: a paged caller needs ids on the host before the FFN and uses
+ * moe_route, arena_map_slots and arena_fill_async, then moe_expert_ffn. */
 int moe_layer(const uint16_t* x, const float* w_router, float* logits, int T, int H, int I, int E, int K, int g,
               unsigned route_flags, int32_t* ids, float* w, const int32_t* slot_table, const void* slots,
               size_t stride, const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,

@@ -70,13 +70,10 @@ namespace {
 
 // Shared argument checks and dispatch of one stage (0 = gate/up, 1 = down +
 // combine, 2 = both) of the expert FFN.
-// fused_logits (moe_layer only): the single-token decode kernels select the
-// experts from these logits inside stage 0 and write ids / w.
 int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K, int g,
                      const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
                      uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
-                     moe_stream_t stream, int stage, const float* fused_logits = nullptr,
-                     unsigned route_flags = 0) {
+                     moe_stream_t stream, int stage) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
   if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED)) return MOE_EINVAL;
   if ((flags & MOE_FORCE_GEMV) && (flags & MOE_FORCE_GROUPED)) return MOE_EINVAL;
@@ -110,13 +107,6 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
   a.status = dev_status;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool dec1 = !grouped && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
-  if (fused_logits) {
-    if (!dec1 || E > moe::kFusedSelectMaxE) return MOE_EUNSUP;
-    a.logits = fused_logits;
-    a.route_flags = route_flags;
-    a.ids_out = const_cast<int32_t*>(ids);
-    a.w_out = const_cast<float*>(w);
-  }
   for (int st = 0; st < 2; ++st) {
     if (stage != 2 && stage != st) continue;
     hipError_t err;
@@ -158,38 +148,12 @@ extern "C" int moe_ffn_down(const uint16_t* x, const int32_t* ids, const float* 
                           dev_status, flags, stream, 1);
 }
 
-namespace {
-
-bool layer_fuses_select(int T, int H, int I, int E, int K, const void* shared_blob, unsigned ffn_flags) {
-  return T == 1 && !ffn_uses_grouped(T, ffn_flags) && E <= moe::kFusedSelectMaxE && moe::shape_ok(H, I, moe::kGroup) &&
-         gemv_shape_ok(T, H, I, K) && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
-}
-
-}  // namespace
-
 extern "C" int moe_layer(const uint16_t* x, const float* w_router, float* logits, int T, int H, int I, int E, int K,
                          int g, unsigned route_flags, int32_t* ids, float* w, const int32_t* slot_table,
                          const void* slots, size_t stride, const void* shared_blob, uint16_t* y, void* ws,
                          size_t ws_bytes, int32_t* dev_status, unsigned ffn_flags, moe_stream_t stream) {
-  if (g != moe::kGroup || !layer_fuses_select(T, H, I, E, K, shared_blob, ffn_flags)) {
-    const int rs = moe_route(x, w_router, logits, T, H, E, K, route_flags, ids, w, stream);
-    if (rs != MOE_OK) return rs;
-    return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
-                            dev_status, ffn_flags, stream, 2);
-  }
-  // the same argument checks as moe_route, then the router GEMV alone
-  if (E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return MOE_EINVAL;
-  if (route_flags & ~(unsigned)MOE_ROUTE_RENORM) return MOE_EINVAL;
-  if (w_router) {
-    if (!x || H <= 0) return MOE_EINVAL;
-    if (H % moe::kGroup || H > 8192) return MOE_EUNSUP;
-  }
-  // check the FFN arguments before anything is enqueued: stage 3 does nothing
-  const int chk = expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws,
-                                   ws_bytes, dev_status, ffn_flags, stream, 3, logits, route_flags);
-  if (chk != MOE_OK) return chk;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (w_router && moe::launch_router_gemv(x, w_router, logits, T, H, E, s) != hipSuccess) return MOE_EHIP;
+  const int rs = moe_route(x, w_router, logits, T, H, E, K, route_flags, ids, w, stream);
+  if (rs != MOE_OK) return rs;
   return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
-                          dev_status, ffn_flags, stream, 2, logits, route_flags);
+                          dev_status, ffn_flags, stream, 2);
 }

@@ -110,14 +110,11 @@ __device__ inline int xcd_item(int bid, int n_items) {
 
 // ------------------------------------------------------------------ gate/up
 // GPL = groups per lane = ceil(GW / 8) with GW = ceil(G / 4) groups per wave.
-// SEL: the workgroup first selects the token's experts from a.logits (wave 0,
-// wave_select, bit-identical to moe_route); workgroup 0 writes them out.
-template <int GPL, bool SEL>
+template <int GPL>
 __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
   // LDS per wave: x slice as fp16 pairs [GW][16] dwords + group corrections [GW]
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float part[2][kWaves][8];
-  __shared__ int32_t sel_id[kMaxK];
   const int H = a.H, I = a.I, K = a.K;
   const int G = H / kGroup;
   const int GW = (G + kWaves - 1) / kWaves;
@@ -141,24 +138,7 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
     q = q < G * 4 ? q : G * 4 - 1;
     xv[v] = reinterpret_cast<const uint4*>(a.x)[q];
   }
-  const int32_t* ids = a.ids;
-  if constexpr (SEL) {
-    if (wave == 0) {
-      int32_t id;
-      float wt;
-      wave_select<kFusedSelectMaxE / 64>(a.logits, a.E, K, a.route_flags, lane, id, wt);
-      if (lane < K) {
-        sel_id[lane] = id;
-        if (blockIdx.x == 0) {
-          a.ids_out[lane] = id;
-          a.w_out[lane] = wt;
-        }
-      }
-    }
-    __syncthreads();
-    ids = sel_id;
-  }
-  const uint8_t* blob = dec_unit_blob(a, u, has_shared, ids);
+  const uint8_t* blob = dec_unit_blob(a, u, has_shared, a.ids);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
   const int n = hb * 8 + r;
@@ -475,13 +455,8 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
     const int grid = n_units * (a.I / 8);
 #define GU(N)                                                                                       \
   do {                                                                                              \
-    if (a.logits) {                                                                                 \
-      set_lds_limit(reinterpret_cast<const void*>(&dec_gateup_kernel<N, true>), lds);               \
-      hipLaunchKernelGGL((dec_gateup_kernel<N, true>), dim3(grid), dim3(kThreads), lds, s, a);      \
-    } else {                                                                                        \
-      set_lds_limit(reinterpret_cast<const void*>(&dec_gateup_kernel<N, false>), lds);              \
-      hipLaunchKernelGGL((dec_gateup_kernel<N, false>), dim3(grid), dim3(kThreads), lds, s, a);     \
-    }                                                                                               \
+    set_lds_limit(reinterpret_cast<const void*>(&dec_gateup_kernel<N>), lds);                       \
+    hipLaunchKernelGGL((dec_gateup_kernel<N>), dim3(grid), dim3(kThreads), lds, s, a);              \
   } while (0)
     if (gpl <= 1) GU(1);
     else if (gpl <= 2) GU(2);

@@ -78,15 +78,7 @@ struct FfnArgs {
   uint8_t* ws;
   size_t ws_bytes;
   int32_t* status;
-  // single-token decode only: when logits is set, the gate/up kernel selects
-  // the top K itself (route_flags as moe_route) and workgroup 0 writes them to
-  // ids_out / w_out, the buffers ids and w point to
-  const float* logits;
-  unsigned route_flags;
-  int32_t* ids_out;
-  float* w_out;
 };
-constexpr int kFusedSelectMaxE = 256;  // experts per token the fused selection covers (4 per lane)
 
 // Each path launches in two stages: stage 0 = gate/up (h into the workspace),
 // stage 1 = down + combine (y).
@@ -95,7 +87,6 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, int stage, hipStream_t s);
 
 // single-token decode kernels (a specialisation of the GEMV path)
 bool decode1_supported(int T, int H, int I, int K, bool has_shared);
-// stage 0 selects the experts itself when a.logits is set (E <= kFusedSelectMaxE)
 hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s);
 
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);

@@ -68,6 +68,53 @@ __global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __rest
   }
 }
 
+// Single token: one workgroup per expert; thread t covers the 16 columns
+// 16 (t + 256 j) for j = 0, 1 (H <= 8192), with four independent fp64
+// accumulators (one per float4 of the row), added in a fixed order, then the
+// lanes and the waves as above; one rounding to fp32.
+__global__ void __launch_bounds__(256) router_gemv1_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ wr, float* __restrict__ logits,
+                                                           int H, int E) {
+  __shared__ double part[4];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* w = wr + (size_t)e * H;
+  float4 wv[2][4];
+  uint4 xv[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = 16 * (tid + 256 * j);
+    const bool ok = c < H;
+    const int cc = ok ? c : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wv[j][q] = reinterpret_cast<const float4*>(w + cc)[q];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) xv[j][q] = reinterpret_cast<const uint4*>(x + cc)[q];
+    if (!ok) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) xv[j][q] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x01 = q & 1 ? (q & 2 ? xv[j][1].z : xv[j][0].z) : (q & 2 ? xv[j][1].x : xv[j][0].x);
+      const uint32_t x23 = q & 1 ? (q & 2 ? xv[j][1].w : xv[j][0].w) : (q & 2 ? xv[j][1].y : xv[j][0].y);
+      acc[q] = fma((double)bf16_lo(x01), (double)wv[j][q].x, acc[q]);
+      acc[q] = fma((double)bf16_hi(x01), (double)wv[j][q].y, acc[q]);
+      acc[q] = fma((double)bf16_lo(x23), (double)wv[j][q].z, acc[q]);
+      acc[q] = fma((double)bf16_hi(x23), (double)wv[j][q].w, acc[q]);
+    }
+  }
+  double a = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  a = wave_sum_f64(a);
+  if (lane == 0) part[wave] = a;
+  __syncthreads();
+  if (tid == 0) logits[e] = (float)(((part[0] + part[1]) + part[2]) + part[3]);
+}
+
 // One wave per token (the selection is wave_select, shared with the fused decode path).
 template <int EPL>
 __global__ void __launch_bounds__(64) route_select_kernel(const float* __restrict__ logits, int T, int E, int K,
@@ -100,6 +147,10 @@ __global__ void __launch_bounds__(64) table_update_kernel(int32_t* table, TableU
 
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H, int E,
                               hipStream_t s) {
+  if (T == 1) {
+    hipLaunchKernelGGL(router_gemv1_kernel, dim3(E), dim3(256), 0, s, x, wr, logits, H, E);
+    return hipGetLastError();
+  }
   dim3 grid(E, (T + kRouterTok - 1) / kRouterTok);
   hipLaunchKernelGGL(router_gemv_kernel, grid, dim3(256), 0, s, x, wr, logits, T, H, E);
   return hipGetLastError();

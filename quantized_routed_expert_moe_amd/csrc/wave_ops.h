@@ -109,12 +109,25 @@ __device__ inline float key_logit(uint64_t k) {
 }
 __device__ inline int32_t key_id(uint64_t k) { return (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu)); }
 
+// The maximum over the 64 lanes, on every lane.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, ror_u32<1>(v));
+  v = max(v, ror_u32<2>(v));
+  v = max(v, ror_u32<4>(v));
+  v = max(v, ror_u32<8>(v));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)s16[0], (uint32_t)s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)s32[0], (uint32_t)s32[1]);
+}
+
 // Softmax top-k of one token's E logits l[0..E) by one whole wave (E <= 64 * EPL,
 // K <= 64). Lane k < K gets rank k: its expert id and its weight
 // softmax(l)[id] (divided by the sum of the K weights with MOE_ROUTE_RENORM).
 // Lane l holds the keys of experts l, l+64, ... sorted descending in
-// registers; K rounds of a wave-wide maximum each take the next expert in rank
-// order from its owner lane.
+// registers; each of K rounds takes the wave-wide maximum of the lanes' first
+// keys (on the 32-bit logit image; among equal images the full key, i.e. the
+// lowest id, decides) and pops it from its owner lane.
 template <int EPL>
 __device__ inline void wave_select(const float* __restrict__ l, int E, int K, unsigned flags, int lane, int32_t& id,
                                    float& wt) {
@@ -124,7 +137,7 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     lg[i] = e < E ? l[e] : 0.0f;
-    key[i] = e < E ? route_key(lg[i], e) : 0ull;
+    key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
   }
   // local descending sort (odd-even transposition)
 #pragma unroll
@@ -138,8 +151,17 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
   }
   uint64_t mine = 0;  // lane k keeps the winner of rank k
   for (int k = 0; k < K; ++k) {
-    const uint64_t best = wave_max_u64(key[0]);
-    if (key[0] == best) {
+    const uint32_t hi = (uint32_t)(key[0] >> 32);
+    const uint32_t m = wave_max_u32(hi);
+    uint64_t owners = __ballot(hi == m);
+    if (__builtin_popcountll(owners) > 1) {  // equal logits: the highest full key (lowest id) wins
+      const uint64_t best = wave_max_u64(hi == m ? key[0] : 0ull);
+      owners = __ballot(key[0] == best);
+    }
+    const int src = (int)__builtin_ctzll(owners);
+    const uint64_t best = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(key[0] >> 32), src) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)key[0], src);
+    if (lane == src) {
 #pragma unroll
       for (int i = 0; i + 1 < EPL; ++i) key[i] = key[i + 1];
       key[EPL - 1] = 0;

@@ -207,16 +207,15 @@ def test_ffn_ragged_shapes(w):
         (gen.Workload("dec_t1_h256_e64_k4_i512", 1, 256, 64, 4, 512, 1, 64, "gemv", 31), True),
         (gen.Workload("dec_t1_h512_e256_k32_i512_shared", 1, 512, 256, 32, 512, 1, 256, "gemv", 32, shared=True),
          False),
-        # more experts than the fused selection covers: moe_layer runs the two calls in turn
         (gen.Workload("dec_t1_h256_e512_k8_i512", 1, 256, 512, 8, 512, 1, 512, "normal", 33), False),
-        # several tokens: the two calls in turn
         (gen.Workload("t5_h256_e64_k4_i512", 5, 256, 64, 4, 512, 1, 64, "gemv", 34), False),
     ],
     ids=lambda v: v.name if hasattr(v, "name") else f"renorm{int(v)}",
 )
 def test_layer_equals_route_then_ffn_bitwise(w, renorm):
-    """moe_layer (selection fused into the first FFN kernel for one token) gives the
-    bits of moe_route followed by moe_expert_ffn: logits, ids, w and y."""
+    """moe_layer gives the bits of moe_route followed by moe_expert_ffn: logits,
+    ids, w and y, for one token and for several, with and without renormalised
+    weights, router GEMV or logits in, with and without a shared expert."""
     layer = 3
     say(f"moe_layer {w.name} renorm={renorm}")
     xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
