@@ -77,6 +77,38 @@ def stage_times(calls, stream, reps=1):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+# HBM traffic per launch of the decode kernels, from the committed rocprofv3
+# counter summary; reported only while the kernel sources still hash to the value
+# recorded there (a changed kernel has not been measured).
+TRAFFIC_SUMMARY = "profiles/decode_t1_h4096_e256_k8_i1536_x48_hbm_traffic.md"
+DECODE_KERNEL_SOURCES = ("quantized_routed_expert_moe_amd/csrc/ffn_decode.hip",
+                         "quantized_routed_expert_moe_amd/csrc/wave_ops.h",
+                         "quantized_routed_expert_moe_amd/csrc/moe_internal.h")
+
+
+def decode_traffic():
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        text = open(os.path.join(root, TRAFFIC_SUMMARY)).read()
+    except OSError:
+        return {}
+    h = hashlib.sha256()
+    for p in DECODE_KERNEL_SOURCES:
+        h.update(open(os.path.join(root, p), "rb").read())
+    rec = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch "):
+            k, v = line[len("traffic_bytes_per_launch "):].split(":")
+            rec[k.strip()] = int(v)
+        elif line.startswith("kernel_sources_sha256:"):
+            rec["sha"] = line.split(":")[1].strip()
+    if rec.get("sha") != h.hexdigest()[:16]:
+        return {}
+    return rec
+
+
 # ------------------------------------------------------------------ decode (headline)
 
 
@@ -163,16 +195,35 @@ def decode_leg(a, dev):
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / a.steps
 
-    # per-stage durations with HIP events on the launch stream, every layer, 3 passes
-    t = {"route": [], "gate_up": [], "down": []}
-    for _ in range(3):
+    # per-stage durations: each stage launched for every layer back to back on the
+    # launch stream (each layer with its own routed experts), 3 passes, HIP events
+    # around the batch -> mean per launch
+    routed = []
+    with torch.cuda.stream(stream):
         for L in stacks:
-            st = stage_times([("route", lambda L=L: run.route(L, stream)),
-                              ("gate_up", lambda L=L: run.ffn(L, stream, stage="gate_up")),
-                              ("down", lambda L=L: run.ffn(L, stream, stage="down"))], stream)
-            for k in t:
-                t[k].append(st[k])
-    us = {k: float(np.mean(v)) for k, v in t.items()}
+            run.route(L, stream)
+            routed.append((run.ids.clone(), run.wts.clone()))
+    stream.synchronize()
+    calls = {
+        "route": lambda i, L: run.route(L, stream),
+        "gate_up": lambda i, L: run.ffn(L, stream, stage="gate_up", ids=routed[i][0], wts=routed[i][1]),
+        "down": lambda i, L: run.ffn(L, stream, stage="down", ids=routed[i][0], wts=routed[i][1]),
+    }
+    us = {}
+    for name, f in calls.items():
+        b0, b1 = ev(), ev()
+        with torch.cuda.stream(stream):
+            for i, L in enumerate(stacks):  # warm
+                f(i, L)
+            b0.record(stream)
+            for _ in range(3):
+                for i, L in enumerate(stacks):
+                    f(i, L)
+            b1.record(stream)
+        stream.synchronize()
+        us[name] = b0.elapsed_time(b1) * 1e3 / (3 * len(stacks))
+    if int(run.status.item()) != 0:
+        raise RuntimeError(f"device status {int(run.status.item())}")
     gu_gbs = bytes_gate_up / (us["gate_up"] * 1e-6) / 1e9
     dn_gbs = bytes_down / (us["down"] * 1e-6) / 1e9
     layer_gbs = bytes_layer * w.layers / (ms_step * 1e-3) / 1e9
@@ -466,6 +517,7 @@ def main():
         log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written")
         del src, dst
     w, d = decode_leg(a, dev)
+    traffic = decode_traffic()
     out = {
         "metric": "MoE-layer decode tokens/s (one token through 48 layers) + achieved HBM GB/s",
         "value": round(d["tok_s"], 2),
@@ -501,7 +553,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(d["gu_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic.get("dec_gateup_kernel"),
             "bytes_per_launch": d["bytes"]["gate_up"],
         },
         "roofline_down": {
@@ -511,6 +563,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(d["dn_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic.get("dec_down_kernel"),
             "bytes_per_launch": d["bytes"]["down"],
         },
         "wall_s_timed": round(d["wall"], 4),

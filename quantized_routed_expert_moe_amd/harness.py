@@ -115,12 +115,13 @@ class LayerRunner:
         lib.moe_route(L.x, L.wr, L.logits, w.T, w.H, w.E, w.K, lib.MOE_ROUTE_RENORM if renorm else 0, self.ids,
                       self.wts, stream)
 
-    def ffn(self, L: DeviceLayer, stream=None, y=None, stage="both"):
-        """Expert FFN of the layer: stage "both", "gate_up" or "down"."""
+    def ffn(self, L: DeviceLayer, stream=None, y=None, stage="both", ids=None, wts=None):
+        """Expert FFN of the layer: stage "both", "gate_up" or "down" (ids / wts default to the last route)."""
         w = self.w
         fn = {"both": lib.moe_expert_ffn, "gate_up": lib.moe_ffn_gate_up, "down": lib.moe_ffn_down}[stage]
-        fn(L.x, self.ids, self.wts, w.T, w.H, w.I, w.E, w.K, w.g, L.table, L.slots, L.stride, L.shared,
-           self.y if y is None else y, self.ws, self.ws_bytes, self.status, self.flags, stream)
+        fn(L.x, self.ids if ids is None else ids, self.wts if wts is None else wts, w.T, w.H, w.I, w.E, w.K, w.g,
+           L.table, L.slots, L.stride, L.shared, self.y if y is None else y, self.ws, self.ws_bytes, self.status,
+           self.flags, stream)
 
     def layer(self, L: DeviceLayer, stream=None, renorm=False):
         """The whole layer in one call (moe_layer): same results as route() then ffn()."""
