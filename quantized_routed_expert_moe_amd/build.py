@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["api.cpp", "pack.cpp", "arena.cpp", "route.hip", "ffn_gemv.hip", "ffn_decode.hip", "ffn_grouped.hip"]
+SOURCES = ["api.cpp", "pack.cpp", "arena.cpp", "route.hip", "ffn_gemv.hip", "ffn_batched.hip", "ffn_decode.hip",
+           "ffn_grouped.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

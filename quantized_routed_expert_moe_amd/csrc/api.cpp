@@ -63,6 +63,7 @@ extern "C" int moe_route(const uint16_t* x, const float* w_router, float* logits
 extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int I, int E, int K, int has_shared, unsigned flags) {
   if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0) return 0;
   if (ffn_uses_grouped(T, flags)) return moe::grouped_workspace_bytes(T, H, I, E, K, has_shared);
+  if (moe::batched_supported(T, H, I, K)) return moe::batched_workspace_bytes(T, H, I, E, K, has_shared);
   return moe::gemv_workspace_bytes(T, H, I, K, has_shared);
 }
 
@@ -107,6 +108,7 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
   a.status = dev_status;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool dec1 = !grouped && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
+  const bool bat = !grouped && moe::batched_supported(T, H, I, K);
   for (int st = 0; st < 2; ++st) {
     if (stage != 2 && stage != st) continue;
     hipError_t err;
@@ -114,6 +116,8 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
       err = moe::launch_ffn_grouped(a, st, s);
     else if (dec1)
       err = moe::launch_ffn_decode1(a, st, s);
+    else if (bat)
+      err = moe::launch_ffn_batched(a, st, s);
     else
       err = moe::launch_ffn_gemv(a, st, s);
     if (err == hipErrorNotSupported) return MOE_EUNSUP;

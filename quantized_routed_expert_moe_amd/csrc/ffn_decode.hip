@@ -51,35 +51,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ inline float dot2h(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-}
-
-// d + the 8 codes of w times the activation pairs x0..x3 of the same columns.
-__device__ inline float code_dot(uint32_t w, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, float d) {
-  const uint32_t w8 = w >> 8;
-  d = dot2h((w & 0x000F000Fu) | 0x64006400u, x0, d);   // columns +0, +1
-  d = dot2h((w & 0x00F000F0u) | 0x54005400u, x1, d);   // +2, +3
-  d = dot2h((w8 & 0x000F000Fu) | 0x64006400u, x2, d);  // +4, +5
-  d = dot2h((w8 & 0x00F000F0u) | 0x54005400u, x3, d);  // +6, +7
-  return d;
-}
-
-__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// fp16 bits of the fp32 value v (round to nearest even); *bad set when it overflows.
-__device__ inline uint32_t to_f16_bits(float v, bool* bad) {
-  const _Float16 h = (_Float16)v;
-  const uint32_t b = __builtin_bit_cast(uint16_t, h);
-  if ((b & 0x7FFFu) == 0x7C00u) *bad = true;
-  return b;
-}
-
-__device__ inline float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
-__device__ inline float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
-
 // Blob of unit u (u = 0 is the shared expert when present) or nullptr with the
 // status word set; ids = the token's routed experts in rank order.
 __device__ inline const uint8_t* dec_unit_blob(const FfnArgs& a, int u, bool has_shared, const int32_t* ids) {

@@ -85,6 +85,11 @@ struct FfnArgs {
 size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared);
 hipError_t launch_ffn_gemv(const FfnArgs& a, int stage, hipStream_t s);
 
+// small-batch kernels (2 <= T <= 32, shapes batched_supported admits)
+bool batched_supported(int T, int H, int I, int K);
+size_t batched_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
+hipError_t launch_ffn_batched(const FfnArgs& a, int stage, hipStream_t s);
+
 // single-token decode kernels (a specialisation of the GEMV path)
 bool decode1_supported(int T, int H, int I, int K, bool has_shared);
 hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s);

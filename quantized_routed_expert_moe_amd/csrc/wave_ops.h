@@ -183,4 +183,52 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
   wt = w;
 }
 
+// ------------------------------------------------------------------ int4 codes x fp16 activations
+// A code dword w holds 8 offset-binary nibbles u = q + 8 (see the blob layout);
+// its four fp16 pairs, one AND-OR each (two also need w >> 8), are exact:
+//   A pairs (nibbles at bits 0..3 / 16..19 of w or w >> 8): 0x6400 | u  = 1024 + u = q + 1032
+//   B pairs (nibbles at bits 4..7 / 20..23):                 0x5400 | 16u = 64 + u  = q + 72
+// Pair k of dword d covers columns 8d + 2k and 8d + 2k + 1 (A: k = 0, 2; B: k = 1, 3).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+// d + the 8 codes of w times the activation pairs x0..x3 of the same columns.
+__device__ inline float code_dot(uint32_t w, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, float d) {
+  const uint32_t w8 = w >> 8;
+  d = dot2h((w & 0x000F000Fu) | 0x64006400u, x0, d);   // columns +0, +1
+  d = dot2h((w & 0x00F000F0u) | 0x54005400u, x1, d);   // +2, +3
+  d = dot2h((w8 & 0x000F000Fu) | 0x64006400u, x2, d);  // +4, +5
+  d = dot2h((w8 & 0x00F000F0u) | 0x54005400u, x3, d);  // +6, +7
+  return d;
+}
+
+// The 16 pairs of a 16-byte code chunk (32 columns), pair k for activation dword k.
+__device__ inline void code_pairs(const uint4& c, uint32_t (&out)[16]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w8 = w[d] >> 8;
+    out[4 * d + 0] = (w[d] & 0x000F000Fu) | 0x64006400u;
+    out[4 * d + 1] = (w[d] & 0x00F000F0u) | 0x54005400u;
+    out[4 * d + 2] = (w8 & 0x000F000Fu) | 0x64006400u;
+    out[4 * d + 3] = (w8 & 0x00F000F0u) | 0x54005400u;
+  }
+}
+
+__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// fp16 bits of the fp32 value v (round to nearest even); *bad set when it overflows.
+__device__ inline uint32_t to_f16_bits(float v, bool* bad) {
+  const _Float16 h = (_Float16)v;
+  const uint32_t b = __builtin_bit_cast(uint16_t, h);
+  if ((b & 0x7FFFu) == 0x7C00u) *bad = true;
+  return b;
+}
+
+__device__ inline float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
+__device__ inline float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+
 }  // namespace moe
