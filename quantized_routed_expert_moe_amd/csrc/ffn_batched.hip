@@ -35,7 +35,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTB = 4;                 // pairs per chunk
+constexpr int kTB = 4;                 // pairs per gate/up chunk
+constexpr int kTBD = 8;                // pairs per down chunk
+constexpr int kUnitPairs = 64;         // pairs one unit can hold (a routed unit has at most T)
 constexpr int kPlanThreads = 1024;
 constexpr int kBatMaxPairs = 512;      // routed pairs T*K the plan covers
 
@@ -46,11 +48,13 @@ __host__ __device__ inline int bat_umax(int T, int K, int E, int has_shared) {
 }
 __host__ __device__ inline int bat_pmax(int T, int K, int has_shared) { return T * K + (has_shared ? T : 0); }
 
-// Workspace: plan ints [n_units | rec[U][4] | pair_list[P]], x16 fp16 [T][H],
-// xc fp32 [T][G] (per-group corrections of x16), h fp16 [P][I] with rows in
-// unit order (row i = pair_list[i]), o fp32 [P][H] with rows in pair order.
-// rec[u] = {slot (-1: the shared expert, -2: not usable), first row of the
-// unit in pair_list, pair count (0 past the last unit), expert}.
+// Workspace: plan ints [n_units | rec[U][4] | ptab[U][kUnitPairs]], x16 fp16
+// [T][H], xc fp32 [T][G] (per-group corrections of x16), h fp16 [P][I] with
+// rows in unit order (row rec[u].y + i is pair ptab[u][i]), o fp32 [P][H] with
+// rows in pair order. rec[u] = {slot (-1: the shared expert, -2: not usable),
+// first h row of the unit, pair count (0 past the last unit), expert}; the
+// pair table has a fixed stride, so a workgroup loads its unit's record and
+// pairs in one round trip.
 struct BatWs {
   size_t x16_off, xc_off, h_off, o_off, bytes;
   int U, P;
@@ -59,7 +63,7 @@ __host__ __device__ inline BatWs bat_ws(int T, int H, int I, int E, int K, int h
   BatWs w;
   w.U = bat_umax(T, K, E, has_shared);
   w.P = bat_pmax(T, K, has_shared);
-  const size_t plan_ints = 4 + (size_t)w.U * 4 + w.P;
+  const size_t plan_ints = 4 + (size_t)w.U * (4 + kUnitPairs);
   w.x16_off = align256(plan_ints * 4);
   w.xc_off = align256(w.x16_off + (size_t)T * H * 2);
   w.h_off = align256(w.xc_off + (size_t)T * (H / kGroup) * 4);
@@ -71,21 +75,15 @@ __host__ __device__ inline BatWs bat_ws(int T, int H, int I, int E, int K, int h
 struct PlanView {
   int* n_units;
   int4* rec;
-  int* pair_list;
+  int* ptab;
 };
 __device__ inline PlanView plan_view(uint8_t* ws, int U, int P) {
   int* p = reinterpret_cast<int*>(ws);
   PlanView v;
   v.n_units = p;
   v.rec = reinterpret_cast<int4*>(p + 4);  // 16-byte aligned
-  v.pair_list = p + 4 + 4 * U;
+  v.ptab = p + 4 + 4 * U;
   return v;
-}
-
-// The plan's unit count through the scalar cache: it is written by the plan
-// kernel and read-only for the kernels after it.
-__device__ inline int plan_n_units(const PlanView& pl) {
-  return *(const __attribute__((address_space(4))) int*)(pl.n_units);
 }
 
 __device__ inline const uint8_t* rec_blob(const FfnArgs& a, int slot) {
@@ -144,7 +142,6 @@ __device__ inline void plan_convert_x(const FfnArgs& a, const BatWs& W, int i) {
 // ------------------------------------------------------------------ plan
 __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
   __shared__ int first[kMaxE];  // lowest pair using expert e, then the unit of expert e
-  __shared__ int unit_of_pair[kBatMaxPairs];
   __shared__ int cnt[kBatMaxPairs + 1];
   __shared__ int uoff[kBatMaxPairs + 1];
   __shared__ int unit_expert_lds[kBatMaxPairs + 1];
@@ -180,13 +177,14 @@ __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
   }
   __syncthreads();
   const int up = valid ? first[e] : -1;
-  if (p < P) unit_of_pair[p] = up;
-  if (valid) atomicAdd(&cnt[up], 1);  // integer counts: the order of additions does not matter
+  // the pair's place in its unit: any order serves, as every pair's arithmetic
+  // is its own and its output row is its pair index
+  const int rank = valid ? atomicAdd(&cnt[up], 1) : 0;
+  if (valid) {
+    if (rank < kUnitPairs) pl.ptab[up * kUnitPairs + rank] = p;
+    else *a.status = MOE_EUNSUP;  // only with an expert repeated within a token's ids
+  }
   __syncthreads();
-  // rank of the pair among its unit's pairs (pair order)
-  int rank = 0;
-  if (valid)
-    for (int q = 0; q < p; ++q) rank += unit_of_pair[q] == up;
   // unit offsets: the shared unit holds T pairs, routed units their counts
   const int n_units = base + n_routed;
   const int c = tid < n_units ? (has_shared && tid == 0 ? T : cnt[tid]) : 0;
@@ -194,8 +192,7 @@ __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
   const int off = block_exclusive_scan(c, wsum, &total);
   if (tid < n_units) uoff[tid] = off;
   __syncthreads();
-  if (valid) pl.pair_list[uoff[up] + rank] = p;
-  if (has_shared && tid < T) pl.pair_list[tid] = T * K + tid;
+  if (has_shared && tid < T) pl.ptab[tid] = T * K + tid;
   // unit records: the slot is resolved here once for every workgroup of the layer
   if (tid == 0) *pl.n_units = n_units;
   for (int u = tid; u < W.U; u += kPlanThreads) {
@@ -217,6 +214,23 @@ __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ unit header
+// The record of unit u and, in lane i, its pair i (lanes past the count: 0).
+// One round trip; a workgroup of a unit past the plan's last leaves at once.
+struct UnitHead {
+  int slot, p0, np, my_pair;
+};
+__device__ inline UnitHead unit_head(const PlanView& pl, int u, int lane) {
+  const int4 rc = pl.rec[u];
+  const int pv = pl.ptab[u * kUnitPairs + lane];
+  UnitHead h;
+  h.slot = rc.x;
+  h.p0 = rc.y;
+  h.np = rc.z;
+  h.my_pair = lane < rc.z ? pv : 0;
+  return h;
+}
+
 // ------------------------------------------------------------------ gate/up
 // GPL = groups per lane = ceil(GW / 8) with GW = ceil(G / 4) groups per wave.
 template <int GPL>
@@ -235,138 +249,155 @@ __global__ void __launch_bounds__(kThreads) bat_gateup_kernel(FfnArgs a) {
   const BatWs W = bat_ws(T, H, I, a.E, K, has_shared);
   const PlanView pl = plan_view(a.ws, W.U, W.P);
   // one item per workgroup; a unit's items are consecutive workgroups, so its rows
-  // stream from HBM together, and the workgroups past the plan's last unit leave at once
+  // stream from HBM together
   const int n_hb = I / 8;
-  {
-    const int item = blockIdx.x;
-    const int u = item / n_hb, hb = item % n_hb;
-    if (u >= plan_n_units(pl)) return;
-    const int4 rc = pl.rec[u];
-    const int p0 = rc.y, np = rc.z;
-    uint32_t* xs = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * kTB * (GW * 17);
-    const int j0 = wave * GW;
-    const int gw_here = G - j0 < GW ? (G - j0 > 0 ? G - j0 : 0) : GW;
-    const uint8_t* blob = rec_blob(a, rc.x);
-    const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
-    if (np > 64) {  // only with an expert repeated within a token's ids (moe_route never does that)
-      if (tid == 0) *a.status = MOE_EUNSUP;
-      return;
+  const int u = blockIdx.x / n_hb, hb = blockIdx.x % n_hb;
+  const UnitHead uh = unit_head(pl, u, lane);
+  const int p0 = uh.p0, np = uh.np;
+  if (np == 0) return;
+  if (np > kUnitPairs) {
+    if (tid == 0) *a.status = MOE_EUNSUP;
+    return;
+  }
+  uint32_t* xs = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * kTB * (GW * 17);
+  const int j0 = wave * GW;
+  const int gw_here = G - j0 < GW ? (G - j0 > 0 ? G - j0 : 0) : GW;
+  const uint8_t* blob = rec_blob(a, uh.slot);
+  const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
+  const uint4* x16 = reinterpret_cast<const uint4*>(a.ws + W.x16_off);
+  const float* xc = reinterpret_cast<const float*>(a.ws + W.xc_off);
+  // a chunk's x slices: uint4 v of a token's slice is columns 8 (lane + 64 v) .. +7
+  // of the wave's groups; every token's loads are issued before any is stored
+  constexpr int XQ = (GPL + 1) / 2;  // uint4 per lane and token (GW <= 8 * GPL groups)
+  uint4 xv[kTB][XQ];
+  float cv[kTB];
+  auto load_x = [&](int c0) {
+    const int tc = np - c0 < kTB ? np - c0 : kTB;
+#pragma unroll
+    for (int ti = 0; ti < kTB; ++ti) {
+      const int t = pair_token(__builtin_amdgcn_readlane(uh.my_pair, c0 + (ti < tc ? ti : tc - 1)), T, K);
+#pragma unroll
+      for (int v = 0; v < XQ; ++v) {
+        int q = j0 * 4 + lane + 64 * v;
+        q = q < G * 4 ? q : G * 4 - 1;
+        xv[ti][v] = x16[(size_t)t * (H / 8) + q];
+      }
+      int jj = j0 + (lane < GW ? lane : 0);
+      jj = jj < G ? jj : G - 1;
+      cv[ti] = xc[(size_t)t * G + jj];
     }
-    const int my_pair = pl.pair_list[p0 + (lane < np ? lane : np - 1)];  // lane i: the unit's pair i
-    const BlobLayout BL = blob_layout(H, I);
-    const int n = hb * 8 + r;
-    uint4 cg[GPL], cu[GPL];
-    uint32_t sgw[GPL], suw[GPL];
-  #pragma unroll
+  };
+  // ... into the wave's LDS (zeros past the wave's groups); the values are selected
+  // on every lane, outside the stores' branches, so each load is waited for on every path
+  auto stage_x = [&](int tc) {
+#pragma unroll
+    for (int ti = 0; ti < kTB; ++ti) {
+      uint32_t* xt = xs + (size_t)ti * (GW * 17);
+#pragma unroll
+      for (int v = 0; v < XQ; ++v) {
+        const int q = lane + 64 * v;
+        const bool keep = q < gw_here * 4;
+        const uint4 val = make_uint4(keep ? xv[ti][v].x : 0u, keep ? xv[ti][v].y : 0u, keep ? xv[ti][v].z : 0u,
+                                     keep ? xv[ti][v].w : 0u);
+        if (ti < tc && q < GW * 4) reinterpret_cast<uint4*>(xt)[q] = val;
+      }
+      const float cval = lane < gw_here ? cv[ti] : 0.0f;
+      if (ti < tc && lane < GW) reinterpret_cast<float*>(xt + GW * 16)[lane] = cval;
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  const BlobLayout BL = blob_layout(H, I);
+  const int n = hb * 8 + r;
+  uint4 cg[GPL], cu[GPL];
+  uint32_t sgw[GPL], suw[GPL];
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) {
+    const int jl = 8 * i + p;
+    int j = j0 + (jl < gw_here ? jl : gw_here - 1);
+    j = j < 0 ? 0 : (j < G ? j : G - 1);
+    const size_t co = code_off(n, j, G, kRowBlockGU);
+    cg[i] = *reinterpret_cast<const uint4*>(src + BL.gate_codes + co);
+    cu[i] = *reinterpret_cast<const uint4*>(src + BL.up_codes + co);
+    const size_t sd = scale_off(n, j, G, kRowBlockGU) >> 2;
+    sgw[i] = reinterpret_cast<const uint32_t*>(src + BL.gate_scales)[sd];
+    suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
+  }
+  load_x(0);  // after the weights: these need the pair table, the weights only the record
+  __builtin_amdgcn_sched_barrier(0);
+  _Float16* hws = reinterpret_cast<_Float16*>(a.ws + W.h_off);
+  const int sh = (r & 1) * 16;
+  stage_x(np < kTB ? np : kTB);
+  for (int c0 = 0;;) {
+    const int tc = np - c0 < kTB ? np - c0 : kTB;
+    float ag[kTB], au[kTB];
+#pragma unroll
+    for (int ti = 0; ti < kTB; ++ti) ag[ti] = au[ti] = 0.0f;
+#pragma unroll
     for (int i = 0; i < GPL; ++i) {
       const int jl = 8 * i + p;
-      int j = j0 + (jl < gw_here ? jl : gw_here - 1);
-      j = j < 0 ? 0 : (j < G ? j : G - 1);
-      const size_t co = code_off(n, j, G, kRowBlockGU);
-      cg[i] = *reinterpret_cast<const uint4*>(src + BL.gate_codes + co);
-      cu[i] = *reinterpret_cast<const uint4*>(src + BL.up_codes + co);
-      const size_t sd = scale_off(n, j, G, kRowBlockGU) >> 2;
-      sgw[i] = reinterpret_cast<const uint32_t*>(src + BL.gate_scales)[sd];
-      suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    _Float16* hws = reinterpret_cast<_Float16*>(a.ws + W.h_off);
-    const uint4* x16 = reinterpret_cast<const uint4*>(a.ws + W.x16_off);
-    const float* xc = reinterpret_cast<const float*>(a.ws + W.xc_off);
-    const int sh = (r & 1) * 16;
-    for (int c0 = 0; c0 < np; c0 += kTB) {
-      const int tc = np - c0 < kTB ? np - c0 : kTB;
-      // copy the chunk's fp16 x slices and corrections into the wave's LDS: uint4 q
-      // of a token's slice is columns 8q .. 8q+7 of the wave's groups; every
-      // token's loads are issued before any is stored
-      constexpr int XQ = (GPL + 1) / 2;  // uint4 per lane and token (GW <= 8 * GPL groups)
-      uint4 xv[kTB][XQ];
-      float cv[kTB];
-  #pragma unroll
+      const bool ok = blob != nullptr && jl < gw_here;
+      const int jc = jl < gw_here ? jl : 0;
+      // the weights are opaque per chunk: nothing is hoisted to before the loop,
+      // where it would wait for them ahead of the staging
+      asm volatile("" : "+v"(cg[i].x), "+v"(cg[i].y), "+v"(cg[i].z), "+v"(cg[i].w), "+v"(sgw[i]));
+      asm volatile("" : "+v"(cu[i].x), "+v"(cu[i].y), "+v"(cu[i].z), "+v"(cu[i].w), "+v"(suw[i]));
+      const float sg = ok ? f16_lo(sgw[i] >> sh) : 0.0f;
+      const float su = ok ? f16_lo(suw[i] >> sh) : 0.0f;
+      // the codes' fp16 pairs once per step, for every token of the chunk
+      uint32_t pg[16], pu[16];
+      code_pairs(cg[i], pg);
+      code_pairs(cu[i], pu);
+#pragma unroll
       for (int ti = 0; ti < kTB; ++ti) {
-        const int t = pair_token(__builtin_amdgcn_readlane(my_pair, c0 + (ti < tc ? ti : tc - 1)), T, K);
-  #pragma unroll
-        for (int v = 0; v < XQ; ++v) {
-          int q = j0 * 4 + lane + 64 * v;
-          q = q < G * 4 ? q : G * 4 - 1;
-          xv[ti][v] = x16[(size_t)t * (H / 8) + q];
-        }
-        int jj = j0 + (lane < GW ? lane : 0);
-        jj = jj < G ? jj : G - 1;
-        cv[ti] = xc[(size_t)t * G + jj];
-      }
-  #pragma unroll
-      for (int ti = 0; ti < kTB; ++ti) {
-        uint32_t* xt = xs + (size_t)ti * (GW * 17);
-  #pragma unroll
-        for (int v = 0; v < XQ; ++v) {
-          const int q = lane + 64 * v;
-          if (q < GW * 4) reinterpret_cast<uint4*>(xt)[q] = (ti < tc && q < gw_here * 4) ? xv[ti][v] : make_uint4(0u, 0u, 0u, 0u);
-        }
-        if (lane < GW) reinterpret_cast<float*>(xt + GW * 16)[lane] = (ti < tc && lane < gw_here) ? cv[ti] : 0.0f;
-      }
-      __builtin_amdgcn_wave_barrier();
-      float ag[kTB], au[kTB];
-  #pragma unroll
-      for (int ti = 0; ti < kTB; ++ti) ag[ti] = au[ti] = 0.0f;
-  #pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const int jl = 8 * i + p;
-        const bool ok = blob != nullptr && jl < gw_here;
-        const int jc = jl < gw_here ? jl : 0;
-        const float sg = ok ? f16_lo(sgw[i] >> sh) : 0.0f;
-        const float su = ok ? f16_lo(suw[i] >> sh) : 0.0f;
-        uint32_t pg[16], pu[16];
-        code_pairs(cg[i], pg);
-        code_pairs(cu[i], pu);
-  #pragma unroll
-        for (int ti = 0; ti < kTB; ++ti) {
-          if (ti < tc) {
-            const uint32_t* xt = xs + (size_t)ti * (GW * 17);
-            const uint4* xq = reinterpret_cast<const uint4*>(xt + jc * 16);
-            const uint4 x0 = xq[0], x1 = xq[1], x2 = xq[2], x3 = xq[3];
-            const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                     x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-            const float C = reinterpret_cast<const float*>(xt + GW * 16)[jc];
-            float dg = 0.0f, du = 0.0f;
-  #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-              dg = dot2h(pg[k], xw[k], dg);
-              du = dot2h(pu[k], xw[k], du);
-            }
-            ag[ti] = fmaf(sg, dg - C, ag[ti]);
-            au[ti] = fmaf(su, du - C, au[ti]);
+        if (ti < tc) {
+          const uint32_t* xt = xs + (size_t)ti * (GW * 17);
+          const uint4* xq = reinterpret_cast<const uint4*>(xt + jc * 16);
+          const uint4 x0 = xq[0], x1 = xq[1], x2 = xq[2], x3 = xq[3];
+          const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                   x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+          const float C = reinterpret_cast<const float*>(xt + GW * 16)[jc];
+          float dg = 0.0f, du = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            dg = dot2h(pg[k], xw[k], dg);
+            du = dot2h(pu[k], xw[k], du);
           }
-          // token ti is done here: the next token's LDS reads are not hoisted above (register pressure)
-          asm volatile("" : "+v"(ag[ti]), "+v"(au[ti])::"memory");
+          ag[ti] = fmaf(sg, dg - C, ag[ti]);
+          au[ti] = fmaf(su, du - C, au[ti]);
         }
+        // token ti is done here: the next token's LDS reads are not hoisted above (register pressure)
+        asm volatile("" : "+v"(ag[ti]), "+v"(au[ti])::"memory");
       }
-      // phases (lane bits 3..5), read from lanes 0..7, then the waves in order
-  #pragma unroll
-      for (int ti = 0; ti < kTB; ++ti) {
-        const float g = sum_rows(dpp_add<8>(ag[ti]));
-        const float uu = sum_rows(dpp_add<8>(au[ti]));
-        if (p == 0) {
-          part[ti][0][wave][r] = g;
-          part[ti][1][wave][r] = uu;
-        }
-      }
-      // pair of the token thread tid < 8 * tc finishes, read while every lane is active
-      __syncthreads();
-      if (tid < 8 * tc) {
-        const int ti = tid >> 3, rr = tid & 7;
-        float g = 0.0f, uu = 0.0f;
-  #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          g += part[ti][0][w][rr];
-          uu += part[ti][1][w][rr];
-        }
-        const float hv = blob ? silu(g) * uu : 0.0f;
-        if (!(fabsf(hv) < 65520.0f)) *a.status = MOE_EUNSUP;
-        hws[(size_t)(p0 + c0 + ti) * I + hb * 8 + rr] = (_Float16)hv;
-      }
-      __syncthreads();
     }
+    // phases (lane bits 3..5), read from lanes 0..7
+#pragma unroll
+    for (int ti = 0; ti < kTB; ++ti) {
+      const float g = sum_rows(dpp_add<8>(ag[ti]));
+      const float uu = sum_rows(dpp_add<8>(au[ti]));
+      if (p == 0) {
+        part[ti][0][wave][r] = g;
+        part[ti][1][wave][r] = uu;
+      }
+    }
+    // the waves in order; pair of the token: thread tid < 8 * tc
+    __syncthreads();
+    if (tid < 8 * tc) {
+      const int ti = tid >> 3, rr = tid & 7;
+      float g = 0.0f, uu = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        g += part[ti][0][w][rr];
+        uu += part[ti][1][w][rr];
+      }
+      const float hv = blob ? silu(g) * uu : 0.0f;
+      if (!(fabsf(hv) < 65520.0f)) *a.status = MOE_EUNSUP;
+      hws[(size_t)(p0 + c0 + ti) * I + hb * 8 + rr] = (_Float16)hv;
+    }
+    c0 += kTB;
+    if (c0 >= np) break;
+    __syncthreads();  // part[] is read before the next chunk writes it
+    load_x(c0);
+    stage_x(np - c0 < kTB ? np - c0 : kTB);
   }
 }
 
@@ -374,15 +405,15 @@ __global__ void __launch_bounds__(kThreads) bat_gateup_kernel(FfnArgs a) {
 // One workgroup per (unit, 64 rows of H); wave w owns rows 16w .. 16w+15 of the
 // item, as four 4-row blocks of the blob. SPL = steps per lane = ceil(Gd / 16):
 // at step i lane (row r of 4, phase p of 16) takes group 16i + p of its row in
-// each block. The chunk's h rows are staged once per wave and serve all four
-// blocks.
+// each block. The workgroup stages the h rows of kTBD pairs at a time into LDS,
+// all of a chunk's loads issued together; the first chunk's before the weights.
 constexpr int kDnRowsPerItem = 64;
 constexpr int kDnBlocks = 4;  // 4-row blocks per wave
 
 template <int SPL>
 __global__ void __launch_bounds__(kThreads) bat_down_kernel(FfnArgs a) {
-  // LDS per wave: for each of the chunk's pairs, the h row as fp16 pairs
-  // [Gd][16] dwords and the group corrections [Gd]
+  // LDS: for each of the chunk's pairs, the h row as fp16 pairs [Gd][16] dwords
+  // and the group corrections [Gd]
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const int Gd = I / kGroup;
@@ -392,117 +423,132 @@ __global__ void __launch_bounds__(kThreads) bat_down_kernel(FfnArgs a) {
   const bool has_shared = a.shared_blob != nullptr;
   const BatWs W = bat_ws(T, H, I, a.E, K, has_shared);
   const PlanView pl = plan_view(a.ws, W.U, W.P);
-  // one item per workgroup, a unit's items consecutive (as in bat_gateup)
   const int n_rb = H / kDnRowsPerItem;
-  {
-    const int item = blockIdx.x;
-    const int u = item / n_rb, rb = item % n_rb;
-    if (u >= plan_n_units(pl)) return;
-    const int4 rc = pl.rec[u];
-    const int p0 = rc.y, np = rc.z;
-    if (np > 64) {  // only with an expert repeated within a token's ids (moe_route never does that)
-      if (lane == 0) *a.status = MOE_EUNSUP;
-      return;
+  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  const UnitHead uh = unit_head(pl, u, lane);
+  const int p0 = uh.p0, np = uh.np;
+  if (np == 0) return;
+  if (np > kUnitPairs) {
+    if (tid == 0) *a.status = MOE_EUNSUP;
+    return;
+  }
+  uint32_t* hsl = reinterpret_cast<uint32_t*>(smem);
+  const int per_pair = Gd * 4;  // uint4 of one h row
+  // uint4 q of a chunk (thread tid holds q = tid + kThreads v) is pair q / per_pair,
+  // group (q / 4) % Gd, columns 8 (q % 4) .. +7: the four lanes of a group are a quad
+  constexpr int HQ = kTBD * SPL * 64 / kThreads;  // kTBD * Gd * 4 <= kThreads * HQ
+  const uint4* h4 = reinterpret_cast<const uint4*>(a.ws + W.h_off);
+  uint4 hv[HQ];
+  auto load_h = [&](int c0) {
+    const int tc = np - c0 < kTBD ? np - c0 : kTBD;
+#pragma unroll
+    for (int v = 0; v < HQ; ++v) {
+      const int q = tid + kThreads * v;
+      const int ti = q / per_pair;
+      const bool live = ti < tc;
+      const int row = p0 + c0 + (live ? ti : 0);
+      const int rem = live ? q - ti * per_pair : 0;
+      hv[v] = h4[(size_t)row * (I / 8) + rem];  // past the chunk: a row of it, never stored
     }
-    const int my_pair = pl.pair_list[p0 + (lane < np ? lane : np - 1)];  // lane i: the unit's pair i
-    uint32_t* hsl = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * kTB * (Gd * 17);
-    const uint8_t* blob = rec_blob(a, rc.x);
-    const uint8_t* src = blob ? blob : a.slots;
-    const BlobLayout BL = blob_layout(H, I);
-    const int n0 = rb * kDnRowsPerItem + wave * 16 + r;  // row of block b: n0 + 4b
-    uint4 cd[kDnBlocks][SPL];
-    uint32_t sdw[kDnBlocks][SPL];
-  #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-  #pragma unroll
-      for (int b = 0; b < kDnBlocks; ++b) {
-        int j = 16 * i + p;
-        j = j < Gd ? j : Gd - 1;
-        const int n = n0 + 4 * b;
-        cd[b][i] = *reinterpret_cast<const uint4*>(src + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
-        sdw[b][i] = reinterpret_cast<const uint32_t*>(src + BL.down_scales)[scale_off(n, j, Gd, kRowBlockDN) >> 2];
+  };
+  load_h(0);  // before the weights: staging waits for these only
+  const uint8_t* blob = rec_blob(a, uh.slot);
+  const uint8_t* src = blob ? blob : a.slots;
+  const BlobLayout BL = blob_layout(H, I);
+  const int n0 = rb * kDnRowsPerItem + wave * 16 + r;  // row of block b: n0 + 4b
+  uint4 cd[kDnBlocks][SPL];
+  uint32_t sdw[kDnBlocks][SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+#pragma unroll
+    for (int b = 0; b < kDnBlocks; ++b) {
+      int j = 16 * i + p;
+      j = j < Gd ? j : Gd - 1;
+      const int n = n0 + 4 * b;
+      cd[b][i] = *reinterpret_cast<const uint4*>(src + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
+      sdw[b][i] = reinterpret_cast<const uint32_t*>(src + BL.down_scales)[scale_off(n, j, Gd, kRowBlockDN) >> 2];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float* ows = reinterpret_cast<float*>(a.ws + W.o_off);
+  const int sh = (r & 1) * 16;
+  // a chunk's h rows and their group corrections into LDS
+  auto stage_h = [&](int tc) {
+#pragma unroll
+    for (int v = 0; v < HQ; ++v) {
+      const int q = tid + kThreads * v;
+      const int ti = q / per_pair;
+      const int rem = q - ti * per_pair;
+      const uint32_t d[4] = {hv[v].x, hv[v].y, hv[v].z, hv[v].w};
+      float sa = (f16_lo(d[0]) + f16_hi(d[0])) + (f16_lo(d[2]) + f16_hi(d[2]));
+      float sb = (f16_lo(d[1]) + f16_hi(d[1])) + (f16_lo(d[3]) + f16_hi(d[3]));
+      sa = quad_xor_add<2>(quad_xor_add<1>(sa));
+      sb = quad_xor_add<2>(quad_xor_add<1>(sb));
+      if (ti < tc) {
+        uint32_t* ht = hsl + (size_t)ti * (Gd * 17);
+        reinterpret_cast<uint4*>(ht)[rem] = hv[v];
+        if ((lane & 3) == 0) reinterpret_cast<float*>(ht + Gd * 16)[rem >> 2] = fmaf(1032.0f, sa, 72.0f * sb);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    const uint4* h4 = reinterpret_cast<const uint4*>(a.ws + W.h_off);  // h fp16 [position][I]
-    float* ows = reinterpret_cast<float*>(a.ws + W.o_off);
-    const int sh = (r & 1) * 16;
-    const int per_pair = Gd * 4;  // uint4 of one h row
-    for (int c0 = 0; c0 < np; c0 += kTB) {
-      const int tc = np - c0 < kTB ? np - c0 : kTB;
-      // stage the chunk's h rows: uint4 q of the chunk = pair q / per_pair, group (q / 4) % Gd,
-      // halves 8 * (q % 4) .. +7; the four lanes of a group are adjacent
-      for (int q0 = 0; q0 < kTB * per_pair; q0 += 64) {
-        const int q = q0 + lane;
-        const int ti = q / per_pair;
-        const int rem = q - ti * per_pair;
-        const bool live = ti < tc;
-        uint4 hv = h4[(size_t)(p0 + c0 + (live ? ti : 0)) * (I / 8) + rem];
-        if (!live) hv = make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t d[4] = {hv.x, hv.y, hv.z, hv.w};
-        float sa = (f16_lo(d[0]) + f16_hi(d[0])) + (f16_lo(d[2]) + f16_hi(d[2]));
-        float sb = (f16_lo(d[1]) + f16_hi(d[1])) + (f16_lo(d[3]) + f16_hi(d[3]));
-        sa = quad_xor_add<2>(quad_xor_add<1>(sa));
-        sb = quad_xor_add<2>(quad_xor_add<1>(sb));
-        if (ti < kTB) {
-          uint32_t* ht = hsl + (size_t)ti * (Gd * 17);
-          reinterpret_cast<uint4*>(ht)[rem] = hv;
-          if ((lane & 3) == 0) reinterpret_cast<float*>(ht + Gd * 16)[rem >> 2] = fmaf(1032.0f, sa, 72.0f * sb);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      float acc[kDnBlocks][kTB];
-  #pragma unroll
-      for (int b = 0; b < kDnBlocks; ++b)
-  #pragma unroll
-        for (int ti = 0; ti < kTB; ++ti) acc[b][ti] = 0.0f;
-  #pragma unroll
+  };
+  // the first chunk is staged ahead of the loop, so that only the weights' first
+  // use waits for them
+  stage_h(np < kTBD ? np : kTBD);
+  __syncthreads();
+  for (int c0 = 0;;) {
+    const int tc = np - c0 < kTBD ? np - c0 : kTBD;
+    // one pair at a time: its four row sums over every step, then the phase sum
+    // (lane bits 2..5, read from lanes 0..3); o rows are in pair order
+    for (int ti = 0; ti < tc; ++ti) {
+      const uint32_t* ht = hsl + (size_t)ti * (Gd * 17);
+      float acc[kDnBlocks];
+#pragma unroll
+      for (int b = 0; b < kDnBlocks; ++b) acc[b] = 0.0f;
+#pragma unroll
       for (int i = 0; i < SPL; ++i) {
         const int j = 16 * i + p;
         const bool ok = blob != nullptr && j < Gd;
         const int jc = j < Gd ? j : 0;
-  #pragma unroll
-        for (int ti = 0; ti < kTB; ++ti) {
-          // the codes are opaque per pair, so their fp16 pairs are formed per pair
-          // instead of being hoisted out for all blocks and steps (register pressure)
+        // the codes and scales are opaque per pair, so their fp16 pairs are formed
+        // per pair instead of being hoisted out of the pair loop (register
+        // pressure), and nothing before the chunk loop waits for the weights
 #pragma unroll
-          for (int b = 0; b < kDnBlocks; ++b)
-            asm volatile("" : "+v"(cd[b][i].x), "+v"(cd[b][i].y), "+v"(cd[b][i].z), "+v"(cd[b][i].w));
-          if (ti < tc) {
-            const uint32_t* ht = hsl + (size_t)ti * (Gd * 17);
-            const uint4* hq = reinterpret_cast<const uint4*>(ht + jc * 16);
-            const uint4 h0 = hq[0], h1 = hq[1], h2 = hq[2], h3 = hq[3];
-            const float C = reinterpret_cast<const float*>(ht + Gd * 16)[jc];
-  #pragma unroll
-            for (int b = 0; b < kDnBlocks; ++b) {
-              float P = 0.0f;
-              P = code_dot(cd[b][i].x, h0.x, h0.y, h0.z, h0.w, P);
-              P = code_dot(cd[b][i].y, h1.x, h1.y, h1.z, h1.w, P);
-              P = code_dot(cd[b][i].z, h2.x, h2.y, h2.z, h2.w, P);
-              P = code_dot(cd[b][i].w, h3.x, h3.y, h3.z, h3.w, P);
-              const float sc = ok ? f16_lo(sdw[b][i] >> sh) : 0.0f;
-              acc[b][ti] = fmaf(sc, P - C, acc[b][ti]);
-            }
-          }
-          asm volatile("" ::: "memory");  // one pair's h operands at a time (register pressure)
-        }
-      }
-      // phases (lane bits 2..5), read from lanes 0..3
-  #pragma unroll
-      for (int ti = 0; ti < kTB; ++ti) {
-        const int pr = __builtin_amdgcn_readlane(my_pair, c0 + ti);  // o rows are in pair order
-  #pragma unroll
+        for (int b = 0; b < kDnBlocks; ++b)
+          asm volatile("" : "+v"(cd[b][i].x), "+v"(cd[b][i].y), "+v"(cd[b][i].z), "+v"(cd[b][i].w), "+v"(sdw[b][i]));
+        const uint4* hq = reinterpret_cast<const uint4*>(ht + jc * 16);
+        const uint4 h0 = hq[0], h1 = hq[1], h2 = hq[2], h3 = hq[3];
+        const float C = reinterpret_cast<const float*>(ht + Gd * 16)[jc];
+#pragma unroll
         for (int b = 0; b < kDnBlocks; ++b) {
-          const float o = sum_rows(dpp_add<8>(dpp_add<4>(acc[b][ti])));
-          if (ti < tc && p == 0) ows[(size_t)pr * H + n0 + 4 * b] = o;
+          float P = 0.0f;
+          P = code_dot(cd[b][i].x, h0.x, h0.y, h0.z, h0.w, P);
+          P = code_dot(cd[b][i].y, h1.x, h1.y, h1.z, h1.w, P);
+          P = code_dot(cd[b][i].z, h2.x, h2.y, h2.z, h2.w, P);
+          P = code_dot(cd[b][i].w, h3.x, h3.y, h3.z, h3.w, P);
+          const float sc = ok ? f16_lo(sdw[b][i] >> sh) : 0.0f;
+          acc[b] = fmaf(sc, P - C, acc[b]);
         }
+        asm volatile("" ::: "memory");  // one step's h operands at a time (register pressure)
       }
-      __builtin_amdgcn_wave_barrier();  // the next chunk rewrites this wave's LDS
+      const int pr = __builtin_amdgcn_readlane(uh.my_pair, c0 + ti);
+#pragma unroll
+      for (int b = 0; b < kDnBlocks; ++b) {
+        const float o = sum_rows(dpp_add<8>(dpp_add<4>(acc[b])));
+        if (p == 0) ows[(size_t)pr * H + n0 + 4 * b] = o;
+      }
     }
+    c0 += kTBD;
+    if (c0 >= np) break;
+    __syncthreads();  // every wave is done with this chunk
+    load_h(c0);
+    stage_h(np - c0 < kTBD ? np - c0 : kTBD);
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ combine
+// y[t][col] = o_shared + sum over k in rank order; every o and w load of an
+// output is issued before the sums.
 __global__ void __launch_bounds__(kThreads) bat_combine_kernel(FfnArgs a) {
   const int H = a.H, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
@@ -513,7 +559,18 @@ __global__ void __launch_bounds__(kThreads) bat_combine_kernel(FfnArgs a) {
     const int t = (int)(idx / H);
     const size_t col = idx % H;
     float acc = has_shared ? ows[(size_t)(T * K + t) * H + col] : 0.0f;
-    for (int k = 0; k < K; ++k) acc = fmaf(a.w[t * K + k], ows[(size_t)(t * K + k) * H + col], acc);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      float ov[8], wv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = k0 + j < K ? k0 + j : K - 1;
+        ov[j] = ows[(size_t)(t * K + k) * H + col];
+        wv[j] = a.w[t * K + k];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < K) acc = fmaf(wv[j], ov[j], acc);
+    }
     a.y[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc);
   }
 }
@@ -562,7 +619,7 @@ hipError_t launch_ffn_batched(const FfnArgs& a, int stage, hipStream_t s) {
   {
     const int Gd = a.I / kGroup;
     const int spl = (Gd + 15) / 16;
-    const size_t lds = (size_t)kWaves * kTB * Gd * 17 * 4;
+    const size_t lds = (size_t)kTBD * Gd * 17 * 4;
     const int grid = W.U * (a.H / kDnRowsPerItem);
 #define DN(N)                                                                                       \
   do {                                                                                              \
