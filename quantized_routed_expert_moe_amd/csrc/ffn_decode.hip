@@ -113,23 +113,9 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
   const int n = hb * 8 + r;
-  // 2. codes and scale dwords of every step, in step order
-  uint4 cg[GPL], cu[GPL];
-  uint32_t sgw[GPL], suw[GPL];
-#pragma unroll
-  for (int i = 0; i < GPL; ++i) {
-    const int jl = 8 * i + p;
-    int j = j0 + (jl < gw_here ? jl : gw_here - 1);
-    j = j < 0 ? 0 : (j < G ? j : G - 1);
-    const size_t co = code_off(n, j, G, kRowBlockGU);  // 8 rows x 8 groups: 1 KB contiguous per wave
-    cg[i] = *reinterpret_cast<const uint4*>(src + BL.gate_codes + co);
-    cu[i] = *reinterpret_cast<const uint4*>(src + BL.up_codes + co);
-    const size_t sd = scale_off(n, j, G, kRowBlockGU) >> 2;  // dword holding the scale
-    sgw[i] = reinterpret_cast<const uint32_t*>(src + BL.gate_scales)[sd];
-    suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
-  }
-  __builtin_amdgcn_sched_barrier(0);  // every load is issued before x is used
-  // 3. x -> fp16 pairs, group corrections, into LDS (lanes 2m, 2m+1 hold group m)
+  // 2. x -> fp16 pairs, group corrections, into LDS (lanes 2m, 2m+1 hold group m).
+  //    Done before the weight loads: x has arrived with the slot lookup (issued
+  //    earlier), and the weights' registers are not live yet (register pressure)
   bool bad = false;
   {
     const bool live = lane * 2 < gw_here * 4;
@@ -159,29 +145,34 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
     }
     __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
   }
-  // 4. the steps; the LDS operands of step i+1 are read during step i
-  float ag = 0.0f, au = 0.0f;
-  const int sh = (r & 1) * 16;
-  uint4 xn[4];
-  float Cn;
-  {
-    const int jc = p < gw_here ? p : 0;
-    const uint4* xq = reinterpret_cast<const uint4*>(xs + jc * 16);
-    xn[0] = xq[0], xn[1] = xq[1], xn[2] = xq[2], xn[3] = xq[3];
-    Cn = Cs[jc];
-  }
+  // 3. codes and scale dwords of every step, in step order
+  uint4 cg[GPL], cu[GPL];
+  uint32_t sgw[GPL], suw[GPL];
 #pragma unroll
   for (int i = 0; i < GPL; ++i) {
-    const uint4 x0 = xn[0], x1 = xn[1], x2 = xn[2], x3 = xn[3];
-    const float C = Cn;
-    if (i + 1 < GPL) {
-      const int jl = 8 * (i + 1) + p;
-      const int jc = jl < gw_here ? jl : 0;
-      const uint4* xq = reinterpret_cast<const uint4*>(xs + jc * 16);
-      xn[0] = xq[0], xn[1] = xq[1], xn[2] = xq[2], xn[3] = xq[3];
-      Cn = Cs[jc];
-    }
-    const bool ok = blob != nullptr && 8 * i + p < gw_here;
+    const int jl = 8 * i + p;
+    int j = j0 + (jl < gw_here ? jl : gw_here - 1);
+    j = j < 0 ? 0 : (j < G ? j : G - 1);
+    const size_t co = code_off(n, j, G, kRowBlockGU);  // 8 rows x 8 groups: 1 KB contiguous per wave
+    cg[i] = *reinterpret_cast<const uint4*>(src + BL.gate_codes + co);
+    cu[i] = *reinterpret_cast<const uint4*>(src + BL.up_codes + co);
+    const size_t sd = scale_off(n, j, G, kRowBlockGU) >> 2;  // dword holding the scale
+    sgw[i] = reinterpret_cast<const uint32_t*>(src + BL.gate_scales)[sd];
+    suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before the steps
+  // 4. the steps, each reading its LDS operands (other waves of the SIMD cover
+  //    the LDS latency: few registers live means six or more waves per SIMD)
+  float ag = 0.0f, au = 0.0f;
+  const int sh = (r & 1) * 16;
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) {
+    const int jl = 8 * i + p;
+    const int jc = jl < gw_here ? jl : 0;
+    const uint4* xq = reinterpret_cast<const uint4*>(xs + jc * 16);
+    const uint4 x0 = xq[0], x1 = xq[1], x2 = xq[2], x3 = xq[3];
+    const float C = Cs[jc];
+    const bool ok = blob != nullptr && jl < gw_here;
     float dg = 0.0f, du = 0.0f;
     dg = code_dot(cg[i].x, x0.x, x0.y, x0.z, x0.w, dg);
     du = code_dot(cu[i].x, x0.x, x0.y, x0.z, x0.w, du);
@@ -195,8 +186,7 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
     const float su = ok ? f16_lo(suw[i] >> sh) : 0.0f;
     ag = fmaf(sg, dg - C, ag);
     au = fmaf(su, du - C, au);
-    // step i is computed here: no later LDS read moves above it and no step's
-    // operands are read more than one step ahead (register pressure)
+    // step i is computed here: no later LDS read moves above it (register pressure)
     asm volatile("" : "+v"(ag), "+v"(au)::"memory");
   }
   if (bad) *a.status = MOE_EUNSUP;

@@ -35,9 +35,8 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBM = 128;  // rows of an M-tile (pairs of one unit)
 constexpr int kGThreads = 256;
-constexpr int kRowE = kBK + 8;  // LDS row length in bf16 (16 bytes of padding)
 constexpr int kPlanThreads = 1024;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -178,26 +177,6 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-// 32 codes of one (row, group) times the group's scale -> 32 fp16 values of
-// fp16(q * s), column order. Nibble pair p of a code dword (bits 4p and 4p+16)
-// holds columns 2p and 2p+1; OR-ing it under the fp16 pattern 0x6400 gives
-// 1024 + u exactly, one packed add of -1032 gives q, one packed multiply by s
-// rounds q * s once to nearest even.
-__device__ inline void dequant_f16(uint4 codes, _Float16 sc, uint32_t out[16]) {
-  const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
-  const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2 s2 = {sc, sc};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t m = ((cw[d] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-      const f16x2 q = __builtin_bit_cast(f16x2, m) + off;
-      out[4 * d + p] = __builtin_bit_cast(uint32_t, q * s2);
-    }
-  }
-}
-
 __global__ void __launch_bounds__(256) to_f16_kernel(FfnArgs a) {
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
@@ -220,20 +199,47 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 // MODE 0: gate/up with SwiGLU epilogue (writes h in segment order).
 // MODE 1: down (writes o at the pair's index).
 //
+// Tile: 128 pair rows x 256 weight rows, K in stages of 64 (two quantisation
+// groups). Wave w owns tile columns 64 w .. +63 for all 128 rows, so every
+// dequantised B fragment feeds eight MFMAs (one per 16-row block). LDS holds,
+// double buffered, the stage's A rows (fp16, rows padded to 144 bytes, which
+// the lanes of a ds_read_b128 reach without bank conflicts) and the weights as
+// int4 codes and fp16 scales, a quarter of their fp16 size. A lane
+// dequantises the B operand of v_mfma_f32_16x16x32_f16 (8 consecutive k of
+// one column) from one code dword: nibble pair p of the dword holds k 2p and
+// 2p + 1 (bits 4p and 4p + 16); OR-ing it under the fp16 pattern 0x6400 gives
+// 1024 + u exactly, a packed add of -1032 gives q, a packed multiply by the
+// scale rounds q * s once. The next stage's global loads are in flight while
+// the current stage is computed (one barrier per stage). A tile with at most
+// 64 rows computes only its first four 16-row blocks.
+//
 // Block -> tile: the n_mt * n_nt tiles are ordered (unit, N-tile, M-tile) and
 // cut into 8 contiguous ranges, one per XCD (blocks are dispatched to XCDs
 // round-robin by block id), so the M-tiles of one unit that share a weight
 // N-tile run back to back on one XCD and meet its weight bytes in that XCD's
-// L2. Global loads run two K-stages ahead of the MFMAs (two register sets),
-// and LDS is double buffered, so one barrier per stage.
+// L2.
+constexpr int kTM = 128, kTN = 256, kTK = 64;
+constexpr int kARow = kTK + 8;  // A row in LDS, fp16 elements (16 bytes of padding)
+
+template <int MODE>
+__host__ __device__ inline int gemm_n_tiles(int H, int I) {
+  return MODE == 0 ? (I + 127) / 128 : (H + kTN - 1) / kTN;
+}
+
+// dword e of the 8 code dwords of LDS column c holds dword e ^ sw(c) of the
+// column's two chunks: 16 lanes reading dword d of 16 consecutive columns meet
+// 16 different banks; the four dwords of a chunk stay in its 16 bytes
+__device__ inline int code_swz(int c) { return (c >> 2) & 3; }
+
 template <int MODE>
 __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
-  __shared__ __align__(16) uint16_t As[2][kBM][kRowE];
-  __shared__ __align__(16) uint16_t Bs[2][kBN][kRowE];
+  __shared__ __align__(16) _Float16 As[2][kTM][kARow];
+  __shared__ __align__(16) uint32_t Bc[2][kTN * 8];  // per column: 2 groups x 4 code dwords (swizzled)
+  __shared__ uint32_t Bs[2][kTN];                    // per column: the 2 groups' fp16 scales
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(T, H, I, a.E, K, has_shared);
-  const int n_nt = MODE == 0 ? I / 64 : H / kBN;
+  const int n_nt = gemm_n_tiles<MODE>(H, I);
   const int* cnts = reinterpret_cast<const int*>(a.ws + W.n_mt);
   const int n_mt = cnts[0], n_units = cnts[1];
   const int N = n_mt * n_nt;
@@ -257,134 +263,161 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   const TileDesc td = reinterpret_cast<const TileDesc*>(a.ws + W.tiles)[mt];
   const uint8_t* blob = reinterpret_cast<const uint8_t* const*>(a.ws + W.ublob)[td.unit];
   const int32_t* sorted = reinterpret_cast<const int32_t*>(a.ws + W.sorted);
-  uint16_t* hws = reinterpret_cast<uint16_t*>(a.ws + W.h);
-  float* ows = reinterpret_cast<float*>(a.ws + W.o);
   const int P = T * K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Kd = MODE == 0 ? H : I;  // reduced dimension
   const int G = Kd / kGroup;
+  const int n_st = Kd / kTK;
+  const bool half = td.rows <= 64;  // only the first four 16-row blocks hold pairs
   const BlobLayout BL = blob_layout(H, I);
 
-  // A loader: thread -> (row ar, 32-element half ah) of the 128 x 64 stage
+  // A loader: thread -> (row ar, 32-element half ah) of the 128 x 64 stage; a
+  // padding row reads the tile's first row (its products are never stored)
   const int ar = tid >> 1, ah = tid & 1;
-  const bool a_ok = ar < td.rows && blob != nullptr;
-  const uint16_t* a_src = nullptr;
-  if (a_ok) {
+  const _Float16* a_src;
+  {
+    const int row = ar < td.rows ? ar : 0;
     if (MODE == 0) {
-      const int p = sorted[td.row0 + ar];
+      const int p = sorted[td.row0 + row];
       const int tok = p < P ? p / K : p - P;
-      a_src = reinterpret_cast<const uint16_t*>(a.ws + W.xh) + (size_t)tok * H + 32 * ah;
+      a_src = reinterpret_cast<const _Float16*>(a.ws + W.xh) + (size_t)tok * H + 32 * ah;
     } else {
-      a_src = hws + (size_t)(td.row0 + ar) * I + 32 * ah;
+      a_src = reinterpret_cast<const _Float16*>(a.ws + W.h) + (size_t)(td.row0 + row) * I + 32 * ah;
     }
   }
-  // B loader: thread -> (tile column bc, group bg of the stage's two)
-  const int bc = tid & (kBN - 1), bg = tid >> 7;
-  int brow;  // weight row
+  // B loader: thread -> tile column c = tid, both groups of the stage
+  const int c = tid;
+  int brow;
   size_t bcodes, bscales;
   if (MODE == 0) {
-    const int mat = (bc >> 4) & 1;
-    brow = nt * 64 + (bc >> 5) * 16 + (bc & 15);
+    const int mat = (c >> 4) & 1;  // gate and up alternate in blocks of 16 columns
+    brow = nt * 128 + (c >> 5) * 16 + (c & 15);
+    brow = brow < I ? brow : I - 1;  // past the last row of a partial tile: a real row, never stored
     bcodes = mat ? BL.up_codes : BL.gate_codes;
     bscales = mat ? BL.up_scales : BL.gate_scales;
   } else {
-    brow = nt * kBN + bc;
+    brow = nt * kTN + c;
+    brow = brow < H ? brow : H - 1;
     bcodes = BL.down_codes;
     bscales = BL.down_scales;
   }
-  // group j of this row: code chunk at bsrc + j * R * 16 bytes, scale at ssrc + j * R * 2 bytes
   const int R = MODE == 0 ? kRowBlockGU : kRowBlockDN;
-  const uint8_t* bsrc = blob ? blob + bcodes + code_off(brow, 0, G, R) : nullptr;
-  const uint8_t* ssrc = blob ? blob + bscales + scale_off(brow, 0, G, R) : nullptr;
+  // group j of this row: code chunk at bsrc + j * R * 16 bytes, scale at ssrc + j * R * 2 bytes
+  const uint8_t* bsrc = (blob ? blob : a.slots) + bcodes + code_off(brow, 0, G, R);
+  const uint8_t* ssrc = (blob ? blob : a.slots) + bscales + scale_off(brow, 0, G, R);
+  const uint32_t scale_mask = blob ? 0xFFFFFFFFu : 0u;  // a unit without a blob contributes zeros
+  const int cs = code_swz(c);
 
-  uint4 ra[2][4];
-  uint4 rb[2];
-  _Float16 rs[2];
-  auto gload = [&](auto SET, int st) {
-    constexpr int q = decltype(SET)::value;
-    const int k0 = st * kBK;
-    if (a_ok) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) ra[q][v] = reinterpret_cast<const uint4*>(a_src + k0)[v];
-    } else {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) ra[q][v] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (blob) {
-      const int j = k0 / kGroup + bg;
-      rb[q] = *reinterpret_cast<const uint4*>(bsrc + (size_t)j * R * 16);
-      rs[q] = *reinterpret_cast<const _Float16*>(ssrc + (size_t)j * R * 2);
-    } else {
-      rb[q] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-      rs[q] = (_Float16)0.0f;
-    }
+  uint4 ra0, ra1, ra2, ra3;  // A of the next stage: 4 x 16 bytes of the thread's row half
+  uint4 rb0, rb1;            // B codes of the next stage's two groups
+  uint32_t rs;               // B scales of the next stage's two groups
+  auto gload = [&](int st) {
+    const uint4* ap = reinterpret_cast<const uint4*>(a_src + st * kTK);
+    ra0 = ap[0];
+    ra1 = ap[1];
+    ra2 = ap[2];
+    ra3 = ap[3];
+    const int j = st * 2;
+    rb0 = *reinterpret_cast<const uint4*>(bsrc + (size_t)j * R * 16);
+    rb1 = *reinterpret_cast<const uint4*>(bsrc + (size_t)(j + 1) * R * 16);
+    const uint32_t s0 = *reinterpret_cast<const uint16_t*>(ssrc + (size_t)j * R * 2);
+    const uint32_t s1 = *reinterpret_cast<const uint16_t*>(ssrc + (size_t)(j + 1) * R * 2);
+    rs = (s0 | (s1 << 16)) & scale_mask;
   };
-  auto sstore = [&](auto SET, int buf) {
-    constexpr int q = decltype(SET)::value;
+  auto sstore = [&](int buf) {
+    uint4* ad = reinterpret_cast<uint4*>(&As[buf][ar][32 * ah]);
+    ad[0] = ra0;
+    ad[1] = ra1;
+    ad[2] = ra2;
+    ad[3] = ra3;
+    const uint32_t w0[4] = {rb0.x, rb0.y, rb0.z, rb0.w}, w1[4] = {rb1.x, rb1.y, rb1.z, rb1.w};
+    uint32_t e0[4], e1[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) reinterpret_cast<uint4*>(&As[buf][ar][32 * ah])[v] = ra[q][v];
-    uint32_t deq[16];
-    dequant_f16(rb[q], rs[q], deq);
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      reinterpret_cast<uint4*>(&Bs[buf][bc][32 * bg])[v] = make_uint4(deq[4 * v], deq[4 * v + 1], deq[4 * v + 2], deq[4 * v + 3]);
-  };
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
-      const int kk = ks * 32 + 8 * (lane >> 4);
-      f16x8 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const f16x8*>(&As[buf][wm * 64 + i * 16 + (lane & 15)][kk]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const f16x8*>(&Bs[buf][wn * 64 + j * 16 + (lane & 15)][kk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int e = 0; e < 4; ++e) {  // e = d ^ cs with cs in 0..3: a permutation inside each chunk
+      const int d = e ^ cs;
+      e0[e] = d == 0 ? w0[0] : d == 1 ? w0[1] : d == 2 ? w0[2] : w0[3];
+      e1[e] = d == 0 ? w1[0] : d == 1 ? w1[1] : d == 2 ? w1[2] : w1[3];
     }
+    reinterpret_cast<uint4*>(&Bc[buf][c * 8])[0] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
+    reinterpret_cast<uint4*>(&Bc[buf][c * 8])[1] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
+    Bs[buf][c] = rs;
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  const int n_st = Kd / kBK;
-  gload(S0{}, 0);
-  if (n_st > 1) gload(S1{}, 1);
-  sstore(S0{}, 0);
-  __syncthreads();
-  // stage st lives in register set st % 2 and LDS buffer st % 2
-  for (int st = 0; st < n_st; st += 2) {
-    if (st + 2 < n_st) gload(S0{}, st + 2);
-    compute(0);
-    if (st + 1 < n_st) sstore(S1{}, 1);
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one stage on LDS buffer buf; NB = 16-row blocks computed (8, or 4 for a half tile)
+  auto compute = [&](auto NBC, int buf) {
+    constexpr int NB = decltype(NBC)::value;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // k-half = one quantisation group
+      f16x8 fb[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int col = wave * 64 + n * 16 + (lane & 15);
+        const uint32_t cw = Bc[buf][col * 8 + h * 4 + ((lane >> 4) ^ code_swz(col))];
+        const uint32_t sw = Bs[buf][col];
+        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(h ? sw >> 16 : sw));
+        const f16x2 s2 = {sc, sc};
+        const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+        uint32_t bq[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t m = ((cw >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
+          bq[p] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m) + off) * s2);
+        }
+        fb[n] = __builtin_bit_cast(f16x8, make_uint4(bq[0], bq[1], bq[2], bq[3]));
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const f16x8 fa = *reinterpret_cast<const f16x8*>(&As[buf][i * 16 + (lane & 15)][h * 32 + 8 * (lane >> 4)]);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb[n], acc[i][n], 0, 0, 0);
+        asm volatile("" ::: "memory");  // A fragments are read one block ahead at most (register pressure)
+      }
+    }
+  };
+
+  using NB8 = std::integral_constant<int, 8>;
+  using NB4 = std::integral_constant<int, 4>;
+  // the stage loop, one copy per block count (one loop body each keeps the
+  // register allocation simple)
+  auto run = [&](auto NBC) {
+    gload(0);
+    sstore(0);
     __syncthreads();
-    if (st + 1 < n_st) {
-      if (st + 3 < n_st) gload(S1{}, st + 3);
-      compute(1);
-      if (st + 2 < n_st) sstore(S0{}, 0);
+    for (int st = 0; st < n_st; ++st) {
+      const int buf = st & 1;
+      // the next stage's loads (past the last stage: the last stage again, so the
+      // count of loads in flight is the same on every path)
+      gload(st + 1 < n_st ? st + 1 : st);
+      compute(NBC, buf);
+      sstore(buf ^ 1);  // buffer buf ^ 1 was last read in stage st - 1, before the barrier below it
       __syncthreads();
     }
-  }
+  };
+  if (half)
+    run(NB4{});
+  else
+    run(NB8{});
 
-  // epilogue: lane holds D[row = 4*(lane/16) + v][col = lane%16] of each 16x16 block
+  // epilogue: lane holds D[row = 4 (lane / 16) + v][col = lane % 16] of each 16 x 16 block
+  const int nb_live = half ? 4 : 8;
   if (MODE == 0) {
+    uint16_t* hws = reinterpret_cast<uint16_t*>(a.ws + W.h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int col_i = nt * 64 + (2 * wn + q) * 16 + (lane & 15);  // intermediate index
+        const int col_i = nt * 128 + (wave * 2 + q) * 16 + (lane & 15);  // intermediate index
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + v;
-          if (row < td.rows) {
+          const int row = i * 16 + 4 * (lane >> 4) + v;
+          if (i < nb_live && row < td.rows && col_i < I) {
             const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
             const float hv = blob ? silu(g) * u : 0.0f;
             if (!(fabsf(hv) < 65520.0f)) *a.status = MOE_EUNSUP;  // h does not fit the fp16 operand
@@ -394,17 +427,18 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
       }
     }
   } else {
+    float* ows = reinterpret_cast<float*>(a.ws + W.o);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + v;
-        if (row < td.rows) {
+        const int row = i * 16 + 4 * (lane >> 4) + v;
+        if (i < nb_live && row < td.rows) {
           const int p = sorted[td.row0 + row];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = nt * kBN + wn * 64 + j * 16 + (lane & 15);
-            ows[(size_t)p * H + n] = acc[i][j][v];
+          for (int n = 0; n < 4; ++n) {
+            const int col = nt * kTN + wave * 64 + n * 16 + (lane & 15);
+            if (col < H) ows[(size_t)p * H + col] = acc[i][n][v];
           }
         }
       }
@@ -441,7 +475,7 @@ inline int round8(int v) { return (v + 7) / 8 * 8; }
 
 }  // namespace
 
-bool grouped_shape_ok(int H, int I) { return H % kBN == 0 && I % 64 == 0 && H % kBK == 0; }
+bool grouped_shape_ok(int H, int I) { return H % kTK == 0 && I % kTK == 0; }
 
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared) {
   return grouped_ws(T, H, I, E, K, has_shared).bytes;
@@ -459,10 +493,10 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
     const size_t cb = (n2 + 255) / 256;
     hipLaunchKernelGGL(to_f16_kernel, dim3(cb < 4096 ? (int)cb : 4096), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(round8(W.max_mt * (a.I / 64))), dim3(kGThreads), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(round8(W.max_mt * gemm_n_tiles<0>(a.H, a.I))), dim3(kGThreads), 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(round8(W.max_mt * (a.H / kBN))), dim3(kGThreads), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(round8(W.max_mt * gemm_n_tiles<1>(a.H, a.I))), dim3(kGThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t n4 = (size_t)a.T * a.H / 4;
   const size_t blocks = (n4 + 255) / 256;
