@@ -207,9 +207,9 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 // int4 codes and fp16 scales, a quarter of their fp16 size. A lane
 // dequantises the B operand of v_mfma_f32_16x16x32_f16 (8 consecutive k of
 // one column) from one code dword: nibble pair p of the dword holds k 2p and
-// 2p + 1 (bits 4p and 4p + 16); OR-ing it under the fp16 pattern 0x6400 gives
-// 1024 + u exactly, a packed add of -1032 gives q, a packed multiply by the
-// scale rounds q * s once. The next stage's global loads are in flight while
+// 2p + 1 (bits 4p and 4p + 16); the pair OR-ed under an fp16 pattern gives
+// 1024 + u (pairs 0, 2) or 64 + u (pairs 1, 3) exactly, a packed add of -1032
+// or -72 gives q, a packed multiply by the scale rounds q * s once. The next stage's global loads are in flight while
 // the current stage is computed (one barrier per stage). A tile with at most
 // 64 rows computes only its first four 16-row blocks.
 //
@@ -220,6 +220,17 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 // L2.
 constexpr int kTM = 128, kTN = 256, kTK = 64;
 constexpr int kARow = kTK + 8;  // A row in LDS, fp16 elements (16 bytes of padding)
+
+// Loads through the global address space. The blob addresses come from the
+// workspace, so the compiler cannot tell they are global and would emit flat
+// loads, which count against the LDS wait counter as well: every LDS wait of
+// a stage would then also wait for the next stage's weights.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 ld_global16(const uint8_t* p) {
+  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint32_t ld_global2(const uint8_t* p) { return *(const __attribute__((address_space(1))) uint16_t*)(p); }
 
 template <int MODE>
 __host__ __device__ inline int gemm_n_tiles(int H, int I) {
@@ -272,76 +283,91 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   const bool half = td.rows <= 64;  // only the first four 16-row blocks hold pairs
   const BlobLayout BL = blob_layout(H, I);
 
-  // A loader: thread -> (row ar, 32-element half ah) of the 128 x 64 stage; a
-  // padding row reads the tile's first row (its products are never stored)
-  const int ar = tid >> 1, ah = tid & 1;
-  const _Float16* a_src;
-  {
-    const int row = ar < td.rows ? ar : 0;
+  // Loaders. A: 16-byte chunk q = v * 256 + tid (v < 4) of the 128 x 64 stage is
+  // row q / 8, columns 8 (q % 8) .. +7, so eight consecutive lanes fill one row's
+  // 128 bytes in LDS and in memory; a padding row reads the tile's first row (its
+  // products are never stored). B: chunk q = k * 256 + tid (k < 2) is tile column
+  // q / 2, group q % 2 of the stage, so consecutive lanes fill consecutive 16 bytes.
+  // (named scalars rather than arrays: a private array indexed before unrolling
+  // would be moved to LDS)
+  auto a_ptr = [&](int v) -> const _Float16* {
+    const int q = v * kGThreads + tid;
+    int row = q >> 3;
+    row = row < td.rows ? row : 0;
+    const int col8 = (q & 7) * 8;
     if (MODE == 0) {
       const int p = sorted[td.row0 + row];
       const int tok = p < P ? p / K : p - P;
-      a_src = reinterpret_cast<const _Float16*>(a.ws + W.xh) + (size_t)tok * H + 32 * ah;
-    } else {
-      a_src = reinterpret_cast<const _Float16*>(a.ws + W.h) + (size_t)(td.row0 + row) * I + 32 * ah;
+      return reinterpret_cast<const _Float16*>(a.ws + W.xh) + (size_t)tok * H + col8;
     }
-  }
-  // B loader: thread -> tile column c = tid, both groups of the stage
-  const int c = tid;
-  int brow;
-  size_t bcodes, bscales;
-  if (MODE == 0) {
-    const int mat = (c >> 4) & 1;  // gate and up alternate in blocks of 16 columns
-    brow = nt * 128 + (c >> 5) * 16 + (c & 15);
-    brow = brow < I ? brow : I - 1;  // past the last row of a partial tile: a real row, never stored
-    bcodes = mat ? BL.up_codes : BL.gate_codes;
-    bscales = mat ? BL.up_scales : BL.gate_scales;
-  } else {
-    brow = nt * kTN + c;
-    brow = brow < H ? brow : H - 1;
-    bcodes = BL.down_codes;
-    bscales = BL.down_scales;
-  }
+    return reinterpret_cast<const _Float16*>(a.ws + W.h) + (size_t)(td.row0 + row) * I + col8;
+  };
+  const _Float16* const a_src0 = a_ptr(0);
+  const _Float16* const a_src1 = a_ptr(1);
+  const _Float16* const a_src2 = a_ptr(2);
+  const _Float16* const a_src3 = a_ptr(3);
   const int R = MODE == 0 ? kRowBlockGU : kRowBlockDN;
-  // group j of this row: code chunk at bsrc + j * R * 16 bytes, scale at ssrc + j * R * 2 bytes
-  const uint8_t* bsrc = (blob ? blob : a.slots) + bcodes + code_off(brow, 0, G, R);
-  const uint8_t* ssrc = (blob ? blob : a.slots) + bscales + scale_off(brow, 0, G, R);
-  const uint32_t scale_mask = blob ? 0xFFFFFFFFu : 0u;  // a unit without a blob contributes zeros
-  const int cs = code_swz(c);
+  // B chunk k: code chunk at bsrc + (2 st + g) * R * 16 bytes, scale at ssrc + (2 st + g) * R * 2
+  struct BSrc {
+    const uint8_t* codes;
+    const uint8_t* scales;
+  };
+  auto b_src = [&](int k) -> BSrc {
+    const int q = k * kGThreads + tid;
+    const int c = q >> 1;
+    int brow;
+    size_t bcodes, bscales;
+    if (MODE == 0) {
+      const int mat = (c >> 4) & 1;  // gate and up alternate in blocks of 16 columns
+      brow = nt * 128 + (c >> 5) * 16 + (c & 15);
+      brow = brow < I ? brow : I - 1;  // past the last row of a partial tile: a real row, never stored
+      bcodes = mat ? BL.up_codes : BL.gate_codes;
+      bscales = mat ? BL.up_scales : BL.gate_scales;
+    } else {
+      brow = nt * kTN + c;
+      brow = brow < H ? brow : H - 1;
+      bcodes = BL.down_codes;
+      bscales = BL.down_scales;
+    }
+    const uint8_t* base = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
+    return BSrc{base + bcodes + code_off(brow, 0, G, R) + (size_t)(q & 1) * R * 16,
+                base + bscales + scale_off(brow, 0, G, R) + (size_t)(q & 1) * R * 2};
+  };
+  const BSrc bs0 = b_src(0), bs1 = b_src(1);
+  const int bcol0 = tid >> 1, bcol1 = (kGThreads + tid) >> 1;
+  const uint32_t scale_mask = blob ? 0xFFFFu : 0u;  // a unit without a blob contributes zeros
+  const int bg = tid & 1;                          // group of both B chunks of this thread
 
-  uint4 ra0, ra1, ra2, ra3;  // A of the next stage: 4 x 16 bytes of the thread's row half
-  uint4 rb0, rb1;            // B codes of the next stage's two groups
-  uint32_t rs;               // B scales of the next stage's two groups
+  uint4 ra0, ra1, ra2, ra3;  // A of the next stage
+  uint4 rb0, rb1;            // B codes of the next stage
+  uint32_t rs0, rs1;         // B scales of the next stage
   auto gload = [&](int st) {
-    const uint4* ap = reinterpret_cast<const uint4*>(a_src + st * kTK);
-    ra0 = ap[0];
-    ra1 = ap[1];
-    ra2 = ap[2];
-    ra3 = ap[3];
-    const int j = st * 2;
-    rb0 = *reinterpret_cast<const uint4*>(bsrc + (size_t)j * R * 16);
-    rb1 = *reinterpret_cast<const uint4*>(bsrc + (size_t)(j + 1) * R * 16);
-    const uint32_t s0 = *reinterpret_cast<const uint16_t*>(ssrc + (size_t)j * R * 2);
-    const uint32_t s1 = *reinterpret_cast<const uint16_t*>(ssrc + (size_t)(j + 1) * R * 2);
-    rs = (s0 | (s1 << 16)) & scale_mask;
+    ra0 = *reinterpret_cast<const uint4*>(a_src0 + st * kTK);
+    ra1 = *reinterpret_cast<const uint4*>(a_src1 + st * kTK);
+    ra2 = *reinterpret_cast<const uint4*>(a_src2 + st * kTK);
+    ra3 = *reinterpret_cast<const uint4*>(a_src3 + st * kTK);
+    rb0 = ld_global16(bs0.codes + (size_t)st * 2 * R * 16);
+    rb1 = ld_global16(bs1.codes + (size_t)st * 2 * R * 16);
+    rs0 = ld_global2(bs0.scales + (size_t)st * 2 * R * 2) & scale_mask;
+    rs1 = ld_global2(bs1.scales + (size_t)st * 2 * R * 2) & scale_mask;
+  };
+  // B chunk of column c into LDS: dword e of the chunk's 16 bytes holds code
+  // dword e ^ code_swz(c), a permutation inside the chunk
+  auto put_b = [&](int buf, int c, const uint4& w, uint32_t sc) {
+    const int cs = code_swz(c);
+    const uint32_t x = cs & 1 ? w.y : w.x, y = cs & 1 ? w.x : w.y;
+    const uint32_t z = cs & 1 ? w.w : w.z, u = cs & 1 ? w.z : w.w;
+    const uint4 o = cs & 2 ? make_uint4(z, u, x, y) : make_uint4(x, y, z, u);
+    reinterpret_cast<uint4*>(&Bc[buf][c * 8])[bg] = o;
+    reinterpret_cast<uint16_t*>(&Bs[buf][c])[bg] = (uint16_t)sc;
   };
   auto sstore = [&](int buf) {
-    uint4* ad = reinterpret_cast<uint4*>(&As[buf][ar][32 * ah]);
-    ad[0] = ra0;
-    ad[1] = ra1;
-    ad[2] = ra2;
-    ad[3] = ra3;
-    const uint32_t w0[4] = {rb0.x, rb0.y, rb0.z, rb0.w}, w1[4] = {rb1.x, rb1.y, rb1.z, rb1.w};
-    uint32_t e0[4], e1[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {  // e = d ^ cs with cs in 0..3: a permutation inside each chunk
-      const int d = e ^ cs;
-      e0[e] = d == 0 ? w0[0] : d == 1 ? w0[1] : d == 2 ? w0[2] : w0[3];
-      e1[e] = d == 0 ? w1[0] : d == 1 ? w1[1] : d == 2 ? w1[2] : w1[3];
-    }
-    reinterpret_cast<uint4*>(&Bc[buf][c * 8])[0] = make_uint4(e0[0], e0[1], e0[2], e0[3]);
-    reinterpret_cast<uint4*>(&Bc[buf][c * 8])[1] = make_uint4(e1[0], e1[1], e1[2], e1[3]);
-    Bs[buf][c] = rs;
+    *reinterpret_cast<uint4*>(&As[buf][tid >> 3][(tid & 7) * 8]) = ra0;
+    *reinterpret_cast<uint4*>(&As[buf][(kGThreads + tid) >> 3][(tid & 7) * 8]) = ra1;
+    *reinterpret_cast<uint4*>(&As[buf][(2 * kGThreads + tid) >> 3][(tid & 7) * 8]) = ra2;
+    *reinterpret_cast<uint4*>(&As[buf][(3 * kGThreads + tid) >> 3][(tid & 7) * 8]) = ra3;
+    put_b(buf, bcol0, rb0, rs0);
+    put_b(buf, bcol1, rb1, rs1);
   };
 
   f32x4 acc[8][4];
@@ -349,6 +375,14 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Dequantisation constants, held in registers so that each AND-OR is one
+  // v_and_or_b32: nibbles at bits 0..3 / 16..19 under 0x6400 give 1024 + u,
+  // nibbles at bits 4..7 / 20..23 under 0x5400 give 64 + u (both exact), so one
+  // shift by 8 serves all four pairs of a code dword.
+  uint32_t k_mlo = 0x000F000Fu, k_mhi = 0x00F000F0u, k_elo = 0x64006400u, k_ehi = 0x54005400u;
+  asm volatile("" : "+v"(k_mlo), "+v"(k_mhi), "+v"(k_elo), "+v"(k_ehi));
+  const f16x2 off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f}, off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
 
   // one stage on LDS buffer buf; NB = 16-row blocks computed (8, or 4 for a half tile)
   auto compute = [&](auto NBC, int buf) {
@@ -363,21 +397,29 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
         const uint32_t sw = Bs[buf][col];
         const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(h ? sw >> 16 : sw));
         const f16x2 s2 = {sc, sc};
-        const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+        const uint32_t w8 = cw >> 8;
+        const uint32_t m0 = (cw & k_mlo) | k_elo, m1 = (cw & k_mhi) | k_ehi;
+        const uint32_t m2 = (w8 & k_mlo) | k_elo, m3 = (w8 & k_mhi) | k_ehi;
         uint32_t bq[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t m = ((cw >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-          bq[p] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m) + off) * s2);
-        }
+        bq[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m0) + off_lo) * s2);
+        bq[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m1) + off_hi) * s2);
+        bq[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m2) + off_lo) * s2);
+        bq[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m3) + off_hi) * s2);
         fb[n] = __builtin_bit_cast(f16x8, make_uint4(bq[0], bq[1], bq[2], bq[3]));
       }
+      // A fragments one block ahead: block i + 1's is read before block i's MFMAs
+      // are issued, so its LDS latency runs under them
+      auto read_a = [&](int i) {
+        return *reinterpret_cast<const f16x8*>(&As[buf][i * 16 + (lane & 15)][h * 32 + 8 * (lane >> 4)]);
+      };
+      f16x8 fa_next = read_a(0);
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const f16x8 fa = *reinterpret_cast<const f16x8*>(&As[buf][i * 16 + (lane & 15)][h * 32 + 8 * (lane >> 4)]);
+        const f16x8 fa = fa_next;
+        if (i + 1 < NB) fa_next = read_a(i + 1);
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb[n], acc[i][n], 0, 0, 0);
-        asm volatile("" ::: "memory");  // A fragments are read one block ahead at most (register pressure)
+        asm volatile("" ::: "memory");  // no A fragment further ahead (register pressure)
       }
     }
   };
