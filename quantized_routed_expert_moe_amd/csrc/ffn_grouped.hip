@@ -15,17 +15,19 @@
 //      round to the fp16 subnormal grid (absolute error <= 2^-25), and a
 //      value that would overflow fp16 sets MOE_EUNSUP in the status word
 //      rather than being clamped.
-//   3. gate/up GEMM: tile = 128 pair rows x (64 gate + 64 up) weight rows,
-//      K = H in steps of 64 (two quantisation groups). A rows are gathered
-//      from the fp16 x; B = fp16(q * s) is formed in registers from the int4
-//      codes with packed fp16 arithmetic (q exact, one rounding of the
-//      product: relative error <= 2^-12) and staged in LDS; both double
-//      buffered. v_mfma_f32_16x16x32_f16 with fp32 accumulation. The tile's
+//   3. gate/up GEMM (grouped_gemm_kernel<0>): tile = 128 pair rows x (128
+//      gate + 128 up) weight rows, K = H in stages of 64 (two quantisation
+//      groups). A rows are gathered from the fp16 x; the weights are staged
+//      in LDS as int4 codes and B = fp16(q * s) is formed in registers right
+//      before the MFMAs (q exact, one rounding of the product: relative error
+//      <= 2^-11). v_mfma_f32_16x16x32_f16 with fp32 accumulation. The tile's
 //      columns interleave gate and up in blocks of 16, so each lane holds
 //      matching g and u and writes h = silu(g) * u in fp16 (the next A
 //      operand; overflow sets the status word).
-//   4. down GEMM: A = h rows, B = fp16(q * s) of the down matrix; o is
-//      written in fp32 at the pair's own index.
+//   4. down GEMM (grouped_gemm_kernel<1>): A = h rows, B = fp16(q * s) of the
+//      down matrix; o is written in bf16 at the pair's own index (one
+//      rounding, relative error <= 2^-9, of each routed term; bf16 rather than
+//      fp16 because an expert's output row is not bounded by 65504).
 //   5. combine: y[t] = o_shared[t] + sum_k w[t][k] * o[t][k] in rank order,
 //      fp32, rounded once to bf16.
 #include <type_traits>
@@ -68,7 +70,7 @@ __host__ __device__ inline GroupedWs grouped_ws(int T, int H, int I, int E, int 
   w.xh = al256(w.sorted + PA * sizeof(int32_t));
   w.h = al256(w.xh + (size_t)T * H * 2);
   w.o = al256(w.h + PA * (size_t)I * 2);
-  w.bytes = al256(w.o + PA * (size_t)H * 4);
+  w.bytes = al256(w.o + PA * (size_t)H * 2);  // o: bf16
   return w;
 }
 
@@ -469,7 +471,7 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
       }
     }
   } else {
-    float* ows = reinterpret_cast<float*>(a.ws + W.o);
+    uint16_t* ows = reinterpret_cast<uint16_t*>(a.ws + W.o);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -480,7 +482,7 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
 #pragma unroll
           for (int n = 0; n < 4; ++n) {
             const int col = nt * kTN + wave * 64 + n * 16 + (lane & 15);
-            if (col < H) ows[(size_t)p * H + col] = acc[i][n][v];
+            if (col < H) ows[(size_t)p * H + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][n][v]);
           }
         }
       }
@@ -489,27 +491,55 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
 }
 
 // ------------------------------------------------------------------ combine
+// Thread: 8 consecutive columns of one token; every o row of the token is
+// loaded (16 bytes each) before the sums, which run in rank order.
+__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
 __global__ void __launch_bounds__(256) grouped_combine_kernel(FfnArgs a) {
   const int H = a.H, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(T, H, a.I, a.E, K, has_shared);
-  const float* ows = reinterpret_cast<const float*>(a.ws + W.o);
+  const uint4* o8 = reinterpret_cast<const uint4*>(a.ws + W.o);  // 8 bf16 per uint4
   const int P = T * K;
-  const size_t n4 = (size_t)T * H / 4;
-  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < n4; idx += (size_t)gridDim.x * 256) {
-    const int t = (int)(idx / (H / 4));
-    const int c4 = (int)(idx % (H / 4));
-    float4 acc = has_shared ? reinterpret_cast<const float4*>(ows + (size_t)(P + t) * H)[c4]
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      const float wk = a.w[t * K + k];
-      const float4 v = reinterpret_cast<const float4*>(ows + (size_t)(t * K + k) * H)[c4];
-      acc.x = fmaf(wk, v.x, acc.x);
-      acc.y = fmaf(wk, v.y, acc.y);
-      acc.z = fmaf(wk, v.z, acc.z);
-      acc.w = fmaf(wk, v.w, acc.w);
+  const int H8 = H / 8;
+  const size_t n8 = (size_t)T * H8;
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < n8; idx += (size_t)gridDim.x * 256) {
+    const int t = (int)(idx / H8);
+    const int c8 = (int)(idx % H8);
+    float acc[8];
+    {
+      const uint4 v = has_shared ? o8[(size_t)(P + t) * H8 + c8] : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = bf16_lo(d[e]);
+        acc[2 * e + 1] = bf16_hi(d[e]);
+      }
     }
-    reinterpret_cast<uint2*>(a.y)[idx] = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      uint4 ov[8];
+      float wv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = k0 + j < K ? k0 + j : K - 1;
+        ov[j] = o8[(size_t)(t * K + k) * H8 + c8];
+        wv[j] = a.w[t * K + k];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (k0 + j < K) {
+          const uint32_t d[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(wv[j], bf16_lo(d[e]), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(wv[j], bf16_hi(d[e]), acc[2 * e + 1]);
+          }
+        }
+      }
+    }
+    reinterpret_cast<uint4*>(a.y)[idx] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   }
 }
 
@@ -517,7 +547,7 @@ inline int round8(int v) { return (v + 7) / 8 * 8; }
 
 }  // namespace
 
-bool grouped_shape_ok(int H, int I) { return H % kTK == 0 && I % kTK == 0; }
+bool grouped_shape_ok(int H, int I) { return H % kTK == 0 && I % kTK == 0; }  // H % 8 for the combine
 
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared) {
   return grouped_ws(T, H, I, E, K, has_shared).bytes;
@@ -540,8 +570,8 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   }
   hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(round8(W.max_mt * gemm_n_tiles<1>(a.H, a.I))), dim3(kGThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t n4 = (size_t)a.T * a.H / 4;
-  const size_t blocks = (n4 + 255) / 256;
+  const size_t n8 = (size_t)a.T * a.H / 8;
+  const size_t blocks = (n8 + 255) / 256;
   hipLaunchKernelGGL(grouped_combine_kernel, dim3(blocks < 8192 ? (int)blocks : 8192), dim3(256), 0, s, a);
   return hipGetLastError();
 }
