@@ -119,12 +119,24 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
   const int P = T * K;
   for (int e = tid; e < kMaxE; e += kPlanThreads) cnt[e] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += kPlanThreads) {
-    const int e = a.ids[p];
-    if (e >= 0 && e < E)
-      atomicAdd(&cnt[e], 1);
-    else
-      *a.status = MOE_EINVAL;
+  // eight pairs per thread and round, their ids loaded before any is used
+  for (int p0 = tid; p0 < P; p0 += 8 * kPlanThreads) {
+    int ev[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j * kPlanThreads;
+      ev[j] = p < P ? a.ids[p] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (p0 + j * kPlanThreads < P) {
+        const int e = ev[j];
+        if (e >= 0 && e < E)
+          atomicAdd(&cnt[e], 1);
+        else
+          *a.status = MOE_EINVAL;
+      }
+    }
   }
   __syncthreads();
   const int base_rows = has_shared ? T : 0;  // the shared unit's rows come first
@@ -168,9 +180,18 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
     unit_mt0[n_units] = shared_mt + total;
   }
   __syncthreads();
-  for (int p = tid; p < P; p += kPlanThreads) {
-    const int e = a.ids[p];
-    if (e >= 0 && e < E) sorted[seg[e] + atomicAdd(&cur[e], 1)] = p;
+  for (int p0 = tid; p0 < P; p0 += 8 * kPlanThreads) {
+    int ev[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j * kPlanThreads;
+      ev[j] = p < P ? a.ids[p] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = ev[j];
+      if (e >= 0 && e < E) sorted[seg[e] + atomicAdd(&cur[e], 1)] = p0 + j * kPlanThreads;
+    }
   }
 }
 
