@@ -20,7 +20,9 @@ SwiGLU with SiLU on the gate projection, an always-on shared expert of weight
 
 Parity pins (tests/test_oracle_pins.py): router logits against exact rational
 arithmetic; selection against brute-force rank counting; softmax against closed
-forms; int4 decoding against hand-written bytes; dequantisation against an
+forms; the scored router variants against closed forms (sigmoid(ln 3) = 3/4,
+softplus(ln 3) = ln 4), monotonicity (unbiased selection equals the logit
+selection) and bias / scale special cases; int4 decoding against hand-written bytes; dequantisation against an
 element-by-element construction; the FFN against a closed form for an
 identity-like expert (SiLU from torch); the layer against zero input,
 linearity, permutation and relabelling invariances and the dense (K = E)
@@ -173,6 +175,62 @@ def softmax_weights(logits: np.ndarray, ids: np.ndarray, renorm: bool = False) -
 def route(logits: np.ndarray, K: int, renorm: bool = False):
     ids = select_topk(logits, K)
     return ids, softmax_weights(logits, ids, renorm)
+
+
+# ---------------------------------------------------------------- router variants
+
+SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = 0, 1, 2
+
+
+def expert_scores(logits: np.ndarray, score: int) -> np.ndarray:
+    """s[t, e] for the per-expert scoring functions the "Strata" README names
+    under "Models": sigmoid (GLM, Laguna) and sqrtsoftplus (DeepSeek).
+
+    The page names the functions only; the plain readings are sigmoid(l) =
+    1 / (1 + e^-l) and sqrtsoftplus(l) = sqrt(ln(1 + e^l)), each evaluated in
+    float64 and rounded once to float32 (the precision of the selection key).
+    softplus is taken as l + ln(1 + e^-l) for l > 0 so that e^l cannot overflow.
+    """
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    if score == SCORE_SIGMOID:
+        s = 1.0 / (1.0 + np.exp(-l))
+    elif score == SCORE_SQRTSOFTPLUS:
+        sp = np.where(l > 0, l + np.log1p(np.exp(-np.abs(l))), np.log1p(np.exp(np.minimum(l, 0.0))))
+        s = np.sqrt(sp)
+    else:
+        raise ValueError("score must be sigmoid or sqrtsoftplus")
+    return s.astype(np.float32)
+
+
+def route_scored(logits: np.ndarray, K: int, score: int, bias=None, routed_scale: float = 1.0, renorm: bool = False):
+    """ids, w for the scored router variants of the "Strata" README, "Models"
+    ("sigmoid/noaux_tc", "sqrtsoftplus/noaux_tc", "sigmoid top-10 routing with a
+    correction bias and a 2.5x routed scale").
+
+    Readings taken where the page only names the method: the experts are
+    selected on c = float32(s + b), the score plus a per-expert correction bias
+    (none when bias is None), with the same total order as ``select_topk``
+    (c descending, equal values to the lower id); the bias steers selection
+    only, so w[t, k] = s[t, ids[t, k]], divided by their sum over the K
+    selected experts when ``renorm``, then multiplied by ``routed_scale``.
+    With softmax scores no bias is defined (the softmax probabilities are not
+    fixed to the last bit), and w is the softmax weight times the scale.
+    """
+    if score == SCORE_SOFTMAX:
+        if bias is not None:
+            raise ValueError("a correction bias needs sigmoid or sqrtsoftplus scores")
+        ids, w = route(logits, K, renorm)
+        return ids, w * float(routed_scale)
+    s = expert_scores(logits, score)
+    c = s if bias is None else (s + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    ids = select_topk(c, K)
+    T = s.shape[0]
+    w = np.empty((T, K), dtype=np.float64)
+    for t in range(T):
+        w[t] = s[t, ids[t]].astype(np.float64)
+        if renorm:
+            w[t] = w[t] / math.fsum(w[t].tolist())
+    return ids, w * float(routed_scale)
 
 
 # ---------------------------------------------------------------- experts

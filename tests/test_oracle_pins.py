@@ -201,6 +201,86 @@ def test_softmax_renorm():
     assert np.all(wp.sum(1) < 1.0)
 
 
+# ------------------------------------------------------------------ scored router variants
+# ("Strata" README, Models: sigmoid / sqrtsoftplus scoring, correction bias, routed scale)
+
+
+def f32(v):
+    return float(np.float32(v))
+
+
+def test_scores_closed_forms():
+    l = np.array([[0.0, math.log(3.0), -math.log(3.0), 1000.0, -1000.0]], dtype=np.float32)
+    s = R.expert_scores(l, R.SCORE_SIGMOID)[0]
+    assert s[0] == 0.5 and s[1] == 0.75 and s[2] == 0.25 and s[3] == 1.0 and s[4] == 0.0
+    s = R.expert_scores(l, R.SCORE_SQRTSOFTPLUS)[0]
+    assert s[0] == f32(math.sqrt(math.log(2.0)))  # softplus(0) = ln 2
+    assert abs(float(s[1]) - math.sqrt(math.log(4.0))) <= 2 ** -23  # softplus(ln 3) = ln 4
+    assert s[3] == f32(math.sqrt(1000.0))  # e^1000 would overflow: softplus(l) -> l
+    assert s[4] == 0.0
+
+
+def test_scored_unbiased_selection_equals_logit_selection():
+    # both scores increase strictly with the logit, so without a bias they pick
+    # the same experts in the same order as the logits (when no two scores round equal)
+    rng = np.random.default_rng(11)
+    l = (2.0 * rng.standard_normal((6, 64))).astype(np.float32)
+    for score in (R.SCORE_SIGMOID, R.SCORE_SQRTSOFTPLUS):
+        s = R.expert_scores(l, score)
+        assert all(len(set(row.tolist())) == 64 for row in s)
+        ids, w = R.route_scored(l, 8, score)
+        assert np.array_equal(ids, R.select_topk(l, 8))
+        assert np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_scored_bias_steers_selection_only():
+    rng = np.random.default_rng(12)
+    l = rng.standard_normal((1, 32)).astype(np.float32)
+    low = int(np.argmin(l[0]))
+    top = int(np.argmax(l[0]))
+    bias = np.zeros(32, dtype=np.float32)
+    bias[low] = 10.0  # the least likely expert is forced in, at rank 0
+    bias[top] = -10.0  # the most likely is forced out
+    for score in (R.SCORE_SIGMOID, R.SCORE_SQRTSOFTPLUS):
+        s = R.expert_scores(l, score)[0]
+        ids, w = R.route_scored(l, 4, score, bias=bias)
+        assert ids[0, 0] == low and top not in ids[0].tolist()
+        assert w[0, 0] == float(s[low])  # the weight is the score, not score + bias
+        c = [float(np.float32(s[e] + bias[e])) for e in range(32)]
+        assert ids[0].tolist() == brute_force_ids(c, 4)
+
+
+def test_scored_renorm_and_routed_scale():
+    rng = np.random.default_rng(13)
+    l = rng.standard_normal((5, 48)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(48)).astype(np.float32)
+    for score in (R.SCORE_SIGMOID, R.SCORE_SQRTSOFTPLUS):
+        s = R.expert_scores(l, score)
+        ids, w1 = R.route_scored(l, 6, score, bias=bias)
+        assert np.array_equal(w1, np.take_along_axis(s, ids, 1).astype(np.float64))
+        _, w25 = R.route_scored(l, 6, score, bias=bias, routed_scale=2.5)
+        assert np.array_equal(w25, 2.5 * w1)  # the scale is applied once
+        _, wn = R.route_scored(l, 6, score, bias=bias, routed_scale=2.5, renorm=True)
+        assert all(abs(math.fsum(row.tolist()) - 2.5) < 1e-15 for row in wn)
+
+
+def test_scored_saturated_scores_tie_to_lower_id():
+    # sigmoid rounds to 1.0f above l ~ 17: the scores tie and the lower id ranks first
+    l = np.array([[30.0, 40.0, 25.0, 35.0, 0.0]], dtype=np.float32)
+    ids, w = R.route_scored(l, 3, R.SCORE_SIGMOID)
+    assert ids[0].tolist() == [0, 1, 2] and np.all(w == 1.0)
+
+
+def test_scored_softmax_scale_and_bias_rule():
+    rng = np.random.default_rng(14)
+    l = rng.standard_normal((3, 16)).astype(np.float32)
+    ids, w = R.route_scored(l, 4, R.SCORE_SOFTMAX, routed_scale=2.5)
+    ids0, w0 = R.route(l, 4)
+    assert np.array_equal(ids, ids0) and np.array_equal(w, 2.5 * w0)
+    with pytest.raises(ValueError):
+        R.route_scored(l, 4, R.SCORE_SOFTMAX, bias=np.zeros(16, dtype=np.float32))
+
+
 # ------------------------------------------------------------------ expert FFN and layer
 
 
