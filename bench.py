@@ -36,8 +36,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=48)
-    p.add_argument("--legs", default="decode,prefill,batched,paged",
-                   help="comma list of decode,prefill,batched,paged")
+    p.add_argument("--legs", default="decode,prefill,batched,paged,route_variants",
+                   help="comma list of decode,prefill,batched,paged,route_variants")
     p.add_argument("--paged-steps", type=int, default=64, help="measured tokens of the paged decode workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=3, help="decode layers in the oracle's timed sample")
@@ -342,6 +342,49 @@ def batched_leg(a, dev, n_sets=16):
     }
 
 
+# ------------------------------------------------------------------ router variants
+
+
+def route_variants_leg(dev, reps=48):
+    """moe_route / moe_route_scored from logits (E = 256, K = 8): the time per call of each
+    scoring function, for one decode token and for the 9,940-token prompt."""
+    import numpy as np
+    import torch
+
+    from quantized_routed_expert_moe_amd import lib
+    from synth import gen
+
+    E, K = 256, 8
+    stream = torch.cuda.Stream()
+    bias = torch.from_numpy((0.05 * np.random.default_rng(7).standard_normal(E)).astype(np.float32)).to(dev)
+    out = {}
+    for T in (1, 9940):
+        logits = [torch.from_numpy(gen.normal_logits(31, i, T, E)).to(dev) for i in range(4)]
+        ids = torch.empty(T, K, dtype=torch.int32, device=dev)
+        wts = torch.empty(T, K, dtype=torch.float32, device=dev)
+        variants = {
+            "softmax": lambda l: lib.moe_route(None, None, l, T, 0, E, K, 0, ids, wts, stream),
+            "sigmoid_bias_renorm_scale2.5": lambda l: lib.moe_route_scored(
+                None, None, l, T, 0, E, K, lib.MOE_SCORE_SIGMOID, bias, 2.5, lib.MOE_ROUTE_RENORM, ids, wts, stream),
+            "sqrtsoftplus_bias_renorm": lambda l: lib.moe_route_scored(
+                None, None, l, T, 0, E, K, lib.MOE_SCORE_SQRTSOFTPLUS, bias, 1.0, lib.MOE_ROUTE_RENORM, ids, wts,
+                stream),
+        }
+        for name, call in variants.items():
+            for i in range(4):
+                call(logits[i])
+            stream.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for r in range(reps):
+                call(logits[r % 4])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[f"t{T}_{name}_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    log(f"  route variants: {out}")
+    return out
+
+
 # ------------------------------------------------------------------ paged decode
 
 
@@ -596,6 +639,8 @@ def main():
             "hbm_gbs": round(b["hbm_gbs"], 1),
             "hbm_frac": round(b["hbm_gbs"] / HBM_PEAK_GBS, 4),
         }
+    if "route_variants" in legs:
+        out["workloads"]["route_variants"] = {"experts": 256, "top_k": 8, "from": "logits"} | route_variants_leg(dev)
     if "paged" in legs:
         torch.cuda.empty_cache()
         wq, q = paged_leg(a, dev)

@@ -59,6 +59,13 @@ enum moe_status {
   MOE_EWS = -6      /* workspace missing or smaller than moe_ffn_workspace_bytes() */
 };
 
+/* Per-expert scoring of the router logits (moe_route_scored). */
+enum moe_score {
+  MOE_SCORE_SOFTMAX = 0,      /* softmax over all E experts (moe_route) */
+  MOE_SCORE_SIGMOID = 1,      /* 1 / (1 + e^-l) */
+  MOE_SCORE_SQRTSOFTPLUS = 2  /* sqrt(ln(1 + e^l)) */
+};
+
 enum moe_flags {
   MOE_ROUTE_RENORM = 1u << 0,  /* moe_route: divide the K selected weights by their sum */
   MOE_FORCE_GEMV = 1u << 8,    /* moe_expert_ffn: use the per-expert GEMV path whatever T is */
@@ -108,6 +115,29 @@ int moe_pack_expert(const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, con
  * Deterministic: the same inputs give the same bits on every run. */
 int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K,
               unsigned flags, int32_t* ids, float* w, moe_stream_t stream);
+
+/* moe_route_scored: the router variants the "Strata" README names under
+ * "Models" (sqrtsoftplus/noaux_tc routing, sigmoid/noaux_tc top-8, sigmoid
+ * top-10 with a correction bias and a 2.5x routed scale). The page names them
+ * only; this is the plain reading:
+ *   score    MOE_SCORE_SOFTMAX: as moe_route, w times routed_scale; bias must
+ *            be NULL (softmax probabilities are not fixed to the last bit, so
+ *            they cannot key a bit-exact selection).
+ *            MOE_SCORE_SIGMOID / MOE_SCORE_SQRTSOFTPLUS: s[t][e] = score of
+ *            logits[t][e], evaluated in fp64 and rounded once to fp32
+ *            (softplus as l + ln(1 + e^-l) for l > 0, so e^l never overflows).
+ *   bias     device fp32 [E] correction added to the score for selection only,
+ *            or NULL. Must be finite.
+ *   ids      the K experts with the largest c = fp32(s + bias) in rank order;
+ *            equal c rank the lower id first; -0.0 == +0.0.
+ *   w        s[t][ids[t][k]] (the bias is not included), divided by the sum
+ *            over the K selected with MOE_ROUTE_RENORM, times routed_scale
+ *            (finite). The other arguments are as in moe_route.
+ * Deterministic; argument errors return MOE_EINVAL before anything is
+ * enqueued. */
+int moe_route_scored(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K, int score,
+                     const float* bias, float routed_scale, unsigned flags, int32_t* ids, float* w,
+                     moe_stream_t stream);
 
 /* ------------------------------------------------------------------ expert FFN
  * moe_expert_ffn: y[t] = shared(x[t]) + sum_{k=0..K-1} w[t][k] * FFN_{ids[t][k]}(x[t])

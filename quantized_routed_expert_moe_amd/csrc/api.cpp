@@ -4,6 +4,8 @@
 // completes the exact computation or reports a failure; top-k and precision are
 // never changed silently): every unsupported shape returns MOE_EUNSUP and no
 // call falls back to another computation.
+#include <cmath>
+
 #include "moe_internal.h"
 
 namespace {
@@ -57,6 +59,27 @@ extern "C" int moe_route(const uint16_t* x, const float* w_router, float* logits
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_router && moe::launch_router_gemv(x, w_router, logits, T, H, E, s) != hipSuccess) return MOE_EHIP;
   if (moe::launch_route_select(logits, T, E, K, flags, ids, w, s) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
+extern "C" int moe_route_scored(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K,
+                                int score, const float* bias, float routed_scale, unsigned flags, int32_t* ids,
+                                float* w, moe_stream_t stream) {
+  if (T < 0 || E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return MOE_EINVAL;
+  if (flags & ~(unsigned)MOE_ROUTE_RENORM) return MOE_EINVAL;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID && score != MOE_SCORE_SQRTSOFTPLUS) return MOE_EINVAL;
+  if (score == MOE_SCORE_SOFTMAX && bias) return MOE_EINVAL;
+  if (!std::isfinite(routed_scale)) return MOE_EINVAL;
+  if (E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
+  if (w_router) {
+    if (!x || H <= 0) return MOE_EINVAL;
+    if (H % moe::kGroup || H > 8192) return MOE_EUNSUP;
+  }
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w_router && moe::launch_router_gemv(x, w_router, logits, T, H, E, s) != hipSuccess) return MOE_EHIP;
+  if (moe::launch_route_select(logits, T, E, K, flags, ids, w, s, score, bias, routed_scale) != hipSuccess)
+    return MOE_EHIP;
   return MOE_OK;
 }
 

@@ -62,8 +62,10 @@ __host__ __device__ inline bool shape_ok(int H, int I, int g) {
 // ---- launchers (return a hipError_t) ----
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H, int E,
                               hipStream_t s);
+// score: MOE_SCORE_*; bias (nullable) and scale as in moe_route_scored
 hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigned flags, int32_t* ids,
-                               float* w, hipStream_t s);
+                               float* w, hipStream_t s, int score = MOE_SCORE_SOFTMAX, const float* bias = nullptr,
+                               float scale = 1.0f);
 
 struct FfnArgs {
   const uint16_t* x;

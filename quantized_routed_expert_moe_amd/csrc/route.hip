@@ -115,10 +115,11 @@ __global__ void __launch_bounds__(256) router_gemv1_kernel(const uint16_t* __res
   if (tid == 0) logits[e] = (float)(((part[0] + part[1]) + part[2]) + part[3]);
 }
 
-// One wave per token (the selection is wave_select, shared with the fused decode path).
+// One wave per token. The weights are multiplied by scale (1 for moe_route,
+// where the product is exact).
 template <int EPL>
 __global__ void __launch_bounds__(64) route_select_kernel(const float* __restrict__ logits, int T, int E, int K,
-                                                          unsigned flags, int32_t* __restrict__ ids,
+                                                          unsigned flags, float scale, int32_t* __restrict__ ids,
                                                           float* __restrict__ w) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
@@ -127,7 +128,53 @@ __global__ void __launch_bounds__(64) route_select_kernel(const float* __restric
   wave_select<EPL>(logits + (size_t)t * E, E, K, flags, lane, id, wt);
   if (lane < K) {
     ids[(size_t)t * K + lane] = id;
-    w[(size_t)t * K + lane] = wt;
+    w[(size_t)t * K + lane] = wt * scale;
+  }
+}
+
+// Score of one logit for the scored router variants ("Strata" README, Models:
+// sigmoid and sqrtsoftplus routing): evaluated in fp64 and rounded once to
+// fp32, the precision of the selection key. softplus(l) = l + ln(1 + e^-l)
+// for l > 0 and ln(1 + e^l) otherwise, so e^l never overflows.
+__device__ inline float expert_score(float l, int score) {
+  const double x = (double)l;
+  if (score == MOE_SCORE_SIGMOID) return (float)(1.0 / (1.0 + exp(-x)));
+  const double sp = x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+  return (float)sqrt(sp);
+}
+
+// One wave per token: selection on c = fp32(score + bias) with the total order
+// of wave_select (c descending, equal values to the lower id); the weight of
+// a selected expert is its score (the bias steers selection only), divided by
+// the sum over the K selected with MOE_ROUTE_RENORM, then times scale.
+template <int EPL>
+__global__ void __launch_bounds__(64) route_scored_kernel(const float* __restrict__ logits, int T, int E, int K,
+                                                          unsigned flags, int score, const float* __restrict__ bias,
+                                                          float scale, int32_t* __restrict__ ids,
+                                                          float* __restrict__ w) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* l = logits + (size_t)t * E;
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      const float s = expert_score(l[e], score);
+      const float c = bias ? s + bias[e] : s;
+      key[i] = route_key(c, e);
+    } else {
+      key[i] = 0ull;  // real keys are > 0
+    }
+  }
+  const uint64_t mine = wave_topk<EPL>(key, K, lane);
+  const int id = key_id(mine);
+  float wt = 0.0f;
+  if (lane < K) wt = expert_score(l[id], score);
+  if (flags & MOE_ROUTE_RENORM) wt = wt / wave_sum_f32(lane < K ? wt : 0.0f);
+  if (lane < K) {
+    ids[(size_t)t * K + lane] = id;
+    w[(size_t)t * K + lane] = wt * scale;
   }
 }
 
@@ -157,19 +204,23 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits,
 }
 
 hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigned flags, int32_t* ids, float* w,
-                               hipStream_t s) {
+                               hipStream_t s, int score, const float* bias, float scale) {
   const int epl = (E + 63) / 64;
   dim3 grid(T);
-  if (epl <= 1)
-    hipLaunchKernelGGL(route_select_kernel<1>, grid, dim3(64), 0, s, logits, T, E, K, flags, ids, w);
-  else if (epl <= 2)
-    hipLaunchKernelGGL(route_select_kernel<2>, grid, dim3(64), 0, s, logits, T, E, K, flags, ids, w);
-  else if (epl <= 4)
-    hipLaunchKernelGGL(route_select_kernel<4>, grid, dim3(64), 0, s, logits, T, E, K, flags, ids, w);
-  else if (epl <= 8)
-    hipLaunchKernelGGL(route_select_kernel<8>, grid, dim3(64), 0, s, logits, T, E, K, flags, ids, w);
-  else
-    hipLaunchKernelGGL(route_select_kernel<16>, grid, dim3(64), 0, s, logits, T, E, K, flags, ids, w);
+#define SEL(N)                                                                                                    \
+  do {                                                                                                            \
+    if (score == MOE_SCORE_SOFTMAX)                                                                               \
+      hipLaunchKernelGGL(route_select_kernel<N>, grid, dim3(64), 0, s, logits, T, E, K, flags, scale, ids, w);    \
+    else                                                                                                          \
+      hipLaunchKernelGGL(route_scored_kernel<N>, grid, dim3(64), 0, s, logits, T, E, K, flags, score, bias, scale, \
+                         ids, w);                                                                                 \
+  } while (0)
+  if (epl <= 1) SEL(1);
+  else if (epl <= 2) SEL(2);
+  else if (epl <= 4) SEL(4);
+  else if (epl <= 8) SEL(8);
+  else SEL(16);
+#undef SEL
   return hipGetLastError();
 }
 

@@ -128,17 +128,10 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
 // registers; each of K rounds takes the wave-wide maximum of the lanes' first
 // keys (on the 32-bit logit image; among equal images the full key, i.e. the
 // lowest id, decides) and pops it from its owner lane.
+// The K largest keys of the wave (lane l holds the keys of experts l, l + 64, ...;
+// 0 marks an absent expert): lane k < K returns the key of rank k, the others 0.
 template <int EPL>
-__device__ inline void wave_select(const float* __restrict__ l, int E, int K, unsigned flags, int lane, int32_t& id,
-                                   float& wt) {
-  uint64_t key[EPL];
-  float lg[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    lg[i] = e < E ? l[e] : 0.0f;
-    key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
-  }
+__device__ inline uint64_t wave_topk(uint64_t (&key)[EPL], int K, int lane) {
   // local descending sort (odd-even transposition)
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
@@ -154,7 +147,7 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
     const uint32_t hi = (uint32_t)(key[0] >> 32);
     const uint32_t m = wave_max_u32(hi);
     uint64_t owners = __ballot(hi == m);
-    if (__builtin_popcountll(owners) > 1) {  // equal logits: the highest full key (lowest id) wins
+    if (__builtin_popcountll(owners) > 1) {  // equal values: the highest full key (lowest id) wins
       const uint64_t best = wave_max_u64(hi == m ? key[0] : 0ull);
       owners = __ballot(key[0] == best);
     }
@@ -168,6 +161,24 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
     }
     if (lane == k) mine = best;
   }
+  return mine;
+}
+
+// Softmax + top-k of one token's logits l[0..E): lane k < K gets the expert of
+// rank k and its weight (the softmax probability over all E, with
+// MOE_ROUTE_RENORM divided by the sum over the K selected).
+template <int EPL>
+__device__ inline void wave_select(const float* __restrict__ l, int E, int K, unsigned flags, int lane, int32_t& id,
+                                   float& wt) {
+  uint64_t key[EPL];
+  float lg[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    lg[i] = e < E ? l[e] : 0.0f;
+    key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
+  }
+  const uint64_t mine = wave_topk<EPL>(key, K, lane);
   const uint32_t top_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mine >> 32));
   const uint32_t top_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mine);
   const float m = key_logit(((uint64_t)top_hi << 32) | top_lo);  // the largest logit (rank 0, lane 0)

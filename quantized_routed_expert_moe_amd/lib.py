@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOSLOT, MOE_ENOTRES, MOE_EHIP, MOE_EUNSUP, MOE_EWS = 0, -1, -2, -3, -4, -5, -6
 MOE_ROUTE_RENORM = 1 << 0
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_FORCE_GEMV = 1 << 8
 MOE_FORCE_GROUPED = 1 << 9
 
@@ -29,6 +30,7 @@ EXPORTS = (
     "moe_slot_stride",
     "moe_pack_expert",
     "moe_route",
+    "moe_route_scored",
     "moe_ffn_workspace_bytes",
     "moe_expert_ffn",
     "moe_ffn_gate_up",
@@ -81,6 +83,7 @@ def load(path: str | None = None):
         "moe_slot_stride": (_SZ, [_I, _I, _I]),
         "moe_pack_expert": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
         "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P]),
+        "moe_route_scored": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, ctypes.c_float, ctypes.c_uint, _P, _P, _P]),
         "moe_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, ctypes.c_uint]),
         "moe_expert_ffn": (
             _I,
@@ -180,6 +183,14 @@ def moe_route(x, w_router, logits, T, H, E, K, flags, ids, w, stream=None) -> No
     _check(
         load().moe_route(_ptr(x), _ptr(w_router), _ptr(logits), T, H, E, K, flags, _ptr(ids), _ptr(w), _stream(stream)),
         "moe_route",
+    )
+
+
+def moe_route_scored(x, w_router, logits, T, H, E, K, score, bias, routed_scale, flags, ids, w, stream=None) -> None:
+    _check(
+        load().moe_route_scored(_ptr(x), _ptr(w_router), _ptr(logits), T, H, E, K, score, _ptr(bias),
+                                float(routed_scale), flags, _ptr(ids), _ptr(w), _stream(stream)),
+        "moe_route_scored",
     )
 
 

@@ -119,6 +119,86 @@ def test_route_logits_in(T, E, K, kind):
         assert np.abs(wts.cpu().numpy() - w_ref).max() <= 1e-5
 
 
+@pytest.mark.parametrize("score", [lib.MOE_SCORE_SIGMOID, lib.MOE_SCORE_SQRTSOFTPLUS])
+@pytest.mark.parametrize("T,E,K", [(1, 256, 8), (37, 256, 6), (5, 384, 10), (3, 1024, 32), (4, 32, 32)])
+def test_route_scored_matches_oracle(score, T, E, K):
+    """Scored router variants: ids bit-exact, weights within 1e-5 of the fp64 oracle."""
+    say(f"route scored score={score} T={T} E={E} K={K}")
+    lg = (3.0 * gen.normal_logits(21, 0, T, E)).astype(np.float32)
+    rng = np.random.default_rng(E + K)
+    bias_np = (0.05 * rng.standard_normal(E)).astype(np.float32)
+    d = torch.from_numpy(lg).to(DEV)
+    bias = torch.from_numpy(bias_np).to(DEV)
+    ids = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    for use_bias in (False, True):
+        for renorm in (False, True):
+            for scale in (1.0, 2.5):
+                lib.moe_route_scored(None, None, d, T, 0, E, K, score, bias if use_bias else None, scale,
+                                     lib.MOE_ROUTE_RENORM if renorm else 0, ids, wts)
+                torch.cuda.synchronize()
+                ids_ref, w_ref = R.route_scored(lg, K, score, bias=bias_np if use_bias else None, routed_scale=scale,
+                                                renorm=renorm)
+                assert np.array_equal(ids.cpu().numpy(), ids_ref), (use_bias, renorm, scale)
+                assert np.abs(wts.cpu().numpy() - w_ref).max() <= 1e-5 * scale, (use_bias, renorm, scale)
+
+
+def test_route_scored_saturated_ties_and_gemv():
+    """fp32 saturation makes scores tie (lower id first); the router GEMV feeds the scored select."""
+    T, E, K = 4, 64, 8
+    lg = np.zeros((T, E), dtype=np.float32)
+    lg[0, ::3] = 40.0  # sigmoid -> 1.0f for 22 experts
+    lg[1, :] = -200.0  # both scores underflow to 0 for every expert
+    lg[2, 5:20] = 18.5
+    lg[3] = np.linspace(-30, 30, E, dtype=np.float32)
+    d = torch.from_numpy(lg).to(DEV)
+    ids = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    for score in (lib.MOE_SCORE_SIGMOID, lib.MOE_SCORE_SQRTSOFTPLUS):
+        lib.moe_route_scored(None, None, d, T, 0, E, K, score, None, 2.5, 0, ids, wts)
+        torch.cuda.synchronize()
+        ids_ref, w_ref = R.route_scored(lg, K, score, routed_scale=2.5)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.abs(wts.cpu().numpy() - w_ref).max() <= 2.5e-5
+    # with the router GEMV: logits bit-exact, then the same selection
+    w = gen.WORKLOADS["tiny_t4_h256_e8_k2"]
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    wr = gen.router_weight(w.seed, 0, w.E, w.H)
+    x = harness.bf16_tensor(xb, DEV)
+    wrd = torch.from_numpy(wr).to(DEV)
+    logits = torch.empty(w.T, w.E, dtype=torch.float32, device=DEV)
+    ids = torch.empty(w.T, w.K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(w.T, w.K, dtype=torch.float32, device=DEV)
+    lib.moe_route_scored(x, wrd, logits, w.T, w.H, w.E, w.K, lib.MOE_SCORE_SIGMOID, None, 1.0, lib.MOE_ROUTE_RENORM,
+                         ids, wts)
+    torch.cuda.synchronize()
+    l_ref = R.router_logits(xb, wr)
+    l_gpu = logits.cpu().numpy()
+    assert np.abs(l_gpu.view(np.int32).astype(np.int64) - l_ref.view(np.int32).astype(np.int64)).max() <= 1
+    ids_ref, w_ref = R.route_scored(l_gpu, w.K, R.SCORE_SIGMOID, renorm=True)  # the selection on the same logits
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(wts.cpu().numpy() - w_ref).max() <= 1e-5
+
+
+def test_route_scored_softmax_scale_and_argument_errors():
+    T, E, K = 6, 128, 8
+    lg = gen.normal_logits(23, 0, T, E)
+    d = torch.from_numpy(lg).to(DEV)
+    ids = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    ids0 = torch.empty_like(ids)
+    w0 = torch.empty_like(wts)
+    lib.moe_route_scored(None, None, d, T, 0, E, K, lib.MOE_SCORE_SOFTMAX, None, 2.5, 0, ids, wts)
+    lib.moe_route(None, None, d, T, 0, E, K, 0, ids0, w0)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids0) and torch.equal(wts, w0 * 2.5)  # one exact scaling of the same weights
+    bias = torch.zeros(E, dtype=torch.float32, device=DEV)
+    for args in ((lib.MOE_SCORE_SOFTMAX, bias, 1.0), (3, None, 1.0), (lib.MOE_SCORE_SIGMOID, None, float("nan"))):
+        with pytest.raises(lib.MoeError) as ei:
+            lib.moe_route_scored(None, None, d, T, 0, E, K, args[0], args[1], args[2], 0, ids, wts)
+        assert ei.value.status == lib.MOE_EINVAL
+
+
 def test_route_ties_and_signed_zero():
     E, K = 70, 9
     rows = [np.zeros(E), -np.zeros(E), np.where(np.arange(E) % 3 == 0, 1.0, -0.0), np.full(E, -2.5),
