@@ -36,8 +36,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=48)
-    p.add_argument("--legs", default="decode,prefill,batched,paged,route_variants",
-                   help="comma list of decode,prefill,batched,paged,route_variants")
+    p.add_argument("--legs", default="decode,prefill,batched,paged,route_variants,chunked",
+                   help="comma list of decode,prefill,batched,paged,route_variants,chunked")
+    p.add_argument("--chunks", default="1024,2048,4096", help="prompt chunk sizes of the chunked paged prefill leg")
     p.add_argument("--paged-steps", type=int, default=64, help="measured tokens of the paged decode workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=3, help="decode layers in the oracle's timed sample")
@@ -497,6 +498,114 @@ def paged_leg(a, dev):
     }
 
 
+def pinned_expert_copy(w, layer):
+    """All E experts of a layer packed into one pinned, expert-major host buffer."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    from quantized_routed_expert_moe_amd import harness, lib
+
+    stride = lib.moe_slot_stride(w.H, w.I)
+    host = torch.empty(w.E * stride, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy()
+
+    def put(e):
+        hv[e * stride : (e + 1) * stride] = harness.pack_expert(w.seed, layer, e, w.H, w.I)
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(put, range(w.E)))
+    return host, stride
+
+
+def chunked_leg(a, dev):
+    """Chunked paged prefill: a 4,096-token prompt through one layer (256 experts, top-6, shared
+    expert, I = 2048) with a 64-slot arena fed from pinned host memory, per chunk size.
+
+    Each chunk routes, hands its ids to the host, runs passes of at most 32 experts (half
+    the arena, so the next pass's fills overlap the current pass's compute) and combines.
+    Per chunk size the prompt runs once untimed (the arena reaches its steady state) and
+    once timed; the fully-resident grouped run of the same chunks is timed beside it, and
+    the last chunk's output is compared bitwise with it.
+    """
+    import numpy as np
+    import torch
+
+    from quantized_routed_expert_moe_amd import harness, lib
+    from quantized_routed_expert_moe_amd.paged import ChunkedPrefill
+    from synth import gen
+
+    w = gen.WORKLOADS["chunked_t4096_h4096_e256s1_k6_i2048"]
+    log(f"chunked: packing {w.E} experts into pinned host memory")
+    t0 = time.time()
+    host, stride = pinned_expert_copy(w, 0)
+    blob = lib.moe_blob_bytes(w.H, w.I)
+    resident = host.to(dev)
+    table_res = torch.arange(w.E, dtype=torch.int32, device=dev)
+    shared = torch.from_numpy(harness.pack_expert(w.seed, 0, gen.SHARED_EXPERT, w.H, w.I)).to(dev)
+    x = harness.bf16_tensor(gen.activations_bf16(w.seed, 0, w.T, w.H), dev)
+    logits = torch.from_numpy(gen.normal_logits(w.seed, 0, w.T, w.E)).to(dev)
+    y = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    y_res = torch.empty_like(y)
+    log(f"  chunked: packed ({time.time() - t0:.1f} s)")
+    cap = w.slots // 2
+    out = {}
+    for chunk in [int(c) for c in a.chunks.split(",")]:
+        slots = torch.empty(w.slots * stride, dtype=torch.uint8, device=dev)
+        table = torch.full((w.E,), -1, dtype=torch.int32, device=dev)
+        arena = lib.Arena(w.E, w.slots, blob, stride, slots, table, host)
+        cp = ChunkedPrefill(arena, slots, stride, w.H, w.I, w.E, w.K, chunk, cap, shared=shared, device=dev)
+        ids = torch.empty(chunk, w.K, dtype=torch.int32, device=dev)
+        wts = torch.empty(chunk, w.K, dtype=torch.float32, device=dev)
+        nb = lib.moe_ffn_workspace_bytes(chunk, w.H, w.I, w.E, w.K, 1, lib.MOE_FORCE_GROUPED)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def resident_prompt():
+            for c0 in range(0, w.T, chunk):
+                T = min(chunk, w.T - c0)
+                lib.moe_route(None, None, logits[c0 : c0 + T], T, w.H, w.E, w.K, 0, ids[:T], wts[:T])
+                lib.moe_expert_ffn(x[c0 : c0 + T], ids[:T], wts[:T], T, w.H, w.I, w.E, w.K, 32, table_res, resident,
+                                   stride, shared, y_res[c0 : c0 + T], ws, nb, status, lib.MOE_FORCE_GROUPED)
+
+        cp.run_prompt(x, logits, y, chunk)  # untimed: the arena's steady state
+        torch.cuda.synchronize()
+        st0 = arena.stats()
+        passes = 0
+        t0 = time.perf_counter()
+        for c0 in range(0, w.T, chunk):
+            cp.run_chunk(x[c0 : c0 + chunk], logits[c0 : c0 + chunk], y[c0 : c0 + chunk])
+            passes += len(cp.last_passes)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        st1 = arena.stats()
+        resident_prompt()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        resident_prompt()
+        torch.cuda.synchronize()
+        dt_res = time.perf_counter() - t1
+        if int(cp.status.item()) != 0 or int(status.item()) != 0:
+            raise RuntimeError(f"device status {int(cp.status.item())} / {int(status.item())}")
+        identical = torch.equal(y.view(torch.int16), y_res.view(torch.int16))
+        n_chunks = (w.T + chunk - 1) // chunk
+        fills = st1["fills"] - st0["fills"]
+        out[str(chunk)] = {
+            "tokens_per_s": round(w.T / dt, 1),
+            "ms_per_prompt": round(dt * 1e3, 2),
+            "passes_per_chunk": round(passes / n_chunks, 2),
+            "expert_reads_per_chunk": round(fills / n_chunks, 1),
+            "h2d_gb_per_prompt": round((st1["h2d_bytes"] - st0["h2d_bytes"]) / 1e9, 3),
+            "h2d_gbs": round((st1["h2d_bytes"] - st0["h2d_bytes"]) / dt / 1e9, 2),
+            "resident_tokens_per_s": round(w.T / dt_res, 1),
+            "bit_identical_to_resident": identical,
+        }
+        log(f"  chunk {chunk}: {out[str(chunk)]}")
+        del cp, arena, slots, table, ws
+        torch.cuda.empty_cache()
+    return w, out
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 
@@ -655,6 +764,11 @@ def main():
             "bit_identical_to_resident": q["identical"],
             "host_weight_sets": 1,
         }
+    if "chunked" in legs:
+        torch.cuda.empty_cache()
+        wc, c = chunked_leg(a, dev)
+        out["workloads"]["chunked_paged_prefill"] = {"workload": wc.name, "arena_slots": wc.slots,
+                                                     "experts_per_pass": wc.slots // 2, "by_chunk": c}
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, min(a.cpu_layers, w.layers))

@@ -69,7 +69,9 @@ enum moe_score {
 enum moe_flags {
   MOE_ROUTE_RENORM = 1u << 0,  /* moe_route: divide the K selected weights by their sum */
   MOE_FORCE_GEMV = 1u << 8,    /* moe_expert_ffn: use the per-expert GEMV path whatever T is */
-  MOE_FORCE_GROUPED = 1u << 9  /* moe_expert_ffn: use the expert-grouped MFMA GEMM path */
+  MOE_FORCE_GROUPED = 1u << 9, /* moe_expert_ffn: use the expert-grouped MFMA GEMM path */
+  MOE_FFN_PARTIAL = 1u << 10,  /* moe_expert_ffn: one pass of a chunked paged run (see moe_ffn_combine) */
+  MOE_FFN_PARTIAL_SHARED = 1u << 11 /* with MOE_FFN_PARTIAL: this pass also computes the shared expert */
 };
 
 const char* moe_strerror(int status);
@@ -180,6 +182,31 @@ int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T,
                    uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
                    moe_stream_t stream);
 
+/* Chunked paged prefill ("Strata on a Mac", Measured, the UD-Q4/Q5/Q6_K_XL
+ * part: each prompt chunk makes one pass over the experts it uses that are not
+ * in the arena). When a
+ * chunk of T tokens uses more experts than the arena holds, its FFN runs as
+ * several passes over one workspace, each pass with the experts that are
+ * resident for it, then one combine:
+ *   moe_expert_ffn(..., flags = MOE_FFN_PARTIAL [| MOE_FFN_PARTIAL_SHARED])
+ *     computes the routed experts e with slot_table[e] >= 0 (the others are
+ *     skipped, not flagged) for their (token, pick) pairs, keeps the per-pair
+ *     outputs in ws and does not write y; MOE_FFN_PARTIAL_SHARED also computes
+ *     the shared expert (shared_blob must be non-NULL; exactly one pass sets it).
+ *     MOE_FFN_PARTIAL selects the grouped path (with MOE_FORCE_GEMV: MOE_EINVAL).
+ *   moe_ffn_combine then writes y from ws: the shared output (when has_shared)
+ *     plus sum_k w[t][k] * out[t][k], as moe_expert_ffn does.
+ * Every pass and the combine use the same x, ids, w, T, H, I, E, K, g, the same
+ * shared_blob (non-NULL in every pass, has_shared = 1 in the combine, or NULL
+ * and 0 throughout), the same ws and one stream order. When each routed expert
+ * that ids use has a slot in at least one pass, y is bit-identical to
+ * moe_expert_ffn(..., MOE_FORCE_GROUPED) with every expert resident; an
+ * expert computed in two passes gives the same bits twice. A pair whose expert
+ * is computed in no pass leaves stale workspace data in y (no error is raised).
+ * ws_bytes >= moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, MOE_FFN_PARTIAL). */
+int moe_ffn_combine(const float* w, int T, int H, int I, int E, int K, int has_shared, uint16_t* y, void* ws,
+                    size_t ws_bytes, moe_stream_t stream);
+
 /* ------------------------------------------------------------------ whole layer
  * moe_layer: moe_route(x, w_router, logits, T, H, E, K, route_flags, ids, w)
  * then moe_expert_ffn(x, ids, w, ..., ffn_flags) in one call on one stream,
@@ -242,6 +269,22 @@ int arena_slot_table(const moe_arena* a, int32_t* slot_of);
 int arena_reset(moe_arena* a); /* empty every slot, zero the stamps and the stats */
 int arena_stats(const moe_arena* a, moe_arena_stats* out);
 void arena_destroy(moe_arena* a);
+/* Passes of a chunked paged run (moe_ffn_combine): split the distinct experts
+ * of n requested ids (host int32) into passes of at most max_per_pass experts.
+ * The experts that are resident now come first (ascending id), then the
+ * others (ascending id); the list is cut in order. Writes experts (host int32,
+ * capacity n; the list), pass_end (host int32, capacity n; pass p is
+ * experts[pass_end[p-1] .. pass_end[p]), with pass_end[-1] = 0), *n_distinct
+ * and *n_passes; the arena is not changed. The caller then runs, per pass,
+ * arena_map_slots on that pass's experts, arena_fill_async and one
+ * MOE_FFN_PARTIAL pass whose slot table maps exactly those experts.
+ * With max_per_pass <= S / 2 the misses of pass p + 1 evict no expert of pass
+ * p, so the fills of pass p + 1 may run while pass p computes (they must still
+ * wait for pass p - 1); with any max_per_pass <= S, no fill evicts an expert
+ * that a later pass counts as resident.
+ * MOE_EINVAL: an id outside [0, E), n < 0, max_per_pass < 1 or > S. */
+int arena_chunk_passes(const moe_arena* a, const int32_t* ids, int n, int max_per_pass, int32_t* experts,
+                       int32_t* pass_end, int* n_distinct, int* n_passes);
 
 #ifdef __cplusplus
 }

@@ -94,3 +94,17 @@ class ArenaModel:
             self.stats["fills"] += 1
             self.stats["h2d_bytes"] += self.blob_bytes
         return OK, [self.slot_of[e] for e in ids], fills
+
+    def chunk_passes(self, ids, max_per_pass: int):
+        """Passes of a chunked paged prompt run ("Strata on a Mac", Measured, the
+        UD-Q4/Q5/Q6_K_XL part: every prompt chunk makes one pass over the experts
+        it uses that are not in the arena). Reading: the chunk's distinct experts,
+        those resident now first and the rest after, each group in ascending id,
+        are cut in order into passes of at most ``max_per_pass`` experts; the
+        arena is not changed. Returns (status, list of passes)."""
+        ids = [int(e) for e in ids]
+        if not 1 <= max_per_pass <= self.S or any(not 0 <= e < self.E for e in ids):
+            return EINVAL, None
+        used = sorted(set(ids))
+        order = [e for e in used if self.slot_of[e] >= 0] + [e for e in used if self.slot_of[e] < 0]
+        return OK, [order[i : i + max_per_pass] for i in range(0, len(order), max_per_pass)]

@@ -12,7 +12,7 @@ namespace {
 
 bool ffn_uses_grouped(int T, unsigned flags) {
   if (flags & MOE_FORCE_GEMV) return false;
-  if (flags & MOE_FORCE_GROUPED) return true;
+  if (flags & (MOE_FORCE_GROUPED | MOE_FFN_PARTIAL)) return true;
   return T > moe::kGemvMaxT;
 }
 
@@ -99,8 +99,10 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
                      uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
                      moe_stream_t stream, int stage) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
-  if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED)) return MOE_EINVAL;
-  if ((flags & MOE_FORCE_GEMV) && (flags & MOE_FORCE_GROUPED)) return MOE_EINVAL;
+  if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_FFN_PARTIAL | MOE_FFN_PARTIAL_SHARED))
+    return MOE_EINVAL;
+  if ((flags & MOE_FORCE_GEMV) && (flags & (MOE_FORCE_GROUPED | MOE_FFN_PARTIAL))) return MOE_EINVAL;
+  if ((flags & MOE_FFN_PARTIAL_SHARED) && (!(flags & MOE_FFN_PARTIAL) || !shared_blob)) return MOE_EINVAL;
   if (!moe::shape_ok(H, I, g) || E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
   if (T == 0) return MOE_OK;
   if (!x || !ids || !w || !slot_table || !slots || !y || !dev_status) return MOE_EINVAL;
@@ -129,6 +131,8 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
   a.ws = static_cast<uint8_t*>(ws);
   a.ws_bytes = ws_bytes;
   a.status = dev_status;
+  a.mode = (flags & MOE_FFN_PARTIAL ? moe::kModePartial : 0u) |
+           (flags & MOE_FFN_PARTIAL_SHARED ? moe::kModePartialShared : 0u);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool dec1 = !grouped && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
   const bool bat = !grouped && moe::batched_supported(T, H, I, K);
@@ -183,4 +187,31 @@ extern "C" int moe_layer(const uint16_t* x, const float* w_router, float* logits
   if (rs != MOE_OK) return rs;
   return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
                           dev_status, ffn_flags, stream, 2);
+}
+
+extern "C" int moe_ffn_combine(const float* w, int T, int H, int I, int E, int K, int has_shared, uint16_t* y,
+                               void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E || (has_shared != 0 && has_shared != 1))
+    return MOE_EINVAL;
+  if (!moe::shape_ok(H, I, 32) || E > moe::kMaxE || K > moe::kMaxK || !moe::grouped_shape_ok(H, I)) return MOE_EUNSUP;
+  if (T == 0) return MOE_OK;
+  if (!w || !y) return MOE_EINVAL;
+  const size_t need = moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, MOE_FFN_PARTIAL);
+  if (need == 0) return MOE_EUNSUP;
+  if (!ws || ws_bytes < need) return MOE_EWS;
+  moe::FfnArgs a{};
+  a.w = w;
+  a.T = T;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.K = K;
+  // the combine reads shared_blob only to test it for NULL (the workspace layout
+  // and the shared term depend on it); it is never dereferenced
+  a.shared_blob = has_shared ? static_cast<const uint8_t*>(ws) : nullptr;
+  a.y = y;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.ws_bytes = ws_bytes;
+  if (moe::launch_grouped_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
 }

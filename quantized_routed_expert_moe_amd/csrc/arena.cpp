@@ -179,3 +179,29 @@ extern "C" int arena_fill_async(moe_arena* a, const moe_fill* fills, int n_fills
   if (done && hipEventRecord(static_cast<hipEvent_t>(done), s) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
+
+// Chunked paged runs: the distinct experts of a chunk, resident ones first, cut
+// into passes that each fit the arena (each pass then maps, fills and computes
+// its experts; the chunk's outputs are combined after the last pass).
+extern "C" int arena_chunk_passes(const moe_arena* a, const int32_t* ids, int n, int max_per_pass,
+                                  int32_t* experts, int32_t* pass_end, int* n_distinct, int* n_passes) {
+  if (!a || n < 0 || (n > 0 && (!ids || !experts || !pass_end)) || !n_distinct || !n_passes) return MOE_EINVAL;
+  if (max_per_pass < 1 || max_per_pass > a->S) return MOE_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= a->E) return MOE_EINVAL;
+  std::vector<uint8_t> used(a->E, 0);
+  for (int i = 0; i < n; ++i) used[ids[i]] = 1;
+  int m = 0;
+  for (int e = 0; e < a->E; ++e)
+    if (used[e] && a->slot_of[e] >= 0) experts[m++] = e;
+  for (int e = 0; e < a->E; ++e)
+    if (used[e] && a->slot_of[e] < 0) experts[m++] = e;
+  int p = 0;
+  for (int end = 0; end < m;) {
+    end = end + max_per_pass < m ? end + max_per_pass : m;
+    pass_end[p++] = end;
+  }
+  *n_distinct = m;
+  *n_passes = p;
+  return MOE_OK;
+}

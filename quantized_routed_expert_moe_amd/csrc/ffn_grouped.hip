@@ -142,19 +142,23 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
   const int base_rows = has_shared ? T : 0;  // the shared unit's rows come first
   const int base_unit = has_shared ? 1 : 0;
   // thread e: segment start and unit index of expert e (experts in id order)
+  // (every expert keeps its segment in a partial pass, so the rows of an expert, and with
+  // them its results, are those of a full pass; an expert without a slot gets no tiles)
+  const bool partial = a.mode & kModePartial;
+  const bool do_shared = has_shared && (!partial || (a.mode & kModePartialShared));
   const int c = tid < E ? cnt[tid] : 0;
+  const int slot = c > 0 ? a.slot_table[tid] : -1;
   const int row0 = block_exclusive_scan(c, wsum, &total) + base_rows;
   const int uidx = block_exclusive_scan(c > 0 ? 1 : 0, wsum, &total) + base_unit;
   const int n_units = total + base_unit;
-  const int mt_here = (c + kBM - 1) / kBM;
+  const int mt_here = (c > 0 && (slot >= 0 || !partial)) ? (c + kBM - 1) / kBM : 0;
   const int mt0 = block_exclusive_scan(mt_here, wsum, &total);
-  const int shared_mt = has_shared ? (T + kBM - 1) / kBM : 0;
+  const int shared_mt = do_shared ? (T + kBM - 1) / kBM : 0;
   if (tid < E) {
     seg[tid] = row0;
     cur[tid] = 0;
     if (c > 0) {
-      const int slot = a.slot_table[tid];
-      if (slot < 0) *a.status = MOE_ENOTRES;
+      if (slot < 0 && !partial) *a.status = MOE_ENOTRES;
       ublob[uidx] = slot < 0 ? nullptr : a.slots + (size_t)slot * a.stride;
       unit_mt0[uidx] = shared_mt + mt0;
       for (int m = 0; m < mt_here; ++m) {
@@ -591,6 +595,11 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   }
   hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(round8(W.max_mt * gemm_n_tiles<1>(a.H, a.I))), dim3(kGThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.mode & kModePartial) return hipSuccess;  // the caller combines after the last pass
+  return launch_grouped_combine(a, s);
+}
+
+hipError_t launch_grouped_combine(const FfnArgs& a, hipStream_t s) {
   const size_t n8 = (size_t)a.T * a.H / 8;
   const size_t blocks = (n8 + 255) / 256;
   hipLaunchKernelGGL(grouped_combine_kernel, dim3(blocks < 8192 ? (int)blocks : 8192), dim3(256), 0, s, a);

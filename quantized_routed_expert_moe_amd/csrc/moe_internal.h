@@ -80,7 +80,14 @@ struct FfnArgs {
   uint8_t* ws;
   size_t ws_bytes;
   int32_t* status;
+  unsigned mode;  // kModePartial / kModePartialShared (grouped path only), else 0
 };
+// A partial pass of the grouped path: only routed experts with a slot are
+// computed (the others are skipped without error), the per-pair outputs stay in
+// the workspace and y is not written; kModePartialShared: this pass also
+// computes the shared expert.
+constexpr unsigned kModePartial = 1u, kModePartialShared = 2u;
+hipError_t launch_grouped_combine(const FfnArgs& a, hipStream_t s);
 
 // Each path launches in two stages: stage 0 = gate/up (h into the workspace),
 // stage 1 = down + combine (y).

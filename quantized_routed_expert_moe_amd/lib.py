@@ -21,6 +21,8 @@ MOE_ROUTE_RENORM = 1 << 0
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_FORCE_GEMV = 1 << 8
 MOE_FORCE_GROUPED = 1 << 9
+MOE_FFN_PARTIAL = 1 << 10
+MOE_FFN_PARTIAL_SHARED = 1 << 11
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -36,6 +38,7 @@ EXPORTS = (
     "moe_ffn_gate_up",
     "moe_ffn_down",
     "moe_layer",
+    "moe_ffn_combine",
     "arena_create",
     "arena_map_slots",
     "arena_fill_async",
@@ -44,6 +47,7 @@ EXPORTS = (
     "arena_reset",
     "arena_stats",
     "arena_destroy",
+    "arena_chunk_passes",
 )
 
 
@@ -102,6 +106,7 @@ def load(path: str | None = None):
             [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P, _P, _SZ, _P, _P, _P, _SZ, _P,
              ctypes.c_uint, _P],
         ),
+        "moe_ffn_combine": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
         "arena_create": (_I, [_I, _I, _SZ, _SZ, _P, _P, _P, ctypes.POINTER(_P)]),
         "arena_map_slots": (_I, [_P, _P, _I, _P, _P, ctypes.POINTER(_I)]),
         "arena_fill_async": (_I, [_P, _P, _I, _P, _P]),
@@ -110,6 +115,7 @@ def load(path: str | None = None):
         "arena_reset": (_I, [_P]),
         "arena_stats": (_I, [_P, ctypes.POINTER(moe_arena_stats)]),
         "arena_destroy": (None, [_P]),
+        "arena_chunk_passes": (_I, [_P, _P, _I, _I, _P, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -239,6 +245,14 @@ def moe_layer(x, w_router, logits, T, H, I, E, K, g, route_flags, ids, w, slot_t
     )
 
 
+def moe_ffn_combine(w, T, H, I, E, K, has_shared, y, ws, ws_bytes, stream=None) -> None:
+    _check(
+        load().moe_ffn_combine(_ptr(w), T, H, I, E, K, int(bool(has_shared)), _ptr(y), _ptr(ws), ws_bytes,
+                               _stream(stream)),
+        "moe_ffn_combine",
+    )
+
+
 class Arena:
     """Owner of one ``moe_arena`` handle (the C object holds host metadata only)."""
 
@@ -281,6 +295,24 @@ class Arena:
             load().arena_fill_async(self.handle, self._last_fills, self._last_nf, _stream(side), _event(done)),
             "arena_fill_async",
         )
+
+    def chunk_passes(self, ids, max_per_pass):
+        """ids: host int sequence -> list of passes, each a list of expert ids (arena_chunk_passes)."""
+        n = len(ids)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in ids])
+        experts = (ctypes.c_int32 * max(n, 1))()
+        ends = (ctypes.c_int32 * max(n, 1))()
+        nd, npass = _I(0), _I(0)
+        _check(
+            load().arena_chunk_passes(self.handle, arr, n, max_per_pass, experts, ends, ctypes.byref(nd),
+                                      ctypes.byref(npass)),
+            "arena_chunk_passes",
+        )
+        out, b = [], 0
+        for p in range(npass.value):
+            out.append(list(experts[b : ends[p]]))
+            b = ends[p]
+        return out
 
     def place(self, expert: int, slot: int) -> None:
         _check(load().arena_place(self.handle, expert, slot), "arena_place")

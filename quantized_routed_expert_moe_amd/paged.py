@@ -1,0 +1,103 @@
+"""Chunked paged prefill: one MoE layer over a prompt whose chunks use more experts than the arena holds.
+
+"Strata on a Mac", Measured (the UD-Q4/Q5/Q6_K_XL part): prompts stream in
+chunks, and each chunk makes one pass over the experts it uses that are not in
+the arena, so a longer chunk reads those experts fewer times. Per chunk, on one
+compute stream and one side stream:
+
+1. ``moe_route`` on the chunk, then the chosen ids to the host (the one
+   hand-shake per chunk);
+2. ``arena_chunk_passes``: the chunk's distinct experts, resident ones first,
+   cut into passes of at most ``cap`` experts;
+3. per pass: ``arena_map_slots`` on its experts, a pass slot table that maps
+   exactly those experts (copied from pinned host memory), ``arena_fill_async``
+   of the misses on the side stream, and one ``moe_expert_ffn`` pass with
+   ``MOE_FFN_PARTIAL`` (the first pass also computes the shared expert);
+4. ``moe_ffn_combine`` writes the chunk's y.
+
+With ``cap <= S / 2`` the fills of pass p + 1 evict nothing pass p reads, so
+they wait only for pass p - 1 and overlap pass p's compute; with a larger cap
+they wait for pass p. The outputs are bit-identical to the fully-resident
+grouped run of the same chunk. This module only sequences library calls.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import lib
+
+
+class ChunkedPrefill:
+    """Runs chunks of up to ``max_T`` tokens of one layer through a paged arena.
+
+    ``arena``: a ``lib.Arena`` with device slots, its device slot table and the
+    pinned expert-major host copy. ``slots``: the arena's device slot buffer.
+    ``shared``: device blob of the shared expert, or None.
+    """
+
+    def __init__(self, arena: lib.Arena, slots: torch.Tensor, stride: int, H: int, I: int, E: int, K: int,
+                 max_T: int, cap: int, shared: torch.Tensor | None = None, g: int = 32, device="cuda"):
+        if not 1 <= cap <= arena.S:
+            raise ValueError("cap must be in [1, S]")
+        self.arena, self.slots, self.stride = arena, slots, stride
+        self.H, self.I, self.E, self.K, self.g = H, I, E, K, g
+        self.max_T, self.cap, self.shared = max_T, cap, shared
+        self.ids = torch.empty(max_T, K, dtype=torch.int32, device=device)
+        self.wts = torch.empty(max_T, K, dtype=torch.float32, device=device)
+        self.ids_h = torch.empty(max_T * K, dtype=torch.int32, pin_memory=True)
+        self.ws_bytes = lib.moe_ffn_workspace_bytes(max_T, H, I, E, K, shared is not None, lib.MOE_FFN_PARTIAL)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.max_passes = (E + cap - 1) // cap
+        self.table_h = torch.full((self.max_passes, E), -1, dtype=torch.int32, pin_memory=True)
+        self.table_d = torch.full((self.max_passes, E), -1, dtype=torch.int32, device=device)
+        self.side = torch.cuda.Stream(device=device)
+        self.filled = [torch.cuda.Event() for _ in range(self.max_passes)]
+        self.computed = [torch.cuda.Event() for _ in range(self.max_passes)]
+        for e in self.filled + self.computed:
+            e.record(self.side)  # creates the HIP events
+        torch.cuda.synchronize(device)
+        self.last_passes: list[list[int]] = []
+
+    def run_chunk(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, w_router=None) -> None:
+        """x bf16 [T, H], logits fp32 [T, E] (written when ``w_router`` is given), y bf16 [T, H] out."""
+        T = x.shape[0]
+        if T > self.max_T:
+            raise ValueError("chunk longer than max_T")
+        if T == 0:
+            return
+        H, I, E, K, g = self.H, self.I, self.E, self.K, self.g
+        comp = torch.cuda.current_stream()
+        ids, wts = self.ids[:T], self.wts[:T]
+        lib.moe_route(x if w_router is not None else None, w_router, logits, T, H, E, K, 0, ids, wts, comp)
+        self.ids_h[: T * K].copy_(ids.view(-1), non_blocking=True)
+        comp.synchronize()  # the hand-shake; also: no earlier work still reads the slots or the tables
+        passes = self.arena.chunk_passes(self.ids_h[: T * K].tolist(), self.cap)
+        self.last_passes = passes
+        overlap = 2 * self.cap <= self.arena.S
+        for p, experts in enumerate(passes):
+            slots_of, _ = self.arena.map_slots(experts)
+            row = self.table_h[p]
+            row.fill_(-1)
+            row[torch.tensor(experts, dtype=torch.long)] = torch.tensor(slots_of, dtype=torch.int32)
+            self.table_d[p].copy_(row, non_blocking=True)  # on comp, before this pass's FFN
+            wait = p - 2 if overlap else p - 1
+            if wait >= 0:
+                self.side.wait_event(self.computed[wait])
+            self.arena.fill_async(self.side, self.filled[p])
+            comp.wait_event(self.filled[p])
+            flags = lib.MOE_FFN_PARTIAL | (lib.MOE_FFN_PARTIAL_SHARED if p == 0 and self.shared is not None else 0)
+            lib.moe_expert_ffn(x, ids, wts, T, H, I, E, K, g, self.table_d[p], self.slots, self.stride, self.shared,
+                               y, self.ws, self.ws_bytes, self.status, flags, comp)
+            self.computed[p].record(comp)
+        lib.moe_ffn_combine(wts, T, H, I, E, K, self.shared is not None, y, self.ws, self.ws_bytes, comp)
+
+    def run_prompt(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, chunk: int, w_router=None) -> None:
+        """The whole prompt in chunks of ``chunk`` tokens (the last one ragged)."""
+        if not 1 <= chunk <= self.max_T:
+            raise ValueError("chunk must be in [1, max_T]")
+        for t0 in range(0, x.shape[0], chunk):
+            t1 = min(t0 + chunk, x.shape[0])
+            self.run_chunk(x[t0:t1], logits[t0:t1], y[t0:t1], w_router)
+

@@ -150,5 +150,7 @@ WORKLOADS = {
         Workload("batched_t16_h2048_e128_k8_i768_zipf", 16, 2048, 128, 8, 768, 1, 128, "zipf", 3),
         Workload("prefill_t9940_h4096_e256_k8_i1536", 9940, 4096, 256, 8, 1536, 1, 256, "normal", 4),
         Workload("paged_t1_h4096_e256s1_k6_i2048_x43", 1, 4096, 256, 6, 2048, 43, 64, "locality", 5, shared=True),
+        # a 4K prompt through one layer of the paged shape, streamed in chunks through the 64-slot arena
+        Workload("chunked_t4096_h4096_e256s1_k6_i2048", 4096, 4096, 256, 6, 2048, 1, 64, "normal", 6, shared=True),
     )
 }

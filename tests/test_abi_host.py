@@ -143,3 +143,23 @@ def test_arena_place_reset_and_errors():
         a.fill_async(side=0)  # bookkeeping-only arena cannot fill
     a.reset()
     assert a.slot_table() == [-1] * 10 and a.stats()["hits"] == 0
+
+
+def test_arena_cpp_chunk_passes_matches_model():
+    rng = np.random.default_rng(4)
+    for E, S, T, K in ((64, 16, 40, 4), (256, 64, 200, 6), (32, 6, 9, 3)):
+        a = lib.Arena(E, S, 100, 4096)
+        m = ArenaModel(E, S, 100)
+        for chunk in range(5):
+            ids = rng.integers(0, E, size=T * K).tolist()
+            for cap in (1, S // 2, S):
+                st, passes = m.chunk_passes(ids, cap)
+                assert st == 0
+                assert a.chunk_passes(ids, cap) == passes
+            for p in m.chunk_passes(ids, S // 2)[1]:
+                assert a.map_slots(p) == m.map_slots(p)[1:]
+        with pytest.raises(lib.MoeError):
+            a.chunk_passes([0, E], 2)
+        with pytest.raises(lib.MoeError):
+            a.chunk_passes([0], S + 1)
+        assert a.chunk_passes([], 1) == []

@@ -89,3 +89,49 @@ def test_lowest_empty_slot_first_and_place():
     assert a.slot_of[3] == 3 and a.expert_in[0] == -1
     st, slots, fills = a.map_slots([9])
     assert fills == [(9, 0)]
+
+
+def test_chunk_passes_hand_worked():
+    # experts 2 and 5 resident; a chunk uses 7, 2, 0, 5, 3, 1 (7 twice)
+    a = ArenaModel(E=8, S=4)
+    assert a.place(2, 0) == OK and a.place(5, 3) == OK
+    st, passes = a.chunk_passes([7, 2, 0, 7, 5, 3, 1], 2)
+    assert st == OK and passes == [[2, 5], [0, 1], [3, 7]]
+    st, passes = a.chunk_passes([7, 2, 0, 7, 5, 3, 1], 4)
+    assert passes == [[2, 5, 0, 1], [3, 7]]
+    assert a.chunk_passes([1, 8], 2)[0] != OK and a.chunk_passes([1], 5)[0] != OK
+    assert a.chunk_passes([1], 0)[0] != OK
+    assert a.chunk_passes([], 3) == (OK, [])
+
+
+def test_chunk_passes_run_reads_each_missing_expert_once():
+    """Driving the passes through the slot policy: every pass maps, each expert the
+    chunk uses and the arena lacks is filled exactly once, the resident ones are
+    hits, and with passes of at most S/2 no fill evicts the previous pass."""
+    rng = np.random.default_rng(3)
+    for E, S, T, K, cap in ((64, 16, 40, 4, 8), (64, 16, 40, 4, 16), (256, 64, 300, 6, 32), (256, 64, 300, 6, 64),
+                            (32, 6, 9, 3, 3), (16, 16, 20, 2, 16)):
+        a = ArenaModel(E, S)
+        for chunk in range(6):
+            ids = rng.integers(0, E, size=T * K).tolist()
+            resident = {e for e in range(E) if a.slot_of[e] >= 0}
+            st, passes = a.chunk_passes(ids, cap)
+            assert st == OK
+            flat = [e for p in passes for e in p]
+            assert sorted(flat) == sorted(set(ids))  # a partition of the used experts
+            assert all(1 <= len(p) <= cap for p in passes) and all(len(p) == cap for p in passes[:-1])
+            n_res = len(set(ids) & resident)
+            assert set(flat[:n_res]) == set(ids) & resident  # resident experts first
+            filled = []
+            prev = []
+            for p in passes:
+                before = list(a.expert_in)
+                st, slots, fills = a.map_slots(p)
+                assert st == OK
+                filled += [e for e, _ in fills]
+                assert {e for e, _ in fills} == {e for e in p if e not in resident}
+                if 2 * cap <= S:
+                    assert not any(before[s] in prev for _, s in fills)
+                prev = p
+            assert sorted(filled) == sorted(set(ids) - resident)
+            check_consistent(a)

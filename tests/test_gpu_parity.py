@@ -537,3 +537,93 @@ def test_grouped_equals_gemv_path_within_tolerance():
         torch.cuda.synchronize()
         assert int(run.status.item()) == 0
         check_close(y_f64(run.y), y_ref, f"  flags {flags}")
+
+
+# ------------------------------------------------------------------ chunked paged prefill
+
+
+def paged_arena(w, layer, S):
+    stride = lib.moe_slot_stride(w.H, w.I)
+    host = torch.empty(w.E * stride, dtype=torch.uint8, pin_memory=True)
+    for e in range(w.E):
+        host[e * stride : (e + 1) * stride].copy_(torch.from_numpy(harness.pack_expert(w.seed, layer, e, w.H, w.I)))
+    slots = torch.empty(S * stride, dtype=torch.uint8, device=DEV)
+    table = torch.full((w.E,), -1, dtype=torch.int32, device=DEV)
+    arena = lib.Arena(w.E, S, lib.moe_blob_bytes(w.H, w.I), stride, slots, table, host)
+    return arena, slots, stride
+
+
+def resident_grouped(L, w, x, logits, T):
+    """The chunk through the fully-resident layer on the grouped path (the bitwise reference)."""
+    ids = torch.empty(T, w.K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, w.K, dtype=torch.float32, device=DEV)
+    y = torch.empty(T, w.H, dtype=torch.bfloat16, device=DEV)
+    nb = lib.moe_ffn_workspace_bytes(T, w.H, w.I, w.E, w.K, w.shared, lib.MOE_FORCE_GROUPED)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    lib.moe_route(None, None, logits, T, w.H, w.E, w.K, 0, ids, wts)
+    lib.moe_expert_ffn(x, ids, wts, T, w.H, w.I, w.E, w.K, 32, L.table, L.slots, L.stride, L.shared, y, ws, nb, st,
+                       lib.MOE_FORCE_GROUPED)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return y
+
+
+@pytest.mark.parametrize("chunk,cap", [(40, 4), (40, 8), (100, 3), (7, 4), (1, 8)])
+def test_chunked_paged_prefill_equals_resident(chunk, cap):
+    """A 100-token prompt through an 8-slot arena of 32 experts (top-4, shared expert) in chunks:
+    every chunk bitwise equal to its fully-resident grouped run, the prompt within the oracle's
+    bar, and each chunk fills exactly the experts it uses that were not resident."""
+    from quantized_routed_expert_moe_amd.paged import ChunkedPrefill
+
+    w = gen.Workload("chunked_t100_h512_e32s1_k4_i256", 100, 512, 32, 4, 256, 1, 8, "normal", 61, shared=True)
+    say(f"chunked paged prefill chunk={chunk} cap={cap}")
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    logits = gen.normal_logits(w.seed, 0, w.T, w.E)
+    L = harness.make_layer(w, 0, DEV, logits=logits, x_bits=xb, place_seed=6)
+    arena, slots, stride = paged_arena(w, 0, w.slots)
+    cp = ChunkedPrefill(arena, slots, stride, w.H, w.I, w.E, w.K, chunk, cap, shared=L.shared, device=DEV)
+    y = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=DEV)
+    ids_all = R.route(logits, w.K)[0]
+    for t0 in range(0, w.T, chunk):
+        t1 = min(t0 + chunk, w.T)
+        before = set(e for e, s in enumerate(arena.slot_table()) if s >= 0)
+        st0 = arena.stats()
+        cp.run_chunk(L.x[t0:t1], L.logits[t0:t1], y[t0:t1])
+        torch.cuda.synchronize()
+        assert int(cp.status.item()) == 0
+        used = set(ids_all[t0:t1].ravel().tolist())
+        assert sorted(e for p in cp.last_passes for e in p) == sorted(used)
+        assert arena.stats()["fills"] - st0["fills"] == len(used - before)
+        y_res = resident_grouped(L, w, L.x[t0:t1], L.logits[t0:t1], t1 - t0)
+        assert torch.equal(y[t0:t1].view(torch.int16), y_res.view(torch.int16)), (t0, t1)
+    y_ref, *_ = oracle_layer(w, 0, xb, logits=logits)
+    check_close(y_f64(y), y_ref, f"  chunked prompt chunk={chunk} cap={cap}")
+
+
+def test_partial_flags_and_combine_errors():
+    w = gen.Workload("partial_t8_h256_e8_k2_i256", 8, 256, 8, 2, 256, 1, 8, "normal", 62, shared=True)
+    L = harness.make_layer(w, 0, DEV)
+    run = harness.LayerRunner(w, DEV, lib.MOE_FFN_PARTIAL)
+    run.route(L)
+    args = (L.x, run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 32, L.table, L.slots, L.stride)
+    for flags, shared in ((lib.MOE_FFN_PARTIAL | lib.MOE_FORCE_GEMV, L.shared), (lib.MOE_FFN_PARTIAL_SHARED, L.shared),
+                          (lib.MOE_FFN_PARTIAL | lib.MOE_FFN_PARTIAL_SHARED, None)):
+        with pytest.raises(lib.MoeError) as ex:
+            lib.moe_expert_ffn(*args, shared, run.y, run.ws, run.ws_bytes, run.status, flags)
+        assert ex.value.status == lib.MOE_EINVAL
+    with pytest.raises(lib.MoeError) as ex:
+        lib.moe_ffn_combine(run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes - 1)
+    assert ex.value.status == lib.MOE_EWS
+    raw = lib.load().moe_ffn_combine  # the binding maps has_shared to 0 / 1; the C ABI takes only those
+    assert raw(run.wts.data_ptr(), w.T, w.H, w.I, w.E, w.K, 2, run.y.data_ptr(), run.ws.data_ptr(), run.ws_bytes,
+               None) == lib.MOE_EINVAL
+    lib.moe_ffn_combine(run.wts, 0, w.H, w.I, w.E, w.K, 1, None, None, 0)  # T = 0: a no-op
+    # one partial pass with every expert resident, then the combine: the plain grouped result
+    lib.moe_expert_ffn(*args, L.shared, run.y, run.ws, run.ws_bytes, run.status,
+                       lib.MOE_FFN_PARTIAL | lib.MOE_FFN_PARTIAL_SHARED)
+    lib.moe_ffn_combine(run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    y_res = resident_grouped(L, w, L.x, L.logits, w.T)
+    assert torch.equal(run.y.view(torch.int16), y_res.view(torch.int16))
