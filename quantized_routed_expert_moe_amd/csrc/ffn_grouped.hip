@@ -228,17 +228,22 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 //
 // Tile: 128 pair rows x 256 weight rows, K in stages of 64 (two quantisation
 // groups). Wave w owns tile columns 64 w .. +63 for all 128 rows, so every
-// dequantised B fragment feeds eight MFMAs (one per 16-row block). LDS holds,
-// double buffered, the stage's A rows (fp16, rows padded to 144 bytes, which
-// the lanes of a ds_read_b128 reach without bank conflicts) and the weights as
-// int4 codes and fp16 scales, a quarter of their fp16 size. A lane
-// dequantises the B operand of v_mfma_f32_16x16x32_f16 (8 consecutive k of
-// one column) from one code dword: nibble pair p of the dword holds k 2p and
-// 2p + 1 (bits 4p and 4p + 16); the pair OR-ed under an fp16 pattern gives
-// 1024 + u (pairs 0, 2) or 64 + u (pairs 1, 3) exactly, a packed add of -1032
-// or -72 gives q, a packed multiply by the scale rounds q * s once. The next stage's global loads are in flight while
-// the current stage is computed (one barrier per stage). A tile with at most
-// 64 rows computes only its first four 16-row blocks.
+// dequantised B fragment feeds eight MFMAs (one per 16-row block). Every operand
+// byte reaches LDS through buffer_load ... lds (no register staging, no LDS store
+// instructions), three stages deep: while stage st is computed, the loads of
+// stages st + 1 and st + 2 are in flight. Within a stage the order is fixed:
+// the B reads and the first k-half's dequantisation, then per 16-row block four
+// MFMAs, the A read two blocks ahead and (first half) a share of the second
+// half's dequantisation, so LDS latency and VALU work run under the MFMAs. A stage buffer holds the A rows (fp16,
+// 16-byte chunks XOR-swizzled by row, which ds_read_b128 reaches without bank
+// conflicts), the weight codes (int4, one 16-byte chunk per column and group,
+// a quarter of their fp16 size) and the fp16 group scales. A lane dequantises
+// the B operand of v_mfma_f32_16x16x32_f16 (8 consecutive k of one column) from
+// one code dword: nibble pair p of the dword holds k 2p and 2p + 1 (bits 4p and
+// 4p + 16); the pair OR-ed under an fp16 pattern gives 1024 + u (pairs 0, 2) or
+// 64 + u (pairs 1, 3) exactly, a packed add of -1032 or -72 gives q, a packed
+// multiply by the scale rounds q * s once. A tile with at most 64 rows computes
+// only its first four 16-row blocks.
 //
 // Block -> tile: the n_mt * n_nt tiles are ordered (unit, N-tile, M-tile) and
 // cut into 8 contiguous ranges, one per XCD (blocks are dispatched to XCDs
@@ -246,34 +251,42 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 // N-tile run back to back on one XCD and meet its weight bytes in that XCD's
 // L2.
 constexpr int kTM = 128, kTN = 256, kTK = 64;
-constexpr int kARow = kTK + 8;  // A row in LDS, fp16 elements (16 bytes of padding)
 
-// Loads through the global address space. The blob addresses come from the
-// workspace, so the compiler cannot tell they are global and would emit flat
-// loads, which count against the LDS wait counter as well: every LDS wait of
-// a stage would then also wait for the next stage's weights.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ inline uint4 ld_global16(const uint8_t* p) {
-  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(p);
-  return make_uint4(v.x, v.y, v.z, v.w);
+// Loads straight into LDS (gfx950 buffer_load ... lds): lane l's n bytes (n = 4
+// or 16) from base + voffset + soffset land at lds + n l; lds must be the same on
+// every lane of the wave (an instruction offset would move the LDS address too,
+// so none is used). The buffer form rather than the global one: the
+// compiler treats a pending global (FLAT) load into LDS as an out-of-order LDS
+// access and then waits for every LDS read at once, instead of only for the one
+// an MFMA needs. A read past the descriptor's byte range returns zeros.
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ inline uint32_t ld_global2(const uint8_t* p) { return *(const __attribute__((address_space(1))) uint16_t*)(p); }
+__device__ inline void ld16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ inline void ld4_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
 
 template <int MODE>
 __host__ __device__ inline int gemm_n_tiles(int H, int I) {
   return MODE == 0 ? (I + 127) / 128 : (H + kTN - 1) / kTN;
 }
 
-// dword e of the 8 code dwords of LDS column c holds dword e ^ sw(c) of the
-// column's two chunks: 16 lanes reading dword d of 16 consecutive columns meet
-// 16 different banks; the four dwords of a chunk stay in its 16 bytes
-__device__ inline int code_swz(int c) { return (c >> 2) & 3; }
+// One stage of operands in LDS (25,600 bytes).
+struct __align__(16) GemmStage {
+  _Float16 a[kTM * kTK];   // row r, chunk c (8 k) at r * 64 + 8 (c ^ (r & 7))
+  uint32_t bc[2 * kTN * 4];  // group g, column c: code dwords at (g * 256 + c) * 4 .. +3
+  uint16_t bs[2 * kTN];      // group g, column c: fp16 scale bits at g * 256 + c
+};
+constexpr int kStageLoads = 7;  // global_load_lds per lane and stage: 4 A, 2 codes, 1 scale pair
 
 template <int MODE>
 __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
-  __shared__ __align__(16) _Float16 As[2][kTM][kARow];
-  __shared__ __align__(16) uint32_t Bc[2][kTN * 8];  // per column: 2 groups x 4 code dwords (swizzled)
-  __shared__ uint32_t Bs[2][kTN];                    // per column: the 2 groups' fp16 scales
+  // three stage buffers (separate objects, so that a stage can name the one it
+  // reads and the one it fills)
+  __shared__ GemmStage S0, S1, S2;
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(T, H, I, a.E, K, has_shared);
@@ -310,91 +323,75 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   const bool half = td.rows <= 64;  // only the first four 16-row blocks hold pairs
   const BlobLayout BL = blob_layout(H, I);
 
-  // Loaders. A: 16-byte chunk q = v * 256 + tid (v < 4) of the 128 x 64 stage is
-  // row q / 8, columns 8 (q % 8) .. +7, so eight consecutive lanes fill one row's
-  // 128 bytes in LDS and in memory; a padding row reads the tile's first row (its
-  // products are never stored). B: chunk q = k * 256 + tid (k < 2) is tile column
-  // q / 2, group q % 2 of the stage, so consecutive lanes fill consecutive 16 bytes.
-  // (named scalars rather than arrays: a private array indexed before unrolling
-  // would be moved to LDS)
-  auto a_ptr = [&](int v) -> const _Float16* {
+  // Loaders (each lane keeps 32-bit byte offsets from wave-uniform bases, so a load
+  // takes a scalar base and one offset register; the host checks that they fit;
+  // named scalars rather than arrays: a private array indexed before unrolling
+  // would be moved to LDS).
+  // A: LDS chunk q = v * 256 + tid (v < 4) is row q / 8, position q % 8, which holds
+  // columns 8 ((q % 8) ^ (row % 8)) .. +7; a wave fills 1 KB (8 rows), each row's 128
+  // bytes read by eight consecutive lanes; a padding row reads the tile's first row
+  // (its products are never stored).
+  auto a_off = [&](int v) -> uint32_t {
     const int q = v * kGThreads + tid;
     int row = q >> 3;
     row = row < td.rows ? row : 0;
-    const int col8 = (q & 7) * 8;
+    const int col8 = ((q & 7) ^ ((q >> 3) & 7)) * 8;
     if (MODE == 0) {
       const int p = sorted[td.row0 + row];
       const int tok = p < P ? p / K : p - P;
-      return reinterpret_cast<const _Float16*>(a.ws + W.xh) + (size_t)tok * H + col8;
+      return ((uint32_t)tok * (uint32_t)H + col8) * 2u;
     }
-    return reinterpret_cast<const _Float16*>(a.ws + W.h) + (size_t)(td.row0 + row) * I + col8;
+    return ((uint32_t)(td.row0 + row) * (uint32_t)I + col8) * 2u;
   };
-  const _Float16* const a_src0 = a_ptr(0);
-  const _Float16* const a_src1 = a_ptr(1);
-  const _Float16* const a_src2 = a_ptr(2);
-  const _Float16* const a_src3 = a_ptr(3);
+  const uint8_t* const a_base = a.ws + (MODE == 0 ? W.xh : W.h);
+  const __amdgpu_buffer_rsrc_t a_rs =
+      buf_rsrc(a_base, MODE == 0 ? (uint32_t)((size_t)T * H * 2) : (uint32_t)((W.o - W.h)));
+  const uint32_t ao0 = a_off(0), ao1 = a_off(1), ao2 = a_off(2), ao3 = a_off(3);
+  // B: tile column c -> weight row; past the last row of a partial tile a real row
+  // (never stored). Codes: thread tid loads column tid's chunk of each group; scales:
+  // thread tid loads the 4 bytes of columns 2 p, 2 p + 1 (p = tid % 128, an even and
+  // the next row of one row block) of group tid / 128.
   const int R = MODE == 0 ? kRowBlockGU : kRowBlockDN;
-  // B chunk k: code chunk at bsrc + (2 st + g) * R * 16 bytes, scale at ssrc + (2 st + g) * R * 2
-  struct BSrc {
-    const uint8_t* codes;
-    const uint8_t* scales;
-  };
-  auto b_src = [&](int k) -> BSrc {
-    const int q = k * kGThreads + tid;
-    const int c = q >> 1;
+  const int n_rows = MODE == 0 ? I : H;
+  auto b_row = [&](int c, size_t& codes, size_t& scales) {
     int brow;
-    size_t bcodes, bscales;
     if (MODE == 0) {
       const int mat = (c >> 4) & 1;  // gate and up alternate in blocks of 16 columns
       brow = nt * 128 + (c >> 5) * 16 + (c & 15);
-      brow = brow < I ? brow : I - 1;  // past the last row of a partial tile: a real row, never stored
-      bcodes = mat ? BL.up_codes : BL.gate_codes;
-      bscales = mat ? BL.up_scales : BL.gate_scales;
+      codes = mat ? BL.up_codes : BL.gate_codes;
+      scales = mat ? BL.up_scales : BL.gate_scales;
     } else {
       brow = nt * kTN + c;
-      brow = brow < H ? brow : H - 1;
-      bcodes = BL.down_codes;
-      bscales = BL.down_scales;
+      codes = BL.down_codes;
+      scales = BL.down_scales;
     }
-    const uint8_t* base = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
-    return BSrc{base + bcodes + code_off(brow, 0, G, R) + (size_t)(q & 1) * R * 16,
-                base + bscales + scale_off(brow, 0, G, R) + (size_t)(q & 1) * R * 2};
+    return brow;
   };
-  const BSrc bs0 = b_src(0), bs1 = b_src(1);
-  const int bcol0 = tid >> 1, bcol1 = (kGThreads + tid) >> 1;
+  const uint8_t* const b_base = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
+  uint32_t bco, bso;
+  {
+    size_t cb, sb;
+    int brow = b_row(tid, cb, sb);
+    brow = brow < n_rows ? brow : n_rows - 1;
+    bco = (uint32_t)(cb + code_off(brow, 0, G, R));
+    const int c2 = 2 * (tid & 127);
+    brow = b_row(c2, cb, sb);
+    brow = brow < n_rows - 1 ? brow : n_rows - 2;  // the pair stays inside the matrix
+    bso = (uint32_t)(sb + scale_off(brow, (tid >> 7), G, R));
+  }
+  const __amdgpu_buffer_rsrc_t b_rs = buf_rsrc(b_base, (uint32_t)BL.bytes);
   const uint32_t scale_mask = blob ? 0xFFFFu : 0u;  // a unit without a blob contributes zeros
-  const int bg = tid & 1;                          // group of both B chunks of this thread
-
-  uint4 ra0, ra1, ra2, ra3;  // A of the next stage
-  uint4 rb0, rb1;            // B codes of the next stage
-  uint32_t rs0, rs1;         // B scales of the next stage
-  auto gload = [&](int st) {
-    ra0 = *reinterpret_cast<const uint4*>(a_src0 + st * kTK);
-    ra1 = *reinterpret_cast<const uint4*>(a_src1 + st * kTK);
-    ra2 = *reinterpret_cast<const uint4*>(a_src2 + st * kTK);
-    ra3 = *reinterpret_cast<const uint4*>(a_src3 + st * kTK);
-    rb0 = ld_global16(bs0.codes + (size_t)st * 2 * R * 16);
-    rb1 = ld_global16(bs1.codes + (size_t)st * 2 * R * 16);
-    rs0 = ld_global2(bs0.scales + (size_t)st * 2 * R * 2) & scale_mask;
-    rs1 = ld_global2(bs1.scales + (size_t)st * 2 * R * 2) & scale_mask;
-  };
-  // B chunk of column c into LDS: dword e of the chunk's 16 bytes holds code
-  // dword e ^ code_swz(c), a permutation inside the chunk
-  auto put_b = [&](int buf, int c, const uint4& w, uint32_t sc) {
-    const int cs = code_swz(c);
-    const uint32_t x = cs & 1 ? w.y : w.x, y = cs & 1 ? w.x : w.y;
-    const uint32_t z = cs & 1 ? w.w : w.z, u = cs & 1 ? w.z : w.w;
-    const uint4 o = cs & 2 ? make_uint4(z, u, x, y) : make_uint4(x, y, z, u);
-    reinterpret_cast<uint4*>(&Bc[buf][c * 8])[bg] = o;
-    reinterpret_cast<uint16_t*>(&Bs[buf][c])[bg] = (uint16_t)sc;
-  };
-  auto sstore = [&](int buf) {
-    *reinterpret_cast<uint4*>(&As[buf][tid >> 3][(tid & 7) * 8]) = ra0;
-    *reinterpret_cast<uint4*>(&As[buf][(kGThreads + tid) >> 3][(tid & 7) * 8]) = ra1;
-    *reinterpret_cast<uint4*>(&As[buf][(2 * kGThreads + tid) >> 3][(tid & 7) * 8]) = ra2;
-    *reinterpret_cast<uint4*>(&As[buf][(3 * kGThreads + tid) >> 3][(tid & 7) * 8]) = ra3;
-    put_b(buf, bcol0, rb0, rs0);
-    put_b(buf, bcol1, rb1, rs1);
+  // all operands of stage st into the stage buffer Sb (kStageLoads loads per lane)
+  auto issue = [&](int st, GemmStage* Sb) {
+    const uint32_t sa = (uint32_t)st * (kTK * 2);
+    ld16_lds(a_rs, ao0, sa, Sb->a + (0 * 4 + wave) * 512);
+    ld16_lds(a_rs, ao1, sa, Sb->a + (1 * 4 + wave) * 512);
+    ld16_lds(a_rs, ao2, sa, Sb->a + (2 * 4 + wave) * 512);
+    ld16_lds(a_rs, ao3, sa, Sb->a + (3 * 4 + wave) * 512);
+    const uint32_t sc = (uint32_t)st * 2 * R * 16;  // group 2 st, then 2 st + 1 (R * 16 bytes on)
+    ld16_lds(b_rs, bco, sc, Sb->bc + (0 * kTN + wave * 64) * 4);
+    ld16_lds(b_rs, bco, sc + R * 16, Sb->bc + (1 * kTN + wave * 64) * 4);
+    ld4_lds(b_rs, bso, (uint32_t)st * 2 * R * 2, Sb->bs + wave * 128);
   };
 
   f32x4 acc[8][4];
@@ -411,62 +408,97 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   asm volatile("" : "+v"(k_mlo), "+v"(k_mhi), "+v"(k_elo), "+v"(k_ehi));
   const f16x2 off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f}, off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
 
-  // one stage on LDS buffer buf; NB = 16-row blocks computed (8, or 4 for a half tile)
-  auto compute = [&](auto NBC, int buf) {
+  // one stage on stage buffer Sb; NB = 16-row blocks computed (8, or 4 for a half tile)
+  auto dequant = [&](uint32_t cw, uint32_t sw) -> f16x8 {
+    const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)sw);
+    const f16x2 s2 = {sc, sc};
+    const uint32_t w8 = cw >> 8;
+    const uint32_t m0 = (cw & k_mlo) | k_elo, m1 = (cw & k_mhi) | k_ehi;
+    const uint32_t m2 = (w8 & k_mlo) | k_elo, m3 = (w8 & k_mhi) | k_ehi;
+    uint32_t bq[4];
+    bq[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m0) + off_lo) * s2);
+    bq[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m1) + off_hi) * s2);
+    bq[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m2) + off_lo) * s2);
+    bq[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m3) + off_hi) * s2);
+    return __builtin_bit_cast(f16x8, make_uint4(bq[0], bq[1], bq[2], bq[3]));
+  };
+  auto compute = [&](auto NBC, const GemmStage* Sb) {
     constexpr int NB = decltype(NBC)::value;
+    const int colb = wave * 64 + (lane & 15);
+    // B code dwords and scales of both k-halves
+    uint32_t c00, c01, c02, c03, c10, c11, c12, c13, s00, s01, s02, s03, s10, s11, s12, s13;
+#define BLD(h, n) c##h##n = Sb->bc[(h * kTN + colb + n * 16) * 4 + (lane >> 4)]; s##h##n = Sb->bs[h * kTN + colb + n * 16] & scale_mask;
+    BLD(0, 0) BLD(0, 1) BLD(0, 2) BLD(0, 3) BLD(1, 0) BLD(1, 1) BLD(1, 2) BLD(1, 3)
+#undef BLD
+    auto read_a = [&](int h, int i) {  // row i 16 + lane % 16, chunk 4 h + lane / 16
+      return *reinterpret_cast<const f16x8*>(
+          &Sb->a[(i * 16 + (lane & 15)) * kTK + (((h * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
+    };
+    // A fragments two blocks ahead, over both halves: block j = h NB + i
+    f16x8 fa0 = read_a(0, 0), fa1 = read_a(0, 1);
+    const f16x8 fb00 = dequant(c00, s00), fb01 = dequant(c01, s01), fb02 = dequant(c02, s02), fb03 = dequant(c03, s03);
+    f16x8 fb10, fb11, fb12, fb13;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // k-half = one quantisation group
-      f16x8 fb[4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int col = wave * 64 + n * 16 + (lane & 15);
-        const uint32_t cw = Bc[buf][col * 8 + h * 4 + ((lane >> 4) ^ code_swz(col))];
-        const uint32_t sw = Bs[buf][col];
-        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(h ? sw >> 16 : sw));
-        const f16x2 s2 = {sc, sc};
-        const uint32_t w8 = cw >> 8;
-        const uint32_t m0 = (cw & k_mlo) | k_elo, m1 = (cw & k_mhi) | k_ehi;
-        const uint32_t m2 = (w8 & k_mlo) | k_elo, m3 = (w8 & k_mhi) | k_ehi;
-        uint32_t bq[4];
-        bq[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m0) + off_lo) * s2);
-        bq[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m1) + off_hi) * s2);
-        bq[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m2) + off_lo) * s2);
-        bq[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m3) + off_hi) * s2);
-        fb[n] = __builtin_bit_cast(f16x8, make_uint4(bq[0], bq[1], bq[2], bq[3]));
+    for (int j = 0; j < 2 * NB; ++j) {
+      const int h = j / NB, i = j % NB;
+      const f16x8 fa = fa0;
+      fa0 = fa1;
+      if (j + 2 < 2 * NB) fa1 = read_a((j + 2) / NB, (j + 2) % NB);
+      if (h == 0) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb00, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb01, acc[i][1], 0, 0, 0);
+        acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb02, acc[i][2], 0, 0, 0);
+        acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb03, acc[i][3], 0, 0, 0);
+        // the second half's B operands under the first half's MFMAs: one fragment
+        // every other block (NB = 8) or every block (NB = 4)
+        if (NB == 8) {
+          if (i == 1) fb10 = dequant(c10, s10);
+          if (i == 3) fb11 = dequant(c11, s11);
+          if (i == 5) fb12 = dequant(c12, s12);
+          if (i == 7) fb13 = dequant(c13, s13);
+        } else {
+          if (i == 0) fb10 = dequant(c10, s10);
+          if (i == 1) fb11 = dequant(c11, s11);
+          if (i == 2) fb12 = dequant(c12, s12);
+          if (i == 3) fb13 = dequant(c13, s13);
+        }
+      } else {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb10, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb11, acc[i][1], 0, 0, 0);
+        acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb12, acc[i][2], 0, 0, 0);
+        acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb13, acc[i][3], 0, 0, 0);
       }
-      // A fragments one block ahead: block i + 1's is read before block i's MFMAs
-      // are issued, so its LDS latency runs under them
-      auto read_a = [&](int i) {
-        return *reinterpret_cast<const f16x8*>(&As[buf][i * 16 + (lane & 15)][h * 32 + 8 * (lane >> 4)]);
-      };
-      f16x8 fa_next = read_a(0);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const f16x8 fa = fa_next;
-        if (i + 1 < NB) fa_next = read_a(i + 1);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb[n], acc[i][n], 0, 0, 0);
-        asm volatile("" ::: "memory");  // no A fragment further ahead (register pressure)
-      }
+      __builtin_amdgcn_sched_barrier(0);  // blocks in this order
     }
   };
 
   using NB8 = std::integral_constant<int, 8>;
   using NB4 = std::integral_constant<int, 4>;
-  // the stage loop, one copy per block count (one loop body each keeps the
-  // register allocation simple)
+  auto sbuf = [&](int i) { return i == 0 ? &S0 : i == 1 ? &S1 : &S2; };
+  // The stage loop, one copy per block count. Iteration st (from -2) issues the
+  // loads of stage st + 2 (past the last stage: the last stage again, into a buffer
+  // nothing reads any more, so every iteration issues the same loads) into buffer
+  // (st + 2) % 3, last read in iteration st - 1, then computes stage st from buffer
+  // st % 3 (iterations -2 and -1 only load). The stage body takes the buffer it
+  // reads and the one it fills as restrict pointers, so the compiler does not make
+  // the reads wait for those loads; the waits are explicit: at the end of iteration
+  // st this wave's loads of stage st + 1 have landed (only the kStageLoads just
+  // issued may still be in flight), then the barrier makes every wave's landed.
   auto run = [&](auto NBC) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int st = 0; st < n_st; ++st) {
-      const int buf = st & 1;
-      // the next stage's loads (past the last stage: the last stage again, so the
-      // count of loads in flight is the same on every path)
-      gload(st + 1 < n_st ? st + 1 : st);
-      compute(NBC, buf);
-      sstore(buf ^ 1);  // buffer buf ^ 1 was last read in stage st - 1, before the barrier below it
-      __syncthreads();
+    auto stage = [&](int st, const GemmStage* __restrict__ Rb, GemmStage* __restrict__ Wb) {
+      issue(st + 2 < n_st ? st + 2 : n_st - 1, Wb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st >= 0) compute(NBC, Rb);
+    };
+    int rb = 1, wb = 0;  // buffer indices (st % 3, (st + 2) % 3) for st = -2
+    for (int st = -2; st < n_st; ++st) {
+      stage(st, sbuf(rb), sbuf(wb));
+      __builtin_amdgcn_sched_barrier(0);
+      // vmcnt(kStageLoads) and no expcnt / lgkmcnt wait (gfx9 s_waitcnt encoding)
+      __builtin_amdgcn_s_waitcnt((kStageLoads & 15) | (7 << 4) | (15 << 8));
+      __builtin_amdgcn_s_barrier();
+      rb = rb == 2 ? 0 : rb + 1;
+      wb = wb == 2 ? 0 : wb + 1;
     }
   };
   if (half)
@@ -574,13 +606,22 @@ inline int round8(int v) { return (v + 7) / 8 * 8; }
 
 bool grouped_shape_ok(int H, int I) { return H % kTK == 0 && I % kTK == 0; }  // H % 8 for the combine
 
+// the GEMM addresses x and h with 32-bit byte offsets (and 32-bit buffer sizes,
+// h's rounded up to 256 bytes)
+static bool grouped_offsets_fit(int T, int H, int I, int K, int has_shared) {
+  const size_t PA = (size_t)T * K + (has_shared ? (size_t)T : 0);
+  return (size_t)T * H * 2 <= 0xFFFFFF00u && PA * I * 2 <= 0xFFFFFF00u;
+}
+
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared) {
+  if (!grouped_offsets_fit(T, H, I, K, has_shared)) return 0;  // unsupported: the caller reports it
   return grouped_ws(T, H, I, E, K, has_shared).bytes;
 }
 
 hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   if (!grouped_shape_ok(a.H, a.I)) return hipErrorNotSupported;
   const bool has_shared = a.shared_blob != nullptr;
+  if (!grouped_offsets_fit(a.T, a.H, a.I, a.K, has_shared)) return hipErrorNotSupported;
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
   hipError_t e;
   if (stage == 0) {
