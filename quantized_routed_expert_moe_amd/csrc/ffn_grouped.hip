@@ -231,10 +231,11 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 // dequantised B fragment feeds eight MFMAs (one per 16-row block). Every operand
 // byte reaches LDS through buffer_load ... lds (no register staging, no LDS store
 // instructions), three stages deep: while stage st is computed, the loads of
-// stages st + 1 and st + 2 are in flight. Within a stage the order is fixed:
-// the B reads and the first k-half's dequantisation, then per 16-row block four
-// MFMAs, the A read two blocks ahead and (first half) a share of the second
-// half's dequantisation, so LDS latency and VALU work run under the MFMAs. A stage buffer holds the A rows (fp16,
+// stages st + 1 and st + 2 are in flight. Within a stage the order is fixed: per
+// 16-row block four MFMAs, the A read two blocks ahead and a share of the next
+// k-half's dequantisation (the second half's during the first, the next stage's
+// first half during the second), so LDS latency and VALU work run under the
+// MFMAs; the one barrier per stage sits between the two halves. A stage buffer holds the A rows (fp16,
 // 16-byte chunks XOR-swizzled by row, which ds_read_b128 reaches without bank
 // conflicts), the weight codes (int4, one 16-byte chunk per column and group,
 // a quarter of their fp16 size) and the fp16 group scales. A lane dequantises
@@ -422,84 +423,114 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
     bq[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m3) + off_hi) * s2);
     return __builtin_bit_cast(f16x8, make_uint4(bq[0], bq[1], bq[2], bq[3]));
   };
-  auto compute = [&](auto NBC, const GemmStage* Sb) {
-    constexpr int NB = decltype(NBC)::value;
-    const int colb = wave * 64 + (lane & 15);
-    // B code dwords and scales of both k-halves
-    uint32_t c00, c01, c02, c03, c10, c11, c12, c13, s00, s01, s02, s03, s10, s11, s12, s13;
-#define BLD(h, n) c##h##n = Sb->bc[(h * kTN + colb + n * 16) * 4 + (lane >> 4)]; s##h##n = Sb->bs[h * kTN + colb + n * 16] & scale_mask;
-    BLD(0, 0) BLD(0, 1) BLD(0, 2) BLD(0, 3) BLD(1, 0) BLD(1, 1) BLD(1, 2) BLD(1, 3)
-#undef BLD
-    auto read_a = [&](int h, int i) {  // row i 16 + lane % 16, chunk 4 h + lane / 16
-      return *reinterpret_cast<const f16x8*>(
-          &Sb->a[(i * 16 + (lane & 15)) * kTK + (((h * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
-    };
-    // A fragments two blocks ahead, over both halves: block j = h NB + i
-    f16x8 fa0 = read_a(0, 0), fa1 = read_a(0, 1);
-    const f16x8 fb00 = dequant(c00, s00), fb01 = dequant(c01, s01), fb02 = dequant(c02, s02), fb03 = dequant(c03, s03);
-    f16x8 fb10, fb11, fb12, fb13;
-#pragma unroll
-    for (int j = 0; j < 2 * NB; ++j) {
-      const int h = j / NB, i = j % NB;
-      const f16x8 fa = fa0;
-      fa0 = fa1;
-      if (j + 2 < 2 * NB) fa1 = read_a((j + 2) / NB, (j + 2) % NB);
-      if (h == 0) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb00, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb01, acc[i][1], 0, 0, 0);
-        acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb02, acc[i][2], 0, 0, 0);
-        acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb03, acc[i][3], 0, 0, 0);
-        // the second half's B operands under the first half's MFMAs: one fragment
-        // every other block (NB = 8) or every block (NB = 4)
-        if (NB == 8) {
-          if (i == 1) fb10 = dequant(c10, s10);
-          if (i == 3) fb11 = dequant(c11, s11);
-          if (i == 5) fb12 = dequant(c12, s12);
-          if (i == 7) fb13 = dequant(c13, s13);
-        } else {
-          if (i == 0) fb10 = dequant(c10, s10);
-          if (i == 1) fb11 = dequant(c11, s11);
-          if (i == 2) fb12 = dequant(c12, s12);
-          if (i == 3) fb13 = dequant(c13, s13);
-        }
-      } else {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb10, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb11, acc[i][1], 0, 0, 0);
-        acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb12, acc[i][2], 0, 0, 0);
-        acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb13, acc[i][3], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // blocks in this order
-    }
+  auto read_a = [&](const GemmStage* Sb, int h, int i) {  // row i 16 + lane % 16, chunk 4 h + lane / 16
+    return *reinterpret_cast<const f16x8*>(
+        &Sb->a[(i * 16 + (lane & 15)) * kTK + (((h * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
   };
+  const int colb = wave * 64 + (lane & 15);
+  // B operands: raw code dwords and scales of one k-half (4 column blocks), then
+  // their dequantised fragments; fbA = the first half of the stage being computed,
+  // fbB = its second half
+  uint32_t rc0, rc1, rc2, rc3, rs0, rs1, rs2, rs3;
+  f16x8 fbA0, fbA1, fbA2, fbA3, fbB0, fbB1, fbB2, fbB3;
+  auto read_b = [&](const GemmStage* Sb, int h) {
+#define BLD(n)                                                          \
+  rc##n = Sb->bc[(h * kTN + colb + n * 16) * 4 + (lane >> 4)]; \
+  rs##n = Sb->bs[h * kTN + colb + n * 16] & scale_mask;
+    BLD(0) BLD(1) BLD(2) BLD(3)
+#undef BLD
+  };
+  f16x8 fa0, fa1;  // the next two A fragments
 
   using NB8 = std::integral_constant<int, 8>;
   using NB4 = std::integral_constant<int, 4>;
   auto sbuf = [&](int i) { return i == 0 ? &S0 : i == 1 ? &S1 : &S2; };
-  // The stage loop, one copy per block count. Iteration st (from -2) issues the
-  // loads of stage st + 2 (past the last stage: the last stage again, into a buffer
-  // nothing reads any more, so every iteration issues the same loads) into buffer
-  // (st + 2) % 3, last read in iteration st - 1, then computes stage st from buffer
-  // st % 3 (iterations -2 and -1 only load). The stage body takes the buffer it
-  // reads and the one it fills as restrict pointers, so the compiler does not make
-  // the reads wait for those loads; the waits are explicit: at the end of iteration
-  // st this wave's loads of stage st + 1 have landed (only the kStageLoads just
-  // issued may still be in flight), then the barrier makes every wave's landed.
+  // The stage loop, one copy per block count. Before it, stages 0 and 1 are loaded
+  // and stage 0's first k-half dequantised (all loads waited for, so the compiler
+  // sees none of them pending in the loop). Iteration st, with R, N and W the
+  // buffers of stages st, st + 1 and st + 2 (st % 3 ...):
+  //   part A: the first k-half's MFMAs of stage st (its B fragments were
+  //     dequantised in iteration st - 1), with the second half's dequantisation
+  //     and the A reads two blocks ahead under them;
+  //   this wave's loads of stage st + 1 have landed; barrier: every wave's have,
+  //     and every wave is done with stage st - 1, whose buffer W now receives
+  //   the loads of stage st + 2 (past the last stage: the last stage again, so every
+  //     iteration issues the same loads; nothing reads that copy);
+  //   part B: the second half's MFMAs of stage st, with the first half of stage
+  //     st + 1 read from N and dequantised under them.
+  // The barrier sits between two runs of MFMAs, so the matrix unit is still busy
+  // while the waves meet. The body takes the three buffers as restrict pointers, so
+  // the compiler does not make the reads of R and N wait for the loads into W; the
+  // waits are explicit.
   auto run = [&](auto NBC) {
-    auto stage = [&](int st, const GemmStage* __restrict__ Rb, GemmStage* __restrict__ Wb) {
+    constexpr int NB = decltype(NBC)::value;
+    issue(0, &S0);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0) (gfx9 s_waitcnt encoding)
+    __builtin_amdgcn_s_barrier();
+    issue(n_st > 1 ? 1 : 0, &S1);
+    read_b(&S0, 0);
+    fbA0 = dequant(rc0, rs0);
+    fbA1 = dequant(rc1, rs1);
+    fbA2 = dequant(rc2, rs2);
+    fbA3 = dequant(rc3, rs3);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();
+    auto body = [&](int st, const GemmStage* __restrict__ Rb, const GemmStage* __restrict__ Nb,
+                    GemmStage* __restrict__ Wb) {
+      // part A
+      read_b(Rb, 1);
+      fa0 = read_a(Rb, 0, 0);
+      fa1 = read_a(Rb, 0, 1);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const f16x8 fa = fa0;
+        fa0 = fa1;
+        fa1 = read_a(Rb, (i + 2) / NB, (i + 2) % NB);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbA0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbA1, acc[i][1], 0, 0, 0);
+        acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbA2, acc[i][2], 0, 0, 0);
+        acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbA3, acc[i][3], 0, 0, 0);
+        // one fragment every other block (NB = 8) or every block (NB = 4)
+        if (i == (NB == 8 ? 1 : 0)) fbB0 = dequant(rc0, rs0);
+        if (i == (NB == 8 ? 3 : 1)) fbB1 = dequant(rc1, rs1);
+        if (i == (NB == 8 ? 5 : 2)) fbB2 = dequant(rc2, rs2);
+        if (i == (NB == 8 ? 7 : 3)) fbB3 = dequant(rc3, rs3);
+        __builtin_amdgcn_sched_barrier(0);  // blocks in this order
+      }
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
       issue(st + 2 < n_st ? st + 2 : n_st - 1, Wb);
       __builtin_amdgcn_sched_barrier(0);
-      if (st >= 0) compute(NBC, Rb);
+      // part B
+      read_b(Nb, 0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const f16x8 fa = fa0;
+        fa0 = fa1;
+        if (i + 2 < NB) fa1 = read_a(Rb, 1, i + 2);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbB0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbB1, acc[i][1], 0, 0, 0);
+        acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbB2, acc[i][2], 0, 0, 0);
+        acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fbB3, acc[i][3], 0, 0, 0);
+        if (i == (NB == 8 ? 1 : 0)) fbA0 = dequant(rc0, rs0);
+        if (i == (NB == 8 ? 3 : 1)) fbA1 = dequant(rc1, rs1);
+        if (i == (NB == 8 ? 5 : 2)) fbA2 = dequant(rc2, rs2);
+        if (i == (NB == 8 ? 7 : 3)) fbA3 = dequant(rc3, rs3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
-    int rb = 1, wb = 0;  // buffer indices (st % 3, (st + 2) % 3) for st = -2
-    for (int st = -2; st < n_st; ++st) {
-      stage(st, sbuf(rb), sbuf(wb));
+    int rb = 0, nb = 1, wb = 2;  // buffer indices (st % 3, (st + 1) % 3, (st + 2) % 3)
+    for (int st = 0; st < n_st; ++st) {
+      body(st, sbuf(rb), sbuf(nb), sbuf(wb));
       __builtin_amdgcn_sched_barrier(0);
-      // vmcnt(kStageLoads) and no expcnt / lgkmcnt wait (gfx9 s_waitcnt encoding)
-      __builtin_amdgcn_s_waitcnt((kStageLoads & 15) | (7 << 4) | (15 << 8));
-      __builtin_amdgcn_s_barrier();
-      rb = rb == 2 ? 0 : rb + 1;
-      wb = wb == 2 ? 0 : wb + 1;
+      const int t0 = rb;
+      rb = nb;
+      nb = wb;
+      wb = t0;
     }
+    // the last iteration's loads into LDS land before the wave can end (the
+    // workgroup's LDS may be handed to another workgroup after that)
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   };
   if (half)
     run(NB4{});
