@@ -221,6 +221,13 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   constexpr int CW = 16 * CPL;
   __shared__ float part[kWaves][kMaxUnits][4];
   __shared__ float wsh[kMaxK];
+  // the argument pointers the first loads need, in registers with the others (one
+  // batch of argument loads instead of two round trips)
+  // (typed as global pointers: through the asm the compiler would otherwise lose
+  // their address space and emit slower flat accesses)
+  const __attribute__((address_space(1))) int32_t* ids_p = (const __attribute__((address_space(1))) int32_t*)a.ids;
+  const __attribute__((address_space(1))) float* w_p = (const __attribute__((address_space(1))) float*)a.w;
+  asm volatile("" : "+s"(ids_p), "+s"(w_p));
   const int H = a.H, I = a.I, K = a.K;
   const int Gd = I / kGroup;
   const bool has_shared = a.shared_blob != nullptr;
@@ -237,7 +244,12 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   const int qb = xcd_item(blockIdx.x, H / 4);
   const int n = qb * 4 + r;
   // the routing weights, loaded first and kept in LDS for the combine
-  const float wk = (wave == 0 && lane < K) ? a.w[lane] : 0.0f;
+  const float wk = (wave == 0 && lane < K) ? w_p[lane] : 0.0f;
+  // the status pointer in registers now, with the other arguments (left to the
+  // compiler, its load lands after the slot lookup, one more round trip on the
+  // path to the weight loads)
+  __attribute__((address_space(1))) int32_t* status = (__attribute__((address_space(1))) int32_t*)a.status;
+  asm volatile("" : "+s"(status));
   // 1. this wave's h slice: uint4 q = lane + 64m = column c0 + q/4, halves 8*(q%4) .. +7;
   //    (unit, group) of the lane's column advance by 16 columns per m. Issued first:
   //    it does not depend on the unit slots.
@@ -266,12 +278,12 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     if (k < 0) {
       my_slot = 0;
     } else {
-      const int e = a.ids[k];
+      const int e = ids_p[k];
       if (e < 0 || e >= a.E) {
-        *a.status = MOE_EINVAL;
+        *status = MOE_EINVAL;
       } else {
         my_slot = a.slot_table[e];
-        if (my_slot < 0) *a.status = MOE_ENOTRES;
+        if (my_slot < 0) *status = MOE_ENOTRES;
       }
     }
   }
