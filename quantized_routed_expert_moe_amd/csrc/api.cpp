@@ -97,7 +97,7 @@ namespace {
 int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K, int g,
                      const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
                      uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
-                     moe_stream_t stream, int stage) {
+                     moe_stream_t stream, int stage, const int32_t* pre_slots = nullptr) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
   if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_FFN_PARTIAL | MOE_FFN_PARTIAL_SHARED))
     return MOE_EINVAL;
@@ -135,6 +135,7 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
            (flags & MOE_FFN_PARTIAL_SHARED ? moe::kModePartialShared : 0u);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool dec1 = !grouped && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
+  if (dec1) a.pre_slots = pre_slots;
   const bool bat = !grouped && moe::batched_supported(T, H, I, K);
   for (int st = 0; st < 2; ++st) {
     if (stage != 2 && stage != st) continue;
@@ -183,6 +184,28 @@ extern "C" int moe_layer(const uint16_t* x, const float* w_router, float* logits
                          int g, unsigned route_flags, int32_t* ids, float* w, const int32_t* slot_table,
                          const void* slots, size_t stride, const void* shared_blob, uint16_t* y, void* ws,
                          size_t ws_bytes, int32_t* dev_status, unsigned ffn_flags, moe_stream_t stream) {
+  // One token on the single-token path: the routing kernel also resolves the
+  // chosen experts' slots into the end of the workspace (same results, one
+  // dependent load less in each FFN kernel). Everything the FFN call checks is
+  // checked here first, so that nothing is enqueued on an argument error.
+  const bool dec1 = T == 1 && !ffn_uses_grouped(T, ffn_flags) && moe::shape_ok(H, I, g) && E <= moe::kMaxE &&
+                    K <= moe::kMaxK && K <= E && moe::decode1_supported(T, H, I, K, shared_blob != nullptr) &&
+                    !(ffn_flags & ~(unsigned)(MOE_FORCE_GEMV)) && slot_table && slots && y && dev_status && ws &&
+                    ws_bytes >= moe_ffn_workspace_bytes(T, H, I, E, K, shared_blob != nullptr, ffn_flags) &&
+                    stride >= moe_blob_bytes(H, I, g) && stride % 256 == 0 && w_router && x && H <= 8192 && logits && ids &&
+                    w &&
+                    !(route_flags & ~(unsigned)MOE_ROUTE_RENORM);
+  if (dec1) {
+    int32_t* pre = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
+                                              moe::decode1_slots_offset(H, I, K, shared_blob != nullptr));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (moe::launch_router_gemv(x, w_router, logits, T, H, E, s) != hipSuccess) return MOE_EHIP;
+    if (moe::launch_route_select(logits, T, E, K, route_flags, ids, w, s, MOE_SCORE_SOFTMAX, nullptr, 1.0f, slot_table,
+                                 pre) != hipSuccess)
+      return MOE_EHIP;
+    return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                            dev_status, ffn_flags, stream, 2, pre);
+  }
   const int rs = moe_route(x, w_router, logits, T, H, E, K, route_flags, ids, w, stream);
   if (rs != MOE_OK) return rs;
   return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,

@@ -53,15 +53,21 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
 // Blob of unit u (u = 0 is the shared expert when present) or nullptr with the
 // status word set; ids = the token's routed experts in rank order.
+// With pre_slots (moe_layer) the routing kernel has resolved the slots already.
 __device__ inline const uint8_t* dec_unit_blob(const FfnArgs& a, int u, bool has_shared, const int32_t* ids) {
   const int k = has_shared ? u - 1 : u;
   if (k < 0) return a.shared_blob;
-  const int e = ids[k];
-  if (e < 0 || e >= a.E) {
-    *a.status = MOE_EINVAL;
-    return nullptr;
+  int slot;
+  if (a.pre_slots) {
+    slot = a.pre_slots[k];
+  } else {
+    const int e = ids[k];
+    if (e < 0 || e >= a.E) {
+      *a.status = MOE_EINVAL;
+      return nullptr;
+    }
+    slot = a.slot_table[e];
   }
-  const int slot = a.slot_table[e];
   if (slot < 0) {
     *a.status = MOE_ENOTRES;
     return nullptr;
@@ -278,12 +284,17 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     if (k < 0) {
       my_slot = 0;
     } else {
-      const int e = ids_p[k];
-      if (e < 0 || e >= a.E) {
-        *status = MOE_EINVAL;
-      } else {
-        my_slot = a.slot_table[e];
+      if (a.pre_slots) {
+        my_slot = a.pre_slots[k];
         if (my_slot < 0) *status = MOE_ENOTRES;
+      } else {
+        const int e = ids_p[k];
+        if (e < 0 || e >= a.E) {
+          *status = MOE_EINVAL;
+        } else {
+          my_slot = a.slot_table[e];
+          if (my_slot < 0) *status = MOE_ENOTRES;
+        }
       }
     }
   }

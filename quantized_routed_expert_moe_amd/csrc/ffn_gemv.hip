@@ -479,8 +479,10 @@ inline int pow2_at_least(int v) {
 }  // namespace
 
 size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared) {
-  return gemv_ws(T, H, I, K, has_shared).bytes;
+  return gemv_ws(T, H, I, K, has_shared).bytes + (T == 1 ? 256 : 0);
 }
+
+size_t decode1_slots_offset(int H, int I, int K, int has_shared) { return gemv_ws(1, H, I, K, has_shared).bytes; }
 
 hipError_t launch_ffn_gemv(const FfnArgs& a, int stage, hipStream_t s) {
   const bool has_shared = a.shared_blob != nullptr;

@@ -63,9 +63,11 @@ __host__ __device__ inline bool shape_ok(int H, int I, int g) {
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H, int E,
                               hipStream_t s);
 // score: MOE_SCORE_*; bias (nullable) and scale as in moe_route_scored
+// slot_table / slots_out (softmax scoring, T = 1 only): also write slots_out[k] =
+// slot_table[ids[k]]
 hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigned flags, int32_t* ids,
                                float* w, hipStream_t s, int score = MOE_SCORE_SOFTMAX, const float* bias = nullptr,
-                               float scale = 1.0f);
+                               float scale = 1.0f, const int32_t* slot_table = nullptr, int32_t* slots_out = nullptr);
 
 struct FfnArgs {
   const uint16_t* x;
@@ -81,6 +83,9 @@ struct FfnArgs {
   size_t ws_bytes;
   int32_t* status;
   unsigned mode;  // kModePartial / kModePartialShared (grouped path only), else 0
+  // single-token path only, else nullptr: slot of routed expert k (rank order),
+  // already resolved through slot_table by the routing kernel
+  const int32_t* pre_slots;
 };
 // A partial pass of the grouped path: only routed experts with a slot are
 // computed (the others are skipped without error), the per-pair outputs stay in
@@ -92,6 +97,8 @@ hipError_t launch_grouped_combine(const FfnArgs& a, hipStream_t s);
 // Each path launches in two stages: stage 0 = gate/up (h into the workspace),
 // stage 1 = down + combine (y).
 size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared);
+// single-token workspaces end with room for the K resolved slots (moe_layer)
+size_t decode1_slots_offset(int H, int I, int K, int has_shared);
 hipError_t launch_ffn_gemv(const FfnArgs& a, int stage, hipStream_t s);
 
 // small-batch kernels (2 <= T <= 32, shapes batched_supported admits)

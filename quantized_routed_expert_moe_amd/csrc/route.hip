@@ -116,19 +116,41 @@ __global__ void __launch_bounds__(256) router_gemv1_kernel(const uint16_t* __res
 }
 
 // One wave per token. The weights are multiplied by scale (1 for moe_route,
-// where the product is exact).
+// where the product is exact). With slot_table (one token): the table is staged
+// in LDS while the logits load, and lane k also writes slots_out[k] =
+// slot_table[ids[k]], so the single-token FFN kernels find their blobs with one
+// load instead of two.
 template <int EPL>
 __global__ void __launch_bounds__(64) route_select_kernel(const float* __restrict__ logits, int T, int E, int K,
                                                           unsigned flags, float scale, int32_t* __restrict__ ids,
-                                                          float* __restrict__ w) {
+                                                          float* __restrict__ w,
+                                                          const int32_t* __restrict__ slot_table,
+                                                          int32_t* __restrict__ slots_out) {
+  __shared__ int32_t tbl[64 * EPL];
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
+  // the table loads go out with the logits loads (clamped index past E); the
+  // values reach LDS only after the selection, so no wait comes between the two
+  int32_t tv[EPL];
+  if (slot_table) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      tv[i] = slot_table[e < E ? e : E - 1];
+    }
+  }
   int32_t id;
   float wt;
   wave_select<EPL>(logits + (size_t)t * E, E, K, flags, lane, id, wt);
   if (lane < K) {
     ids[(size_t)t * K + lane] = id;
     w[(size_t)t * K + lane] = wt * scale;
+  }
+  if (slot_table) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) tbl[lane + 64 * i] = tv[i];  // entries past E are never read
+    __builtin_amdgcn_wave_barrier();  // one wave: its LDS stores precede its loads
+    if (lane < K) slots_out[lane] = tbl[id];
   }
 }
 
@@ -156,12 +178,20 @@ __global__ void __launch_bounds__(64) route_scored_kernel(const float* __restric
   const int lane = threadIdx.x;
   const float* l = logits + (size_t)t * E;
   uint64_t key[EPL];
+  float lv[EPL], bv[EPL];  // loads first, all in flight together (clamped index past E)
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    const int ec = e < E ? e : E - 1;
+    lv[i] = l[ec];
+    bv[i] = bias ? bias[ec] : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float s = expert_score(l[e], score);
-      const float c = bias ? s + bias[e] : s;
+      const float s = expert_score(lv[i], score);
+      const float c = bias ? s + bv[i] : s;
       key[i] = route_key(c, e);
     } else {
       key[i] = 0ull;  // real keys are > 0
@@ -204,13 +234,16 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits,
 }
 
 hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigned flags, int32_t* ids, float* w,
-                               hipStream_t s, int score, const float* bias, float scale) {
+                               hipStream_t s, int score, const float* bias, float scale, const int32_t* slot_table,
+                               int32_t* slots_out) {
+  if (slot_table && (T != 1 || score != MOE_SCORE_SOFTMAX || !slots_out)) return hipErrorInvalidValue;
   const int epl = (E + 63) / 64;
   dim3 grid(T);
 #define SEL(N)                                                                                                    \
   do {                                                                                                            \
     if (score == MOE_SCORE_SOFTMAX)                                                                               \
-      hipLaunchKernelGGL(route_select_kernel<N>, grid, dim3(64), 0, s, logits, T, E, K, flags, scale, ids, w);    \
+      hipLaunchKernelGGL(route_select_kernel<N>, grid, dim3(64), 0, s, logits, T, E, K, flags, scale, ids, w,     \
+                         slot_table, slots_out);                                                                  \
     else                                                                                                          \
       hipLaunchKernelGGL(route_scored_kernel<N>, grid, dim3(64), 0, s, logits, T, E, K, flags, score, bias, scale, \
                          ids, w);                                                                                 \

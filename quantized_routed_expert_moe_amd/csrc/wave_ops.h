@@ -172,10 +172,17 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
                                    float& wt) {
   uint64_t key[EPL];
   float lg[EPL];
+  // every load unconditional (a clamped index past E), so that all of them are in
+  // flight at once: a load under a branch is waited for before the branch joins
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    lg[i] = e < E ? l[e] : 0.0f;
+    lg[i] = l[e < E ? e : E - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e >= E) lg[i] = 0.0f;
     key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
   }
   const uint64_t mine = wave_topk<EPL>(key, K, lane);

@@ -390,6 +390,36 @@ def test_not_resident_and_bad_id_set_status():
     assert int(run.status.item()) in (lib.MOE_EINVAL, lib.MOE_ENOTRES)
 
 
+def test_layer_single_token_not_resident_sets_status():
+    """moe_layer on one token resolves the slots inside the routing kernel: a routed
+    expert without a slot still sets MOE_ENOTRES, and with every slot back the
+    output is that of moe_route then moe_expert_ffn again."""
+    w = gen.Workload("dec_t1_h256_e64_k4_i512_status", 1, 256, 64, 4, 512, 1, 64, "gemv", 35, shared=True)
+    L = harness.make_layer(w, 0, DEV, place_seed=8)
+    run = harness.LayerRunner(w, DEV)
+    run.layer(L)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    y0 = run.y.view(torch.int16).clone()
+    for k in (0, w.K - 1):
+        e = int(run.ids[0, k].item())
+        saved = int(L.table[e].item())
+        L.table[e] = -1
+        run.layer(L)
+        torch.cuda.synchronize()
+        assert int(run.status.item()) == lib.MOE_ENOTRES, k
+        run.status.zero_()
+        L.table[e] = saved
+    run.layer(L)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    assert torch.equal(run.y.view(torch.int16), y0)
+    run.route(L)
+    run.ffn(L)
+    torch.cuda.synchronize()
+    assert torch.equal(run.y.view(torch.int16), y0)
+
+
 def test_argument_errors_return_status():
     w = gen.WORKLOADS["tiny_t4_h256_e8_k2"]
     L = harness.make_layer(w, 0, DEV)
