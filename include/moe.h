@@ -66,6 +66,13 @@ enum moe_score {
   MOE_SCORE_SQRTSOFTPLUS = 2  /* sqrt(ln(1 + e^l)) */
 };
 
+/* Expert weight formats (moe_pack_expert_fmt, moe_expert_ffn_fmt). */
+enum moe_format {
+  MOE_FMT_INT4_G32 = 0,  /* int4, one fp16 scale per 32 columns: the blob of moe_pack_expert */
+  MOE_FMT_INT4_G128 = 1, /* int4, one fp16 scale per 128 columns */
+  MOE_FMT_INT8_G32 = 2   /* int8, one fp16 scale per 32 columns */
+};
+
 enum moe_flags {
   MOE_ROUTE_RENORM = 1u << 0,  /* moe_route: divide the K selected weights by their sum */
   MOE_FORCE_GEMV = 1u << 8,    /* moe_expert_ffn: use the per-expert GEMV path whatever T is */
@@ -181,6 +188,34 @@ int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T,
                    int g, const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
                    uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
                    moe_stream_t stream);
+
+/* ------------------------------------------------------------------ other expert formats
+ * The other expert formats of the "Strata" README (Models: INT8 group-32
+ * linears; Kernels: INT4 group-128 and INT8 group-32 kernels, 16-bit
+ * activations). W[n][j] = q[n][j] * s[n][j / g] as for the int4 group-32
+ * experts; the layer and every argument are as in moe_expert_ffn, with
+ * fmt in moe_format:
+ *   MOE_FMT_INT4_G32  the blob of moe_pack_expert; moe_expert_ffn_fmt is
+ *                     moe_expert_ffn(..., g = 32, flags = 0) and the two
+ *                     functions below return moe_blob_bytes / moe_slot_stride;
+ *   MOE_FMT_INT4_G128 codes as for moe_pack_expert (uint8 [rows][cols/2],
+ *                     two's-complement nibbles, even column in the low nibble),
+ *                     fp16 scales [rows][cols/128]; H, I multiples of 128;
+ *   MOE_FMT_INT8_G32  codes int8 [rows][cols] (two's complement, passed as
+ *                     uint8), fp16 scales [rows][cols/32]; H, I multiples of 32.
+ * For the two new formats T <= 32 and H, I <= 4096 (int8) / 8192 (int4);
+ * larger shapes return MOE_EUNSUP (no fallback). Each (token, expert) pair
+ * reads its expert's rows (one read per chosen expert for one token). x, and
+ * the intermediate h, must fit fp16 (else MOE_EUNSUP in dev_status). The
+ * layout of these blobs belongs to the library. */
+size_t moe_fmt_blob_bytes(int fmt, int H, int I);  /* 0 on an unsupported format or shape */
+size_t moe_fmt_slot_stride(int fmt, int H, int I); /* moe_fmt_blob_bytes rounded up to 4096 */
+int moe_pack_expert_fmt(int fmt, const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, const uint16_t* sg,
+                        const uint16_t* su, const uint16_t* sd, int H, int I, void* blob_out);
+size_t moe_fmt_workspace_bytes(int fmt, int T, int H, int I, int E, int K, int has_shared);
+int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E,
+                       int K, const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
+                       uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, moe_stream_t stream);
 
 /* Chunked paged prefill ("Strata on a Mac", Measured, the UD-Q4/Q5/Q6_K_XL
  * part: each prompt chunk makes one pass over the experts it uses that are not

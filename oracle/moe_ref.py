@@ -76,6 +76,25 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, cols: int, g: int = 32) -
     return q * np.repeat(s, g, axis=-1)
 
 
+def unpack_int8(codes: np.ndarray) -> np.ndarray:
+    """Decode int8 codes held as bytes (uint8) to int64 values in [-128, 127]:
+    two's complement, b - 256 for b >= 128 (the INT8 group-32 experts of the
+    "Strata" README, Models and Kernels)."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(b >= 128, b - 256, b)
+
+
+def dequantize_int8(codes: np.ndarray, scales: np.ndarray, cols: int, g: int = 32) -> np.ndarray:
+    """W[n, j] = q[n, j] * s[n, j // g] in float64 for int8 codes [rows, cols]."""
+    q = unpack_int8(codes).astype(np.float64)
+    if q.shape[-1] != cols:
+        raise ValueError("code row length does not match cols")
+    s = f16_to_f64(scales)
+    if s.shape[-1] * g != cols:
+        raise ValueError("scale count does not match cols / g")
+    return q * np.repeat(s, g, axis=-1)
+
+
 # ---------------------------------------------------------------- router
 
 
@@ -245,13 +264,17 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 class Expert:
-    """One int4 expert held as fp64 matrices: gate [I, H], up [I, H], down [H, I]."""
+    """One expert held as fp64 matrices: gate [I, H], up [I, H], down [H, I].
 
-    def __init__(self, tensors: dict, H: int, I: int, g: int = 32):
+    bits = 4: packed int4 codes (group g = 32 or 128); bits = 8: int8 codes
+    (group 32). W[n, j] = q[n, j] * s[n, j // g] either way."""
+
+    def __init__(self, tensors: dict, H: int, I: int, g: int = 32, bits: int = 4):
         self.H, self.I = H, I
-        self.Wg = dequantize(tensors["qg"], tensors["sg"], H, g)
-        self.Wu = dequantize(tensors["qu"], tensors["su"], H, g)
-        self.Wd = dequantize(tensors["qd"], tensors["sd"], I, g)
+        deq = dequantize if bits == 4 else dequantize_int8
+        self.Wg = deq(tensors["qg"], tensors["sg"], H, g)
+        self.Wu = deq(tensors["qu"], tensors["su"], H, g)
+        self.Wd = deq(tensors["qd"], tensors["sd"], I, g)
         if self.Wg.shape != (I, H) or self.Wu.shape != (I, H) or self.Wd.shape != (H, I):
             raise ValueError("expert tensor shapes do not match (H, I)")
 

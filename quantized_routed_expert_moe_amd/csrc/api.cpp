@@ -238,3 +238,47 @@ extern "C" int moe_ffn_combine(const float* w, int T, int H, int I, int E, int K
   if (moe::launch_grouped_combine(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
+
+extern "C" size_t moe_fmt_workspace_bytes(int fmt, int T, int H, int I, int E, int K, int has_shared) {
+  if (fmt == MOE_FMT_INT4_G32) return moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, 0);
+  if (T <= 0 || T > moe::kGemvMaxT || E <= 0 || K <= 0 || !moe::fmt_shape_ok(fmt, H, I)) return 0;
+  return moe::fmt_workspace_bytes(T, H, I, K, has_shared);
+}
+
+extern "C" int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I,
+                                  int E, int K, const int32_t* slot_table, const void* slots, size_t stride,
+                                  const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
+                                  int32_t* dev_status, moe_stream_t stream) {
+  if (fmt == MOE_FMT_INT4_G32)
+    return moe_expert_ffn(x, ids, w, T, H, I, E, K, moe::kGroup, slot_table, slots, stride, shared_blob, y, ws,
+                          ws_bytes, dev_status, 0, stream);
+  if (fmt != MOE_FMT_INT4_G128 && fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
+  if (!moe::fmt_shape_ok(fmt, H, I) || E > moe::kMaxE || K > moe::kMaxK || T > moe::kGemvMaxT) return MOE_EUNSUP;
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !w || !slot_table || !slots || !y || !dev_status) return MOE_EINVAL;
+  if (stride < moe_fmt_blob_bytes(fmt, H, I) || stride % 256) return MOE_EINVAL;
+  const size_t need = moe_fmt_workspace_bytes(fmt, T, H, I, E, K, shared_blob != nullptr);
+  if (need == 0) return MOE_EUNSUP;
+  if (!ws || ws_bytes < need) return MOE_EWS;
+  moe::FfnArgs a{};
+  a.x = x;
+  a.ids = ids;
+  a.w = w;
+  a.T = T;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.K = K;
+  a.slot_table = slot_table;
+  a.slots = static_cast<const uint8_t*>(slots);
+  a.stride = stride;
+  a.shared_blob = static_cast<const uint8_t*>(shared_blob);
+  a.y = y;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.ws_bytes = ws_bytes;
+  a.status = dev_status;
+  const hipError_t err = moe::launch_ffn_fmt(fmt, a, static_cast<hipStream_t>(stream));
+  if (err == hipErrorNotSupported) return MOE_EUNSUP;
+  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}

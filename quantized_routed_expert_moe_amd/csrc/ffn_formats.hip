@@ -1,0 +1,310 @@
+// Expert FFN for the other weight formats the "Strata" README names (Models:
+// INT8 group-32 linears; Kernels: INT4 group-128 and INT8 group-32 kernels; all
+// with 16-bit activations): the same layer as moe_expert_ffn,
+//   y[t] = shared(x[t]) + sum_k w[t][k] * FFN_{ids[t][k]}(x[t]),
+//   FFN(x) = Wd (silu(Wg x) * (Wu x)),  W[n][j] = q[n][j] * s[n][j / g],
+// with int8 (g = 32) or int4 (g = 128) codes and fp16 scales, for T <= 32.
+//
+// Blob (FmtLayout): gate codes [I] rows, up codes [I], down codes [H] rows, each
+// row contiguous, then the fp16 scales [rows][cols / g] of the three matrices.
+// A row is a run of 16-byte chunks: int8, 16 columns per chunk, offset binary
+// u = q + 128 in column order; int4, 32 columns per chunk, the nibble
+// interleave of the group-32 blob (offset binary u = q + 8), so that one mask
+// and one OR give fp16 pairs of consecutive columns.
+//
+// Dequantisation is exact and lives in the fp16 dot products: int8 pairs
+// (0x64 << 8 | u) = 1024 + u = q + 1152 come from one v_perm_b32 per two codes;
+// int4 pairs are q + 1032 or q + 72 (one AND-OR each). A chunk's v_dot2 sum
+// D = sum_c (q_c + off_c) x_c then gives sum_c q_c x_c = D - sum_c off_c x_c,
+// with the x sums per chunk staged once, and the chunk result is scaled by its
+// group's fp16 scale in fp32. x (and h for the down projection) are staged as
+// fp16 (a value past the fp16 range sets MOE_EUNSUP).
+//
+// Work: one item per (token, expert) pair and row block, so an expert's bytes
+// are read once per token that uses it (the single-token decode reads each
+// chosen expert once). Kernel 1: item = (pair, 8 rows of I), wave w the rows
+// 2w, 2w + 1 of gate and up, lanes the chunks of a row; h = silu(g) * u in
+// fp32. Kernel 2: item = (pair, 8 rows of H), o in fp32. Kernel 3: the
+// combine in rank order, one bf16 rounding. No atomics: the reduction order
+// depends only on (T, K, the format).
+#include "moe_internal.h"
+#include "wave_ops.h"
+
+namespace moe {
+namespace {
+
+constexpr int kFThreads = 256;
+constexpr int kRowsPerItem = 8;
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<MOE_FMT_INT8_G32> {
+  static constexpr int kCols = 16;  // columns per 16-byte chunk
+  static constexpr int kG = 32;
+};
+template <>
+struct Fmt<MOE_FMT_INT4_G128> {
+  static constexpr int kCols = 32;
+  static constexpr int kG = 128;
+};
+
+__host__ __device__ inline size_t fmt_al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct FmtWs {
+  size_t h, o, bytes;
+};
+__host__ __device__ inline FmtWs fmt_ws(int T, int H, int I, int K, int has_shared) {
+  const size_t PA = (size_t)T * K + (has_shared ? T : 0);
+  FmtWs w;
+  w.h = 0;
+  w.o = fmt_al256(PA * I * 4);
+  w.bytes = fmt_al256(w.o + PA * H * 4);
+  return w;
+}
+
+// Blob of pair p (the shared expert for p >= T K), or nullptr with the status set.
+__device__ inline const uint8_t* fmt_pair_blob(const FfnArgs& a, int p) {
+  const int P = a.T * a.K;
+  if (p >= P) return a.shared_blob;
+  const int e = a.ids[p];
+  if (e < 0 || e >= a.E) {
+    *a.status = MOE_EINVAL;
+    return nullptr;
+  }
+  const int slot = a.slot_table[e];
+  if (slot < 0) {
+    *a.status = MOE_ENOTRES;
+    return nullptr;
+  }
+  return a.slots + (size_t)slot * a.stride;
+}
+
+// Stage n activations (fp32 or bf16 source) as fp16 pairs into xs, and per chunk
+// the sum of its fp16 values times the code offsets: int8, 1152 * sum over the
+// chunk; int4, 1032 * (columns 8d + 0, 1, 4, 5) + 72 * (8d + 2, 3, 6, 7).
+template <int FMT, typename Src>
+__device__ inline void stage_act(const Src* src, int n, uint32_t* xs, float* corr, int32_t* status) {
+  constexpr int C = Fmt<FMT>::kCols;
+  const int n_chunks = n / C;
+  bool bad = false;
+  for (int c = threadIdx.x; c < n_chunks; c += kFThreads) {
+    float ca = 0.0f, cb = 0.0f;
+#pragma unroll
+    for (int j = 0; j < C; j += 2) {
+      float v0, v1;
+      if constexpr (sizeof(Src) == 2) {
+        const uint32_t b = reinterpret_cast<const uint32_t*>(src)[(c * C + j) / 2];
+        v0 = __uint_as_float(b << 16);
+        v1 = __uint_as_float(b & 0xFFFF0000u);
+      } else {
+        v0 = src[c * C + j];
+        v1 = src[c * C + j + 1];
+      }
+      const uint32_t h0 = to_f16_bits(v0, &bad), h1 = to_f16_bits(v1, &bad);
+      xs[(c * C + j) / 2] = h0 | (h1 << 16);
+      const float s = f16_lo(h0) + f16_lo(h1);
+      // int4: the pair of columns j, j + 1 is an A pair (offset 1032) for j % 8 in
+      // {0, 4} and a B pair (offset 72) for j % 8 in {2, 6}
+      if (FMT == MOE_FMT_INT4_G128 && ((j >> 1) & 1))
+        cb += s;
+      else
+        ca += s;
+    }
+    corr[c] = FMT == MOE_FMT_INT8_G32 ? 1152.0f * ca : fmaf(1032.0f, ca, 72.0f * cb);
+  }
+  if (bad) *status = MOE_EUNSUP;
+}
+
+// D for one 16-byte chunk against its fp16 activation pairs xp[0 .. C/2).
+template <int FMT>
+__device__ inline float chunk_dot(const uint4& cw, const uint32_t* xp) {
+  const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+  float d = 0.0f;
+  if constexpr (FMT == MOE_FMT_INT8_G32) {
+    // bytes [b0, 0x64, b1, 0x64] and [b2, 0x64, b3, 0x64]: fp16 1024 + u of columns 4i .. 4i + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d = dot2h(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04010400u), xp[2 * i], d);
+      d = dot2h(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04030402u), xp[2 * i + 1], d);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d = code_dot(w[i], xp[4 * i], xp[4 * i + 1], xp[4 * i + 2], xp[4 * i + 3], d);
+  }
+  return d;
+}
+
+template <int FMT>
+__host__ __device__ inline size_t row_bytes(int cols) {
+  return (size_t)cols / Fmt<FMT>::kCols * 16;
+}
+
+// One wave: S row streams (codes rows, scale rows) over cols columns against the
+// staged activations; lane l takes chunks l, l + 64, ...; returns the full dot
+// products on every lane.
+template <int FMT, int S, int STEPS>
+__device__ inline void rows_dot(const uint8_t* const (&codes)[S], const _Float16* const (&scales)[S], int cols,
+                                const uint32_t* xs, const float* corr, float scale_mask, int lane, float (&out)[S]) {
+  constexpr int C = Fmt<FMT>::kCols;
+  const int n_chunks = cols / C;
+  uint4 cw[S][STEPS];
+  float sc[S][STEPS];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      int c = i * 64 + lane;
+      c = c < n_chunks ? c : n_chunks - 1;  // a real chunk, scaled by 0 below
+      cw[s][i] = *reinterpret_cast<const uint4*>(codes[s] + (size_t)c * 16);
+      sc[s][i] = (float)scales[s][(size_t)c * C / Fmt<FMT>::kG];
+    }
+#pragma unroll
+  for (int s = 0; s < S; ++s) out[s] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+    const int c = i * 64 + lane;
+    const bool live = c < n_chunks;
+    const int cc = live ? c : n_chunks - 1;
+    const uint32_t* xp = xs + cc * (C / 2);
+    const float k = live ? scale_mask : 0.0f;
+    const float cr = corr[cc];
+#pragma unroll
+    for (int s = 0; s < S; ++s) out[s] = fmaf(sc[s][i] * k, chunk_dot<FMT>(cw[s][i], xp) - cr, out[s]);
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) out[s] = wave_sum_f32(out[s]);
+}
+
+template <int FMT, int STEPS>
+__global__ void __launch_bounds__(kFThreads) fmt_gateup_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I, K = a.K, P = a.T * a.K;
+  uint32_t* xs = reinterpret_cast<uint32_t*>(smem);
+  float* corr = reinterpret_cast<float*>(smem + (size_t)H * 2);
+  const int n_rb = I / kRowsPerItem;
+  const int p = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  const int t = p < P ? p / K : p - P;
+  const uint8_t* blob = fmt_pair_blob(a, p);
+  stage_act<FMT>(a.x + (size_t)t * H, H, xs, corr, a.status);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const FmtLayout L = fmt_layout(FMT, H, I);
+  const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
+  const int n0 = rb * kRowsPerItem + 2 * wave;
+  const size_t rbytes = row_bytes<FMT>(H);
+  const int gs = H / Fmt<FMT>::kG;
+  const uint8_t* const codes[4] = {src + L.gate_codes + n0 * rbytes, src + L.gate_codes + (n0 + 1) * rbytes,
+                                   src + L.up_codes + n0 * rbytes, src + L.up_codes + (n0 + 1) * rbytes};
+  const _Float16* gsc = reinterpret_cast<const _Float16*>(src + L.gate_scales);
+  const _Float16* usc = reinterpret_cast<const _Float16*>(src + L.up_scales);
+  const _Float16* const scales[4] = {gsc + (size_t)n0 * gs, gsc + (size_t)(n0 + 1) * gs, usc + (size_t)n0 * gs,
+                                     usc + (size_t)(n0 + 1) * gs};
+  float r[4];
+  rows_dot<FMT, 4, STEPS>(codes, scales, H, xs, corr, blob ? 1.0f : 0.0f, lane, r);
+  if (lane < 2) {
+    const float g = lane ? r[1] : r[0], u = lane ? r[3] : r[2];
+    reinterpret_cast<float*>(a.ws)[(size_t)p * I + n0 + lane] = silu(g) * u;
+  }
+}
+
+template <int FMT, int STEPS>
+__global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I;
+  const bool has_shared = a.shared_blob != nullptr;
+  const FmtWs W = fmt_ws(a.T, H, I, a.K, has_shared);
+  uint32_t* hs = reinterpret_cast<uint32_t*>(smem);
+  float* corr = reinterpret_cast<float*>(smem + (size_t)I * 2);
+  const int n_rb = H / kRowsPerItem;
+  const int p = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  const uint8_t* blob = fmt_pair_blob(a, p);
+  stage_act<FMT>(reinterpret_cast<const float*>(a.ws + W.h) + (size_t)p * I, I, hs, corr, a.status);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const FmtLayout L = fmt_layout(FMT, H, I);
+  const uint8_t* src = blob ? blob : a.slots;
+  const int n0 = rb * kRowsPerItem + 2 * wave;
+  const size_t rbytes = row_bytes<FMT>(I);
+  const int gs = I / Fmt<FMT>::kG;
+  const uint8_t* const codes[2] = {src + L.down_codes + n0 * rbytes, src + L.down_codes + (n0 + 1) * rbytes};
+  const _Float16* dsc = reinterpret_cast<const _Float16*>(src + L.down_scales);
+  const _Float16* const scales[2] = {dsc + (size_t)n0 * gs, dsc + (size_t)(n0 + 1) * gs};
+  float r[2];
+  rows_dot<FMT, 2, STEPS>(codes, scales, I, hs, corr, blob ? 1.0f : 0.0f, lane, r);
+  if (lane < 2) reinterpret_cast<float*>(a.ws + W.o)[(size_t)p * H + n0 + lane] = lane ? r[1] : r[0];
+}
+
+__global__ void __launch_bounds__(256) fmt_combine_kernel(FfnArgs a) {
+  const int H = a.H, T = a.T, K = a.K, P = T * K;
+  const bool has_shared = a.shared_blob != nullptr;
+  const FmtWs W = fmt_ws(T, H, a.I, K, has_shared);
+  const float* o = reinterpret_cast<const float*>(a.ws + W.o);
+  const size_t n = (size_t)T * H;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int t = (int)(i / H), c = (int)(i % H);
+    float acc = has_shared ? o[(size_t)(P + t) * H + c] : 0.0f;
+    for (int k = 0; k < K; ++k) acc = fmaf(a.w[t * K + k], o[(size_t)(t * K + k) * H + c], acc);
+    a.y[i] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+  }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const FfnArgs& a, hipStream_t s) {
+  constexpr int C = Fmt<FMT>::kCols;
+  const bool has_shared = a.shared_blob != nullptr;
+  const int PA = a.T * a.K + (has_shared ? a.T : 0);
+  const int steps_gu = (a.H / C + 63) / 64, steps_dn = (a.I / C + 63) / 64;
+  const size_t lds_gu = (size_t)a.H * 2 + (size_t)a.H / C * 4, lds_dn = (size_t)a.I * 2 + (size_t)a.I / C * 4;
+  const int grid_gu = PA * (a.I / kRowsPerItem), grid_dn = PA * (a.H / kRowsPerItem);
+#define GU(N)                                                                                     \
+  do {                                                                                            \
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fmt_gateup_kernel<FMT, N>),          \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu);           \
+    hipLaunchKernelGGL((fmt_gateup_kernel<FMT, N>), dim3(grid_gu), dim3(kFThreads), lds_gu, s, a); \
+  } while (0)
+#define DN(N)                                                                                   \
+  do {                                                                                          \
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fmt_down_kernel<FMT, N>),          \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn);         \
+    hipLaunchKernelGGL((fmt_down_kernel<FMT, N>), dim3(grid_dn), dim3(kFThreads), lds_dn, s, a); \
+  } while (0)
+  if (steps_gu == 1) GU(1);
+  else if (steps_gu == 2) GU(2);
+  else if (steps_gu <= 4) GU(4);
+  else return hipErrorNotSupported;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (steps_dn == 1) DN(1);
+  else if (steps_dn == 2) DN(2);
+  else if (steps_dn <= 4) DN(4);
+  else return hipErrorNotSupported;
+#undef GU
+#undef DN
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t n = (size_t)a.T * a.H;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fmt_combine_kernel, dim3(blocks < 4096 ? (int)blocks : 4096), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fmt_shape_ok(int fmt, int H, int I) {
+  if (fmt != MOE_FMT_INT8_G32 && fmt != MOE_FMT_INT4_G128) return false;
+  const int C = fmt == MOE_FMT_INT8_G32 ? 16 : 32, g = fmt == MOE_FMT_INT8_G32 ? 32 : 128;
+  // at most 4 steps of 64 chunks per row, whole groups, whole row blocks
+  return H > 0 && I > 0 && H % g == 0 && I % g == 0 && H / C <= 256 && I / C <= 256 && H % kRowsPerItem == 0 &&
+         I % kRowsPerItem == 0;
+}
+
+size_t fmt_workspace_bytes(int T, int H, int I, int K, int has_shared) {
+  return fmt_ws(T, H, I, K, has_shared).bytes;
+}
+
+hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
+  if (!fmt_shape_ok(fmt, a.H, a.I)) return hipErrorNotSupported;
+  return fmt == MOE_FMT_INT8_G32 ? launch_fmt<MOE_FMT_INT8_G32>(a, s) : launch_fmt<MOE_FMT_INT4_G128>(a, s);
+}
+
+}  // namespace moe

@@ -46,6 +46,32 @@ __host__ __device__ inline BlobLayout blob_layout(int H, int I) {
   return L;
 }
 
+// Blob of the other formats (moe_pack_expert_fmt; the kernels in
+// ffn_formats.hip): per matrix the rows one after another, a row being its
+// 16-byte code chunks in column order (int8: 16 columns per chunk, offset binary
+// u = q + 128; int4: 32 columns, the nibble interleave of the group-32 blob),
+// then the fp16 scales [rows][cols / g]; every region starts on 256 bytes.
+struct FmtLayout {
+  size_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales, bytes;
+};
+__host__ __device__ inline FmtLayout fmt_layout(int fmt, int H, int I) {
+  const int bits = fmt == MOE_FMT_INT8_G32 ? 8 : 4, g = fmt == MOE_FMT_INT8_G32 ? 32 : 128;
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t gu_codes = (size_t)I * H * bits / 8, dn_codes = (size_t)H * I * bits / 8;
+  const size_t gu_scales = (size_t)I * (H / g) * 2, dn_scales = (size_t)H * (I / g) * 2;
+  FmtLayout L;
+  L.gate_codes = 0;
+  L.up_codes = al(L.gate_codes + gu_codes);
+  L.down_codes = al(L.up_codes + gu_codes);
+  L.gate_scales = al(L.down_codes + dn_codes);
+  L.up_scales = al(L.gate_scales + gu_scales);
+  L.down_scales = al(L.up_scales + gu_scales);
+  L.bytes = al(L.down_scales + dn_scales);
+  return L;
+}
+bool fmt_shape_ok(int fmt, int H, int I);
+size_t fmt_workspace_bytes(int T, int H, int I, int K, int has_shared);
+
 // Byte offset of the code chunk / the scale of (row n, group j) within a matrix
 // of G groups stored in blocks of R rows.
 __host__ __device__ inline size_t chunk_index(int n, int j, int G, int R) {
@@ -93,6 +119,8 @@ struct FfnArgs {
 // computes the shared expert.
 constexpr unsigned kModePartial = 1u, kModePartialShared = 2u;
 hipError_t launch_grouped_combine(const FfnArgs& a, hipStream_t s);
+// the other expert formats (ffn_formats.hip): gate/up, down and combine
+hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, hipStream_t s);
 
 // Each path launches in two stages: stage 0 = gate/up (h into the workspace),
 // stage 1 = down + combine (y).

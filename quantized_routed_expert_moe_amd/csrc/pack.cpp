@@ -66,3 +66,53 @@ extern "C" int moe_pack_expert(const uint8_t* qg, const uint8_t* qu, const uint8
   pack_matrix(qd, sd, H, I, moe::kRowBlockDN, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
   return MOE_OK;
 }
+
+// ------------------------------------------------------------------ other formats
+namespace {
+
+// one matrix of N rows and C columns into the row-major layout of the formats
+// blob (moe_internal.h, FmtLayout)
+void pack_matrix_fmt(int fmt, const uint8_t* q, const uint16_t* s, int N, int C, uint8_t* codes, uint16_t* scales) {
+  const int g = fmt == MOE_FMT_INT8_G32 ? 32 : 128;
+  if (fmt == MOE_FMT_INT8_G32) {
+    for (size_t i = 0; i < (size_t)N * C; ++i) codes[i] = (uint8_t)(q[i] ^ 0x80u);  // two's complement -> q + 128
+  } else {
+    const size_t chunks = (size_t)N * C / 32;  // 16 bytes = 32 columns each, rows back to back
+    for (size_t k = 0; k < chunks; ++k) {
+      uint32_t src[4], dst[4];
+      memcpy(src, q + k * 16, 16);
+      for (int d = 0; d < 4; ++d) dst[d] = interleave_dword(src[d]);
+      memcpy(codes + k * 16, dst, 16);
+    }
+  }
+  memcpy(scales, s, (size_t)N * (C / g) * 2);
+}
+
+}  // namespace
+
+extern "C" size_t moe_fmt_blob_bytes(int fmt, int H, int I) {
+  if (fmt == MOE_FMT_INT4_G32) return moe_blob_bytes(H, I, moe::kGroup);
+  if (!moe::fmt_shape_ok(fmt, H, I)) return 0;
+  return moe::fmt_layout(fmt, H, I).bytes;
+}
+
+extern "C" size_t moe_fmt_slot_stride(int fmt, int H, int I) {
+  const size_t b = moe_fmt_blob_bytes(fmt, H, I);
+  return (b + 4095) / 4096 * 4096;
+}
+
+extern "C" int moe_pack_expert_fmt(int fmt, const uint8_t* qg, const uint8_t* qu, const uint8_t* qd,
+                                   const uint16_t* sg, const uint16_t* su, const uint16_t* sd, int H, int I,
+                                   void* blob_out) {
+  if (fmt == MOE_FMT_INT4_G32) return moe_pack_expert(qg, qu, qd, sg, su, sd, H, I, moe::kGroup, blob_out);
+  if (fmt != MOE_FMT_INT4_G128 && fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;
+  if (!qg || !qu || !qd || !sg || !su || !sd || !blob_out) return MOE_EINVAL;
+  if (!moe::fmt_shape_ok(fmt, H, I)) return MOE_EUNSUP;
+  const moe::FmtLayout L = moe::fmt_layout(fmt, H, I);
+  uint8_t* b = static_cast<uint8_t*>(blob_out);
+  memset(b, 0, L.bytes);  // padding between regions
+  pack_matrix_fmt(fmt, qg, sg, I, H, b + L.gate_codes, reinterpret_cast<uint16_t*>(b + L.gate_scales));
+  pack_matrix_fmt(fmt, qu, su, I, H, b + L.up_codes, reinterpret_cast<uint16_t*>(b + L.up_scales));
+  pack_matrix_fmt(fmt, qd, sd, H, I, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
+  return MOE_OK;
+}

@@ -28,6 +28,17 @@ def pack_expert(seed: int, layer: int, expert: int, H: int, I: int, g: int = 32)
     return out
 
 
+def pack_expert_fmt(seed: int, layer: int, expert: int, H: int, I: int, fmt: int) -> np.ndarray:
+    """Seeded expert in format ``fmt`` -> host blob (uint8, one slot stride long)."""
+    t = gen.expert_tensors_fmt(seed, layer, expert, H, I, fmt)
+    out = np.zeros(lib.moe_fmt_slot_stride(fmt, H, I), dtype=np.uint8)
+    lib.moe_pack_expert_fmt(
+        fmt, t["qg"], t["qu"], t["qd"], t["sg"].view(np.uint16), t["su"].view(np.uint16), t["sd"].view(np.uint16),
+        H, I, out,
+    )
+    return out
+
+
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
 

@@ -21,6 +21,7 @@ MOE_ROUTE_RENORM = 1 << 0
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_FORCE_GEMV = 1 << 8
 MOE_FORCE_GROUPED = 1 << 9
+MOE_FMT_INT4_G32, MOE_FMT_INT4_G128, MOE_FMT_INT8_G32 = 0, 1, 2
 MOE_FFN_PARTIAL = 1 << 10
 MOE_FFN_PARTIAL_SHARED = 1 << 11
 
@@ -39,6 +40,11 @@ EXPORTS = (
     "moe_ffn_down",
     "moe_layer",
     "moe_ffn_combine",
+    "moe_fmt_blob_bytes",
+    "moe_fmt_slot_stride",
+    "moe_pack_expert_fmt",
+    "moe_fmt_workspace_bytes",
+    "moe_expert_ffn_fmt",
     "arena_create",
     "arena_map_slots",
     "arena_fill_async",
@@ -107,6 +113,14 @@ def load(path: str | None = None):
              ctypes.c_uint, _P],
         ),
         "moe_ffn_combine": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+        "moe_fmt_blob_bytes": (_SZ, [_I, _I, _I]),
+        "moe_fmt_slot_stride": (_SZ, [_I, _I, _I]),
+        "moe_pack_expert_fmt": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
+        "moe_fmt_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+        "moe_expert_ffn_fmt": (
+            _I,
+            [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P, _P, _SZ, _P, _P],
+        ),
         "arena_create": (_I, [_I, _I, _SZ, _SZ, _P, _P, _P, ctypes.POINTER(_P)]),
         "arena_map_slots": (_I, [_P, _P, _I, _P, _P, ctypes.POINTER(_I)]),
         "arena_fill_async": (_I, [_P, _P, _I, _P, _P]),
@@ -185,6 +199,15 @@ def moe_pack_expert(qg, qu, qd, sg, su, sd, H, I, g, blob_out) -> None:
     )
 
 
+def moe_pack_expert_fmt(fmt, qg, qu, qd, sg, su, sd, H, I, blob_out) -> None:
+    """moe_pack_expert for format ``fmt`` (host numpy arrays)."""
+    _check(
+        load().moe_pack_expert_fmt(fmt, _ptr(qg), _ptr(qu), _ptr(qd), _ptr(sg), _ptr(su), _ptr(sd), H, I,
+                                   _ptr(blob_out)),
+        "moe_pack_expert_fmt",
+    )
+
+
 def moe_route(x, w_router, logits, T, H, E, K, flags, ids, w, stream=None) -> None:
     _check(
         load().moe_route(_ptr(x), _ptr(w_router), _ptr(logits), T, H, E, K, flags, _ptr(ids), _ptr(w), _stream(stream)),
@@ -250,6 +273,34 @@ def moe_ffn_combine(w, T, H, I, E, K, has_shared, y, ws, ws_bytes, stream=None) 
         load().moe_ffn_combine(_ptr(w), T, H, I, E, K, int(bool(has_shared)), _ptr(y), _ptr(ws), ws_bytes,
                                _stream(stream)),
         "moe_ffn_combine",
+    "moe_fmt_blob_bytes",
+    "moe_fmt_slot_stride",
+    "moe_pack_expert_fmt",
+    "moe_fmt_workspace_bytes",
+    "moe_expert_ffn_fmt",
+    )
+
+
+def moe_fmt_blob_bytes(fmt, H, I) -> int:
+    return load().moe_fmt_blob_bytes(fmt, H, I)
+
+
+def moe_fmt_slot_stride(fmt, H, I) -> int:
+    return load().moe_fmt_slot_stride(fmt, H, I)
+
+
+def moe_fmt_workspace_bytes(fmt, T, H, I, E, K, has_shared) -> int:
+    return load().moe_fmt_workspace_bytes(fmt, T, H, I, E, K, int(bool(has_shared)))
+
+
+def moe_expert_ffn_fmt(fmt, x, ids, w, T, H, I, E, K, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                       dev_status, stream=None) -> None:
+    _check(
+        load().moe_expert_ffn_fmt(
+            fmt, _ptr(x), _ptr(ids), _ptr(w), T, H, I, E, K, _ptr(slot_table), _ptr(slots), stride,
+            _ptr(shared_blob), _ptr(y), _ptr(ws), ws_bytes, _ptr(dev_status), _stream(stream),
+        ),
+        "moe_expert_ffn_fmt",
     )
 
 

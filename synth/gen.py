@@ -75,6 +75,35 @@ def expert_tensors(seed: int, layer: int, expert: int, H: int, I: int, g: int = 
     }
 
 
+# expert weight formats (the C enum moe_format)
+FMT_INT4_G32, FMT_INT4_G128, FMT_INT8_G32 = 0, 1, 2
+FMT_BITS_G = {FMT_INT4_G32: (4, 32), FMT_INT4_G128: (4, 128), FMT_INT8_G32: (8, 32)}
+
+
+def expert_tensors_fmt(seed: int, layer: int, expert: int, H: int, I: int, fmt: int) -> dict:
+    """Codes and scales of one expert in format ``fmt``. int4: as expert_tensors with
+    group 32 or 128. int8: uniform bytes (every code -128..127 occurs), scales
+    U(0.005, 0.02) / 16 in fp16, so the weights span the int4 experts' range."""
+    bits, g = FMT_BITS_G[fmt]
+    if bits == 4:
+        return expert_tensors(seed, layer, expert, H, I, g)
+
+    def codes(kind, rows, cols):
+        return _rng(seed, layer, expert, kind).integers(0, 256, size=(rows, cols), dtype=np.uint8)
+
+    def scales(kind, rows, cols):
+        return (_rng(seed, layer, expert, kind).uniform(0.005, 0.02, size=(rows, cols // g)) / 16).astype(np.float16)
+
+    return {
+        "qg": codes(KIND_QG, I, H),
+        "qu": codes(KIND_QU, I, H),
+        "qd": codes(KIND_QD, H, I),
+        "sg": scales(KIND_SG, I, H),
+        "su": scales(KIND_SU, I, H),
+        "sd": scales(KIND_SD, H, I),
+    }
+
+
 def normal_logits(seed: int, layer: int, T: int, E: int) -> np.ndarray:
     return _rng(seed, layer, 0, KIND_LOGITS).standard_normal((T, E), dtype=np.float32)
 

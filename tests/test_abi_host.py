@@ -163,3 +163,58 @@ def test_arena_cpp_chunk_passes_matches_model():
         with pytest.raises(lib.MoeError):
             a.chunk_passes([0], S + 1)
         assert a.chunk_passes([], 1) == []
+
+
+def al256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("fmt,H,I", [(gen.FMT_INT8_G32, 256, 96), (gen.FMT_INT8_G32, 4096, 1536),
+                                     (gen.FMT_INT4_G128, 512, 256), (gen.FMT_INT4_G128, 4096, 1536)])
+def test_fmt_pack_layout_roundtrip(fmt, H, I):
+    """The format blobs decode back to the interchange codes and scales (an independent
+    reader of the documented row-major layout)."""
+    bits, g = gen.FMT_BITS_G[fmt]
+    t = gen.expert_tensors_fmt(9, 0, 3, H, I, fmt)
+    nb = lib.moe_fmt_blob_bytes(fmt, H, I)
+    cb_gu, cb_dn = I * H * bits // 8, H * I * bits // 8
+    sb_gu, sb_dn = I * (H // g) * 2, H * (I // g) * 2
+    offs = [0]
+    for size in (cb_gu, cb_gu, cb_dn, sb_gu, sb_gu, sb_dn):
+        offs.append(al256(offs[-1] + size))
+    assert nb == offs[-1]
+    assert lib.moe_fmt_slot_stride(fmt, H, I) == (nb + 4095) // 4096 * 4096
+    blob = np.zeros(lib.moe_fmt_slot_stride(fmt, H, I), dtype=np.uint8)
+    lib.moe_pack_expert_fmt(fmt, t["qg"], t["qu"], t["qd"], t["sg"].view(np.uint16), t["su"].view(np.uint16),
+                            t["sd"].view(np.uint16), H, I, blob)
+    mats = [("qg", "sg", I, H, offs[0], offs[3]), ("qu", "su", I, H, offs[1], offs[4]),
+            ("qd", "sd", H, I, offs[2], offs[5])]
+    for qk, sk, N, C, oc, os_ in mats:
+        if bits == 8:
+            u = blob[oc : oc + N * C].reshape(N, C).astype(np.int64)
+            assert np.array_equal(u - 128, t[qk].view(np.int8).astype(np.int64))
+        else:
+            # rows back to back, 16-byte chunks of 32 columns, the group-32 blob's nibble interleave
+            w = np.frombuffer(blob.tobytes(), dtype=np.uint32, count=N * C // 8, offset=oc).reshape(N, C // 32, 4)
+            q = np.empty((N, C), dtype=np.int64)
+            for d in range(4):
+                for i in range(8):
+                    col = 8 * d + (2 * i if i < 4 else 2 * (i - 4) + 1)
+                    q[:, col::32] = ((w[:, :, d] >> (4 * i)) & 0xF).astype(np.int64) - 8
+            assert np.array_equal(q, unpack_plain(t[qk], C))
+        s = np.frombuffer(blob.tobytes(), dtype=np.uint16, count=N * (C // g), offset=os_).reshape(N, C // g)
+        assert np.array_equal(s, t[sk].view(np.uint16))
+
+
+def test_fmt_sizes_and_rejections():
+    assert lib.moe_fmt_blob_bytes(gen.FMT_INT4_G32, 4096, 1536) == lib.moe_blob_bytes(4096, 1536, 32)
+    assert lib.moe_fmt_slot_stride(gen.FMT_INT4_G32, 4096, 1536) == lib.moe_slot_stride(4096, 1536, 32)
+    assert lib.moe_fmt_blob_bytes(gen.FMT_INT4_G128, 4096, 1600) == 0  # I not a multiple of 128
+    assert lib.moe_fmt_blob_bytes(gen.FMT_INT8_G32, 8192, 1536) == 0  # int8 rows past 4096 columns
+    assert lib.moe_fmt_blob_bytes(7, 4096, 1536) == 0
+    assert lib.moe_fmt_workspace_bytes(gen.FMT_INT8_G32, 33, 4096, 1536, 256, 8, 1) == 0  # T > 32
+    z = np.zeros(16, np.uint8)
+    with pytest.raises(lib.MoeError):
+        lib.moe_pack_expert_fmt(7, z, z, z, z, z, z, 256, 96, z)
+    with pytest.raises(lib.MoeError):
+        lib.moe_pack_expert_fmt(gen.FMT_INT4_G128, z, z, z, z, z, z, 256, 96, z)

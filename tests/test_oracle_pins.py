@@ -373,3 +373,69 @@ def test_dense_limit_is_softmax_mixture():
     x = R.bf16_bits_to_f64(xb)
     want = sum(p[:, e : e + 1] * experts[e](x) for e in range(E))
     assert np.allclose(y, want, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ other expert formats
+
+
+def test_int8_decoding_all_bytes_against_numpy():
+    b = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(R.unpack_int8(b), b.view(np.int8).astype(np.int64))
+
+
+def test_int8_dequantize_hand_values():
+    # two's complement bytes 0x00, 0x7F (scale 0.5) and 0x80, 0xFF (scale 0.125); g = 2
+    # here to keep the fixture small
+    codes = np.array([[0x00, 0x7F, 0x80, 0xFF]], dtype=np.uint8)
+    s = np.array([[0.5, 0.125]], dtype=np.float16)
+    assert R.dequantize_int8(codes, s, 4, g=2).tolist() == [[0.0, 63.5, -16.0, -0.125]]
+    with pytest.raises(ValueError):
+        R.dequantize_int8(codes, s, 4, g=4)
+
+
+def test_group_128_equals_group_32_with_repeated_scales():
+    rng = np.random.default_rng(12)
+    packed = rng.integers(0, 256, size=(3, 128), dtype=np.uint8)  # 256 columns
+    s128 = rng.uniform(0.005, 0.02, size=(3, 2)).astype(np.float16)
+    w128 = R.dequantize(packed, s128, 256, g=128)
+    w32 = R.dequantize(packed, np.repeat(s128, 4, axis=1), 256, g=32)
+    assert np.array_equal(w128, w32)
+    # and a different scale in one group changes exactly that group's 128 columns
+    s2 = s128.copy()
+    s2[1, 1] = np.float16(0.5)
+    d = R.dequantize(packed, s2, 256, g=128) != w128
+    assert not d[:, :128].any() and not d[0].any() and not d[2].any()
+
+
+def test_int8_identity_expert_closed_form():
+    H, I = 64, 96
+    eye_gu = np.zeros((I, H), dtype=np.int64)
+    eye_gu[np.arange(H), np.arange(H)] = 1
+    eye_dn = np.zeros((H, I), dtype=np.int64)
+    eye_dn[np.arange(H), np.arange(H)] = 1
+
+    def as_bytes(q, mult):
+        return ((q * mult) & 0xFF).astype(np.uint8)
+
+    t = {
+        "qg": as_bytes(eye_gu, 4), "qu": as_bytes(eye_gu, -3), "qd": as_bytes(eye_dn, 127),
+        "sg": np.full((I, H // 32), 0.5, dtype=np.float16), "su": np.full((I, H // 32), 0.25, dtype=np.float16),
+        "sd": np.full((H, I // 32), 0.125, dtype=np.float16),
+    }
+    ex = R.Expert(t, H, I, g=32, bits=8)
+    rng = np.random.default_rng(13)
+    x = R.bf16_bits_to_f64(bits_of(rng.standard_normal((3, H))))
+    xt = torch.from_numpy(x)
+    # gate = 4 * 0.5 x, up = -3 * 0.25 x, down = 127 * 0.125 h
+    want = (127 * 0.125 * (-0.75 * xt) * torch.nn.functional.silu(2.0 * xt)).numpy()
+    assert np.allclose(ex(x), want, rtol=1e-14, atol=1e-300)
+
+
+def test_format_generator_ranges():
+    t8 = gen.expert_tensors_fmt(3, 0, 5, 64, 96, gen.FMT_INT8_G32)
+    q = R.unpack_int8(t8["qg"])
+    assert q.shape == (96, 64) and q.min() == -128 and q.max() == 127
+    assert t8["sg"].shape == (96, 2) and t8["sd"].shape == (64, 3)
+    t128 = gen.expert_tensors_fmt(3, 0, 5, 256, 128, gen.FMT_INT4_G128)
+    assert t128["sg"].shape == (128, 2) and t128["sd"].shape == (256, 1)
+    assert np.array_equal(t128["qg"], gen.expert_tensors(3, 0, 5, 256, 128, 32)["qg"])
