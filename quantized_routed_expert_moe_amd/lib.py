@@ -273,11 +273,6 @@ def moe_ffn_combine(w, T, H, I, E, K, has_shared, y, ws, ws_bytes, stream=None) 
         load().moe_ffn_combine(_ptr(w), T, H, I, E, K, int(bool(has_shared)), _ptr(y), _ptr(ws), ws_bytes,
                                _stream(stream)),
         "moe_ffn_combine",
-    "moe_fmt_blob_bytes",
-    "moe_fmt_slot_stride",
-    "moe_pack_expert_fmt",
-    "moe_fmt_workspace_bytes",
-    "moe_expert_ffn_fmt",
     )
 
 

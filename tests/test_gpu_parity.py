@@ -657,3 +657,156 @@ def test_partial_flags_and_combine_errors():
     assert int(run.status.item()) == 0
     y_res = resident_grouped(L, w, L.x, L.logits, w.T)
     assert torch.equal(run.y.view(torch.int16), y_res.view(torch.int16))
+
+
+# ------------------------------------------------------------------ other expert formats
+
+
+def fmt_layer(fmt, w, layer=0, place_seed=None, experts=None, S=None):
+    """Pack seeded experts of format fmt into slots (all E, or ``experts``), a table and a shared blob."""
+    stride = lib.moe_fmt_slot_stride(fmt, w.H, w.I)
+    ex = list(range(w.E)) if experts is None else list(experts)
+    S = S or len(ex)
+    order = np.random.default_rng(place_seed).permutation(S)[: len(ex)] if place_seed is not None else np.arange(len(ex))
+    slots = torch.zeros(S * stride, dtype=torch.uint8, device=DEV)
+    table = np.full(w.E, -1, dtype=np.int32)
+    for e, s in zip(ex, order):
+        slots[int(s) * stride : (int(s) + 1) * stride].copy_(
+            torch.from_numpy(harness.pack_expert_fmt(w.seed, layer, int(e), w.H, w.I, fmt)))
+        table[int(e)] = int(s)
+    shared = None
+    if w.shared:
+        shared = torch.from_numpy(harness.pack_expert_fmt(w.seed, layer, gen.SHARED_EXPERT, w.H, w.I, fmt)).to(DEV)
+    return slots, torch.from_numpy(table).to(DEV), shared, stride
+
+
+def fmt_oracle_expert(fmt, w, layer, e):
+    bits, g = gen.FMT_BITS_G[fmt]
+    return R.Expert(gen.expert_tensors_fmt(w.seed, layer, e, w.H, w.I, fmt), w.H, w.I, g=g, bits=bits)
+
+
+def fmt_run(fmt, w, slots, table, shared, stride, xb, logits):
+    x = harness.bf16_tensor(xb, DEV)
+    lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).to(DEV)
+    ids = torch.empty(w.T, w.K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(w.T, w.K, dtype=torch.float32, device=DEV)
+    y = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=DEV)
+    nb = lib.moe_fmt_workspace_bytes(fmt, w.T, w.H, w.I, w.E, w.K, shared is not None)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    lib.moe_route(None, None, lg, w.T, w.H, w.E, w.K, 0, ids, wts)
+    lib.moe_expert_ffn_fmt(fmt, x, ids, wts, w.T, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb, st)
+    torch.cuda.synchronize()
+    return ids, wts, y, st, (x, ws, nb)
+
+
+@pytest.mark.parametrize(
+    "fmt,w",
+    [
+        (gen.FMT_INT8_G32, gen.Workload("fmt8_t1_h512_e16_k4_i256_shared", 1, 512, 16, 4, 256, 1, 16, "normal", 71,
+                                        shared=True)),
+        (gen.FMT_INT8_G32, gen.Workload("fmt8_t7_h256_e8_k2_i96", 7, 256, 8, 2, 96, 1, 8, "normal", 72)),
+        (gen.FMT_INT8_G32, gen.Workload("fmt8_t32_h1024_e32_k8_i512_shared", 32, 1024, 32, 8, 512, 1, 32, "zipf", 73,
+                                        shared=True)),
+        (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t1_h512_e16_k4_i256_shared", 1, 512, 16, 4, 256, 1, 16, "normal",
+                                         74, shared=True)),
+        (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t9_h1024_e8_k3_i384", 9, 1024, 8, 3, 384, 1, 8, "normal", 75)),
+        (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t32_h2048_e32_k8_i768", 32, 2048, 32, 8, 768, 1, 32, "zipf", 76)),
+    ],
+    ids=lambda v: v.name if hasattr(v, "name") else f"fmt{v}",
+)
+def test_fmt_matches_oracle(fmt, w):
+    """INT8 group-32 and INT4 group-128 experts: ids bit-exact, y within the oracle's bar,
+    the same bits on a second run and under a permuted slot map."""
+    say(f"format {fmt} {w.name}")
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    logits = {"normal": gen.normal_logits, "zipf": gen.zipf_logits}[w.router](w.seed, 0, w.T, w.E)
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = fmt_oracle_expert(fmt, w, 0, e)
+        return cache[e]
+
+    shared_ref = fmt_oracle_expert(fmt, w, 0, gen.SHARED_EXPERT) if w.shared else None
+    y_ref, ids_ref, w_ref, _ = R.moe_layer(xb, expert, w.K, logits=logits, shared=shared_ref)
+    outs = []
+    for place in (None, 3):
+        slots, table, shared, stride = fmt_layer(fmt, w, place_seed=place)
+        ids, wts, y, st, _ = fmt_run(fmt, w, slots, table, shared, stride, xb, logits)
+        assert int(st.item()) == 0
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        if place is None:
+            check_close(y_f64(y), y_ref, f"  format {fmt} {w.name}")
+        outs.append(y.view(torch.int16).clone())
+        _, _, y2, _, _ = fmt_run(fmt, w, slots, table, shared, stride, xb, logits)
+        assert torch.equal(y2.view(torch.int16), outs[-1])
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_INT8_G32, gen.FMT_INT4_G128])
+def test_fmt_decode_full_size(fmt):
+    """One token, 256 experts, top-8, H 4096, I 1536 (the decode shape), the 8 routed experts
+    in a 64-slot arena: against the oracle."""
+    w = gen.Workload("fmt_decode_t1_h4096_e256_k8_i1536", 1, 4096, 256, 8, 1536, 1, 64, "normal", 77)
+    xb = gen.activations_bf16(w.seed, 0, 1, w.H)
+    logits = gen.normal_logits(w.seed, 0, 1, w.E)
+    ids_ref, _ = R.route(logits, w.K)
+    routed = sorted(set(ids_ref.ravel().tolist()))
+    say(f"format {fmt} decode: packing {len(routed)} experts")
+    slots, table, shared, stride = fmt_layer(fmt, w, place_seed=5, experts=routed, S=w.slots)
+    y_ref, _, _, _ = R.moe_layer(xb, {e: fmt_oracle_expert(fmt, w, 0, e) for e in routed}, w.K, logits=logits)
+    ids, wts, y, st, _ = fmt_run(fmt, w, slots, table, shared, stride, xb, logits)
+    assert int(st.item()) == 0
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    check_close(y_f64(y), y_ref, f"  format {fmt} decode full size")
+
+
+def test_fmt_status_and_argument_errors():
+    fmt = gen.FMT_INT8_G32
+    w = gen.Workload("fmt8_t3_h256_e8_k2_i96_err", 3, 256, 8, 2, 96, 1, 8, "normal", 78, shared=True)
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    logits = gen.normal_logits(w.seed, 0, w.T, w.E)
+    slots, table, shared, stride = fmt_layer(fmt, w)
+    ids, wts, y, st, (x, ws, nb) = fmt_run(fmt, w, slots, table, shared, stride, xb, logits)
+    assert int(st.item()) == 0
+    e0 = int(ids[0, 0].item())
+    table[e0] = -1
+    lib.moe_expert_ffn_fmt(fmt, x, ids, wts, w.T, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == lib.MOE_ENOTRES
+    st.zero_()
+    table[e0] = 0
+    ids[1, 1] = w.E
+    lib.moe_expert_ffn_fmt(fmt, x, ids, wts, w.T, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) in (lib.MOE_EINVAL, lib.MOE_ENOTRES)
+    args = (x, ids, wts, w.T, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb, st)
+    for bad_fmt, code in ((7, lib.MOE_EINVAL),):
+        with pytest.raises(lib.MoeError) as ex:
+            lib.moe_expert_ffn_fmt(bad_fmt, *args)
+        assert ex.value.status == code
+    with pytest.raises(lib.MoeError) as ex:  # 33 tokens: past the format path's T <= 32
+        lib.moe_expert_ffn_fmt(fmt, x, ids, wts, 33, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb, st)
+    assert ex.value.status == lib.MOE_EUNSUP
+    with pytest.raises(lib.MoeError) as ex:
+        lib.moe_expert_ffn_fmt(fmt, x, ids, wts, w.T, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb - 1, st)
+    assert ex.value.status == lib.MOE_EWS
+    with pytest.raises(lib.MoeError) as ex:
+        lib.moe_expert_ffn_fmt(fmt, x, ids, wts, w.T, w.H, w.I, w.E, w.K, table, slots, 100, shared, y, ws, nb, st)
+    assert ex.value.status == lib.MOE_EINVAL
+
+
+def test_fmt_int4_g32_is_moe_expert_ffn():
+    w = gen.Workload("fmt4g32_t5_h512_e16_k4_i256_shared", 5, 512, 16, 4, 256, 1, 16, "normal", 79, shared=True)
+    L = harness.make_layer(w, 0, DEV, place_seed=1)
+    run = harness.LayerRunner(w, DEV)
+    run.route(L)
+    run.ffn(L)
+    torch.cuda.synchronize()
+    y0 = run.y.view(torch.int16).clone()
+    lib.moe_expert_ffn_fmt(gen.FMT_INT4_G32, L.x, run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, L.table, L.slots,
+                           L.stride, L.shared, run.y, run.ws, run.ws_bytes, run.status)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    assert torch.equal(run.y.view(torch.int16), y0)
