@@ -36,8 +36,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=48)
-    p.add_argument("--legs", default="decode,prefill,batched,paged,route_variants,chunked",
-                   help="comma list of decode,prefill,batched,paged,route_variants,chunked")
+    p.add_argument("--legs", default="decode,prefill,batched,paged,route_variants,chunked,formats",
+                   help="comma list of decode,prefill,batched,paged,route_variants,chunked,formats")
     p.add_argument("--chunks", default="1024,2048,4096", help="prompt chunk sizes of the chunked paged prefill leg")
     p.add_argument("--paged-steps", type=int, default=64, help="measured tokens of the paged decode workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -606,6 +606,61 @@ def chunked_leg(a, dev):
     return w, out
 
 
+def formats_leg(dev, steps=192, n_blobs=64):
+    """Expert FFN of one token (H 4096, I 1536, 256 experts, top-8) per weight format:
+    int4 group 32 (the single-token path of moe_expert_ffn), int4 group 128 and int8
+    group 32 (moe_expert_ffn_fmt). 64 distinct experts are packed per format (the
+    table maps expert e to blob e % 64, more bytes than the 256 MB last-level cache);
+    every timed call routes to 8 other experts (seeded draws without replacement)."""
+    import numpy as np
+    import torch
+
+    from quantized_routed_expert_moe_amd import harness, lib
+    from synth import gen
+
+    H, I, E, K, seed = 4096, 1536, 256, 8, 7
+    rng = np.random.default_rng(seed)
+    ids_all = np.stack([rng.choice(E, size=K, replace=False) for _ in range(steps + 8)]).astype(np.int32)
+    ids_d = torch.from_numpy(ids_all).to(dev)
+    wts = torch.full((K,), 1.0 / K, dtype=torch.float32, device=dev)
+    x = harness.bf16_tensor(gen.activations_bf16(seed, 0, 1, H), dev)
+    y = torch.empty(1, H, dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    table = torch.from_numpy((np.arange(E) % n_blobs).astype(np.int32)).to(dev)
+    out = {}
+    for name, fmt in (("int4_g32", gen.FMT_INT4_G32), ("int4_g128", gen.FMT_INT4_G128), ("int8_g32", gen.FMT_INT8_G32)):
+        stride = lib.moe_fmt_slot_stride(fmt, H, I)
+        blob = lib.moe_fmt_blob_bytes(fmt, H, I)
+        slots = torch.empty(n_blobs * stride, dtype=torch.uint8, device=dev)
+        for b in range(n_blobs):
+            slots[b * stride : (b + 1) * stride].copy_(torch.from_numpy(harness.pack_expert_fmt(seed, 0, b, H, I, fmt)))
+        nb = lib.moe_fmt_workspace_bytes(fmt, 1, H, I, E, K, 0)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+        def call(i):
+            lib.moe_expert_ffn_fmt(fmt, x, ids_d[i], wts, 1, H, I, E, K, table, slots, stride, None, y, ws, nb, status)
+
+        for i in range(8):
+            call(steps + i)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for i in range(steps):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise RuntimeError(f"device status {int(status.item())}")
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out[name] = {"us_per_layer": round(us, 2), "blob_bytes": blob,
+                     "hbm_gbs": round(K * blob / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(K * blob / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"  formats {name}: {out[name]}")
+        del slots, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 
@@ -764,6 +819,9 @@ def main():
             "bit_identical_to_resident": q["identical"],
             "host_weight_sets": 1,
         }
+    if "formats" in legs:
+        out["workloads"]["formats"] = {"workload": "decode_t1_h4096_e256_k8_i1536 expert FFN per weight format",
+                                       "by_format": formats_leg(dev)}
     if "chunked" in legs:
         torch.cuda.empty_cache()
         wc, c = chunked_leg(a, dev)

@@ -200,14 +200,18 @@ int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T,
  *                     functions below return moe_blob_bytes / moe_slot_stride;
  *   MOE_FMT_INT4_G128 codes as for moe_pack_expert (uint8 [rows][cols/2],
  *                     two's-complement nibbles, even column in the low nibble),
- *                     fp16 scales [rows][cols/128]; H, I multiples of 128;
+ *                     fp16 scales [rows][cols/128]; H, I multiples of 128. Packed
+ *                     as a group-32 blob with each scale repeated for its four
+ *                     32-column groups (the same weights), so every path of
+ *                     moe_expert_ffn serves it (moe_expert_ffn_fmt calls it);
  *   MOE_FMT_INT8_G32  codes int8 [rows][cols] (two's complement, passed as
- *                     uint8), fp16 scales [rows][cols/32]; H, I multiples of 32.
- * For the two new formats T <= 32 and H, I <= 4096 (int8) / 8192 (int4);
- * larger shapes return MOE_EUNSUP (no fallback). Each (token, expert) pair
- * reads its expert's rows (one read per chosen expert for one token). x, and
- * the intermediate h, must fit fp16 (else MOE_EUNSUP in dev_status). The
- * layout of these blobs belongs to the library. */
+ *                     uint8), fp16 scales [rows][cols/32]; H, I multiples of 32
+ *                     and at most 4096; T <= 32 (else MOE_EUNSUP, no fallback).
+ *                     Each (token, expert) pair reads its expert's rows (one
+ *                     read per chosen expert for one token); x, and the
+ *                     intermediate h, must fit fp16 (else MOE_EUNSUP in
+ *                     dev_status).
+ * The layout of these blobs belongs to the library. */
 size_t moe_fmt_blob_bytes(int fmt, int H, int I);  /* 0 on an unsupported format or shape */
 size_t moe_fmt_slot_stride(int fmt, int H, int I); /* moe_fmt_blob_bytes rounded up to 4096 */
 int moe_pack_expert_fmt(int fmt, const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, const uint16_t* sg,

@@ -240,7 +240,10 @@ extern "C" int moe_ffn_combine(const float* w, int T, int H, int I, int E, int K
 }
 
 extern "C" size_t moe_fmt_workspace_bytes(int fmt, int T, int H, int I, int E, int K, int has_shared) {
-  if (fmt == MOE_FMT_INT4_G32) return moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, 0);
+  if (fmt == MOE_FMT_INT4_G32 || fmt == MOE_FMT_INT4_G128) {
+    if (fmt == MOE_FMT_INT4_G128 && moe_fmt_blob_bytes(fmt, H, I) == 0) return 0;
+    return moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, 0);
+  }
   if (T <= 0 || T > moe::kGemvMaxT || E <= 0 || K <= 0 || !moe::fmt_shape_ok(fmt, H, I)) return 0;
   return moe::fmt_workspace_bytes(T, H, I, K, has_shared);
 }
@@ -249,10 +252,11 @@ extern "C" int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids
                                   int E, int K, const int32_t* slot_table, const void* slots, size_t stride,
                                   const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
                                   int32_t* dev_status, moe_stream_t stream) {
-  if (fmt == MOE_FMT_INT4_G32)
+  if (fmt == MOE_FMT_INT4_G128 && T >= 0 && H > 0 && I > 0 && moe_fmt_blob_bytes(fmt, H, I) == 0) return MOE_EUNSUP;
+  if (fmt == MOE_FMT_INT4_G32 || fmt == MOE_FMT_INT4_G128)  // group 128 is packed as group 32 (repeated scales)
     return moe_expert_ffn(x, ids, w, T, H, I, E, K, moe::kGroup, slot_table, slots, stride, shared_blob, y, ws,
                           ws_bytes, dev_status, 0, stream);
-  if (fmt != MOE_FMT_INT4_G128 && fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;
+  if (fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
   if (!moe::fmt_shape_ok(fmt, H, I) || E > moe::kMaxE || K > moe::kMaxK || T > moe::kGemvMaxT) return MOE_EUNSUP;
   if (T == 0) return MOE_OK;

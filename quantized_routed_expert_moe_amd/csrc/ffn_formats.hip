@@ -1,24 +1,21 @@
-// Expert FFN for the other weight formats the "Strata" README names (Models:
-// INT8 group-32 linears; Kernels: INT4 group-128 and INT8 group-32 kernels; all
-// with 16-bit activations): the same layer as moe_expert_ffn,
+// Expert FFN for INT8 group-32 experts (the "Strata" README, Models: INT8
+// group-32 linears; Kernels: INT8 group-32 kernels; 16-bit activations): the
+// same layer as moe_expert_ffn,
 //   y[t] = shared(x[t]) + sum_k w[t][k] * FFN_{ids[t][k]}(x[t]),
-//   FFN(x) = Wd (silu(Wg x) * (Wu x)),  W[n][j] = q[n][j] * s[n][j / g],
-// with int8 (g = 32) or int4 (g = 128) codes and fp16 scales, for T <= 32.
+//   FFN(x) = Wd (silu(Wg x) * (Wu x)),  W[n][j] = q[n][j] * s[n][j / 32],
+// with int8 codes and fp16 scales, for T <= 32. (INT4 group-128 experts need no
+// kernel of their own: they are packed as group-32 blobs with repeated scales.)
 //
 // Blob (FmtLayout): gate codes [I] rows, up codes [I], down codes [H] rows, each
-// row contiguous, then the fp16 scales [rows][cols / g] of the three matrices.
-// A row is a run of 16-byte chunks: int8, 16 columns per chunk, offset binary
-// u = q + 128 in column order; int4, 32 columns per chunk, the nibble
-// interleave of the group-32 blob (offset binary u = q + 8), so that one mask
-// and one OR give fp16 pairs of consecutive columns.
+// row contiguous (16-byte chunks of 16 columns, offset binary u = q + 128 in
+// column order), then the fp16 scales [rows][cols / 32] of the three matrices.
 //
-// Dequantisation is exact and lives in the fp16 dot products: int8 pairs
-// (0x64 << 8 | u) = 1024 + u = q + 1152 come from one v_perm_b32 per two codes;
-// int4 pairs are q + 1032 or q + 72 (one AND-OR each). A chunk's v_dot2 sum
-// D = sum_c (q_c + off_c) x_c then gives sum_c q_c x_c = D - sum_c off_c x_c,
-// with the x sums per chunk staged once, and the chunk result is scaled by its
-// group's fp16 scale in fp32. x (and h for the down projection) are staged as
-// fp16 (a value past the fp16 range sets MOE_EUNSUP).
+// Dequantisation is exact and lives in the fp16 dot products: the pairs
+// (0x64 << 8 | u) = 1024 + u = q + 1152 come from one v_perm_b32 per two codes,
+// a chunk's v_dot2 sum D = sum_c (q_c + 1152) x_c gives sum_c q_c x_c = D - 1152
+// sum_c x_c with the x sums per chunk staged once, and the chunk result is
+// scaled by its group's fp16 scale in fp32. x (and h for the down projection)
+// are staged as fp16 (a value past the fp16 range sets MOE_EUNSUP).
 //
 // Work: one item per (token, expert) pair and row block, so an expert's bytes
 // are read once per token that uses it (the single-token decode reads each
@@ -42,11 +39,6 @@ template <>
 struct Fmt<MOE_FMT_INT8_G32> {
   static constexpr int kCols = 16;  // columns per 16-byte chunk
   static constexpr int kG = 32;
-};
-template <>
-struct Fmt<MOE_FMT_INT4_G128> {
-  static constexpr int kCols = 32;
-  static constexpr int kG = 128;
 };
 
 __host__ __device__ inline size_t fmt_al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -81,15 +73,14 @@ __device__ inline const uint8_t* fmt_pair_blob(const FfnArgs& a, int p) {
 }
 
 // Stage n activations (fp32 or bf16 source) as fp16 pairs into xs, and per chunk
-// the sum of its fp16 values times the code offsets: int8, 1152 * sum over the
-// chunk; int4, 1032 * (columns 8d + 0, 1, 4, 5) + 72 * (8d + 2, 3, 6, 7).
+// the sum of its fp16 values times the code offset 1152.
 template <int FMT, typename Src>
 __device__ inline void stage_act(const Src* src, int n, uint32_t* xs, float* corr, int32_t* status) {
   constexpr int C = Fmt<FMT>::kCols;
   const int n_chunks = n / C;
   bool bad = false;
   for (int c = threadIdx.x; c < n_chunks; c += kFThreads) {
-    float ca = 0.0f, cb = 0.0f;
+    float ca = 0.0f;
 #pragma unroll
     for (int j = 0; j < C; j += 2) {
       float v0, v1;
@@ -103,15 +94,9 @@ __device__ inline void stage_act(const Src* src, int n, uint32_t* xs, float* cor
       }
       const uint32_t h0 = to_f16_bits(v0, &bad), h1 = to_f16_bits(v1, &bad);
       xs[(c * C + j) / 2] = h0 | (h1 << 16);
-      const float s = f16_lo(h0) + f16_lo(h1);
-      // int4: the pair of columns j, j + 1 is an A pair (offset 1032) for j % 8 in
-      // {0, 4} and a B pair (offset 72) for j % 8 in {2, 6}
-      if (FMT == MOE_FMT_INT4_G128 && ((j >> 1) & 1))
-        cb += s;
-      else
-        ca += s;
+      ca += f16_lo(h0) + f16_lo(h1);
     }
-    corr[c] = FMT == MOE_FMT_INT8_G32 ? 1152.0f * ca : fmaf(1032.0f, ca, 72.0f * cb);
+    corr[c] = 1152.0f * ca;
   }
   if (bad) *status = MOE_EUNSUP;
 }
@@ -119,18 +104,14 @@ __device__ inline void stage_act(const Src* src, int n, uint32_t* xs, float* cor
 // D for one 16-byte chunk against its fp16 activation pairs xp[0 .. C/2).
 template <int FMT>
 __device__ inline float chunk_dot(const uint4& cw, const uint32_t* xp) {
+  static_assert(FMT == MOE_FMT_INT8_G32, "int8 codes only");
   const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
   float d = 0.0f;
-  if constexpr (FMT == MOE_FMT_INT8_G32) {
-    // bytes [b0, 0x64, b1, 0x64] and [b2, 0x64, b3, 0x64]: fp16 1024 + u of columns 4i .. 4i + 3
+  // bytes [b0, 0x64, b1, 0x64] and [b2, 0x64, b3, 0x64]: fp16 1024 + u of columns 4i .. 4i + 3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      d = dot2h(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04010400u), xp[2 * i], d);
-      d = dot2h(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04030402u), xp[2 * i + 1], d);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d = code_dot(w[i], xp[4 * i], xp[4 * i + 1], xp[4 * i + 2], xp[4 * i + 3], d);
+  for (int i = 0; i < 4; ++i) {
+    d = dot2h(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04010400u), xp[2 * i], d);
+    d = dot2h(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04030402u), xp[2 * i + 1], d);
   }
   return d;
 }
@@ -291,11 +272,9 @@ hipError_t launch_fmt(const FfnArgs& a, hipStream_t s) {
 }  // namespace
 
 bool fmt_shape_ok(int fmt, int H, int I) {
-  if (fmt != MOE_FMT_INT8_G32 && fmt != MOE_FMT_INT4_G128) return false;
-  const int C = fmt == MOE_FMT_INT8_G32 ? 16 : 32, g = fmt == MOE_FMT_INT8_G32 ? 32 : 128;
-  // at most 4 steps of 64 chunks per row, whole groups, whole row blocks
-  return H > 0 && I > 0 && H % g == 0 && I % g == 0 && H / C <= 256 && I / C <= 256 && H % kRowsPerItem == 0 &&
-         I % kRowsPerItem == 0;
+  if (fmt != MOE_FMT_INT8_G32) return false;
+  // at most 4 steps of 64 chunks of 16 columns per row, whole groups, whole row blocks
+  return H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0 && H <= 4096 && I <= 4096;
 }
 
 size_t fmt_workspace_bytes(int T, int H, int I, int K, int has_shared) {
@@ -304,7 +283,7 @@ size_t fmt_workspace_bytes(int T, int H, int I, int K, int has_shared) {
 
 hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
   if (!fmt_shape_ok(fmt, a.H, a.I)) return hipErrorNotSupported;
-  return fmt == MOE_FMT_INT8_G32 ? launch_fmt<MOE_FMT_INT8_G32>(a, s) : launch_fmt<MOE_FMT_INT4_G128>(a, s);
+  return launch_fmt<MOE_FMT_INT8_G32>(a, s);
 }
 
 }  // namespace moe

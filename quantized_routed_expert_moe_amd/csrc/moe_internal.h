@@ -46,16 +46,16 @@ __host__ __device__ inline BlobLayout blob_layout(int H, int I) {
   return L;
 }
 
-// Blob of the other formats (moe_pack_expert_fmt; the kernels in
+// Blob of the int8 group-32 format (moe_pack_expert_fmt; the kernels in
 // ffn_formats.hip): per matrix the rows one after another, a row being its
-// 16-byte code chunks in column order (int8: 16 columns per chunk, offset binary
-// u = q + 128; int4: 32 columns, the nibble interleave of the group-32 blob),
-// then the fp16 scales [rows][cols / g]; every region starts on 256 bytes.
+// int8 codes in column order (offset binary u = q + 128), then the fp16 scales
+// [rows][cols / 32]; every region starts on 256 bytes.
 struct FmtLayout {
   size_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales, bytes;
 };
 __host__ __device__ inline FmtLayout fmt_layout(int fmt, int H, int I) {
-  const int bits = fmt == MOE_FMT_INT8_G32 ? 8 : 4, g = fmt == MOE_FMT_INT8_G32 ? 32 : 128;
+  (void)fmt;  // MOE_FMT_INT8_G32
+  const int bits = 8, g = 32;
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   const size_t gu_codes = (size_t)I * H * bits / 8, dn_codes = (size_t)H * I * bits / 8;
   const size_t gu_scales = (size_t)I * (H / g) * 2, dn_scales = (size_t)H * (I / g) * 2;

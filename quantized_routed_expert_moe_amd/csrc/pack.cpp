@@ -10,6 +10,8 @@
 // layout is documented in moe_internal.h.
 #include <string.h>
 
+#include <vector>
+
 #include "moe_internal.h"
 
 namespace {
@@ -72,26 +74,28 @@ namespace {
 
 // one matrix of N rows and C columns into the row-major layout of the formats
 // blob (moe_internal.h, FmtLayout)
-void pack_matrix_fmt(int fmt, const uint8_t* q, const uint16_t* s, int N, int C, uint8_t* codes, uint16_t* scales) {
-  const int g = fmt == MOE_FMT_INT8_G32 ? 32 : 128;
-  if (fmt == MOE_FMT_INT8_G32) {
-    for (size_t i = 0; i < (size_t)N * C; ++i) codes[i] = (uint8_t)(q[i] ^ 0x80u);  // two's complement -> q + 128
-  } else {
-    const size_t chunks = (size_t)N * C / 32;  // 16 bytes = 32 columns each, rows back to back
-    for (size_t k = 0; k < chunks; ++k) {
-      uint32_t src[4], dst[4];
-      memcpy(src, q + k * 16, 16);
-      for (int d = 0; d < 4; ++d) dst[d] = interleave_dword(src[d]);
-      memcpy(codes + k * 16, dst, 16);
-    }
-  }
-  memcpy(scales, s, (size_t)N * (C / g) * 2);
+// int8 matrix of N rows and C columns into the row-major layout of the int8 blob
+// (moe_internal.h, FmtLayout)
+void pack_matrix_int8(const uint8_t* q, const uint16_t* s, int N, int C, uint8_t* codes, uint16_t* scales) {
+  for (size_t i = 0; i < (size_t)N * C; ++i) codes[i] = (uint8_t)(q[i] ^ 0x80u);  // two's complement -> q + 128
+  memcpy(scales, s, (size_t)N * (C / 32) * 2);
 }
+
+// group-128 scales [N][C/128] -> group-32 scales [N][C/32], each repeated for the
+// four 32-column groups it covers (the same W[n][j] = q[n][j] * s[n][j / 128])
+std::vector<uint16_t> repeat_scales(const uint16_t* s, int N, int C) {
+  std::vector<uint16_t> out((size_t)N * (C / 32));
+  for (size_t i = 0; i < out.size(); ++i) out[i] = s[i / 4];
+  return out;
+}
+
+bool g128_shape_ok(int H, int I) { return H % 128 == 0 && I % 128 == 0 && moe::shape_ok(H, I, moe::kGroup); }
 
 }  // namespace
 
 extern "C" size_t moe_fmt_blob_bytes(int fmt, int H, int I) {
   if (fmt == MOE_FMT_INT4_G32) return moe_blob_bytes(H, I, moe::kGroup);
+  if (fmt == MOE_FMT_INT4_G128) return g128_shape_ok(H, I) ? moe_blob_bytes(H, I, moe::kGroup) : 0;
   if (!moe::fmt_shape_ok(fmt, H, I)) return 0;
   return moe::fmt_layout(fmt, H, I).bytes;
 }
@@ -107,12 +111,17 @@ extern "C" int moe_pack_expert_fmt(int fmt, const uint8_t* qg, const uint8_t* qu
   if (fmt == MOE_FMT_INT4_G32) return moe_pack_expert(qg, qu, qd, sg, su, sd, H, I, moe::kGroup, blob_out);
   if (fmt != MOE_FMT_INT4_G128 && fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;
   if (!qg || !qu || !qd || !sg || !su || !sd || !blob_out) return MOE_EINVAL;
+  if (fmt == MOE_FMT_INT4_G128) {  // the group-32 blob with repeated scales
+    if (!g128_shape_ok(H, I)) return MOE_EUNSUP;
+    const std::vector<uint16_t> g = repeat_scales(sg, I, H), u = repeat_scales(su, I, H), d = repeat_scales(sd, H, I);
+    return moe_pack_expert(qg, qu, qd, g.data(), u.data(), d.data(), H, I, moe::kGroup, blob_out);
+  }
   if (!moe::fmt_shape_ok(fmt, H, I)) return MOE_EUNSUP;
   const moe::FmtLayout L = moe::fmt_layout(fmt, H, I);
   uint8_t* b = static_cast<uint8_t*>(blob_out);
   memset(b, 0, L.bytes);  // padding between regions
-  pack_matrix_fmt(fmt, qg, sg, I, H, b + L.gate_codes, reinterpret_cast<uint16_t*>(b + L.gate_scales));
-  pack_matrix_fmt(fmt, qu, su, I, H, b + L.up_codes, reinterpret_cast<uint16_t*>(b + L.up_scales));
-  pack_matrix_fmt(fmt, qd, sd, H, I, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
+  pack_matrix_int8(qg, sg, I, H, b + L.gate_codes, reinterpret_cast<uint16_t*>(b + L.gate_scales));
+  pack_matrix_int8(qu, su, I, H, b + L.up_codes, reinterpret_cast<uint16_t*>(b + L.up_scales));
+  pack_matrix_int8(qd, sd, H, I, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
   return MOE_OK;
 }

@@ -169,10 +169,25 @@ def al256(v):
     return (v + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("fmt,H,I", [(gen.FMT_INT8_G32, 256, 96), (gen.FMT_INT8_G32, 4096, 1536),
-                                     (gen.FMT_INT4_G128, 512, 256), (gen.FMT_INT4_G128, 4096, 1536)])
+@pytest.mark.parametrize("H,I", [(512, 256), (4096, 1536)])
+def test_fmt_int4_g128_is_the_g32_blob_with_repeated_scales(H, I):
+    t = gen.expert_tensors_fmt(9, 0, 3, H, I, gen.FMT_INT4_G128)
+    assert lib.moe_fmt_blob_bytes(gen.FMT_INT4_G128, H, I) == lib.moe_blob_bytes(H, I, 32)
+    blob = np.zeros(lib.moe_fmt_slot_stride(gen.FMT_INT4_G128, H, I), dtype=np.uint8)
+    lib.moe_pack_expert_fmt(gen.FMT_INT4_G128, t["qg"], t["qu"], t["qd"], t["sg"].view(np.uint16),
+                            t["su"].view(np.uint16), t["sd"].view(np.uint16), H, I, blob)
+    mc, ms = H * I // 2, H * I // 16
+    offs = [(0, 3 * mc, I, H, 8, "qg", "sg"), (mc, 3 * mc + ms, I, H, 8, "qu", "su"),
+            (2 * mc, 3 * mc + 2 * ms, H, I, 4, "qd", "sd")]
+    for oc, os_, N, C, R, qk, sk in offs:
+        q, s = decode_blob_matrix(blob.tobytes(), oc, os_, N, C, R)
+        assert np.array_equal(q, unpack_plain(t[qk], C))
+        assert np.array_equal(s.view(np.uint16), np.repeat(t[sk].view(np.uint16), 4, axis=1))
+
+
+@pytest.mark.parametrize("fmt,H,I", [(gen.FMT_INT8_G32, 256, 96), (gen.FMT_INT8_G32, 4096, 1536)])
 def test_fmt_pack_layout_roundtrip(fmt, H, I):
-    """The format blobs decode back to the interchange codes and scales (an independent
+    """The int8 blobs decode back to the interchange codes and scales (an independent
     reader of the documented row-major layout)."""
     bits, g = gen.FMT_BITS_G[fmt]
     t = gen.expert_tensors_fmt(9, 0, 3, H, I, fmt)
@@ -190,18 +205,8 @@ def test_fmt_pack_layout_roundtrip(fmt, H, I):
     mats = [("qg", "sg", I, H, offs[0], offs[3]), ("qu", "su", I, H, offs[1], offs[4]),
             ("qd", "sd", H, I, offs[2], offs[5])]
     for qk, sk, N, C, oc, os_ in mats:
-        if bits == 8:
-            u = blob[oc : oc + N * C].reshape(N, C).astype(np.int64)
-            assert np.array_equal(u - 128, t[qk].view(np.int8).astype(np.int64))
-        else:
-            # rows back to back, 16-byte chunks of 32 columns, the group-32 blob's nibble interleave
-            w = np.frombuffer(blob.tobytes(), dtype=np.uint32, count=N * C // 8, offset=oc).reshape(N, C // 32, 4)
-            q = np.empty((N, C), dtype=np.int64)
-            for d in range(4):
-                for i in range(8):
-                    col = 8 * d + (2 * i if i < 4 else 2 * (i - 4) + 1)
-                    q[:, col::32] = ((w[:, :, d] >> (4 * i)) & 0xF).astype(np.int64) - 8
-            assert np.array_equal(q, unpack_plain(t[qk], C))
+        u = blob[oc : oc + N * C].reshape(N, C).astype(np.int64)
+        assert np.array_equal(u - 128, t[qk].view(np.int8).astype(np.int64))
         s = np.frombuffer(blob.tobytes(), dtype=np.uint16, count=N * (C // g), offset=os_).reshape(N, C // g)
         assert np.array_equal(s, t[sk].view(np.uint16))
 

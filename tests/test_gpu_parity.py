@@ -712,12 +712,15 @@ def fmt_run(fmt, w, slots, table, shared, stride, xb, logits):
                                          74, shared=True)),
         (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t9_h1024_e8_k3_i384", 9, 1024, 8, 3, 384, 1, 8, "normal", 75)),
         (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t32_h2048_e32_k8_i768", 32, 2048, 32, 8, 768, 1, 32, "zipf", 76)),
+        (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t77_h1024_e16_k4_i256_shared", 77, 1024, 16, 4, 256, 1, 16,
+                                         "normal", 80, shared=True)),
     ],
     ids=lambda v: v.name if hasattr(v, "name") else f"fmt{v}",
 )
 def test_fmt_matches_oracle(fmt, w):
-    """INT8 group-32 and INT4 group-128 experts: ids bit-exact, y within the oracle's bar,
-    the same bits on a second run and under a permuted slot map."""
+    """INT8 group-32 and INT4 group-128 experts (the latter on every path of moe_expert_ffn,
+    77 tokens on the grouped one): ids bit-exact, y within the oracle's bar, the same bits
+    on a second run and under a permuted slot map."""
     say(f"format {fmt} {w.name}")
     xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
     logits = {"normal": gen.normal_logits, "zipf": gen.zipf_logits}[w.router](w.seed, 0, w.T, w.E)
