@@ -70,7 +70,8 @@ enum moe_score {
 enum moe_format {
   MOE_FMT_INT4_G32 = 0,  /* int4, one fp16 scale per 32 columns: the blob of moe_pack_expert */
   MOE_FMT_INT4_G128 = 1, /* int4, one fp16 scale per 128 columns */
-  MOE_FMT_INT8_G32 = 2   /* int8, one fp16 scale per 32 columns */
+  MOE_FMT_INT8_G32 = 2,  /* int8, one fp16 scale per 32 columns */
+  MOE_FMT_NVFP4 = 3      /* E2M1, one E4M3 scale per 16 columns, one fp32 scale per matrix */
 };
 
 enum moe_flags {
@@ -211,11 +212,23 @@ int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T,
  *                     read per chosen expert for one token); x, and the
  *                     intermediate h, must fit fp16 (else MOE_EUNSUP in
  *                     dev_status).
+ *   MOE_FMT_NVFP4     ("Strata" README, Models: E2M1 pairs, group-16 E4M3
+ *                     scales, FP32 per-tensor global scale): W[n][j] =
+ *                     e2m1(c[n][j]) * e4m3(s[n][j / 16]) * global; packed with
+ *                     moe_pack_expert_nvfp4; H, I multiples of 32 and at most
+ *                     8192; T <= 32; otherwise as MOE_FMT_INT8_G32.
  * The layout of these blobs belongs to the library. */
 size_t moe_fmt_blob_bytes(int fmt, int H, int I);  /* 0 on an unsupported format or shape */
 size_t moe_fmt_slot_stride(int fmt, int H, int I); /* moe_fmt_blob_bytes rounded up to 4096 */
 int moe_pack_expert_fmt(int fmt, const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, const uint16_t* sg,
                         const uint16_t* su, const uint16_t* sd, int H, int I, void* blob_out);
+/* NVFP4 expert (all pointers host memory): qg, qu uint8 [I][H/2], qd [H][I/2],
+ * two E2M1 codes per byte (1 sign, 2 exponent bits with bias 1, 1 mantissa
+ * bit; the even column in the low nibble); sg, su uint8 [I][H/16], sd
+ * [H][I/16], E4M3 scales (bias 7, no infinities; the NaN pattern is rejected
+ * with MOE_EINVAL); global3 = the fp32 global scales of gate, up, down. */
+int moe_pack_expert_nvfp4(const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, const uint8_t* sg,
+                          const uint8_t* su, const uint8_t* sd, const float* global3, int H, int I, void* blob_out);
 size_t moe_fmt_workspace_bytes(int fmt, int T, int H, int I, int E, int K, int has_shared);
 int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E,
                        int K, const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,

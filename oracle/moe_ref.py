@@ -95,6 +95,41 @@ def dequantize_int8(codes: np.ndarray, scales: np.ndarray, cols: int, g: int = 3
     return q * np.repeat(s, g, axis=-1)
 
 
+def decode_e2m1(nibbles: np.ndarray) -> np.ndarray:
+    """E2M1 (FP4) codes 0..15 to float64: 1 sign bit, 2 exponent bits (bias 1),
+    1 mantissa bit; exponent 0 is subnormal (0 or 0.5). The NVFP4 experts of the
+    "Strata" README (Models) hold E2M1 pairs."""
+    c = np.asarray(nibbles, dtype=np.int64)
+    e, m = (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(c & 8, -mag, mag)
+
+
+def decode_e4m3(b: np.ndarray) -> np.ndarray:
+    """E4M3 (FP8) bytes to float64: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 is subnormal (m * 2^-9); no infinities, S.1111.111 is NaN."""
+    v = np.asarray(b, dtype=np.int64)
+    e, m = (v >> 3) & 15, v & 7
+    mag = np.where(e == 0, m * 2.0**-9, np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(v & 0x80, -mag, mag)
+
+
+def dequantize_nvfp4(packed: np.ndarray, scales: np.ndarray, global_scale: float, cols: int) -> np.ndarray:
+    """W[n, j] = e2m1(c[n, j]) * e4m3(s[n, j // 16]) * global in float64; codes two per
+    byte, the even column in the low nibble (group 16, as the README gives NVFP4)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    if p.shape[-1] * 2 != cols:
+        raise ValueError("packed row length does not match cols")
+    c = np.empty(p.shape[:-1] + (cols,), dtype=np.int64)
+    c[..., 0::2] = p & 0x0F
+    c[..., 1::2] = p >> 4
+    s = decode_e4m3(scales)
+    if s.shape[-1] * 16 != cols:
+        raise ValueError("scale count does not match cols / 16")
+    return decode_e2m1(c) * np.repeat(s, 16, axis=-1) * float(global_scale)
+
+
 # ---------------------------------------------------------------- router
 
 
@@ -267,14 +302,21 @@ class Expert:
     """One expert held as fp64 matrices: gate [I, H], up [I, H], down [H, I].
 
     bits = 4: packed int4 codes (group g = 32 or 128); bits = 8: int8 codes
-    (group 32). W[n, j] = q[n, j] * s[n, j // g] either way."""
+    (group 32). W[n, j] = q[n, j] * s[n, j // g] either way. With a "global" entry
+    the tensors are NVFP4 (dequantize_nvfp4)."""
 
     def __init__(self, tensors: dict, H: int, I: int, g: int = 32, bits: int = 4):
         self.H, self.I = H, I
-        deq = dequantize if bits == 4 else dequantize_int8
-        self.Wg = deq(tensors["qg"], tensors["sg"], H, g)
-        self.Wu = deq(tensors["qu"], tensors["su"], H, g)
-        self.Wd = deq(tensors["qd"], tensors["sd"], I, g)
+        if "global" in tensors:  # NVFP4: E2M1 codes, E4M3 scales, fp32 global scales
+            gl = tensors["global"]
+            self.Wg = dequantize_nvfp4(tensors["qg"], tensors["sg"], gl[0], H)
+            self.Wu = dequantize_nvfp4(tensors["qu"], tensors["su"], gl[1], H)
+            self.Wd = dequantize_nvfp4(tensors["qd"], tensors["sd"], gl[2], I)
+        else:
+            deq = dequantize if bits == 4 else dequantize_int8
+            self.Wg = deq(tensors["qg"], tensors["sg"], H, g)
+            self.Wu = deq(tensors["qu"], tensors["su"], H, g)
+            self.Wd = deq(tensors["qd"], tensors["sd"], I, g)
         if self.Wg.shape != (I, H) or self.Wu.shape != (I, H) or self.Wd.shape != (H, I):
             raise ValueError("expert tensor shapes do not match (H, I)")
 

@@ -256,7 +256,7 @@ extern "C" int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids
   if (fmt == MOE_FMT_INT4_G32 || fmt == MOE_FMT_INT4_G128)  // group 128 is packed as group 32 (repeated scales)
     return moe_expert_ffn(x, ids, w, T, H, I, E, K, moe::kGroup, slot_table, slots, stride, shared_blob, y, ws,
                           ws_bytes, dev_status, 0, stream);
-  if (fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;
+  if (fmt != MOE_FMT_INT8_G32 && fmt != MOE_FMT_NVFP4) return MOE_EINVAL;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
   if (!moe::fmt_shape_ok(fmt, H, I) || E > moe::kMaxE || K > moe::kMaxK || T > moe::kGemvMaxT) return MOE_EUNSUP;
   if (T == 0) return MOE_OK;

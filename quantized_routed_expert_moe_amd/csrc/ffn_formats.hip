@@ -1,21 +1,31 @@
-// Expert FFN for INT8 group-32 experts (the "Strata" README, Models: INT8
-// group-32 linears; Kernels: INT8 group-32 kernels; 16-bit activations): the
-// same layer as moe_expert_ffn,
+// Expert FFN for the INT8 group-32 and NVFP4 experts of the "Strata" README
+// (Models: INT8 group-32 linears; NVFP4 experts, E2M1 pairs with group-16 E4M3
+// scales and an FP32 per-tensor global scale; both with 16-bit activations):
+// the same layer as moe_expert_ffn,
 //   y[t] = shared(x[t]) + sum_k w[t][k] * FFN_{ids[t][k]}(x[t]),
-//   FFN(x) = Wd (silu(Wg x) * (Wu x)),  W[n][j] = q[n][j] * s[n][j / 32],
-// with int8 codes and fp16 scales, for T <= 32. (INT4 group-128 experts need no
-// kernel of their own: they are packed as group-32 blobs with repeated scales.)
+//   FFN(x) = Wd (silu(Wg x) * (Wu x)),
+//   int8:  W[n][j] = q[n][j] * s[n][j / 32]      (fp16 s),
+//   NVFP4: W[n][j] = e2m1(c[n][j]) * e4m3(s[n][j / 16]) * global,
+// for T <= 32. (INT4 group-128 experts need no kernel of their own: they are
+// packed as group-32 blobs with repeated scales.)
 //
 // Blob (FmtLayout): gate codes [I] rows, up codes [I], down codes [H] rows, each
-// row contiguous (16-byte chunks of 16 columns, offset binary u = q + 128 in
-// column order), then the fp16 scales [rows][cols / 32] of the three matrices.
+// row contiguous, then the scales [rows][cols / g] of the three matrices (and
+// for NVFP4 the three fp32 global scales). int8 rows are 16-byte chunks of 16
+// columns (offset binary u = q + 128, column order); NVFP4 rows are 16-byte
+// chunks of 32 columns (two E2M1 codes per byte, the even column in the low
+// nibble, as delivered).
 //
-// Dequantisation is exact and lives in the fp16 dot products: the pairs
+// Dequantisation is exact and lives in the fp16 dot products. int8: the pairs
 // (0x64 << 8 | u) = 1024 + u = q + 1152 come from one v_perm_b32 per two codes,
-// a chunk's v_dot2 sum D = sum_c (q_c + 1152) x_c gives sum_c q_c x_c = D - 1152
-// sum_c x_c with the x sums per chunk staged once, and the chunk result is
-// scaled by its group's fp16 scale in fp32. x (and h for the down projection)
-// are staged as fp16 (a value past the fp16 range sets MOE_EUNSUP).
+// and sum_c q_c x_c = D - 1152 sum_c x_c with the x sums per chunk staged once.
+// NVFP4: the fp16 value of an E2M1 magnitude has a zero low byte, so one v_perm
+// over an 8-byte table gives four high bytes, one v_perm per pair places two of
+// them, and one v_perm plus one AND-OR adds the two sign bits; the E2M1 values
+// are exact in fp16. Each group's dot product is scaled in fp32 by its scale
+// (fp16, or E4M3 decoded exactly), and an NVFP4 row by its global scale. x (and
+// h for the down projection) are staged as fp16 (a value past the fp16 range
+// sets MOE_EUNSUP).
 //
 // Work: one item per (token, expert) pair and row block, so an expert's bytes
 // are read once per token that uses it (the single-token decode reads each
@@ -38,8 +48,21 @@ struct Fmt;
 template <>
 struct Fmt<MOE_FMT_INT8_G32> {
   static constexpr int kCols = 16;  // columns per 16-byte chunk
-  static constexpr int kG = 32;
+  static constexpr int kG = 32;     // columns per scale
 };
+template <>
+struct Fmt<MOE_FMT_NVFP4> {
+  static constexpr int kCols = 32;
+  static constexpr int kG = 16;
+};
+
+// E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities,
+// S.1111.111 is NaN and never stored) to fp32, exactly.
+__device__ inline float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;  // 2^-9 m
+  return (b & 0x80u) ? -mag : mag;
+}
 
 __host__ __device__ inline size_t fmt_al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -96,15 +119,39 @@ __device__ inline void stage_act(const Src* src, int n, uint32_t* xs, float* cor
       xs[(c * C + j) / 2] = h0 | (h1 << 16);
       ca += f16_lo(h0) + f16_lo(h1);
     }
-    corr[c] = 1152.0f * ca;
+    corr[c] = FMT == MOE_FMT_INT8_G32 ? 1152.0f * ca : 0.0f;
   }
   if (bad) *status = MOE_EUNSUP;
+}
+
+// NVFP4: the two groups' sums (columns 0..15 and 16..31 of the chunk).
+__device__ inline void chunk_dot_nvfp4(const uint4& cw, const uint32_t* xp, float& d0, float& d1) {
+  // fp16 high bytes of the E2M1 magnitudes 0, 0.5, 1, 1.5 | 2, 3, 4, 6
+  const uint32_t lut_lo = 0x3E3C3800u, lut_hi = 0x46444240u;
+  const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+  float d[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // dword i: columns 8i .. 8i + 7
+    const uint32_t e = __builtin_amdgcn_perm(lut_hi, lut_lo, w[i] & 0x07070707u);         // cols 8i + 0, 2, 4, 6
+    const uint32_t o = __builtin_amdgcn_perm(lut_hi, lut_lo, (w[i] >> 4) & 0x07070707u);  // cols 8i + 1, 3, 5, 7
+    const uint32_t w4 = w[i] << 4;  // even columns' sign bits at the top of their bytes
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // pair k: columns 8i + 2k, 8i + 2k + 1
+      // bytes [0, e_k, 0, o_k]: fp16 magnitudes of the two columns
+      const uint32_t mag = __builtin_amdgcn_perm(o, e, 0x000C000Cu | ((4u + k) << 24) | ((uint32_t)k << 8));
+      // bytes [-, byte k of w4, -, byte k of w]: the sign bits land on bits 15 and 31
+      const uint32_t sgn = __builtin_amdgcn_perm(w[i], w4, ((4u + k) << 24) | ((uint32_t)k << 8));
+      d[i >> 1] = dot2h((sgn & 0x80008000u) | mag, xp[4 * i + k], d[i >> 1]);
+    }
+  }
+  d0 = d[0];
+  d1 = d[1];
 }
 
 // D for one 16-byte chunk against its fp16 activation pairs xp[0 .. C/2).
 template <int FMT>
 __device__ inline float chunk_dot(const uint4& cw, const uint32_t* xp) {
-  static_assert(FMT == MOE_FMT_INT8_G32, "int8 codes only");
+  static_assert(FMT == MOE_FMT_INT8_G32, "int8 codes here");
   const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
   float d = 0.0f;
   // bytes [b0, 0x64, b1, 0x64] and [b2, 0x64, b3, 0x64]: fp16 1024 + u of columns 4i .. 4i + 3
@@ -124,13 +171,14 @@ __host__ __device__ inline size_t row_bytes(int cols) {
 // One wave: S row streams (codes rows, scale rows) over cols columns against the
 // staged activations; lane l takes chunks l, l + 64, ...; returns the full dot
 // products on every lane.
+// (scales: fp16 [cols / 32] per row for int8, E4M3 bytes [cols / 16] for NVFP4)
 template <int FMT, int S, int STEPS>
-__device__ inline void rows_dot(const uint8_t* const (&codes)[S], const _Float16* const (&scales)[S], int cols,
+__device__ inline void rows_dot(const uint8_t* const (&codes)[S], const uint8_t* const (&scales)[S], int cols,
                                 const uint32_t* xs, const float* corr, float scale_mask, int lane, float (&out)[S]) {
   constexpr int C = Fmt<FMT>::kCols;
   const int n_chunks = cols / C;
   uint4 cw[S][STEPS];
-  float sc[S][STEPS];
+  uint32_t sr[S][STEPS];  // int8: the fp16 scale; NVFP4: the chunk's two E4M3 scales
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -138,7 +186,10 @@ __device__ inline void rows_dot(const uint8_t* const (&codes)[S], const _Float16
       int c = i * 64 + lane;
       c = c < n_chunks ? c : n_chunks - 1;  // a real chunk, scaled by 0 below
       cw[s][i] = *reinterpret_cast<const uint4*>(codes[s] + (size_t)c * 16);
-      sc[s][i] = (float)scales[s][(size_t)c * C / Fmt<FMT>::kG];
+      if (FMT == MOE_FMT_INT8_G32)
+        sr[s][i] = reinterpret_cast<const uint16_t*>(scales[s])[(size_t)c * C / Fmt<FMT>::kG];
+      else
+        sr[s][i] = reinterpret_cast<const uint16_t*>(scales[s])[c];  // groups 2c, 2c + 1
     }
 #pragma unroll
   for (int s = 0; s < S; ++s) out[s] = 0.0f;
@@ -151,7 +202,17 @@ __device__ inline void rows_dot(const uint8_t* const (&codes)[S], const _Float16
     const float k = live ? scale_mask : 0.0f;
     const float cr = corr[cc];
 #pragma unroll
-    for (int s = 0; s < S; ++s) out[s] = fmaf(sc[s][i] * k, chunk_dot<FMT>(cw[s][i], xp) - cr, out[s]);
+    for (int s = 0; s < S; ++s) {
+      if constexpr (FMT == MOE_FMT_INT8_G32) {
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[s][i]);
+        out[s] = fmaf(sc * k, chunk_dot<FMT>(cw[s][i], xp) - cr, out[s]);
+      } else {
+        float d0, d1;
+        chunk_dot_nvfp4(cw[s][i], xp, d0, d1);
+        out[s] = fmaf(e4m3_to_f32(sr[s][i] & 0xFFu) * k, d0, out[s]);
+        out[s] = fmaf(e4m3_to_f32(sr[s][i] >> 8) * k, d1, out[s]);
+      }
+    }
   }
 #pragma unroll
   for (int s = 0; s < S; ++s) out[s] = wave_sum_f32(out[s]);
@@ -174,15 +235,21 @@ __global__ void __launch_bounds__(kFThreads) fmt_gateup_kernel(FfnArgs a) {
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const int n0 = rb * kRowsPerItem + 2 * wave;
   const size_t rbytes = row_bytes<FMT>(H);
-  const int gs = H / Fmt<FMT>::kG;
+  const size_t sbytes = (size_t)H / Fmt<FMT>::kG * (FMT == MOE_FMT_INT8_G32 ? 2 : 1);  // scale bytes per row
   const uint8_t* const codes[4] = {src + L.gate_codes + n0 * rbytes, src + L.gate_codes + (n0 + 1) * rbytes,
                                    src + L.up_codes + n0 * rbytes, src + L.up_codes + (n0 + 1) * rbytes};
-  const _Float16* gsc = reinterpret_cast<const _Float16*>(src + L.gate_scales);
-  const _Float16* usc = reinterpret_cast<const _Float16*>(src + L.up_scales);
-  const _Float16* const scales[4] = {gsc + (size_t)n0 * gs, gsc + (size_t)(n0 + 1) * gs, usc + (size_t)n0 * gs,
-                                     usc + (size_t)(n0 + 1) * gs};
+  const uint8_t* const scales[4] = {src + L.gate_scales + n0 * sbytes, src + L.gate_scales + (n0 + 1) * sbytes,
+                                    src + L.up_scales + n0 * sbytes, src + L.up_scales + (n0 + 1) * sbytes};
   float r[4];
   rows_dot<FMT, 4, STEPS>(codes, scales, H, xs, corr, blob ? 1.0f : 0.0f, lane, r);
+  if (FMT == MOE_FMT_NVFP4) {  // per-tensor global scales of gate and up
+    const float* gl = reinterpret_cast<const float*>(src + L.globals);
+    const float gg = gl[0], gu = gl[1];
+    r[0] *= gg;
+    r[1] *= gg;
+    r[2] *= gu;
+    r[3] *= gu;
+  }
   if (lane < 2) {
     const float g = lane ? r[1] : r[0], u = lane ? r[3] : r[2];
     reinterpret_cast<float*>(a.ws)[(size_t)p * I + n0 + lane] = silu(g) * u;
@@ -207,12 +274,16 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
   const uint8_t* src = blob ? blob : a.slots;
   const int n0 = rb * kRowsPerItem + 2 * wave;
   const size_t rbytes = row_bytes<FMT>(I);
-  const int gs = I / Fmt<FMT>::kG;
+  const size_t sbytes = (size_t)I / Fmt<FMT>::kG * (FMT == MOE_FMT_INT8_G32 ? 2 : 1);
   const uint8_t* const codes[2] = {src + L.down_codes + n0 * rbytes, src + L.down_codes + (n0 + 1) * rbytes};
-  const _Float16* dsc = reinterpret_cast<const _Float16*>(src + L.down_scales);
-  const _Float16* const scales[2] = {dsc + (size_t)n0 * gs, dsc + (size_t)(n0 + 1) * gs};
+  const uint8_t* const scales[2] = {src + L.down_scales + n0 * sbytes, src + L.down_scales + (n0 + 1) * sbytes};
   float r[2];
   rows_dot<FMT, 2, STEPS>(codes, scales, I, hs, corr, blob ? 1.0f : 0.0f, lane, r);
+  if (FMT == MOE_FMT_NVFP4) {
+    const float gd = reinterpret_cast<const float*>(src + L.globals)[2];
+    r[0] *= gd;
+    r[1] *= gd;
+  }
   if (lane < 2) reinterpret_cast<float*>(a.ws + W.o)[(size_t)p * H + n0 + lane] = lane ? r[1] : r[0];
 }
 
@@ -272,9 +343,11 @@ hipError_t launch_fmt(const FfnArgs& a, hipStream_t s) {
 }  // namespace
 
 bool fmt_shape_ok(int fmt, int H, int I) {
-  if (fmt != MOE_FMT_INT8_G32) return false;
-  // at most 4 steps of 64 chunks of 16 columns per row, whole groups, whole row blocks
-  return H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0 && H <= 4096 && I <= 4096;
+  // at most 4 steps of 64 chunks per row (16 columns per chunk for int8, 32 for
+  // NVFP4), whole chunks and groups, whole row blocks
+  if (fmt == MOE_FMT_INT8_G32) return H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0 && H <= 4096 && I <= 4096;
+  if (fmt == MOE_FMT_NVFP4) return H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0 && H <= 8192 && I <= 8192;
+  return false;
 }
 
 size_t fmt_workspace_bytes(int T, int H, int I, int K, int has_shared) {
@@ -283,7 +356,7 @@ size_t fmt_workspace_bytes(int T, int H, int I, int K, int has_shared) {
 
 hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
   if (!fmt_shape_ok(fmt, a.H, a.I)) return hipErrorNotSupported;
-  return launch_fmt<MOE_FMT_INT8_G32>(a, s);
+  return fmt == MOE_FMT_INT8_G32 ? launch_fmt<MOE_FMT_INT8_G32>(a, s) : launch_fmt<MOE_FMT_NVFP4>(a, s);
 }
 
 }  // namespace moe

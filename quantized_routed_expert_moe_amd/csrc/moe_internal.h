@@ -46,19 +46,22 @@ __host__ __device__ inline BlobLayout blob_layout(int H, int I) {
   return L;
 }
 
-// Blob of the int8 group-32 format (moe_pack_expert_fmt; the kernels in
-// ffn_formats.hip): per matrix the rows one after another, a row being its
-// int8 codes in column order (offset binary u = q + 128), then the fp16 scales
-// [rows][cols / 32]; every region starts on 256 bytes.
+// Blob of the int8 group-32 and NVFP4 formats (moe_pack_expert_fmt,
+// moe_pack_expert_nvfp4; the kernels in ffn_formats.hip): per matrix the rows
+// one after another (int8 codes in column order, offset binary u = q + 128;
+// NVFP4: two E2M1 codes per byte, the even column in the low nibble), then the
+// scales [rows][cols / g] (int8: fp16, g = 32; NVFP4: E4M3 bytes, g = 16), then
+// (NVFP4) the fp32 global scales of gate, up and down; every region starts on
+// 256 bytes.
 struct FmtLayout {
-  size_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales, bytes;
+  size_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales, globals, bytes;
 };
 __host__ __device__ inline FmtLayout fmt_layout(int fmt, int H, int I) {
-  (void)fmt;  // MOE_FMT_INT8_G32
-  const int bits = 8, g = 32;
+  const bool nv = fmt == MOE_FMT_NVFP4;
+  const int bits = nv ? 4 : 8, g = nv ? 16 : 32, sb = nv ? 1 : 2;
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   const size_t gu_codes = (size_t)I * H * bits / 8, dn_codes = (size_t)H * I * bits / 8;
-  const size_t gu_scales = (size_t)I * (H / g) * 2, dn_scales = (size_t)H * (I / g) * 2;
+  const size_t gu_scales = (size_t)I * (H / g) * sb, dn_scales = (size_t)H * (I / g) * sb;
   FmtLayout L;
   L.gate_codes = 0;
   L.up_codes = al(L.gate_codes + gu_codes);
@@ -66,7 +69,8 @@ __host__ __device__ inline FmtLayout fmt_layout(int fmt, int H, int I) {
   L.gate_scales = al(L.down_codes + dn_codes);
   L.up_scales = al(L.gate_scales + gu_scales);
   L.down_scales = al(L.up_scales + gu_scales);
-  L.bytes = al(L.down_scales + dn_scales);
+  L.globals = al(L.down_scales + dn_scales);
+  L.bytes = nv ? al(L.globals + 12) : L.globals;
   return L;
 }
 bool fmt_shape_ok(int fmt, int H, int I);

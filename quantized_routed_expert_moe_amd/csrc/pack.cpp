@@ -10,6 +10,8 @@
 // layout is documented in moe_internal.h.
 #include <string.h>
 
+#include <cmath>
+#include <utility>
 #include <vector>
 
 #include "moe_internal.h"
@@ -109,7 +111,7 @@ extern "C" int moe_pack_expert_fmt(int fmt, const uint8_t* qg, const uint8_t* qu
                                    const uint16_t* sg, const uint16_t* su, const uint16_t* sd, int H, int I,
                                    void* blob_out) {
   if (fmt == MOE_FMT_INT4_G32) return moe_pack_expert(qg, qu, qd, sg, su, sd, H, I, moe::kGroup, blob_out);
-  if (fmt != MOE_FMT_INT4_G128 && fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;
+  if (fmt != MOE_FMT_INT4_G128 && fmt != MOE_FMT_INT8_G32) return MOE_EINVAL;  // NVFP4: moe_pack_expert_nvfp4
   if (!qg || !qu || !qd || !sg || !su || !sd || !blob_out) return MOE_EINVAL;
   if (fmt == MOE_FMT_INT4_G128) {  // the group-32 blob with repeated scales
     if (!g128_shape_ok(H, I)) return MOE_EUNSUP;
@@ -123,5 +125,29 @@ extern "C" int moe_pack_expert_fmt(int fmt, const uint8_t* qg, const uint8_t* qu
   pack_matrix_int8(qg, sg, I, H, b + L.gate_codes, reinterpret_cast<uint16_t*>(b + L.gate_scales));
   pack_matrix_int8(qu, su, I, H, b + L.up_codes, reinterpret_cast<uint16_t*>(b + L.up_scales));
   pack_matrix_int8(qd, sd, H, I, b + L.down_codes, reinterpret_cast<uint16_t*>(b + L.down_scales));
+  return MOE_OK;
+}
+
+extern "C" int moe_pack_expert_nvfp4(const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, const uint8_t* sg,
+                                     const uint8_t* su, const uint8_t* sd, const float* global3, int H, int I,
+                                     void* blob_out) {
+  if (!qg || !qu || !qd || !sg || !su || !sd || !global3 || !blob_out) return MOE_EINVAL;
+  if (!moe::fmt_shape_ok(MOE_FMT_NVFP4, H, I)) return MOE_EUNSUP;
+  for (int m = 0; m < 3; ++m)
+    if (!std::isfinite(global3[m])) return MOE_EINVAL;
+  const size_t n_gu = (size_t)I * (H / 16), n_dn = (size_t)H * (I / 16);
+  for (const auto& sc : {std::make_pair(sg, n_gu), std::make_pair(su, n_gu), std::make_pair(sd, n_dn)})
+    for (size_t i = 0; i < sc.second; ++i)
+      if ((sc.first[i] & 0x7Fu) == 0x7Fu) return MOE_EINVAL;  // the E4M3 NaN
+  const moe::FmtLayout L = moe::fmt_layout(MOE_FMT_NVFP4, H, I);
+  uint8_t* b = static_cast<uint8_t*>(blob_out);
+  memset(b, 0, L.bytes);
+  memcpy(b + L.gate_codes, qg, (size_t)I * H / 2);  // E2M1 pairs as delivered
+  memcpy(b + L.up_codes, qu, (size_t)I * H / 2);
+  memcpy(b + L.down_codes, qd, (size_t)H * I / 2);
+  memcpy(b + L.gate_scales, sg, n_gu);
+  memcpy(b + L.up_scales, su, n_gu);
+  memcpy(b + L.down_scales, sd, n_dn);
+  memcpy(b + L.globals, global3, 12);
   return MOE_OK;
 }

@@ -32,6 +32,9 @@ def pack_expert_fmt(seed: int, layer: int, expert: int, H: int, I: int, fmt: int
     """Seeded expert in format ``fmt`` -> host blob (uint8, one slot stride long)."""
     t = gen.expert_tensors_fmt(seed, layer, expert, H, I, fmt)
     out = np.zeros(lib.moe_fmt_slot_stride(fmt, H, I), dtype=np.uint8)
+    if fmt == gen.FMT_NVFP4:
+        lib.moe_pack_expert_nvfp4(t["qg"], t["qu"], t["qd"], t["sg"], t["su"], t["sd"], t["global"], H, I, out)
+        return out
     lib.moe_pack_expert_fmt(
         fmt, t["qg"], t["qu"], t["qd"], t["sg"].view(np.uint16), t["su"].view(np.uint16), t["sd"].view(np.uint16),
         H, I, out,

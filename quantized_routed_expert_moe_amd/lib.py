@@ -21,7 +21,7 @@ MOE_ROUTE_RENORM = 1 << 0
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_FORCE_GEMV = 1 << 8
 MOE_FORCE_GROUPED = 1 << 9
-MOE_FMT_INT4_G32, MOE_FMT_INT4_G128, MOE_FMT_INT8_G32 = 0, 1, 2
+MOE_FMT_INT4_G32, MOE_FMT_INT4_G128, MOE_FMT_INT8_G32, MOE_FMT_NVFP4 = 0, 1, 2, 3
 MOE_FFN_PARTIAL = 1 << 10
 MOE_FFN_PARTIAL_SHARED = 1 << 11
 
@@ -43,6 +43,7 @@ EXPORTS = (
     "moe_fmt_blob_bytes",
     "moe_fmt_slot_stride",
     "moe_pack_expert_fmt",
+    "moe_pack_expert_nvfp4",
     "moe_fmt_workspace_bytes",
     "moe_expert_ffn_fmt",
     "arena_create",
@@ -116,6 +117,7 @@ def load(path: str | None = None):
         "moe_fmt_blob_bytes": (_SZ, [_I, _I, _I]),
         "moe_fmt_slot_stride": (_SZ, [_I, _I, _I]),
         "moe_pack_expert_fmt": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
+        "moe_pack_expert_nvfp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
         "moe_fmt_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
         "moe_expert_ffn_fmt": (
             _I,
@@ -205,6 +207,14 @@ def moe_pack_expert_fmt(fmt, qg, qu, qd, sg, su, sd, H, I, blob_out) -> None:
         load().moe_pack_expert_fmt(fmt, _ptr(qg), _ptr(qu), _ptr(qd), _ptr(sg), _ptr(su), _ptr(sd), H, I,
                                    _ptr(blob_out)),
         "moe_pack_expert_fmt",
+    )
+
+
+def moe_pack_expert_nvfp4(qg, qu, qd, sg, su, sd, global3, H, I, blob_out) -> None:
+    _check(
+        load().moe_pack_expert_nvfp4(_ptr(qg), _ptr(qu), _ptr(qd), _ptr(sg), _ptr(su), _ptr(sd), _ptr(global3), H, I,
+                                     _ptr(blob_out)),
+        "moe_pack_expert_nvfp4",
     )
 
 

@@ -76,8 +76,9 @@ def expert_tensors(seed: int, layer: int, expert: int, H: int, I: int, g: int = 
 
 
 # expert weight formats (the C enum moe_format)
-FMT_INT4_G32, FMT_INT4_G128, FMT_INT8_G32 = 0, 1, 2
-FMT_BITS_G = {FMT_INT4_G32: (4, 32), FMT_INT4_G128: (4, 128), FMT_INT8_G32: (8, 32)}
+FMT_INT4_G32, FMT_INT4_G128, FMT_INT8_G32, FMT_NVFP4 = 0, 1, 2, 3
+FMT_BITS_G = {FMT_INT4_G32: (4, 32), FMT_INT4_G128: (4, 128), FMT_INT8_G32: (8, 32), FMT_NVFP4: (4, 16)}
+KIND_GLOBAL = 97
 
 
 def expert_tensors_fmt(seed: int, layer: int, expert: int, H: int, I: int, fmt: int) -> dict:
@@ -85,6 +86,23 @@ def expert_tensors_fmt(seed: int, layer: int, expert: int, H: int, I: int, fmt: 
     group 32 or 128. int8: uniform bytes (every code -128..127 occurs), scales
     U(0.005, 0.02) / 16 in fp16, so the weights span the int4 experts' range."""
     bits, g = FMT_BITS_G[fmt]
+    if fmt == FMT_NVFP4:
+        # uniform code bytes (every E2M1 code occurs); E4M3 scales with exponent
+        # field 1 or 2 and any mantissa (2^-6 .. 2^-4.1); globals U(0.5, 1) in fp32
+        def nv_scales(kind, rows, cols):
+            r = _rng(seed, layer, expert, kind)
+            return ((r.integers(1, 3, size=(rows, cols // 16)) << 3) | r.integers(0, 8, size=(rows, cols // 16))).astype(
+                np.uint8)
+
+        return {
+            "qg": _codes(seed, layer, expert, KIND_QG, I, H),
+            "qu": _codes(seed, layer, expert, KIND_QU, I, H),
+            "qd": _codes(seed, layer, expert, KIND_QD, H, I),
+            "sg": nv_scales(KIND_SG, I, H),
+            "su": nv_scales(KIND_SU, I, H),
+            "sd": nv_scales(KIND_SD, H, I),
+            "global": _rng(seed, layer, expert, KIND_GLOBAL).uniform(0.5, 1.0, size=3).astype(np.float32),
+        }
     if bits == 4:
         return expert_tensors(seed, layer, expert, H, I, g)
 

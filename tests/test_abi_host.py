@@ -223,3 +223,36 @@ def test_fmt_sizes_and_rejections():
         lib.moe_pack_expert_fmt(7, z, z, z, z, z, z, 256, 96, z)
     with pytest.raises(lib.MoeError):
         lib.moe_pack_expert_fmt(gen.FMT_INT4_G128, z, z, z, z, z, z, 256, 96, z)
+
+
+@pytest.mark.parametrize("H,I", [(256, 96), (4096, 1536)])
+def test_nvfp4_pack_layout_roundtrip(H, I):
+    t = gen.expert_tensors_fmt(9, 0, 3, H, I, gen.FMT_NVFP4)
+    nb = lib.moe_fmt_blob_bytes(gen.FMT_NVFP4, H, I)
+    offs = [0]
+    for size in (I * H // 2, I * H // 2, H * I // 2, I * H // 16, I * H // 16, H * I // 16, 12):
+        offs.append(al256(offs[-1] + size))
+    assert nb == offs[-1]
+    blob = np.zeros(lib.moe_fmt_slot_stride(gen.FMT_NVFP4, H, I), dtype=np.uint8)
+    lib.moe_pack_expert_nvfp4(t["qg"], t["qu"], t["qd"], t["sg"], t["su"], t["sd"], t["global"], H, I, blob)
+    for i, (k, n) in enumerate((("qg", I * H // 2), ("qu", I * H // 2), ("qd", H * I // 2), ("sg", I * H // 16),
+                                ("su", I * H // 16), ("sd", H * I // 16))):
+        assert np.array_equal(blob[offs[i] : offs[i] + n], t[k].ravel())
+    assert np.array_equal(blob[offs[6] : offs[6] + 12].view(np.float32), t["global"])
+
+
+def test_nvfp4_pack_rejections():
+    H, I = 256, 96
+    t = gen.expert_tensors_fmt(9, 0, 3, H, I, gen.FMT_NVFP4)
+    blob = np.zeros(lib.moe_fmt_slot_stride(gen.FMT_NVFP4, H, I), dtype=np.uint8)
+    bad = t["sd"].copy()
+    bad[3, 2] = 0xFF  # the E4M3 NaN
+    with pytest.raises(lib.MoeError):
+        lib.moe_pack_expert_nvfp4(t["qg"], t["qu"], t["qd"], t["sg"], t["su"], bad, t["global"], H, I, blob)
+    g = t["global"].copy()
+    g[1] = np.inf
+    with pytest.raises(lib.MoeError):
+        lib.moe_pack_expert_nvfp4(t["qg"], t["qu"], t["qd"], t["sg"], t["su"], t["sd"], g, H, I, blob)
+    with pytest.raises(lib.MoeError):  # H not a multiple of 32
+        lib.moe_pack_expert_nvfp4(t["qg"], t["qu"], t["qd"], t["sg"], t["su"], t["sd"], t["global"], 240, I, blob)
+    assert lib.moe_fmt_blob_bytes(gen.FMT_NVFP4, 16384, 1536) == 0

@@ -714,12 +714,17 @@ def fmt_run(fmt, w, slots, table, shared, stride, xb, logits):
         (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t32_h2048_e32_k8_i768", 32, 2048, 32, 8, 768, 1, 32, "zipf", 76)),
         (gen.FMT_INT4_G128, gen.Workload("fmt4g128_t77_h1024_e16_k4_i256_shared", 77, 1024, 16, 4, 256, 1, 16,
                                          "normal", 80, shared=True)),
+        (gen.FMT_NVFP4, gen.Workload("nvfp4_t1_h512_e16_k4_i256_shared", 1, 512, 16, 4, 256, 1, 16, "normal", 81,
+                                     shared=True)),
+        (gen.FMT_NVFP4, gen.Workload("nvfp4_t7_h256_e8_k2_i96", 7, 256, 8, 2, 96, 1, 8, "normal", 82)),
+        (gen.FMT_NVFP4, gen.Workload("nvfp4_t32_h2048_e32_k8_i768_shared", 32, 2048, 32, 8, 768, 1, 32, "zipf", 83,
+                                     shared=True)),
     ],
     ids=lambda v: v.name if hasattr(v, "name") else f"fmt{v}",
 )
 def test_fmt_matches_oracle(fmt, w):
-    """INT8 group-32 and INT4 group-128 experts (the latter on every path of moe_expert_ffn,
-    77 tokens on the grouped one): ids bit-exact, y within the oracle's bar, the same bits
+    """INT8 group-32, INT4 group-128 (on every path of moe_expert_ffn, 77 tokens on the
+    grouped one) and NVFP4 experts: ids bit-exact, y within the oracle's bar, the same bits
     on a second run and under a permuted slot map."""
     say(f"format {fmt} {w.name}")
     xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
@@ -747,7 +752,7 @@ def test_fmt_matches_oracle(fmt, w):
     assert torch.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("fmt", [gen.FMT_INT8_G32, gen.FMT_INT4_G128])
+@pytest.mark.parametrize("fmt", [gen.FMT_INT8_G32, gen.FMT_INT4_G128, gen.FMT_NVFP4])
 def test_fmt_decode_full_size(fmt):
     """One token, 256 experts, top-8, H 4096, I 1536 (the decode shape), the 8 routed experts
     in a 64-slot arena: against the oracle."""

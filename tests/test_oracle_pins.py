@@ -439,3 +439,47 @@ def test_format_generator_ranges():
     t128 = gen.expert_tensors_fmt(3, 0, 5, 256, 128, gen.FMT_INT4_G128)
     assert t128["sg"].shape == (128, 2) and t128["sd"].shape == (256, 1)
     assert np.array_equal(t128["qg"], gen.expert_tensors(3, 0, 5, 256, 128, 32)["qg"])
+
+
+def test_e4m3_decoding_against_torch():
+    b = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(b).view(torch.float8_e4m3fn).double().numpy()
+    got = R.decode_e4m3(b)
+    nan = np.isnan(want)
+    assert np.array_equal(nan, np.isnan(got)) and nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_e2m1_decoding_against_torch_e4m3():
+    # the E4M3 pattern with the same value: exponent + 6, mantissa bit at the top of the
+    # three, the E2M1 subnormal 0.5 as 2^-1; decoded by torch, an independent routine
+    c = np.arange(16)
+    s, e, m = c >> 3, (c >> 1) & 3, c & 1
+    pat = np.where(e > 0, (s << 7) | ((e + 6) << 3) | (m << 2), np.where(m == 1, (s << 7) | (6 << 3), s << 7))
+    want = torch.from_numpy(pat.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(R.decode_e2m1(c), want)
+    assert R.decode_e2m1(c).tolist()[:8] == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_nvfp4_dequantize_hand_values():
+    # one row of 32 columns: code bytes 0x71 (columns 0, 1 = 0.5, 6.0), 0xF8 (columns 2, 3 =
+    # -0.0, -6.0) and 0x2A (columns 16, 17 = -1.0, 1.0), the rest zero; scales 0x38 (1.0)
+    # and 0x01 (2^-9); global 0.25
+    packed = np.zeros((1, 16), dtype=np.uint8)
+    packed[0, 0], packed[0, 1], packed[0, 8] = 0x71, 0xF8, 0x2A
+    W = R.dequantize_nvfp4(packed, np.array([[0x38, 0x01]], dtype=np.uint8), 0.25, 32)
+    assert W[0, :4].tolist() == [0.125, 1.5, -0.0, -1.5]
+    assert W[0, 16] == -(2.0**-9) * 0.25 and W[0, 17] == 2.0**-9 * 0.25
+    assert not W[0, 4:16].any() and not W[0, 18:].any()
+
+
+def test_nvfp4_unit_scales_give_the_code_values():
+    rng = np.random.default_rng(14)
+    packed = rng.integers(0, 256, size=(5, 32), dtype=np.uint8)
+    W = R.dequantize_nvfp4(packed, np.full((5, 4), 0x38, dtype=np.uint8), 1.0, 64)
+    c = np.empty((5, 64), dtype=np.int64)
+    c[:, 0::2], c[:, 1::2] = packed & 15, packed >> 4
+    assert np.array_equal(W, R.decode_e2m1(c))
+    t = gen.expert_tensors_fmt(3, 0, 5, 64, 96, gen.FMT_NVFP4)
+    sc = R.decode_e4m3(t["sg"])
+    assert sc.min() >= 2.0**-6 and sc.max() < 2.0**-4 and t["sg"].shape == (96, 4) and t["global"].dtype == np.float32
