@@ -608,8 +608,8 @@ def chunked_leg(a, dev):
 
 def formats_leg(dev, steps=192, n_blobs=64):
     """Expert FFN of one token (H 4096, I 1536, 256 experts, top-8) per weight format:
-    int4 group 32 (the single-token path of moe_expert_ffn), int4 group 128 and int8
-    group 32 (moe_expert_ffn_fmt). 64 distinct experts are packed per format (the
+    int4 group 32 and int4 group 128 (the single-token path of moe_expert_ffn), int8
+    group 32 and NVFP4 (moe_expert_ffn_fmt). 64 distinct experts are packed per format (the
     table maps expert e to blob e % 64, more bytes than the 256 MB last-level cache);
     every timed call routes to 8 other experts (seeded draws without replacement)."""
     import numpy as np
@@ -628,7 +628,8 @@ def formats_leg(dev, steps=192, n_blobs=64):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     table = torch.from_numpy((np.arange(E) % n_blobs).astype(np.int32)).to(dev)
     out = {}
-    for name, fmt in (("int4_g32", gen.FMT_INT4_G32), ("int4_g128", gen.FMT_INT4_G128), ("int8_g32", gen.FMT_INT8_G32)):
+    for name, fmt in (("int4_g32", gen.FMT_INT4_G32), ("int4_g128", gen.FMT_INT4_G128), ("int8_g32", gen.FMT_INT8_G32),
+                      ("nvfp4", gen.FMT_NVFP4)):
         stride = lib.moe_fmt_slot_stride(fmt, H, I)
         blob = lib.moe_fmt_blob_bytes(fmt, H, I)
         slots = torch.empty(n_blobs * stride, dtype=torch.uint8, device=dev)

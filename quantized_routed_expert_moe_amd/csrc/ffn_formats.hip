@@ -19,11 +19,10 @@
 // Dequantisation is exact and lives in the fp16 dot products. int8: the pairs
 // (0x64 << 8 | u) = 1024 + u = q + 1152 come from one v_perm_b32 per two codes,
 // and sum_c q_c x_c = D - 1152 sum_c x_c with the x sums per chunk staged once.
-// NVFP4: the fp16 value of an E2M1 magnitude has a zero low byte, so one v_perm
-// over an 8-byte table gives four high bytes, one v_perm per pair places two of
-// them, and one v_perm plus one AND-OR adds the two sign bits; the E2M1 values
-// are exact in fp16. Each group's dot product is scaled in fp32 by its scale
-// (fp16, or E4M3 decoded exactly), and an NVFP4 row by its global scale. x (and
+// NVFP4: v_cvt_scalef32_pk_f16_fp4 turns a code byte into the fp16 pair of its
+// two columns (the E2M1 values are exact in fp16). Each group's dot product is
+// scaled in fp32 by its scale (fp16, or E4M3 decoded exactly), and an NVFP4 row
+// by its global scale. x (and
 // h for the down projection) are staged as fp16 (a value past the fp16 range
 // sets MOE_EUNSUP).
 //
@@ -124,25 +123,24 @@ __device__ inline void stage_act(const Src* src, int n, uint32_t* xs, float* cor
   if (bad) *status = MOE_EUNSUP;
 }
 
-// NVFP4: the two groups' sums (columns 0..15 and 16..31 of the chunk).
+// NVFP4: the two groups' sums (columns 0..15 and 16..31 of the chunk). Byte b of
+// a code dword holds columns 2b (low nibble) and 2b + 1; gfx950 converts it to
+// the fp16 pair of those columns in one instruction (scale 1: the E4M3 and
+// global scales are applied in fp32 to the group sums and the row).
 __device__ inline void chunk_dot_nvfp4(const uint4& cw, const uint32_t* xp, float& d0, float& d1) {
-  // fp16 high bytes of the E2M1 magnitudes 0, 0.5, 1, 1.5 | 2, 3, 4, 6
-  const uint32_t lut_lo = 0x3E3C3800u, lut_hi = 0x46444240u;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
   float d[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {  // dword i: columns 8i .. 8i + 7
-    const uint32_t e = __builtin_amdgcn_perm(lut_hi, lut_lo, w[i] & 0x07070707u);         // cols 8i + 0, 2, 4, 6
-    const uint32_t o = __builtin_amdgcn_perm(lut_hi, lut_lo, (w[i] >> 4) & 0x07070707u);  // cols 8i + 1, 3, 5, 7
-    const uint32_t w4 = w[i] << 4;  // even columns' sign bits at the top of their bytes
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {  // pair k: columns 8i + 2k, 8i + 2k + 1
-      // bytes [0, e_k, 0, o_k]: fp16 magnitudes of the two columns
-      const uint32_t mag = __builtin_amdgcn_perm(o, e, 0x000C000Cu | ((4u + k) << 24) | ((uint32_t)k << 8));
-      // bytes [-, byte k of w4, -, byte k of w]: the sign bits land on bits 15 and 31
-      const uint32_t sgn = __builtin_amdgcn_perm(w[i], w4, ((4u + k) << 24) | ((uint32_t)k << 8));
-      d[i >> 1] = dot2h((sgn & 0x80008000u) | mag, xp[4 * i + k], d[i >> 1]);
-    }
+    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0);
+    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1);
+    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2);
+    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3);
+    d[i >> 1] = dot2h(__builtin_bit_cast(uint32_t, p0), xp[4 * i + 0], d[i >> 1]);
+    d[i >> 1] = dot2h(__builtin_bit_cast(uint32_t, p1), xp[4 * i + 1], d[i >> 1]);
+    d[i >> 1] = dot2h(__builtin_bit_cast(uint32_t, p2), xp[4 * i + 2], d[i >> 1]);
+    d[i >> 1] = dot2h(__builtin_bit_cast(uint32_t, p3), xp[4 * i + 3], d[i >> 1]);
   }
   d0 = d[0];
   d1 = d[1];
