@@ -291,6 +291,10 @@ typedef struct {
 } moe_fill;
 typedef struct {
   uint64_t hits, misses, evictions, fills, h2d_bytes;
+  /* arena_prefetch: fills it made (also counted in fills and h2d_bytes, not in
+   * misses), and hits of arena_map_slots on an expert a prefetch filled and no
+   * arena_map_slots call had requested since */
+  uint64_t prefetch_fills, prefetch_hits;
 } moe_arena_stats;
 
 /* Create an arena of S slots for E experts.
@@ -311,8 +315,28 @@ int arena_map_slots(moe_arena* a, const int32_t* ids, int n, int32_t* slots, moe
  * slots_dev + slot * stride, blob_bytes), then the slot_table_dev updates
  * (table[evicted] = -1, table[filled] = slot), then hipEventRecord(done) when
  * done != NULL. The compute stream must wait on `done` before using the
- * slots. Fills must come from the last arena_map_slots call. */
+ * slots. Fills must come from the last arena_map_slots or arena_prefetch call. */
 int arena_fill_async(moe_arena* a, const moe_fill* fills, int n_fills, moe_stream_t side, moe_event_t done);
+/* Read-ahead ("Strata on a Mac", What you need: the experts the next layer
+ * will probably use are read ahead; "Strata" README, the execution model: a
+ * predictor may steer only what is fetched and when, never what is computed).
+ * Maps n predicted ids (host int32) into the arena without counting hits or
+ * misses; the fills they need go to fills (host, capacity n; count in
+ * *n_fills), to be enqueued with arena_fill_async like those of
+ * arena_map_slots:
+ *   1. and 2. as arena_map_slots (MOE_EINVAL, MOE_ENOSLOT: arena unchanged);
+ *   3. a predicted expert already resident is left as it is (its stamp too);
+ *   4. each predicted expert not resident takes a slot by rule 4 of
+ *      arena_map_slots (protected: the experts predicted in this call) and the
+ *      call's stamp, and becomes a fill;
+ *   5. the call number grows by one per successful call.
+ * Precondition as arena_map_slots: no GPU work still reads a slot that may be
+ * evicted. A later arena_map_slots that requests a prefetched expert finds it
+ * resident; the compute stream must then wait for an event recorded on the
+ * side stream after the prefetch's copies (arena_fill_async of that later
+ * call, on the same side stream, records one). The predicted ids never change
+ * a result: every output equals the run without read-ahead, bit for bit. */
+int arena_prefetch(moe_arena* a, const int32_t* ids, int n, moe_fill* fills, int* n_fills);
 /* Set-up placement: the caller has put expert's blob into slot (no copy, no
  * table write). An expert placed elsewhere before is moved. */
 int arena_place(moe_arena* a, int expert, int slot);

@@ -16,6 +16,16 @@ eviction order as a small effect, so one plain deterministic LRU is used:
    current stamp and is reported as a fill (expert, slot);
 5. the call number grows by one per successful call.
 
+Read-ahead ("Strata on a Mac", What you need: the engine reads ahead the
+experts the next layer will probably use; "Strata" README, the execution
+model: a predictor may steer fetching only, never the computation). The pages
+give no rule; the reading here: a prefetch call takes the predicted ids through
+steps 1, 2, 4 and 5 with the predicted experts as the protected set, leaves a
+predicted expert that is already resident untouched (no stamp, no hit), and
+counts no hits or misses. Its fills are counted as prefetch fills; a later
+requested hit on an expert that a prefetch filled, first since that fill, is a
+prefetch hit.
+
 Parity: pinned by a hand-worked sequence and by invariants in
 tests/test_arena_model.py.
 """
@@ -36,8 +46,9 @@ class ArenaModel:
         self.slot_of = [-1] * self.E  # expert -> slot (-1 absent)
         self.expert_in = [-1] * self.S  # slot -> expert (-1 empty)
         self.stamp = [0] * self.S
+        self.by_prefetch = [False] * self.S  # slot filled by a prefetch, not requested since
         self.calls = 0
-        self.stats = dict(hits=0, misses=0, evictions=0, fills=0, h2d_bytes=0)
+        self.stats = dict(hits=0, misses=0, evictions=0, fills=0, h2d_bytes=0, prefetch_fills=0, prefetch_hits=0)
 
     def place(self, expert: int, slot: int) -> int:
         """Set-up placement: the caller has put ``expert``'s data in ``slot``."""
@@ -52,19 +63,44 @@ class ArenaModel:
         self.expert_in[slot] = expert
         self.slot_of[expert] = slot
         self.stamp[slot] = 0
+        self.by_prefetch[slot] = False
         return OK
 
-    def map_slots(self, ids):
-        """Returns (status, slots per input entry, fills [(expert, slot)])."""
+    def _distinct(self, ids):
         ids = [int(e) for e in ids]
         if any(not 0 <= e < self.E for e in ids):
-            return EINVAL, None, None
+            return EINVAL, None
         distinct = []
         for e in ids:
             if e not in distinct:
                 distinct.append(e)
         if len(distinct) > self.S:
-            return ENOSLOT, None, None
+            return ENOSLOT, None
+        return OK, distinct
+
+    def _take_slot(self, e, now, protected, by_prefetch):
+        """Step 4 for one expert that is not resident; returns its slot."""
+        empty = [s for s in range(self.S) if self.expert_in[s] < 0]
+        if empty:
+            s = empty[0]
+        else:
+            cands = [s for s in range(self.S) if self.expert_in[s] not in protected]
+            s = min(cands, key=lambda c: (self.stamp[c], c))
+            self.slot_of[self.expert_in[s]] = -1
+            self.stats["evictions"] += 1
+        self.expert_in[s] = e
+        self.slot_of[e] = s
+        self.stamp[s] = now
+        self.by_prefetch[s] = by_prefetch
+        self.stats["fills"] += 1
+        self.stats["h2d_bytes"] += self.blob_bytes
+        return s
+
+    def map_slots(self, ids):
+        """Returns (status, slots per input entry, fills [(expert, slot)])."""
+        status, distinct = self._distinct(ids)
+        if status != OK:
+            return status, None, None
         self.calls += 1
         now = self.calls
         requested = set(distinct)
@@ -74,26 +110,31 @@ class ArenaModel:
             if s >= 0:
                 self.stamp[s] = now
                 self.stats["hits"] += 1
+                if self.by_prefetch[s]:
+                    self.stats["prefetch_hits"] += 1
+                    self.by_prefetch[s] = False
             else:
                 misses.append(e)
         fills = []
         for e in misses:
-            empty = [s for s in range(self.S) if self.expert_in[s] < 0]
-            if empty:
-                s = empty[0]
-            else:
-                cands = [s for s in range(self.S) if self.expert_in[s] not in requested]
-                s = min(cands, key=lambda c: (self.stamp[c], c))
-                self.slot_of[self.expert_in[s]] = -1
-                self.stats["evictions"] += 1
-            self.expert_in[s] = e
-            self.slot_of[e] = s
-            self.stamp[s] = now
-            fills.append((e, s))
+            fills.append((e, self._take_slot(e, now, requested, False)))
             self.stats["misses"] += 1
-            self.stats["fills"] += 1
-            self.stats["h2d_bytes"] += self.blob_bytes
-        return OK, [self.slot_of[e] for e in ids], fills
+        return OK, [self.slot_of[int(e)] for e in ids], fills
+
+    def prefetch(self, ids):
+        """Read-ahead of predicted ids. Returns (status, fills [(expert, slot)])."""
+        status, distinct = self._distinct(ids)
+        if status != OK:
+            return status, None
+        self.calls += 1
+        now = self.calls
+        predicted = set(distinct)
+        fills = []
+        for e in distinct:
+            if self.slot_of[e] < 0:
+                fills.append((e, self._take_slot(e, now, predicted, True)))
+                self.stats["prefetch_fills"] += 1
+        return OK, fills
 
     def chunk_passes(self, ids, max_per_pass: int):
         """Passes of a chunked paged prompt run ("Strata on a Mac", Measured, the

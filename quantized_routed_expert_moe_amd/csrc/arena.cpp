@@ -5,7 +5,9 @@
 // experts leased into device memory per decode step through an LRU cache);
 // see moe.h for the exact rule. Misses are filled with one asynchronous copy
 // per expert from a pinned host source (one contiguous read per expert,
-// "Strata on a Mac", What you need), on a caller-chosen side stream.
+// "Strata on a Mac", What you need), on a caller-chosen side stream. Read-ahead
+// (arena_prefetch) maps predicted experts with the same eviction rule; it
+// changes which bytes are in the slots early, never what a later call computes.
 #include <new>
 #include <vector>
 
@@ -20,6 +22,7 @@ struct moe_arena {
   std::vector<int32_t> slot_of;    // expert -> slot, -1 absent
   std::vector<int32_t> expert_in;  // slot -> expert, -1 empty
   std::vector<uint64_t> stamp;     // slot -> call number of last use
+  std::vector<uint8_t> prefetched; // slot -> filled by arena_prefetch, not requested since
   std::vector<uint64_t> req_mark;  // expert -> call number that requested it
   uint64_t calls = 0;
   uint64_t marker = 0;             // distinct value per map call (also failed ones)
@@ -44,6 +47,7 @@ extern "C" int arena_create(int E, int S, size_t blob_bytes, size_t stride, void
   a->slot_of.assign(E, -1);
   a->expert_in.assign(S, -1);
   a->stamp.assign(S, 0);
+  a->prefetched.assign(S, 0);
   a->req_mark.assign(E, 0);
   *out = a;
   return MOE_OK;
@@ -56,6 +60,7 @@ extern "C" int arena_reset(moe_arena* a) {
   a->slot_of.assign(a->E, -1);
   a->expert_in.assign(a->S, -1);
   a->stamp.assign(a->S, 0);
+  a->prefetched.assign(a->S, 0);
   a->calls = 0;
   a->stats = moe_arena_stats{};
   a->last_fills.clear();
@@ -84,17 +89,20 @@ extern "C" int arena_place(moe_arena* a, int expert, int slot) {
   a->expert_in[slot] = expert;
   a->slot_of[expert] = slot;
   a->stamp[slot] = 0;
+  a->prefetched[slot] = 0;
   return MOE_OK;
 }
 
-extern "C" int arena_map_slots(moe_arena* a, const int32_t* ids, int n, int32_t* slots, moe_fill* fills,
-                               int* n_fills) {
-  if (!a || n < 0 || (n > 0 && (!ids || !slots || !fills)) || !n_fills) return MOE_EINVAL;
+namespace {
+
+// Checks the ids and de-duplicates them in first-occurrence order; the experts
+// of this call are marked in req_mark. MOE_ENOSLOT leaves the arena as it was
+// (but for the marks, which only ever compare equal to the current call's).
+int distinct_ids(moe_arena* a, const int32_t* ids, int n, std::vector<int32_t>& distinct) {
   for (int i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= a->E) return MOE_EINVAL;
-  // De-duplicate in first-occurrence order.
   const uint64_t mark = ++a->marker;
-  std::vector<int32_t> distinct;
+  distinct.clear();
   distinct.reserve(n);
   for (int i = 0; i < n; ++i) {
     if (a->req_mark[ids[i]] != mark) {
@@ -102,7 +110,53 @@ extern "C" int arena_map_slots(moe_arena* a, const int32_t* ids, int n, int32_t*
       distinct.push_back(ids[i]);
     }
   }
-  if ((int)distinct.size() > a->S) return MOE_ENOSLOT;  // nothing changed but the marks
+  return (int)distinct.size() > a->S ? MOE_ENOSLOT : MOE_OK;
+}
+
+// Places expert e (not resident) with stamp now: the lowest empty slot, else the
+// slot of the oldest expert not marked in this call (ties to the lower slot).
+// Records the fill and what it evicted.
+void place_miss(moe_arena* a, int e, uint64_t now, bool by_prefetch) {
+  int victim_slot = -1;
+  for (int s = 0; s < a->S; ++s)
+    if (a->expert_in[s] < 0) {
+      victim_slot = s;
+      break;
+    }
+  int evicted = -1;
+  if (victim_slot < 0) {
+    for (int s = 0; s < a->S; ++s) {
+      const int r = a->expert_in[s];
+      if (a->req_mark[r] == a->marker) continue;  // named in this call: protected
+      if (victim_slot < 0 || a->stamp[s] < a->stamp[victim_slot]) victim_slot = s;
+    }
+    evicted = a->expert_in[victim_slot];
+    a->slot_of[evicted] = -1;
+    a->stats.evictions++;
+  }
+  a->expert_in[victim_slot] = e;
+  a->slot_of[e] = victim_slot;
+  a->stamp[victim_slot] = now;
+  a->prefetched[victim_slot] = by_prefetch ? 1 : 0;
+  a->last_fills.push_back(moe_fill{e, victim_slot});
+  a->last_evicted.push_back(evicted);
+  a->stats.fills++;
+  a->stats.h2d_bytes += a->blob_bytes;
+}
+
+void copy_fills(const moe_arena* a, moe_fill* fills, int* n_fills) {
+  for (size_t i = 0; i < a->last_fills.size(); ++i) fills[i] = a->last_fills[i];
+  *n_fills = (int)a->last_fills.size();
+}
+
+}  // namespace
+
+extern "C" int arena_map_slots(moe_arena* a, const int32_t* ids, int n, int32_t* slots, moe_fill* fills,
+                               int* n_fills) {
+  if (!a || n < 0 || (n > 0 && (!ids || !slots || !fills)) || !n_fills) return MOE_EINVAL;
+  std::vector<int32_t> distinct;
+  const int rc = distinct_ids(a, ids, n, distinct);
+  if (rc != MOE_OK) return rc;
   const uint64_t now = ++a->calls;
   std::vector<int32_t> misses;
   for (int e : distinct) {
@@ -110,6 +164,10 @@ extern "C" int arena_map_slots(moe_arena* a, const int32_t* ids, int n, int32_t*
     if (s >= 0) {
       a->stamp[s] = now;
       a->stats.hits++;
+      if (a->prefetched[s]) {
+        a->stats.prefetch_hits++;
+        a->prefetched[s] = 0;
+      }
     } else {
       misses.push_back(e);
     }
@@ -117,35 +175,28 @@ extern "C" int arena_map_slots(moe_arena* a, const int32_t* ids, int n, int32_t*
   a->last_fills.clear();
   a->last_evicted.clear();
   for (int e : misses) {
-    int victim_slot = -1;
-    for (int s = 0; s < a->S; ++s)
-      if (a->expert_in[s] < 0) {
-        victim_slot = s;
-        break;
-      }
-    int evicted = -1;
-    if (victim_slot < 0) {
-      for (int s = 0; s < a->S; ++s) {
-        const int r = a->expert_in[s];
-        if (a->req_mark[r] == mark) continue;  // requested in this call: protected
-        if (victim_slot < 0 || a->stamp[s] < a->stamp[victim_slot]) victim_slot = s;
-      }
-      evicted = a->expert_in[victim_slot];
-      a->slot_of[evicted] = -1;
-      a->stats.evictions++;
-    }
-    a->expert_in[victim_slot] = e;
-    a->slot_of[e] = victim_slot;
-    a->stamp[victim_slot] = now;
-    a->last_fills.push_back(moe_fill{e, victim_slot});
-    a->last_evicted.push_back(evicted);
+    place_miss(a, e, now, false);
     a->stats.misses++;
-    a->stats.fills++;
-    a->stats.h2d_bytes += a->blob_bytes;
   }
   for (int i = 0; i < n; ++i) slots[i] = a->slot_of[ids[i]];
-  for (size_t i = 0; i < a->last_fills.size(); ++i) fills[i] = a->last_fills[i];
-  *n_fills = (int)a->last_fills.size();
+  copy_fills(a, fills, n_fills);
+  return MOE_OK;
+}
+
+extern "C" int arena_prefetch(moe_arena* a, const int32_t* ids, int n, moe_fill* fills, int* n_fills) {
+  if (!a || n < 0 || (n > 0 && (!ids || !fills)) || !n_fills) return MOE_EINVAL;
+  std::vector<int32_t> distinct;
+  const int rc = distinct_ids(a, ids, n, distinct);
+  if (rc != MOE_OK) return rc;
+  const uint64_t now = ++a->calls;
+  a->last_fills.clear();
+  a->last_evicted.clear();
+  for (int e : distinct)
+    if (a->slot_of[e] < 0) {  // a resident prediction is left as it is
+      place_miss(a, e, now, true);
+      a->stats.prefetch_fills++;
+    }
+  copy_fills(a, fills, n_fills);
   return MOE_OK;
 }
 

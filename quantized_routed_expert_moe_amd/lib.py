@@ -55,6 +55,7 @@ EXPORTS = (
     "arena_stats",
     "arena_destroy",
     "arena_chunk_passes",
+    "arena_prefetch",
 )
 
 
@@ -69,7 +70,8 @@ class moe_fill(ctypes.Structure):
 
 
 class moe_arena_stats(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_uint64) for n in ("hits", "misses", "evictions", "fills", "h2d_bytes")]
+    _fields_ = [(n, ctypes.c_uint64)
+                for n in ("hits", "misses", "evictions", "fills", "h2d_bytes", "prefetch_fills", "prefetch_hits")]
 
 
 _lib = None
@@ -132,6 +134,7 @@ def load(path: str | None = None):
         "arena_stats": (_I, [_P, ctypes.POINTER(moe_arena_stats)]),
         "arena_destroy": (None, [_P]),
         "arena_chunk_passes": (_I, [_P, _P, _I, _I, _P, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+        "arena_prefetch": (_I, [_P, _P, _I, _P, ctypes.POINTER(_I)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -345,8 +348,27 @@ class Arena:
         nf = _I(0)
         return load().arena_map_slots(self.handle, arr, n, slots, fills, ctypes.byref(nf))
 
+    def prefetch(self, ids):
+        """Read-ahead of predicted ids (host int sequence) -> fills list of (expert, slot)."""
+        n = len(ids)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in ids])
+        fills = (moe_fill * max(n, 1))()
+        nf = _I(0)
+        _check(load().arena_prefetch(self.handle, arr, n, fills, ctypes.byref(nf)), "arena_prefetch")
+        self._last_fills = fills
+        self._last_nf = nf.value
+        return [(fills[i].expert, fills[i].slot) for i in range(nf.value)]
+
+    def prefetch_status(self, ids) -> int:
+        """Like prefetch but returns the raw status instead of raising."""
+        n = len(ids)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in ids])
+        fills = (moe_fill * max(n, 1))()
+        nf = _I(0)
+        return load().arena_prefetch(self.handle, arr, n, fills, ctypes.byref(nf))
+
     def fill_async(self, side=None, done=None) -> None:
-        """Enqueue the fills of the last map_slots call on ``side``; record ``done``."""
+        """Enqueue the fills of the last map_slots or prefetch call on ``side``; record ``done``."""
         _check(
             load().arena_fill_async(self.handle, self._last_fills, self._last_nf, _stream(side), _event(done)),
             "arena_fill_async",

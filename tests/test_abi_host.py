@@ -130,6 +130,47 @@ def test_arena_cpp_locality_stream():
             run_both(256, S, stream)
 
 
+def test_arena_cpp_prefetch_matches_model():
+    """arena_prefetch interleaved with arena_map_slots: the same fills, slots, statuses and
+    stats as the model, on random streams and on a next-layer prediction stream."""
+    rng = np.random.default_rng(6)
+    for E, S, n in ((16, 4, 4), (256, 64, 8), (8, 8, 8), (40, 6, 7)):
+        a = lib.Arena(E, S, 100, 4096)
+        m = ArenaModel(E, S, 100)
+        for i in range(500):
+            ids = rng.integers(0, E, size=int(rng.integers(1, n + 1))).tolist()
+            if i % 97 == 5:
+                ids = ids + [E if i % 2 else -1]  # invalid id
+            if rng.random() < 0.5:
+                st_m, fills_m = m.prefetch(ids)
+                if st_m != 0:
+                    assert a.prefetch_status(ids) == st_m, ids
+                    continue
+                assert a.prefetch(ids) == fills_m, ids
+            else:
+                st_m, slots_m, fills_m = m.map_slots(ids)
+                if st_m != 0:
+                    assert a.map_slots_status(ids) == st_m, ids
+                    continue
+                assert a.map_slots(ids) == (slots_m, fills_m), ids
+            assert a.slot_table() == m.slot_of
+        assert a.stats() == m.stats
+    # the read-ahead decode pattern: demand at one layer, prediction for the next
+    lg = gen.locality_logits(5, 3, 48, 256, 6)
+    arenas = [(lib.Arena(256, 64, 100, 4096), ArenaModel(256, 64, 100)) for _ in range(3)]
+    for s in range(48):
+        for layer in range(3):
+            ids = np.argsort(-lg[s, layer], kind="stable")[:6].tolist()
+            a, m = arenas[layer]
+            assert a.map_slots(ids) == m.map_slots(ids)[1:]
+            if layer + 1 < 3 and s + 1 < 48:
+                pred = np.argsort(-lg[s + 1, layer + 1], kind="stable")[:6].tolist()
+                a, m = arenas[layer + 1]
+                assert a.prefetch(pred) == m.prefetch(pred)[1]
+    for a, m in arenas:
+        assert a.stats() == m.stats and a.slot_table() == m.slot_of
+
+
 def test_arena_place_reset_and_errors():
     a = lib.Arena(10, 4, 100, 4096)
     a.place(7, 2)

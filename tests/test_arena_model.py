@@ -135,3 +135,107 @@ def test_chunk_passes_run_reads_each_missing_expert_once():
                 prev = p
             assert sorted(filled) == sorted(set(ids) - resident)
             check_consistent(a)
+
+
+def load_prefetch_sequence():
+    steps, stats = [], None
+    with open(os.path.join(GOLDEN, "arena_prefetch_sequence.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            if line.startswith("stats"):
+                stats = [int(v) for v in line.split()[1:]]
+                continue
+            op, req, st, slots, fills = [p.strip() for p in line.split("|")]
+            steps.append(
+                (
+                    op,
+                    [int(v) for v in req.split()],
+                    int(st),
+                    None if slots == "-" else [int(v) for v in slots.split()],
+                    [] if fills == "-" else [tuple(int(v) for v in f.split(":")) for f in fills.split()],
+                )
+            )
+    return steps, stats
+
+
+def test_prefetch_hand_worked_sequence():
+    steps, stats = load_prefetch_sequence()
+    a = ArenaModel(E=8, S=3, blob_bytes=100)
+    for op, req, st, slots, fills in steps:
+        if op == "map":
+            got_st, got_slots, got_fills = a.map_slots(req)
+            if st == OK:
+                assert got_slots == slots, req
+        else:
+            got_st, got_fills = a.prefetch(req)
+        assert got_st == st, (op, req)
+        if st == OK:
+            assert got_fills == fills, (op, req)
+    keys = ("hits", "misses", "evictions", "fills", "prefetch_fills", "prefetch_hits")
+    assert [a.stats[k] for k in keys] == stats
+    assert a.stats["h2d_bytes"] == 100 * stats[3]
+
+
+def test_prefetch_invariants_random_stream():
+    rng = np.random.default_rng(7)
+    for E, S, n in ((16, 4, 3), (256, 64, 6), (8, 8, 8), (32, 5, 5)):
+        a = ArenaModel(E, S)
+        demand_distinct = 0
+        for _ in range(400):
+            ids = rng.integers(0, E, size=int(rng.integers(1, n + 1))).tolist()
+            distinct = list(dict.fromkeys(ids))
+            before, stamps, st0 = list(a.expert_in), list(a.stamp), dict(a.stats)
+            if rng.random() < 0.5:
+                st, fills = a.prefetch(ids)
+                if len(distinct) > S:
+                    assert st == ENOSLOT and a.expert_in == before and a.stats == st0
+                    continue
+                assert st == OK
+                missing = [e for e in distinct if e not in before]
+                assert [f[0] for f in fills] == missing  # fills: the predicted experts not resident
+                for e, s in fills:
+                    assert before[s] == -1 or before[s] not in distinct
+                for e in distinct:
+                    if e in before:  # a resident prediction keeps its slot and its stamp
+                        s = before.index(e)
+                        assert a.expert_in[s] == e and a.stamp[s] == stamps[s]
+                assert a.stats["hits"] == st0["hits"] and a.stats["misses"] == st0["misses"]
+                assert a.stats["prefetch_fills"] == st0["prefetch_fills"] + len(fills)
+                # the same ids requested now: all hits, one prefetch hit per prefetched expert
+                if rng.random() < 0.5:
+                    pf = sum(1 for e in distinct if a.by_prefetch[a.slot_of[e]])
+                    st, slots, fills2 = a.map_slots(ids)
+                    assert st == OK and fills2 == []
+                    assert a.stats["prefetch_hits"] == st0["prefetch_hits"] + pf
+                    demand_distinct += len(distinct)
+            else:
+                st, slots, fills = a.map_slots(ids)
+                if len(distinct) > S:
+                    assert st == ENOSLOT and a.expert_in == before
+                    continue
+                demand_distinct += len(distinct)
+                for e, s in zip(ids, slots):
+                    assert a.expert_in[s] == e
+            check_consistent(a)
+        assert a.stats["hits"] + a.stats["misses"] == demand_distinct
+        assert a.stats["fills"] == a.stats["misses"] + a.stats["prefetch_fills"]
+        assert a.stats["prefetch_hits"] <= a.stats["prefetch_fills"]
+
+
+def test_prefetch_changes_no_demand_result():
+    # the slots a demand stream reports always hold the requested experts, with or
+    # without read-ahead (of the true next request, of a wrong one, or of nothing)
+    rng = np.random.default_rng(8)
+    E, S, K = 64, 12, 4
+    stream = [rng.choice(E, size=K, replace=False).tolist() for _ in range(200)]
+    for mode in ("none", "exact", "wrong"):
+        a = ArenaModel(E, S)
+        for i, ids in enumerate(stream):
+            st, slots, fills = a.map_slots(ids)
+            assert st == OK and [a.expert_in[s] for s in slots] == ids
+            if i + 1 < len(stream) and mode != "none":
+                nxt = stream[i + 1] if mode == "exact" else rng.choice(E, size=K, replace=False).tolist()
+                assert a.prefetch(nxt)[0] == OK
+        if mode == "exact":  # every demand after the first is then a hit
+            assert a.stats["misses"] == K and a.stats["prefetch_hits"] == a.stats["prefetch_fills"]
