@@ -36,10 +36,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=48)
-    p.add_argument("--legs", default="decode,prefill,batched,paged,route_variants,chunked,formats",
-                   help="comma list of decode,prefill,batched,paged,route_variants,chunked,formats")
+    p.add_argument("--legs", default="decode,prefill,batched,paged,readahead,route_variants,chunked,formats",
+                   help="comma list of decode,prefill,batched,paged,readahead,route_variants,chunked,formats")
     p.add_argument("--chunks", default="1024,2048,4096", help="prompt chunk sizes of the chunked paged prefill leg")
     p.add_argument("--paged-steps", type=int, default=64, help="measured tokens of the paged decode workload")
+    p.add_argument("--readahead", default="2,3,4,6", help="experts read ahead per layer in the read-ahead leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=3, help="decode layers in the oracle's timed sample")
     p.add_argument("--graph", type=int, default=1, help="replay the decode layer stack as a HIP graph")
@@ -498,6 +499,97 @@ def paged_leg(a, dev):
     }
 
 
+def readahead_leg(a, dev):
+    """Paged single-token decode through 43 layers routed by per-layer router GEMVs on a
+    residual stream, without and with next-layer read-ahead (paged.PagedDecode).
+
+    The paged shape (256 experts + a shared one, top-6, I 2048, 64 slots per layer);
+    the layers draw misses from one pinned host copy of one 256-expert weight set (arena
+    keys stay per layer, so every miss is a real 14 MB copy); each layer has its own
+    router. The layer inputs follow gen.residual_stream (a 0.99 between tokens, rho 0.15
+    between layers). Read-ahead predicts layer l + 1's top-6 with its router on layer
+    l's input. Both modes run the same tokens from empty arenas; 16 warm-up tokens.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    from quantized_routed_expert_moe_amd import harness, lib, paged
+    from synth import gen
+
+    w = gen.WORKLOADS["readahead_t1_h4096_e256s1_k6_i2048_x43"]
+    warm = 16
+    steps = warm + a.paged_steps
+    stride = lib.moe_slot_stride(w.H, w.I)
+    blob = lib.moe_blob_bytes(w.H, w.I)
+    log(f"read-ahead: packing {w.E} experts into pinned host memory ({w.E * stride / 2**30:.1f} GiB)")
+    host = torch.empty(w.E * stride, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy()
+
+    def put(e):
+        hv[e * stride : (e + 1) * stride] = harness.pack_expert(w.seed, 0, e, w.H, w.I)
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(put, range(w.E)))
+    shared = torch.from_numpy(harness.pack_expert(w.seed, 0, gen.SHARED_EXPERT, w.H, w.I)).to(dev)
+    resident = host.to(dev)
+    resident_table = torch.arange(w.E, dtype=torch.int32, device=dev)
+    routers = [torch.from_numpy(gen.router_weight(w.seed, l, w.E, w.H)).to(dev) for l in range(w.layers)]
+    xs_all = torch.from_numpy(gen.residual_stream(w.seed, steps + 1, w.layers, w.H).view("int16")).to(dev)
+    xs_all = xs_all.view(torch.bfloat16)  # [steps + 1, layers, H]
+    layers = []
+    for l in range(w.layers):
+        sl = torch.empty(w.slots * stride, dtype=torch.uint8, device=dev)
+        tb = torch.full((w.E,), -1, dtype=torch.int32, device=dev)
+        layers.append((lib.Arena(w.E, w.slots, blob, stride, sl, tb, host), sl, tb))
+    ys = [torch.empty(1, w.H, dtype=torch.bfloat16, device=dev) for _ in range(w.layers)]
+    y_res = torch.empty(1, w.H, dtype=torch.bfloat16, device=dev)
+    out = {}
+    for P in [0] + [int(v) for v in a.readahead.split(",") if v]:
+        mode = f"next_layer_top{P}" if P else "off"
+        for ar, _, tb in layers:
+            ar.reset()
+            tb.fill_(-1)
+        dec = paged.PagedDecode(layers, routers, stride, w.H, w.I, w.E, w.K, shared=[shared] * w.layers,
+                                predict=P, device=dev)
+        for t in range(warm):
+            dec.token([xs_all[t, l][None, :] for l in range(w.layers)], ys)
+        torch.cuda.synchronize()
+        st0 = [ar.stats() for ar, _, _ in layers]
+        t0 = time.perf_counter()
+        for t in range(warm, steps):
+            dec.token([xs_all[t, l][None, :] for l in range(w.layers)], ys)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        st1 = [ar.stats() for ar, _, _ in layers]
+        if int(dec.status.item()) != 0:
+            raise RuntimeError(f"device status {int(dec.status.item())}")
+        d = {k: sum(b[k] - a_[k] for a_, b in zip(st0, st1)) for k in st0[0]}
+        identical = True  # one more token, each layer against the fully-resident run
+        for l in range(w.layers):
+            x = xs_all[steps, l][None, :]
+            dec.layer(l, x, ys[l])
+            lib.moe_expert_ffn(x, dec.ids, dec.wts, 1, w.H, w.I, w.E, w.K, 32, resident_table, resident, stride,
+                               shared, y_res, dec.ws, dec.ws_bytes, dec.status)
+            torch.cuda.synchronize()
+            identical = identical and torch.equal(ys[l].view(torch.int16), y_res.view(torch.int16))
+        n_tok, n_lay = steps - warm, (steps - warm) * w.layers
+        out[mode] = {
+            "tokens_per_s": round(n_tok / dt, 2),
+            "ms_per_token": round(dt * 1e3 / n_tok, 3),
+            "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"]), 4),
+            "demand_misses_per_layer_step": round(d["misses"] / n_lay, 3),
+            "prefetch_fills_per_layer_step": round(d["prefetch_fills"] / n_lay, 3),
+            "prefetch_precision": round(d["prefetch_hits"] / d["prefetch_fills"], 4) if d["prefetch_fills"] else None,
+            "copies_per_layer_step": round(d["fills"] / n_lay, 3),
+            "h2d_gbs": round(d["h2d_bytes"] / dt / 1e9, 2),
+            "bit_identical_to_resident": identical,
+        }
+        log(f"  read-ahead {mode}: {out[mode]}")
+    out["speedup"] = {m: round(v["tokens_per_s"] / out["off"]["tokens_per_s"], 4) for m, v in out.items() if m != "off"}
+    return w, out
+
+
 def pinned_expert_copy(w, layer):
     """All E experts of a layer packed into one pinned, expert-major host buffer."""
     from concurrent.futures import ThreadPoolExecutor
@@ -820,6 +912,11 @@ def main():
             "bit_identical_to_resident": q["identical"],
             "host_weight_sets": 1,
         }
+    if "readahead" in legs:
+        torch.cuda.empty_cache()
+        wr, r = readahead_leg(a, dev)
+        out["workloads"]["readahead_paged"] = {"workload": wr.name, "predictor": "next layer's router on this "
+                                               "layer's input, top-P", "residual_stream": {"a": 0.99, "rho": 0.15}} | r
     if "formats" in legs:
         out["workloads"]["formats"] = {"workload": "decode_t1_h4096_e256_k8_i1536 expert FFN per weight format",
                                        "by_format": formats_leg(dev)}

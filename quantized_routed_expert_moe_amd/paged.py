@@ -1,4 +1,6 @@
-"""Chunked paged prefill: one MoE layer over a prompt whose chunks use more experts than the arena holds.
+"""Paged runs whose experts do not all fit in device memory: chunked prefill and read-ahead decode.
+
+ChunkedPrefill: one MoE layer over a prompt whose chunks use more experts than the arena holds.
 
 "Strata on a Mac", Measured (the UD-Q4/Q5/Q6_K_XL part): prompts stream in
 chunks, and each chunk makes one pass over the experts it uses that are not in
@@ -18,7 +20,29 @@ compute stream and one side stream:
 With ``cap <= S / 2`` the fills of pass p + 1 evict nothing pass p reads, so
 they wait only for pass p - 1 and overlap pass p's compute; with a larger cap
 they wait for pass p. The outputs are bit-identical to the fully-resident
-grouped run of the same chunk. This module only sequences library calls.
+grouped run of the same chunk.
+
+PagedDecode: single-token decode through a stack of layers, each with its own
+arena, with read-ahead ("Strata on a Mac", What you need: the experts the next
+layer will probably use are read ahead). Per layer l:
+
+1. ``moe_route`` of x_l with layer l's router; with read-ahead, also the top-P
+   of layer l + 1's router on the same x_l (the prediction: a residual stream
+   changes little from one layer to the next);
+2. the ids (and the prediction) to the host, the one hand-shake per layer;
+3. ``arena_map_slots`` and ``arena_fill_async`` of the misses on the side
+   stream, recording this layer's event;
+4. ``arena_prefetch`` of the prediction into layer l + 1's arena and its fills
+   on the side stream, after this layer's (so they never delay them);
+5. the compute stream waits on the event, then ``moe_expert_ffn``.
+
+The hand-shake has drained every earlier compute launch, so no GPU work still
+reads a slot that the map or the prefetch may evict. Layer l + 1's event is
+recorded after its prefetched copies on the same side stream, so its FFN never
+reads a slot before its bytes have landed. A prediction only moves copies
+earlier: every output equals the run without read-ahead, bit for bit ("Strata"
+README: a predictor never changes what is computed). This module only
+sequences library calls.
 """
 
 from __future__ import annotations
@@ -100,4 +124,76 @@ class ChunkedPrefill:
         for t0 in range(0, x.shape[0], chunk):
             t1 = min(t0 + chunk, x.shape[0])
             self.run_chunk(x[t0:t1], logits[t0:t1], y[t0:t1], w_router)
+
+
+class PagedDecode:
+    """Single-token decode through per-layer arenas, optionally reading the next layer ahead.
+
+    ``layers``: per layer ``(arena, slots, table)`` (a ``lib.Arena``, its device
+    slot buffer and device slot table). ``routers``: per layer, device fp32
+    ``[E, H]``. ``shared``: per layer a device blob of the shared expert, or None.
+    ``predict``: experts read ahead per layer (0: none). ``predictors``: per layer,
+    the device fp32 ``[E, H]`` matrix applied to the previous layer's input to
+    predict this layer's experts (default: the layer's own router).
+    """
+
+    def __init__(self, layers, routers, stride: int, H: int, I: int, E: int, K: int, shared=None,
+                 predict: int = 0, g: int = 32, device="cuda", predictors=None):
+        if len(routers) != len(layers) or (predictors is not None and len(predictors) != len(layers)):
+            raise ValueError("one router (and one predictor) per layer")
+        if not 0 <= predict <= min(E, layers[0][0].S):
+            raise ValueError("predict must be in [0, min(E, S)]")
+        self.layers, self.routers, self.stride = layers, routers, stride
+        self.predictors = predictors if predictors is not None else routers
+        self.H, self.I, self.E, self.K, self.g, self.predict = H, I, E, K, g, predict
+        self.shared = shared if shared is not None else [None] * len(layers)
+        self.logits = torch.empty(1, E, dtype=torch.float32, device=device)
+        self.ids = torch.empty(1, K, dtype=torch.int32, device=device)
+        self.wts = torch.empty(1, K, dtype=torch.float32, device=device)
+        P = max(predict, 1)
+        self.p_logits = torch.empty(1, E, dtype=torch.float32, device=device)
+        self.p_ids = torch.empty(1, P, dtype=torch.int32, device=device)
+        self.p_wts = torch.empty(1, P, dtype=torch.float32, device=device)
+        self.ids_h = torch.empty(K + P, dtype=torch.int32, pin_memory=True)
+        has_shared = any(b is not None for b in self.shared)
+        self.ws_bytes = lib.moe_ffn_workspace_bytes(1, H, I, E, K, has_shared)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.side = torch.cuda.Stream(device=device)
+        self.done = torch.cuda.Event()
+        self.done.record(self.side)  # creates the HIP event
+        torch.cuda.synchronize(device)
+        self.log: list | None = None  # (op, layer, ids) of every arena call when a list
+
+    def layer(self, l: int, x: torch.Tensor, y: torch.Tensor) -> None:
+        """x bf16 [1, H]: layer l's input; y bf16 [1, H] out."""
+        H, E, K, P = self.H, self.E, self.K, self.predict
+        comp = torch.cuda.current_stream()
+        arena, slots, table = self.layers[l]
+        lib.moe_route(x, self.routers[l], self.logits, 1, H, E, K, 0, self.ids, self.wts, comp)
+        self.ids_h[:K].copy_(self.ids.view(-1), non_blocking=True)
+        ahead = P > 0 and l + 1 < len(self.layers)
+        if ahead:
+            lib.moe_route(x, self.predictors[l + 1], self.p_logits, 1, H, E, P, 0, self.p_ids, self.p_wts, comp)
+            self.ids_h[K : K + P].copy_(self.p_ids.view(-1), non_blocking=True)
+        comp.synchronize()  # the hand-shake; no earlier launch still reads any arena
+        ids = self.ids_h[:K].tolist()
+        arena.map_slots(ids)
+        arena.fill_async(self.side, self.done)
+        if self.log is not None:
+            self.log.append(("map", l, ids))
+        if ahead:
+            pred = self.ids_h[K : K + P].tolist()
+            self.layers[l + 1][0].prefetch(pred)
+            self.layers[l + 1][0].fill_async(self.side, None)
+            if self.log is not None:
+                self.log.append(("pre", l + 1, pred))
+        comp.wait_event(self.done)
+        lib.moe_expert_ffn(x, self.ids, self.wts, 1, H, self.I, E, K, self.g, table, slots, self.stride,
+                           self.shared[l], y, self.ws, self.ws_bytes, self.status, 0, comp)
+
+    def token(self, xs, ys) -> None:
+        """One token through every layer: xs[l] the inputs, ys[l] the outputs."""
+        for l in range(len(self.layers)):
+            self.layer(l, xs[l], ys[l])
 

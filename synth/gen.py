@@ -27,7 +27,7 @@ import dataclasses
 import numpy as np
 
 KIND_QG, KIND_QU, KIND_QD, KIND_SG, KIND_SU, KIND_SD = 0, 1, 2, 3, 4, 5
-KIND_ROUTER, KIND_X, KIND_LOGITS = 10, 11, 12
+KIND_ROUTER, KIND_X, KIND_LOGITS, KIND_STREAM = 10, 11, 12, 13
 SHARED_EXPERT = 1 << 20  # expert index used to seed the always-on shared expert
 
 
@@ -171,6 +171,30 @@ def locality_logits(seed: int, layers: int, steps: int, E: int, K: int, p_prev: 
     return out
 
 
+def residual_stream(seed: int, steps: int, layers: int, H: int, a: float = 0.99, rho: float = 0.15) -> np.ndarray:
+    """Layer inputs of a single-token decode, bf16 bits ``uint16 [steps, layers, H]``.
+
+    A stand-in for a model's residual stream (no trained weights exist here):
+    token t's first-layer input is b_t = a b_{t-1} + sqrt(1 - a^2) z (b_0 = z), and
+    each layer adds an update, x_{l+1} = (x_l + rho z') / sqrt(1 + rho^2), with z, z'
+    N(0, 1) in fp32. ``a`` sets how far consecutive tokens pick the same experts,
+    ``rho`` how far consecutive layers' inputs differ. Every vector is N(0, I).
+    """
+    rng = _rng(seed, 0, 0, KIND_STREAM)
+    out = np.empty((steps, layers, H), dtype=np.uint16)
+    b = rng.standard_normal(H, dtype=np.float32)
+    ca, cb = np.float32(a), np.float32(np.sqrt(1.0 - a * a))
+    cn = np.float32(1.0 / np.sqrt(1.0 + rho * rho))
+    for t in range(steps):
+        if t:
+            b = ca * b + cb * rng.standard_normal(H, dtype=np.float32)
+        x = b
+        for layer in range(layers):
+            out[t, layer] = bf16_bits_from_f32(x)
+            x = (x + np.float32(rho) * rng.standard_normal(H, dtype=np.float32)) * cn
+    return out
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     """Shape and input recipe of one synthetic MoE-layer workload."""
@@ -183,7 +207,8 @@ class Workload:
     I: int  # expert FFN intermediate size
     layers: int
     slots: int  # arena slots per layer
-    router: str  # "gemv" (x @ Wr^T), "normal", "zipf" or "locality" (logits supplied)
+    router: str  # "gemv" (x @ Wr^T), "normal", "zipf" or "locality" (logits supplied), or
+    # "residual" (x @ Wr^T on the layer inputs of residual_stream, one router per layer)
     seed: int
     shared: bool = False  # one always-on shared expert (weight 1)
     g: int = 32
@@ -199,5 +224,9 @@ WORKLOADS = {
         Workload("paged_t1_h4096_e256s1_k6_i2048_x43", 1, 4096, 256, 6, 2048, 43, 64, "locality", 5, shared=True),
         # a 4K prompt through one layer of the paged shape, streamed in chunks through the 64-slot arena
         Workload("chunked_t4096_h4096_e256s1_k6_i2048", 4096, 4096, 256, 6, 2048, 1, 64, "normal", 6, shared=True),
+        # the paged shape routed by per-layer router GEMVs on a residual stream: the next
+        # layer's router on this layer's input predicts what to read ahead
+        Workload("readahead_t1_h4096_e256s1_k6_i2048_x43", 1, 4096, 256, 6, 2048, 43, 64, "residual", 7,
+                 shared=True),
     )
 }

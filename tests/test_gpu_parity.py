@@ -818,3 +818,75 @@ def test_fmt_int4_g32_is_moe_expert_ffn():
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     assert torch.equal(run.y.view(torch.int16), y0)
+
+
+# ------------------------------------------------------------------ read-ahead decode
+
+
+@pytest.mark.parametrize("predict,wrong", [(0, False), (4, False), (8, False), (4, True)],
+                         ids=["off", "p4", "p8", "p4_wrong_predictor"])
+def test_readahead_paged_decode(predict, wrong):
+    """PagedDecode through 4 layers with 8-slot arenas, routed by per-layer router GEMVs on a
+    residual stream, reading ahead the next layer's top-P (from its router or from an unrelated
+    matrix): every layer's output bitwise equal to the fully-resident run, ids equal to the
+    oracle's selection on its own GEMV logits, the last token within the oracle's bar, and each
+    arena's stats equal to the slot-policy model replayed on the logged calls."""
+    from oracle.arena_ref import ArenaModel
+    from quantized_routed_expert_moe_amd import paged
+
+    w = gen.Workload("readahead_t1_h512_e32s1_k4_i256_x4", 1, 512, 32, 4, 256, 4, 8, "residual", 91, shared=True)
+    steps = 10
+    say(f"read-ahead decode predict={predict} wrong={wrong}")
+    xs_bits = gen.residual_stream(w.seed, steps, w.layers, w.H, a=0.9, rho=0.2)
+    stride, blob = lib.moe_slot_stride(w.H, w.I), lib.moe_blob_bytes(w.H, w.I)
+    layers, routers, preds, shared, resident = [], [], [], [], []
+    for l in range(w.layers):
+        host = torch.empty(w.E * stride, dtype=torch.uint8, pin_memory=True)
+        for e in range(w.E):
+            host[e * stride : e * stride + blob].copy_(torch.from_numpy(harness.pack_expert(w.seed, l, e, w.H, w.I)))
+        slots = torch.empty(w.slots * stride, dtype=torch.uint8, device=DEV)
+        table = torch.full((w.E,), -1, dtype=torch.int32, device=DEV)
+        layers.append((lib.Arena(w.E, w.slots, blob, stride, slots, table, host), slots, table))
+        routers.append(torch.from_numpy(gen.router_weight(w.seed, l, w.E, w.H)).to(DEV))
+        preds.append(torch.from_numpy(gen.router_weight(w.seed + 1000, l, w.E, w.H)).to(DEV) if wrong else routers[-1])
+        shared.append(torch.from_numpy(harness.pack_expert(w.seed, l, gen.SHARED_EXPERT, w.H, w.I)).to(DEV))
+        resident.append((host.to(DEV), torch.arange(w.E, dtype=torch.int32, device=DEV)))
+    dec = paged.PagedDecode(layers, routers, stride, w.H, w.I, w.E, w.K, shared=shared, predict=predict,
+                            device=DEV, predictors=preds)
+    dec.log = []
+    y = torch.empty(1, w.H, dtype=torch.bfloat16, device=DEV)
+    y_res = torch.empty_like(y)
+    ws2 = torch.empty_like(dec.ws)
+    for t in range(steps):
+        for l in range(w.layers):
+            x = harness.bf16_tensor(xs_bits[t, l][None, :], DEV)
+            dec.layer(l, x, y)
+            lib.moe_expert_ffn(x, dec.ids, dec.wts, 1, w.H, w.I, w.E, w.K, 32, resident[l][1], resident[l][0], stride,
+                               shared[l], y_res, ws2, dec.ws_bytes, dec.status)
+            torch.cuda.synchronize()
+            assert int(dec.status.item()) == 0
+            assert torch.equal(y.view(torch.int16), y_res.view(torch.int16)), (t, l)
+            wr = gen.router_weight(w.seed, l, w.E, w.H)
+            ids_ref, _ = R.route(R.router_logits(xs_bits[t, l][None, :], wr), w.K)
+            assert np.array_equal(dec.ids.cpu().numpy(), ids_ref), (t, l)
+            if t == steps - 1:
+                sh = R.Expert(gen.expert_tensors(w.seed, l, gen.SHARED_EXPERT, w.H, w.I), w.H, w.I)
+                y_ref, _, _, _ = R.moe_layer(xs_bits[t, l][None, :], OracleExperts(w, l), w.K, w_router=wr, shared=sh)
+                check_close(y_f64(y), y_ref, f"  read-ahead layer {l}")
+    models = [ArenaModel(w.E, w.slots, blob) for _ in range(w.layers)]
+    for op, l, ids in dec.log:
+        if op == "map":
+            assert models[l].map_slots(ids)[0] == 0
+        else:
+            assert models[l].prefetch(ids)[0] == 0
+    for l in range(w.layers):
+        st = layers[l][0].stats()
+        assert st == models[l].stats, l
+        say(f"  layer {l}: {st}")
+    n_pre = sum(layers[l][0].stats()["prefetch_fills"] for l in range(w.layers))
+    if predict:
+        assert n_pre > 0 and sum(1 for op, _, _ in dec.log if op == "pre") == steps * (w.layers - 1)
+    else:
+        assert n_pre == 0
+    if predict and not wrong:
+        assert sum(layers[l][0].stats()["prefetch_hits"] for l in range(w.layers)) > 0
