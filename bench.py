@@ -508,7 +508,10 @@ def readahead_leg(a, dev):
     keys stay per layer, so every miss is a real 14 MB copy); each layer has its own
     router. The layer inputs follow gen.residual_stream (a 0.99 between tokens, rho 0.15
     between layers). Read-ahead predicts layer l + 1's top-6 with its router on layer
-    l's input. Both modes run the same tokens from empty arenas; 16 warm-up tokens.
+    l's input. Modes: "python_off" sequences each layer from Python (route, hand-shake,
+    map, fill, FFN); "off" and "next_layer_topP" are one moe_paged_layer call per layer
+    (native sequencing, speculative FFN), without and with read-ahead of P experts. Every
+    mode runs the same tokens from empty arenas; 16 warm-up tokens.
     """
     from concurrent.futures import ThreadPoolExecutor
 
@@ -545,13 +548,14 @@ def readahead_leg(a, dev):
     ys = [torch.empty(1, w.H, dtype=torch.bfloat16, device=dev) for _ in range(w.layers)]
     y_res = torch.empty(1, w.H, dtype=torch.bfloat16, device=dev)
     out = {}
-    for P in [0] + [int(v) for v in a.readahead.split(",") if v]:
-        mode = f"next_layer_top{P}" if P else "off"
+    modes = [("python_off", 0, False), ("off", 0, True)]
+    modes += [(f"next_layer_top{P}", P, True) for P in (int(v) for v in a.readahead.split(",") if v)]
+    for mode, P, native in modes:
         for ar, _, tb in layers:
             ar.reset()
             tb.fill_(-1)
         dec = paged.PagedDecode(layers, routers, stride, w.H, w.I, w.E, w.K, shared=[shared] * w.layers,
-                                predict=P, device=dev)
+                                predict=P, device=dev, native=native, speculate=native)
         for t in range(warm):
             dec.token([xs_all[t, l][None, :] for l in range(w.layers)], ys)
         torch.cuda.synchronize()
@@ -569,7 +573,8 @@ def readahead_leg(a, dev):
         for l in range(w.layers):
             x = xs_all[steps, l][None, :]
             dec.layer(l, x, ys[l])
-            lib.moe_expert_ffn(x, dec.ids, dec.wts, 1, w.H, w.I, w.E, w.K, 32, resident_table, resident, stride,
+            ids_d, wts_d = dec.routed
+            lib.moe_expert_ffn(x, ids_d, wts_d, 1, w.H, w.I, w.E, w.K, 32, resident_table, resident, stride,
                                shared, y_res, dec.ws, dec.ws_bytes, dec.status)
             torch.cuda.synchronize()
             identical = identical and torch.equal(ys[l].view(torch.int16), y_res.view(torch.int16))
@@ -586,7 +591,8 @@ def readahead_leg(a, dev):
             "bit_identical_to_resident": identical,
         }
         log(f"  read-ahead {mode}: {out[mode]}")
-    out["speedup"] = {m: round(v["tokens_per_s"] / out["off"]["tokens_per_s"], 4) for m, v in out.items() if m != "off"}
+    out["speedup_vs_off"] = {m: round(v["tokens_per_s"] / out["off"]["tokens_per_s"], 4) for m, v in out.items()
+                             if m != "off"}
     return w, out
 
 

@@ -345,6 +345,58 @@ int arena_slot_table(const moe_arena* a, int32_t* slot_of);
 int arena_reset(moe_arena* a); /* empty every slot, zero the stamps and the stats */
 int arena_stats(const moe_arena* a, moe_arena_stats* out);
 void arena_destroy(moe_arena* a);
+/* ------------------------------------------------------------------ paged decode layer
+ * One layer of single-token decode whose experts page through an arena, with
+ * the host hand-shake, the fills and the optional read-ahead sequenced in
+ * native code ("Strata on a Mac", What you need: the rest of the experts are
+ * read when a token needs them, and the ones the next layer will probably use
+ * are read ahead). Per call, on `stream` (compute) and `side` (copies):
+ *   1. moe_route(x, layer->w_router) -> ids[0..K), w[0..K); with read-ahead
+ *      (next, w_predict and P > 0) also the top-P of w_predict on the same x
+ *      -> ids[K..K+P), w[K..K+P) (logits is scratch for both);
+ *   2. the K (+ P) ids to ids_host, then hipEventRecord(ids_ready);
+ *   3. with MOE_PAGED_SPECULATE the expert FFN is enqueued at once, after the
+ *      last fills into layer->arena, with its status word in the workspace;
+ *   4. the host waits for ids_ready, arena_map_slots on the K ids, enqueues
+ *      the misses on `side` (arena_fill_async), then arena_prefetch of the P
+ *      predicted ids into next->arena and their fills, after the misses;
+ *   5. if the map missed any expert, or without MOE_PAGED_SPECULATE, `stream`
+ *      waits for this arena's fills and the expert FFN runs (again) with
+ *      dev_status.
+ * y (device bf16 [H]) then equals moe_expert_ffn on the fully-resident
+ * experts, bit for bit, speculation and prediction or not ("Strata" README,
+ * the execution model: a predictor changes only what is fetched and when).
+ *   layer, next   the arena (its device slots, slot table and pinned host
+ *                 source must be set), device fp32 router [E][H] and the
+ *                 shared expert's blob (or NULL); next may be NULL and its
+ *                 arena must differ from layer's;
+ *   w_predict     device fp32 [E][H] predicting next's experts from x, or NULL;
+ *   ids, w        device int32 / fp32, K + P entries; logits device fp32 [E];
+ *   ids_host      pinned host int32, K + P entries (the ids, readable on
+ *                 return);
+ *   ws            device, ws_bytes >= moe_paged_workspace_bytes();
+ *   ids_ready     a HIP event owned by the caller;
+ *   n_misses, n_prefetched  (host, may be NULL) the fills of the map and of
+ *                 the prefetch.
+ * The call returns after step 5 is enqueued (it blocks only on ids_ready).
+ * Calls for the layers of a token go in order on one compute stream; no other
+ * GPU work may read an arena while these calls run. Arena rules and errors as
+ * arena_map_slots / arena_prefetch / moe_expert_ffn; MOE_EINVAL also for an
+ * arena without device buffers, E other than the arena's, K or P larger than
+ * an arena, or next->arena == layer->arena; MOE_EWS for a short workspace. */
+typedef struct {
+  moe_arena* arena;
+  const float* w_router;   /* device fp32 [E][H] */
+  const void* shared_blob; /* device blob of the always-on shared expert, or NULL */
+} moe_paged_layer_t;
+#define MOE_PAGED_SPECULATE 1u
+size_t moe_paged_workspace_bytes(int H, int I, int E, int K, int has_shared); /* 0: unsupported shape */
+int moe_paged_layer(const moe_paged_layer_t* layer, const moe_paged_layer_t* next, const float* w_predict, int P,
+                    const uint16_t* x, int H, int I, int E, int K, int g, float* logits, int32_t* ids, float* w,
+                    int32_t* ids_host, uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
+                    moe_stream_t stream, moe_stream_t side, moe_event_t ids_ready, int* n_misses,
+                    int* n_prefetched);
+
 /* Passes of a chunked paged run (moe_ffn_combine): split the distinct experts
  * of n requested ids (host int32) into passes of at most max_per_pass experts.
  * The experts that are resident now come first (ascending id), then the

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["api.cpp", "pack.cpp", "arena.cpp", "route.hip", "ffn_gemv.hip", "ffn_batched.hip", "ffn_decode.hip",
+SOURCES = ["api.cpp", "pack.cpp", "arena.cpp", "paged.cpp", "route.hip", "ffn_gemv.hip", "ffn_batched.hip", "ffn_decode.hip",
            "ffn_grouped.hip", "ffn_formats.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

@@ -11,25 +11,7 @@
 #include <new>
 #include <vector>
 
-#include "moe_internal.h"
-
-struct moe_arena {
-  int E = 0, S = 0;
-  size_t blob_bytes = 0, stride = 0;
-  uint8_t* slots_dev = nullptr;
-  int32_t* table_dev = nullptr;
-  const uint8_t* host_src = nullptr;
-  std::vector<int32_t> slot_of;    // expert -> slot, -1 absent
-  std::vector<int32_t> expert_in;  // slot -> expert, -1 empty
-  std::vector<uint64_t> stamp;     // slot -> call number of last use
-  std::vector<uint8_t> prefetched; // slot -> filled by arena_prefetch, not requested since
-  std::vector<uint64_t> req_mark;  // expert -> call number that requested it
-  uint64_t calls = 0;
-  uint64_t marker = 0;             // distinct value per map call (also failed ones)
-  moe_arena_stats stats{};
-  std::vector<moe_fill> last_fills;
-  std::vector<int32_t> last_evicted;  // per last fill: evicted expert or -1
-};
+#include "arena_internal.h"
 
 extern "C" int arena_create(int E, int S, size_t blob_bytes, size_t stride, void* slots_dev,
                             int32_t* slot_table_dev, const void* host_src, moe_arena** out) {
@@ -53,7 +35,10 @@ extern "C" int arena_create(int E, int S, size_t blob_bytes, size_t stride, void
   return MOE_OK;
 }
 
-extern "C" void arena_destroy(moe_arena* a) { delete a; }
+extern "C" void arena_destroy(moe_arena* a) {
+  if (a && a->fill_event) (void)hipEventDestroy(a->fill_event);
+  delete a;
+}
 
 extern "C" int arena_reset(moe_arena* a) {
   if (!a) return MOE_EINVAL;
@@ -227,6 +212,13 @@ extern "C" int arena_fill_async(moe_arena* a, const moe_fill* fills, int n_fills
     return MOE_EHIP;
   a->last_fills.clear();
   a->last_evicted.clear();
+  if (n_fills > 0) {
+    if (!a->fill_event && hipEventCreateWithFlags(&a->fill_event, hipEventDisableTiming) != hipSuccess) {
+      a->fill_event = nullptr;
+      return MOE_EHIP;
+    }
+    if (hipEventRecord(a->fill_event, s) != hipSuccess) return MOE_EHIP;
+  }
   if (done && hipEventRecord(static_cast<hipEvent_t>(done), s) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }

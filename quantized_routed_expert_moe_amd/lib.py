@@ -56,6 +56,8 @@ EXPORTS = (
     "arena_destroy",
     "arena_chunk_passes",
     "arena_prefetch",
+    "moe_paged_workspace_bytes",
+    "moe_paged_layer",
 )
 
 
@@ -67,6 +69,13 @@ class MoeError(RuntimeError):
 
 class moe_fill(ctypes.Structure):
     _fields_ = [("expert", ctypes.c_int32), ("slot", ctypes.c_int32)]
+
+
+class moe_paged_layer_t(ctypes.Structure):
+    _fields_ = [("arena", ctypes.c_void_p), ("w_router", ctypes.c_void_p), ("shared_blob", ctypes.c_void_p)]
+
+
+MOE_PAGED_SPECULATE = 1
 
 
 class moe_arena_stats(ctypes.Structure):
@@ -135,6 +144,10 @@ def load(path: str | None = None):
         "arena_destroy": (None, [_P]),
         "arena_chunk_passes": (_I, [_P, _P, _I, _I, _P, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
         "arena_prefetch": (_I, [_P, _P, _I, _P, ctypes.POINTER(_I)]),
+        "moe_paged_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+        "moe_paged_layer": (_I, [ctypes.POINTER(moe_paged_layer_t), ctypes.POINTER(moe_paged_layer_t), _P, _I, _P, _I,
+                                 _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P, ctypes.c_uint, _P, _P, _P,
+                                 ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -310,6 +323,28 @@ def moe_expert_ffn_fmt(fmt, x, ids, w, T, H, I, E, K, slot_table, slots, stride,
         ),
         "moe_expert_ffn_fmt",
     )
+
+
+def moe_paged_workspace_bytes(H, I, E, K, has_shared) -> int:
+    return load().moe_paged_workspace_bytes(H, I, E, K, int(bool(has_shared)))
+
+
+def paged_layer_desc(arena, w_router, shared_blob=None) -> moe_paged_layer_t:
+    return moe_paged_layer_t(arena.handle, _ptr(w_router), _ptr(shared_blob))
+
+
+def moe_paged_layer(layer, next_layer, w_predict, P, x, H, I, E, K, g, logits, ids, w, ids_host, y, ws, ws_bytes,
+                    dev_status, flags, stream, side, ids_ready):
+    """layer, next_layer: moe_paged_layer_t (next_layer may be None). Returns (misses, prefetched)."""
+    nm, npf = _I(0), _I(0)
+    _check(
+        load().moe_paged_layer(ctypes.byref(layer), ctypes.byref(next_layer) if next_layer is not None else None,
+                               _ptr(w_predict), P, _ptr(x), H, I, E, K, g, _ptr(logits), _ptr(ids), _ptr(w),
+                               _ptr(ids_host), _ptr(y), _ptr(ws), ws_bytes, _ptr(dev_status), flags, _stream(stream),
+                               _stream(side), _event(ids_ready), ctypes.byref(nm), ctypes.byref(npf)),
+        "moe_paged_layer",
+    )
+    return nm.value, npf.value
 
 
 class Arena:

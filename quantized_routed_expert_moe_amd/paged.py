@@ -41,8 +41,12 @@ reads a slot that the map or the prefetch may evict. Layer l + 1's event is
 recorded after its prefetched copies on the same side stream, so its FFN never
 reads a slot before its bytes have landed. A prediction only moves copies
 earlier: every output equals the run without read-ahead, bit for bit ("Strata"
-README: a predictor never changes what is computed). This module only
-sequences library calls.
+README: a predictor never changes what is computed).
+
+With ``native=True`` (the default) each layer is one ``moe_paged_layer`` call,
+which runs the same steps in the library's C++ and, with ``speculate``, starts
+the FFN before the hand-shake and runs it again only when the layer missed.
+This module only sequences library calls.
 """
 
 from __future__ import annotations
@@ -138,7 +142,8 @@ class PagedDecode:
     """
 
     def __init__(self, layers, routers, stride: int, H: int, I: int, E: int, K: int, shared=None,
-                 predict: int = 0, g: int = 32, device="cuda", predictors=None):
+                 predict: int = 0, g: int = 32, device="cuda", predictors=None, native: bool = True,
+                 speculate: bool = True):
         if len(routers) != len(layers) or (predictors is not None and len(predictors) != len(layers)):
             raise ValueError("one router (and one predictor) per layer")
         if not 0 <= predict <= min(E, layers[0][0].S):
@@ -157,6 +162,14 @@ class PagedDecode:
         self.ids_h = torch.empty(K + P, dtype=torch.int32, pin_memory=True)
         has_shared = any(b is not None for b in self.shared)
         self.ws_bytes = lib.moe_ffn_workspace_bytes(1, H, I, E, K, has_shared)
+        self.native, self.speculate = native, speculate
+        if native:
+            self.ws_bytes = lib.moe_paged_workspace_bytes(H, I, E, K, has_shared)
+            self.nat_ids = torch.empty(K + P, dtype=torch.int32, device=device)
+            self.nat_w = torch.empty(K + P, dtype=torch.float32, device=device)
+            self.descs = [lib.paged_layer_desc(a, r, b) for (a, _, _), r, b in zip(layers, routers, self.shared)]
+            self.ids_ready = torch.cuda.Event()
+            self.ids_ready.record()  # creates the HIP event
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.side = torch.cuda.Stream(device=device)
@@ -167,6 +180,9 @@ class PagedDecode:
 
     def layer(self, l: int, x: torch.Tensor, y: torch.Tensor) -> None:
         """x bf16 [1, H]: layer l's input; y bf16 [1, H] out."""
+        if self.native:
+            self._layer_native(l, x, y)
+            return
         H, E, K, P = self.H, self.E, self.K, self.predict
         comp = torch.cuda.current_stream()
         arena, slots, table = self.layers[l]
@@ -191,6 +207,26 @@ class PagedDecode:
         comp.wait_event(self.done)
         lib.moe_expert_ffn(x, self.ids, self.wts, 1, H, self.I, E, K, self.g, table, slots, self.stride,
                            self.shared[l], y, self.ws, self.ws_bytes, self.status, 0, comp)
+
+    def _layer_native(self, l: int, x: torch.Tensor, y: torch.Tensor) -> None:
+        K, P = self.K, self.predict
+        ahead = P > 0 and l + 1 < len(self.layers)
+        lib.moe_paged_layer(self.descs[l], self.descs[l + 1] if ahead else None,
+                            self.predictors[l + 1] if ahead else None, P if ahead else 0, x, self.H, self.I, self.E,
+                            K, self.g, self.logits, self.nat_ids, self.nat_w, self.ids_h, y, self.ws, self.ws_bytes,
+                            self.status, lib.MOE_PAGED_SPECULATE if self.speculate else 0,
+                            torch.cuda.current_stream(), self.side, self.ids_ready)
+        if self.log is not None:
+            self.log.append(("map", l, self.ids_h[:K].tolist()))
+            if ahead:
+                self.log.append(("pre", l + 1, self.ids_h[K : K + P].tolist()))
+
+    @property
+    def routed(self):
+        """The last layer's ids and weights on the device ([1, K] each)."""
+        if self.native:
+            return self.nat_ids[: self.K].view(1, -1), self.nat_w[: self.K].view(1, -1)
+        return self.ids, self.wts
 
     def token(self, xs, ys) -> None:
         """One token through every layer: xs[l] the inputs, ys[l] the outputs."""

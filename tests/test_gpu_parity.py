@@ -823,20 +823,25 @@ def test_fmt_int4_g32_is_moe_expert_ffn():
 # ------------------------------------------------------------------ read-ahead decode
 
 
-@pytest.mark.parametrize("predict,wrong", [(0, False), (4, False), (8, False), (4, True)],
-                         ids=["off", "p4", "p8", "p4_wrong_predictor"])
-def test_readahead_paged_decode(predict, wrong):
+@pytest.mark.parametrize(
+    "predict,wrong,native,speculate",
+    [(0, False, False, False), (4, False, False, False), (0, False, True, True), (4, False, True, True),
+     (8, False, True, True), (4, False, True, False), (4, True, True, True), (4, True, False, False)],
+    ids=["py_off", "py_p4", "native_spec_off", "native_spec_p4", "native_spec_p8", "native_p4",
+         "native_spec_p4_wrong_predictor", "py_p4_wrong_predictor"])
+def test_readahead_paged_decode(predict, wrong, native, speculate):
     """PagedDecode through 4 layers with 8-slot arenas, routed by per-layer router GEMVs on a
     residual stream, reading ahead the next layer's top-P (from its router or from an unrelated
-    matrix): every layer's output bitwise equal to the fully-resident run, ids equal to the
-    oracle's selection on its own GEMV logits, the last token within the oracle's bar, and each
-    arena's stats equal to the slot-policy model replayed on the logged calls."""
+    matrix), sequenced in Python or by moe_paged_layer (with or without the speculative FFN):
+    every layer's output bitwise equal to the fully-resident run, ids equal to the oracle's
+    selection on its own GEMV logits, the last token within the oracle's bar, and each arena's
+    stats equal to the slot-policy model replayed on the logged calls."""
     from oracle.arena_ref import ArenaModel
     from quantized_routed_expert_moe_amd import paged
 
     w = gen.Workload("readahead_t1_h512_e32s1_k4_i256_x4", 1, 512, 32, 4, 256, 4, 8, "residual", 91, shared=True)
     steps = 10
-    say(f"read-ahead decode predict={predict} wrong={wrong}")
+    say(f"read-ahead decode predict={predict} wrong={wrong} native={native} speculate={speculate}")
     xs_bits = gen.residual_stream(w.seed, steps, w.layers, w.H, a=0.9, rho=0.2)
     stride, blob = lib.moe_slot_stride(w.H, w.I), lib.moe_blob_bytes(w.H, w.I)
     layers, routers, preds, shared, resident = [], [], [], [], []
@@ -852,7 +857,7 @@ def test_readahead_paged_decode(predict, wrong):
         shared.append(torch.from_numpy(harness.pack_expert(w.seed, l, gen.SHARED_EXPERT, w.H, w.I)).to(DEV))
         resident.append((host.to(DEV), torch.arange(w.E, dtype=torch.int32, device=DEV)))
     dec = paged.PagedDecode(layers, routers, stride, w.H, w.I, w.E, w.K, shared=shared, predict=predict,
-                            device=DEV, predictors=preds)
+                            device=DEV, predictors=preds, native=native, speculate=speculate)
     dec.log = []
     y = torch.empty(1, w.H, dtype=torch.bfloat16, device=DEV)
     y_res = torch.empty_like(y)
@@ -861,14 +866,15 @@ def test_readahead_paged_decode(predict, wrong):
         for l in range(w.layers):
             x = harness.bf16_tensor(xs_bits[t, l][None, :], DEV)
             dec.layer(l, x, y)
-            lib.moe_expert_ffn(x, dec.ids, dec.wts, 1, w.H, w.I, w.E, w.K, 32, resident[l][1], resident[l][0], stride,
+            ids_d, wts_d = dec.routed
+            lib.moe_expert_ffn(x, ids_d, wts_d, 1, w.H, w.I, w.E, w.K, 32, resident[l][1], resident[l][0], stride,
                                shared[l], y_res, ws2, dec.ws_bytes, dec.status)
             torch.cuda.synchronize()
             assert int(dec.status.item()) == 0
             assert torch.equal(y.view(torch.int16), y_res.view(torch.int16)), (t, l)
             wr = gen.router_weight(w.seed, l, w.E, w.H)
             ids_ref, _ = R.route(R.router_logits(xs_bits[t, l][None, :], wr), w.K)
-            assert np.array_equal(dec.ids.cpu().numpy(), ids_ref), (t, l)
+            assert np.array_equal(ids_d.cpu().numpy(), ids_ref), (t, l)
             if t == steps - 1:
                 sh = R.Expert(gen.expert_tensors(w.seed, l, gen.SHARED_EXPERT, w.H, w.I), w.H, w.I)
                 y_ref, _, _, _ = R.moe_layer(xs_bits[t, l][None, :], OracleExperts(w, l), w.K, w_router=wr, shared=sh)
@@ -890,3 +896,51 @@ def test_readahead_paged_decode(predict, wrong):
         assert n_pre == 0
     if predict and not wrong:
         assert sum(layers[l][0].stats()["prefetch_hits"] for l in range(w.layers)) > 0
+
+
+def test_paged_layer_argument_errors():
+    """moe_paged_layer rejects a bookkeeping-only arena, the next layer's arena equal to its
+    own, E other than the arena's, K above the slots, a short workspace and unknown flags,
+    before launching anything."""
+    H, I, E, K, S = 256, 128, 16, 4, 6
+    stride, blob = lib.moe_slot_stride(H, I), lib.moe_blob_bytes(H, I)
+    host = torch.zeros(E * stride, dtype=torch.uint8, pin_memory=True)
+
+    def arena():
+        sl = torch.zeros(S * stride, dtype=torch.uint8, device=DEV)
+        tb = torch.full((E,), -1, dtype=torch.int32, device=DEV)
+        return lib.Arena(E, S, blob, stride, sl, tb, host), sl, tb
+
+    (a0, _, _), (a1, _, _) = arena(), arena()
+    wr = torch.zeros(E, H, dtype=torch.float32, device=DEV)
+    d0, d1 = lib.paged_layer_desc(a0, wr), lib.paged_layer_desc(a1, wr)
+    x = torch.zeros(1, H, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty_like(x)
+    logits = torch.empty(E, dtype=torch.float32, device=DEV)
+    ids = torch.empty(2 * K, dtype=torch.int32, device=DEV)
+    wts = torch.empty(2 * K, dtype=torch.float32, device=DEV)
+    ids_h = torch.empty(2 * K, dtype=torch.int32, pin_memory=True)
+    nb = lib.moe_paged_workspace_bytes(H, I, E, K, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    side, ev = torch.cuda.Stream(), torch.cuda.Event()
+    ev.record()
+    torch.cuda.synchronize()
+
+    def call(layer=d0, nxt=d1, P=K, E_=E, K_=K, nbytes=nb, flags=lib.MOE_PAGED_SPECULATE):
+        with pytest.raises(lib.MoeError) as ex:
+            lib.moe_paged_layer(layer, nxt, wr, P, x, H, I, E_, K_, 32, logits, ids, wts, ids_h, y, ws, nbytes, st,
+                                flags, None, side, ev)
+        return ex.value.status
+
+    book = lib.Arena(E, S, blob, stride)  # no device buffers
+    assert call(layer=lib.paged_layer_desc(book, wr)) == lib.MOE_EINVAL
+    assert call(nxt=lib.paged_layer_desc(book, wr)) == lib.MOE_EINVAL
+    assert call(nxt=d0) == lib.MOE_EINVAL
+    assert call(E_=E + 1) == lib.MOE_EINVAL
+    assert call(K_=S + 1) == lib.MOE_EINVAL
+    assert call(P=S + 1) == lib.MOE_EINVAL
+    assert call(nbytes=nb - 1) == lib.MOE_EWS
+    assert call(flags=2) == lib.MOE_EINVAL
+    torch.cuda.synchronize()
+    assert a0.stats()["fills"] == 0 and a1.stats()["fills"] == 0 and int(st.item()) == 0
