@@ -399,14 +399,15 @@ def paged_leg(a, dev):
     layer and token: moe_route on logits with temporal locality, the ids come
     back to the host (the hand-shake), arena_map_slots, arena_fill_async on a
     side stream, the compute stream waits on its event, then moe_expert_ffn
-    (six routed experts plus the shared expert).
+    (six routed experts plus the shared expert). Timed twice from empty arenas on
+    the same tokens: sequenced from Python (paged.PagedDecode(native=False)) and
+    by moe_paged_layer with the speculative FFN (the reported rate).
     """
     from concurrent.futures import ThreadPoolExecutor
 
-    import numpy as np
     import torch
 
-    from quantized_routed_expert_moe_amd import harness, lib
+    from quantized_routed_expert_moe_amd import harness, lib, paged
     from synth import gen
 
     w = gen.WORKLOADS["paged_t1_h4096_e256s1_k6_i2048_x43"]
@@ -434,49 +435,40 @@ def paged_leg(a, dev):
     for l in range(w.layers):
         sl = torch.empty(w.slots * stride, dtype=torch.uint8, device=dev)
         tb = torch.full((w.E,), -1, dtype=torch.int32, device=dev)
-        layers.append((sl, tb, lib.Arena(w.E, w.slots, blob, stride, sl, tb, host)))
-    run = harness.LayerRunner(w, dev)
-    comp = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    done = torch.cuda.Event()
-    done.record(side)
-    ids_h = torch.empty(w.K, dtype=torch.int32, pin_memory=True)
-    y_res = torch.empty_like(run.y)
-
-    def layer_step(s, l, check=False):
-        sl, tb, ar = layers[l]
-        lib.moe_route(None, None, lg[s, l], 1, 0, w.E, w.K, 0, run.ids, run.wts)
-        ids_h.copy_(run.ids.view(-1), non_blocking=True)
-        comp.synchronize()  # hand-shake: the router's choice on the host
-        ar.map_slots(ids_h.tolist())
-        ar.fill_async(side, done)
-        comp.wait_event(done)
-        lib.moe_expert_ffn(xs[l], run.ids, run.wts, 1, w.H, w.I, w.E, w.K, 32, tb, sl, stride, shared, run.y,
-                           run.ws, run.ws_bytes, run.status)
-        if check:
-            lib.moe_expert_ffn(xs[l], run.ids, run.wts, 1, w.H, w.I, w.E, w.K, 32, resident_table, resident,
-                               stride, shared, y_res, run.ws, run.ws_bytes, run.status)
+        layers.append((lib.Arena(w.E, w.slots, blob, stride, sl, tb, host), sl, tb))
+    ys = [torch.empty(1, w.H, dtype=torch.bfloat16, device=dev) for _ in range(w.layers)]
+    y_res = torch.empty(1, w.H, dtype=torch.bfloat16, device=dev)
+    res = {}
+    for mode, native in (("python", False), ("native", True)):
+        for ar, _, tb in layers:
+            ar.reset()
+            tb.fill_(-1)
+        dec = paged.PagedDecode(layers, [None] * w.layers, stride, w.H, w.I, w.E, w.K, shared=[shared] * w.layers,
+                                device=dev, native=native, speculate=native)
+        lgs = [[lg[s, l] for l in range(w.layers)] for s in range(steps)]
+        for s in range(warm):
+            dec.token(xs, ys, lgs[s])
+        torch.cuda.synchronize()
+        st0 = [ar.stats() for ar, _, _ in layers]
+        t0 = time.perf_counter()
+        for s in range(warm, steps):
+            dec.token(xs, ys, lgs[s])
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        st1 = [ar.stats() for ar, _, _ in layers]
+        if int(dec.status.item()) != 0:
+            raise RuntimeError(f"device status {int(dec.status.item())}")
+        d = {k: sum(b[k] - a_[k] for a_, b in zip(st0, st1)) for k in st0[0]}
+        identical = True  # one more token, every layer's paged output against the fully-resident one
+        for l in range(w.layers):
+            dec.layer(l, xs[l], ys[l], lg[steps - 1, l])
+            ids_d, wts_d = dec.routed
+            lib.moe_expert_ffn(xs[l], ids_d, wts_d, 1, w.H, w.I, w.E, w.K, 32, resident_table, resident, stride,
+                               shared, y_res, dec.ws, dec.ws_bytes, dec.status)
             torch.cuda.synchronize()
-            return torch.equal(run.y.view(torch.int16), y_res.view(torch.int16))
-        return True
-
-    for s in range(warm):
-        for l in range(w.layers):
-            layer_step(s, l)
-    torch.cuda.synchronize()
-    st0 = [ar.stats() for _, _, ar in layers]
-    t0 = time.perf_counter()
-    for s in range(warm, steps):
-        for l in range(w.layers):
-            layer_step(s, l)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    st1 = [ar.stats() for _, _, ar in layers]
-    if int(run.status.item()) != 0:
-        raise RuntimeError(f"device status {int(run.status.item())}")
-    d = {k: sum(b[k] - a_[k] for a_, b in zip(st0, st1)) for k in st0[0]}
-    # fidelity: one more token, every layer's paged output against the fully-resident one
-    identical = all(layer_step(steps - 1, l, check=True) for l in range(w.layers))
+            identical = identical and torch.equal(ys[l].view(torch.int16), y_res.view(torch.int16))
+        res[mode] = (dt, d, identical)
+        log(f"  paged {mode}: {(steps - warm) / dt:.2f} tok/s")
     # pinned host -> device copy rate for context
     probe_dev = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     probe_host = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
@@ -488,6 +480,7 @@ def paged_leg(a, dev):
     torch.cuda.synchronize()
     h2d_peak = 3 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     n_tok = steps - warm
+    dt, d, identical = res["native"]
     return w, {
         "tok_s": n_tok / dt,
         "ms_per_token": dt * 1e3 / n_tok,
@@ -495,7 +488,8 @@ def paged_leg(a, dev):
         "misses_per_layer_step": d["misses"] / (n_tok * w.layers),
         "h2d_gbs": d["h2d_bytes"] / dt / 1e9,
         "h2d_peak_gbs": h2d_peak,
-        "identical": identical,
+        "identical": identical and res["python"][2],
+        "python_tok_s": n_tok / res["python"][0],
     }
 
 
@@ -917,6 +911,8 @@ def main():
             "h2d_pinned_copy_gbs": round(q["h2d_peak_gbs"], 2),
             "bit_identical_to_resident": q["identical"],
             "host_weight_sets": 1,
+            "sequencing": "moe_paged_layer (native, speculative FFN)",
+            "python_sequenced_tokens_per_s": round(q["python_tok_s"], 2),
         }
     if "readahead" in legs:
         torch.cuda.empty_cache()

@@ -351,9 +351,11 @@ void arena_destroy(moe_arena* a);
  * native code ("Strata on a Mac", What you need: the rest of the experts are
  * read when a token needs them, and the ones the next layer will probably use
  * are read ahead). Per call, on `stream` (compute) and `side` (copies):
- *   1. moe_route(x, layer->w_router) -> ids[0..K), w[0..K); with read-ahead
- *      (next, w_predict and P > 0) also the top-P of w_predict on the same x
- *      -> ids[K..K+P), w[K..K+P) (logits is scratch for both);
+ *   1. moe_route(x, layer->w_router) -> ids[0..K), w[0..K), or, when
+ *      layer->w_router is NULL, moe_route on the logits the caller put in
+ *      logits; with read-ahead (next, w_predict and P > 0) also the top-P of
+ *      w_predict on the same x -> ids[K..K+P), w[K..K+P) (which overwrites
+ *      logits);
  *   2. the K (+ P) ids to ids_host, then hipEventRecord(ids_ready);
  *   3. with MOE_PAGED_SPECULATE the expert FFN is enqueued at once, after the
  *      last fills into layer->arena, with its status word in the workspace;
@@ -386,7 +388,7 @@ void arena_destroy(moe_arena* a);
  * an arena, or next->arena == layer->arena; MOE_EWS for a short workspace. */
 typedef struct {
   moe_arena* arena;
-  const float* w_router;   /* device fp32 [E][H] */
+  const float* w_router;   /* device fp32 [E][H], or NULL: the caller supplies the logits */
   const void* shared_blob; /* device blob of the always-on shared expert, or NULL */
 } moe_paged_layer_t;
 #define MOE_PAGED_SPECULATE 1u

@@ -5,8 +5,9 @@
 // read ahead. Per call, on the compute stream `stream` and the copy stream
 // `side`:
 //
-//   1. moe_route of x with the layer's router (and, with read-ahead, the top-P
-//      of the predictor on the same x: the next layer's probable experts);
+//   1. moe_route of x with the layer's router, or on the caller's logits (and,
+//      with read-ahead, the top-P of the predictor on the same x: the next
+//      layer's probable experts);
 //   2. the ids to pinned host memory, event `ids_ready`;
 //   3. with MOE_PAGED_SPECULATE: the expert FFN is enqueued at once, after the
 //      last fills into this layer's arena, with its status word in the
@@ -52,8 +53,8 @@ extern "C" int moe_paged_layer(const moe_paged_layer_t* cur, const moe_paged_lay
                                int32_t* ids, float* w, int32_t* ids_host, uint16_t* y, void* ws, size_t ws_bytes,
                                int32_t* dev_status, unsigned flags, moe_stream_t stream, moe_stream_t side,
                                moe_event_t ids_ready, int* n_misses, int* n_prefetched) {
-  if (!cur || !arena_ready(cur->arena) || !cur->w_router || !x || !logits || !ids || !w || !ids_host || !y ||
-      !ws || !dev_status || !ids_ready)
+  if (!cur || !arena_ready(cur->arena) || !x || !logits || !ids || !w || !ids_host || !y || !ws || !dev_status ||
+      !ids_ready)
     return MOE_EINVAL;
   if (flags & ~(unsigned)MOE_PAGED_SPECULATE) return MOE_EINVAL;
   moe_arena* A = cur->arena;
@@ -71,7 +72,8 @@ extern "C" int moe_paged_layer(const moe_paged_layer_t* cur, const moe_paged_lay
   int32_t* spec_status = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + round256(ffn_ws));
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  int rc = moe_route(x, cur->w_router, logits, 1, H, E, K, 0, ids, w, stream);
+  // no router: logits already holds this layer's logits
+  int rc = moe_route(cur->w_router ? x : nullptr, cur->w_router, logits, 1, H, E, K, 0, ids, w, stream);
   if (rc != MOE_OK) return rc;
   const int n_ids = K + (ahead ? P : 0);
   if (ahead) {

@@ -135,7 +135,7 @@ class PagedDecode:
 
     ``layers``: per layer ``(arena, slots, table)`` (a ``lib.Arena``, its device
     slot buffer and device slot table). ``routers``: per layer, device fp32
-    ``[E, H]``. ``shared``: per layer a device blob of the shared expert, or None.
+    ``[E, H]``, or None when the caller passes the layer's logits to ``layer``. ``shared``: per layer a device blob of the shared expert, or None.
     ``predict``: experts read ahead per layer (0: none). ``predictors``: per layer,
     the device fp32 ``[E, H]`` matrix applied to the previous layer's input to
     predict this layer's experts (default: the layer's own router).
@@ -150,6 +150,8 @@ class PagedDecode:
             raise ValueError("predict must be in [0, min(E, S)]")
         self.layers, self.routers, self.stride = layers, routers, stride
         self.predictors = predictors if predictors is not None else routers
+        if predict and any(p is None for p in self.predictors[1:]):
+            raise ValueError("read-ahead needs a predictor for every layer after the first")
         self.H, self.I, self.E, self.K, self.g, self.predict = H, I, E, K, g, predict
         self.shared = shared if shared is not None else [None] * len(layers)
         self.logits = torch.empty(1, E, dtype=torch.float32, device=device)
@@ -178,15 +180,20 @@ class PagedDecode:
         torch.cuda.synchronize(device)
         self.log: list | None = None  # (op, layer, ids) of every arena call when a list
 
-    def layer(self, l: int, x: torch.Tensor, y: torch.Tensor) -> None:
-        """x bf16 [1, H]: layer l's input; y bf16 [1, H] out."""
+    def layer(self, l: int, x: torch.Tensor, y: torch.Tensor, logits: torch.Tensor | None = None) -> None:
+        """x bf16 [1, H]: layer l's input; y bf16 [1, H] out; logits fp32 [E]: layer l's
+        logits when it has no router (overwritten by a read-ahead prediction)."""
+        if (logits is None) != (self.routers[l] is not None):
+            raise ValueError("pass logits exactly when the layer has no router")
+        lg = self.logits if logits is None else logits.view(1, -1)
         if self.native:
-            self._layer_native(l, x, y)
+            self._layer_native(l, x, y, lg)
             return
         H, E, K, P = self.H, self.E, self.K, self.predict
         comp = torch.cuda.current_stream()
         arena, slots, table = self.layers[l]
-        lib.moe_route(x, self.routers[l], self.logits, 1, H, E, K, 0, self.ids, self.wts, comp)
+        router = self.routers[l]
+        lib.moe_route(x if router is not None else None, router, lg, 1, H, E, K, 0, self.ids, self.wts, comp)
         self.ids_h[:K].copy_(self.ids.view(-1), non_blocking=True)
         ahead = P > 0 and l + 1 < len(self.layers)
         if ahead:
@@ -208,12 +215,12 @@ class PagedDecode:
         lib.moe_expert_ffn(x, self.ids, self.wts, 1, H, self.I, E, K, self.g, table, slots, self.stride,
                            self.shared[l], y, self.ws, self.ws_bytes, self.status, 0, comp)
 
-    def _layer_native(self, l: int, x: torch.Tensor, y: torch.Tensor) -> None:
+    def _layer_native(self, l: int, x: torch.Tensor, y: torch.Tensor, lg: torch.Tensor) -> None:
         K, P = self.K, self.predict
         ahead = P > 0 and l + 1 < len(self.layers)
         lib.moe_paged_layer(self.descs[l], self.descs[l + 1] if ahead else None,
                             self.predictors[l + 1] if ahead else None, P if ahead else 0, x, self.H, self.I, self.E,
-                            K, self.g, self.logits, self.nat_ids, self.nat_w, self.ids_h, y, self.ws, self.ws_bytes,
+                            K, self.g, lg, self.nat_ids, self.nat_w, self.ids_h, y, self.ws, self.ws_bytes,
                             self.status, lib.MOE_PAGED_SPECULATE if self.speculate else 0,
                             torch.cuda.current_stream(), self.side, self.ids_ready)
         if self.log is not None:
@@ -228,8 +235,9 @@ class PagedDecode:
             return self.nat_ids[: self.K].view(1, -1), self.nat_w[: self.K].view(1, -1)
         return self.ids, self.wts
 
-    def token(self, xs, ys) -> None:
-        """One token through every layer: xs[l] the inputs, ys[l] the outputs."""
+    def token(self, xs, ys, logits=None) -> None:
+        """One token through every layer: xs[l] the inputs, ys[l] the outputs (logits[l]
+        the logits of the layers without a router)."""
         for l in range(len(self.layers)):
-            self.layer(l, xs[l], ys[l])
+            self.layer(l, xs[l], ys[l], None if logits is None else logits[l])
 

@@ -944,3 +944,51 @@ def test_paged_layer_argument_errors():
     assert call(flags=2) == lib.MOE_EINVAL
     torch.cuda.synchronize()
     assert a0.stats()["fills"] == 0 and a1.stats()["fills"] == 0 and int(st.item()) == 0
+
+
+@pytest.mark.parametrize("speculate", [False, True], ids=["wait", "speculate"])
+def test_paged_layer_logits_in_at_budget_top_k(speculate):
+    """moe_paged_layer on supplied logits (no router) through arenas of S = K slots, every map
+    a likely miss: each step bitwise equal to the fully-resident run, the stats equal to the
+    slot-policy model on the same ids."""
+    from oracle.arena_ref import ArenaModel
+    from quantized_routed_expert_moe_amd import paged
+
+    w = gen.Workload("paged_t1_h1024_e32s1_k4_i512_native", 1, 1024, 32, 4, 512, 2, 4, "locality", 42, shared=True)
+    steps = 20
+    say(f"paged layer, logits in, speculate={speculate}")
+    lg = torch.from_numpy(gen.locality_logits(w.seed, w.layers, steps, w.E, w.K)).to(DEV)
+    stride, blob = lib.moe_slot_stride(w.H, w.I), lib.moe_blob_bytes(w.H, w.I)
+    layers, shared, resident, xs = [], [], [], []
+    for l in range(w.layers):
+        host = torch.empty(w.E * stride, dtype=torch.uint8, pin_memory=True)
+        for e in range(w.E):
+            host[e * stride : e * stride + blob].copy_(torch.from_numpy(harness.pack_expert(w.seed, l, e, w.H, w.I)))
+        slots = torch.empty(w.slots * stride, dtype=torch.uint8, device=DEV)
+        table = torch.full((w.E,), -1, dtype=torch.int32, device=DEV)
+        layers.append((lib.Arena(w.E, w.slots, blob, stride, slots, table, host), slots, table))
+        shared.append(torch.from_numpy(harness.pack_expert(w.seed, l, gen.SHARED_EXPERT, w.H, w.I)).to(DEV))
+        resident.append((host.to(DEV), torch.arange(w.E, dtype=torch.int32, device=DEV)))
+        xs.append(harness.bf16_tensor(gen.activations_bf16(w.seed, l, 1, w.H), DEV))
+    dec = paged.PagedDecode(layers, [None] * w.layers, stride, w.H, w.I, w.E, w.K, shared=shared, device=DEV,
+                            native=True, speculate=speculate)
+    dec.log = []
+    y = torch.empty(1, w.H, dtype=torch.bfloat16, device=DEV)
+    y_res = torch.empty_like(y)
+    ws2 = torch.empty_like(dec.ws)
+    for s in range(steps):
+        for l in range(w.layers):
+            dec.layer(l, xs[l], y, lg[s, l])
+            ids_d, wts_d = dec.routed
+            lib.moe_expert_ffn(xs[l], ids_d, wts_d, 1, w.H, w.I, w.E, w.K, 32, resident[l][1], resident[l][0],
+                               stride, shared[l], y_res, ws2, dec.ws_bytes, dec.status)
+            torch.cuda.synchronize()
+            assert int(dec.status.item()) == 0
+            assert torch.equal(y.view(torch.int16), y_res.view(torch.int16)), (s, l)
+            assert ids_d.cpu().numpy().tolist()[0] == R.route(lg[s, l][None, :].cpu().numpy(), w.K)[0][0].tolist()
+    models = [ArenaModel(w.E, w.slots, blob) for _ in range(w.layers)]
+    for op, l, ids in dec.log:
+        assert op == "map" and models[l].map_slots(ids)[0] == 0
+    for l in range(w.layers):
+        assert layers[l][0].stats() == models[l].stats
+        assert models[l].stats["misses"] > steps  # the arena really pages
