@@ -343,30 +343,37 @@ __global__ void __launch_bounds__(kThreads) bat_gateup_kernel(FfnArgs a) {
       asm volatile("" : "+v"(cu[i].x), "+v"(cu[i].y), "+v"(cu[i].z), "+v"(cu[i].w), "+v"(suw[i]));
       const float sg = ok ? f16_lo(sgw[i] >> sh) : 0.0f;
       const float su = ok ? f16_lo(suw[i] >> sh) : 0.0f;
-      // the codes' fp16 pairs once per step, for every token of the chunk
-      uint32_t pg[16], pu[16];
-      code_pairs(cg[i], pg);
-      code_pairs(cu[i], pu);
+      // a code dword at a time: its four fp16 pairs of gate and of up, then every
+      // token of the chunk against the activation dwords of the same 8 columns (each
+      // token's sum still runs over the chunk's 16 dwords in order)
+      const uint32_t wg[4] = {cg[i].x, cg[i].y, cg[i].z, cg[i].w};
+      const uint32_t wu[4] = {cu[i].x, cu[i].y, cu[i].z, cu[i].w};
+      float dg[kTB], du[kTB];
+#pragma unroll
+      for (int ti = 0; ti < kTB; ++ti) dg[ti] = du[ti] = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t g8 = wg[d] >> 8, u8 = wu[d] >> 8;
+        const uint32_t pg0 = (wg[d] & 0x000F000Fu) | 0x64006400u, pg1 = (wg[d] & 0x00F000F0u) | 0x54005400u;
+        const uint32_t pg2 = (g8 & 0x000F000Fu) | 0x64006400u, pg3 = (g8 & 0x00F000F0u) | 0x54005400u;
+        const uint32_t pu0 = (wu[d] & 0x000F000Fu) | 0x64006400u, pu1 = (wu[d] & 0x00F000F0u) | 0x54005400u;
+        const uint32_t pu2 = (u8 & 0x000F000Fu) | 0x64006400u, pu3 = (u8 & 0x00F000F0u) | 0x54005400u;
+#pragma unroll
+        for (int ti = 0; ti < kTB; ++ti) {
+          if (ti < tc) {
+            const uint4 xq = reinterpret_cast<const uint4*>(xs + (size_t)ti * (GW * 17) + jc * 16)[d];
+            dg[ti] = dot2h(pg3, xq.w, dot2h(pg2, xq.z, dot2h(pg1, xq.y, dot2h(pg0, xq.x, dg[ti]))));
+            du[ti] = dot2h(pu3, xq.w, dot2h(pu2, xq.z, dot2h(pu1, xq.y, dot2h(pu0, xq.x, du[ti]))));
+          }
+        }
+      }
 #pragma unroll
       for (int ti = 0; ti < kTB; ++ti) {
         if (ti < tc) {
-          const uint32_t* xt = xs + (size_t)ti * (GW * 17);
-          const uint4* xq = reinterpret_cast<const uint4*>(xt + jc * 16);
-          const uint4 x0 = xq[0], x1 = xq[1], x2 = xq[2], x3 = xq[3];
-          const uint32_t xw[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                   x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-          const float C = reinterpret_cast<const float*>(xt + GW * 16)[jc];
-          float dg = 0.0f, du = 0.0f;
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            dg = dot2h(pg[k], xw[k], dg);
-            du = dot2h(pu[k], xw[k], du);
-          }
-          ag[ti] = fmaf(sg, dg - C, ag[ti]);
-          au[ti] = fmaf(su, du - C, au[ti]);
+          const float C = reinterpret_cast<const float*>(xs + (size_t)ti * (GW * 17) + GW * 16)[jc];
+          ag[ti] = fmaf(sg, dg[ti] - C, ag[ti]);
+          au[ti] = fmaf(su, du[ti] - C, au[ti]);
         }
-        // token ti is done here: the next token's LDS reads are not hoisted above (register pressure)
-        asm volatile("" : "+v"(ag[ti]), "+v"(au[ti])::"memory");
       }
     }
     // phases (lane bits 3..5), read from lanes 0..7
