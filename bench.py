@@ -469,6 +469,51 @@ def paged_leg(a, dev):
             identical = identical and torch.equal(ys[l].view(torch.int16), y_res.view(torch.int16))
         res[mode] = (dt, d, identical)
         log(f"  paged {mode}: {(steps - warm) / dt:.2f} tok/s")
+    # the same tokens with every expert resident (identity slot map, no hand-shake): the
+    # rate of the layer stack when the arena holds everything. One token's 43 moe_layer
+    # calls are replayed as a HIP graph (checked bitwise against eager), its logits
+    # copied into the graph's input before each replay.
+    ids_r = torch.empty(1, w.K, dtype=torch.int32, device=dev)
+    wts_r = torch.empty(1, w.K, dtype=torch.float32, device=dev)
+    ws_r = torch.empty(max(lib.moe_ffn_workspace_bytes(1, w.H, w.I, w.E, w.K, True), 256), dtype=torch.uint8,
+                       device=dev)
+    st_r = torch.zeros(1, dtype=torch.int32, device=dev)
+    lg_cur = torch.empty(w.layers, w.E, dtype=torch.float32, device=dev)
+    rs = torch.cuda.Stream()
+
+    def resident_token():
+        for l in range(w.layers):
+            lib.moe_layer(xs[l], None, lg_cur[l], 1, w.H, w.I, w.E, w.K, 32, 0, ids_r, wts_r, resident_table, resident,
+                          stride, shared, ys[l], ws_r, ws_r.numel(), st_r, 0, rs)
+
+    with torch.cuda.stream(rs):
+        lg_cur.copy_(lg[steps - 1])
+        resident_token()
+        y_eager = torch.stack([y.clone() for y in ys])
+    rs.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=rs):
+        resident_token()
+    with torch.cuda.stream(rs):
+        graph.replay()
+    rs.synchronize()
+    if not torch.equal(torch.stack(ys).view(torch.int16), y_eager.view(torch.int16)):
+        raise RuntimeError("resident graph replay differs from the eager run")
+    e0, e1 = ev(), ev()
+    with torch.cuda.stream(rs):
+        for s in range(warm):
+            lg_cur.copy_(lg[s])
+            graph.replay()
+        e0.record(rs)
+        for s in range(warm, steps):
+            lg_cur.copy_(lg[s])
+            graph.replay()
+        e1.record(rs)
+    torch.cuda.synchronize()
+    if int(st_r.item()) != 0:
+        raise RuntimeError(f"device status {int(st_r.item())}")
+    res_ms = e0.elapsed_time(e1) / (steps - warm)
+    res_bytes = w.layers * ((w.K + 1) * blob + w.E * 4 + 2 * w.H * 2)  # 6 routed + shared blobs, logits, x, y
     # pinned host -> device copy rate for context
     probe_dev = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     probe_host = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
@@ -490,6 +535,8 @@ def paged_leg(a, dev):
         "h2d_peak_gbs": h2d_peak,
         "identical": identical and res["python"][2],
         "python_tok_s": n_tok / res["python"][0],
+        "resident_tok_s": 1e3 / res_ms,
+        "resident_hbm_gbs": res_bytes / (res_ms * 1e-3) / 1e9,
     }
 
 
@@ -913,6 +960,9 @@ def main():
             "host_weight_sets": 1,
             "sequencing": "moe_paged_layer (native, speculative FFN)",
             "python_sequenced_tokens_per_s": round(q["python_tok_s"], 2),
+            "resident_tokens_per_s": round(q["resident_tok_s"], 1),
+            "resident_hbm_gbs": round(q["resident_hbm_gbs"], 1),
+            "resident_hbm_frac": round(q["resident_hbm_gbs"] / HBM_PEAK_GBS, 4),
         }
     if "readahead" in legs:
         torch.cuda.empty_cache()
