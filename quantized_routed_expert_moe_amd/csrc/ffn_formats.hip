@@ -55,12 +55,13 @@ struct Fmt<MOE_FMT_NVFP4> {
   static constexpr int kG = 16;
 };
 
-// E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities,
-// S.1111.111 is NaN and never stored) to fp32, exactly.
-__device__ inline float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;  // 2^-9 m
-  return (b & 0x80u) ? -mag : mag;
+// Byte SEL of w as E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// no infinities, S.1111.111 is NaN and never stored) in fp32, exactly: gfx950's
+// v_cvt_f32_fp8 decodes the OCP E4M3 format (checked on all 256 bytes against
+// the format's definition).
+template <int SEL>
+__device__ inline float e4m3_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
 }
 
 __host__ __device__ inline size_t fmt_al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -207,8 +208,8 @@ __device__ inline void rows_dot(const uint8_t* const (&codes)[S], const uint8_t*
       } else {
         float d0, d1;
         chunk_dot_nvfp4(cw[s][i], xp, d0, d1);
-        out[s] = fmaf(e4m3_to_f32(sr[s][i] & 0xFFu) * k, d0, out[s]);
-        out[s] = fmaf(e4m3_to_f32(sr[s][i] >> 8) * k, d1, out[s]);
+        out[s] = fmaf(e4m3_to_f32<0>(sr[s][i]) * k, d0, out[s]);
+        out[s] = fmaf(e4m3_to_f32<1>(sr[s][i]) * k, d1, out[s]);
       }
     }
   }

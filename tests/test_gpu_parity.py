@@ -770,6 +770,47 @@ def test_fmt_decode_full_size(fmt):
     check_close(y_f64(y), y_ref, f"  format {fmt} decode full size")
 
 
+def test_nvfp4_every_e4m3_scale():
+    """NVFP4 experts whose group scales run through all 254 finite E4M3 codes (zero, the
+    subnormals, up to 448, both signs), with small global scales and activations so that h
+    stays in fp16: one token through 8 experts against the oracle."""
+    H, I, E, K = 64, 64, 8, 8
+    say("nvfp4 with every finite E4M3 scale")
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+    assert finite.size == 254
+    rng = np.random.default_rng(41)
+    stride = lib.moe_fmt_slot_stride(gen.FMT_NVFP4, H, I)
+    slots = torch.zeros(E * stride, dtype=torch.uint8, device=DEV)
+    experts = {}
+    pos = 0
+    for e in range(E):
+        def scales(rows, cols):
+            nonlocal pos
+            n = rows * (cols // 16)
+            out = finite[(pos + np.arange(n)) % finite.size].reshape(rows, cols // 16)
+            pos += n
+            return out
+        t = {"qg": rng.integers(0, 256, size=(I, H // 2), dtype=np.uint8),
+             "qu": rng.integers(0, 256, size=(I, H // 2), dtype=np.uint8),
+             "qd": rng.integers(0, 256, size=(H, I // 2), dtype=np.uint8),
+             "sg": scales(I, H), "su": scales(I, H), "sd": scales(H, I),
+             "global": np.full(3, 2.0**-8, dtype=np.float32)}
+        blob = np.zeros(stride, dtype=np.uint8)
+        lib.moe_pack_expert_nvfp4(t["qg"], t["qu"], t["qd"], t["sg"], t["su"], t["sd"], t["global"], H, I, blob)
+        slots[e * stride : (e + 1) * stride].copy_(torch.from_numpy(blob))
+        experts[e] = R.Expert(t, H, I, g=16, bits=4)
+    assert pos >= 3 * finite.size  # every code in several matrices
+    table = torch.arange(E, dtype=torch.int32, device=DEV)
+    xb = gen.bf16_bits_from_f32((rng.standard_normal((1, H)) * 0.125).astype(np.float32))
+    logits = rng.standard_normal((1, E)).astype(np.float32)
+    w = gen.Workload("nvfp4_all_e4m3_t1_h64_e8_k8_i64", 1, H, E, K, I, 1, E, "normal", 0)
+    y_ref, ids_ref, _, _ = R.moe_layer(xb, experts.__getitem__, K, logits=logits)
+    ids, _, y, st, _ = fmt_run(gen.FMT_NVFP4, w, slots, table, None, stride, xb, logits)
+    assert int(st.item()) == 0
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    check_close(y_f64(y), y_ref, "  nvfp4 every E4M3 scale")
+
+
 def test_fmt_status_and_argument_errors():
     fmt = gen.FMT_INT8_G32
     w = gen.Workload("fmt8_t3_h256_e8_k2_i96_err", 3, 256, 8, 2, 96, 1, 8, "normal", 78, shared=True)
