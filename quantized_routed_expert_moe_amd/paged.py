@@ -135,10 +135,13 @@ class PagedDecode:
 
     ``layers``: per layer ``(arena, slots, table)`` (a ``lib.Arena``, its device
     slot buffer and device slot table). ``routers``: per layer, device fp32
-    ``[E, H]``, or None when the caller passes the layer's logits to ``layer``. ``shared``: per layer a device blob of the shared expert, or None.
+    ``[E, H]``, or None when the caller passes the layer's logits to ``layer``.
+    ``shared``: per layer a device blob of the shared expert, or None.
     ``predict``: experts read ahead per layer (0: none). ``predictors``: per layer,
     the device fp32 ``[E, H]`` matrix applied to the previous layer's input to
-    predict this layer's experts (default: the layer's own router).
+    predict this layer's experts (default: the layer's own router). ``native``:
+    one ``moe_paged_layer`` call per layer (else the same steps from Python);
+    ``speculate``: with ``native``, the FFN starts before the hand-shake.
     """
 
     def __init__(self, layers, routers, stride: int, H: int, I: int, E: int, K: int, shared=None,
@@ -146,7 +149,7 @@ class PagedDecode:
                  speculate: bool = True):
         if len(routers) != len(layers) or (predictors is not None and len(predictors) != len(layers)):
             raise ValueError("one router (and one predictor) per layer")
-        if not 0 <= predict <= min(E, layers[0][0].S):
+        if not 0 <= predict <= min([E] + [a.S for a, _, _ in layers]):
             raise ValueError("predict must be in [0, min(E, S)]")
         self.layers, self.routers, self.stride = layers, routers, stride
         self.predictors = predictors if predictors is not None else routers
@@ -182,7 +185,8 @@ class PagedDecode:
 
     def layer(self, l: int, x: torch.Tensor, y: torch.Tensor, logits: torch.Tensor | None = None) -> None:
         """x bf16 [1, H]: layer l's input; y bf16 [1, H] out; logits fp32 [E]: layer l's
-        logits when it has no router (overwritten by a read-ahead prediction)."""
+        logits when it has no router (the native path with read-ahead then reuses that
+        buffer for the prediction's logits)."""
         if (logits is None) != (self.routers[l] is not None):
             raise ValueError("pass logits exactly when the layer has no router")
         lg = self.logits if logits is None else logits.view(1, -1)
