@@ -844,8 +844,8 @@ def cpu_baseline(w, n_layers):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported: this build has no multi-GPU path "
-              "(see DESIGN.md for how the layer would shard)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported: the layer has no multi-GPU path "
+              "(expert-parallel sharding over xGMI is designed, not built)", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The loaded C-ABI library on a GPU machine; fails loudly when it is missing."""
+    """The loaded C-ABI library on a machine with a GPU; fails loudly when it is missing."""
     import torch
 
     if not torch.cuda.is_available():
