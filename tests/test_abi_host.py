@@ -297,3 +297,17 @@ def test_nvfp4_pack_rejections():
     with pytest.raises(lib.MoeError):  # H not a multiple of 32
         lib.moe_pack_expert_nvfp4(t["qg"], t["qu"], t["qd"], t["sg"], t["su"], t["sd"], t["global"], 240, I, blob)
     assert lib.moe_fmt_blob_bytes(gen.FMT_NVFP4, 16384, 1536) == 0
+
+
+def test_missing_library_is_an_error():
+    """Without the built library nothing computes: loading fails with ImportError (checked in a
+    fresh process, since this one has the library loaded)."""
+    import subprocess
+    import sys
+
+    code = ("import quantized_routed_expert_moe_amd.lib as L\n"
+            "L.LIB_PATH = '/nonexistent/libmoe.so'\n"
+            "try:\n    L.load()\nexcept ImportError as e:\n    print('ImportError', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0 and out.stdout.startswith("ImportError"), (out.stdout, out.stderr)
