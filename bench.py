@@ -841,6 +841,27 @@ def cpu_baseline(w, n_layers):
     }
 
 
+def hbm_read_probe(dev, gib=2, reps=5):
+    """GB/s of a plain streaming read: torch's sum over a 2 GiB int64 tensor (best of 5; the
+    integer sum keeps up with HBM where torch's fp32 reductions do not)."""
+    import torch
+
+    t = torch.ones(gib << 27, dtype=torch.int64, device=dev)
+    t.sum()
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        t.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, (gib << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del t
+    torch.cuda.empty_cache()
+    return best
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -865,6 +886,7 @@ def main():
         del src, dst
     w, d = decode_leg(a, dev)
     traffic = decode_traffic()
+    probe_gbs = hbm_read_probe(dev)
     out = {
         "metric": "MoE-layer decode tokens/s (one token through 48 layers) + achieved HBM GB/s",
         "value": round(d["tok_s"], 2),
@@ -914,6 +936,9 @@ def main():
             "bytes_per_launch": d["bytes"]["down"],
         },
         "wall_s_timed": round(d["wall"], 4),
+        # context: a plain streaming read (torch's int64 sum over 2 GiB) on the same GPU
+        "hbm_read_probe_gbs": round(probe_gbs, 1),
+        "frac_of_read_probe": {"gate_up": round(d["gu_gbs"] / probe_gbs, 4), "down": round(d["dn_gbs"] / probe_gbs, 4)},
         "workloads": {},
     }
     torch.cuda.empty_cache()
