@@ -53,13 +53,17 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
 // Blob of unit u (u = 0 is the shared expert when present) or nullptr with the
 // status word set; ids = the token's routed experts in rank order.
-// With pre_slots (moe_layer) the routing kernel has resolved the slots already.
-__device__ inline const uint8_t* dec_unit_blob(const FfnArgs& a, int u, bool has_shared, const int32_t* ids) {
+// With pre_slots (moe_layer) the routing kernel has resolved the slots already:
+// pre is a.pre_slots as a constant-space pointer, so that the workgroup's slot
+// (u is uniform) comes from one scalar load.
+typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+__device__ inline const uint8_t* dec_unit_blob(const FfnArgs& a, int u, bool has_shared, const int32_t* ids,
+                                               const_i32p pre) {
   const int k = has_shared ? u - 1 : u;
   if (k < 0) return a.shared_blob;
   int slot;
-  if (a.pre_slots) {
-    slot = a.pre_slots[k];
+  if (pre) {
+    slot = pre[k];
   } else {
     const int e = ids[k];
     if (e < 0 || e >= a.E) {
@@ -103,6 +107,10 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
   const int j0 = wave * GW;
   const int gw_here = G - j0 < GW ? (G - j0 > 0 ? G - j0 : 0) : GW;  // groups this wave really owns
   const bool has_shared = a.shared_blob != nullptr;
+  // the resolved slots' pointer in registers now, with the first argument loads (left
+  // to the compiler, it is loaded after them: one more round trip before the weights)
+  const_i32p pre = (const_i32p)a.pre_slots;
+  asm volatile("" : "+s"(pre));
   const int n_hb = I / 8;
   const int item = xcd_item(blockIdx.x, (K + (has_shared ? 1 : 0)) * n_hb);
   const int u = item / n_hb, hb = item % n_hb;
@@ -115,7 +123,7 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
     q = q < G * 4 ? q : G * 4 - 1;
     xv[v] = reinterpret_cast<const uint4*>(a.x)[q];
   }
-  const uint8_t* blob = dec_unit_blob(a, u, has_shared, a.ids);
+  const uint8_t* blob = dec_unit_blob(a, u, has_shared, a.ids, pre);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
   const int n = hb * 8 + r;
