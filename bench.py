@@ -114,31 +114,6 @@ def decode_traffic():
 # ------------------------------------------------------------------ decode (headline)
 
 
-def build_decode_stack(w, dev):
-    import torch
-
-    from quantized_routed_expert_moe_amd import harness, lib
-    from synth import gen
-
-    stacks = []
-    run = harness.LayerRunner(w, dev)
-    t0 = time.time()
-    lg = torch.empty(w.T, w.E, dtype=torch.float32, device=dev)
-    for layer in range(w.layers):
-        xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
-        # set-up only: route first, then place the routed experts in the layer's arena
-        x = harness.bf16_tensor(xb, dev)
-        wr = torch.from_numpy(gen.router_weight(w.seed, layer, w.E, w.H)).to(dev)
-        lib.moe_route(x, wr, lg, w.T, w.H, w.E, w.K, 0, run.ids, run.wts)
-        routed = sorted(set(run.ids.cpu().numpy().ravel().tolist()))
-        stacks.append(harness.make_layer(w, layer, dev, slots=w.slots, experts=routed, place_seed=1000 + layer,
-                                         x_bits=xb))
-        if layer % 16 == 15:
-            log(f"  decode: packed layers 0..{layer} ({time.time() - t0:.1f} s)")
-    torch.cuda.synchronize()
-    return stacks
-
-
 def decode_leg(a, dev):
     import numpy as np
     import torch
@@ -149,8 +124,9 @@ def decode_leg(a, dev):
     base = gen.WORKLOADS["decode_t1_h4096_e256_k8_i1536_x48"]
     w = gen.Workload(base.name, base.T, base.H, base.E, base.K, base.I, a.layers, base.slots, base.router, base.seed)
     log(f"decode: building {w.layers} layers of {w.name}")
-    stacks = build_decode_stack(w, dev)
-    run = harness.LayerRunner(w, dev)
+    stacks = harness.decode_stack(w, dev, log)
+    stack = harness.StackRunner(w, stacks, dev)  # one moe_layer per layer, each layer with its own outputs
+    run = harness.LayerRunner(w, dev)  # per-stage timings below
     stream = torch.cuda.Stream()
     blob = lib.moe_blob_bytes(w.H, w.I)
     mat_bytes = w.H * w.I // 2 + w.H * w.I // 32 * 2  # codes + fp16 scales of one matrix
@@ -159,28 +135,29 @@ def decode_leg(a, dev):
     bytes_down = w.K * mat_bytes + w.T * w.K * w.I * 2 + w.T * w.H * 2  # experts + h (fp16) + y
     bytes_layer = bytes_router + w.K * blob + w.T * w.H * 2 * 2
 
-    def step():  # one token through the layer stack: one moe_layer call per layer
-        for L in stacks:
-            run.layer(L, stream)
-
     with torch.cuda.stream(stream):
         for _ in range(a.warmup):
-            step()
+            stack.step(stream)
     stream.synchronize()
-    if int(run.status.item()) != 0:
-        raise RuntimeError(f"device status {int(run.status.item())}")
-    graph = None
+    if int(stack.status.item()) != 0:
+        raise RuntimeError(f"device status {int(stack.status.item())}")
+    eager = stack.outputs()
     if a.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            step()
+        stack.capture(stream)
+        # the captured step must recompute every layer: poison all outputs, replay once,
+        # and compare every layer's y, ids and w with the eager step, bit for bit
+        stack.poison()
+        torch.cuda.synchronize()
+        stack.replay(stream)
         stream.synchronize()
-        y_graph = run.y.clone()
-        with torch.cuda.stream(stream):
-            step()
-        stream.synchronize()
-        if not torch.equal(run.y.view(torch.int16), y_graph.view(torch.int16)):
-            raise RuntimeError("graph replay output differs from the eager output")
+        replayed = stack.outputs()
+        for name, e_, r_ in zip(("y", "ids", "w"), eager, replayed):
+            if not np.array_equal(e_.view(np.uint8), r_.view(np.uint8)):
+                raise RuntimeError(f"graph replay {name} differs from the eager step")
+        log(f"  decode: graph replay equals the eager step bitwise on all {w.layers} layers")
+
+    def step():
+        stack.step(stream)
 
     torch.cuda.synchronize()
     e0, e1 = ev(), ev()
@@ -188,14 +165,17 @@ def decode_leg(a, dev):
     e0.record(stream)
     with torch.cuda.stream(stream):
         for _ in range(a.steps):
-            if graph is not None:
-                graph.replay()
+            if stack.graph is not None:
+                stack.graph.replay()
             else:
                 step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / a.steps
+    after = stack.outputs()  # the timed steps left the same bits in every layer
+    if not all(np.array_equal(e_.view(np.uint8), r_.view(np.uint8)) for e_, r_ in zip(eager, after)):
+        raise RuntimeError("the timed decode steps left outputs that differ from the eager step")
 
     # per-stage durations: each stage launched for every layer back to back on the
     # launch stream (each layer with its own routed experts), 3 passes, HIP events
@@ -224,8 +204,8 @@ def decode_leg(a, dev):
             b1.record(stream)
         stream.synchronize()
         us[name] = b0.elapsed_time(b1) * 1e3 / (3 * len(stacks))
-    if int(run.status.item()) != 0:
-        raise RuntimeError(f"device status {int(run.status.item())}")
+    if int(run.status.item()) != 0 or int(stack.status.item()) != 0:
+        raise RuntimeError(f"device status {int(run.status.item())} / {int(stack.status.item())}")
     gu_gbs = bytes_gate_up / (us["gate_up"] * 1e-6) / 1e9
     dn_gbs = bytes_down / (us["down"] * 1e-6) / 1e9
     layer_gbs = bytes_layer * w.layers / (ms_step * 1e-3) / 1e9
@@ -233,7 +213,7 @@ def decode_leg(a, dev):
         "tok_s": 1000.0 / ms_step,
         "ms_step": ms_step,
         "wall": wall,
-        "graph": graph is not None,
+        "graph": stack.graph is not None,
         "layer_gbs": layer_gbs,
         "us": us,
         "bytes": {"router": bytes_router, "gate_up": bytes_gate_up, "down": bytes_down, "layer": bytes_layer},
@@ -494,6 +474,9 @@ def paged_leg(a, dev):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=rs):
         resident_token()
+    for y in ys:  # poisoned: a replay that computed nothing cannot pass
+        y.view(torch.int16).fill_(-1)
+    torch.cuda.synchronize()
     with torch.cuda.stream(rs):
         graph.replay()
     rs.synchronize()

@@ -79,7 +79,8 @@ enum moe_flags {
   MOE_FORCE_GEMV = 1u << 8,    /* moe_expert_ffn: use the per-expert GEMV path whatever T is */
   MOE_FORCE_GROUPED = 1u << 9, /* moe_expert_ffn: use the expert-grouped MFMA GEMM path */
   MOE_FFN_PARTIAL = 1u << 10,  /* moe_expert_ffn: one pass of a chunked paged run (see moe_ffn_combine) */
-  MOE_FFN_PARTIAL_SHARED = 1u << 11 /* with MOE_FFN_PARTIAL: this pass also computes the shared expert */
+  MOE_FFN_PARTIAL_SHARED = 1u << 11, /* with MOE_FFN_PARTIAL: this pass also computes the shared expert */
+  MOE_FFN_PARTIAL_FIRST = 1u << 12   /* with MOE_FFN_PARTIAL: the first pass of a chunk */
 };
 
 const char* moe_strerror(int status);
@@ -240,11 +241,14 @@ int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids, const flo
  * chunk of T tokens uses more experts than the arena holds, its FFN runs as
  * several passes over one workspace, each pass with the experts that are
  * resident for it, then one combine:
- *   moe_expert_ffn(..., flags = MOE_FFN_PARTIAL [| MOE_FFN_PARTIAL_SHARED])
+ *   moe_expert_ffn(..., flags = MOE_FFN_PARTIAL [| MOE_FFN_PARTIAL_SHARED]
+ *                  [| MOE_FFN_PARTIAL_FIRST])
  *     computes the routed experts e with slot_table[e] >= 0 (the others are
  *     skipped, not flagged) for their (token, pick) pairs, keeps the per-pair
  *     outputs in ws and does not write y; MOE_FFN_PARTIAL_SHARED also computes
  *     the shared expert (shared_blob must be non-NULL; exactly one pass sets it).
+ *     The first pass of every chunk sets MOE_FFN_PARTIAL_FIRST (it starts the
+ *     workspace's record of which experts the chunk's passes computed).
  *     MOE_FFN_PARTIAL selects the grouped path (with MOE_FORCE_GEMV: MOE_EINVAL).
  *   moe_ffn_combine then writes y from ws: the shared output (when has_shared)
  *     plus sum_k w[t][k] * out[t][k], as moe_expert_ffn does.
@@ -253,11 +257,16 @@ int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids, const flo
  * and 0 throughout), the same ws and one stream order. When each routed expert
  * that ids use has a slot in at least one pass, y is bit-identical to
  * moe_expert_ffn(..., MOE_FORCE_GROUPED) with every expert resident; an
- * expert computed in two passes gives the same bits twice. A pair whose expert
- * is computed in no pass leaves stale workspace data in y (no error is raised).
+ * expert computed in two passes gives the same bits twice.
+ * Exact or explicit failure ("Strata" README, the execution rules): the combine
+ * sets *dev_status (device int32, zeroed by the caller; the first error stays)
+ * to MOE_ENOTRES when a pair's expert, or the shared expert, was computed in no
+ * pass since the chunk's first pass, and to MOE_EINVAL when no pass with
+ * MOE_FFN_PARTIAL_FIRST ran since the previous combine on this workspace; y is
+ * then unspecified. ids: device int32 [T][K], the ids the passes used.
  * ws_bytes >= moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, MOE_FFN_PARTIAL). */
-int moe_ffn_combine(const float* w, int T, int H, int I, int E, int K, int has_shared, uint16_t* y, void* ws,
-                    size_t ws_bytes, moe_stream_t stream);
+int moe_ffn_combine(const int32_t* ids, const float* w, int T, int H, int I, int E, int K, int has_shared,
+                    uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, moe_stream_t stream);
 
 /* ------------------------------------------------------------------ whole layer
  * moe_layer: moe_route(x, w_router, logits, T, H, E, K, route_flags, ids, w)

@@ -350,3 +350,44 @@ def moe_layer(x_bits, experts, K, logits=None, w_router=None, shared=None, renor
             acc = acc + w[t, k] * get(int(ids[t, k]))(x[t])
         y[t] = acc
     return y, ids, w, np.asarray(logits, dtype=np.float32)
+
+
+def expert_outputs(x_bits, experts, ids):
+    """o[t, k] = expert_{ids[t, k]}(x[t]) for every (token, pick) pair, float64 [T, K, H].
+
+    The same per-pair FFN as ``moe_layer``, evaluated one expert at a time over
+    all the tokens that picked it (one batched product per expert instead of one
+    vector product per pair). Only the summation order inside the products can
+    differ from ``moe_layer``, so the two agree to float64 rounding."""
+    x = bf16_bits_to_f64(x_bits)
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    get = experts if callable(experts) else experts.__getitem__
+    o = np.empty((T, K, x.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        t_idx, k_idx = np.nonzero(ids == e)
+        o[t_idx, k_idx] = get(int(e))(x[t_idx])
+    return o
+
+
+def combine(o, w, shared_out=None):
+    """y[t] = shared_out[t] + sum_{k=0..K-1} w[t, k] * o[t, k], accumulated in rank order
+    (the combine of ``moe_layer``); shared_out None means no shared expert."""
+    T, K, H = o.shape
+    y = np.zeros((T, H), dtype=np.float64) if shared_out is None else np.array(shared_out, dtype=np.float64)
+    for k in range(K):
+        y = y + w[:, k : k + 1] * o[:, k]
+    return y
+
+
+def moe_layer_expert_major(x_bits, experts, K, logits=None, w_router=None, shared=None, renorm=False):
+    """``moe_layer`` evaluated expert by expert (``expert_outputs`` then ``combine``): the
+    same routing and the same rank-ordered combine, for prompts too long to evaluate one
+    pair at a time. Returns (y, ids, w, l) as ``moe_layer``."""
+    x = bf16_bits_to_f64(x_bits)
+    if logits is None:
+        logits = router_logits(x_bits, w_router)
+    ids, w = route(logits, K, renorm)
+    o = expert_outputs(x_bits, experts, ids)
+    y = combine(o, w, shared(x) if shared is not None else None)
+    return y, ids, w, np.asarray(logits, dtype=np.float32)

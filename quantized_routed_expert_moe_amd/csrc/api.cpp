@@ -99,10 +99,12 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
                      uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
                      moe_stream_t stream, int stage, const int32_t* pre_slots = nullptr) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
-  if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_FFN_PARTIAL | MOE_FFN_PARTIAL_SHARED))
+  if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_FFN_PARTIAL | MOE_FFN_PARTIAL_SHARED |
+                          MOE_FFN_PARTIAL_FIRST))
     return MOE_EINVAL;
   if ((flags & MOE_FORCE_GEMV) && (flags & (MOE_FORCE_GROUPED | MOE_FFN_PARTIAL))) return MOE_EINVAL;
   if ((flags & MOE_FFN_PARTIAL_SHARED) && (!(flags & MOE_FFN_PARTIAL) || !shared_blob)) return MOE_EINVAL;
+  if ((flags & MOE_FFN_PARTIAL_FIRST) && !(flags & MOE_FFN_PARTIAL)) return MOE_EINVAL;
   if (!moe::shape_ok(H, I, g) || E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
   if (T == 0) return MOE_OK;
   if (!x || !ids || !w || !slot_table || !slots || !y || !dev_status) return MOE_EINVAL;
@@ -132,7 +134,8 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
   a.ws_bytes = ws_bytes;
   a.status = dev_status;
   a.mode = (flags & MOE_FFN_PARTIAL ? moe::kModePartial : 0u) |
-           (flags & MOE_FFN_PARTIAL_SHARED ? moe::kModePartialShared : 0u);
+           (flags & MOE_FFN_PARTIAL_SHARED ? moe::kModePartialShared : 0u) |
+           (flags & MOE_FFN_PARTIAL_FIRST ? moe::kModePartialFirst : 0u);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool dec1 = !grouped && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
   if (dec1) a.pre_slots = pre_slots;
@@ -212,23 +215,26 @@ extern "C" int moe_layer(const uint16_t* x, const float* w_router, float* logits
                           dev_status, ffn_flags, stream, 2);
 }
 
-extern "C" int moe_ffn_combine(const float* w, int T, int H, int I, int E, int K, int has_shared, uint16_t* y,
-                               void* ws, size_t ws_bytes, moe_stream_t stream) {
+extern "C" int moe_ffn_combine(const int32_t* ids, const float* w, int T, int H, int I, int E, int K, int has_shared,
+                               uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, moe_stream_t stream) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E || (has_shared != 0 && has_shared != 1))
     return MOE_EINVAL;
   if (!moe::shape_ok(H, I, 32) || E > moe::kMaxE || K > moe::kMaxK || !moe::grouped_shape_ok(H, I)) return MOE_EUNSUP;
   if (T == 0) return MOE_OK;
-  if (!w || !y) return MOE_EINVAL;
+  if (!ids || !w || !y || !dev_status) return MOE_EINVAL;
   const size_t need = moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, MOE_FFN_PARTIAL);
   if (need == 0) return MOE_EUNSUP;
   if (!ws || ws_bytes < need) return MOE_EWS;
   moe::FfnArgs a{};
+  a.ids = ids;
   a.w = w;
   a.T = T;
   a.H = H;
   a.I = I;
   a.E = E;
   a.K = K;
+  a.status = dev_status;
+  a.mode = moe::kModeCheckDone;
   // the combine reads shared_blob only to test it for NULL (the workspace layout
   // and the shared term depend on it); it is never dereferenced
   a.shared_blob = has_shared ? static_cast<const uint8_t*>(ws) : nullptr;

@@ -50,9 +50,15 @@ struct TileDesc {
 };
 
 struct GroupedWs {
-  size_t n_mt, tiles, ublob, unit_mt0, sorted, xh, h, o, bytes;
+  size_t n_mt, tiles, ublob, unit_mt0, sorted, xh, h, o, done, bytes;
   int max_units, max_mt;
 };
+
+// Partial passes (chunked paged prefill) record what they computed in the
+// workspace: done[e] (e < E) = 1 once expert e was computed by a pass of the
+// current chunk, done[E] the same for the shared expert, done[E + 1] = kSession
+// from the chunk's first pass until the combine has run.
+constexpr int32_t kSession = 0x50415254;
 
 __host__ __device__ inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -70,7 +76,8 @@ __host__ __device__ inline GroupedWs grouped_ws(int T, int H, int I, int E, int 
   w.xh = al256(w.sorted + PA * sizeof(int32_t));
   w.h = al256(w.xh + (size_t)T * H * 2);
   w.o = al256(w.h + PA * (size_t)I * 2);
-  w.bytes = al256(w.o + PA * (size_t)H * 2);  // o: bf16
+  w.done = al256(w.o + PA * (size_t)H * 2);  // o: bf16
+  w.bytes = al256(w.done + ((size_t)E + 2) * sizeof(int32_t));
   return w;
 }
 
@@ -154,6 +161,17 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
   const int mt_here = (c > 0 && (slot >= 0 || !partial)) ? (c + kBM - 1) / kBM : 0;
   const int mt0 = block_exclusive_scan(mt_here, wsum, &total);
   const int shared_mt = do_shared ? (T + kBM - 1) / kBM : 0;
+  if (partial) {
+    // marks of what this pass computes; the chunk's first pass starts them afresh
+    int32_t* done = reinterpret_cast<int32_t*>(a.ws + W.done);
+    const bool first = a.mode & kModePartialFirst;
+    const bool here = c > 0 && slot >= 0;
+    if (tid < E && (first || here)) done[tid] = here ? 1 : 0;
+    if (tid == 0) {
+      if (first || do_shared) done[E] = do_shared ? 1 : 0;
+      if (first) done[E + 1] = kSession;
+    }
+  }
   if (tid < E) {
     seg[tid] = row0;
     cur[tid] = 0;
@@ -592,9 +610,22 @@ __global__ void __launch_bounds__(256) grouped_combine_kernel(FfnArgs a) {
   const int P = T * K;
   const int H8 = H / 8;
   const size_t n8 = (size_t)T * H8;
+  const bool check = a.mode & kModeCheckDone;
+  const int32_t* done = reinterpret_cast<const int32_t*>(a.ws + W.done);
+  if (check && blockIdx.x == 0 && threadIdx.x == 0 && done[a.E + 1] != kSession)
+    *a.status = MOE_EINVAL;  // no first pass (MOE_FFN_PARTIAL_FIRST) since the last combine
   for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < n8; idx += (size_t)gridDim.x * 256) {
     const int t = (int)(idx / H8);
     const int c8 = (int)(idx % H8);
+    if (check && c8 == 0) {
+      // every pair of the token (and the shared term) must come from a pass of this chunk
+      bool missing = has_shared && done[a.E] != 1;
+      for (int k = 0; k < K; ++k) {
+        const int e = a.ids[(size_t)t * K + k];
+        missing |= e < 0 || e >= a.E || done[e] != 1;
+      }
+      if (missing) *a.status = MOE_ENOTRES;
+    }
     float acc[8];
     {
       const uint4 v = has_shared ? o8[(size_t)(P + t) * H8 + c8] : make_uint4(0u, 0u, 0u, 0u);
@@ -675,7 +706,11 @@ hipError_t launch_grouped_combine(const FfnArgs& a, hipStream_t s) {
   const size_t n8 = (size_t)a.T * a.H / 8;
   const size_t blocks = (n8 + 255) / 256;
   hipLaunchKernelGGL(grouped_combine_kernel, dim3(blocks < 8192 ? (int)blocks : 8192), dim3(256), 0, s, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !(a.mode & kModeCheckDone)) return e;
+  // close the chunk's session: the next chunk must start with a first pass
+  const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, a.shared_blob != nullptr);
+  return launch_status(reinterpret_cast<int32_t*>(a.ws + W.done) + a.E + 1, nullptr, s);
 }
 
 }  // namespace moe

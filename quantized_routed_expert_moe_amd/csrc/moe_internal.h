@@ -120,8 +120,10 @@ struct FfnArgs {
 // A partial pass of the grouped path: only routed experts with a slot are
 // computed (the others are skipped without error), the per-pair outputs stay in
 // the workspace and y is not written; kModePartialShared: this pass also
-// computes the shared expert.
-constexpr unsigned kModePartial = 1u, kModePartialShared = 2u;
+// computes the shared expert; kModePartialFirst: the chunk's first pass (it
+// resets the workspace's record of computed experts). kModeCheckDone (the
+// combine of moe_ffn_combine): every pair must have been computed by a pass.
+constexpr unsigned kModePartial = 1u, kModePartialShared = 2u, kModePartialFirst = 4u, kModeCheckDone = 8u;
 hipError_t launch_grouped_combine(const FfnArgs& a, hipStream_t s);
 // the other expert formats (ffn_formats.hip): gate/up, down and combine
 hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, hipStream_t s);
@@ -147,5 +149,8 @@ bool grouped_shape_ok(int H, int I);
 hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s);
 
 hipError_t launch_table_update(int32_t* table, const int32_t* idx, const int32_t* val, int n, hipStream_t s);
+// one-thread status word kernel: src == nullptr clears *dst; otherwise a non-zero
+// *src is copied into *dst if *dst is still zero (the first error is kept)
+hipError_t launch_status(int32_t* dst, const int32_t* src, hipStream_t s);
 
 }  // namespace moe

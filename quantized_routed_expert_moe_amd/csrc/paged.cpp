@@ -19,7 +19,9 @@
 //      stream waits for this arena's fills and runs the FFN (again).
 //
 // Exactness: a layer with misses always ends with an FFN that waited for every
-// copy into its arena. A layer without misses keeps the speculative FFN: it ran
+// copy into its arena. A layer without misses keeps the speculative FFN and its
+// status word (copied into dev_status after the decision, so an error the kept
+// run raised, such as an activation outside the fp16 range, is reported): it ran
 // after every fill that had been enqueued into this arena, none was enqueued
 // since (the map made no fill), and every expert it reads was resident then,
 // in the slot the table names. So every output equals the fully-resident run,
@@ -91,7 +93,12 @@ extern "C" int moe_paged_layer(const moe_paged_layer_t* cur, const moe_paged_lay
     return moe_expert_ffn(x, ids, w, 1, H, I, E, K, g, A->table_dev, A->slots_dev, A->stride, cur->shared_blob, y,
                           ws, ffn_ws, status, 0, stream);
   };
-  if (spec && (rc = run_ffn(spec_status)) != MOE_OK) return rc;
+  if (spec) {
+    // the speculative run reports into its own word, cleared first (the workspace
+    // arrives uninitialised); it reaches dev_status only if its result is kept
+    if (moe::launch_status(spec_status, nullptr, s) != hipSuccess) return MOE_EHIP;
+    if ((rc = run_ffn(spec_status)) != MOE_OK) return rc;
+  }
 
   if (hipEventSynchronize(static_cast<hipEvent_t>(ids_ready)) != hipSuccess) return MOE_EHIP;
   int32_t slots_of[moe::kMaxK];
@@ -107,7 +114,11 @@ extern "C" int moe_paged_layer(const moe_paged_layer_t* cur, const moe_paged_lay
     if (rc != MOE_OK) return rc;
     if (npf > 0 && (rc = arena_fill_async(next->arena, pf.data(), npf, side, nullptr)) != MOE_OK) return rc;
   }
-  if ((!spec || nf > 0) && (rc = run_ffn(dev_status)) != MOE_OK) return rc;
+  if (!spec || nf > 0) {
+    if ((rc = run_ffn(dev_status)) != MOE_OK) return rc;
+  } else if (moe::launch_status(dev_status, spec_status, s) != hipSuccess) {
+    return MOE_EHIP;  // the speculative result is kept, and with it its status
+  }
   if (n_misses) *n_misses = nf;
   if (n_prefetched) *n_prefetched = npf;
   return MOE_OK;

@@ -220,6 +220,18 @@ __global__ void __launch_bounds__(64) table_update_kernel(int32_t* table, TableU
   if (i < u.n) table[u.idx[i]] = u.val[i];
 }
 
+// src == nullptr: *dst = 0. Else the first error wins: a non-zero *src is copied
+// into *dst when *dst is still 0.
+__global__ void __launch_bounds__(64) status_kernel(int32_t* dst, const int32_t* src) {
+  if (threadIdx.x != 0) return;
+  if (!src) {
+    *dst = 0;
+    return;
+  }
+  const int32_t v = *src;
+  if (v != 0 && *dst == 0) *dst = v;
+}
+
 }  // namespace
 
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H, int E,
@@ -254,6 +266,11 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigne
   else if (epl <= 8) SEL(8);
   else SEL(16);
 #undef SEL
+  return hipGetLastError();
+}
+
+hipError_t launch_status(int32_t* dst, const int32_t* src, hipStream_t s) {
+  hipLaunchKernelGGL(status_kernel, dim3(1), dim3(64), 0, s, dst, src);
   return hipGetLastError();
 }
 

@@ -148,3 +148,75 @@ class LayerRunner:
         self.route(L, stream)
         self.ffn(L, stream)
         return self.y
+
+
+def decode_stack(w: gen.Workload, device, log=None) -> list[DeviceLayer]:
+    """The layers of single-token decode: per layer a fresh seeded x and router, and an
+    arena of ``w.slots`` slots holding the layer's routed experts in seeded random slots
+    (set-up only: the layer is routed once to know which experts to place)."""
+    import time
+
+    stacks = []
+    ids = torch.empty(w.T, w.K, dtype=torch.int32, device=device)
+    wts = torch.empty(w.T, w.K, dtype=torch.float32, device=device)
+    lg = torch.empty(w.T, w.E, dtype=torch.float32, device=device)
+    t0 = time.time()
+    for layer in range(w.layers):
+        xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
+        x = bf16_tensor(xb, device)
+        wr = torch.from_numpy(gen.router_weight(w.seed, layer, w.E, w.H)).to(device)
+        lib.moe_route(x, wr, lg, w.T, w.H, w.E, w.K, 0, ids, wts)
+        routed = sorted(set(ids.cpu().numpy().ravel().tolist()))
+        stacks.append(make_layer(w, layer, device, slots=w.slots, experts=routed, place_seed=1000 + layer, x_bits=xb))
+        if log is not None and layer % 16 == 15:
+            log(f"  decode: packed layers 0..{layer} ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize(device)
+    return stacks
+
+
+class StackRunner:
+    """One token through a stack of layers: one ``moe_layer`` call per layer, in order on
+    one stream, each layer with its own logits, ids, w and y (the workspace is shared:
+    the layers run one after another)."""
+
+    def __init__(self, w: gen.Workload, layers: list[DeviceLayer], device):
+        n = len(layers)
+        self.w, self.layers = w, layers
+        self.ids = torch.empty(n, w.T, w.K, dtype=torch.int32, device=device)
+        self.wts = torch.empty(n, w.T, w.K, dtype=torch.float32, device=device)
+        self.y = torch.empty(n, w.T, w.H, dtype=torch.bfloat16, device=device)
+        self.ws_bytes = lib.moe_ffn_workspace_bytes(w.T, w.H, w.I, w.E, w.K, w.shared, 0)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.graph = None
+
+    def step(self, stream=None) -> None:
+        w = self.w
+        for i, L in enumerate(self.layers):
+            lib.moe_layer(L.x, L.wr, L.logits, w.T, w.H, w.I, w.E, w.K, w.g, 0, self.ids[i], self.wts[i], L.table,
+                          L.slots, L.stride, L.shared, self.y[i], self.ws, self.ws_bytes, self.status, 0, stream)
+
+    def poison(self) -> None:
+        """Overwrite every output (y with bf16 NaN bits, ids with -1, w with NaN) and the
+        logits the router writes, so that a run which does nothing cannot pass a check."""
+        self.y.view(torch.int16).fill_(-1)
+        self.ids.fill_(-1)
+        self.wts.fill_(float("nan"))
+        for L in self.layers:
+            if L.wr is not None:
+                L.logits.fill_(float("nan"))
+
+    def capture(self, stream) -> None:
+        """Record one step as a HIP graph on ``stream`` (the capture does not execute it)."""
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=stream):
+            self.step(stream)
+
+    def replay(self, stream) -> None:
+        with torch.cuda.stream(stream):
+            self.graph.replay()
+
+    def outputs(self):
+        """Host copies: (y bit patterns int16 [n, T, H], ids, w)."""
+        return (self.y.view(torch.int16).cpu().numpy().copy(), self.ids.cpu().numpy().copy(),
+                self.wts.cpu().numpy().copy())

@@ -24,6 +24,7 @@ MOE_FORCE_GROUPED = 1 << 9
 MOE_FMT_INT4_G32, MOE_FMT_INT4_G128, MOE_FMT_INT8_G32, MOE_FMT_NVFP4 = 0, 1, 2, 3
 MOE_FFN_PARTIAL = 1 << 10
 MOE_FFN_PARTIAL_SHARED = 1 << 11
+MOE_FFN_PARTIAL_FIRST = 1 << 12
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -124,7 +125,7 @@ def load(path: str | None = None):
             [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P, _P, _SZ, _P, _P, _P, _SZ, _P,
              ctypes.c_uint, _P],
         ),
-        "moe_ffn_combine": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+        "moe_ffn_combine": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P]),
         "moe_fmt_blob_bytes": (_SZ, [_I, _I, _I]),
         "moe_fmt_slot_stride": (_SZ, [_I, _I, _I]),
         "moe_pack_expert_fmt": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
@@ -294,10 +295,10 @@ def moe_layer(x, w_router, logits, T, H, I, E, K, g, route_flags, ids, w, slot_t
     )
 
 
-def moe_ffn_combine(w, T, H, I, E, K, has_shared, y, ws, ws_bytes, stream=None) -> None:
+def moe_ffn_combine(ids, w, T, H, I, E, K, has_shared, y, ws, ws_bytes, dev_status, stream=None) -> None:
     _check(
-        load().moe_ffn_combine(_ptr(w), T, H, I, E, K, int(bool(has_shared)), _ptr(y), _ptr(ws), ws_bytes,
-                               _stream(stream)),
+        load().moe_ffn_combine(_ptr(ids), _ptr(w), T, H, I, E, K, int(bool(has_shared)), _ptr(y), _ptr(ws), ws_bytes,
+                               _ptr(dev_status), _stream(stream)),
         "moe_ffn_combine",
     )
 

@@ -14,8 +14,10 @@ compute stream and one side stream:
 3. per pass: ``arena_map_slots`` on its experts, a pass slot table that maps
    exactly those experts (copied from pinned host memory), ``arena_fill_async``
    of the misses on the side stream, and one ``moe_expert_ffn`` pass with
-   ``MOE_FFN_PARTIAL`` (the first pass also computes the shared expert);
-4. ``moe_ffn_combine`` writes the chunk's y.
+   ``MOE_FFN_PARTIAL`` (the first pass, flagged ``MOE_FFN_PARTIAL_FIRST``, also
+   computes the shared expert);
+4. ``moe_ffn_combine`` writes the chunk's y, and flags in the status word any
+   pair whose expert no pass computed.
 
 With ``cap <= S / 2`` the fills of pass p + 1 evict nothing pass p reads, so
 they wait only for pass p - 1 and overlap pass p's compute; with a larger cap
@@ -115,11 +117,13 @@ class ChunkedPrefill:
                 self.side.wait_event(self.computed[wait])
             self.arena.fill_async(self.side, self.filled[p])
             comp.wait_event(self.filled[p])
-            flags = lib.MOE_FFN_PARTIAL | (lib.MOE_FFN_PARTIAL_SHARED if p == 0 and self.shared is not None else 0)
+            flags = lib.MOE_FFN_PARTIAL | (lib.MOE_FFN_PARTIAL_FIRST if p == 0 else 0)
+            flags |= lib.MOE_FFN_PARTIAL_SHARED if p == 0 and self.shared is not None else 0
             lib.moe_expert_ffn(x, ids, wts, T, H, I, E, K, g, self.table_d[p], self.slots, self.stride, self.shared,
                                y, self.ws, self.ws_bytes, self.status, flags, comp)
             self.computed[p].record(comp)
-        lib.moe_ffn_combine(wts, T, H, I, E, K, self.shared is not None, y, self.ws, self.ws_bytes, comp)
+        lib.moe_ffn_combine(ids, wts, T, H, I, E, K, self.shared is not None, y, self.ws, self.ws_bytes, self.status,
+                            comp)
 
     def run_prompt(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, chunk: int, w_router=None) -> None:
         """The whole prompt in chunks of ``chunk`` tokens (the last one ragged)."""

@@ -1,14 +1,9 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
 Bars: expert ids bit-exact; routing weights within 1e-5; layer outputs within
-2e-2 * rms(y_ref) of the fp64 oracle beyond the output format's own rounding,
-i.e. |y - y_ref| <= 2e-2 * rms(y_ref) + ulp_bf16(y_ref) / 2 elementwise (the
-layer's outputs are heavy-tailed, max|y| / rms up to ~12, so rounding the exact
-result to bf16 alone can exceed 2e-2 * rms); paged and fully-resident runs
-bitwise equal.
+max|y - y_ref| <= 2e-2 * rms(y_ref) of the fp64 oracle (parity_util.check_close);
+paged and fully-resident runs bitwise equal.
 """
-
-import sys
 
 import numpy as np
 import pytest
@@ -18,59 +13,9 @@ from oracle import moe_ref as R
 from quantized_routed_expert_moe_amd import harness, lib
 from synth import gen
 
+from parity_util import DEV, TOL, OracleExperts, check_close, oracle_layer, say, y_f64  # noqa: F401
+
 pytestmark = pytest.mark.gpu
-DEV = "cuda:0"
-TOL = 2e-2
-
-
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
-def y_f64(y):
-    return y.float().cpu().numpy().astype(np.float64)
-
-
-class OracleExperts:
-    """Oracle experts built on demand from the seeded generator (never from the GPU)."""
-
-    def __init__(self, w, layer):
-        self.w, self.layer, self.cache = w, layer, {}
-
-    def __call__(self, e):
-        if e not in self.cache:
-            self.cache[e] = R.Expert(gen.expert_tensors(self.w.seed, self.layer, e, self.w.H, self.w.I), self.w.H,
-                                     self.w.I)
-        return self.cache[e]
-
-
-def oracle_layer(w, layer, x_bits, logits=None, renorm=False):
-    wr = gen.router_weight(w.seed, layer, w.E, w.H) if w.router == "gemv" else None
-    shared = None
-    if w.shared:
-        shared = R.Expert(gen.expert_tensors(w.seed, layer, gen.SHARED_EXPERT, w.H, w.I), w.H, w.I)
-    return R.moe_layer(x_bits, OracleExperts(w, layer), w.K, logits=logits, w_router=wr, shared=shared,
-                       renorm=renorm)
-
-
-def bf16_half_ulp(y):
-    """Half the bf16 spacing at each value: the rounding any bf16 output of it carries."""
-    a = np.abs(y)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    return np.where(a > 0, np.exp2(e - 8), 0.0)
-
-
-def check_close(y_gpu, y_ref, what):
-    d = np.abs(y_gpu - y_ref)
-    rms = np.sqrt(np.mean(y_ref**2))
-    beyond = np.max(d - bf16_half_ulp(y_ref))
-    say(f"{what}: max|err| / rms = {d.max() / rms if rms else float('nan'):.3e}, beyond the bf16 half-ulp "
-        f"{beyond / rms if rms else float('nan'):.3e}, max|y_ref| / rms = {np.abs(y_ref).max() / rms if rms else 0:.1f}")
-    if rms == 0:
-        assert d.max() == 0
-    else:
-        assert beyond <= TOL * rms
 
 
 def small(name, **kw):
@@ -524,36 +469,6 @@ def test_grouped_matches_oracle(w):
     assert torch.equal(run.y.view(torch.int16), first)
 
 
-def test_grouped_prefill_full_size_sampled_tokens():
-    """Prefill at full size (9940 tokens, 256 experts, top-8): sampled tokens vs the oracle."""
-    w = gen.WORKLOADS["prefill_t9940_h4096_e256_k8_i1536"]
-    say("packing 256 experts for the prefill layer")
-    logits = gen.normal_logits(w.seed, 0, w.T, w.E)
-    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
-    L = harness.make_layer(w, 0, DEV, logits=logits, x_bits=xb, place_seed=4)
-    run = harness.LayerRunner(w, DEV)
-    run(L)
-    torch.cuda.synchronize()
-    assert int(run.status.item()) == 0
-    ids_ref, w_ref = R.route(logits, w.K)
-    assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
-    counts = np.bincount(ids_ref.ravel(), minlength=w.E)
-    say(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}")
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(w.T, size=10, replace=False))
-    sample = np.concatenate([sample, [0, w.T - 1]])
-    experts = OracleExperts(w, 0)
-    y_ref, *_ = R.moe_layer(xb[sample], experts, w.K, logits=logits[sample])
-    y = y_f64(run.y)
-    check_close(y[sample], y_ref, "  prefill sampled tokens")
-    # the whole output is finite and the layer is deterministic
-    assert np.isfinite(y).all()
-    first = run.y.view(torch.int16).clone()
-    run.ffn(L)
-    torch.cuda.synchronize()
-    assert torch.equal(run.y.view(torch.int16), first)
-
-
 def test_grouped_equals_gemv_path_within_tolerance():
     """The two paths are separate kernels; on a shape both serve they agree to the oracle's bar."""
     w = gen.Workload("both_t24_h512_e12_k3_i256", 24, 512, 12, 3, 256, 1, 12, "normal", 55, shared=True)
@@ -638,24 +553,75 @@ def test_partial_flags_and_combine_errors():
     run.route(L)
     args = (L.x, run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 32, L.table, L.slots, L.stride)
     for flags, shared in ((lib.MOE_FFN_PARTIAL | lib.MOE_FORCE_GEMV, L.shared), (lib.MOE_FFN_PARTIAL_SHARED, L.shared),
-                          (lib.MOE_FFN_PARTIAL | lib.MOE_FFN_PARTIAL_SHARED, None)):
+                          (lib.MOE_FFN_PARTIAL | lib.MOE_FFN_PARTIAL_SHARED, None), (lib.MOE_FFN_PARTIAL_FIRST, L.shared)):
         with pytest.raises(lib.MoeError) as ex:
             lib.moe_expert_ffn(*args, shared, run.y, run.ws, run.ws_bytes, run.status, flags)
         assert ex.value.status == lib.MOE_EINVAL
     with pytest.raises(lib.MoeError) as ex:
-        lib.moe_ffn_combine(run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes - 1)
+        lib.moe_ffn_combine(run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes - 1, run.status)
     assert ex.value.status == lib.MOE_EWS
+    with pytest.raises(lib.MoeError) as ex:
+        lib.moe_ffn_combine(None, run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes, run.status)
+    assert ex.value.status == lib.MOE_EINVAL
     raw = lib.load().moe_ffn_combine  # the binding maps has_shared to 0 / 1; the C ABI takes only those
-    assert raw(run.wts.data_ptr(), w.T, w.H, w.I, w.E, w.K, 2, run.y.data_ptr(), run.ws.data_ptr(), run.ws_bytes,
-               None) == lib.MOE_EINVAL
-    lib.moe_ffn_combine(run.wts, 0, w.H, w.I, w.E, w.K, 1, None, None, 0)  # T = 0: a no-op
+    assert raw(run.ids.data_ptr(), run.wts.data_ptr(), w.T, w.H, w.I, w.E, w.K, 2, run.y.data_ptr(),
+               run.ws.data_ptr(), run.ws_bytes, run.status.data_ptr(), None) == lib.MOE_EINVAL
+    lib.moe_ffn_combine(run.ids, run.wts, 0, w.H, w.I, w.E, w.K, 1, None, None, 0, None)  # T = 0: a no-op
     # one partial pass with every expert resident, then the combine: the plain grouped result
-    lib.moe_expert_ffn(*args, L.shared, run.y, run.ws, run.ws_bytes, run.status,
-                       lib.MOE_FFN_PARTIAL | lib.MOE_FFN_PARTIAL_SHARED)
-    lib.moe_ffn_combine(run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes)
+    first = lib.MOE_FFN_PARTIAL | lib.MOE_FFN_PARTIAL_SHARED | lib.MOE_FFN_PARTIAL_FIRST
+    lib.moe_expert_ffn(*args, L.shared, run.y, run.ws, run.ws_bytes, run.status, first)
+    lib.moe_ffn_combine(run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes, run.status)
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     y_res = resident_grouped(L, w, L.x, L.logits, w.T)
+    assert torch.equal(run.y.view(torch.int16), y_res.view(torch.int16))
+
+
+def test_combine_reports_pairs_no_pass_computed():
+    """Exact or explicit failure for chunked passes: a pair whose expert no pass of the
+    chunk computed, a shared expert no pass computed, and a combine with no first pass
+    since the previous one each set the status word; the complete run still gives the
+    resident bits afterwards on the same workspace."""
+    w = gen.Workload("partial_t40_h256_e8_k2_i256_shared", 40, 256, 8, 2, 256, 1, 8, "normal", 63, shared=True)
+    L = harness.make_layer(w, 0, DEV)
+    run = harness.LayerRunner(w, DEV, lib.MOE_FFN_PARTIAL)
+    run.route(L)
+    torch.cuda.synchronize()
+    used = sorted(set(run.ids.cpu().numpy().ravel().tolist()))
+    assert len(used) >= 3
+    args = (L.x, run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 32)
+    full = L.table.clone()
+
+    def table_of(experts):
+        t = torch.full_like(full, -1)
+        for e in experts:
+            t[e] = full[e]
+        return t
+
+    def passes(tables, shared_pass=0, first=True):
+        for p, tb in enumerate(tables):
+            fl = lib.MOE_FFN_PARTIAL | (lib.MOE_FFN_PARTIAL_FIRST if first and p == 0 else 0)
+            fl |= lib.MOE_FFN_PARTIAL_SHARED if p == shared_pass else 0
+            lib.moe_expert_ffn(*args, tb, L.slots, L.stride, L.shared, run.y, run.ws, run.ws_bytes, run.status, fl)
+        lib.moe_ffn_combine(run.ids, run.wts, w.T, w.H, w.I, w.E, w.K, 1, run.y, run.ws, run.ws_bytes, run.status)
+        torch.cuda.synchronize()
+        st = int(run.status.item())
+        run.status.zero_()
+        return st
+
+    half = len(used) // 2
+    # two passes covering every used expert: no error, and the resident bits
+    assert passes([table_of(used[:half]), table_of(used[half:])]) == 0
+    y_res = resident_grouped(L, w, L.x, L.logits, w.T)
+    assert torch.equal(run.y.view(torch.int16), y_res.view(torch.int16))
+    # the last used expert in no pass
+    assert passes([table_of(used[:half]), table_of(used[half:-1])]) == lib.MOE_ENOTRES
+    # every routed expert, but the shared expert in no pass
+    assert passes([table_of(used)], shared_pass=-1) == lib.MOE_ENOTRES
+    # a chunk whose first pass is not flagged: the marks of the previous chunk must not count
+    assert passes([table_of(used)], first=False) == lib.MOE_EINVAL
+    # and again complete: same bits as the resident run
+    assert passes([table_of(used[half:]), table_of(used[:half])], shared_pass=1) == 0
     assert torch.equal(run.y.view(torch.int16), y_res.view(torch.int16))
 
 

@@ -483,3 +483,79 @@ def test_nvfp4_unit_scales_give_the_code_values():
     t = gen.expert_tensors_fmt(3, 0, 5, 64, 96, gen.FMT_NVFP4)
     sc = R.decode_e4m3(t["sg"])
     assert sc.min() >= 2.0**-6 and sc.max() < 2.0**-4 and t["sg"].shape == (96, 4) and t["global"].dtype == np.float32
+
+
+# ------------------------------------------------------------------ expert-major evaluation
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_expert_major_equals_per_pair_layer(shared):
+    """moe_layer_expert_major (one batched product per expert, then the rank-ordered
+    combine) gives moe_layer's ids and weights exactly and its y to float64 rounding,
+    with uneven expert loads, an expert nobody picks and repeated tokens."""
+    T, H, E, K, I = 37, 256, 9, 3, 160
+    rng = np.random.default_rng(31)
+    xb = bits_of(rng.standard_normal((T, H)))
+    xb[5] = xb[2]
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 4] = -50.0  # expert 4 never selected
+    logits[:, 7] += 1.5  # expert 7 in most tokens
+    experts = tiny_experts(9, E, H, I)
+    sh = R.Expert(gen.expert_tensors(9, 0, gen.SHARED_EXPERT, H, I), H, I) if shared else None
+    y1, ids1, w1, _ = R.moe_layer(xb, experts, K, logits=logits, shared=sh)
+    y2, ids2, w2, _ = R.moe_layer_expert_major(xb, experts, K, logits=logits, shared=sh)
+    assert np.array_equal(ids1, ids2) and np.array_equal(w1, w2)
+    assert 4 not in ids1 and (ids1 == 7).any(axis=1).sum() > T // 2
+    rms = np.sqrt(np.mean(y1**2))
+    assert np.abs(y2 - y1).max() <= 1e-13 * rms
+
+
+def test_expert_major_dense_limit_and_zero_input():
+    """K = E gives the textbook softmax mixture (torch's softmax); x = 0 gives y = 0."""
+    T, H, E, I = 4, 256, 5, 512
+    rng = np.random.default_rng(13)
+    xb = bits_of(rng.standard_normal((T, H)))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    experts = tiny_experts(5, E, H, I)
+    y, *_ = R.moe_layer_expert_major(xb, experts, E, logits=logits)
+    p = torch.softmax(torch.from_numpy(logits.astype(np.float64)), dim=1).numpy()
+    x = R.bf16_bits_to_f64(xb)
+    want = sum(p[:, e : e + 1] * experts[e](x) for e in range(E))
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-14)
+    y0, *_ = R.moe_layer_expert_major(np.zeros((T, H), np.uint16), experts, 2, logits=logits)
+    assert np.all(y0 == 0.0)
+
+
+def test_combine_rank_order_and_shared_term():
+    """combine adds the shared output and w[t, k] * o[t, k] for k = 0..K-1: checked on
+    values where each term is exactly representable, and the order against a sum whose
+    float64 result depends on it (1 + 2^-53 + 2^-53 rounds differently in the other order)."""
+    o = np.zeros((1, 3, 2))
+    o[0, :, 0] = [1.0, 2.0**-53, 2.0**-53]
+    o[0, :, 1] = [3.0, 5.0, 7.0]
+    w = np.array([[1.0, 1.0, 1.0]])
+    y = R.combine(o, w, shared_out=np.array([[0.0, 0.5]]))
+    assert y[0, 0] == 1.0  # (1 + 2^-53) rounds to 1, then again: rank order
+    assert y[0, 1] == 15.5
+    o2 = o[:, ::-1].copy()
+    assert R.combine(o2, w)[0, 0] == 1.0 + 2.0**-52  # the other order keeps both small terms
+
+
+def test_oracle_pool_expert_major_equals_oracle():
+    """The worker-pool evaluation the full-size GPU tests use (tests/oracle_pool.py) gives
+    moe_layer_expert_major's ids and weights exactly and its y to float64 rounding."""
+    import oracle_pool as OP
+
+    w = gen.Workload("pool_t50_h256_e6_k2_i128_shared", 50, 256, 6, 2, 128, 1, 6, "normal", 17, shared=True)
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    logits = gen.normal_logits(w.seed, 0, w.T, w.E)
+    experts = {e: R.Expert(gen.expert_tensors(w.seed, 0, e, w.H, w.I), w.H, w.I) for e in range(w.E)}
+    shared = R.Expert(gen.expert_tensors(w.seed, 0, gen.SHARED_EXPERT, w.H, w.I), w.H, w.I)
+    y1, ids1, w1, _ = R.moe_layer_expert_major(xb, experts, w.K, logits=logits, shared=shared)
+    with OP.pool(2) as ex:
+        y2, ids2, w2 = OP.expert_major_layer(ex, w, 0, xb, logits)
+        y3, ids3, w3, _ = ex.submit(OP.layer_ref, w, 0, xb, logits).result()
+    assert np.array_equal(ids1, ids2) and np.array_equal(w1, w2) and np.array_equal(ids1, ids3)
+    rms = np.sqrt(np.mean(y1**2))
+    assert np.abs(y2 - y1).max() <= 1e-13 * rms
+    assert np.abs(y3 - y1).max() <= 1e-13 * rms
