@@ -25,9 +25,10 @@
 //      matching g and u and writes h = silu(g) * u in fp16 (the next A
 //      operand; overflow sets the status word).
 //   4. down GEMM (grouped_gemm_kernel<1>): A = h rows, B = fp16(q * s) of the
-//      down matrix; o is written in bf16 at the pair's own index (one
-//      rounding, relative error <= 2^-9, of each routed term; bf16 rather than
-//      fp16 because an expert's output row is not bounded by 65504).
+//      down matrix; o is written in fp32 at the pair's own index (no rounding
+//      before the combine: a routed term rounded to bf16 would carry up to
+//      2^-8 of its own magnitude into y, which the 2e-2 * rms bar cannot
+//      absorb when the weighted terms are several times rms(y)).
 //   5. combine: y[t] = o_shared[t] + sum_k w[t][k] * o[t][k] in rank order,
 //      fp32, rounded once to bf16.
 #include <type_traits>
@@ -76,7 +77,7 @@ __host__ __device__ inline GroupedWs grouped_ws(int T, int H, int I, int E, int 
   w.xh = al256(w.sorted + PA * sizeof(int32_t));
   w.h = al256(w.xh + (size_t)T * H * 2);
   w.o = al256(w.h + PA * (size_t)I * 2);
-  w.done = al256(w.o + PA * (size_t)H * 2);  // o: bf16
+  w.done = al256(w.o + PA * (size_t)H * 4);  // o: fp32
   w.bytes = al256(w.done + ((size_t)E + 2) * sizeof(int32_t));
   return w;
 }
@@ -577,7 +578,7 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
       }
     }
   } else {
-    uint16_t* ows = reinterpret_cast<uint16_t*>(a.ws + W.o);
+    float* ows = reinterpret_cast<float*>(a.ws + W.o);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -588,7 +589,7 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
 #pragma unroll
           for (int n = 0; n < 4; ++n) {
             const int col = nt * kTN + wave * 64 + n * 16 + (lane & 15);
-            if (col < H) ows[(size_t)p * H + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][n][v]);
+            if (col < H) ows[(size_t)p * H + col] = acc[i][n][v];
           }
         }
       }
@@ -597,18 +598,15 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
 }
 
 // ------------------------------------------------------------------ combine
-// Thread: 8 consecutive columns of one token; every o row of the token is
-// loaded (16 bytes each) before the sums, which run in rank order.
-__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
+// Thread: 8 consecutive columns of one token; the token's o rows (fp32, 32 bytes
+// each) are loaded eight at a time before the sums, which run in rank order.
 __global__ void __launch_bounds__(256) grouped_combine_kernel(FfnArgs a) {
   const int H = a.H, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(T, H, a.I, a.E, K, has_shared);
-  const uint4* o8 = reinterpret_cast<const uint4*>(a.ws + W.o);  // 8 bf16 per uint4
+  const float4* o4 = reinterpret_cast<const float4*>(a.ws + W.o);  // 4 fp32 per float4
   const int P = T * K;
-  const int H8 = H / 8;
+  const int H8 = H / 8, H4 = H / 4;
   const size_t n8 = (size_t)T * H8;
   const bool check = a.mode & kModeCheckDone;
   const int32_t* done = reinterpret_cast<const int32_t*>(a.ws + W.done);
@@ -627,33 +625,31 @@ __global__ void __launch_bounds__(256) grouped_combine_kernel(FfnArgs a) {
       if (missing) *a.status = MOE_ENOTRES;
     }
     float acc[8];
-    {
-      const uint4 v = has_shared ? o8[(size_t)(P + t) * H8 + c8] : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    if (has_shared) {
+      const float4 v0 = o4[(size_t)(P + t) * H4 + 2 * c8], v1 = o4[(size_t)(P + t) * H4 + 2 * c8 + 1];
+      acc[0] = v0.x, acc[1] = v0.y, acc[2] = v0.z, acc[3] = v0.w;
+      acc[4] = v1.x, acc[5] = v1.y, acc[6] = v1.z, acc[7] = v1.w;
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = bf16_lo(d[e]);
-        acc[2 * e + 1] = bf16_hi(d[e]);
-      }
+      for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     }
     for (int k0 = 0; k0 < K; k0 += 8) {
-      uint4 ov[8];
+      float4 ov[8][2];
       float wv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int k = k0 + j < K ? k0 + j : K - 1;
-        ov[j] = o8[(size_t)(t * K + k) * H8 + c8];
+        ov[j][0] = o4[(size_t)(t * K + k) * H4 + 2 * c8];
+        ov[j][1] = o4[(size_t)(t * K + k) * H4 + 2 * c8 + 1];
         wv[j] = a.w[t * K + k];
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (k0 + j < K) {
-          const uint32_t d[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
+          const float d[8] = {ov[j][0].x, ov[j][0].y, ov[j][0].z, ov[j][0].w,
+                              ov[j][1].x, ov[j][1].y, ov[j][1].z, ov[j][1].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = fmaf(wv[j], bf16_lo(d[e]), acc[2 * e]);
-            acc[2 * e + 1] = fmaf(wv[j], bf16_hi(d[e]), acc[2 * e + 1]);
-          }
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(wv[j], d[e], acc[e]);
         }
       }
     }

@@ -106,14 +106,18 @@ def test_format_paths_report_fp16_overflow(fmt, kind, T):
     assert int(st.item()) == lib.MOE_EUNSUP
 
 
-@pytest.mark.parametrize("T", [1, 5])
-def test_gemv_path_computes_large_activations(T):
-    """The GEMV path (bf16 x, fp32 h) takes the activations that overflow fp16 on the
-    other paths and matches the oracle."""
-    w = gen.Workload(f"large_x_gemv_t{T}", T, 256, 8, 2, 512, 1, 8, "normal", 304, shared=True)
+@pytest.mark.parametrize("T,H,I", [(1, 256, 96), (5, 96, 512)])
+def test_gemv_path_computes_large_activations(T, H, I):
+    """The general GEMV kernels (bf16 x, fp32 h; the shapes the single-token and batched
+    kernels do not take: I / 32 not a multiple of 16 for one token, H not a multiple of 64
+    for several) compute activations whose h overflows fp16, against the oracle."""
+    from parity_util import OracleExperts
+
+    w = gen.Workload(f"large_x_gemv_t{T}_h{H}_i{I}", T, H, 8, 2, I, 1, 8, "normal", 304, shared=True)
     xb = big_x("h", T, w.H, 10)
     logits = gen.normal_logits(w.seed, 0, T, w.E)
     y_ref, ids_ref, _, _ = oracle_layer(w, 0, xb, logits=logits)
+    assert max_h(OracleExperts(w, 0), xb, ids_ref) > FP16_MAX
     L = harness.make_layer(w, 0, DEV, logits=logits, x_bits=xb)
     run = harness.LayerRunner(w, DEV, lib.MOE_FORCE_GEMV)
     run(L)
