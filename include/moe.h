@@ -281,6 +281,24 @@ int moe_layer(const uint16_t* x, const float* w_router, float* logits, int T, in
               size_t stride, const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
               int32_t* dev_status, unsigned ffn_flags, moe_stream_t stream);
 
+/* moe_layer_noalloc: moe_layer for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). It allocates nothing: its workspace is the library's own static
+ * device array of moe_noalloc_scratch_bytes() bytes (64 MiB) on each GPU, held
+ * from the first call on that GPU until the process ends. Arguments, results
+ * and errors are those of moe_layer without ws and ws_bytes; in addition
+ * MOE_EWS when moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, ffn_flags)
+ * exceeds that size, and MOE_EINVAL for the MOE_FFN_PARTIAL* flags (a partial
+ * pass leaves its results in a workspace the caller cannot pass on to
+ * moe_ffn_combine). All calls on one GPU share its array: calls that overlap
+ * on one GPU (on other streams or host threads) race and must be serialised
+ * by the caller. */
+size_t moe_noalloc_scratch_bytes(void);
+int moe_layer_noalloc(const uint16_t* x, const float* w_router, float* logits, int T, int H, int I, int E, int K,
+                      int g, unsigned route_flags, int32_t* ids, float* w, const int32_t* slot_table,
+                      const void* slots, size_t stride, const void* shared_blob, uint16_t* y, int32_t* dev_status,
+                      unsigned ffn_flags, moe_stream_t stream);
+
 /* ------------------------------------------------------------------ expert arena
  * A fixed-slot expert arena for one layer ("Strata on a Mac", Status: the
  * expert cache at 64 slots; "Strata" README, Architecture: an LRU lease per

@@ -40,6 +40,8 @@ EXPORTS = (
     "moe_ffn_gate_up",
     "moe_ffn_down",
     "moe_layer",
+    "moe_noalloc_scratch_bytes",
+    "moe_layer_noalloc",
     "moe_ffn_combine",
     "moe_fmt_blob_bytes",
     "moe_fmt_slot_stride",
@@ -124,6 +126,11 @@ def load(path: str | None = None):
             _I,
             [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P, _P, _SZ, _P, _P, _P, _SZ, _P,
              ctypes.c_uint, _P],
+        ),
+        "moe_noalloc_scratch_bytes": (_SZ, []),
+        "moe_layer_noalloc": (
+            _I,
+            [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_uint, _P, _P, _P, _P, _SZ, _P, _P, _P, ctypes.c_uint, _P],
         ),
         "moe_ffn_combine": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P, _P]),
         "moe_fmt_blob_bytes": (_SZ, [_I, _I, _I]),
@@ -292,6 +299,22 @@ def moe_layer(x, w_router, logits, T, H, I, E, K, g, route_flags, ids, w, slot_t
             _ptr(dev_status), ffn_flags, _stream(stream),
         ),
         "moe_layer",
+    )
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return load().moe_noalloc_scratch_bytes()
+
+
+def moe_layer_noalloc(x, w_router, logits, T, H, I, E, K, g, route_flags, ids, w, slot_table, slots, stride,
+                      shared_blob, y, dev_status, ffn_flags=0, stream=None) -> None:
+    _check(
+        load().moe_layer_noalloc(
+            _ptr(x), _ptr(w_router), _ptr(logits), T, H, I, E, K, g, route_flags, _ptr(ids), _ptr(w),
+            _ptr(slot_table), _ptr(slots), stride, _ptr(shared_blob), _ptr(y), _ptr(dev_status), ffn_flags,
+            _stream(stream),
+        ),
+        "moe_layer_noalloc",
     )
 
 
