@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=3, help="decode layers in the oracle's timed sample")
     p.add_argument("--graph", type=int, default=1, help="replay the decode layer stack as a HIP graph")
+    p.add_argument("--onepass", type=int, default=1,
+                   help="decode headline with one-pass routing fused into the gate/up dispatch (MOE_ROUTE_ONEPASS); "
+                        "the other routing is timed beside it")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="first run one plain device-to-device copy of this many MiB (counter calibration for profiles)")
     return p.parse_args()
@@ -125,7 +128,9 @@ def decode_leg(a, dev):
     w = gen.Workload(base.name, base.T, base.H, base.E, base.K, base.I, a.layers, base.slots, base.router, base.seed)
     log(f"decode: building {w.layers} layers of {w.name}")
     stacks = harness.decode_stack(w, dev, log)
-    stack = harness.StackRunner(w, stacks, dev)  # one moe_layer per layer, each layer with its own outputs
+    # one moe_layer per layer, each layer with its own outputs; route_flags picks the routing
+    stack = harness.StackRunner(w, stacks, dev, route_flags=lib.MOE_ROUTE_ONEPASS if a.onepass else 0)
+    other = harness.StackRunner(w, stacks, dev, route_flags=0 if a.onepass else lib.MOE_ROUTE_ONEPASS)
     run = harness.LayerRunner(w, dev)  # per-stage timings below
     stream = torch.cuda.Stream()
     blob = lib.moe_blob_bytes(w.H, w.I)
@@ -176,6 +181,28 @@ def decode_leg(a, dev):
     after = stack.outputs()  # the timed steps left the same bits in every layer
     if not all(np.array_equal(e_.view(np.uint8), r_.view(np.uint8)) for e_, r_ in zip(eager, after)):
         raise RuntimeError("the timed decode steps left outputs that differ from the eager step")
+    # the other routing on the same layers: the same bits, timed the same way
+    with torch.cuda.stream(stream):
+        for _ in range(a.warmup):
+            other.step(stream)
+    stream.synchronize()
+    if not all(np.array_equal(e_.view(np.uint8), r_.view(np.uint8)) for e_, r_ in zip(eager, other.outputs())):
+        raise RuntimeError("one-pass and two-dispatch routing give different outputs")
+    if a.graph:
+        other.capture(stream)
+    o0, o1 = ev(), ev()
+    o0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(a.steps):
+            if other.graph is not None:
+                other.graph.replay()
+            else:
+                other.step(stream)
+    o1.record(stream)
+    torch.cuda.synchronize()
+    other_ms = o0.elapsed_time(o1) / a.steps
+    if int(other.status.item()) != 0:
+        raise RuntimeError(f"device status {int(other.status.item())}")
 
     # per-stage durations: each stage launched for every layer back to back on the
     # launch stream (each layer with its own routed experts), 3 passes, HIP events
@@ -214,6 +241,8 @@ def decode_leg(a, dev):
         "ms_step": ms_step,
         "wall": wall,
         "graph": stack.graph is not None,
+        "onepass": bool(a.onepass),
+        "other_ms_step": other_ms,
         "layer_gbs": layer_gbs,
         "us": us,
         "bytes": {"router": bytes_router, "gate_up": bytes_gate_up, "down": bytes_down, "layer": bytes_layer},
@@ -894,7 +923,11 @@ def main():
             "group": w.g,
             "arena_slots": w.slots,
             "hip_graph": d["graph"],
+            "routing": "one-pass (router GEMV + top-k + gate/up in one dispatch)" if d["onepass"]
+            else "two dispatches (router GEMV, then top-k) before the gate/up dispatch",
         },
+        # the same layers and tokens with the other routing (same bits, checked)
+        "other_routing_tokens_per_s": round(1000.0 / d["other_ms_step"], 2),
         "hbm_gbs": round(d["layer_gbs"], 1),
         "hbm_frac": round(d["layer_gbs"] / HBM_PEAK_GBS, 4),
         "per_layer_us": {k: round(v, 2) for k, v in d["us"].items()} | {"step_avg": round(d["ms_step"] * 1e3 / w.layers, 2)},

@@ -76,6 +76,7 @@ enum moe_format {
 
 enum moe_flags {
   MOE_ROUTE_RENORM = 1u << 0,  /* moe_route: divide the K selected weights by their sum */
+  MOE_ROUTE_ONEPASS = 1u << 1, /* moe_layer (route_flags): one-pass routing fused with the gate/up dispatch */
   MOE_FORCE_GEMV = 1u << 8,    /* moe_expert_ffn: use the per-expert GEMV path whatever T is */
   MOE_FORCE_GROUPED = 1u << 9, /* moe_expert_ffn: use the expert-grouped MFMA GEMM path */
   MOE_FFN_PARTIAL = 1u << 10,  /* moe_expert_ffn: one pass of a chunked paged run (see moe_ffn_combine) */
@@ -149,6 +150,28 @@ int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, in
 int moe_route_scored(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K, int score,
                      const float* bias, float routed_scale, unsigned flags, int32_t* ids, float* w,
                      moe_stream_t stream);
+
+/* moe_route_onepass: moe_route of one token with a router GEMV (T = 1), the
+ * router GEMV and the softmax top-k in ONE dispatch ("Strata on a Mac",
+ * Switches: the router GEMV and moe_route fused into one dispatch; the page
+ * reports that its relaxed-atomics hand-off to the last threadgroup read stale
+ * logits). Workgroup e computes logit e and publishes it in its own 64-bit word
+ * (a 32-bit call number with the value); the last workgroup waits until all E
+ * words carry this call's number, then selects. No word depends on another's
+ * ordering, so no cache writeback or invalidation is needed, and the bits of
+ * logits, ids and w equal moe_route's.
+ *   ws        device, ws_bytes >= moe_route_onepass_ws_bytes(E, K). It must be
+ *             all zero before its first one-pass call (zero it once; the calls
+ *             keep it consistent), and zeroed again after it is used for
+ *             anything else or a call reported an error. One-pass calls on one
+ *             workspace must not overlap (one stream, or ordered).
+ *   dev_status device int32, zeroed by the caller: MOE_EHIP when the words did
+ *             not arrive within a bounded wait (workspace not zeroed, or
+ *             overlapping calls); the outputs are then unspecified.
+ * Other arguments as moe_route with T = 1; H <= 8192. */
+size_t moe_route_onepass_ws_bytes(int E, int K); /* 0 on an unsupported E or K */
+int moe_route_onepass(const uint16_t* x, const float* w_router, float* logits, int H, int E, int K, unsigned flags,
+                      int32_t* ids, float* w, void* ws, size_t ws_bytes, int32_t* dev_status, moe_stream_t stream);
 
 /* ------------------------------------------------------------------ expert FFN
  * moe_expert_ffn: y[t] = shared(x[t]) + sum_{k=0..K-1} w[t][k] * FFN_{ids[t][k]}(x[t])
@@ -275,7 +298,17 @@ int moe_ffn_combine(const int32_t* ids, const float* w, int T, int H, int I, int
  * the router GEMV and moe_route run before the expert FFN); ids and w are
  * outputs. A route error returns before the FFN is enqueued. For a resident
  * arena: a paged caller needs ids on the host before the FFN and uses
- * moe_route, arena_map_slots and arena_fill_async, then moe_expert_ffn. */
+ * moe_route, arena_map_slots and arena_fill_async, then moe_expert_ffn.
+ * route_flags may add MOE_ROUTE_ONEPASS for one token (T = 1) with a router
+ * GEMV on the single-token path: the router GEMV, the selection and the gate/up
+ * stage run as one dispatch (as moe_route_onepass; the gate/up workgroups wait
+ * for their expert's slot word), then the down stage; the same bits as
+ * without it. Its hand-off words live in ws, which must then be all zero
+ * before the first such call on it, zeroed again after it is used for
+ * anything else or a call reported an error, and not shared by overlapping
+ * calls; a hand-off that does not complete within a bounded wait sets
+ * *dev_status = MOE_EHIP. Other cases with MOE_ROUTE_ONEPASS return
+ * MOE_EUNSUP. */
 int moe_layer(const uint16_t* x, const float* w_router, float* logits, int T, int H, int I, int E, int K, int g,
               unsigned route_flags, int32_t* ids, float* w, const int32_t* slot_table, const void* slots,
               size_t stride, const void* shared_blob, uint16_t* y, void* ws, size_t ws_bytes,
@@ -290,7 +323,7 @@ int moe_layer(const uint16_t* x, const float* w_router, float* logits, int T, in
  * MOE_EWS when moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, ffn_flags)
  * exceeds that size, and MOE_EINVAL for the MOE_FFN_PARTIAL* flags (a partial
  * pass leaves its results in a workspace the caller cannot pass on to
- * moe_ffn_combine). All calls on one GPU share its array: calls that overlap
+ * moe_ffn_combine) and for MOE_ROUTE_ONEPASS (its workspace must start at zero). All calls on one GPU share its array: calls that overlap
  * on one GPU (on other streams or host threads) race and must be serialised
  * by the caller. */
 size_t moe_noalloc_scratch_bytes(void);

@@ -183,10 +183,31 @@ extern "C" int moe_ffn_down(const uint16_t* x, const int32_t* ids, const float* 
                           dev_status, flags, stream, 1);
 }
 
+extern "C" size_t moe_route_onepass_ws_bytes(int E, int K) {
+  if (E <= 0 || K <= 0 || E > moe::kMaxE || K > moe::kMaxK) return 0;
+  return moe::onepass_region_bytes(E, K);
+}
+
+extern "C" int moe_route_onepass(const uint16_t* x, const float* w_router, float* logits, int H, int E, int K,
+                                 unsigned flags, int32_t* ids, float* w, void* ws, size_t ws_bytes, int32_t* dev_status,
+                                 moe_stream_t stream) {
+  if (!x || !w_router || !logits || !ids || !w || !dev_status || H <= 0 || E <= 0 || K <= 0 || K > E)
+    return MOE_EINVAL;
+  if (flags & ~(unsigned)MOE_ROUTE_RENORM) return MOE_EINVAL;
+  if (E > moe::kMaxE || K > moe::kMaxK || H % moe::kGroup || H > 8192) return MOE_EUNSUP;
+  if (!ws || ws_bytes < moe::onepass_region_bytes(E, K)) return MOE_EWS;
+  if (moe::launch_route_onepass(x, w_router, logits, H, E, K, flags, ids, w, static_cast<uint64_t*>(ws), dev_status,
+                                static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
 extern "C" int moe_layer(const uint16_t* x, const float* w_router, float* logits, int T, int H, int I, int E, int K,
                          int g, unsigned route_flags, int32_t* ids, float* w, const int32_t* slot_table,
                          const void* slots, size_t stride, const void* shared_blob, uint16_t* y, void* ws,
                          size_t ws_bytes, int32_t* dev_status, unsigned ffn_flags, moe_stream_t stream) {
+  const bool onepass = (route_flags & MOE_ROUTE_ONEPASS) != 0;
+  route_flags &= ~(unsigned)MOE_ROUTE_ONEPASS;
   // One token on the single-token path: the routing kernel also resolves the
   // chosen experts' slots into the end of the workspace (same results, one
   // dependent load less in each FFN kernel). Everything the FFN call checks is
@@ -198,10 +219,45 @@ extern "C" int moe_layer(const uint16_t* x, const float* w_router, float* logits
                     stride >= moe_blob_bytes(H, I, g) && stride % 256 == 0 && w_router && x && H <= 8192 && logits && ids &&
                     w &&
                     !(route_flags & ~(unsigned)MOE_ROUTE_RENORM);
+  if (onepass && !dec1) {
+    // one-pass routing covers one token with a router GEMV on the single-token path;
+    // anything else is reported, never run another way
+    if (!x || !logits || !ids || !w || !slot_table || !slots || !y || !dev_status || K <= 0 || E <= 0 || K > E)
+      return MOE_EINVAL;
+    if (route_flags & ~(unsigned)MOE_ROUTE_RENORM) return MOE_EINVAL;
+    if (T != 1 || !w_router || (ffn_flags & ~(unsigned)MOE_FORCE_GEMV) || !moe::shape_ok(H, I, g) ||
+        E > moe::kMaxE || K > moe::kMaxK || H > 8192 || !moe::decode1_supported(T, H, I, K, shared_blob != nullptr))
+      return MOE_EUNSUP;
+    if (stride < moe_blob_bytes(H, I, g) || stride % 256) return MOE_EINVAL;
+    return MOE_EWS;  // every other condition holds: the workspace is missing or short
+  }
   if (dec1) {
     int32_t* pre = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
                                               moe::decode1_slots_offset(H, I, K, shared_blob != nullptr));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (onepass) {
+      moe::FfnArgs a{};
+      a.x = x;
+      a.ids = ids;
+      a.w = w;
+      a.T = T;
+      a.H = H;
+      a.I = I;
+      a.E = E;
+      a.K = K;
+      a.slot_table = slot_table;
+      a.slots = static_cast<const uint8_t*>(slots);
+      a.stride = stride;
+      a.shared_blob = static_cast<const uint8_t*>(shared_blob);
+      a.y = y;
+      a.ws = static_cast<uint8_t*>(ws);
+      a.ws_bytes = ws_bytes;
+      a.status = dev_status;
+      a.pre_slots = pre;
+      moe::OnepassRoute r{w_router, logits, ids, w, route_flags,
+                          reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(pre) + 256)};
+      return moe::launch_ffn_decode1_onepass(a, r, s) == hipSuccess ? MOE_OK : MOE_EHIP;
+    }
     if (moe::launch_router_gemv(x, w_router, logits, T, H, E, s) != hipSuccess) return MOE_EHIP;
     if (moe::launch_route_select(logits, T, E, K, route_flags, ids, w, s, MOE_SCORE_SOFTMAX, nullptr, 1.0f, slot_table,
                                  pre) != hipSuccess)

@@ -43,6 +43,7 @@
 // No atomics and no data-dependent reduction order: results depend only on
 // the inputs, never on slot addresses.
 #include "moe_internal.h"
+#include "onepass.h"
 #include "wave_ops.h"
 
 namespace moe {
@@ -89,10 +90,25 @@ __device__ inline int xcd_item(int bid, int n_items) {
   return n_items % kXcds == 0 ? (bid % kXcds) * (n_items / kXcds) + bid / kXcds : bid;
 }
 
+// One-pass path: the blob of unit u from the selector's slot word of this call.
+__device__ inline const uint8_t* onepass_unit_blob(const FfnArgs& a, int u, bool has_shared, const uint64_t* words,
+                                                   uint32_t ep) {
+  const int k = has_shared ? u - 1 : u;
+  if (k < 0) return a.shared_blob;
+  const int32_t slot = onepass_wait_slot(words, a.E, k, ep);
+  if (slot < 0) {
+    *a.status = slot == (int32_t)0x80000000 ? MOE_EHIP : MOE_ENOTRES;  // hand-off timed out / not resident
+    return nullptr;
+  }
+  return a.slots + (size_t)slot * a.stride;
+}
+
 // ------------------------------------------------------------------ gate/up
 // GPL = groups per lane = ceil(GW / 8) with GW = ceil(G / 4) groups per wave.
-template <int GPL>
-__global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
+// bid: the workgroup's index among the gate/up workgroups. ONEPASS: the unit's
+// slot comes from the one-pass hand-off words (epoch ep) instead of the table.
+template <int GPL, bool ONEPASS>
+__device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const uint64_t* words, uint32_t ep) {
   // LDS per wave: x slice as fp16 pairs [GW][16] dwords + group corrections [GW]
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float part[2][kWaves][8];
@@ -112,7 +128,7 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
   const_i32p pre = (const_i32p)a.pre_slots;
   asm volatile("" : "+s"(pre));
   const int n_hb = I / 8;
-  const int item = xcd_item(blockIdx.x, (K + (has_shared ? 1 : 0)) * n_hb);
+  const int item = xcd_item(bid, (K + (has_shared ? 1 : 0)) * n_hb);
   const int u = item / n_hb, hb = item % n_hb;
   // 1. this wave's slice of x: uint4 q (8 bf16) of the slice = columns 8q .. 8q+7
   //    (issued before the two dependent loads that find the unit's blob)
@@ -123,7 +139,8 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
     q = q < G * 4 ? q : G * 4 - 1;
     xv[v] = reinterpret_cast<const uint4*>(a.x)[q];
   }
-  const uint8_t* blob = dec_unit_blob(a, u, has_shared, a.ids, pre);
+  const uint8_t* blob =
+      ONEPASS ? onepass_unit_blob(a, u, has_shared, words, ep) : dec_unit_blob(a, u, has_shared, a.ids, pre);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
   const int n = hb * 8 + r;
@@ -225,6 +242,47 @@ __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
   }
 }
 
+template <int GPL>
+__global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
+  dec_gateup_body<GPL, false>(a, blockIdx.x, nullptr, 0);
+}
+
+// moe_layer's one-pass single-token path in one dispatch: workgroups 0 .. E-1
+// compute the router logits and publish them (onepass.h); the last of them
+// selects, writes logits, ids, w and the resolved slots (for the down kernel),
+// and publishes each rank's slot; the other workgroups are the gate/up items,
+// which stage x and then wait for their unit's slot word. The arithmetic is
+// that of router_gemv1_kernel, route_select_kernel and dec_gateup_kernel, so
+// the results are the same bits. Workgroups are dispatched in index order on
+// each XCD and the GEMV workgroups wait for nothing, so every word that a
+// waiting workgroup needs is eventually written (each wait is also bounded).
+template <int GPL, int EPL>
+__global__ void __launch_bounds__(kThreads) dec_route_gateup_kernel(FfnArgs a, OnepassRoute r) {
+  const uint32_t ep = onepass_epoch(r.words);
+  const int E = a.E;
+  if ((int)blockIdx.x >= E) {
+    dec_gateup_body<GPL, true>(a, blockIdx.x - E, r.words, ep);
+    return;
+  }
+  __shared__ double part[4];
+  onepass_publish_logit(a.x, r.w_router, a.H, blockIdx.x, r.words, ep, part);
+  if ((int)blockIdx.x != E - 1 || threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int32_t id;
+  float wt;
+  const bool ok = onepass_select<EPL>(r.words, E, a.K, r.flags, ep, r.logits, a.status, id, wt);
+  if (lane < a.K) {
+    int32_t slot = (int32_t)0x80000000;  // the hand-off failed: consumers report it
+    if (ok) {
+      r.ids[lane] = id;
+      r.w[lane] = wt;
+      slot = a.slot_table[id];
+      const_cast<int32_t*>(a.pre_slots)[lane] = slot;
+    }
+    ll_store(r.words + 1 + E + lane, ep, (uint32_t)slot);
+  }
+}
+
 // ------------------------------------------------------------------ down + combine
 // CPL = columns per lane; a wave owns CW = 16 * CPL consecutive columns.
 template <int CPL>
@@ -306,6 +364,10 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
       }
     }
   }
+  // after a one-pass dispatch: every workgroup of it has read the region's call
+  // number (that dispatch has completed), so the call is numbered done here
+  if (a.onepass && blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(a.onepass, (uint64_t)onepass_epoch(a.onepass), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // this wave's entries of the partial sums start at zero (only this wave writes them)
   for (int q = lane; q < kMaxUnits * 4; q += 64) (&part[wave][0][0])[q] = 0.0f;
   // 2. codes and scale dwords of every step; a step is one unit for all lanes
@@ -434,6 +496,40 @@ bool decode1_supported(int T, int H, int I, int K, bool has_shared) {
   const int G = H / kGroup, Gd = I / kGroup;
   // gate/up: at most 4 groups per lane; down: whole steps of 16 columns per unit, at most 8 per lane
   return T == 1 && G <= 4 * 8 * 4 && Gd % 16 == 0 && H % 4 == 0 && dec_down_cpl(n_units, Gd) <= 8;
+}
+
+hipError_t launch_ffn_decode1_onepass(const FfnArgs& a, const OnepassRoute& r, hipStream_t s) {
+  const bool has_shared = a.shared_blob != nullptr;
+  const int n_units = a.K + (has_shared ? 1 : 0);
+  const int G = a.H / kGroup;
+  const int GW = (G + kWaves - 1) / kWaves;
+  const int gpl = (GW + 7) / 8;
+  const int epl = (a.E + 63) / 64;
+  const size_t lds = (size_t)kWaves * GW * 17 * 4;
+  const int grid = a.E + n_units * (a.I / 8);
+#define RG(N, M)                                                                                    \
+  do {                                                                                              \
+    set_lds_limit(reinterpret_cast<const void*>(&dec_route_gateup_kernel<N, M>), lds);              \
+    hipLaunchKernelGGL((dec_route_gateup_kernel<N, M>), dim3(grid), dim3(kThreads), lds, s, a, r);  \
+  } while (0)
+#define RGE(N)               \
+  do {                       \
+    if (epl <= 1) RG(N, 1);  \
+    else if (epl <= 2) RG(N, 2); \
+    else if (epl <= 4) RG(N, 4); \
+    else if (epl <= 8) RG(N, 8); \
+    else RG(N, 16);          \
+  } while (0)
+  if (gpl <= 1) RGE(1);
+  else if (gpl <= 2) RGE(2);
+  else RGE(4);
+#undef RGE
+#undef RG
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FfnArgs d = a;
+  d.onepass = r.words;
+  return launch_ffn_decode1(d, 1, s);
 }
 
 hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {

@@ -478,8 +478,9 @@ inline int pow2_at_least(int v) {
 
 }  // namespace
 
+// one token: the K resolved slots (256 bytes), then the one-pass routing region
 size_t gemv_workspace_bytes(int T, int H, int I, int K, int has_shared) {
-  return gemv_ws(T, H, I, K, has_shared).bytes + (T == 1 ? 256 : 0);
+  return gemv_ws(T, H, I, K, has_shared).bytes + (T == 1 ? 256 + onepass_region_bytes(kMaxE, kMaxK) : 0);
 }
 
 size_t decode1_slots_offset(int H, int I, int K, int has_shared) { return gemv_ws(1, H, I, K, has_shared).bytes; }

@@ -99,6 +99,14 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigne
                                float* w, hipStream_t s, int score = MOE_SCORE_SOFTMAX, const float* bias = nullptr,
                                float scale = 1.0f, const int32_t* slot_table = nullptr, int32_t* slots_out = nullptr);
 
+// One-pass routing (onepass.h): the hand-off region of one token's routing,
+// 64-bit words [0] call number, [1 + e] logit of expert e, [1 + E + k] slot of rank k.
+__host__ __device__ inline size_t onepass_region_bytes(int E, int K) {
+  return (((size_t)1 + E + K) * 8 + 255) & ~(size_t)255;
+}
+hipError_t launch_route_onepass(const uint16_t* x, const float* wr, float* logits, int H, int E, int K, unsigned flags,
+                                int32_t* ids, float* w, uint64_t* words, int32_t* status, hipStream_t s);
+
 struct FfnArgs {
   const uint16_t* x;
   const int32_t* ids;
@@ -116,7 +124,21 @@ struct FfnArgs {
   // single-token path only, else nullptr: slot of routed expert k (rank order),
   // already resolved through slot_table by the routing kernel
   const int32_t* pre_slots;
+  // single-token down kernel after a one-pass route + gate/up dispatch: the
+  // region whose call number it advances; else nullptr
+  uint64_t* onepass;
 };
+// The router side of moe_layer's one-pass single-token path.
+struct OnepassRoute {
+  const float* w_router;
+  float* logits;
+  int32_t* ids;  // ids and w written by the selector (FfnArgs ids / w are the same buffers)
+  float* w;
+  unsigned flags;  // MOE_ROUTE_RENORM
+  uint64_t* words;
+};
+// one dispatch: router GEMV, selection and gate/up; then the down kernel
+hipError_t launch_ffn_decode1_onepass(const FfnArgs& a, const OnepassRoute& r, hipStream_t s);
 // A partial pass of the grouped path: only routed experts with a slot are
 // computed (the others are skipped without error), the per-pair outputs stay in
 // the workspace and y is not written; kModePartialShared: this pass also

@@ -5,6 +5,7 @@
 // Softmax and the tie rule (equal logits -> lower id) follow the plain reading
 // of a softmax top-k router.
 #include "moe_internal.h"
+#include "onepass.h"
 #include "wave_ops.h"
 
 namespace moe {
@@ -68,51 +69,40 @@ __global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __rest
   }
 }
 
-// Single token: one workgroup per expert; thread t covers the 16 columns
-// 16 (t + 256 j) for j = 0, 1 (H <= 8192), with four independent fp64
-// accumulators (one per float4 of the row), added in a fixed order, then the
-// lanes and the waves as above; one rounding to fp32.
+// Single token: one workgroup per expert (router_row_sum), one rounding to fp32.
 __global__ void __launch_bounds__(256) router_gemv1_kernel(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ wr, float* __restrict__ logits,
                                                            int H, int E) {
   __shared__ double part[4];
   const int e = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* w = wr + (size_t)e * H;
-  float4 wv[2][4];
-  uint4 xv[2][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = 16 * (tid + 256 * j);
-    const bool ok = c < H;
-    const int cc = ok ? c : 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wv[j][q] = reinterpret_cast<const float4*>(w + cc)[q];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) xv[j][q] = reinterpret_cast<const uint4*>(x + cc)[q];
-    if (!ok) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) xv[j][q] = make_uint4(0u, 0u, 0u, 0u);
-    }
+  const double s = router_row_sum(x, wr + (size_t)e * H, H, part);
+  if (threadIdx.x == 0) logits[e] = (float)s;
+}
+
+// One-pass routing of one token (moe_route_onepass): workgroup e computes
+// logit e (router_row_sum, the bits of router_gemv1_kernel) and publishes it;
+// the last workgroup's first wave waits for all E words of this call, writes
+// the logits, selects (the bits of route_select_kernel) and advances the
+// region's call number (every workgroup has read it by then: each published a
+// word of this epoch).
+template <int EPL>
+__global__ void __launch_bounds__(256) route_onepass_kernel(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ wr, float* __restrict__ logits,
+                                                            int H, int E, int K, unsigned flags, int32_t* ids, float* w,
+                                                            uint64_t* words, int32_t* status) {
+  __shared__ double part[4];
+  const uint32_t ep = onepass_epoch(words);
+  onepass_publish_logit(x, wr, H, blockIdx.x, words, ep, part);
+  if ((int)blockIdx.x != E - 1 || threadIdx.x >= 64) return;
+  int32_t id;
+  float wt;
+  if (!onepass_select<EPL>(words, E, K, flags, ep, logits, status, id, wt)) return;
+  const int lane = threadIdx.x;
+  if (lane < K) {
+    ids[lane] = id;
+    w[lane] = wt;
   }
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t x01 = q & 1 ? (q & 2 ? xv[j][1].z : xv[j][0].z) : (q & 2 ? xv[j][1].x : xv[j][0].x);
-      const uint32_t x23 = q & 1 ? (q & 2 ? xv[j][1].w : xv[j][0].w) : (q & 2 ? xv[j][1].y : xv[j][0].y);
-      acc[q] = fma((double)bf16_lo(x01), (double)wv[j][q].x, acc[q]);
-      acc[q] = fma((double)bf16_hi(x01), (double)wv[j][q].y, acc[q]);
-      acc[q] = fma((double)bf16_lo(x23), (double)wv[j][q].z, acc[q]);
-      acc[q] = fma((double)bf16_hi(x23), (double)wv[j][q].w, acc[q]);
-    }
-  }
-  double a = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  a = wave_sum_f64(a);
-  if (lane == 0) part[wave] = a;
-  __syncthreads();
-  if (tid == 0) logits[e] = (float)(((part[0] + part[1]) + part[2]) + part[3]);
+  if (lane == 0) __hip_atomic_store(words, (uint64_t)ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One wave per token. The weights are multiplied by scale (1 for moe_route,
@@ -271,6 +261,20 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigne
 
 hipError_t launch_status(int32_t* dst, const int32_t* src, hipStream_t s) {
   hipLaunchKernelGGL(status_kernel, dim3(1), dim3(64), 0, s, dst, src);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_onepass(const uint16_t* x, const float* wr, float* logits, int H, int E, int K, unsigned flags,
+                                int32_t* ids, float* w, uint64_t* words, int32_t* status, hipStream_t s) {
+  const int epl = (E + 63) / 64;
+#define OP(N) hipLaunchKernelGGL(route_onepass_kernel<N>, dim3(E), dim3(256), 0, s, x, wr, logits, H, E, K, flags, ids, \
+                                 w, words, status)
+  if (epl <= 1) OP(1);
+  else if (epl <= 2) OP(2);
+  else if (epl <= 4) OP(4);
+  else if (epl <= 8) OP(8);
+  else OP(16);
+#undef OP
   return hipGetLastError();
 }
 

@@ -57,6 +57,9 @@ extern "C" int moe_layer_noalloc(const uint16_t* x, const float* w_router, float
   // partial passes keep their results in the workspace for moe_ffn_combine, which a
   // caller of this entry point cannot name
   if (ffn_flags & (MOE_FFN_PARTIAL | MOE_FFN_PARTIAL_SHARED | MOE_FFN_PARTIAL_FIRST)) return MOE_EINVAL;
+  // one-pass routing keeps hand-off words in a workspace that must start at zero,
+  // which a shared array reused by calls of every shape cannot promise
+  if (route_flags & MOE_ROUTE_ONEPASS) return MOE_EINVAL;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   const size_t need = moe_ffn_workspace_bytes(T, H, I, E, K, shared_blob != nullptr, ffn_flags);

@@ -164,21 +164,15 @@ __device__ inline uint64_t wave_topk(uint64_t (&key)[EPL], int K, int lane) {
   return mine;
 }
 
-// Softmax + top-k of one token's logits l[0..E): lane k < K gets the expert of
-// rank k and its weight (the softmax probability over all E, with
-// MOE_ROUTE_RENORM divided by the sum over the K selected).
+// Softmax + top-k of one token's logits: lane k < K gets the expert of rank k
+// and its weight (the softmax probability over all E, with MOE_ROUTE_RENORM
+// divided by the sum over the K selected).
+// Softmax + top-k of one token's logits held in registers: lane l holds lg[i] =
+// logit of expert l + 64 i (entries past E ignored).
 template <int EPL>
-__device__ inline void wave_select(const float* __restrict__ l, int E, int K, unsigned flags, int lane, int32_t& id,
-                                   float& wt) {
+__device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsigned flags, int lane, int32_t& id,
+                                          float& wt) {
   uint64_t key[EPL];
-  float lg[EPL];
-  // every load unconditional (a clamped index past E), so that all of them are in
-  // flight at once: a load under a branch is waited for before the branch joins
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    lg[i] = l[e < E ? e : E - 1];
-  }
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
@@ -199,6 +193,66 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
   if (flags & MOE_ROUTE_RENORM) w = w / wave_sum_f32(lane < K ? w : 0.0f);
   id = key_id(mine);
   wt = w;
+}
+
+template <int EPL>
+__device__ inline void wave_select(const float* __restrict__ l, int E, int K, unsigned flags, int lane, int32_t& id,
+                                   float& wt) {
+  float lg[EPL];
+  // every load unconditional (a clamped index past E), so that all of them are in
+  // flight at once: a load under a branch is waited for before the branch joins
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    lg[i] = l[e < E ? e : E - 1];
+  }
+  wave_select_values<EPL>(lg, E, K, flags, lane, id, wt);
+}
+
+// ------------------------------------------------------------------ router GEMV of one token
+// l = sum_h x[h] * w[h] over one router row, by a workgroup of 256 threads (4
+// waves): thread t covers the 16 columns 16 (t + 256 j) for j = 0, 1 (H <= 8192)
+// with four independent fp64 accumulators (one per float4 of the row; bf16 x
+// fp32 products are exact in fp64), added in a fixed order, then the lanes
+// (wave_sum_f64) and the four waves in order. Every workgroup-wide path through
+// here gives the same bits. part: 4 doubles of LDS. Thread 0 returns the sum.
+__device__ inline double router_row_sum(const uint16_t* __restrict__ x, const float* __restrict__ w, int H,
+                                        double* part) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float4 wv[2][4];
+  uint4 xv[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = 16 * (tid + 256 * j);
+    const bool ok = c < H;
+    const int cc = ok ? c : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wv[j][q] = reinterpret_cast<const float4*>(w + cc)[q];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) xv[j][q] = reinterpret_cast<const uint4*>(x + cc)[q];
+    if (!ok) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) xv[j][q] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x01 = q & 1 ? (q & 2 ? xv[j][1].z : xv[j][0].z) : (q & 2 ? xv[j][1].x : xv[j][0].x);
+      const uint32_t x23 = q & 1 ? (q & 2 ? xv[j][1].w : xv[j][0].w) : (q & 2 ? xv[j][1].y : xv[j][0].y);
+      acc[q] = fma((double)__uint_as_float(x01 << 16), (double)wv[j][q].x, acc[q]);
+      acc[q] = fma((double)__uint_as_float(x01 & 0xFFFF0000u), (double)wv[j][q].y, acc[q]);
+      acc[q] = fma((double)__uint_as_float(x23 << 16), (double)wv[j][q].z, acc[q]);
+      acc[q] = fma((double)__uint_as_float(x23 & 0xFFFF0000u), (double)wv[j][q].w, acc[q]);
+    }
+  }
+  double a = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  a = wave_sum_f64(a);
+  if (lane == 0) part[wave] = a;
+  __syncthreads();
+  return ((part[0] + part[1]) + part[2]) + part[3];
 }
 
 // ------------------------------------------------------------------ int4 codes x fp16 activations

@@ -179,22 +179,24 @@ class StackRunner:
     one stream, each layer with its own logits, ids, w and y (the workspace is shared:
     the layers run one after another)."""
 
-    def __init__(self, w: gen.Workload, layers: list[DeviceLayer], device):
+    def __init__(self, w: gen.Workload, layers: list[DeviceLayer], device, route_flags: int = 0):
         n = len(layers)
-        self.w, self.layers = w, layers
+        self.w, self.layers, self.route_flags = w, layers, route_flags
         self.ids = torch.empty(n, w.T, w.K, dtype=torch.int32, device=device)
         self.wts = torch.empty(n, w.T, w.K, dtype=torch.float32, device=device)
         self.y = torch.empty(n, w.T, w.H, dtype=torch.bfloat16, device=device)
         self.ws_bytes = lib.moe_ffn_workspace_bytes(w.T, w.H, w.I, w.E, w.K, w.shared, 0)
-        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        # zeroed: with MOE_ROUTE_ONEPASS the workspace holds hand-off words that start at zero
+        self.ws = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.graph = None
 
     def step(self, stream=None) -> None:
         w = self.w
         for i, L in enumerate(self.layers):
-            lib.moe_layer(L.x, L.wr, L.logits, w.T, w.H, w.I, w.E, w.K, w.g, 0, self.ids[i], self.wts[i], L.table,
-                          L.slots, L.stride, L.shared, self.y[i], self.ws, self.ws_bytes, self.status, 0, stream)
+            lib.moe_layer(L.x, L.wr, L.logits, w.T, w.H, w.I, w.E, w.K, w.g, self.route_flags, self.ids[i],
+                          self.wts[i], L.table, L.slots, L.stride, L.shared, self.y[i], self.ws, self.ws_bytes,
+                          self.status, 0, stream)
 
     def poison(self) -> None:
         """Overwrite every output (y with bf16 NaN bits, ids with -1, w with NaN) and the
