@@ -90,12 +90,20 @@ __device__ inline int xcd_item(int bid, int n_items) {
   return n_items % kXcds == 0 ? (bid % kXcds) * (n_items / kXcds) + bid / kXcds : bid;
 }
 
-// One-pass path: the blob of unit u from the selector's slot word of this call.
+// One-pass path: the blob of unit u from the selector's slot word of this call,
+// polled by the first wave only (one poller per workgroup) and handed to the
+// others through LDS.
 __device__ inline const uint8_t* onepass_unit_blob(const FfnArgs& a, int u, bool has_shared, const uint64_t* words,
-                                                   uint32_t ep) {
+                                                   uint32_t ep, int wave) {
   const int k = has_shared ? u - 1 : u;
   if (k < 0) return a.shared_blob;
-  const int32_t slot = onepass_wait_slot(words, a.E, k, ep);
+  __shared__ int32_t slot_sh;
+  if (wave == 0) {
+    const int32_t sl = onepass_wait_slot(words, a.E, k, ep, blockIdx.x % kOnepassCopies);
+    if ((threadIdx.x & 63) == 0) slot_sh = sl;
+  }
+  __syncthreads();
+  const int32_t slot = slot_sh;
   if (slot < 0) {
     *a.status = slot == (int32_t)0x80000000 ? MOE_EHIP : MOE_ENOTRES;  // hand-off timed out / not resident
     return nullptr;
@@ -140,7 +148,7 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
     xv[v] = reinterpret_cast<const uint4*>(a.x)[q];
   }
   const uint8_t* blob =
-      ONEPASS ? onepass_unit_blob(a, u, has_shared, words, ep) : dec_unit_blob(a, u, has_shared, a.ids, pre);
+      ONEPASS ? onepass_unit_blob(a, u, has_shared, words, ep, wave) : dec_unit_blob(a, u, has_shared, a.ids, pre);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
   const int n = hb * 8 + r;
@@ -265,22 +273,46 @@ __global__ void __launch_bounds__(kThreads) dec_route_gateup_kernel(FfnArgs a, O
     return;
   }
   __shared__ double part[4];
-  onepass_publish_logit(a.x, r.w_router, a.H, blockIdx.x, r.words, ep, part);
-  if ((int)blockIdx.x != E - 1 || threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  int32_t id;
-  float wt;
-  const bool ok = onepass_select<EPL>(r.words, E, a.K, r.flags, ep, r.logits, a.status, id, wt);
-  if (lane < a.K) {
-    int32_t slot = (int32_t)0x80000000;  // the hand-off failed: consumers report it
-    if (ok) {
-      r.ids[lane] = id;
-      r.w[lane] = wt;
-      slot = a.slot_table[id];
-      const_cast<int32_t*>(a.pre_slots)[lane] = slot;
+  __shared__ int32_t tbl[64 * EPL];
+  const bool selector = (int)blockIdx.x == E - 1 && threadIdx.x < 64;
+  // the selector's slot-table loads go out first and land while it waits
+  const int lane = threadIdx.x & 63;
+  int32_t tv[EPL];
+  if (selector) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      tv[i] = a.slot_table[e < E ? e : E - 1];
     }
-    ll_store(r.words + 1 + E + lane, ep, (uint32_t)slot);
   }
+  onepass_publish_logit(a.x, r.w_router, a.H, blockIdx.x, r.words, ep, part);
+  if (!selector) return;
+  // wait, select and publish the slots first; the output stores come after
+  float lg[EPL];
+  const bool ok = onepass_wait_logits<EPL>(r.words, E, ep, a.status, lg);
+  float sel[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) sel[i] = lg[i];
+  int32_t id = 0;
+  float wt = 0.0f;
+  if (ok) wave_select_values<EPL>(sel, E, a.K, r.flags, lane, id, wt);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) tbl[lane + 64 * i] = tv[i];  // entries past E are never read
+  __builtin_amdgcn_wave_barrier();  // one wave: its LDS stores precede its loads
+  int32_t slot = (int32_t)0x80000000;  // the hand-off failed: consumers report it
+  if (ok && lane < a.K) slot = tbl[id];
+  // kOnepassCopies copies of each rank's slot (lane c writes copy c)
+  for (int k = 0; k < a.K; ++k) {
+    const int32_t sk = __builtin_amdgcn_readlane(slot, k);
+    if (lane < kOnepassCopies) ll_store(r.words + onepass_slot_word(E, k, lane), ep, (uint32_t)sk);
+  }
+  if (!ok) return;
+  if (lane < a.K) {
+    r.ids[lane] = id;
+    r.w[lane] = wt;
+    const_cast<int32_t*>(a.pre_slots)[lane] = slot;
+  }
+  onepass_store_logits<EPL>(lg, E, r.logits);
 }
 
 // ------------------------------------------------------------------ down + combine

@@ -100,9 +100,16 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigne
                                float scale = 1.0f, const int32_t* slot_table = nullptr, int32_t* slots_out = nullptr);
 
 // One-pass routing (onepass.h): the hand-off region of one token's routing,
-// 64-bit words [0] call number, [1 + e] logit of expert e, [1 + E + k] slot of rank k.
+// 64-bit words [0] call number, [1 + e] logit of expert e, and kOnepassCopies
+// copies of the slot of rank k at onepass_slot_word(E, k, c), each in a 128-byte
+// line of its own: the gate/up workgroups of one expert poll copy (workgroup % 8),
+// so about 1/8 of them share a line.
+constexpr int kOnepassCopies = 8;
+__host__ __device__ inline int onepass_slot_word(int E, int k, int c) {
+  return ((1 + E + 15) & ~15) + 16 * (k * kOnepassCopies + c);
+}
 __host__ __device__ inline size_t onepass_region_bytes(int E, int K) {
-  return (((size_t)1 + E + K) * 8 + 255) & ~(size_t)255;
+  return ((size_t)onepass_slot_word(E, K, 0) * 8 + 255) & ~(size_t)255;
 }
 hipError_t launch_route_onepass(const uint16_t* x, const float* wr, float* logits, int H, int E, int K, unsigned flags,
                                 int32_t* ids, float* w, uint64_t* words, int32_t* status, hipStream_t s);

@@ -15,7 +15,8 @@
 // (the caller zeroes it once), so no stale word can carry the current epoch.
 //
 // Region (64-bit words): [0] epoch of the last call; [1 + e] logit of expert e;
-// [1 + E + k] slot of the expert of rank k (moe_layer's one-pass path).
+// [onepass_slot_word(E, k, c)] copy c of the slot of the expert of rank k
+// (moe_layer's one-pass path).
 #pragma once
 
 #include "moe_internal.h"
@@ -41,56 +42,56 @@ __device__ inline void onepass_publish_logit(const uint16_t* x, const float* wr,
   if (threadIdx.x == 0) ll_store(words + 1 + e, ep, __float_as_uint((float)s));
 }
 
-// The selector (one wave, lanes 0..63): waits for all E logit words of this
-// epoch, writes the fp32 logits, and selects as moe_route does. Returns false
-// when the words did not arrive within the spin limit (status set; id = -1).
+// The selector (one wave, lanes 0..63): waits until all E logit words carry
+// this epoch; lane l gets lg[i] = logit of expert l + 64 i (0 past E). Every poll
+// issues all of its loads before it waits (one round trip per poll). Returns
+// false when the words did not arrive within the spin limit (status set).
 template <int EPL>
-__device__ inline bool onepass_select(const uint64_t* words, int E, int K, unsigned flags, uint32_t ep,
-                                      float* logits, int32_t* status, int32_t& id, float& wt) {
+__device__ inline bool onepass_wait_logits(const uint64_t* words, int E, uint32_t ep, int32_t* status,
+                                           float (&lg)[EPL]) {
   const int lane = threadIdx.x & 63;
-  float lg[EPL];
-  uint32_t got = 0;  // bit i: word of expert lane + 64 i is fresh
-#pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i >= E) got |= 1u << i;
   for (int spins = 0;; ++spins) {
+    uint64_t v[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      if (!(got & (1u << i))) {
-        const uint64_t v = ll_load(words + 1 + lane + 64 * i);
-        if ((uint32_t)(v >> 32) == ep) {
-          lg[i] = __uint_as_float((uint32_t)v);
-          got |= 1u << i;
-        }
-      }
+      const int e = lane + 64 * i;
+      v[i] = ll_load(words + 1 + (e < E ? e : E - 1));
     }
-    if (__ballot(got != (1u << EPL) - 1u) == 0) break;
+    bool fresh = true;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) fresh = fresh && (uint32_t)(v[i] >> 32) == ep;
+    if (__ballot(!fresh) == 0) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) lg[i] = lane + 64 * i < E ? __uint_as_float((uint32_t)v[i]) : 0.0f;
+      return true;
+    }
     if (spins >= kOnepassSpinLimit) {
       if (lane == 0) *status = MOE_EHIP;
-      id = -1;
-      wt = 0.0f;
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
   }
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E) logits[e] = lg[i];
-    else lg[i] = 0.0f;
-  }
-  wave_select_values<EPL>(lg, E, K, flags, lane, id, wt);
-  return true;
 }
 
-// Wait for word k (rank k's slot in moe_layer's one-pass path) of this epoch;
-// every lane of the calling wave gets the slot, or INT32_MIN after the spin limit.
-__device__ inline int32_t onepass_wait_slot(const uint64_t* words, int E, int k, uint32_t ep) {
+// Lane l writes the logits of experts l + 64 i (stores are issued after the
+// selection and the hand-off, so that no wait for them lands on the critical path).
+template <int EPL>
+__device__ inline void onepass_store_logits(const float (&lg)[EPL], int E, float* logits) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + 64 * i < E) logits[lane + 64 * i] = lg[i];
+}
+
+// Wait for copy `copy` of rank k's slot word of this epoch (moe_layer's one-pass
+// path); every lane of the calling wave gets the slot, or INT32_MIN after the
+// spin limit.
+__device__ inline int32_t onepass_wait_slot(const uint64_t* words, int E, int k, uint32_t ep, int copy) {
   for (int spins = 0; spins < kOnepassSpinLimit; ++spins) {
-    const uint64_t v = ll_load(words + 1 + E + k);
+    const uint64_t v = ll_load(words + onepass_slot_word(E, k, copy));
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     if (hi == ep) return (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(2);
   }
   return INT32_MIN;
 }

@@ -94,14 +94,20 @@ __global__ void __launch_bounds__(256) route_onepass_kernel(const uint16_t* __re
   const uint32_t ep = onepass_epoch(words);
   onepass_publish_logit(x, wr, H, blockIdx.x, words, ep, part);
   if ((int)blockIdx.x != E - 1 || threadIdx.x >= 64) return;
+  float lg[EPL];
+  if (!onepass_wait_logits<EPL>(words, E, ep, status, lg)) return;
+  float sel[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) sel[i] = lg[i];
   int32_t id;
   float wt;
-  if (!onepass_select<EPL>(words, E, K, flags, ep, logits, status, id, wt)) return;
+  wave_select_values<EPL>(sel, E, K, flags, threadIdx.x, id, wt);
   const int lane = threadIdx.x;
   if (lane < K) {
     ids[lane] = id;
     w[lane] = wt;
   }
+  onepass_store_logits<EPL>(lg, E, logits);
   if (lane == 0) __hip_atomic_store(words, (uint64_t)ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
