@@ -1,32 +1,24 @@
-// Small-batch expert FFN (2 <= T <= 32 tokens): the decode kernels' design
-// for several tokens per expert.
+// Small-batch expert FFN (2 <= T <= 32 tokens).
 //
 // A unit is one distinct expert of the batch (or the always-on shared expert)
 // with every (token, rank) pair routed to it, so each expert's bytes stream
 // from HBM once however many tokens use it ("Strata" README, Models: W4A16
 // experts). Four kernels:
-//   bat_plan     one workgroup: units in order of their first pair (the shared
-//                expert first), each unit's pairs in pair order, and per unit
-//                one record (slot, first pair, pair count) into the workspace;
-//                also x as fp16 pairs with its per-group corrections, once.
-//                Pair p = t*K + k for routed pairs, T*K + t for the shared
-//                expert's.
-//   bat_gateup   one workgroup per (unit, 8 rows of I), as dec_gateup: one
-//                record load, then the weights of the item into registers,
-//                then the unit's tokens 4 at a time; each chunk copies its
-//                tokens' fp16 x slices and corrections into the wave's LDS,
-//                and the fp16 pairs of the codes are formed once per step for
-//                all tokens of the chunk. h = silu(g) * u in fp16 per pair.
-//   bat_down     one workgroup per (unit, 16 rows of H); each wave owns 4 rows
-//                (one 4-row block of the blob) and all groups of the unit, so
-//                no wave waits for another; per chunk of 4 pairs the wave
-//                stages their h rows and writes o[pair] (fp32) for its rows.
-//   bat_combine  y[t] = o_shared[t] + sum_k w[t][k] * o[t*K + k] in rank order,
-//                rounded once to bf16.
-// Arithmetic as in the single-token kernels: codes become exact fp16 pairs
-// (q + 1032, q + 72) for v_dot2_f32_f16 against fp16 activations, one
-// correction per group, the fp16 scale applied per group in fp32. No atomics
-// on floating-point values; every sum has a fixed order.
+//   bat_plan      one workgroup: units in order of their first pair (the
+//                 shared expert first), each unit's pairs in pair order, and
+//                 per unit one record (slot, first pair, pair count) into the
+//                 workspace; other workgroups convert x to fp16 once. Pair
+//                 p = t*K + k for routed pairs, T*K + t for the shared
+//                 expert's.
+//   bmx_gateup    MFMA over (unit pairs x 16 weight rows) tiles; h =
+//                 silu(g) * u in fp16, one row per pair in unit order.
+//   bmx_down      the same for the down matrix; o (fp32) at each pair's row.
+//   bat_combine   y[t] = o_shared[t] + sum_k w[t][k] * o[t*K + k] in rank
+//                 order, rounded once to bf16.
+// No atomics on floating-point values; every sum has a fixed order.
+#include <type_traits>
+
+#include "lds_dma.h"
 #include "moe_internal.h"
 #include "wave_ops.h"
 
@@ -34,9 +26,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kTB = 4;                 // pairs per gate/up chunk
-constexpr int kTBD = 8;                // pairs per down chunk
 constexpr int kUnitPairs = 64;         // pairs one unit can hold (a routed unit has at most T)
 constexpr int kPlanThreads = 1024;
 constexpr int kBatMaxPairs = 512;      // routed pairs T*K the plan covers
@@ -49,14 +38,13 @@ __host__ __device__ inline int bat_umax(int T, int K, int E, int has_shared) {
 __host__ __device__ inline int bat_pmax(int T, int K, int has_shared) { return T * K + (has_shared ? T : 0); }
 
 // Workspace: plan ints [n_units | rec[U][4] | ptab[U][kUnitPairs]], x16 fp16
-// [T][H], xc fp32 [T][G] (per-group corrections of x16), h fp16 [P][I] with
-// rows in unit order (row rec[u].y + i is pair ptab[u][i]), o fp32 [P][H] with
+// [T][H], h fp16 [P][I] with rows in unit order (row rec[u].y + i is pair ptab[u][i]), o fp32 [P][H] with
 // rows in pair order. rec[u] = {slot (-1: the shared expert, -2: not usable),
 // first h row of the unit, pair count (0 past the last unit), expert}; the
 // pair table has a fixed stride, so a workgroup loads its unit's record and
 // pairs in one round trip.
 struct BatWs {
-  size_t x16_off, xc_off, h_off, o_off, bytes;
+  size_t x16_off, h_off, o_off, bytes;
   int U, P;
 };
 __host__ __device__ inline BatWs bat_ws(int T, int H, int I, int E, int K, int has_shared) {
@@ -65,8 +53,7 @@ __host__ __device__ inline BatWs bat_ws(int T, int H, int I, int E, int K, int h
   w.P = bat_pmax(T, K, has_shared);
   const size_t plan_ints = 4 + (size_t)w.U * (4 + kUnitPairs);
   w.x16_off = align256(plan_ints * 4);
-  w.xc_off = align256(w.x16_off + (size_t)T * H * 2);
-  w.h_off = align256(w.xc_off + (size_t)T * (H / kGroup) * 4);
+  w.h_off = align256(w.x16_off + (size_t)T * H * 2);
   w.o_off = align256(w.h_off + (size_t)w.P * I * 2);
   w.bytes = align256(w.o_off + (size_t)w.P * H * 4);
   return w;
@@ -117,26 +104,16 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return before + s - v;
 }
 
-// x as fp16 pairs (x16) and the per-group corrections xc = 1032 * A + 72 * B,
-// where A sums columns 8d + {0,1,4,5} and B columns 8d + {2,3,6,7} of the
-// group: thread i converts dword i of x; the 16 dwords of a group are one row
-// of 16 lanes, whose sums are taken with DPP rotations (lane 0 of the row writes).
+// x as fp16 (x16): thread i converts dword i of x; a value that does not fit
+// fp16 sets MOE_EUNSUP (bf16 converts exactly for |x| in [2^-17, 65504]).
 __device__ inline void plan_convert_x(const FfnArgs& a, const BatWs& W, int i) {
-  const int n_dw = a.T * a.H / 2;
-  const bool live = i < n_dw;
-  const uint32_t v = live ? reinterpret_cast<const uint32_t*>(a.x)[i] : 0u;
+  if (i >= a.T * a.H / 2) return;
+  const uint32_t v = reinterpret_cast<const uint32_t*>(a.x)[i];
   bool bad = false;
   const uint32_t lo = to_f16_bits(__uint_as_float(v << 16), &bad);
   const uint32_t hi = to_f16_bits(__uint_as_float(v & 0xFFFF0000u), &bad);
-  const uint32_t pr = lo | (hi << 16);
-  if (live) reinterpret_cast<uint32_t*>(a.ws + W.x16_off)[i] = pr;
-  if (bad && live) *a.status = MOE_EUNSUP;
-  const float s2 = f16_lo(pr) + f16_hi(pr);
-  float sa = (i & 1) ? 0.0f : s2;  // dword 2k of a group: columns of A pairs
-  float sb = (i & 1) ? s2 : 0.0f;
-  sa = dpp_add<8>(dpp_add<4>(dpp_add<2>(dpp_add<1>(sa))));
-  sb = dpp_add<8>(dpp_add<4>(dpp_add<2>(dpp_add<1>(sb))));
-  if (live && (i & 15) == 0) reinterpret_cast<float*>(a.ws + W.xc_off)[i >> 4] = fmaf(1032.0f, sa, 72.0f * sb);
+  reinterpret_cast<uint32_t*>(a.ws + W.x16_off)[i] = lo | (hi << 16);
+  if (bad) *a.status = MOE_EUNSUP;
 }
 
 // ------------------------------------------------------------------ plan
@@ -231,27 +208,103 @@ __device__ inline UnitHead unit_head(const PlanView& pl, int u, int lane) {
   return h;
 }
 
-// ------------------------------------------------------------------ gate/up
-// GPL = groups per lane = ceil(GW / 8) with GW = ceil(G / 4) groups per wave.
-template <int GPL>
-__global__ void __launch_bounds__(kThreads) bat_gateup_kernel(FfnArgs a) {
-  // LDS per wave: for each of the chunk's tokens, the x slice as fp16 pairs
-  // [GW][16] dwords and the group corrections [GW]
+// ------------------------------------------------------------------ MFMA helpers
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline f16x8_t dequant_qs(uint32_t cw, _Float16 sc) {
+  const f16x2_t s2 = {sc, sc};
+  const f16x2_t off_a = {(_Float16)-1032.0f, (_Float16)-1032.0f}, off_b = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t w8 = cw >> 8;
+  const uint32_t m0 = (cw & 0x000F000Fu) | 0x64006400u, m1 = (cw & 0x00F000F0u) | 0x54005400u;
+  const uint32_t m2 = (w8 & 0x000F000Fu) | 0x64006400u, m3 = (w8 & 0x00F000F0u) | 0x54005400u;
+  uint32_t b[4];
+  b[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, m0) + off_a) * s2);
+  b[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, m1) + off_b) * s2);
+  b[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, m2) + off_a) * s2);
+  b[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, m3) + off_b) * s2);
+  return __builtin_bit_cast(f16x8_t, make_uint4(b[0], b[1], b[2], b[3]));
+}
+__device__ inline f16x8_t as_f16x8(const uint4& v) { return __builtin_bit_cast(f16x8_t, v); }
+// Buffer loads (a read past the descriptor's range returns zeros)
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ inline uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ inline uint32_t dword_of(const uint4& v, int i) { return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w)); }
+
+// Scale of one chunk: 0 for a chunk past the groups or an unusable unit; a
+// magnitude >= 8192 sets *bad.
+__device__ inline _Float16 chunk_scale(uint16_t bits, bool ok, bool* bad) {
+  const _Float16 s = __builtin_bit_cast(_Float16, bits);
+  if (ok && !((float)__builtin_fabsf16(s) < 8192.0f)) *bad = true;
+  return ok ? s : (_Float16)0.0f;
+}
+
+// ------------------------------------------------------------------ gate/up and down
+// The unit's pairs are the M rows of v_mfma_f32_16x16x32_f16 and 16 weight
+// rows its N columns, so one dequantised weight fragment serves every pair of
+// the unit and the work per item hardly depends on the pair count. Lane l
+// (n = l % 16, q = l / 16) loads the 16-byte code chunk of (row n, group
+// 4c + q); MFMA i of chunk c takes dword i of every lane, i.e. columns
+// 32 (4c + q) + 8i .. +7 of each quarter's group, and the A fragment of lane
+// (m, q) holds the same columns of pair row m. B = fp16(q * s): the code's
+// exact fp16 value (1024 + u or 64 + u under an fp16 pattern, minus 1032 or
+// 72) times the group's fp16 scale, rounded once (relative error <= 2^-11),
+// so a chunk's four groups share one accumulator. A scale of magnitude
+// >= 8192 could overflow that product and sets MOE_EUNSUP. The D fragment of
+// lane l holds pair rows 4 (l / 16) + v of weight row l % 16.
+//
+// Each wave owns whole 16-row tiles over every group, so its D fragments are
+// final sums and no partial crosses waves. The A rows (x of the pairs'
+// tokens, or the unit's h rows), KM per M-tile, go to LDS by direct
+// buffer-to-LDS loads issued before the weight loads and waited for alone;
+// A rows past the unit's pairs, the 16-byte pad after each row (which keeps
+// the 8 lanes of a ds_read_b128 phase on distinct banks) and a tail are
+// zeros, so every fragment is read as is. A unit with more pairs than KM
+// runs further M-tiles (the weights are read again). The weight loads are
+// buffer loads with a per-lane offset and a per-chunk constant; a group past
+// the last reads other blob bytes or zeros past its end and gets scale 0.
+// Workgroup sizes are chosen so that the items of a 16-token layer are
+// resident at once with a small spread of rows per CU:
+//   gate/up: NW waves of one 16-row tile each (96 rows where I allows); the
+//     codes and scales of CW chunks are in flight per wave, the load of
+//     chunk c + CW issued once chunk c is done.
+//   down: NW waves of one tile each, all codes loaded up front.
+__host__ __device__ inline int bmx_row_bytes(int cols) { return cols * 2 + 16; }
+constexpr int kBmxTail = 256;  // zero bytes after the rows: reads of a group past the last stay inside
+__host__ __device__ inline size_t bmx_lds(int cols, int KM) { return (size_t)KM * bmx_row_bytes(cols) + kBmxTail; }
+
+// Zero the pads of rows < live, rows live .. KM - 1 whole, and the tail (the
+// workgroup's nt threads; LDS stores, waited for before the next barrier).
+__device__ inline void bmx_zero_rows(unsigned char* base, int cols, int KM, int live, int tid, int nt) {
+  const int RB = bmx_row_bytes(cols);
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (int r = tid; r < live; r += nt) *reinterpret_cast<uint4*>(base + r * RB + cols * 2) = z;
+  const int n16 = (KM - live) * (RB / 16) + kBmxTail / 16;
+  uint4* d = reinterpret_cast<uint4*>(base + live * RB);
+  for (int i = tid; i < n16; i += nt) d[i] = z;
+}
+
+// s_waitcnt: at most vm vector-memory operations outstanding and every LDS access done
+__host__ __device__ constexpr int vm_lds_imm(int vm) { return vmcnt_imm(vm) & ~(15 << 8); }
+
+template <int NW, int CQ, int CW, int KM>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) bmx_gateup_kernel(FfnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float part[kTB][2][kWaves][8];
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const int G = H / kGroup;
-  const int GW = (G + kWaves - 1) / kWaves;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 7, p = lane >> 3;
+  const int n = lane & 15, q = lane >> 4;
   const bool has_shared = a.shared_blob != nullptr;
   const BatWs W = bat_ws(T, H, I, a.E, K, has_shared);
   const PlanView pl = plan_view(a.ws, W.U, W.P);
-  // one item per workgroup; a unit's items are consecutive workgroups, so its rows
-  // stream from HBM together
-  const int n_hb = I / 8;
-  const int u = blockIdx.x / n_hb, hb = blockIdx.x % n_hb;
+  const int n_nt = I / (16 * NW);
+  const int u = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const UnitHead uh = unit_head(pl, u, lane);
   const int p0 = uh.p0, np = uh.np;
   if (np == 0) return;
@@ -259,179 +312,89 @@ __global__ void __launch_bounds__(kThreads) bat_gateup_kernel(FfnArgs a) {
     if (tid == 0) *a.status = MOE_EUNSUP;
     return;
   }
-  uint32_t* xs = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * kTB * (GW * 17);
-  const int j0 = wave * GW;
-  const int gw_here = G - j0 < GW ? (G - j0 > 0 ? G - j0 : 0) : GW;
   const uint8_t* blob = rec_blob(a, uh.slot);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
-  const uint4* x16 = reinterpret_cast<const uint4*>(a.ws + W.x16_off);
-  const float* xc = reinterpret_cast<const float*>(a.ws + W.xc_off);
-  // a chunk's x slices: uint4 v of a token's slice is columns 8 (lane + 64 v) .. +7
-  // of the wave's groups; every token's loads are issued before any is stored
-  constexpr int XQ = (GPL + 1) / 2;  // uint4 per lane and token (GW <= 8 * GPL groups)
-  uint4 xv[kTB][XQ];
-  float cv[kTB];
-  auto load_x = [&](int c0) {
-    const int tc = np - c0 < kTB ? np - c0 : kTB;
-#pragma unroll
-    for (int ti = 0; ti < kTB; ++ti) {
-      const int t = pair_token(__builtin_amdgcn_readlane(uh.my_pair, c0 + (ti < tc ? ti : tc - 1)), T, K);
-#pragma unroll
-      for (int v = 0; v < XQ; ++v) {
-        int q = j0 * 4 + lane + 64 * v;
-        q = q < G * 4 ? q : G * 4 - 1;
-        xv[ti][v] = x16[(size_t)t * (H / 8) + q];
-      }
-      int jj = j0 + (lane < GW ? lane : 0);
-      jj = jj < G ? jj : G - 1;
-      cv[ti] = xc[(size_t)t * G + jj];
-    }
-  };
-  // ... into the wave's LDS (zeros past the wave's groups); the values are selected
-  // on every lane, outside the stores' branches, so each load is waited for on every path
-  auto stage_x = [&](int tc) {
-#pragma unroll
-    for (int ti = 0; ti < kTB; ++ti) {
-      uint32_t* xt = xs + (size_t)ti * (GW * 17);
-#pragma unroll
-      for (int v = 0; v < XQ; ++v) {
-        const int q = lane + 64 * v;
-        const bool keep = q < gw_here * 4;
-        const uint4 val = make_uint4(keep ? xv[ti][v].x : 0u, keep ? xv[ti][v].y : 0u, keep ? xv[ti][v].z : 0u,
-                                     keep ? xv[ti][v].w : 0u);
-        if (ti < tc && q < GW * 4) reinterpret_cast<uint4*>(xt)[q] = val;
-      }
-      const float cval = lane < gw_here ? cv[ti] : 0.0f;
-      if (ti < tc && lane < GW) reinterpret_cast<float*>(xt + GW * 16)[lane] = cval;
-    }
-    __builtin_amdgcn_wave_barrier();
-  };
   const BlobLayout BL = blob_layout(H, I);
-  const int n = hb * 8 + r;
-  uint4 cg[GPL], cu[GPL];
-  uint32_t sgw[GPL], suw[GPL];
-#pragma unroll
-  for (int i = 0; i < GPL; ++i) {
-    const int jl = 8 * i + p;
-    int j = j0 + (jl < gw_here ? jl : gw_here - 1);
-    j = j < 0 ? 0 : (j < G ? j : G - 1);
-    const size_t co = code_off(n, j, G, kRowBlockGU);
-    cg[i] = *reinterpret_cast<const uint4*>(src + BL.gate_codes + co);
-    cu[i] = *reinterpret_cast<const uint4*>(src + BL.up_codes + co);
-    const size_t sd = scale_off(n, j, G, kRowBlockGU) >> 2;
-    sgw[i] = reinterpret_cast<const uint32_t*>(src + BL.gate_scales)[sd];
-    suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
-  }
-  load_x(0);  // after the weights: these need the pair table, the weights only the record
-  __builtin_amdgcn_sched_barrier(0);
+  const int XB = bmx_row_bytes(H);
+  unsigned char* xs = smem;  // [KM][XB], then the zero tail
+  const __amdgpu_buffer_rsrc_t xr = buf_rsrc(a.ws + W.x16_off, (uint32_t)((size_t)T * H * 2));
+  const __amdgpu_buffer_rsrc_t br = buf_rsrc(src, (uint32_t)BL.bytes);
+  const int row = (nt * NW + wave) * 16 + n;  // this lane's weight row (B column n)
+  const uint4* xap = reinterpret_cast<const uint4*>(xs + n * XB + q * 64);  // A row n (lane % 16)
   _Float16* hws = reinterpret_cast<_Float16*>(a.ws + W.h_off);
-  const int sh = (r & 1) * 16;
-  stage_x(np < kTB ? np : kTB);
-  for (int c0 = 0;;) {
-    const int tc = np - c0 < kTB ? np - c0 : kTB;
-    float ag[kTB], au[kTB];
+  const uint32_t c_off = (uint32_t)code_off(row, q, G, kRowBlockGU), s_off = (uint32_t)scale_off(row, q, G, kRowBlockGU);
+  uint4 cg[CW], cu[CW];
+  uint16_t sgb[CW], sub[CW];
+  uint32_t zo = 0;
+  auto load_chunk = [&](int c) {
+    const uint32_t dc = (uint32_t)c * 4 * kRowBlockGU * 16, ds = (uint32_t)c * 4 * kRowBlockGU * 2;
+    cg[c % CW] = bload16(br, c_off, zo + (uint32_t)BL.gate_codes + dc);
+    cu[c % CW] = bload16(br, c_off, zo + (uint32_t)BL.up_codes + dc);
+    sgb[c % CW] = bload2(br, s_off, zo + (uint32_t)BL.gate_scales + ds);
+    sub[c % CW] = bload2(br, s_off, zo + (uint32_t)BL.up_scales + ds);
+  };
+  bool bad = false;
+  for (int m0 = 0; m0 < np; m0 += KM) {
+    if (m0 > 0) __syncthreads();  // every wave is done with the staged rows
+    // an opaque zero offset per M-tile keeps the weight loads (and their fp16 forms)
+    // inside the tile, not hoisted out of the loop and held for every chunk at once
+    asm volatile("" : "+s"(zo));
+    const int rows = np - m0 < KM ? np - m0 : KM;
+    for (int r = 0; r < rows; ++r) {
+      const int t = pair_token(__builtin_amdgcn_readlane(uh.my_pair, m0 + r), T, K);
+      stage_lds(xr, (uint32_t)((size_t)t * H * 2), H / 8, xs + r * XB, wave, lane, NW);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ti = 0; ti < kTB; ++ti) ag[ti] = au[ti] = 0.0f;
+    for (int c = 0; c < CW; ++c) load_chunk(c);
+    __builtin_amdgcn_sched_barrier(0);
+    bmx_zero_rows(xs, H, KM, rows, tid, NW * 64);
+    __builtin_amdgcn_s_waitcnt(vm_lds_imm(4 * CW));  // the staged rows (issued first) and the zeros are in LDS
+    __builtin_amdgcn_s_barrier();
+    f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int jl = 8 * i + p;
-      const bool ok = blob != nullptr && jl < gw_here;
-      const int jc = jl < gw_here ? jl : 0;
-      // the weights are opaque per chunk: nothing is hoisted to before the loop,
-      // where it would wait for them ahead of the staging
-      asm volatile("" : "+v"(cg[i].x), "+v"(cg[i].y), "+v"(cg[i].z), "+v"(cg[i].w), "+v"(sgw[i]));
-      asm volatile("" : "+v"(cu[i].x), "+v"(cu[i].y), "+v"(cu[i].z), "+v"(cu[i].w), "+v"(suw[i]));
-      const float sg = ok ? f16_lo(sgw[i] >> sh) : 0.0f;
-      const float su = ok ? f16_lo(suw[i] >> sh) : 0.0f;
-      // a code dword at a time: its four fp16 pairs of gate and of up, then every
-      // token of the chunk against the activation dwords of the same 8 columns (each
-      // token's sum still runs over the chunk's 16 dwords in order)
-      const uint32_t wg[4] = {cg[i].x, cg[i].y, cg[i].z, cg[i].w};
-      const uint32_t wu[4] = {cu[i].x, cu[i].y, cu[i].z, cu[i].w};
-      float dg[kTB], du[kTB];
+    for (int c = 0; c < CQ; ++c) {
+      if (4 * c >= G) continue;  // a chunk wholly past the groups
+      uint4 xa[4];
 #pragma unroll
-      for (int ti = 0; ti < kTB; ++ti) dg[ti] = du[ti] = 0.0f;
+      for (int i = 0; i < 4; ++i) xa[i] = xap[16 * c + i];
+      const bool ok = blob != nullptr && 4 * c + q < G;
+      const _Float16 sg = chunk_scale(sgb[c % CW], ok, &bad);
+      const _Float16 su = chunk_scale(sub[c % CW], ok, &bad);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t g8 = wg[d] >> 8, u8 = wu[d] >> 8;
-        const uint32_t pg0 = (wg[d] & 0x000F000Fu) | 0x64006400u, pg1 = (wg[d] & 0x00F000F0u) | 0x54005400u;
-        const uint32_t pg2 = (g8 & 0x000F000Fu) | 0x64006400u, pg3 = (g8 & 0x00F000F0u) | 0x54005400u;
-        const uint32_t pu0 = (wu[d] & 0x000F000Fu) | 0x64006400u, pu1 = (wu[d] & 0x00F000F0u) | 0x54005400u;
-        const uint32_t pu2 = (u8 & 0x000F000Fu) | 0x64006400u, pu3 = (u8 & 0x00F000F0u) | 0x54005400u;
-#pragma unroll
-        for (int ti = 0; ti < kTB; ++ti) {
-          if (ti < tc) {
-            const uint4 xq = reinterpret_cast<const uint4*>(xs + (size_t)ti * (GW * 17) + jc * 16)[d];
-            dg[ti] = dot2h(pg3, xq.w, dot2h(pg2, xq.z, dot2h(pg1, xq.y, dot2h(pg0, xq.x, dg[ti]))));
-            du[ti] = dot2h(pu3, xq.w, dot2h(pu2, xq.z, dot2h(pu1, xq.y, dot2h(pu0, xq.x, du[ti]))));
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xa[i]), dequant_qs(dword_of(cg[c % CW], i), sg), ag, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xa[i]), dequant_qs(dword_of(cu[c % CW], i), su), au, 0, 0, 0);
       }
+      if (c + CW < CQ && 4 * (c + CW) < G) load_chunk(c + CW);
+      __builtin_amdgcn_sched_barrier(0);  // one chunk's operands at a time (register pressure)
+    }
 #pragma unroll
-      for (int ti = 0; ti < kTB; ++ti) {
-        if (ti < tc) {
-          const float C = reinterpret_cast<const float*>(xs + (size_t)ti * (GW * 17) + GW * 16)[jc];
-          ag[ti] = fmaf(sg, dg[ti] - C, ag[ti]);
-          au[ti] = fmaf(su, du[ti] - C, au[ti]);
-        }
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * q + v;
+      if (m < rows) {
+        const float hv = blob ? silu(ag[v]) * au[v] : 0.0f;
+        if (!(fabsf(hv) < 65520.0f)) bad = true;
+        hws[(size_t)(p0 + m0 + m) * I + row] = (_Float16)hv;
       }
     }
-    // phases (lane bits 3..5), read from lanes 0..7
-#pragma unroll
-    for (int ti = 0; ti < kTB; ++ti) {
-      const float g = sum_rows(dpp_add<8>(ag[ti]));
-      const float uu = sum_rows(dpp_add<8>(au[ti]));
-      if (p == 0) {
-        part[ti][0][wave][r] = g;
-        part[ti][1][wave][r] = uu;
-      }
-    }
-    // the waves in order; pair of the token: thread tid < 8 * tc
-    __syncthreads();
-    if (tid < 8 * tc) {
-      const int ti = tid >> 3, rr = tid & 7;
-      float g = 0.0f, uu = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        g += part[ti][0][w][rr];
-        uu += part[ti][1][w][rr];
-      }
-      const float hv = blob ? silu(g) * uu : 0.0f;
-      if (!(fabsf(hv) < 65520.0f)) *a.status = MOE_EUNSUP;
-      hws[(size_t)(p0 + c0 + ti) * I + hb * 8 + rr] = (_Float16)hv;
-    }
-    c0 += kTB;
-    if (c0 >= np) break;
-    __syncthreads();  // part[] is read before the next chunk writes it
-    load_x(c0);
-    stage_x(np - c0 < kTB ? np - c0 : kTB);
   }
+  if (bad) *a.status = MOE_EUNSUP;
 }
 
-// ------------------------------------------------------------------ down
-// One workgroup per (unit, 64 rows of H); wave w owns rows 16w .. 16w+15 of the
-// item, as four 4-row blocks of the blob. SPL = steps per lane = ceil(Gd / 16):
-// at step i lane (row r of 4, phase p of 16) takes group 16i + p of its row in
-// each block. The workgroup stages the h rows of kTBD pairs at a time into LDS,
-// all of a chunk's loads issued together; the first chunk's before the weights.
-constexpr int kDnRowsPerItem = 64;
-constexpr int kDnBlocks = 4;  // 4-row blocks per wave
-
-template <int SPL>
-__global__ void __launch_bounds__(kThreads) bat_down_kernel(FfnArgs a) {
-  // LDS: for each of the chunk's pairs, the h row as fp16 pairs [Gd][16] dwords
-  // and the group corrections [Gd]
+template <int NW, int CQ, int KM>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CQ <= 6 ? 6 : 4))) bmx_down_kernel(FfnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const int Gd = I / kGroup;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 3, p = lane >> 2;
+  const int n = lane & 15, q = lane >> 4;
   const bool has_shared = a.shared_blob != nullptr;
   const BatWs W = bat_ws(T, H, I, a.E, K, has_shared);
   const PlanView pl = plan_view(a.ws, W.U, W.P);
-  const int n_rb = H / kDnRowsPerItem;
-  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  const int n_nt = H / (16 * NW);
+  const int u = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const UnitHead uh = unit_head(pl, u, lane);
   const int p0 = uh.p0, np = uh.np;
   if (np == 0) return;
@@ -439,118 +402,58 @@ __global__ void __launch_bounds__(kThreads) bat_down_kernel(FfnArgs a) {
     if (tid == 0) *a.status = MOE_EUNSUP;
     return;
   }
-  uint32_t* hsl = reinterpret_cast<uint32_t*>(smem);
-  const int per_pair = Gd * 4;  // uint4 of one h row
-  // uint4 q of a chunk (thread tid holds q = tid + kThreads v) is pair q / per_pair,
-  // group (q / 4) % Gd, columns 8 (q % 4) .. +7: the four lanes of a group are a quad
-  constexpr int HQ = kTBD * SPL * 64 / kThreads;  // kTBD * Gd * 4 <= kThreads * HQ
-  const uint4* h4 = reinterpret_cast<const uint4*>(a.ws + W.h_off);
-  uint4 hv[HQ];
-  auto load_h = [&](int c0) {
-    const int tc = np - c0 < kTBD ? np - c0 : kTBD;
-#pragma unroll
-    for (int v = 0; v < HQ; ++v) {
-      const int q = tid + kThreads * v;
-      const int ti = q / per_pair;
-      const bool live = ti < tc;
-      const int row = p0 + c0 + (live ? ti : 0);
-      const int rem = live ? q - ti * per_pair : 0;
-      hv[v] = h4[(size_t)row * (I / 8) + rem];  // past the chunk: a row of it, never stored
-    }
-  };
-  load_h(0);  // before the weights: staging waits for these only
   const uint8_t* blob = rec_blob(a, uh.slot);
   const uint8_t* src = blob ? blob : a.slots;
   const BlobLayout BL = blob_layout(H, I);
-  const int n0 = rb * kDnRowsPerItem + wave * 16 + r;  // row of block b: n0 + 4b
-  uint4 cd[kDnBlocks][SPL];
-  uint32_t sdw[kDnBlocks][SPL];
-#pragma unroll
-  for (int i = 0; i < SPL; ++i) {
-#pragma unroll
-    for (int b = 0; b < kDnBlocks; ++b) {
-      int j = 16 * i + p;
-      j = j < Gd ? j : Gd - 1;
-      const int n = n0 + 4 * b;
-      cd[b][i] = *reinterpret_cast<const uint4*>(src + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
-      sdw[b][i] = reinterpret_cast<const uint32_t*>(src + BL.down_scales)[scale_off(n, j, Gd, kRowBlockDN) >> 2];
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  const int HB = bmx_row_bytes(I);
+  unsigned char* hs = smem;  // [KM][HB], then the zero tail
+  const __amdgpu_buffer_rsrc_t hr = buf_rsrc(a.ws + W.h_off, (uint32_t)((size_t)W.P * I * 2));
+  const __amdgpu_buffer_rsrc_t br = buf_rsrc(src, (uint32_t)BL.bytes);
+  const int row = (nt * NW + wave) * 16 + n;
+  const uint4* hap = reinterpret_cast<const uint4*>(hs + n * HB + q * 64);
   float* ows = reinterpret_cast<float*>(a.ws + W.o_off);
-  const int sh = (r & 1) * 16;
-  // a chunk's h rows and their group corrections into LDS
-  auto stage_h = [&](int tc) {
+  const uint32_t c_off = (uint32_t)code_off(row, q, Gd, kRowBlockDN), s_off = (uint32_t)scale_off(row, q, Gd, kRowBlockDN);
+  uint4 cd[CQ];
+  uint16_t sdb[CQ];
+  uint32_t zo = 0;
+  bool bad = false;
+  for (int m0 = 0; m0 < np; m0 += KM) {
+    if (m0 > 0) __syncthreads();
+    asm volatile("" : "+s"(zo));  // weight loads stay inside the M-tile (register pressure)
+    const int rows = np - m0 < KM ? np - m0 : KM;
+    for (int r = 0; r < rows; ++r)
+      stage_lds(hr, (uint32_t)((size_t)(p0 + m0 + r) * I * 2), I / 8, hs + r * HB, wave, lane, NW);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int v = 0; v < HQ; ++v) {
-      const int q = tid + kThreads * v;
-      const int ti = q / per_pair;
-      const int rem = q - ti * per_pair;
-      const uint32_t d[4] = {hv[v].x, hv[v].y, hv[v].z, hv[v].w};
-      float sa = (f16_lo(d[0]) + f16_hi(d[0])) + (f16_lo(d[2]) + f16_hi(d[2]));
-      float sb = (f16_lo(d[1]) + f16_hi(d[1])) + (f16_lo(d[3]) + f16_hi(d[3]));
-      sa = quad_xor_add<2>(quad_xor_add<1>(sa));
-      sb = quad_xor_add<2>(quad_xor_add<1>(sb));
-      if (ti < tc) {
-        uint32_t* ht = hsl + (size_t)ti * (Gd * 17);
-        reinterpret_cast<uint4*>(ht)[rem] = hv[v];
-        if ((lane & 3) == 0) reinterpret_cast<float*>(ht + Gd * 16)[rem >> 2] = fmaf(1032.0f, sa, 72.0f * sb);
-      }
+    for (int c = 0; c < CQ; ++c) {
+      cd[c] = bload16(br, c_off, zo + (uint32_t)BL.down_codes + (uint32_t)c * 4 * kRowBlockDN * 16);
+      sdb[c] = bload2(br, s_off, zo + (uint32_t)BL.down_scales + (uint32_t)c * 4 * kRowBlockDN * 2);
     }
-  };
-  // the first chunk is staged ahead of the loop, so that only the weights' first
-  // use waits for them
-  stage_h(np < kTBD ? np : kTBD);
-  __syncthreads();
-  for (int c0 = 0;;) {
-    const int tc = np - c0 < kTBD ? np - c0 : kTBD;
-    // one pair at a time: its four row sums over every step, then the phase sum
-    // (lane bits 2..5, read from lanes 0..3); o rows are in pair order
-    for (int ti = 0; ti < tc; ++ti) {
-      const uint32_t* ht = hsl + (size_t)ti * (Gd * 17);
-      float acc[kDnBlocks];
+    __builtin_amdgcn_sched_barrier(0);
+    bmx_zero_rows(hs, I, KM, rows, tid, NW * 64);
+    __builtin_amdgcn_s_waitcnt(vm_lds_imm(2 * CQ));
+    __builtin_amdgcn_s_barrier();
+    f32x4_t ao = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int b = 0; b < kDnBlocks; ++b) acc[b] = 0.0f;
+    for (int c = 0; c < CQ; ++c) {
+      if (4 * c >= Gd) continue;
+      uint4 ha[4];
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const int j = 16 * i + p;
-        const bool ok = blob != nullptr && j < Gd;
-        const int jc = j < Gd ? j : 0;
-        // the codes and scales are opaque per pair, so their fp16 pairs are formed
-        // per pair instead of being hoisted out of the pair loop (register
-        // pressure), and nothing before the chunk loop waits for the weights
+      for (int i = 0; i < 4; ++i) ha[i] = hap[16 * c + i];
+      const _Float16 sd = chunk_scale(sdb[c], blob != nullptr && 4 * c + q < Gd, &bad);
 #pragma unroll
-        for (int b = 0; b < kDnBlocks; ++b)
-          asm volatile("" : "+v"(cd[b][i].x), "+v"(cd[b][i].y), "+v"(cd[b][i].z), "+v"(cd[b][i].w), "+v"(sdw[b][i]));
-        const uint4* hq = reinterpret_cast<const uint4*>(ht + jc * 16);
-        const uint4 h0 = hq[0], h1 = hq[1], h2 = hq[2], h3 = hq[3];
-        const float C = reinterpret_cast<const float*>(ht + Gd * 16)[jc];
-#pragma unroll
-        for (int b = 0; b < kDnBlocks; ++b) {
-          float P = 0.0f;
-          P = code_dot(cd[b][i].x, h0.x, h0.y, h0.z, h0.w, P);
-          P = code_dot(cd[b][i].y, h1.x, h1.y, h1.z, h1.w, P);
-          P = code_dot(cd[b][i].z, h2.x, h2.y, h2.z, h2.w, P);
-          P = code_dot(cd[b][i].w, h3.x, h3.y, h3.z, h3.w, P);
-          const float sc = ok ? f16_lo(sdw[b][i] >> sh) : 0.0f;
-          acc[b] = fmaf(sc, P - C, acc[b]);
-        }
-        asm volatile("" ::: "memory");  // one step's h operands at a time (register pressure)
-      }
-      const int pr = __builtin_amdgcn_readlane(uh.my_pair, c0 + ti);
-#pragma unroll
-      for (int b = 0; b < kDnBlocks; ++b) {
-        const float o = sum_rows(dpp_add<8>(dpp_add<4>(acc[b])));
-        if (p == 0) ows[(size_t)pr * H + n0 + 4 * b] = o;
-      }
+      for (int i = 0; i < 4; ++i)
+        ao = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ha[i]), dequant_qs(dword_of(cd[c], i), sd), ao, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // one chunk's operands at a time (register pressure)
     }
-    c0 += kTBD;
-    if (c0 >= np) break;
-    __syncthreads();  // every wave is done with this chunk
-    load_h(c0);
-    stage_h(np - c0 < kTBD ? np - c0 : kTBD);
-    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * q + v;
+      const int pr = __shfl(uh.my_pair, m0 + (m < rows ? m : 0), 64);
+      if (m < rows) ows[(size_t)pr * H + row] = ao[v];
+    }
   }
+  if (bad) *a.status = MOE_EUNSUP;
 }
 
 // ------------------------------------------------------------------ combine
@@ -590,9 +493,8 @@ inline void set_lds_limit(const void* fn, size_t lds) {
 
 bool batched_supported(int T, int H, int I, int K) {
   const int G = H / kGroup, Gd = I / kGroup;
-  // gate/up: at most 4 groups per lane; down: at most 4 steps of 16 groups
-  return T >= 2 && T <= kGemvMaxT && T * K <= kBatMaxPairs && G <= 4 * 8 * 4 && Gd <= 4 * 16 && H % kDnRowsPerItem == 0 &&
-         I % 8 == 0;
+  // gate/up: at most 32 chunks of 4 groups (LDS: 16 rows of x); down: at most 16
+  return T >= 2 && T <= kGemvMaxT && T * K <= kBatMaxPairs && G <= 128 && Gd <= 64;
 }
 
 size_t batched_workspace_bytes(int T, int H, int I, int E, int K, int has_shared) {
@@ -602,40 +504,56 @@ size_t batched_workspace_bytes(int T, int H, int I, int E, int K, int has_shared
 hipError_t launch_ffn_batched(const FfnArgs& a, int stage, hipStream_t s) {
   const bool has_shared = a.shared_blob != nullptr;
   const BatWs W = bat_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
+  constexpr int KM = 16;  // pairs per M-tile
   if (stage == 0) {
     const int conv_blocks = (a.T * a.H / 2 + kPlanThreads - 1) / kPlanThreads;
     hipLaunchKernelGGL(bat_plan_kernel, dim3(1 + conv_blocks), dim3(kPlanThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int G = a.H / kGroup;
-    const int GW = (G + kWaves - 1) / kWaves;
-    const int gpl = (GW + 7) / 8;
-    const size_t lds = (size_t)kWaves * kTB * GW * 17 * 4;
-    const int grid = W.U * (a.I / 8);
-#define GU(N)                                                                                       \
+    const int chunks = (a.H / kGroup + 3) / 4;
+    const size_t lds = bmx_lds(a.H, KM);
+    // 96-row workgroups where I allows (two resident per CU), else 64 or 32 rows
+    const int nw = a.I % 96 == 0 ? 6 : (a.I % 64 == 0 ? 4 : 2);
+#define GU(NW, CQ)                                                                                  \
   do {                                                                                              \
-    set_lds_limit(reinterpret_cast<const void*>(&bat_gateup_kernel<N>), lds);                       \
-    hipLaunchKernelGGL((bat_gateup_kernel<N>), dim3(grid), dim3(kThreads), lds, s, a);              \
+    constexpr int CW = CQ < 6 ? CQ : 6;                                                             \
+    set_lds_limit(reinterpret_cast<const void*>(&bmx_gateup_kernel<NW, CQ, CW, KM>), lds);          \
+    hipLaunchKernelGGL((bmx_gateup_kernel<NW, CQ, CW, KM>), dim3(W.U * (a.I / (16 * NW))), dim3(NW * 64), lds, s, a); \
   } while (0)
-    if (gpl <= 1) GU(1);
-    else if (gpl <= 2) GU(2);
-    else GU(4);
+#define GU_NW(CQ)                \
+  do {                           \
+    if (nw == 6) GU(6, CQ);      \
+    else if (nw == 4) GU(4, CQ); \
+    else GU(2, CQ);              \
+  } while (0)
+    if (chunks <= 4) GU_NW(4);
+    else if (chunks <= 8) GU_NW(8);
+    else if (chunks <= 16) GU_NW(16);
+    else GU_NW(32);
+#undef GU_NW
 #undef GU
     return hipGetLastError();
   }
   {
-    const int Gd = a.I / kGroup;
-    const int spl = (Gd + 15) / 16;
-    const size_t lds = (size_t)kTBD * Gd * 17 * 4;
-    const int grid = W.U * (a.H / kDnRowsPerItem);
-#define DN(N)                                                                                       \
+    const int chunks = (a.I / kGroup + 3) / 4;
+    const size_t lds = bmx_lds(a.I, KM);
+    const int nw = a.H % 64 == 0 ? 4 : 2;
+#define DN(NW, CQ)                                                                                  \
   do {                                                                                              \
-    set_lds_limit(reinterpret_cast<const void*>(&bat_down_kernel<N>), lds);                         \
-    hipLaunchKernelGGL((bat_down_kernel<N>), dim3(grid), dim3(kThreads), lds, s, a);                \
+    set_lds_limit(reinterpret_cast<const void*>(&bmx_down_kernel<NW, CQ, KM>), lds);                \
+    hipLaunchKernelGGL((bmx_down_kernel<NW, CQ, KM>), dim3(W.U * (a.H / (16 * NW))), dim3(NW * 64), lds, s, a); \
   } while (0)
-    if (spl <= 1) DN(1);
-    else if (spl <= 2) DN(2);
-    else DN(4);
+#define DN_NW(CQ)           \
+  do {                      \
+    if (nw == 4) DN(4, CQ); \
+    else DN(2, CQ);         \
+  } while (0)
+    if (chunks <= 2) DN_NW(2);
+    else if (chunks <= 4) DN_NW(4);
+    else if (chunks <= 6) DN_NW(6);
+    else if (chunks <= 8) DN_NW(8);
+    else DN_NW(16);
+#undef DN_NW
 #undef DN
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -33,6 +33,7 @@
 //      fp32, rounded once to bf16.
 #include <type_traits>
 
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -271,23 +272,6 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 // N-tile run back to back on one XCD and meet its weight bytes in that XCD's
 // L2.
 constexpr int kTM = 128, kTN = 256, kTK = 64;
-
-// Loads straight into LDS (gfx950 buffer_load ... lds): lane l's n bytes (n = 4
-// or 16) from base + voffset + soffset land at lds + n l; lds must be the same on
-// every lane of the wave (an instruction offset would move the LDS address too,
-// so none is used). The buffer form rather than the global one: the
-// compiler treats a pending global (FLAT) load into LDS as an out-of-order LDS
-// access and then waits for every LDS read at once, instead of only for the one
-// an MFMA needs. A read past the descriptor's byte range returns zeros.
-__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ inline void ld16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-}
-__device__ inline void ld4_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
-}
 
 template <int MODE>
 __host__ __device__ inline int gemm_n_tiles(int H, int I) {

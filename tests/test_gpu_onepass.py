@@ -69,6 +69,10 @@ WLS = [
     gen.Workload("onepass_t1_h4096_e256_k8_i1536", 1, 4096, 256, 8, 1536, 3, 64, "gemv", 601),
     gen.Workload("onepass_t1_h512_e64_k4_i512_shared", 1, 512, 64, 4, 512, 3, 64, "gemv", 602, shared=True),
     gen.Workload("onepass_t1_h256_e8_k8_i512", 1, 256, 8, 8, 512, 3, 8, "gemv", 603),
+    # 9 units of 48 groups: the two-kernel down splits a unit's columns between two waves
+    gen.Workload("onepass_t1_h512_e64_k8_i1536_shared", 1, 512, 64, 8, 1536, 3, 64, "gemv", 605, shared=True),
+    # the paged decode shape (6 routed + a shared expert, I 2048)
+    gen.Workload("onepass_t1_h4096_e256_k6_i2048_shared", 1, 4096, 256, 6, 2048, 2, 64, "gemv", 606, shared=True),
 ]
 
 

@@ -220,6 +220,28 @@ def test_ffn_ragged_shapes(w):
     ffn_case(w, 0, flags=lib.MOE_FORCE_GEMV)
 
 
+@pytest.mark.parametrize(
+    "w",
+    [
+        # 32 shared pairs (two M-tiles of 16), I 160: 32-row gate/up workgroups
+        gen.Workload("bat_t32_h512_e40_k5_i160_shared", 32, 512, 40, 5, 160, 1, 40, "normal", 25, shared=True),
+        # 3 groups in H and in I: one partial chunk each; H 96: 32-row down workgroups
+        gen.Workload("bat_t7_h96_e16_k3_i96", 7, 96, 16, 3, 96, 1, 16, "normal", 26),
+        # 32 chunks of gate/up codes per wave, 16 of down
+        gen.Workload("bat_t3_h4096_e8_k4_i2048", 3, 4096, 8, 4, 2048, 1, 8, "zipf", 27),
+        # two tokens, I 64 (one 64-row item), H 160 (5 groups)
+        gen.Workload("bat_t2_h160_e6_k6_i64", 2, 160, 6, 6, 64, 1, 6, "normal", 28),
+        # every expert takes all 24 tokens: 24 pairs per unit, two M-tiles everywhere
+        gen.Workload("bat_t24_h1024_e8_k8_i512_shared", 24, 1024, 8, 8, 512, 1, 8, "normal", 29, shared=True),
+    ],
+    ids=lambda w: w.name,
+)
+def test_ffn_batched_shapes(w):
+    """The small-batch path (default for 2 <= T <= 32) on partial chunks, each
+    workgroup width and units with more pairs than one M-tile."""
+    ffn_case(w, 0)
+
+
 # ------------------------------------------------------------------ whole layer (moe_layer)
 
 

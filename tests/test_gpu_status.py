@@ -106,11 +106,11 @@ def test_format_paths_report_fp16_overflow(fmt, kind, T):
     assert int(st.item()) == lib.MOE_EUNSUP
 
 
-@pytest.mark.parametrize("T,H,I", [(1, 256, 96), (5, 96, 512)])
+@pytest.mark.parametrize("T,H,I", [(1, 256, 96), (5, 96, 2080)])
 def test_gemv_path_computes_large_activations(T, H, I):
     """The general GEMV kernels (bf16 x, fp32 h; the shapes the single-token and batched
-    kernels do not take: I / 32 not a multiple of 16 for one token, H not a multiple of 64
-    for several) compute activations whose h overflows fp16, against the oracle."""
+    kernels do not take: I / 32 not a multiple of 16 for one token, I / 32 above 64 for
+    several) compute activations whose h overflows fp16, against the oracle."""
     from parity_util import OracleExperts
 
     w = gen.Workload(f"large_x_gemv_t{T}_h{H}_i{I}", T, H, 8, 2, I, 1, 8, "normal", 304, shared=True)
@@ -159,3 +159,25 @@ def test_paged_layer_speculative_result_keeps_its_status():
         assert (st1["misses"] > st0["misses"]) == misses  # no miss: the speculative result is the one kept
         assert int(dec.status.item()) == want, step
         dec.status.zero_()
+
+
+def test_batched_reports_scale_past_fp16_product_range():
+    """The small-batch path forms fp16(q * s) as its MFMA operand; a group scale of
+    magnitude >= 8192 could overflow that product and must set MOE_EUNSUP. One scale
+    (gate, row 0, group 0) of a routed expert is set to 8192 in the arena."""
+    T = 6
+    w = gen.Workload("status_batched_scale", T, 256, 8, 2, 512, 1, 8, "normal", 302)
+    logits = gen.normal_logits(w.seed, 0, T, w.E)
+    ids_ref, _ = R.route(logits, w.K)
+    L = harness.make_layer(w, 0, DEV, logits=logits)
+    e = int(ids_ref[0, 0])
+    slot = int(L.table[e].item())
+    gate_scales = 3 * w.H * w.I // 2  # codes of gate, up and down come first in the blob
+    off = slot * L.stride + gate_scales
+    L.slots[off:off + 2] = torch.tensor([0x00, 0x70], dtype=torch.uint8, device=DEV)  # fp16 8192, little-endian
+    say("batched scale 8192")
+    run = harness.LayerRunner(w, DEV)
+    run(L)
+    torch.cuda.synchronize()
+    assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
+    assert int(run.status.item()) == lib.MOE_EUNSUP
