@@ -910,7 +910,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights + fp16 group scales, bf16 activations, fp32 accumulate",
+        "dtype": "int4 weights (fp16 group scales); bf16 x and y, x and h fed to the dot products as fp16; fp32 accumulate",
         "data": "synthetic (seeded)",
         "config": {
             "workload": w.name,

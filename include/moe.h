@@ -178,6 +178,18 @@ int moe_route_onepass(const uint16_t* x, const float* w_router, float* logits, i
  * with FFN(x) = Wd (silu(Wg x) * (Wu x)), silu(z) = z / (1 + e^-z), the terms
  * added in rank order, fp32 accumulation and one bf16 rounding (nearest even)
  * of y. Expert e's blob is at slots + slot_table[e] * stride.
+ * Passages: top-k routed experts plus one shared expert ("Strata" README,
+ * the models table: 256 experts + 1 shared, top-10 / top-8 / top-6); 4-bit
+ * group-quantised experts executed W4A16, i.e. dequantised inside the matrix
+ * products against 16-bit activations ("Strata" README, the models table and
+ * Kernels: native INT4 group kernels); the prompt's expert GEMMs ("Strata on
+ * a Mac", Switches). The SwiGLU form of each expert is this library's reading
+ * of the expert FFN, which the pages name but do not write out. Arithmetic of the
+ * paths: codes become exact fp16 values; x and h are fp16 operands (bf16 x
+ * converts exactly for |x| in [2^-17, 65504], a value past fp16 sets
+ * MOE_EUNSUP); the single-token path applies each group's fp16 scale in fp32,
+ * the batched and grouped paths multiply it into an fp16 operand fp16(q * s)
+ * (one rounding, relative error <= 2^-11).
  *   x          device bf16 [T][H].
  *   ids, w     device [T][K] as written by moe_route.
  *   slot_table device int32 [E]; -1 marks an expert that is not resident.
