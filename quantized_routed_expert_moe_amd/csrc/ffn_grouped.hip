@@ -25,10 +25,12 @@
 //      matching g and u and writes h = silu(g) * u in fp16 (the next A
 //      operand; overflow sets the status word).
 //   4. down GEMM (grouped_gemm_kernel<1>): A = h rows, B = fp16(q * s) of the
-//      down matrix; o is written in fp32 at the pair's own index (no rounding
-//      before the combine: a routed term rounded to bf16 would carry up to
-//      2^-8 of its own magnitude into y, which the 2e-2 * rms bar cannot
-//      absorb when the weighted terms are several times rms(y)).
+//      down matrix; o is written in fp16 at the pair's own index: one rounding
+//      of relative error <= 2^-11 per routed term (bf16 would carry up to 2^-8
+//      of the term's magnitude into y, more than a 2e-2 * rms bar absorbs when
+//      the weighted terms are several times rms(y)); a value that does not
+//      fit fp16 sets MOE_EUNSUP. fp16 halves the o bytes written here and
+//      read by the combine (o is the largest buffer of a prompt layer).
 //   5. combine: y[t] = o_shared[t] + sum_k w[t][k] * o[t][k] in rank order,
 //      fp32, rounded once to bf16.
 #include <type_traits>
@@ -78,7 +80,7 @@ __host__ __device__ inline GroupedWs grouped_ws(int T, int H, int I, int E, int 
   w.xh = al256(w.sorted + PA * sizeof(int32_t));
   w.h = al256(w.xh + (size_t)T * H * 2);
   w.o = al256(w.h + PA * (size_t)I * 2);
-  w.done = al256(w.o + PA * (size_t)H * 4);  // o: fp32
+  w.done = al256(w.o + PA * (size_t)H * 2);  // o: fp16
   w.bytes = al256(w.done + ((size_t)E + 2) * sizeof(int32_t));
   return w;
 }
@@ -242,6 +244,8 @@ __global__ void __launch_bounds__(256) to_f16_kernel(FfnArgs a) {
 }
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+__device__ inline float f16_lo_f(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
+__device__ inline float f16_hi_f(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 
 // MODE 0: gate/up with SwiGLU epilogue (writes h in segment order).
 // MODE 1: down (writes o at the pair's index).
@@ -562,7 +566,8 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
       }
     }
   } else {
-    float* ows = reinterpret_cast<float*>(a.ws + W.o);
+    _Float16* ows = reinterpret_cast<_Float16*>(a.ws + W.o);
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -573,24 +578,29 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
 #pragma unroll
           for (int n = 0; n < 4; ++n) {
             const int col = nt * kTN + wave * 64 + n * 16 + (lane & 15);
-            if (col < H) ows[(size_t)p * H + col] = acc[i][n][v];
+            if (col < H) {
+              const float ov = acc[i][n][v];
+              bad |= !(fabsf(ov) < 65520.0f);  // o does not fit its fp16 store
+              ows[(size_t)p * H + col] = (_Float16)ov;
+            }
           }
         }
       }
     }
+    if (bad) *a.status = MOE_EUNSUP;
   }
 }
 
 // ------------------------------------------------------------------ combine
-// Thread: 8 consecutive columns of one token; the token's o rows (fp32, 32 bytes
+// Thread: 8 consecutive columns of one token; the token's o rows (fp16, 16 bytes
 // each) are loaded eight at a time before the sums, which run in rank order.
 __global__ void __launch_bounds__(256) grouped_combine_kernel(FfnArgs a) {
   const int H = a.H, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(T, H, a.I, a.E, K, has_shared);
-  const float4* o4 = reinterpret_cast<const float4*>(a.ws + W.o);  // 4 fp32 per float4
+  const uint4* o8 = reinterpret_cast<const uint4*>(a.ws + W.o);  // 8 fp16 per uint4
   const int P = T * K;
-  const int H8 = H / 8, H4 = H / 4;
+  const int H8 = H / 8;
   const size_t n8 = (size_t)T * H8;
   const bool check = a.mode & kModeCheckDone;
   const int32_t* done = reinterpret_cast<const int32_t*>(a.ws + W.done);
@@ -610,30 +620,32 @@ __global__ void __launch_bounds__(256) grouped_combine_kernel(FfnArgs a) {
     }
     float acc[8];
     if (has_shared) {
-      const float4 v0 = o4[(size_t)(P + t) * H4 + 2 * c8], v1 = o4[(size_t)(P + t) * H4 + 2 * c8 + 1];
-      acc[0] = v0.x, acc[1] = v0.y, acc[2] = v0.z, acc[3] = v0.w;
-      acc[4] = v1.x, acc[5] = v1.y, acc[6] = v1.z, acc[7] = v1.w;
+      const uint4 v = o8[(size_t)(P + t) * H8 + c8];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[2 * e] = f16_lo_f(d[e]), acc[2 * e + 1] = f16_hi_f(d[e]);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     }
     for (int k0 = 0; k0 < K; k0 += 8) {
-      float4 ov[8][2];
+      uint4 ov[8];
       float wv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int k = k0 + j < K ? k0 + j : K - 1;
-        ov[j][0] = o4[(size_t)(t * K + k) * H4 + 2 * c8];
-        ov[j][1] = o4[(size_t)(t * K + k) * H4 + 2 * c8 + 1];
+        ov[j] = o8[(size_t)(t * K + k) * H8 + c8];
         wv[j] = a.w[t * K + k];
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (k0 + j < K) {
-          const float d[8] = {ov[j][0].x, ov[j][0].y, ov[j][0].z, ov[j][0].w,
-                              ov[j][1].x, ov[j][1].y, ov[j][1].z, ov[j][1].w};
+          const uint32_t d[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = fmaf(wv[j], d[e], acc[e]);
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(wv[j], f16_lo_f(d[e]), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(wv[j], f16_hi_f(d[e]), acc[2 * e + 1]);
+          }
         }
       }
     }
