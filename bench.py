@@ -448,12 +448,13 @@ def paged_leg(a, dev):
     ys = [torch.empty(1, w.H, dtype=torch.bfloat16, device=dev) for _ in range(w.layers)]
     y_res = torch.empty(1, w.H, dtype=torch.bfloat16, device=dev)
     res = {}
-    for mode, native in (("python", False), ("native", True)):
+    # native: ids to the host through the polled word; native_event: through a copy and an event
+    for mode, native, poll in (("python", False, False), ("native_event", True, False), ("native", True, True)):
         for ar, _, tb in layers:
             ar.reset()
             tb.fill_(-1)
         dec = paged.PagedDecode(layers, [None] * w.layers, stride, w.H, w.I, w.E, w.K, shared=[shared] * w.layers,
-                                device=dev, native=native, speculate=native)
+                                device=dev, native=native, speculate=native, host_poll=poll)
         lgs = [[lg[s, l] for l in range(w.layers)] for s in range(steps)]
         for s in range(warm):
             dec.token(xs, ys, lgs[s])
@@ -545,8 +546,10 @@ def paged_leg(a, dev):
         "misses_per_layer_step": d["misses"] / (n_tok * w.layers),
         "h2d_gbs": d["h2d_bytes"] / dt / 1e9,
         "h2d_peak_gbs": h2d_peak,
-        "identical": identical and res["python"][2],
+        "identical": identical and res["python"][2] and res["native_event"][2],
         "python_tok_s": n_tok / res["python"][0],
+        "event_handshake_tok_s": n_tok / res["native_event"][0],
+        "event_handshake_h2d_gbs": res["native_event"][1]["h2d_bytes"] / res["native_event"][0] / 1e9,
         "resident_tok_s": 1e3 / res_ms,
         "resident_hbm_gbs": res_bytes / (res_ms * 1e-3) / 1e9,
     }
@@ -999,7 +1002,9 @@ def main():
             "h2d_pinned_copy_gbs": round(q["h2d_peak_gbs"], 2),
             "bit_identical_to_resident": q["identical"],
             "host_weight_sets": 1,
-            "sequencing": "moe_paged_layer (native, speculative FFN)",
+            "sequencing": "moe_paged_layer (native, speculative FFN, ids to the host through a polled word)",
+            "event_handshake_tokens_per_s": round(q["event_handshake_tok_s"], 2),
+            "event_handshake_h2d_gbs": round(q["event_handshake_h2d_gbs"], 2),
             "python_sequenced_tokens_per_s": round(q["python_tok_s"], 2),
             "resident_tokens_per_s": round(q["resident_tok_s"], 1),
             "resident_hbm_gbs": round(q["resident_hbm_gbs"], 1),

@@ -428,10 +428,14 @@ void arena_destroy(moe_arena* a);
  *      logits; with read-ahead (next, w_predict and P > 0) also the top-P of
  *      w_predict on the same x -> ids[K..K+P), w[K..K+P) (which overwrites
  *      logits);
- *   2. the K (+ P) ids to ids_host, then hipEventRecord(ids_ready);
+ *   2. the K (+ P) ids to ids_host, then hipEventRecord(ids_ready); with
+ *      MOE_PAGED_HOST_POLL instead a one-wave kernel stores the ids into
+ *      ids_host and then ids_host[K (+ P)] = s + 1, where s is the value that
+ *      word held when the call began (system-scope stores, the word released
+ *      last), and the host spins on that word;
  *   3. with MOE_PAGED_SPECULATE the expert FFN is enqueued at once, after the
  *      last fills into layer->arena, with its status word in the workspace;
- *   4. the host waits for ids_ready, arena_map_slots on the K ids, enqueues
+ *   4. the host waits for ids_ready (or the word), arena_map_slots on the K ids, enqueues
  *      the misses on `side` (arena_fill_async), then arena_prefetch of the P
  *      predicted ids into next->arena and their fills, after the misses;
  *   5. if the map missed any expert, or without MOE_PAGED_SPECULATE, `stream`
@@ -447,12 +451,15 @@ void arena_destroy(moe_arena* a);
  *   w_predict     device fp32 [E][H] predicting next's experts from x, or NULL;
  *   ids, w        device int32 / fp32, K + P entries; logits device fp32 [E];
  *   ids_host      pinned host int32, K + P entries (the ids, readable on
- *                 return);
+ *                 return), K + P + 1 with MOE_PAGED_HOST_POLL (the last is the
+ *                 sequence word; the host spins on it for at most 5 s, then
+ *                 returns MOE_EHIP);
  *   ws            device, ws_bytes >= moe_paged_workspace_bytes();
- *   ids_ready     a HIP event owned by the caller;
+ *   ids_ready     a HIP event owned by the caller (may be NULL with
+ *                 MOE_PAGED_HOST_POLL);
  *   n_misses, n_prefetched  (host, may be NULL) the fills of the map and of
  *                 the prefetch.
- * The call returns after step 5 is enqueued (it blocks only on ids_ready).
+ * The call returns after step 5 is enqueued (it blocks only on the ids).
  * Calls for the layers of a token go in order on one compute stream; no other
  * GPU work may read an arena while these calls run. Arena rules and errors as
  * arena_map_slots / arena_prefetch / moe_expert_ffn; MOE_EINVAL also for an
@@ -464,6 +471,7 @@ typedef struct {
   const void* shared_blob; /* device blob of the always-on shared expert, or NULL */
 } moe_paged_layer_t;
 #define MOE_PAGED_SPECULATE 1u
+#define MOE_PAGED_HOST_POLL 2u /* the ids reach the host through a polled word, not an event */
 size_t moe_paged_workspace_bytes(int H, int I, int E, int K, int has_shared); /* 0: unsupported shape */
 int moe_paged_layer(const moe_paged_layer_t* layer, const moe_paged_layer_t* next, const float* w_predict, int P,
                     const uint16_t* x, int H, int I, int E, int K, int g, float* logits, int32_t* ids, float* w,

@@ -181,5 +181,7 @@ hipError_t launch_table_update(int32_t* table, const int32_t* idx, const int32_t
 // one-thread status word kernel: src == nullptr clears *dst; otherwise a non-zero
 // *src is copied into *dst if *dst is still zero (the first error is kept)
 hipError_t launch_status(int32_t* dst, const int32_t* src, hipStream_t s);
+// ids[0..n) to pinned host memory host[0..n), then host[n] = seq (system scope, released)
+hipError_t launch_publish_ids(const int32_t* ids, int n, int32_t* host, int32_t seq, hipStream_t s);
 
 }  // namespace moe

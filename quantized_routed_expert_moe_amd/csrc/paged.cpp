@@ -8,11 +8,15 @@
 //   1. moe_route of x with the layer's router, or on the caller's logits (and,
 //      with read-ahead, the top-P of the predictor on the same x: the next
 //      layer's probable experts);
-//   2. the ids to pinned host memory, event `ids_ready`;
+//   2. the ids to pinned host memory, event `ids_ready`; with
+//      MOE_PAGED_HOST_POLL instead a one-wave kernel stores them there and then
+//      a sequence word (system scope), which the host polls (no copy launch and
+//      no event wake-up between the route and the fills);
 //   3. with MOE_PAGED_SPECULATE: the expert FFN is enqueued at once, after the
 //      last fills into this layer's arena, with its status word in the
 //      workspace. It reads the slots the device table names when it runs;
-//   4. the host waits for `ids_ready` only (not for the FFN), maps the ids
+//   4. the host waits for `ids_ready` (or the sequence word) only (not for the
+//      FFN), maps the ids
 //      (arena_map_slots) and enqueues the misses' copies on `side`, then the
 //      read-ahead (arena_prefetch into the next layer's arena) after them;
 //   5. if the layer missed any expert, or without speculation, the compute
@@ -35,9 +39,13 @@
 // prefetch writes another layer's arena (the same arena as the layer's own is
 // rejected). A caller that runs several layers must call them in order on one
 // compute stream.
+#include <chrono>
+
 #include "arena_internal.h"
 
 namespace {
+
+constexpr double kPollSeconds = 5.0;  // bound of the host's wait for the ids
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -55,10 +63,11 @@ extern "C" int moe_paged_layer(const moe_paged_layer_t* cur, const moe_paged_lay
                                int32_t* ids, float* w, int32_t* ids_host, uint16_t* y, void* ws, size_t ws_bytes,
                                int32_t* dev_status, unsigned flags, moe_stream_t stream, moe_stream_t side,
                                moe_event_t ids_ready, int* n_misses, int* n_prefetched) {
+  const bool poll = (flags & MOE_PAGED_HOST_POLL) != 0;
   if (!cur || !arena_ready(cur->arena) || !x || !logits || !ids || !w || !ids_host || !y || !ws || !dev_status ||
-      !ids_ready)
+      (!ids_ready && !poll))
     return MOE_EINVAL;
-  if (flags & ~(unsigned)MOE_PAGED_SPECULATE) return MOE_EINVAL;
+  if (flags & ~(unsigned)(MOE_PAGED_SPECULATE | MOE_PAGED_HOST_POLL)) return MOE_EINVAL;
   moe_arena* A = cur->arena;
   if (E != A->E || K < 1 || K > A->S) return MOE_EINVAL;
   if (K > moe::kMaxK) return MOE_EUNSUP;
@@ -82,9 +91,17 @@ extern "C" int moe_paged_layer(const moe_paged_layer_t* cur, const moe_paged_lay
     rc = moe_route(x, w_predict, logits, 1, H, E, P, 0, ids + K, w + K, stream);
     if (rc != MOE_OK) return rc;
   }
-  if (hipMemcpyAsync(ids_host, ids, sizeof(int32_t) * n_ids, hipMemcpyDeviceToHost, s) != hipSuccess)
-    return MOE_EHIP;
-  if (hipEventRecord(static_cast<hipEvent_t>(ids_ready), s) != hipSuccess) return MOE_EHIP;
+  int32_t seq = 0;
+  if (poll) {
+    // the word after the ids: this call waits for the next value of whatever it holds
+    seq = __atomic_load_n(ids_host + n_ids, __ATOMIC_ACQUIRE) + 1;
+    if (seq == 0) seq = 1;
+    if (moe::launch_publish_ids(ids, n_ids, ids_host, seq, s) != hipSuccess) return MOE_EHIP;
+  } else {
+    if (hipMemcpyAsync(ids_host, ids, sizeof(int32_t) * n_ids, hipMemcpyDeviceToHost, s) != hipSuccess)
+      return MOE_EHIP;
+    if (hipEventRecord(static_cast<hipEvent_t>(ids_ready), s) != hipSuccess) return MOE_EHIP;
+  }
 
   const bool spec = (flags & MOE_PAGED_SPECULATE) != 0;
   auto run_ffn = [&](int32_t* status) -> int {
@@ -100,7 +117,15 @@ extern "C" int moe_paged_layer(const moe_paged_layer_t* cur, const moe_paged_lay
     if ((rc = run_ffn(spec_status)) != MOE_OK) return rc;
   }
 
-  if (hipEventSynchronize(static_cast<hipEvent_t>(ids_ready)) != hipSuccess) return MOE_EHIP;
+  if (poll) {
+    const auto t0 = std::chrono::steady_clock::now();
+    for (unsigned it = 1; __atomic_load_n(ids_host + n_ids, __ATOMIC_ACQUIRE) != seq; ++it)
+      if ((it & 4095u) == 0 &&
+          std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() > kPollSeconds)
+        return MOE_EHIP;  // the ids did not arrive (a failed launch upstream)
+  } else if (hipEventSynchronize(static_cast<hipEvent_t>(ids_ready)) != hipSuccess) {
+    return MOE_EHIP;
+  }
   int32_t slots_of[moe::kMaxK];
   moe_fill fills[moe::kMaxK];
   int nf = 0;

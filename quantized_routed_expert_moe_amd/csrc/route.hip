@@ -216,6 +216,15 @@ __global__ void __launch_bounds__(64) table_update_kernel(int32_t* table, TableU
   if (i < u.n) table[u.idx[i]] = u.val[i];
 }
 
+// The n ids to pinned host memory, then host[n] = seq: one lane stores every id
+// at system scope and then the sequence word with a system-scope release, so a
+// host that reads seq in host[n] (acquire) also reads the ids of this call.
+__global__ void __launch_bounds__(64) publish_ids_kernel(const int32_t* ids, int n, int32_t* host, int32_t seq) {
+  if (threadIdx.x != 0) return;
+  for (int i = 0; i < n; ++i) __hip_atomic_store(host + i, ids[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(host + n, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // src == nullptr: *dst = 0. Else the first error wins: a non-zero *src is copied
 // into *dst when *dst is still 0.
 __global__ void __launch_bounds__(64) status_kernel(int32_t* dst, const int32_t* src) {
@@ -262,6 +271,11 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigne
   else if (epl <= 8) SEL(8);
   else SEL(16);
 #undef SEL
+  return hipGetLastError();
+}
+
+hipError_t launch_publish_ids(const int32_t* ids, int n, int32_t* host, int32_t seq, hipStream_t s) {
+  hipLaunchKernelGGL(publish_ids_kernel, dim3(1), dim3(64), 0, s, ids, n, host, seq);
   return hipGetLastError();
 }
 

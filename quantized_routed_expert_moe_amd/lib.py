@@ -82,6 +82,7 @@ class moe_paged_layer_t(ctypes.Structure):
 
 
 MOE_PAGED_SPECULATE = 1
+MOE_PAGED_HOST_POLL = 2
 
 
 class moe_arena_stats(ctypes.Structure):

@@ -145,12 +145,14 @@ class PagedDecode:
     the device fp32 ``[E, H]`` matrix applied to the previous layer's input to
     predict this layer's experts (default: the layer's own router). ``native``:
     one ``moe_paged_layer`` call per layer (else the same steps from Python);
-    ``speculate``: with ``native``, the FFN starts before the hand-shake.
+    ``speculate``: with ``native``, the FFN starts before the hand-shake;
+    ``host_poll``: with ``native``, the ids reach the host through a polled word in
+    pinned memory rather than a copy and an event.
     """
 
     def __init__(self, layers, routers, stride: int, H: int, I: int, E: int, K: int, shared=None,
                  predict: int = 0, g: int = 32, device="cuda", predictors=None, native: bool = True,
-                 speculate: bool = True):
+                 speculate: bool = True, host_poll: bool = True):
         if len(routers) != len(layers) or (predictors is not None and len(predictors) != len(layers)):
             raise ValueError("one router (and one predictor) per layer")
         if not 0 <= predict <= min([E] + [a.S for a, _, _ in layers]):
@@ -168,10 +170,10 @@ class PagedDecode:
         self.p_logits = torch.empty(1, E, dtype=torch.float32, device=device)
         self.p_ids = torch.empty(1, P, dtype=torch.int32, device=device)
         self.p_wts = torch.empty(1, P, dtype=torch.float32, device=device)
-        self.ids_h = torch.empty(K + P, dtype=torch.int32, pin_memory=True)
+        self.ids_h = torch.zeros(K + P + 1, dtype=torch.int32, pin_memory=True)  # + the polled word
         has_shared = any(b is not None for b in self.shared)
         self.ws_bytes = lib.moe_ffn_workspace_bytes(1, H, I, E, K, has_shared)
-        self.native, self.speculate = native, speculate
+        self.native, self.speculate, self.host_poll = native, speculate, host_poll
         if native:
             self.ws_bytes = lib.moe_paged_workspace_bytes(H, I, E, K, has_shared)
             self.nat_ids = torch.empty(K + P, dtype=torch.int32, device=device)
@@ -229,7 +231,8 @@ class PagedDecode:
         lib.moe_paged_layer(self.descs[l], self.descs[l + 1] if ahead else None,
                             self.predictors[l + 1] if ahead else None, P if ahead else 0, x, self.H, self.I, self.E,
                             K, self.g, lg, self.nat_ids, self.nat_w, self.ids_h, y, self.ws, self.ws_bytes,
-                            self.status, lib.MOE_PAGED_SPECULATE if self.speculate else 0,
+                            self.status, (lib.MOE_PAGED_SPECULATE if self.speculate else 0)
+                            | (lib.MOE_PAGED_HOST_POLL if self.host_poll else 0),
                             torch.cuda.current_stream(), self.side, self.ids_ready)
         if self.log is not None:
             self.log.append(("map", l, self.ids_h[:K].tolist()))

@@ -853,15 +853,17 @@ def test_fmt_int4_g32_is_moe_expert_ffn():
 
 
 @pytest.mark.parametrize(
-    "predict,wrong,native,speculate",
-    [(0, False, False, False), (4, False, False, False), (0, False, True, True), (4, False, True, True),
-     (8, False, True, True), (4, False, True, False), (4, True, True, True), (4, True, False, False)],
+    "predict,wrong,native,speculate,host_poll",
+    [(0, False, False, False, False), (4, False, False, False, False), (0, False, True, True, True),
+     (4, False, True, True, True), (8, False, True, True, True), (4, False, True, False, True),
+     (4, True, True, True, True), (4, True, False, False, False), (4, False, True, True, False)],
     ids=["py_off", "py_p4", "native_spec_off", "native_spec_p4", "native_spec_p8", "native_p4",
-         "native_spec_p4_wrong_predictor", "py_p4_wrong_predictor"])
-def test_readahead_paged_decode(predict, wrong, native, speculate):
+         "native_spec_p4_wrong_predictor", "py_p4_wrong_predictor", "native_spec_p4_event"])
+def test_readahead_paged_decode(predict, wrong, native, speculate, host_poll):
     """PagedDecode through 4 layers with 8-slot arenas, routed by per-layer router GEMVs on a
     residual stream, reading ahead the next layer's top-P (from its router or from an unrelated
-    matrix), sequenced in Python or by moe_paged_layer (with or without the speculative FFN):
+    matrix), sequenced in Python or by moe_paged_layer (with or without the speculative FFN; the
+    ids reach the host through the polled word, or through a copy and an event):
     every layer's output bitwise equal to the fully-resident run, ids equal to the oracle's
     selection on its own GEMV logits, the last token within the oracle's bar, and each arena's
     stats equal to the slot-policy model replayed on the logged calls."""
@@ -886,7 +888,7 @@ def test_readahead_paged_decode(predict, wrong, native, speculate):
         shared.append(torch.from_numpy(harness.pack_expert(w.seed, l, gen.SHARED_EXPERT, w.H, w.I)).to(DEV))
         resident.append((host.to(DEV), torch.arange(w.E, dtype=torch.int32, device=DEV)))
     dec = paged.PagedDecode(layers, routers, stride, w.H, w.I, w.E, w.K, shared=shared, predict=predict,
-                            device=DEV, predictors=preds, native=native, speculate=speculate)
+                            device=DEV, predictors=preds, native=native, speculate=speculate, host_poll=host_poll)
     dec.log = []
     y = torch.empty(1, w.H, dtype=torch.bfloat16, device=DEV)
     y_res = torch.empty_like(y)
@@ -970,7 +972,7 @@ def test_paged_layer_argument_errors():
     assert call(K_=S + 1) == lib.MOE_EINVAL
     assert call(P=S + 1) == lib.MOE_EINVAL
     assert call(nbytes=nb - 1) == lib.MOE_EWS
-    assert call(flags=2) == lib.MOE_EINVAL
+    assert call(flags=4) == lib.MOE_EINVAL
     torch.cuda.synchronize()
     assert a0.stats()["fills"] == 0 and a1.stats()["fills"] == 0 and int(st.item()) == 0
 

@@ -181,3 +181,27 @@ def test_batched_reports_scale_past_fp16_product_range():
     torch.cuda.synchronize()
     assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
     assert int(run.status.item()) == lib.MOE_EUNSUP
+
+
+def test_grouped_reports_term_past_fp16_store():
+    """The grouped path stores each routed term o in fp16; a term past the fp16 range
+    must set MOE_EUNSUP. Every down scale of one routed expert is set to 8000 (below the
+    operand guard of 8192): with I = 512 codes of magnitude up to 8 against h of order
+    one, that expert's o is far past 65504."""
+    T = 40
+    w = gen.Workload("status_grouped_o", T, 256, 8, 2, 512, 1, 8, "normal", 305)
+    logits = gen.normal_logits(w.seed, 0, T, w.E)
+    ids_ref, _ = R.route(logits, w.K)
+    L = harness.make_layer(w, 0, DEV, logits=logits)
+    e = int(ids_ref[0, 0])
+    slot = int(L.table[e].item())
+    mat_scales = w.H * w.I // 32 * 2
+    down_scales = 3 * w.H * w.I // 2 + 2 * mat_scales  # codes of the three matrices, then gate and up scales
+    off = slot * L.stride + down_scales
+    L.slots[off:off + mat_scales] = torch.tensor([0xD0, 0x6F], dtype=torch.uint8, device=DEV).repeat(mat_scales // 2)
+    say("grouped o past fp16")
+    run = harness.LayerRunner(w, DEV)
+    run(L)
+    torch.cuda.synchronize()
+    assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
+    assert int(run.status.item()) == lib.MOE_EUNSUP
