@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--readahead", default="2,3,4,6", help="experts read ahead per layer in the read-ahead leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=3, help="decode layers in the oracle's timed sample")
+    p.add_argument("--cpu-matrix", action="store_true",
+                   help="also time the oracle on every workload at 1 thread and at all cores (about a minute)")
     p.add_argument("--graph", type=int, default=1, help="replay the decode layer stack as a HIP graph")
     p.add_argument("--onepass", type=int, default=1,
                    help="decode headline with one-pass routing fused into the gate/up dispatch (MOE_ROUTE_ONEPASS); "
@@ -856,6 +858,64 @@ def cpu_baseline(w, n_layers):
     }
 
 
+def cpu_matrix():
+    """The oracle on a bounded sample of each workload, at one thread and at all cores
+    (NumPy's BLAS pool; the oracle's own loops are single-threaded Python). Expert
+    tensors are generated outside the timed region; each used expert is dequantised
+    (fp64) once inside it, on first use. Rates are scaled from the sample to the
+    workload's unit: tokens/s of the layer stack (decode, paged) or of one layer."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import moe_ref as R
+    from synth import gen
+
+    all_cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+    def time_layer(w, layer, tokens, logits=None, with_router=False):
+        xb = gen.activations_bf16(w.seed, layer, w.T, w.H)[:tokens]
+        wr = gen.router_weight(w.seed, layer, w.E, w.H) if with_router else None
+        lg = None if logits is None else logits[:tokens]
+        ids = R.select_topk(R.router_logits(xb, wr) if with_router else lg, w.K)
+        tensors = {e: gen.expert_tensors(w.seed, layer, e, w.H, w.I) for e in set(ids.ravel().tolist())}
+        sh_t = gen.expert_tensors(w.seed, layer, gen.SHARED_EXPERT, w.H, w.I) if w.shared else None
+        t = time.perf_counter()
+        built = {}
+
+        def experts(e):
+            if e not in built:
+                built[e] = R.Expert(tensors[e], w.H, w.I)
+            return built[e]
+
+        shared = R.Expert(sh_t, w.H, w.I) if sh_t is not None else None
+        R.moe_layer(xb, experts, w.K, logits=lg, w_router=wr, shared=shared)
+        return time.perf_counter() - t
+
+    W = gen.WORKLOADS
+    cases = [  # (workload, sample, tokens per sample, scale: seconds of the sample -> tokens/s)
+        (W["tiny_t4_h256_e8_k2"], "the whole layer (4 tokens)", lambda w: time_layer(w, 0, 4, with_router=True),
+         lambda w, t: 4 / t),
+        (W["decode_t1_h4096_e256_k8_i1536_x48"], "1 of 48 layers (1 token), scaled to 48 layers",
+         lambda w: time_layer(w, 0, 1, with_router=True), lambda w, t: 1 / (t * w.layers)),
+        (W["batched_t16_h2048_e128_k8_i768_zipf"], "the whole layer (16 tokens)",
+         lambda w: time_layer(w, 0, 16, logits=gen.zipf_logits(w.seed, 0, w.T, w.E)), lambda w, t: 16 / t),
+        (W["prefill_t9940_h4096_e256_k8_i1536"], "4 of the 9,940 tokens, scaled to tokens/s",
+         lambda w: time_layer(w, 0, 4, logits=gen.normal_logits(w.seed, 0, 4, w.E)), lambda w, t: 4 / t),
+        (W["paged_t1_h4096_e256s1_k6_i2048_x43"], "1 of 43 layers (1 token, 6 routed + 1 shared), scaled to 43 layers",
+         lambda w: time_layer(w, 0, 1, logits=gen.locality_logits(w.seed, 1, 1, w.E, w.K)[0]),
+         lambda w, t: 1 / (t * w.layers)),
+    ]
+    out = []
+    for w, sample, run, scale in cases:
+        row = {"workload": w.name, "unit": "tokens/s", "sample": sample}
+        for label, n in (("1_thread", 1), ("all_cores", all_cores)):
+            with threadpool_limits(n):
+                row[label] = round(scale(w, run(w)), 6)
+        row["all_cores_threads"] = all_cores
+        log(f"  oracle {w.name}: {row['1_thread']} / {row['all_cores']} tokens/s")
+        out.append(row)
+    return out
+
+
 def hbm_read_probe(dev, gib=2, reps=5):
     """GB/s of a plain streaming read: torch's sum over a 2 GiB int64 tensor (best of 5; the
     integer sum keeps up with HBM where torch's fp32 reductions do not)."""
@@ -1026,6 +1086,8 @@ def main():
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, min(a.cpu_layers, w.layers))
+        if a.cpu_matrix:
+            out["cpu_baseline"]["by_workload"] = cpu_matrix()
     print(json.dumps(out), flush=True)
 
 
