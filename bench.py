@@ -360,7 +360,8 @@ def batched_leg(a, dev, n_sets=16):
 
 def route_variants_leg(dev, reps=48):
     """moe_route / moe_route_scored from logits (E = 256, K = 8): the time per call of each
-    scoring function, for one decode token and for the 9,940-token prompt."""
+    scoring function (and of the bitonic selection), for one decode token and for the
+    9,940-token prompt."""
     import numpy as np
     import torch
 
@@ -377,6 +378,8 @@ def route_variants_leg(dev, reps=48):
         wts = torch.empty(T, K, dtype=torch.float32, device=dev)
         variants = {
             "softmax": lambda l: lib.moe_route(None, None, l, T, 0, E, K, 0, ids, wts, stream),
+            "softmax_bitonic_select": lambda l: lib.moe_route(None, None, l, T, 0, E, K, lib.MOE_ROUTE_BITONIC, ids,
+                                                              wts, stream),
             "sigmoid_bias_renorm_scale2.5": lambda l: lib.moe_route_scored(
                 None, None, l, T, 0, E, K, lib.MOE_SCORE_SIGMOID, bias, 2.5, lib.MOE_ROUTE_RENORM, ids, wts, stream),
             "sqrtsoftplus_bias_renorm": lambda l: lib.moe_route_scored(

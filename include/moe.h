@@ -77,6 +77,7 @@ enum moe_format {
 enum moe_flags {
   MOE_ROUTE_RENORM = 1u << 0,  /* moe_route: divide the K selected weights by their sum */
   MOE_ROUTE_ONEPASS = 1u << 1, /* moe_layer (route_flags): one-pass routing fused with the gate/up dispatch */
+  MOE_ROUTE_BITONIC = 1u << 2, /* moe_route: top-k by a wave-wide bitonic sort of all keys (same results) */
   MOE_FORCE_GEMV = 1u << 8,    /* moe_expert_ffn: use the per-expert GEMV path whatever T is */
   MOE_FORCE_GROUPED = 1u << 9, /* moe_expert_ffn: use the expert-grouped MFMA GEMM path */
   MOE_FFN_PARTIAL = 1u << 10,  /* moe_expert_ffn: one pass of a chunked paged run (see moe_ffn_combine) */
@@ -124,6 +125,10 @@ int moe_pack_expert(const uint8_t* qg, const uint8_t* qu, const uint8_t* qd, con
  *            Logits must be finite.
  *   w        device fp32 [T][K], out: w[t][k] = softmax(logits[t][:])[ids[t][k]]
  *            over all E experts; with MOE_ROUTE_RENORM divided by sum_k w[t][k].
+ *   flags    MOE_ROUTE_RENORM; MOE_ROUTE_BITONIC selects the K by a wave-wide
+ *            bitonic sort of all (logit, id) keys instead of the default K
+ *            rounds of a wave-wide maximum over per-lane sorted keys (the
+ *            keys are distinct, so ids and w are the same bits either way).
  * Deterministic: the same inputs give the same bits on every run. */
 int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K,
               unsigned flags, int32_t* ids, float* w, moe_stream_t stream);

@@ -49,7 +49,7 @@ extern "C" int moe_version(void) { return 100; }
 extern "C" int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K,
                          unsigned flags, int32_t* ids, float* w, moe_stream_t stream) {
   if (T < 0 || E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return MOE_EINVAL;
-  if (flags & ~(unsigned)MOE_ROUTE_RENORM) return MOE_EINVAL;
+  if (flags & ~(unsigned)(MOE_ROUTE_RENORM | MOE_ROUTE_BITONIC)) return MOE_EINVAL;
   if (E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
   if (w_router) {
     if (!x || H <= 0) return MOE_EINVAL;

@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(256) route_onepass_kernel(const uint16_t* __re
 // in LDS while the logits load, and lane k also writes slots_out[k] =
 // slot_table[ids[k]], so the single-token FFN kernels find their blobs with one
 // load instead of two.
-template <int EPL>
+template <int EPL, bool BITONIC>
 __global__ void __launch_bounds__(64) route_select_kernel(const float* __restrict__ logits, int T, int E, int K,
                                                           unsigned flags, float scale, int32_t* __restrict__ ids,
                                                           float* __restrict__ w,
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(64) route_select_kernel(const float* __restric
   }
   int32_t id;
   float wt;
-  wave_select<EPL>(logits + (size_t)t * E, E, K, flags, lane, id, wt);
+  wave_select<EPL, BITONIC>(logits + (size_t)t * E, E, K, flags, lane, id, wt);
   if (lane < K) {
     ids[(size_t)t * K + lane] = id;
     w[(size_t)t * K + lane] = wt * scale;
@@ -258,9 +258,12 @@ hipError_t launch_route_select(const float* logits, int T, int E, int K, unsigne
   dim3 grid(T);
 #define SEL(N)                                                                                                    \
   do {                                                                                                            \
-    if (score == MOE_SCORE_SOFTMAX)                                                                               \
-      hipLaunchKernelGGL(route_select_kernel<N>, grid, dim3(64), 0, s, logits, T, E, K, flags, scale, ids, w,     \
-                         slot_table, slots_out);                                                                  \
+    if (score == MOE_SCORE_SOFTMAX && (flags & MOE_ROUTE_BITONIC))                                                \
+      hipLaunchKernelGGL((route_select_kernel<N, true>), grid, dim3(64), 0, s, logits, T, E, K, flags, scale, ids, \
+                         w, slot_table, slots_out);                                                               \
+    else if (score == MOE_SCORE_SOFTMAX)                                                                          \
+      hipLaunchKernelGGL((route_select_kernel<N, false>), grid, dim3(64), 0, s, logits, T, E, K, flags, scale, ids, \
+                         w, slot_table, slots_out);                                                               \
     else                                                                                                          \
       hipLaunchKernelGGL(route_scored_kernel<N>, grid, dim3(64), 0, s, logits, T, E, K, flags, score, bias, scale, \
                          ids, w);                                                                                 \

@@ -164,12 +164,54 @@ __device__ inline uint64_t wave_topk(uint64_t (&key)[EPL], int K, int lane) {
   return mine;
 }
 
+// The same contract as wave_topk by a wave-wide bitonic sort of all 64 * EPL keys
+// (EPL a power of two), descending: element i is key[i / 64] of lane i % 64, so
+// rank k ends in key[0] of lane k. A compare-exchange at distance j < 64 pairs
+// lanes (shuffle), at j >= 64 registers of one lane. The keys are distinct, so
+// the order, and the K selected, equal wave_topk's.
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int EPL>
+__device__ inline uint64_t wave_topk_bitonic(uint64_t (&key)[EPL], int K, int lane) {
+  constexpr int N = 64 * EPL;
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      if (j < 64) {
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+          const bool desc = ((r * 64 + lane) & size) == 0;  // block sorted descending
+          const uint64_t a = key[r], b = shfl_xor_u64(a, j);
+          const bool take_max = ((lane & j) == 0) == desc;
+          key[r] = take_max ? (a > b ? a : b) : (a > b ? b : a);
+        }
+      } else {
+        const int jr = j / 64;
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+          if ((r & jr) == 0) {
+            const bool desc = ((r * 64) & size) == 0;
+            const uint64_t a = key[r], b = key[r | jr];
+            const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+            key[r] = desc ? hi : lo;
+            key[r | jr] = desc ? lo : hi;
+          }
+        }
+      }
+    }
+  }
+  return lane < K ? key[0] : 0ull;
+}
+
 // Softmax + top-k of one token's logits: lane k < K gets the expert of rank k
 // and its weight (the softmax probability over all E, with MOE_ROUTE_RENORM
 // divided by the sum over the K selected).
 // Softmax + top-k of one token's logits held in registers: lane l holds lg[i] =
 // logit of expert l + 64 i (entries past E ignored).
-template <int EPL>
+template <int EPL, bool BITONIC = false>
 __device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsigned flags, int lane, int32_t& id,
                                           float& wt) {
   uint64_t key[EPL];
@@ -179,7 +221,7 @@ __device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsign
     if (e >= E) lg[i] = 0.0f;
     key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
   }
-  const uint64_t mine = wave_topk<EPL>(key, K, lane);
+  const uint64_t mine = BITONIC ? wave_topk_bitonic<EPL>(key, K, lane) : wave_topk<EPL>(key, K, lane);
   const uint32_t top_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mine >> 32));
   const uint32_t top_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mine);
   const float m = key_logit(((uint64_t)top_hi << 32) | top_lo);  // the largest logit (rank 0, lane 0)
@@ -195,7 +237,7 @@ __device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsign
   wt = w;
 }
 
-template <int EPL>
+template <int EPL, bool BITONIC = false>
 __device__ inline void wave_select(const float* __restrict__ l, int E, int K, unsigned flags, int lane, int32_t& id,
                                    float& wt) {
   float lg[EPL];
@@ -206,7 +248,7 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
     const int e = lane + 64 * i;
     lg[i] = l[e < E ? e : E - 1];
   }
-  wave_select_values<EPL>(lg, E, K, flags, lane, id, wt);
+  wave_select_values<EPL, BITONIC>(lg, E, K, flags, lane, id, wt);
 }
 
 // ------------------------------------------------------------------ router GEMV of one token

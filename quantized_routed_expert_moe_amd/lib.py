@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOSLOT, MOE_ENOTRES, MOE_EHIP, MOE_EUNSUP, MOE_EWS = 0, -1, -2, -3, -4, -5, -6
 MOE_ROUTE_RENORM = 1 << 0
 MOE_ROUTE_ONEPASS = 1 << 1
+MOE_ROUTE_BITONIC = 4
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS = 0, 1, 2
 MOE_FORCE_GEMV = 1 << 8
 MOE_FORCE_GROUPED = 1 << 9

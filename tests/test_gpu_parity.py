@@ -144,6 +144,34 @@ def test_route_scored_softmax_scale_and_argument_errors():
         assert ei.value.status == lib.MOE_EINVAL
 
 
+@pytest.mark.parametrize("E,K", [(8, 2), (70, 9), (128, 8), (256, 8), (256, 32), (1000, 32), (1024, 1)])
+def test_route_bitonic_selection_equals_default(E, K):
+    """MOE_ROUTE_BITONIC (a wave-wide bitonic sort of every key) selects the same ids with
+    the same weights, bit for bit, as the default selection, and both equal the oracle's ids;
+    the logits include ties and signed zeros."""
+    T = 33
+    rng = np.random.default_rng(E * 100 + K)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[1] = 0.0
+    lg[2] = -0.0
+    lg[3, ::3] = 1.5  # many equal logits
+    lg[4] = np.round(lg[4] * 2) / 2  # coarse values: ties across the top
+    d = torch.from_numpy(lg).to(DEV)
+    out = {}
+    for name, flags in (("default", 0), ("bitonic", lib.MOE_ROUTE_BITONIC), ("bitonic_renorm",
+                                                                           lib.MOE_ROUTE_BITONIC | lib.MOE_ROUTE_RENORM),
+                        ("renorm", lib.MOE_ROUTE_RENORM)):
+        ids = torch.empty(T, K, dtype=torch.int32, device=DEV)
+        wts = torch.empty(T, K, dtype=torch.float32, device=DEV)
+        lib.moe_route(None, None, d, T, 0, E, K, flags, ids, wts)
+        torch.cuda.synchronize()
+        out[name] = (ids.cpu().numpy(), wts.cpu().numpy().view(np.int32))
+    ids_ref, _ = R.route(lg, K)
+    assert np.array_equal(out["default"][0], ids_ref)
+    for a, b in (("default", "bitonic"), ("renorm", "bitonic_renorm")):
+        assert np.array_equal(out[a][0], out[b][0]) and np.array_equal(out[a][1], out[b][1]), (a, b)
+
+
 def test_route_ties_and_signed_zero():
     E, K = 70, 9
     rows = [np.zeros(E), -np.zeros(E), np.where(np.arange(E) % 3 == 0, 1.0, -0.0), np.full(E, -2.5),
