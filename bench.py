@@ -770,7 +770,9 @@ def formats_leg(dev, steps=192, n_blobs=64):
     int4 group 32 and int4 group 128 (the single-token path of moe_expert_ffn), int8
     group 32 and NVFP4 (moe_expert_ffn_fmt). 64 distinct experts are packed per format (the
     table maps expert e to blob e % 64, more bytes than the 256 MB last-level cache);
-    every timed call routes to 8 other experts (seeded draws without replacement)."""
+    every timed call routes to 8 other experts (seeded draws without replacement). Also a
+    prompt of 2,048 tokens over the 64 packed experts (top-8 of seeded N(0,1) logits): the
+    int4 grouped GEMM and the int8 / NVFP4 prompt GEMMs, ms per layer and useful TFLOP/s."""
     import numpy as np
     import torch
 
@@ -815,6 +817,37 @@ def formats_leg(dev, steps=192, n_blobs=64):
         out[name] = {"us_per_layer": round(us, 2), "blob_bytes": blob,
                      "hbm_gbs": round(K * blob / (us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(K * blob / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if name != "int4_g128":  # a prompt: 2,048 tokens routed over the 64 packed experts
+            Tp, Ep = 2048, n_blobs
+            lg = torch.from_numpy(gen.normal_logits(seed, 1, Tp, Ep)).to(dev)
+            ids_p = torch.empty(Tp, K, dtype=torch.int32, device=dev)
+            wts_p = torch.empty(Tp, K, dtype=torch.float32, device=dev)
+            lib.moe_route(None, None, lg, Tp, H, Ep, K, 0, ids_p, wts_p)
+            xp = harness.bf16_tensor(gen.activations_bf16(seed, 1, Tp, H), dev)
+            yp = torch.empty(Tp, H, dtype=torch.bfloat16, device=dev)
+            tbl_p = torch.arange(Ep, dtype=torch.int32, device=dev)
+            nbp = lib.moe_fmt_workspace_bytes(fmt, Tp, H, I, Ep, K, 0)
+            wsp = torch.empty(nbp, dtype=torch.uint8, device=dev)
+
+            def prompt():
+                lib.moe_expert_ffn_fmt(fmt, xp, ids_p, wts_p, Tp, H, I, Ep, K, tbl_p, slots, stride, None, yp, wsp,
+                                       nbp, status)
+
+            prompt()
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record()
+            for _ in range(5):
+                prompt()
+            e1.record()
+            torch.cuda.synchronize()
+            if int(status.item()) != 0:
+                raise RuntimeError(f"device status {int(status.item())}")
+            ms = e0.elapsed_time(e1) / 5
+            flops = 2.0 * Tp * K * 3 * H * I
+            out[name]["prompt_t2048_e64_ms"] = round(ms, 3)
+            out[name]["prompt_t2048_e64_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            del wsp, yp, xp
         log(f"  formats {name}: {out[name]}")
         del slots, ws
         torch.cuda.empty_cache()

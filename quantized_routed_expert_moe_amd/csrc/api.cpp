@@ -306,7 +306,12 @@ extern "C" size_t moe_fmt_workspace_bytes(int fmt, int T, int H, int I, int E, i
     if (fmt == MOE_FMT_INT4_G128 && moe_fmt_blob_bytes(fmt, H, I) == 0) return 0;
     return moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, 0);
   }
-  if (T <= 0 || T > moe::kGemvMaxT || E <= 0 || K <= 0 || !moe::fmt_shape_ok(fmt, H, I)) return 0;
+  if (T <= 0 || E <= 0 || K <= 0 || E > moe::kMaxE) return 0;
+  if (T > moe::kGemvMaxT) {  // the grouped MFMA path
+    if (fmt != MOE_FMT_INT8_G32 && fmt != MOE_FMT_NVFP4) return 0;
+    return moe::grouped_fmt_workspace_bytes(T, H, I, E, K, has_shared);
+  }
+  if (!moe::fmt_shape_ok(fmt, H, I)) return 0;
   return moe::fmt_workspace_bytes(T, H, I, K, has_shared);
 }
 
@@ -320,7 +325,9 @@ extern "C" int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids
                           ws_bytes, dev_status, 0, stream);
   if (fmt != MOE_FMT_INT8_G32 && fmt != MOE_FMT_NVFP4) return MOE_EINVAL;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
-  if (!moe::fmt_shape_ok(fmt, H, I) || E > moe::kMaxE || K > moe::kMaxK || T > moe::kGemvMaxT) return MOE_EUNSUP;
+  const bool grouped = T > moe::kGemvMaxT;
+  if (E > moe::kMaxE || K > moe::kMaxK) return MOE_EUNSUP;
+  if (grouped ? !moe::grouped_fmt_shape_ok(H, I) : !moe::fmt_shape_ok(fmt, H, I)) return MOE_EUNSUP;
   if (T == 0) return MOE_OK;
   if (!x || !ids || !w || !slot_table || !slots || !y || !dev_status) return MOE_EINVAL;
   if (stride < moe_fmt_blob_bytes(fmt, H, I) || stride % 256) return MOE_EINVAL;
@@ -344,7 +351,8 @@ extern "C" int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids
   a.ws = static_cast<uint8_t*>(ws);
   a.ws_bytes = ws_bytes;
   a.status = dev_status;
-  const hipError_t err = moe::launch_ffn_fmt(fmt, a, static_cast<hipStream_t>(stream));
+  const hipError_t err = grouped ? moe::launch_ffn_grouped_fmt(fmt, a, static_cast<hipStream_t>(stream))
+                                  : moe::launch_ffn_fmt(fmt, a, static_cast<hipStream_t>(stream));
   if (err == hipErrorNotSupported) return MOE_EUNSUP;
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -277,36 +277,24 @@ __device__ inline float f16_hi_f(uint32_t v) { return (float)__builtin_bit_cast(
 // L2.
 constexpr int kTM = 128, kTN = 256, kTK = 64;
 
-template <int MODE>
-__host__ __device__ inline int gemm_n_tiles(int H, int I) {
-  return MODE == 0 ? (I + 127) / 128 : (H + kTN - 1) / kTN;
-}
-
-// One stage of operands in LDS (25,600 bytes).
-struct __align__(16) GemmStage {
-  _Float16 a[kTM * kTK];   // row r, chunk c (8 k) at r * 64 + 8 (c ^ (r & 7))
-  uint32_t bc[2 * kTN * 4];  // group g, column c: code dwords at (g * 256 + c) * 4 .. +3
-  uint16_t bs[2 * kTN];      // group g, column c: fp16 scale bits at g * 256 + c
+// Tile of this workgroup: the tiles, (unit, N-tile, M-tile) in order, are cut into
+// 8 contiguous ranges, one per XCD (blocks go to XCDs round-robin by block id), so
+// the M-tiles of one unit that share a weight N-tile run back to back in one L2.
+// False for a block past the plan's tiles.
+struct GemmTile {
+  TileDesc td;
+  const uint8_t* blob;
+  int nt;
 };
-constexpr int kStageLoads = 7;  // global_load_lds per lane and stage: 4 A, 2 codes, 1 scale pair
-
-template <int MODE>
-__global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
-  // three stage buffers (separate objects, so that a stage can name the one it
-  // reads and the one it fills)
-  __shared__ GemmStage S0, S1, S2;
-  const int H = a.H, I = a.I, T = a.T, K = a.K;
-  const bool has_shared = a.shared_blob != nullptr;
-  const GroupedWs W = grouped_ws(T, H, I, a.E, K, has_shared);
-  const int n_nt = gemm_n_tiles<MODE>(H, I);
+__device__ inline bool grouped_tile(const FfnArgs& a, const GroupedWs& W, int n_nt, GemmTile& g) {
   const int* cnts = reinterpret_cast<const int*>(a.ws + W.n_mt);
   const int n_mt = cnts[0], n_units = cnts[1];
   const int N = n_mt * n_nt;
   const int chunk = (N + 7) / 8;
   const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
-  if (jx >= chunk) return;
+  if (jx >= chunk) return false;
   const int t = xcd * chunk + jx;
-  if (t >= N) return;
+  if (t >= N) return false;
   const int32_t* unit_mt0 = reinterpret_cast<const int32_t*>(a.ws + W.unit_mt0);
   int lo = 0, hi = n_units - 1;  // last unit whose first tile index <= t
   while (lo < hi) {
@@ -318,9 +306,38 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   }
   const int m_first = unit_mt0[lo], m_cnt = unit_mt0[lo + 1] - m_first;
   const int rr = t - m_first * n_nt;
-  const int nt = rr / m_cnt, mt = m_first + rr % m_cnt;
-  const TileDesc td = reinterpret_cast<const TileDesc*>(a.ws + W.tiles)[mt];
-  const uint8_t* blob = reinterpret_cast<const uint8_t* const*>(a.ws + W.ublob)[td.unit];
+  g.nt = rr / m_cnt;
+  g.td = reinterpret_cast<const TileDesc*>(a.ws + W.tiles)[m_first + rr % m_cnt];
+  g.blob = reinterpret_cast<const uint8_t* const*>(a.ws + W.ublob)[g.td.unit];
+  return true;
+}
+
+template <int MODE>
+__host__ __device__ inline int gemm_n_tiles(int H, int I) {
+  return MODE == 0 ? (I + 127) / 128 : (H + kTN - 1) / kTN;
+}
+
+// One stage of operands in LDS (25,600 bytes).
+struct __align__(16) GemmStage {
+  _Float16 a[kTM * kTK];   // row r, chunk c (8 k) at r * 64 + 8 (c ^ (r & 7))
+  uint32_t bc[2 * kTN * 4];  // group g, column c: code dwords at (g * 256 + c) * 4 .. +3
+  uint16_t bs[2 * kTN];      // group g, column c: fp16 scale bits at g * 256 + c
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
+  // three stage buffers (separate objects, so that a stage can name the one it
+  // reads and the one it fills)
+  __shared__ GemmStage S0, S1, S2;
+  const int H = a.H, I = a.I, T = a.T, K = a.K;
+  const bool has_shared = a.shared_blob != nullptr;
+  const GroupedWs W = grouped_ws(T, H, I, a.E, K, has_shared);
+  const int n_nt = gemm_n_tiles<MODE>(H, I);
+  GemmTile gt;
+  if (!grouped_tile(a, W, n_nt, gt)) return;
+  const TileDesc td = gt.td;
+  const uint8_t* blob = gt.blob;
+  const int nt = gt.nt;
   const int32_t* sorted = reinterpret_cast<const int32_t*>(a.ws + W.sorted);
   const int P = T * K;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -389,7 +406,7 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   }
   const __amdgpu_buffer_rsrc_t b_rs = buf_rsrc(b_base, (uint32_t)BL.bytes);
   const uint32_t scale_mask = blob ? 0xFFFFu : 0u;  // a unit without a blob contributes zeros
-  // all operands of stage st into the stage buffer Sb (kStageLoads loads per lane)
+  // all operands of stage st into the stage buffer Sb (7 loads per lane: 4 A, 2 codes, 1 scale pair)
   auto issue = [&](int st, GemmStage* Sb) {
     const uint32_t sa = (uint32_t)st * (kTK * 2);
     ld16_lds(a_rs, ao0, sa, Sb->a + (0 * 4 + wave) * 512);
@@ -591,6 +608,231 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ INT8 / NVFP4 GEMM
+// The prompt path of the INT8 group-32 and NVFP4 experts ("Strata" README, the
+// models table: INT8 group-32 linears; NVFP4 experts, E2M1 pairs, group-16 E4M3
+// scales, an FP32 per-tensor global scale), on the same plan, fp16 x, fp16 o and
+// combine as the int4 GEMM. Blob: fmt_layout (rows of codes, row-major, then the
+// scales [rows][cols / g], then for NVFP4 the three global scales).
+//
+// Tile: 128 pair rows x 64 weight rows (MODE 0: rows of I in gate and in up;
+// MODE 1: rows of H), K in stages of 64 columns. Wave w owns weight rows 16w ..
+// 16w + 15 of the tile for all pair rows. The A rows (x or h, fp16) reach LDS by
+// buffer-to-LDS loads, two stages deep, 16-byte chunks XOR-swizzled by row as in
+// the int4 GEMM. Lane (n = lane % 16, q = lane / 16) streams columns 16q .. 16q
+// + 15 of the stage of its weight row with one buffer load per matrix (int8: 16
+// bytes, NVFP4: 8 bytes), one stage ahead; MFMA s (s = 0, 1) of a stage takes
+// columns 16q + 8s .. +7 in quarter q, and the A fragment the same columns. B =
+// int8: fp16(q * s) with one rounding: the codes (offset binary u = q + 128)
+// become fp16 1024 + u by v_perm_b32 under a 0x64 byte, minus 1152, times the
+// fp16 group scale; a scale of magnitude >= 512, whose product with a code could
+// leave fp16, sets MOE_EUNSUP. NVFP4: e2m1 * e4m3 exactly (v_cvt_scalef32_pk_f16_fp4
+// gives the code's exact fp16, the product of a 2-bit and a 4-bit significand is
+// exact in fp16 and at most 6 * 448), the per-tensor global scale applied to the
+// fp32 sums. Each 16-column run lies inside one scale group (int8: group
+// (stage * 64 + 16q) / 32; NVFP4: stage * 4 + q).
+constexpr int kFM = 128, kFN = 64, kFK = 64;
+
+template <int FMT>
+__device__ inline f16x8 fmt_dequant(uint32_t w0, uint32_t w1, _Float16 sc) {
+  const f16x2 s2 = {sc, sc};
+  uint32_t b[4];
+  if constexpr (FMT == MOE_FMT_INT8_G32) {
+    const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    // bytes [u0, 0x64, u1, 0x64] and [u2, 0x64, u3, 0x64] of each dword
+    const uint32_t m0 = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
+    const uint32_t m1 = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);
+    const uint32_t m2 = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);
+    const uint32_t m3 = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
+    b[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m0) + off) * s2);
+    b[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m1) + off) * s2);
+    b[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m2) + off) * s2);
+    b[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, m3) + off) * s2);
+  } else {
+    // w0: 8 E2M1 codes, byte i = columns 2i (low nibble), 2i + 1
+    b[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * s2);
+    b[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * s2);
+    b[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) * s2);
+    b[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) * s2);
+    (void)w1;
+  }
+  return __builtin_bit_cast(f16x8, make_uint4(b[0], b[1], b[2], b[3]));
+}
+
+template <int FMT, int MODE>
+__global__ void __launch_bounds__(kGThreads, 2) fmt_gemm_kernel(FfnArgs a) {
+  __shared__ __align__(16) _Float16 As[2][kFM * kFK];
+  constexpr bool kI8 = FMT == MOE_FMT_INT8_G32;
+  constexpr int NM = MODE == 0 ? 2 : 1;  // matrices per tile
+  const int H = a.H, I = a.I, T = a.T, K = a.K;
+  const bool has_shared = a.shared_blob != nullptr;
+  const GroupedWs W = grouped_ws(T, H, I, a.E, K, has_shared);
+  GemmTile gt;
+  if (!grouped_tile(a, W, MODE == 0 ? I / kFN : H / kFN, gt)) return;
+  const TileDesc td = gt.td;
+  const uint8_t* blob = gt.blob;
+  const int32_t* sorted = reinterpret_cast<const int32_t*>(a.ws + W.sorted);
+  const int P = T * K;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q = lane >> 4;
+  const int Kd = MODE == 0 ? H : I;  // reduced dimension
+  const int n_st = Kd / kFK;
+  const int NB = td.rows <= 64 ? 4 : 8;  // 16-row blocks that hold pairs
+  // A: LDS chunk c = v * 256 + tid (v < 4) is row c / 8, position c % 8, which holds
+  // columns 8 ((c % 8) ^ (row % 8)) .. +7 of the stage; a padding row reads the
+  // tile's first row (its products are never stored)
+  auto a_off = [&](int v) -> uint32_t {
+    const int c = v * kGThreads + tid;
+    int row = c >> 3;
+    row = row < td.rows ? row : 0;
+    const int col8 = ((c & 7) ^ (row & 7)) * 8;
+    if (MODE == 0) {
+      const int p = sorted[td.row0 + row];
+      const int tok = p < P ? p / K : p - P;
+      return ((uint32_t)tok * (uint32_t)H + col8) * 2u;
+    }
+    return ((uint32_t)(td.row0 + row) * (uint32_t)I + col8) * 2u;
+  };
+  const __amdgpu_buffer_rsrc_t a_rs =
+      buf_rsrc(a.ws + (MODE == 0 ? W.xh : W.h), MODE == 0 ? (uint32_t)((size_t)T * H * 2) : (uint32_t)((W.o - W.h)));
+  const uint32_t ao0 = a_off(0), ao1 = a_off(1), ao2 = a_off(2), ao3 = a_off(3);
+  auto issue_a = [&](int st, int buf) {
+    const uint32_t sa = (uint32_t)st * (kFK * 2);
+    _Float16* d = As[buf];
+    ld16_lds(a_rs, ao0, sa, d + (0 * 4 + wave) * 512);
+    ld16_lds(a_rs, ao1, sa, d + (1 * 4 + wave) * 512);
+    ld16_lds(a_rs, ao2, sa, d + (2 * 4 + wave) * 512);
+    ld16_lds(a_rs, ao3, sa, d + (3 * 4 + wave) * 512);
+  };
+  // B: this lane's weight row and its byte offsets within the blob
+  const FmtLayout L = fmt_layout(FMT, H, I);
+  const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
+  const __amdgpu_buffer_rsrc_t b_rs = buf_rsrc(src, (uint32_t)L.bytes);
+  const int wr = gt.nt * kFN + wave * 16 + n;
+  const uint32_t row_codes = kI8 ? (uint32_t)Kd : (uint32_t)Kd / 2, row_scales = kI8 ? Kd / 32 * 2 : Kd / 16;
+  uint32_t co[NM], so[NM];
+  float glob[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const size_t cb = MODE == 1 ? L.down_codes : (m == 0 ? L.gate_codes : L.up_codes);
+    const size_t sb = MODE == 1 ? L.down_scales : (m == 0 ? L.gate_scales : L.up_scales);
+    co[m] = (uint32_t)(cb + (size_t)wr * row_codes) + (uint32_t)q * (kI8 ? 16u : 8u);
+    so[m] = (uint32_t)(sb + (size_t)wr * row_scales) + (kI8 ? (uint32_t)(q >> 1) * 2u : (uint32_t)q);
+    glob[m] = 1.0f;
+    if constexpr (!kI8) glob[m] = reinterpret_cast<const float*>(src + L.globals)[MODE == 1 ? 2 : m];
+  }
+  // per stage: codes advance 64 (int8) or 32 (NVFP4) bytes, scales 4 bytes
+  uint4 cw[2][NM];
+  uint32_t sw[2][NM];
+  auto issue_b = [&](int st, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;  // a constant index: the buffers stay in registers
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if constexpr (kI8) {
+        cw[buf][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, co[m], (uint32_t)st * 64u, 0));
+        sw[buf][m] = __builtin_amdgcn_raw_buffer_load_b16(b_rs, so[m], (uint32_t)st * 4u, 0);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(b_rs, co[m], (uint32_t)st * 32u, 0);
+        cw[buf][m] = make_uint4((uint32_t)v[0], (uint32_t)v[1], 0u, 0u);
+        sw[buf][m] = __builtin_amdgcn_raw_buffer_load_b8(b_rs, so[m], (uint32_t)st * 4u, 0);
+      }
+    }
+  };
+  f32x4 acc[NM][8];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[m][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+  auto scale_of = [&](uint32_t raw, int m) -> _Float16 {
+    float sf;
+    if constexpr (kI8) {
+      sf = (float)__builtin_bit_cast(_Float16, (uint16_t)raw);
+      if (blob && !(fabsf(sf) < 512.0f)) bad = true;
+    } else {
+      sf = __builtin_amdgcn_cvt_f32_fp8((int)raw, 0);  // exact in fp16 (E4M3 has 4 significant bits)
+    }
+    (void)m;
+    return blob ? (_Float16)sf : (_Float16)0.0f;
+  };
+  // A fragment of block i, MFMA s: row 16 i + n, columns 16 q + 8 s .. +7 of the stage
+  auto read_a = [&](int buf, int i, int s) {
+    const int row = i * 16 + n, c = 2 * q + s;
+    return *reinterpret_cast<const f16x8*>(&As[buf][row * kFK + ((c ^ (row & 7)) * 8)]);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  issue_a(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_b(0, B0{});
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  // stage st on buffer cur = st % 2 (stages in pairs, so the index is a constant)
+  auto stage = [&](int st, auto curc) {
+    constexpr int cur = decltype(curc)::value;
+    if (st + 1 < n_st) {
+      issue_a(st + 1, cur ^ 1);  // the other buffer: every wave finished reading it last stage
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(st + 1, std::integral_constant<int, cur ^ 1>{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const _Float16 sc = scale_of(sw[cur][m], m);
+      const f16x8 b0 = fmt_dequant<FMT>(cw[cur][m].x, cw[cur][m].y, sc);
+      const f16x8 b1 = kI8 ? fmt_dequant<FMT>(cw[cur][m].z, cw[cur][m].w, sc) : fmt_dequant<FMT>(cw[cur][m].y, 0u, sc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < NB) {
+          acc[m][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a(cur, i, 0), b0, acc[m][i], 0, 0, 0);
+          acc[m][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a(cur, i, 1), b1, acc[m][i], 0, 0, 0);
+        }
+      }
+    }
+    // the next stage's A rows have landed (issued before its B loads), and every
+    // wave is done with this stage's buffer
+    if (st + 1 < n_st) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NM));
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int st = 0; st < n_st; st += 2) {
+    stage(st, B0{});
+    if (st + 1 < n_st) stage(st + 1, B1{});
+  }
+  // epilogue: lane holds D[row = 4 (lane / 16) + v][col = lane % 16] of each 16 x 16 block
+  if (MODE == 0) {
+    uint16_t* hws = reinterpret_cast<uint16_t*>(a.ws + W.h);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i * 16 + 4 * q + v;
+        if (i < NB && row < td.rows) {
+          const float g = acc[0][i][v] * glob[0], u = acc[NM - 1][i][v] * glob[NM - 1];
+          const float hv = blob ? silu(g) * u : 0.0f;
+          if (!(fabsf(hv) < 65520.0f)) bad = true;  // h does not fit the fp16 operand
+          hws[(size_t)(td.row0 + row) * I + wr] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+        }
+      }
+    }
+  } else {
+    _Float16* ows = reinterpret_cast<_Float16*>(a.ws + W.o);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i * 16 + 4 * q + v;
+        if (i < NB && row < td.rows) {
+          const float ov = acc[0][i][v] * glob[0];
+          bad |= !(fabsf(ov) < 65520.0f);  // o does not fit its fp16 store
+          ows[(size_t)sorted[td.row0 + row] * H + wr] = (_Float16)ov;
+        }
+      }
+    }
+  }
+  if (bad) *a.status = MOE_EUNSUP;
+}
+
 // ------------------------------------------------------------------ combine
 // Thread: 8 consecutive columns of one token; the token's o rows (fp16, 16 bytes
 // each) are loaded eight at a time before the sums, which run in rank order.
@@ -691,6 +933,39 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(round8(W.max_mt * gemm_n_tiles<1>(a.H, a.I))), dim3(kGThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.mode & kModePartial) return hipSuccess;  // the caller combines after the last pass
+  return launch_grouped_combine(a, s);
+}
+
+bool grouped_fmt_shape_ok(int H, int I) { return H % kFN == 0 && I % kFN == 0; }  // K stages and N tiles of 64
+
+size_t grouped_fmt_workspace_bytes(int T, int H, int I, int E, int K, int has_shared) {
+  return grouped_fmt_shape_ok(H, I) ? grouped_workspace_bytes(T, H, I, E, K, has_shared) : 0;
+}
+
+hipError_t launch_ffn_grouped_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
+  if (!grouped_fmt_shape_ok(a.H, a.I) || (fmt != MOE_FMT_INT8_G32 && fmt != MOE_FMT_NVFP4))
+    return hipErrorNotSupported;
+  const bool has_shared = a.shared_blob != nullptr;
+  if (!grouped_offsets_fit(a.T, a.H, a.I, a.K, has_shared)) return hipErrorNotSupported;
+  const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
+  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  hipError_t e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t n2 = (size_t)a.T * a.H / 2;
+  const size_t cb = (n2 + 255) / 256;
+  hipLaunchKernelGGL(to_f16_kernel, dim3(cb < 4096 ? (int)cb : 4096), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int g0 = round8(W.max_mt * (a.I / kFN)), g1 = round8(W.max_mt * (a.H / kFN));
+  if (fmt == MOE_FMT_INT8_G32) {
+    hipLaunchKernelGGL((fmt_gemm_kernel<MOE_FMT_INT8_G32, 0>), dim3(g0), dim3(kGThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((fmt_gemm_kernel<MOE_FMT_INT8_G32, 1>), dim3(g1), dim3(kGThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fmt_gemm_kernel<MOE_FMT_NVFP4, 0>), dim3(g0), dim3(kGThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((fmt_gemm_kernel<MOE_FMT_NVFP4, 1>), dim3(g1), dim3(kGThreads), 0, s, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_grouped_combine(a, s);
 }
 

@@ -176,6 +176,11 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s);
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
 bool grouped_shape_ok(int H, int I);
 hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s);
+// INT8 group-32 / NVFP4 experts for prompts: the grouped plan, fp16 x, fp16 o and
+// combine with the format's MFMA GEMM (H and I multiples of 64)
+bool grouped_fmt_shape_ok(int H, int I);
+size_t grouped_fmt_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
+hipError_t launch_ffn_grouped_fmt(int fmt, const FfnArgs& a, hipStream_t s);
 
 hipError_t launch_table_update(int32_t* table, const int32_t* idx, const int32_t* val, int n, hipStream_t s);
 // one-thread status word kernel: src == nullptr clears *dst; otherwise a non-zero

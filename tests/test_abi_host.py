@@ -258,7 +258,10 @@ def test_fmt_sizes_and_rejections():
     assert lib.moe_fmt_blob_bytes(gen.FMT_INT4_G128, 4096, 1600) == 0  # I not a multiple of 128
     assert lib.moe_fmt_blob_bytes(gen.FMT_INT8_G32, 8192, 1536) == 0  # int8 rows past 4096 columns
     assert lib.moe_fmt_blob_bytes(7, 4096, 1536) == 0
-    assert lib.moe_fmt_workspace_bytes(gen.FMT_INT8_G32, 33, 4096, 1536, 256, 8, 1) == 0  # T > 32
+    # T > 32: the grouped (prompt) workspace, for H and I multiples of 64 only
+    assert lib.moe_fmt_workspace_bytes(gen.FMT_INT8_G32, 33, 4096, 1536, 256, 8, 1) == lib.moe_ffn_workspace_bytes(
+        33, 4096, 1536, 256, 8, 1, lib.MOE_FORCE_GROUPED)
+    assert lib.moe_fmt_workspace_bytes(gen.FMT_NVFP4, 33, 4096, 1504, 256, 8, 1) == 0
     z = np.zeros(16, np.uint8)
     with pytest.raises(lib.MoeError):
         lib.moe_pack_expert_fmt(7, z, z, z, z, z, z, 256, 96, z)

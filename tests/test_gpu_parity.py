@@ -735,13 +735,23 @@ def fmt_run(fmt, w, slots, table, shared, stride, xb, logits):
         (gen.FMT_NVFP4, gen.Workload("nvfp4_t7_h256_e8_k2_i96", 7, 256, 8, 2, 96, 1, 8, "normal", 82)),
         (gen.FMT_NVFP4, gen.Workload("nvfp4_t32_h2048_e32_k8_i768_shared", 32, 2048, 32, 8, 768, 1, 32, "zipf", 83,
                                      shared=True)),
+        # prompts (T > 32): the formats' grouped MFMA GEMMs
+        (gen.FMT_INT8_G32, gen.Workload("fmt8_t40_h512_e16_k4_i256_shared", 40, 512, 16, 4, 256, 1, 16, "normal", 84,
+                                        shared=True)),
+        (gen.FMT_INT8_G32, gen.Workload("fmt8_t300_h256_e4_k2_i128", 300, 256, 4, 2, 128, 1, 4, "normal", 85)),
+        (gen.FMT_NVFP4, gen.Workload("nvfp4_t77_h1024_e16_k4_i256_shared", 77, 1024, 16, 4, 256, 1, 16, "zipf", 86,
+                                     shared=True)),
+        (gen.FMT_NVFP4, gen.Workload("nvfp4_t300_h256_e4_k2_i192", 300, 256, 4, 2, 192, 1, 4, "normal", 89)),
     ],
     ids=lambda v: v.name if hasattr(v, "name") else f"fmt{v}",
 )
 def test_fmt_matches_oracle(fmt, w):
     """INT8 group-32, INT4 group-128 (on every path of moe_expert_ffn, 77 tokens on the
-    grouped one) and NVFP4 experts: ids bit-exact, y within the oracle's bar, the same bits
-    on a second run and under a permuted slot map."""
+    grouped one) and NVFP4 experts, one token to prompts of 300 (the formats' own grouped
+    MFMA GEMMs above 32 tokens, experts over two 128-row tiles, a full and a half one; the
+    seeds keep the oracle's bf16 rounding floor below the bar, so the plain bar holds): ids
+    bit-exact, y within the oracle's bar, the same bits on a second run and under a
+    permuted slot map."""
     say(f"format {fmt} {w.name}")
     xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
     logits = {"normal": gen.normal_logits, "zipf": gen.zipf_logits}[w.router](w.seed, 0, w.T, w.E)
@@ -851,9 +861,10 @@ def test_fmt_status_and_argument_errors():
         with pytest.raises(lib.MoeError) as ex:
             lib.moe_expert_ffn_fmt(bad_fmt, *args)
         assert ex.value.status == code
-    with pytest.raises(lib.MoeError) as ex:  # 33 tokens: past the format path's T <= 32
+    with pytest.raises(lib.MoeError) as ex:  # 33 tokens with I = 96: the prompt GEMM takes multiples of 64
         lib.moe_expert_ffn_fmt(fmt, x, ids, wts, 33, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb, st)
     assert ex.value.status == lib.MOE_EUNSUP
+    assert lib.moe_fmt_workspace_bytes(fmt, 33, w.H, w.I, w.E, w.K, True) == 0
     with pytest.raises(lib.MoeError) as ex:
         lib.moe_expert_ffn_fmt(fmt, x, ids, wts, w.T, w.H, w.I, w.E, w.K, table, slots, stride, shared, y, ws, nb - 1, st)
     assert ex.value.status == lib.MOE_EWS

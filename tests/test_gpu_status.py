@@ -205,3 +205,26 @@ def test_grouped_reports_term_past_fp16_store():
     torch.cuda.synchronize()
     assert np.array_equal(run.ids.cpu().numpy(), ids_ref)
     assert int(run.status.item()) == lib.MOE_EUNSUP
+
+
+def test_int8_prompt_reports_scale_past_fp16_product_range():
+    """The INT8 prompt GEMM forms fp16(q * s) as its MFMA operand (|q| <= 128); a group
+    scale of magnitude >= 512 could overflow that product and must set MOE_EUNSUP. One
+    gate scale of the expert every token picks first is set to 600 in the arena."""
+    from test_gpu_parity import fmt_layer, fmt_run
+
+    fmt = gen.FMT_INT8_G32
+    w = gen.Workload("status_int8_prompt_scale", 48, 256, 8, 2, 128, 1, 8, "normal", 306)
+    xb = gen.activations_bf16(w.seed, 0, w.T, w.H)
+    logits = gen.normal_logits(w.seed, 0, w.T, w.E)
+    ids_ref, _ = R.route(logits, w.K)
+    slots, table, shared, stride = fmt_layer(fmt, w)
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731  (regions of the format blob start on 256 bytes)
+    mat = w.I * w.H  # int8 codes of gate / up / down
+    gate_scales = al(al(al(mat) + mat) + mat)
+    off = int(table[int(ids_ref[0, 0])].item()) * stride + gate_scales
+    slots[off:off + 2] = torch.tensor([0xB0, 0x60], dtype=torch.uint8, device=DEV)  # fp16 600, little-endian
+    say("int8 prompt scale 600")
+    ids, _, _, st, _ = fmt_run(fmt, w, slots, table, shared, stride, xb, logits)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert int(st.item()) == lib.MOE_EUNSUP
