@@ -248,16 +248,22 @@ int moe_expert_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T,
  *                     moe_expert_ffn serves it (moe_expert_ffn_fmt calls it);
  *   MOE_FMT_INT8_G32  codes int8 [rows][cols] (two's complement, passed as
  *                     uint8), fp16 scales [rows][cols/32]; H, I multiples of 32
- *                     and at most 4096; T <= 32 (else MOE_EUNSUP, no fallback).
- *                     Each (token, expert) pair reads its expert's rows (one
- *                     read per chosen expert for one token); x, and the
- *                     intermediate h, must fit fp16 (else MOE_EUNSUP in
- *                     dev_status).
- *   MOE_FMT_NVFP4     ("Strata" README, Models: E2M1 pairs, group-16 E4M3
- *                     scales, FP32 per-tensor global scale): W[n][j] =
+ *                     and at most 4096. T <= 32: each (token, expert) pair reads
+ *                     its expert's rows (one read per chosen expert for one
+ *                     token), the scales applied in fp32. T > 32 (prompts): the
+ *                     grouped plan with the format's MFMA GEMM, H and I
+ *                     multiples of 64 (else MOE_EUNSUP, no fallback), operand
+ *                     fp16(q * s) rounded once, a scale of magnitude >= 512
+ *                     sets MOE_EUNSUP in dev_status. x, the intermediate h and,
+ *                     for T > 32, each routed term must fit fp16 (else
+ *                     MOE_EUNSUP in dev_status).
+ *   MOE_FMT_NVFP4     ("Strata" README, the models table: E2M1 pairs, group-16
+ *                     E4M3 scales, FP32 per-tensor global scale): W[n][j] =
  *                     e2m1(c[n][j]) * e4m3(s[n][j / 16]) * global; packed with
  *                     moe_pack_expert_nvfp4; H, I multiples of 32 and at most
- *                     8192; T <= 32; otherwise as MOE_FMT_INT8_G32.
+ *                     8192; for T > 32 the operand e2m1 * e4m3 is exact in fp16
+ *                     and the global scale applies to the fp32 sums; otherwise
+ *                     as MOE_FMT_INT8_G32.
  * The layout of these blobs belongs to the library. */
 size_t moe_fmt_blob_bytes(int fmt, int H, int I);  /* 0 on an unsupported format or shape */
 size_t moe_fmt_slot_stride(int fmt, int H, int I); /* moe_fmt_blob_bytes rounded up to 4096 */
