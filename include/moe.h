@@ -346,9 +346,10 @@ int moe_layer(const uint16_t* x, const float* w_router, float* logits, int T, in
  * MOE_EWS when moe_ffn_workspace_bytes(T, H, I, E, K, has_shared, ffn_flags)
  * exceeds that size, and MOE_EINVAL for the MOE_FFN_PARTIAL* flags (a partial
  * pass leaves its results in a workspace the caller cannot pass on to
- * moe_ffn_combine) and for MOE_ROUTE_ONEPASS (its workspace must start at zero). All calls on one GPU share its array: calls that overlap
- * on one GPU (on other streams or host threads) race and must be serialised
- * by the caller. */
+ * moe_ffn_combine) and for MOE_ROUTE_ONEPASS (its workspace must start at
+ * zero). All calls on one GPU share its array: calls that overlap on one GPU
+ * (on other streams or host threads) race and must be serialised by the
+ * caller. */
 size_t moe_noalloc_scratch_bytes(void);
 int moe_layer_noalloc(const uint16_t* x, const float* w_router, float* logits, int T, int H, int I, int E, int K,
                       int g, unsigned route_flags, int32_t* ids, float* w, const int32_t* slot_table,
