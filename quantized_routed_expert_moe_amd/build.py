@@ -1,4 +1,6 @@
-"""Build the HIP library ``libmoe.so`` in-tree with hipcc for gfx950."""
+"""Build the HIP library ``libmoe.so`` in-tree with hipcc for gfx950, and its
+instrumented twin ``libmoe_timeline.so`` (the same sources with MOE_TIMELINE:
+per-workgroup stamps, include/moe_timeline.h)."""
 
 from __future__ import annotations
 
@@ -11,6 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
+TIMELINE_LIB = os.path.join(PKG, "libmoe_timeline.so")
 
 SOURCES = ["api.cpp", "pack.cpp", "arena.cpp", "paged.cpp", "route.hip", "ffn_gemv.hip", "ffn_batched.hip", "ffn_decode.hip",
            "ffn_grouped.hip", "ffn_formats.hip", "scratch.hip"]
@@ -35,16 +38,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source to an object (in parallel) and link libmoe.so; returns its path."""
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, jobs: int = 8, timeline: bool = False) -> str:
+    """Compile every source to an object (in parallel) and link libmoe.so (timeline:
+    libmoe_timeline.so); returns its path."""
+    objdir = os.path.join(PKG, "_build_timeline" if timeline else "_build")
+    lib = TIMELINE_LIB if timeline else LIB
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC]
+        cmd = [cc, *HIPCC_FLAGS, *(["-DMOE_TIMELINE"] if timeline else []), "-I", INCLUDE, "-I", CSRC]
         cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -61,12 +66,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, timeline="--timeline" in sys.argv))

@@ -7,6 +7,7 @@
 #include <cmath>
 
 #include "moe_internal.h"
+#include "moe_timeline.h"
 
 namespace {
 
@@ -356,3 +357,24 @@ extern "C" int moe_expert_ffn_fmt(int fmt, const uint16_t* x, const int32_t* ids
   if (err == hipErrorNotSupported) return MOE_EUNSUP;
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }
+
+#ifdef MOE_TIMELINE
+// The instrumented build's row buffers (include/moe_timeline.h).
+extern "C" int moe_timeline_read(int kernel, uint64_t* host, int max_blocks) {
+  if (kernel < 0 || kernel >= MOE_TL_KERNELS || !host || max_blocks < 1 || max_blocks > MOE_TL_MAX_BLOCKS)
+    return MOE_EINVAL;
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
+  hipError_t err = hipErrorInvalidValue;
+  if (moe::tl_owns_route(kernel)) err = moe::tl_read_route(kernel, host, max_blocks);
+  if (moe::tl_owns_decode(kernel)) err = moe::tl_read_decode(kernel, host, max_blocks);
+  if (moe::tl_owns_batched(kernel)) err = moe::tl_read_batched(kernel, host, max_blocks);
+  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+extern "C" int moe_timeline_clear(void) {
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
+  const bool ok = moe::tl_clear_route() == hipSuccess && moe::tl_clear_decode() == hipSuccess &&
+                  moe::tl_clear_batched() == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+  return ok ? MOE_OK : MOE_EHIP;
+}
+#endif

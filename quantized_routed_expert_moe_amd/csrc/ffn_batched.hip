@@ -20,9 +20,11 @@
 
 #include "lds_dma.h"
 #include "moe_internal.h"
+#include "timeline.h"
 #include "wave_ops.h"
 
 namespace moe {
+MOE_TL_UNIT(batched, MOE_TL_BAT_PLAN, 4)
 namespace {
 
 constexpr int kThreads = 256;
@@ -118,6 +120,7 @@ __device__ inline void plan_convert_x(const FfnArgs& a, const BatWs& W, int i) {
 
 // ------------------------------------------------------------------ plan
 __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
+  const TlRow tl = tl_begin(MOE_TL_BAT_PLAN);
   __shared__ int first[kMaxE];  // lowest pair using expert e, then the unit of expert e
   __shared__ int cnt[kBatMaxPairs + 1];
   __shared__ int uoff[kBatMaxPairs + 1];
@@ -132,6 +135,7 @@ __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
   const int tid = threadIdx.x;
   if (blockIdx.x > 0) {
     plan_convert_x(a, W, (blockIdx.x - 1) * kPlanThreads + tid);
+    tl_end(tl);
     return;
   }
   for (int e = tid; e < E; e += kPlanThreads) first[e] = 0x7FFFFFFF;
@@ -189,6 +193,7 @@ __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
     }
     pl.rec[u] = rc;
   }
+  tl_end(tl);
 }
 
 // ------------------------------------------------------------------ unit header
@@ -294,6 +299,7 @@ __host__ __device__ constexpr int vm_lds_imm(int vm) { return vmcnt_imm(vm) & ~(
 
 template <int NW, int CQ, int CW, int KM>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) bmx_gateup_kernel(FfnArgs a) {
+  const TlRow tl = tl_begin(MOE_TL_BMX_GATEUP);
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const int G = H / kGroup;
@@ -307,7 +313,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)
   const int u = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const UnitHead uh = unit_head(pl, u, lane);
   const int p0 = uh.p0, np = uh.np;
-  if (np == 0) return;
+  if (np == 0) {
+    tl_end(tl);
+    return;
+  }
+  tl_mark(tl, 0);
   if (np > kUnitPairs) {
     if (tid == 0) *a.status = MOE_EUNSUP;
     return;
@@ -351,6 +361,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)
     bmx_zero_rows(xs, H, KM, rows, tid, NW * 64);
     __builtin_amdgcn_s_waitcnt(vm_lds_imm(4 * CW));  // the staged rows (issued first) and the zeros are in LDS
     __builtin_amdgcn_s_barrier();
+    if (m0 == 0) tl_mark(tl, 1);
     f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < CQ; ++c) {
@@ -369,6 +380,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)
       if (c + CW < CQ && 4 * (c + CW) < G) load_chunk(c + CW);
       __builtin_amdgcn_sched_barrier(0);  // one chunk's operands at a time (register pressure)
     }
+    tl_mark(tl, 2);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * q + v;
@@ -380,10 +392,12 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)
     }
   }
   if (bad) *a.status = MOE_EUNSUP;
+  tl_end(tl);
 }
 
 template <int NW, int CQ, int KM>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CQ <= 6 ? 6 : 4))) bmx_down_kernel(FfnArgs a) {
+  const TlRow tl = tl_begin(MOE_TL_BMX_DOWN);
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const int Gd = I / kGroup;
@@ -397,7 +411,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CQ
   const int u = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const UnitHead uh = unit_head(pl, u, lane);
   const int p0 = uh.p0, np = uh.np;
-  if (np == 0) return;
+  if (np == 0) {
+    tl_end(tl);
+    return;
+  }
+  tl_mark(tl, 0);
   if (np > kUnitPairs) {
     if (tid == 0) *a.status = MOE_EUNSUP;
     return;
@@ -433,6 +451,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CQ
     bmx_zero_rows(hs, I, KM, rows, tid, NW * 64);
     __builtin_amdgcn_s_waitcnt(vm_lds_imm(2 * CQ));
     __builtin_amdgcn_s_barrier();
+    if (m0 == 0) tl_mark(tl, 1);
     f32x4_t ao = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < CQ; ++c) {
@@ -446,6 +465,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CQ
         ao = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ha[i]), dequant_qs(dword_of(cd[c], i), sd), ao, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // one chunk's operands at a time (register pressure)
     }
+    tl_mark(tl, 2);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * q + v;
@@ -454,12 +474,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CQ
     }
   }
   if (bad) *a.status = MOE_EUNSUP;
+  tl_end(tl);
 }
 
 // ------------------------------------------------------------------ combine
 // y[t][col] = o_shared + sum over k in rank order; every o and w load of an
 // output is issued before the sums.
 __global__ void __launch_bounds__(kThreads) bat_combine_kernel(FfnArgs a) {
+  const TlRow tl = tl_begin(MOE_TL_BAT_COMBINE);
   const int H = a.H, T = a.T, K = a.K;
   const bool has_shared = a.shared_blob != nullptr;
   const BatWs W = bat_ws(T, H, a.I, a.E, K, has_shared);
@@ -483,6 +505,7 @@ __global__ void __launch_bounds__(kThreads) bat_combine_kernel(FfnArgs a) {
     }
     a.y[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc);
   }
+  tl_end(tl);
 }
 
 inline void set_lds_limit(const void* fn, size_t lds) {

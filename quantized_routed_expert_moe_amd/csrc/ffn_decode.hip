@@ -44,9 +44,11 @@
 // the inputs, never on slot addresses.
 #include "moe_internal.h"
 #include "onepass.h"
+#include "timeline.h"
 #include "wave_ops.h"
 
 namespace moe {
+MOE_TL_UNIT(decode, MOE_TL_DEC_ROUTE_GATEUP, 3)
 namespace {
 
 constexpr int kThreads = 256;
@@ -116,7 +118,8 @@ __device__ inline const uint8_t* onepass_unit_blob(const FfnArgs& a, int u, bool
 // bid: the workgroup's index among the gate/up workgroups. ONEPASS: the unit's
 // slot comes from the one-pass hand-off words (epoch ep) instead of the table.
 template <int GPL, bool ONEPASS>
-__device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const uint64_t* words, uint32_t ep) {
+__device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const uint64_t* words, uint32_t ep,
+                                                const TlRow& tl) {
   // LDS per wave: x slice as fp16 pairs [GW][16] dwords + group corrections [GW]
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float part[2][kWaves][8];
@@ -136,7 +139,10 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
   const_i32p pre = (const_i32p)a.pre_slots;
   asm volatile("" : "+s"(pre));
   const int n_hb = I / 8;
-  const int item = xcd_item(bid, (K + (has_shared ? 1 : 0)) * n_hb);
+  // ONEPASS: the ranks' slots arrive one after another, so each unit's row blocks
+  // are dealt round-robin over the XCDs (every XCD streams rank 0 first); else
+  // each XCD takes a contiguous run of items
+  const int item = ONEPASS ? bid : xcd_item(bid, (K + (has_shared ? 1 : 0)) * n_hb);
   const int u = item / n_hb, hb = item % n_hb;
   // 1. this wave's slice of x: uint4 q (8 bf16) of the slice = columns 8q .. 8q+7
   //    (issued before the two dependent loads that find the unit's blob)
@@ -149,6 +155,7 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
   }
   const uint8_t* blob =
       ONEPASS ? onepass_unit_blob(a, u, has_shared, words, ep, wave) : dec_unit_blob(a, u, has_shared, a.ids, pre);
+  tl_mark(tl, 3);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
   const BlobLayout BL = blob_layout(H, I);
   const int n = hb * 8 + r;
@@ -200,6 +207,7 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
     suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
   }
   __builtin_amdgcn_sched_barrier(0);  // every load is issued before the steps
+  tl_mark(tl, 4);
   // 4. the steps, each reading its LDS operands (other waves of the SIMD cover
   //    the LDS latency: few registers live means six or more waves per SIMD)
   float ag = 0.0f, au = 0.0f;
@@ -248,32 +256,35 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
     if (!(fabsf(hv) < 65520.0f)) *a.status = MOE_EUNSUP;  // h does not fit fp16
     reinterpret_cast<_Float16*>(a.ws)[(size_t)unit_pair(u, K, has_shared) * I + hb * 8 + tid] = (_Float16)hv;
   }
+  tl_end(tl);
 }
 
 template <int GPL>
 __global__ void __launch_bounds__(kThreads) dec_gateup_kernel(FfnArgs a) {
-  dec_gateup_body<GPL, false>(a, blockIdx.x, nullptr, 0);
+  const TlRow tl = tl_begin(MOE_TL_DEC_GATEUP);
+  dec_gateup_body<GPL, false>(a, blockIdx.x, nullptr, 0, tl);
 }
 
 // moe_layer's one-pass single-token path in one dispatch: workgroups 0 .. E-1
 // compute the router logits and publish them (onepass.h); the last of them
-// selects, writes logits, ids, w and the resolved slots (for the down kernel),
-// and publishes each rank's slot; the other workgroups are the gate/up items,
-// which stage x and then wait for their unit's slot word. The arithmetic is
+// selects, publishes each rank's slot as soon as that rank is selected, and
+// writes logits, ids, w and the resolved slots (for the down kernel); the other
+// workgroups are the gate/up items, which stage x and then wait for their unit's
+// slot word. The arithmetic is
 // that of router_gemv1_kernel, route_select_kernel and dec_gateup_kernel, so
 // the results are the same bits. Workgroups are dispatched in index order on
 // each XCD and the GEMV workgroups wait for nothing, so every word that a
 // waiting workgroup needs is eventually written (each wait is also bounded).
 template <int GPL, int EPL>
 __global__ void __launch_bounds__(kThreads) dec_route_gateup_kernel(FfnArgs a, OnepassRoute r) {
+  const TlRow tl = tl_begin(MOE_TL_DEC_ROUTE_GATEUP);
   const uint32_t ep = onepass_epoch(r.words);
   const int E = a.E;
   if ((int)blockIdx.x >= E) {
-    dec_gateup_body<GPL, true>(a, blockIdx.x - E, r.words, ep);
+    dec_gateup_body<GPL, true>(a, blockIdx.x - E, r.words, ep, tl);
     return;
   }
   __shared__ double part[4];
-  __shared__ int32_t tbl[64 * EPL];
   const bool selector = (int)blockIdx.x == E - 1 && threadIdx.x < 64;
   // the selector's slot-table loads go out first and land while it waits
   const int lane = threadIdx.x & 63;
@@ -286,39 +297,64 @@ __global__ void __launch_bounds__(kThreads) dec_route_gateup_kernel(FfnArgs a, O
     }
   }
   onepass_publish_logit(a.x, r.w_router, a.H, blockIdx.x, r.words, ep, part);
-  if (!selector) return;
+  tl_mark(tl, 0);
+  if (!selector) {
+    tl_end(tl);
+    return;
+  }
   // wait, select and publish the slots first; the output stores come after
   float lg[EPL];
   const bool ok = onepass_wait_logits<EPL>(r.words, E, ep, a.status, lg);
+  tl_mark(tl, 1);
   float sel[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) sel[i] = lg[i];
   int32_t id = 0;
   float wt = 0.0f;
-  if (ok) wave_select_values<EPL>(sel, E, a.K, r.flags, lane, id, wt);
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) tbl[lane + 64 * i] = tv[i];  // entries past E are never read
-  __builtin_amdgcn_wave_barrier();  // one wave: its LDS stores precede its loads
   int32_t slot = (int32_t)0x80000000;  // the hand-off failed: consumers report it
-  if (ok && lane < a.K) slot = tbl[id];
-  // kOnepassCopies copies of each rank's slot (lane c writes copy c)
-  for (int k = 0; k < a.K; ++k) {
-    const int32_t sk = __builtin_amdgcn_readlane(slot, k);
-    if (lane < kOnepassCopies) ll_store(r.words + onepass_slot_word(E, k, lane), ep, (uint32_t)sk);
+  if (ok) {
+    // each rank's slot is published in the round that selects it (kOnepassCopies
+    // copies, lane c writes copy c), so the gate/up items of rank k start while
+    // the later ranks are still being selected; the slot of expert e is tv[e / 64]
+    // of lane e % 64
+    auto publish = [&](int k, uint64_t best) {
+      const int e = key_id(best);
+      int32_t sk = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int32_t v = __builtin_amdgcn_readlane(tv[i], e & 63);
+        sk = (e >> 6) == i ? v : sk;
+      }
+      if (lane < kOnepassCopies) ll_store(r.words + onepass_slot_word(E, k, lane), ep, (uint32_t)sk);
+      if (lane == k) slot = sk;
+    };
+    wave_select_values<EPL>(sel, E, a.K, r.flags, lane, id, wt, publish);
+  } else {
+    for (int k = 0; k < a.K; ++k)
+      if (lane < kOnepassCopies) ll_store(r.words + onepass_slot_word(E, k, lane), ep, (uint32_t)slot);
   }
-  if (!ok) return;
+  tl_mark(tl, 2);
+  if (!ok) {
+    tl_end(tl);
+    return;
+  }
   if (lane < a.K) {
     r.ids[lane] = id;
     r.w[lane] = wt;
     const_cast<int32_t*>(a.pre_slots)[lane] = slot;
   }
   onepass_store_logits<EPL>(lg, E, r.logits);
+  tl_end(tl);
 }
 
 // ------------------------------------------------------------------ down + combine
 // CPL = columns per lane; a wave owns CW = 16 * CPL consecutive columns.
-template <int CPL>
+// PRE: the K slots were resolved by the routing kernel (a.pre_slots); they are
+// loaded first, before h, so that the weight loads wait for one round trip
+// only (loads complete in order: a slot load issued after h would wait for h).
+template <int CPL, bool PRE>
 __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
+  const TlRow tl = tl_begin(MOE_TL_DEC_DOWN);
   // LDS per wave: h slice as fp16 pairs [CW][16] dwords + column corrections [CW]
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kMaxUnits = kMaxK + 1;
@@ -347,6 +383,13 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   const BlobLayout BL = blob_layout(H, I);
   const int qb = xcd_item(blockIdx.x, H / 4);
   const int n = qb * 4 + r;
+  // the resolved slots (PRE), every lane's load unconditional (a clamped rank):
+  // a load under a lane-dependent branch would be waited for at the branch
+  int32_t pre_v = 0;
+  if constexpr (PRE) {
+    const int kk = lane - (has_shared ? 1 : 0);
+    pre_v = a.pre_slots[kk < 0 ? 0 : (kk < K ? kk : K - 1)];
+  }
   // the routing weights, loaded first and kept in LDS for the combine
   const float wk = (wave == 0 && lane < K) ? w_p[lane] : 0.0f;
   // the status pointer in registers now, with the other arguments (left to the
@@ -355,8 +398,8 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   __attribute__((address_space(1))) int32_t* status = (__attribute__((address_space(1))) int32_t*)a.status;
   asm volatile("" : "+s"(status));
   // 1. this wave's h slice: uint4 q = lane + 64m = column c0 + q/4, halves 8*(q%4) .. +7;
-  //    (unit, group) of the lane's column advance by 16 columns per m. Issued first:
-  //    it does not depend on the unit slots.
+  //    (unit, group) of the lane's column advance by 16 columns per m. Issued before
+  //    the slot lookup below: it does not depend on the unit slots.
   uint4 hv[CPL];
   {
     int cu = c0 + lane / 4;
@@ -382,8 +425,8 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     if (k < 0) {
       my_slot = 0;
     } else {
-      if (a.pre_slots) {
-        my_slot = a.pre_slots[k];
+      if (PRE) {
+        my_slot = pre_v;
         if (my_slot < 0) *status = MOE_ENOTRES;
       } else {
         const int e = ids_p[k];
@@ -396,10 +439,6 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
       }
     }
   }
-  // after a one-pass dispatch: every workgroup of it has read the region's call
-  // number (that dispatch has completed), so the call is numbered done here
-  if (a.onepass && blockIdx.x == 0 && tid == 0)
-    __hip_atomic_store(a.onepass, (uint64_t)onepass_epoch(a.onepass), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // this wave's entries of the partial sums start at zero (only this wave writes them)
   for (int q = lane; q < kMaxUnits * 4; q += 64) (&part[wave][0][0])[q] = 0.0f;
   // 2. codes and scale dwords of every step; a step is one unit for all lanes
@@ -429,6 +468,7 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // every load is issued before h is used
+  tl_mark(tl, 0);
   if (wave == 0 && lane < K) wsh[lane] = wk;
   // 3. h slice into LDS with its column corrections (lanes 4t .. 4t+3 hold one column)
 #pragma unroll
@@ -444,6 +484,7 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     if ((lane & 3) == 0) Cc[q / 4] = fmaf(1032.0f, sa, 72.0f * sb);
   }
   __builtin_amdgcn_wave_barrier();
+  tl_mark(tl, 1);
   // 4. the steps; the LDS operands of step i+1 are read during step i
   const int sh = (r & 1) * 16;
   float acc = 0.0f;
@@ -489,6 +530,7 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     const float t = sum_rows(dpp_add<8>(dpp_add<4>(acc)));
     if (p == 0) part[wave][cur][r] = t;
   }
+  tl_mark(tl, 2);
   __syncthreads();
   if (tid < 4) {
     float y = 0.0f;
@@ -507,6 +549,12 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     }
     a.y[(size_t)qb * 4 + tid] = __builtin_bit_cast(uint16_t, (__bf16)y);
   }
+  // after a one-pass dispatch: every workgroup of it has read the region's call
+  // number (that dispatch has completed), so the call is numbered done here (at the
+  // end: its load would otherwise be waited for with this wave's h and code loads)
+  if (a.onepass && blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(a.onepass, (uint64_t)onepass_epoch(a.onepass), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  tl_end(tl);
 }
 
 inline void set_lds_limit(const void* fn, size_t lds) {
@@ -591,8 +639,13 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
     const int grid = a.H / 4;
 #define DN(N)                                                                                       \
   do {                                                                                              \
-    set_lds_limit(reinterpret_cast<const void*>(&dec_down_kernel<N>), lds);                         \
-    hipLaunchKernelGGL((dec_down_kernel<N>), dim3(grid), dim3(kThreads), lds, s, a);                \
+    if (a.pre_slots) {                                                                              \
+      set_lds_limit(reinterpret_cast<const void*>(&dec_down_kernel<N, true>), lds);                 \
+      hipLaunchKernelGGL((dec_down_kernel<N, true>), dim3(grid), dim3(kThreads), lds, s, a);        \
+    } else {                                                                                        \
+      set_lds_limit(reinterpret_cast<const void*>(&dec_down_kernel<N, false>), lds);                \
+      hipLaunchKernelGGL((dec_down_kernel<N, false>), dim3(grid), dim3(kThreads), lds, s, a);       \
+    }                                                                                               \
   } while (0)
     if (cpl == 2) DN(2);
     else if (cpl == 4) DN(4);

@@ -189,4 +189,17 @@ hipError_t launch_status(int32_t* dst, const int32_t* src, hipStream_t s);
 // ids[0..n) to pinned host memory host[0..n), then host[n] = seq (system scope, released)
 hipError_t launch_publish_ids(const int32_t* ids, int n, int32_t* host, int32_t seq, hipStream_t s);
 
+#ifdef MOE_TIMELINE
+// per-unit row buffers of the instrumented build (timeline.h, MOE_TL_UNIT)
+bool tl_owns_route(int kernel);
+bool tl_owns_decode(int kernel);
+bool tl_owns_batched(int kernel);
+hipError_t tl_read_route(int kernel, uint64_t* host, int blocks);
+hipError_t tl_read_decode(int kernel, uint64_t* host, int blocks);
+hipError_t tl_read_batched(int kernel, uint64_t* host, int blocks);
+hipError_t tl_clear_route();
+hipError_t tl_clear_decode();
+hipError_t tl_clear_batched();
+#endif
+
 }  // namespace moe

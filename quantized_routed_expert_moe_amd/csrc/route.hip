@@ -6,9 +6,11 @@
 // of a softmax top-k router.
 #include "moe_internal.h"
 #include "onepass.h"
+#include "timeline.h"
 #include "wave_ops.h"
 
 namespace moe {
+MOE_TL_UNIT(route, MOE_TL_ROUTER_GEMV, 2)
 namespace {
 
 constexpr int kRouterTok = 4;  // tokens per router wave (one router row is read once for them)
@@ -73,10 +75,12 @@ __global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __rest
 __global__ void __launch_bounds__(256) router_gemv1_kernel(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ wr, float* __restrict__ logits,
                                                            int H, int E) {
+  const TlRow tl = tl_begin(MOE_TL_ROUTER_GEMV);
   __shared__ double part[4];
   const int e = blockIdx.x;
   const double s = router_row_sum(x, wr + (size_t)e * H, H, part);
   if (threadIdx.x == 0) logits[e] = (float)s;
+  tl_end(tl);
 }
 
 // One-pass routing of one token (moe_route_onepass): workgroup e computes
@@ -122,6 +126,7 @@ __global__ void __launch_bounds__(64) route_select_kernel(const float* __restric
                                                           float* __restrict__ w,
                                                           const int32_t* __restrict__ slot_table,
                                                           int32_t* __restrict__ slots_out) {
+  const TlRow tl = tl_begin(MOE_TL_ROUTE_SELECT);
   __shared__ int32_t tbl[64 * EPL];
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
@@ -148,6 +153,7 @@ __global__ void __launch_bounds__(64) route_select_kernel(const float* __restric
     __builtin_amdgcn_wave_barrier();  // one wave: its LDS stores precede its loads
     if (lane < K) slots_out[lane] = tbl[id];
   }
+  tl_end(tl);
 }
 
 // Score of one logit for the scored router variants ("Strata" README, Models:

@@ -130,8 +130,14 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
 // lowest id, decides) and pops it from its owner lane.
 // The K largest keys of the wave (lane l holds the keys of experts l, l + 64, ...;
 // 0 marks an absent expert): lane k < K returns the key of rank k, the others 0.
-template <int EPL>
-__device__ inline uint64_t wave_topk(uint64_t (&key)[EPL], int K, int lane) {
+// A rank hook is called as hook(k, key) once per rank k = 0 .. K-1 as soon as
+// that rank's key is known (key is wave-uniform); the default does nothing.
+struct NoRankHook {
+  __device__ void operator()(int, uint64_t) const {}
+};
+
+template <int EPL, typename Hook = NoRankHook>
+__device__ inline uint64_t wave_topk(uint64_t (&key)[EPL], int K, int lane, const Hook& hook = Hook{}) {
   // local descending sort (odd-even transposition)
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
@@ -160,6 +166,7 @@ __device__ inline uint64_t wave_topk(uint64_t (&key)[EPL], int K, int lane) {
       key[EPL - 1] = 0;
     }
     if (lane == k) mine = best;
+    hook(k, best);
   }
   return mine;
 }
@@ -173,8 +180,8 @@ __device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
   return ((uint64_t)hi << 32) | lo;
 }
-template <int EPL>
-__device__ inline uint64_t wave_topk_bitonic(uint64_t (&key)[EPL], int K, int lane) {
+template <int EPL, typename Hook = NoRankHook>
+__device__ inline uint64_t wave_topk_bitonic(uint64_t (&key)[EPL], int K, int lane, const Hook& hook = Hook{}) {
   constexpr int N = 64 * EPL;
 #pragma unroll
   for (int size = 2; size <= N; size <<= 1) {
@@ -203,6 +210,11 @@ __device__ inline uint64_t wave_topk_bitonic(uint64_t (&key)[EPL], int K, int la
       }
     }
   }
+  for (int k = 0; k < K; ++k) {
+    const uint64_t best = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(key[0] >> 32), k) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)key[0], k);
+    hook(k, best);
+  }
   return lane < K ? key[0] : 0ull;
 }
 
@@ -211,9 +223,9 @@ __device__ inline uint64_t wave_topk_bitonic(uint64_t (&key)[EPL], int K, int la
 // divided by the sum over the K selected).
 // Softmax + top-k of one token's logits held in registers: lane l holds lg[i] =
 // logit of expert l + 64 i (entries past E ignored).
-template <int EPL, bool BITONIC = false>
+template <int EPL, bool BITONIC = false, typename Hook = NoRankHook>
 __device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsigned flags, int lane, int32_t& id,
-                                          float& wt) {
+                                          float& wt, const Hook& hook = Hook{}) {
   uint64_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
@@ -221,7 +233,7 @@ __device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsign
     if (e >= E) lg[i] = 0.0f;
     key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
   }
-  const uint64_t mine = BITONIC ? wave_topk_bitonic<EPL>(key, K, lane) : wave_topk<EPL>(key, K, lane);
+  const uint64_t mine = BITONIC ? wave_topk_bitonic<EPL>(key, K, lane, hook) : wave_topk<EPL>(key, K, lane, hook);
   const uint32_t top_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mine >> 32));
   const uint32_t top_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mine);
   const float m = key_logit(((uint64_t)top_hi << 32) | top_lo);  // the largest logit (rank 0, lane 0)

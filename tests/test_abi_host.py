@@ -1,6 +1,7 @@
 """Host-side checks of the C-ABI library (CPU only, no GPU compute calls).
 
-* libmoe.so loads and exports every function include/moe.h declares;
+* libmoe.so loads and exports every function include/moe.h declares, and its
+  instrumented twin libmoe_timeline.so also those of include/moe_timeline.h;
 * moe_pack_expert writes the documented blob layout (decoded here by an
   independent reader of that layout and compared with the interchange input);
 * the arena's slot policy in C++ replays the reference model's slot, fill,
@@ -32,6 +33,25 @@ def test_library_exports_every_declared_function():
     assert names == set(lib.EXPORTS), names ^ set(lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_timeline_build_exports_its_functions_and_the_product_does_not():
+    """libmoe_timeline.so (the instrumented twin) exports what include/moe.h and
+    include/moe_timeline.h declare; libmoe.so exports nothing of the timeline."""
+    import ctypes
+
+    from quantized_routed_expert_moe_amd import build
+
+    src = open(os.path.join(ROOT, "include", "moe_timeline.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    tl_names = set(re.findall(r"\b(moe_timeline_\w+)\s*\(", src))
+    assert tl_names == {"moe_timeline_read", "moe_timeline_clear"}
+    T = ctypes.CDLL(build.TIMELINE_LIB)
+    for n in tl_names | header_functions():
+        assert hasattr(T, n), n
+    P = lib.load()
+    for n in tl_names:
+        assert not hasattr(P, n), n
 
 
 def test_strerror_and_sizes():
