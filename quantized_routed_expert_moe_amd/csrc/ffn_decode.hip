@@ -349,9 +349,10 @@ __global__ void __launch_bounds__(kThreads) dec_route_gateup_kernel(FfnArgs a, O
 
 // ------------------------------------------------------------------ down + combine
 // CPL = columns per lane; a wave owns CW = 16 * CPL consecutive columns.
-// PRE: the K slots were resolved by the routing kernel (a.pre_slots); they are
-// loaded first, before h, so that the weight loads wait for one round trip
-// only (loads complete in order: a slot load issued after h would wait for h).
+// PRE: the K slots were resolved by the routing kernel (a.pre_slots); else they
+// are looked up as slot_table[ids[k]]. Either way the slot loads go out before
+// h, so that the weight loads wait for the slots only (loads complete in order:
+// a slot load issued after h would also wait for h).
 template <int CPL, bool PRE>
 __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   const TlRow tl = tl_begin(MOE_TL_DEC_DOWN);
@@ -383,15 +384,20 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   const BlobLayout BL = blob_layout(H, I);
   const int qb = xcd_item(blockIdx.x, H / 4);
   const int n = qb * 4 + r;
-  // the resolved slots (PRE), every lane's load unconditional (a clamped rank):
-  // a load under a lane-dependent branch would be waited for at the branch
-  int32_t pre_v = 0;
+  // the slot of rank kk (lane kk + 1 with a shared expert), every lane's load
+  // unconditional (a clamped rank): a load under a lane-dependent branch would be
+  // waited for at the branch. PRE: one load; else the id, then its table entry.
+  const int kk = lane - (has_shared ? 1 : 0);
+  const int kc = kk < 0 ? 0 : (kk < K ? kk : K - 1);
+  int32_t pre_v = 0, e_v = 0;
   if constexpr (PRE) {
-    const int kk = lane - (has_shared ? 1 : 0);
-    pre_v = a.pre_slots[kk < 0 ? 0 : (kk < K ? kk : K - 1)];
+    pre_v = a.pre_slots[kc];
+  } else {
+    e_v = ids_p[kc];
   }
-  // the routing weights, loaded first and kept in LDS for the combine
+  // the routing weights, loaded early and kept in LDS for the combine
   const float wk = (wave == 0 && lane < K) ? w_p[lane] : 0.0f;
+  if constexpr (!PRE) pre_v = a.slot_table[e_v >= 0 && e_v < a.E ? e_v : 0];
   // the status pointer in registers now, with the other arguments (left to the
   // compiler, its load lands after the slot lookup, one more round trip on the
   // path to the weight loads)
@@ -416,26 +422,20 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
       hu += w1;
     }
   }
-  // unit slots (two dependent loads): lane u of every wave holds unit u's slot,
-  // -1 when it cannot be used (the status word says why); the shared expert
-  // (unit 0 when present) is marked 0 and read from shared_blob
+  // unit slots (loaded above): lane u of every wave holds unit u's slot, -1 when
+  // it cannot be used (the status word says why); the shared expert (unit 0 when
+  // present) is marked 0 and read from shared_blob
   int my_slot = -1;
   if (lane < n_units) {
     const int k = has_shared ? lane - 1 : lane;
     if (k < 0) {
       my_slot = 0;
     } else {
-      if (PRE) {
+      if (!PRE && (e_v < 0 || e_v >= a.E)) {
+        *status = MOE_EINVAL;
+      } else {
         my_slot = pre_v;
         if (my_slot < 0) *status = MOE_ENOTRES;
-      } else {
-        const int e = ids_p[k];
-        if (e < 0 || e >= a.E) {
-          *status = MOE_EINVAL;
-        } else {
-          my_slot = a.slot_table[e];
-          if (my_slot < 0) *status = MOE_ENOTRES;
-        }
       }
     }
   }
