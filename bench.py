@@ -323,9 +323,11 @@ def batched_leg(a, dev, n_sets=16):
     log(f"  batched: packed ({time.time() - t0:.1f} s)")
     run = harness.LayerRunner(w, dev)
     stream = torch.cuda.Stream()
+    # each layer is one moe_layer call (route and expert FFN; on this path the plan
+    # kernel does the top-k selection itself)
     with torch.cuda.stream(stream):
         for L in sets:
-            run(L, stream)
+            run.layer(L, stream)
     stream.synchronize()
     if int(run.status.item()) != 0:
         raise RuntimeError(f"device status {int(run.status.item())}")
@@ -340,7 +342,7 @@ def batched_leg(a, dev, n_sets=16):
     with torch.cuda.stream(stream):
         for _ in range(reps):
             for L in sets:
-                run(L, stream)
+                run.layer(L, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     us_layer = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))

@@ -47,6 +47,18 @@ extern "C" const char* moe_strerror(int status) {
 
 extern "C" int moe_version(void) { return 100; }
 
+namespace {
+// moe_route's argument checks, true when it would enqueue work (T > 0, valid arguments).
+bool shape_ok_for_route(int T, int H, int E, int K, unsigned flags, const float* w_router, const uint16_t* x,
+                        const float* logits, const int32_t* ids, const float* w) {
+  if (T <= 0 || E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return false;
+  if (flags & ~(unsigned)(MOE_ROUTE_RENORM | MOE_ROUTE_BITONIC)) return false;
+  if (E > moe::kMaxE || K > moe::kMaxK) return false;
+  if (w_router && (!x || H <= 0 || H % moe::kGroup || H > 8192)) return false;
+  return true;
+}
+}  // namespace
+
 extern "C" int moe_route(const uint16_t* x, const float* w_router, float* logits, int T, int H, int E, int K,
                          unsigned flags, int32_t* ids, float* w, moe_stream_t stream) {
   if (T < 0 || E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return MOE_EINVAL;
@@ -93,12 +105,20 @@ extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int I, int E, int K, int
 
 namespace {
 
+// Whether expert_ffn_stage takes the batched path for these arguments.
+bool ffn_uses_batched(int T, int H, int I, int K, unsigned flags, bool has_shared) {
+  return !ffn_uses_grouped(T, flags) && gemv_shape_ok(T, H, I, K) &&
+         !moe::decode1_supported(T, H, I, K, has_shared) && moe::batched_supported(T, H, I, K);
+}
+
 // Shared argument checks and dispatch of one stage (0 = gate/up, 1 = down +
-// combine, 2 = both) of the expert FFN.
+// combine, 2 = both) of the expert FFN. route_logits (batched path only): the
+// plan kernel selects the top-k from them and writes ids and w itself.
 int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int T, int H, int I, int E, int K, int g,
                      const int32_t* slot_table, const void* slots, size_t stride, const void* shared_blob,
                      uint16_t* y, void* ws, size_t ws_bytes, int32_t* dev_status, unsigned flags,
-                     moe_stream_t stream, int stage, const int32_t* pre_slots = nullptr) {
+                     moe_stream_t stream, int stage, const int32_t* pre_slots = nullptr,
+                     const float* route_logits = nullptr, unsigned route_flags = 0) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E) return MOE_EINVAL;
   if (flags & ~(unsigned)(MOE_FORCE_GEMV | MOE_FORCE_GROUPED | MOE_FFN_PARTIAL | MOE_FFN_PARTIAL_SHARED |
                           MOE_FFN_PARTIAL_FIRST))
@@ -141,6 +161,11 @@ int expert_ffn_stage(const uint16_t* x, const int32_t* ids, const float* w, int 
   const bool dec1 = !grouped && moe::decode1_supported(T, H, I, K, shared_blob != nullptr);
   if (dec1) a.pre_slots = pre_slots;
   const bool bat = !grouped && moe::batched_supported(T, H, I, K);
+  if (route_logits) {
+    if (!bat || dec1 || stage != 2) return MOE_EINVAL;  // callers check ffn_uses_batched first
+    a.route_logits = route_logits;
+    a.route_flags = route_flags;
+  }
   for (int st = 0; st < 2; ++st) {
     if (stage != 2 && stage != st) continue;
     hipError_t err;
@@ -265,6 +290,17 @@ extern "C" int moe_layer(const uint16_t* x, const float* w_router, float* logits
       return MOE_EHIP;
     return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
                             dev_status, ffn_flags, stream, 2, pre);
+  }
+  // The batched path (2..32 tokens): the plan kernel also does the selection (same
+  // ids and weights as moe_route's), which saves a launch; the router GEMV, when
+  // there is a router, runs first as in moe_route.
+  if (T >= 2 && shape_ok_for_route(T, H, E, K, route_flags, w_router, x, logits, ids, w) &&
+      !(route_flags & MOE_ROUTE_BITONIC) && moe::batched_routes(E) &&
+      ffn_uses_batched(T, H, I, K, ffn_flags, shared_blob != nullptr)) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (w_router && moe::launch_router_gemv(x, w_router, logits, T, H, E, s) != hipSuccess) return MOE_EHIP;
+    return expert_ffn_stage(x, ids, w, T, H, I, E, K, g, slot_table, slots, stride, shared_blob, y, ws, ws_bytes,
+                            dev_status, ffn_flags, stream, 2, nullptr, logits, route_flags);
   }
   const int rs = moe_route(x, w_router, logits, T, H, E, K, route_flags, ids, w, stream);
   if (rs != MOE_OK) return rs;

@@ -9,7 +9,10 @@
 //                 per unit one record (slot, first pair, pair count) into the
 //                 workspace; other workgroups convert x to fp16 once. Pair
 //                 p = t*K + k for routed pairs, T*K + t for the shared
-//                 expert's.
+//                 expert's. Under moe_layer the same workgroup first selects
+//                 every token's top-k from the logits (one wave per token,
+//                 the selection of route_select_kernel, so the same ids and
+//                 weights), which saves the routing launch.
 //   bmx_gateup    MFMA over (unit pairs x 16 weight rows) tiles; h =
 //                 silu(g) * u in fp16, one row per pair in unit order.
 //   bmx_down      the same for the down matrix; o (fp32) at each pair's row.
@@ -31,6 +34,7 @@ constexpr int kThreads = 256;
 constexpr int kUnitPairs = 64;         // pairs one unit can hold (a routed unit has at most T)
 constexpr int kPlanThreads = 1024;
 constexpr int kBatMaxPairs = 512;      // routed pairs T*K the plan covers
+static_assert(kMaxE <= kPlanThreads, "the plan loads one slot-table entry per thread");
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -119,9 +123,14 @@ __device__ inline void plan_convert_x(const FfnArgs& a, const BatWs& W, int i) {
 }
 
 // ------------------------------------------------------------------ plan
+// EPL > 0: workgroup 0 first selects the top-k of every token from a.route_logits
+// (wave v takes tokens v, v + 16, ...; EPL = experts per lane) and writes ids and w.
+template <int EPL>
 __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
   const TlRow tl = tl_begin(MOE_TL_BAT_PLAN);
   __shared__ int first[kMaxE];  // lowest pair using expert e, then the unit of expert e
+  __shared__ int slot_lds[kMaxE];  // the slot table, loaded at the start
+  __shared__ int ids_lds[kBatMaxPairs];
   __shared__ int cnt[kBatMaxPairs + 1];
   __shared__ int uoff[kBatMaxPairs + 1];
   __shared__ int unit_expert_lds[kBatMaxPairs + 1];
@@ -138,11 +147,32 @@ __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
     tl_end(tl);
     return;
   }
-  for (int e = tid; e < E; e += kPlanThreads) first[e] = 0x7FFFFFFF;
-  for (int u = tid; u <= kBatMaxPairs; u += kPlanThreads) cnt[u] = 0;
-  __syncthreads();
+  // the slot table (E <= kPlanThreads entries, one per thread) and the ids or
+  // logits go out first: the records need the table only after the dedup, so no
+  // dependent load is left for later
+  const int sv = tid < E ? a.slot_table[tid] : 0;
   const int p = tid;  // P <= kBatMaxPairs < kPlanThreads: one pair per thread
-  const int e = p < P ? a.ids[p] : -1;
+  int e = -1;
+  if constexpr (EPL == 0) {
+    e = p < P ? a.ids[p] : -1;
+  } else {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int t = wave; t < T; t += kPlanThreads / 64) {
+      int32_t id;
+      float wt;
+      wave_select<EPL>(a.route_logits + (size_t)t * E, E, K, a.route_flags, lane, id, wt);
+      if (lane < K) {
+        const_cast<int32_t*>(a.ids)[t * K + lane] = id;
+        const_cast<float*>(a.w)[t * K + lane] = wt;
+        ids_lds[t * K + lane] = id;
+      }
+    }
+  }
+  for (int x = tid; x < E; x += kPlanThreads) first[x] = 0x7FFFFFFF;
+  for (int u = tid; u <= kBatMaxPairs; u += kPlanThreads) cnt[u] = 0;
+  if (tid < E) slot_lds[tid] = sv;
+  __syncthreads();
+  if constexpr (EPL > 0) e = p < P ? ids_lds[p] : -1;
   const bool valid = p < P && e >= 0 && e < E;
   if (p < P && !valid) *a.status = MOE_EINVAL;
   if (valid) atomicMin(&first[e], p);
@@ -186,7 +216,7 @@ __global__ void __launch_bounds__(kPlanThreads) bat_plan_kernel(FfnArgs a) {
       if (ex == -1) {
         rc.x = -1;
       } else {
-        const int slot = a.slot_table[ex];
+        const int slot = slot_lds[ex];
         if (slot < 0) *a.status = MOE_ENOTRES;
         rc.x = slot < 0 ? -2 : slot;
       }
@@ -514,6 +544,8 @@ inline void set_lds_limit(const void* fn, size_t lds) {
 
 }  // namespace
 
+bool batched_routes(int E) { return E >= 1 && E <= 1024; }
+
 bool batched_supported(int T, int H, int I, int K) {
   const int G = H / kGroup, Gd = I / kGroup;
   // gate/up: at most 32 chunks of 4 groups (LDS: 16 rows of x); down: at most 16
@@ -530,7 +562,14 @@ hipError_t launch_ffn_batched(const FfnArgs& a, int stage, hipStream_t s) {
   constexpr int KM = 16;  // pairs per M-tile
   if (stage == 0) {
     const int conv_blocks = (a.T * a.H / 2 + kPlanThreads - 1) / kPlanThreads;
-    hipLaunchKernelGGL(bat_plan_kernel, dim3(1 + conv_blocks), dim3(kPlanThreads), 0, s, a);
+    const dim3 pg(1 + conv_blocks), pb(kPlanThreads);
+    const int epl = (a.E + 63) / 64;
+    if (!a.route_logits) hipLaunchKernelGGL(bat_plan_kernel<0>, pg, pb, 0, s, a);
+    else if (epl <= 1) hipLaunchKernelGGL(bat_plan_kernel<1>, pg, pb, 0, s, a);
+    else if (epl <= 2) hipLaunchKernelGGL(bat_plan_kernel<2>, pg, pb, 0, s, a);
+    else if (epl <= 4) hipLaunchKernelGGL(bat_plan_kernel<4>, pg, pb, 0, s, a);
+    else if (epl <= 8) hipLaunchKernelGGL(bat_plan_kernel<8>, pg, pb, 0, s, a);
+    else hipLaunchKernelGGL(bat_plan_kernel<16>, pg, pb, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int chunks = (a.H / kGroup + 3) / 4;

@@ -134,6 +134,10 @@ struct FfnArgs {
   // single-token down kernel after a one-pass route + gate/up dispatch: the
   // region whose call number it advances; else nullptr
   uint64_t* onepass;
+  // batched path under moe_layer: the plan kernel selects the top-k from these
+  // logits itself (writing ids and w) before it plans; else nullptr
+  const float* route_logits;
+  unsigned route_flags;  // MOE_ROUTE_RENORM
 };
 // The router side of moe_layer's one-pass single-token path.
 struct OnepassRoute {
@@ -166,6 +170,8 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, int stage, hipStream_t s);
 
 // small-batch kernels (2 <= T <= 32, shapes batched_supported admits)
 bool batched_supported(int T, int H, int I, int K);
+// the batched plan kernel can also select the top-k (FfnArgs::route_logits) for E experts
+bool batched_routes(int E);
 size_t batched_workspace_bytes(int T, int H, int I, int E, int K, int has_shared);
 hipError_t launch_ffn_batched(const FfnArgs& a, int stage, hipStream_t s);
 

@@ -214,17 +214,18 @@ def batched(n_sets: int) -> str:
     with torch.cuda.stream(stream):
         for _ in range(3):
             for Ly in sets:
-                run(Ly, stream)
+                run.layer(Ly, stream)
     stream.synchronize()
     clear(L)
     with torch.cuda.stream(stream):
         for Ly in sets:
-            run(Ly, stream)
+            run.layer(Ly, stream)
     stream.synchronize()
     if int(run.status.item()) != 0:
         raise RuntimeError(f"device status {int(run.status.item())}")
     units = len(set(run.ids.cpu().numpy().ravel().tolist()))
-    title = f"{w.name}, layer set {n_sets - 1} of {n_sets} ({units} distinct experts), after the other sets"
+    title = (f"{w.name}, layer set {n_sets - 1} of {n_sets} ({units} distinct experts), after the other sets; "
+             "one moe_layer call per set")
     return layer_report(L, ["route_select_kernel", "bat_plan_kernel", "bmx_gateup_kernel", "bmx_down_kernel",
                             "bat_combine_kernel"], title)
 

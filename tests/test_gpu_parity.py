@@ -284,13 +284,22 @@ def test_ffn_batched_shapes(w):
          False),
         (gen.Workload("dec_t1_h256_e512_k8_i512", 1, 256, 512, 8, 512, 1, 512, "normal", 33), False),
         (gen.Workload("t5_h256_e64_k4_i512", 5, 256, 64, 4, 512, 1, 64, "gemv", 34), False),
+        # batched path (2..32 tokens): moe_layer selects inside the plan kernel
+        (gen.Workload("bat_t16_h2048_e128_k8_i768", 16, 2048, 128, 8, 768, 1, 128, "normal", 35), False),
+        (gen.Workload("bat_t16_h2048_e128_k8_i768", 16, 2048, 128, 8, 768, 1, 128, "normal", 35), True),
+        (gen.Workload("bat_t32_h512_e512_k8_i256_shared", 32, 512, 512, 8, 256, 1, 512, "gemv", 36, shared=True),
+         False),
+        (gen.Workload("bat_t2_h256_e1024_k32_i256", 2, 256, 1024, 32, 256, 1, 1024, "normal", 37), True),
+        (gen.Workload("bat_t7_h256_e40_k3_i512", 7, 256, 40, 3, 512, 1, 40, "gemv", 38), False),
     ],
     ids=lambda v: v.name if hasattr(v, "name") else f"renorm{int(v)}",
 )
 def test_layer_equals_route_then_ffn_bitwise(w, renorm):
     """moe_layer gives the bits of moe_route followed by moe_expert_ffn: logits,
     ids, w and y, for one token and for several, with and without renormalised
-    weights, router GEMV or logits in, with and without a shared expert."""
+    weights, router GEMV or logits in, with and without a shared expert; on the
+    batched path (2..32 tokens) moe_layer's plan kernel does the selection itself
+    (E of 40 to 1024 experts, so every experts-per-lane width)."""
     layer = 3
     say(f"moe_layer {w.name} renorm={renorm}")
     xb = gen.activations_bf16(w.seed, layer, w.T, w.H)
