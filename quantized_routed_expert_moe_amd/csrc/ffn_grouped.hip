@@ -593,13 +593,24 @@ __global__ void __launch_bounds__(kGThreads, 2) grouped_gemm_kernel(FfnArgs a) {
   } else {
     _Float16* ows = reinterpret_cast<_Float16*>(a.ws + W.o);
     bool bad = false;
+    // every row's pair index first, in one batch: loaded between the stores, each
+    // load would wait for the stores before it (they might alias), 32 round trips
+    int prow[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i * 16 + 4 * (lane >> 4) + v;
+        prow[i][v] = sorted[td.row0 + (row < td.rows ? row : 0)];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = i * 16 + 4 * (lane >> 4) + v;
         if (i < nb_live && row < td.rows) {
-          const int p = sorted[td.row0 + row];
+          const int p = prow[i][v];
 #pragma unroll
           for (int n = 0; n < 4; ++n) {
             const int col = nt * kTN + wave * 64 + n * 16 + (lane & 15);
@@ -825,6 +836,16 @@ __global__ void __launch_bounds__(kGThreads, 2) fmt_gemm_kernel(FfnArgs a) {
     }
   } else {
     _Float16* ows = reinterpret_cast<_Float16*>(a.ws + W.o);
+    // the rows' pair indices in one batch before the stores (as in the int4 GEMM)
+    int prow[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i * 16 + 4 * q + v;
+        prow[i][v] = sorted[td.row0 + (row < td.rows ? row : 0)];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -833,7 +854,7 @@ __global__ void __launch_bounds__(kGThreads, 2) fmt_gemm_kernel(FfnArgs a) {
         if (i < NB && row < td.rows) {
           const float ov = acc[0][i][v] * glob[0];
           bad |= !(fabsf(ov) < 65520.0f);  // o does not fit its fp16 store
-          ows[(size_t)sorted[td.row0 + row] * H + wr] = (_Float16)ov;
+          ows[(size_t)prow[i][v] * H + wr] = (_Float16)ov;
         }
       }
     }
