@@ -1,5 +1,5 @@
-// Prefill expert FFN: expert-grouped GEMMs on bf16 MFMA with LDS-staged
-// dequantised weight tiles.
+// Prefill expert FFN: expert-grouped GEMMs on fp16 MFMA with LDS-staged int4
+// weight tiles dequantised in registers.
 //
 // With many tokens per expert the FFN is a dense contraction per expert
 // ("Strata on a Mac", Switches: the prompt's expert GEMMs), so it runs on the
@@ -10,7 +10,8 @@
 //      unit's blob address, and the scatter of pair indices into segments.
 //      The order of pairs inside a segment does not matter: every output row
 //      of an MFMA tile depends on its own A row only.
-//   2. convert: x (bf16) -> fp16 in the workspace. bf16 carries 8 significant
+//   2. convert (the plan kernel's other workgroups, while the plan runs): x
+//      (bf16) -> fp16 in the workspace. bf16 carries 8 significant
 //      bits, so every |x| in [2^-17, 65504] converts exactly; smaller values
 //      round to the fp16 subnormal grid (absolute error <= 2^-25), and a
 //      value that would overflow fp16 sets MOE_EUNSUP in the status word
@@ -112,7 +113,14 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return r;
 }
 
+__device__ void convert_x_f16(const FfnArgs& a, size_t first, size_t stride);
+
+// Block 0 plans; blocks 1 .. convert x to fp16 meanwhile (plan_grid blocks in all).
 __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
+  if (blockIdx.x > 0) {
+    convert_x_f16(a, (size_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x, (size_t)(gridDim.x - 1) * kPlanThreads);
+    return;
+  }
   __shared__ int cnt[kMaxE];
   __shared__ int seg[kMaxE];
   __shared__ int cur[kMaxE];
@@ -226,14 +234,16 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-__global__ void __launch_bounds__(256) to_f16_kernel(FfnArgs a) {
+// x (bf16) to fp16 pairs in the workspace, by threads first .. first + stride - 1
+// of a grid-stride loop
+__device__ void convert_x_f16(const FfnArgs& a, size_t first, size_t stride) {
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
   uint32_t* xh = reinterpret_cast<uint32_t*>(a.ws + W.xh);
   const size_t n2 = (size_t)a.T * a.H / 2;
   const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.x);
   bool bad = false;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n2; i += (size_t)gridDim.x * 256) {
+  for (size_t i = first; i < n2; i += stride) {
     const uint32_t v = xb[i];
     const float lo = __uint_as_float(v << 16), hi = __uint_as_float(v & 0xFFFF0000u);
     bad |= !(fabsf(lo) < 65520.0f) || !(fabsf(hi) < 65520.0f);
@@ -938,6 +948,13 @@ static bool grouped_offsets_fit(int T, int H, int I, int K, int has_shared) {
   return (size_t)T * H * 2 <= 0xFFFFFF00u && PA * I * 2 <= 0xFFFFFF00u;
 }
 
+// the plan workgroup plus the fp16 conversion blocks (at most 1024)
+inline int plan_grid(const FfnArgs& a) {
+  const size_t n2 = (size_t)a.T * a.H / 2;
+  const size_t cb = (n2 + kPlanThreads - 1) / kPlanThreads;
+  return 1 + (int)(cb < 1024 ? cb : 1024);
+}
+
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared) {
   if (!grouped_offsets_fit(T, H, I, K, has_shared)) return 0;  // unsupported: the caller reports it
   return grouped_ws(T, H, I, E, K, has_shared).bytes;
@@ -950,11 +967,7 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
   hipError_t e;
   if (stage == 0) {
-    hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t n2 = (size_t)a.T * a.H / 2;
-    const size_t cb = (n2 + 255) / 256;
-    hipLaunchKernelGGL(to_f16_kernel, dim3(cb < 4096 ? (int)cb : 4096), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(grouped_plan_kernel, dim3(plan_grid(a)), dim3(kPlanThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(round8(W.max_mt * gemm_n_tiles<0>(a.H, a.I))), dim3(kGThreads), 0, s, a);
     return hipGetLastError();
@@ -977,12 +990,8 @@ hipError_t launch_ffn_grouped_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
   const bool has_shared = a.shared_blob != nullptr;
   if (!grouped_offsets_fit(a.T, a.H, a.I, a.K, has_shared)) return hipErrorNotSupported;
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
-  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  hipLaunchKernelGGL(grouped_plan_kernel, dim3(plan_grid(a)), dim3(kPlanThreads), 0, s, a);
   hipError_t e;
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t n2 = (size_t)a.T * a.H / 2;
-  const size_t cb = (n2 + 255) / 256;
-  hipLaunchKernelGGL(to_f16_kernel, dim3(cb < 4096 ? (int)cb : 4096), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int g0 = round8(W.max_mt * (a.I / kFN)), g1 = round8(W.max_mt * (a.H / kFN));
   if (fmt == MOE_FMT_INT8_G32) {
