@@ -55,9 +55,19 @@ struct TileDesc {
 };
 
 struct GroupedWs {
-  size_t n_mt, tiles, ublob, unit_mt0, sorted, xh, h, o, done, bytes;
+  size_t n_mt, tiles, ublob, unit_mt0, sorted, xh, h, o, bh, done, bytes;
   int max_units, max_mt;
 };
+
+// The pairs are counted and scattered by up to kHistBlocks workgroups, each a
+// contiguous slice of at least kHistPairs pairs; the plan workgroup turns their
+// counts into segment offsets and a base per (workgroup, expert).
+constexpr int kHistBlocks = 64;
+constexpr int kHistPairs = 2048;
+__host__ __device__ inline int hist_blocks(size_t P) {
+  const size_t nb = (P + kHistPairs - 1) / kHistPairs;
+  return nb < 1 ? 1 : (nb > (size_t)kHistBlocks ? kHistBlocks : (int)nb);
+}
 
 // Partial passes (chunked paged prefill) record what they computed in the
 // workspace: done[e] (e < E) = 1 once expert e was computed by a pass of the
@@ -81,7 +91,8 @@ __host__ __device__ inline GroupedWs grouped_ws(int T, int H, int I, int E, int 
   w.xh = al256(w.sorted + PA * sizeof(int32_t));
   w.h = al256(w.xh + (size_t)T * H * 2);
   w.o = al256(w.h + PA * (size_t)I * 2);
-  w.done = al256(w.o + PA * (size_t)H * 2);  // o: fp16
+  w.bh = al256(w.o + PA * (size_t)H * 2);  // o: fp16
+  w.done = al256(w.bh + 2 * (size_t)kHistBlocks * E * sizeof(int32_t));  // bh: counts [NB][E], bases [NB][E]
   w.bytes = al256(w.done + ((size_t)E + 2) * sizeof(int32_t));
   return w;
 }
@@ -115,15 +126,57 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
 
 __device__ void convert_x_f16(const FfnArgs& a, size_t first, size_t stride);
 
-// Block 0 plans; blocks 1 .. convert x to fp16 meanwhile (plan_grid blocks in all).
-__global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
-  if (blockIdx.x > 0) {
-    convert_x_f16(a, (size_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x, (size_t)(gridDim.x - 1) * kPlanThreads);
+// The pair slice of workgroup b of the histogram and scatter kernels.
+__device__ inline void hist_slice(int P, int NB, int b, int* begin, int* end) {
+  const int per = (P + NB - 1) / NB;
+  *begin = b * per < P ? b * per : P;
+  *end = *begin + per < P ? *begin + per : P;
+}
+
+// Workgroups 0 .. NB-1 count the experts of their slice of pairs (NB = hist_blocks);
+// the others convert x to fp16 meanwhile.
+__global__ void __launch_bounds__(kPlanThreads) grouped_hist_kernel(FfnArgs a) {
+  const int T = a.T, K = a.K, E = a.E, P = T * K;
+  const int NB = hist_blocks((size_t)P);
+  if ((int)blockIdx.x >= NB) {
+    convert_x_f16(a, (size_t)(blockIdx.x - NB) * kPlanThreads + threadIdx.x, (size_t)(gridDim.x - NB) * kPlanThreads);
     return;
   }
   __shared__ int cnt[kMaxE];
-  __shared__ int seg[kMaxE];
-  __shared__ int cur[kMaxE];
+  const GroupedWs W = grouped_ws(T, a.H, a.I, E, K, a.shared_blob != nullptr);
+  int32_t* bh = reinterpret_cast<int32_t*>(a.ws + W.bh);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
+  __syncthreads();
+  int p_begin, p_end;
+  hist_slice(P, NB, blockIdx.x, &p_begin, &p_end);
+  // eight pairs per thread and round, their ids loaded before any is used
+  for (int p0 = p_begin + tid; p0 < p_end; p0 += 8 * kPlanThreads) {
+    int ev[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j * kPlanThreads;
+      ev[j] = p < p_end ? a.ids[p] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (p0 + j * kPlanThreads < p_end) {
+        const int e = ev[j];
+        if (e >= 0 && e < E)
+          atomicAdd(&cnt[e], 1);
+        else
+          *a.status = MOE_EINVAL;
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) bh[blockIdx.x * E + e] = cnt[e];
+}
+
+// One workgroup: segments, tiles and unit records from the histogram workgroups'
+// counts, and the base of every (histogram workgroup, expert) for the scatter.
+__global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
+  __shared__ int cnt[kMaxE];
   __shared__ int wsum[kPlanThreads / 64];
   __shared__ int total;
   const int T = a.T, K = a.K, E = a.E;
@@ -136,26 +189,20 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
   int32_t* sorted = reinterpret_cast<int32_t*>(a.ws + W.sorted);
   const int tid = threadIdx.x;
   const int P = T * K;
-  for (int e = tid; e < kMaxE; e += kPlanThreads) cnt[e] = 0;
-  __syncthreads();
-  // eight pairs per thread and round, their ids loaded before any is used
-  for (int p0 = tid; p0 < P; p0 += 8 * kPlanThreads) {
-    int ev[8];
+  const int NB = hist_blocks((size_t)P);
+  int32_t* bh = reinterpret_cast<int32_t*>(a.ws + W.bh);
+  // expert e's count: the sum over the histogram workgroups (E <= kPlanThreads:
+  // one expert per thread), sixteen loads in flight at a time
+  {
+    int c = 0;
+    for (int b0 = 0; b0 < NB; b0 += 16) {
+      int v[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int p = p0 + j * kPlanThreads;
-      ev[j] = p < P ? a.ids[p] : 0;
-    }
+      for (int j = 0; j < 16; ++j) v[j] = (tid < E && b0 + j < NB) ? bh[(b0 + j) * E + tid] : 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (p0 + j * kPlanThreads < P) {
-        const int e = ev[j];
-        if (e >= 0 && e < E)
-          atomicAdd(&cnt[e], 1);
-        else
-          *a.status = MOE_EINVAL;
-      }
+      for (int j = 0; j < 16; ++j) c += v[j];
     }
+    if (tid < E) cnt[tid] = c;
   }
   __syncthreads();
   const int base_rows = has_shared ? T : 0;  // the shared unit's rows come first
@@ -185,8 +232,6 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
     }
   }
   if (tid < E) {
-    seg[tid] = row0;
-    cur[tid] = 0;
     if (c > 0) {
       if (slot < 0 && !partial) *a.status = MOE_ENOTRES;
       ublob[uidx] = slot < 0 ? nullptr : a.slots + (size_t)slot * a.stride;
@@ -213,19 +258,56 @@ __global__ void __launch_bounds__(kPlanThreads) grouped_plan_kernel(FfnArgs a) {
     n_mt[1] = n_units;
     unit_mt0[n_units] = shared_mt + total;
   }
+  // bases: histogram workgroup b places its pairs of expert e from the segment
+  // start + the counts of workgroups 0 .. b-1 (sixteen counts loaded before their
+  // bases are stored: a load after a store to the same array waits for it)
+  if (tid < E) {
+    int run = row0;
+    for (int b0 = 0; b0 < NB; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = b0 + j < NB ? bh[(b0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < NB) bh[(kHistBlocks + b0 + j) * E + tid] = run;
+        run += v[j];
+      }
+    }
+  }
+}
+
+// Workgroup b (of hist_blocks) writes the pair indices of its slice into their
+// experts' segments of `sorted`, from its bases; the order inside a segment
+// follows the LDS atomics (any order serves, as every output row of a GEMM tile
+// depends on its own A row only).
+__global__ void __launch_bounds__(kPlanThreads) grouped_scatter_kernel(FfnArgs a) {
+  __shared__ int cur[kMaxE];
+  const int T = a.T, K = a.K, E = a.E, P = T * K;
+  const int NB = hist_blocks((size_t)P);
+  const GroupedWs W = grouped_ws(T, a.H, a.I, E, K, a.shared_blob != nullptr);
+  const int32_t* base = reinterpret_cast<const int32_t*>(a.ws + W.bh) + (size_t)(kHistBlocks + blockIdx.x) * E;
+  int32_t* sorted = reinterpret_cast<int32_t*>(a.ws + W.sorted);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) cur[e] = base[e];
   __syncthreads();
-  for (int p0 = tid; p0 < P; p0 += 8 * kPlanThreads) {
+  int p_begin, p_end;
+  hist_slice(P, NB, blockIdx.x, &p_begin, &p_end);
+  for (int p0 = p_begin + tid; p0 < p_end; p0 += 8 * kPlanThreads) {
     int ev[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int p = p0 + j * kPlanThreads;
-      ev[j] = p < P ? a.ids[p] : -1;
+      ev[j] = p < p_end ? a.ids[p] : -1;
     }
+    int at[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int e = ev[j];
-      if (e >= 0 && e < E) sorted[seg[e] + atomicAdd(&cur[e], 1)] = p0 + j * kPlanThreads;
+      at[j] = (e >= 0 && e < E) ? atomicAdd(&cur[e], 1) : -1;
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (at[j] >= 0) sorted[at[j]] = p0 + j * kPlanThreads;
   }
 }
 
@@ -235,20 +317,39 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // x (bf16) to fp16 pairs in the workspace, by threads first .. first + stride - 1
-// of a grid-stride loop
+// of a grid-stride loop over 16-byte pieces (T * H is a multiple of 8: H is a
+// multiple of 64). Each round loads kConvRound pieces before it stores any: a
+// load after a store would wait for it (the pointers might alias).
+constexpr int kConvRound = 4;
 __device__ void convert_x_f16(const FfnArgs& a, size_t first, size_t stride) {
   const bool has_shared = a.shared_blob != nullptr;
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
-  uint32_t* xh = reinterpret_cast<uint32_t*>(a.ws + W.xh);
-  const size_t n2 = (size_t)a.T * a.H / 2;
-  const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.x);
+  uint4* __restrict__ xh = reinterpret_cast<uint4*>(a.ws + W.xh);
+  const size_t n8 = (size_t)a.T * a.H / 8;
+  const uint4* __restrict__ xb = reinterpret_cast<const uint4*>(a.x);
   bool bad = false;
-  for (size_t i = first; i < n2; i += stride) {
-    const uint32_t v = xb[i];
-    const float lo = __uint_as_float(v << 16), hi = __uint_as_float(v & 0xFFFF0000u);
-    bad |= !(fabsf(lo) < 65520.0f) || !(fabsf(hi) < 65520.0f);
-    const f16x2 h = {(_Float16)lo, (_Float16)hi};
-    xh[i] = __builtin_bit_cast(uint32_t, h);
+  for (size_t i0 = first; i0 < n8; i0 += stride * kConvRound) {
+    uint4 v[kConvRound];
+#pragma unroll
+    for (int r = 0; r < kConvRound; ++r) {
+      const size_t i = i0 + (size_t)r * stride;
+      v[r] = xb[i < n8 ? i : 0];
+    }
+#pragma unroll
+    for (int r = 0; r < kConvRound; ++r) {
+      const size_t i = i0 + (size_t)r * stride;
+      if (i >= n8) continue;
+      const uint32_t d[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float lo = __uint_as_float(d[c] << 16), hi = __uint_as_float(d[c] & 0xFFFF0000u);
+        bad |= !(fabsf(lo) < 65520.0f) || !(fabsf(hi) < 65520.0f);
+        const f16x2 h = {(_Float16)lo, (_Float16)hi};
+        o[c] = __builtin_bit_cast(uint32_t, h);
+      }
+      xh[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
   if (bad) *a.status = MOE_EUNSUP;
 }
@@ -948,11 +1049,20 @@ static bool grouped_offsets_fit(int T, int H, int I, int K, int has_shared) {
   return (size_t)T * H * 2 <= 0xFFFFFF00u && PA * I * 2 <= 0xFFFFFF00u;
 }
 
-// the plan workgroup plus the fp16 conversion blocks (at most 1024)
-inline int plan_grid(const FfnArgs& a) {
-  const size_t n2 = (size_t)a.T * a.H / 2;
-  const size_t cb = (n2 + kPlanThreads - 1) / kPlanThreads;
-  return 1 + (int)(cb < 1024 ? cb : 1024);
+// The plan in three launches: counts (with the fp16 conversion of x in the same
+// grid, a 16-byte piece per thread and round, at most 256 workgroups), the
+// one-workgroup plan, the scatter.
+inline hipError_t launch_grouped_plan(const FfnArgs& a, hipStream_t s) {
+  const int nb = hist_blocks((size_t)a.T * a.K);
+  const size_t n8 = (size_t)a.T * a.H / 8;
+  const size_t cb = (n8 + (size_t)kPlanThreads * kConvRound - 1) / ((size_t)kPlanThreads * kConvRound);
+  hipLaunchKernelGGL(grouped_hist_kernel, dim3(nb + (int)(cb < 256 ? cb : 256)), dim3(kPlanThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(grouped_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(grouped_scatter_kernel, dim3(nb), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 size_t grouped_workspace_bytes(int T, int H, int I, int E, int K, int has_shared) {
@@ -967,8 +1077,7 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int stage, hipStream_t s) {
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
   hipError_t e;
   if (stage == 0) {
-    hipLaunchKernelGGL(grouped_plan_kernel, dim3(plan_grid(a)), dim3(kPlanThreads), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_grouped_plan(a, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((grouped_gemm_kernel<0>), dim3(round8(W.max_mt * gemm_n_tiles<0>(a.H, a.I))), dim3(kGThreads), 0, s, a);
     return hipGetLastError();
   }
@@ -990,9 +1099,8 @@ hipError_t launch_ffn_grouped_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
   const bool has_shared = a.shared_blob != nullptr;
   if (!grouped_offsets_fit(a.T, a.H, a.I, a.K, has_shared)) return hipErrorNotSupported;
   const GroupedWs W = grouped_ws(a.T, a.H, a.I, a.E, a.K, has_shared);
-  hipLaunchKernelGGL(grouped_plan_kernel, dim3(plan_grid(a)), dim3(kPlanThreads), 0, s, a);
   hipError_t e;
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_grouped_plan(a, s)) != hipSuccess) return e;
   const int g0 = round8(W.max_mt * (a.I / kFN)), g1 = round8(W.max_mt * (a.H / kFN));
   if (fmt == MOE_FMT_INT8_G32) {
     hipLaunchKernelGGL((fmt_gemm_kernel<MOE_FMT_INT8_G32, 0>), dim3(g0), dim3(kGThreads), 0, s, a);
