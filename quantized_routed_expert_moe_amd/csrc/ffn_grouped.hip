@@ -1117,8 +1117,10 @@ hipError_t launch_ffn_grouped_fmt(int fmt, const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_grouped_combine(const FfnArgs& a, hipStream_t s) {
   const size_t n8 = (size_t)a.T * a.H / 8;
+  // one output piece per thread where the grid allows: a thread's second piece
+  // would load after its first store and wait for it (the buffers might alias)
   const size_t blocks = (n8 + 255) / 256;
-  hipLaunchKernelGGL(grouped_combine_kernel, dim3(blocks < 8192 ? (int)blocks : 8192), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(grouped_combine_kernel, dim3(blocks < (1u << 20) ? (int)blocks : (1 << 20)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(a.mode & kModeCheckDone)) return e;
   // close the chunk's session: the next chunk must start with a first pass
