@@ -54,6 +54,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;
+
+// Expert codes and scales are read once per token: their loads carry the
+// non-temporal hint, so that the streamed weights do not evict from the caches
+// what the next dispatches read again (router weights, x, h, the hand-off words).
+typedef unsigned int StreamU32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_u4(const uint8_t* p) {
+  const StreamU32x4 v = __builtin_nontemporal_load(reinterpret_cast<const StreamU32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t stream_u32(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 // Blob of unit u (u = 0 is the shared expert when present) or nullptr with the
 // status word set; ids = the token's routed experts in rank order.
 // With pre_slots (moe_layer) the routing kernel has resolved the slots already:
@@ -200,11 +212,11 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
     int j = j0 + (jl < gw_here ? jl : gw_here - 1);
     j = j < 0 ? 0 : (j < G ? j : G - 1);
     const size_t co = code_off(n, j, G, kRowBlockGU);  // 8 rows x 8 groups: 1 KB contiguous per wave
-    cg[i] = *reinterpret_cast<const uint4*>(src + BL.gate_codes + co);
-    cu[i] = *reinterpret_cast<const uint4*>(src + BL.up_codes + co);
+    cg[i] = stream_u4(src + BL.gate_codes + co);
+    cu[i] = stream_u4(src + BL.up_codes + co);
     const size_t sd = scale_off(n, j, G, kRowBlockGU) >> 2;  // dword holding the scale
-    sgw[i] = reinterpret_cast<const uint32_t*>(src + BL.gate_scales)[sd];
-    suw[i] = reinterpret_cast<const uint32_t*>(src + BL.up_scales)[sd];
+    sgw[i] = stream_u32(src + BL.gate_scales + 4 * sd);
+    suw[i] = stream_u32(src + BL.up_scales + 4 * sd);
   }
   __builtin_amdgcn_sched_barrier(0);  // every load is issued before the steps
   tl_mark(tl, 4);
@@ -458,8 +470,8 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
       const uint8_t* src = (has_shared && uc == 0) ? a.shared_blob : a.slots + (size_t)(sl > 0 ? sl : 0) * a.stride;
       const int j = jc + p;
       // 4 rows x 16 groups: 1 KB of contiguous codes per wave
-      cd[i] = *reinterpret_cast<const uint4*>(src + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
-      sdw[i] = reinterpret_cast<const uint32_t*>(src + BL.down_scales)[scale_off(n, j, Gd, kRowBlockDN) >> 2];
+      cd[i] = stream_u4(src + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
+      sdw[i] = stream_u32(src + BL.down_scales + (scale_off(n, j, Gd, kRowBlockDN) & ~(size_t)3));
       js += 16;
       if (js >= Gd) {
         js -= Gd;
