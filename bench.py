@@ -18,6 +18,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -993,6 +994,12 @@ def main():
 
     lib.load()
     dev = "cuda:0"
+    # The cyclic garbage collector runs only between legs (gc.collect() before
+    # each): a full pass over a process holding torch takes tens of milliseconds,
+    # and one that started inside a timed region would stall the host while the
+    # GPU drains its queue.
+    gc.collect()
+    gc.disable()
     legs = set(a.legs.split(","))
     if a.copy_probe_mib:
         src = torch.empty(a.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -1003,6 +1010,7 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written")
         del src, dst
+    gc.collect()
     w, d = decode_leg(a, dev)
     traffic = decode_traffic()
     probe_gbs = hbm_read_probe(dev)
@@ -1066,6 +1074,7 @@ def main():
     }
     torch.cuda.empty_cache()
     if "prefill" in legs:
+        gc.collect()
         wp, p = prefill_leg(a, dev)
         out["workloads"]["prefill"] = {
             "workload": wp.name,
@@ -1082,6 +1091,7 @@ def main():
         }
         torch.cuda.empty_cache()
     if "batched" in legs:
+        gc.collect()
         wb, b = batched_leg(a, dev)
         out["workloads"]["batched"] = {
             "workload": wb.name,
@@ -1092,9 +1102,11 @@ def main():
             "hbm_frac": round(b["hbm_gbs"] / HBM_PEAK_GBS, 4),
         }
     if "route_variants" in legs:
+        gc.collect()
         out["workloads"]["route_variants"] = {"experts": 256, "top_k": 8, "from": "logits"} | route_variants_leg(dev)
     if "paged" in legs:
         torch.cuda.empty_cache()
+        gc.collect()
         wq, q = paged_leg(a, dev)
         out["workloads"]["paged"] = {
             "workload": wq.name,
@@ -1116,14 +1128,17 @@ def main():
         }
     if "readahead" in legs:
         torch.cuda.empty_cache()
+        gc.collect()
         wr, r = readahead_leg(a, dev)
         out["workloads"]["readahead_paged"] = {"workload": wr.name, "predictor": "next layer's router on this "
                                                "layer's input, top-P", "residual_stream": {"a": 0.99, "rho": 0.15}} | r
     if "formats" in legs:
+        gc.collect()
         out["workloads"]["formats"] = {"workload": "decode_t1_h4096_e256_k8_i1536 expert FFN per weight format",
                                        "by_format": formats_leg(dev)}
     if "chunked" in legs:
         torch.cuda.empty_cache()
+        gc.collect()
         wc, c = chunked_leg(a, dev)
         out["workloads"]["chunked_paged_prefill"] = {"workload": wc.name, "arena_slots": wc.slots,
                                                      "experts_per_pass": wc.slots // 2, "by_chunk": c}

@@ -262,12 +262,16 @@ __device__ inline f16x8_t dequant_qs(uint32_t cw, _Float16 sc) {
   return __builtin_bit_cast(f16x8_t, make_uint4(b[0], b[1], b[2], b[3]));
 }
 __device__ inline f16x8_t as_f16x8(const uint4& v) { return __builtin_bit_cast(f16x8_t, v); }
-// Buffer loads (a read past the descriptor's range returns zeros)
+// Buffer loads of expert codes and scales (a read past the descriptor's range
+// returns zeros). Each unit's weights are read once per layer, so the loads
+// carry the non-temporal hint (cache-policy bit 1, nt) and leave the caches to
+// the data that is read again (x, the plan records, h).
+constexpr int kStreamPolicy = 2;
 __device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamPolicy));
 }
 __device__ inline uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStreamPolicy);
 }
 __device__ inline uint32_t dword_of(const uint4& v, int i) { return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w)); }
 
