@@ -95,33 +95,61 @@ __device__ inline const uint8_t* fmt_pair_blob(const FfnArgs& a, int p) {
   return a.slots + (size_t)slot * a.stride;
 }
 
-// Stage n activations (fp32 or bf16 source) as fp16 pairs into xs, and per chunk
-// the sum of its fp16 values times the code offset 1152.
+// Activation staging in two halves, so that a workgroup's weight loads are in
+// flight while its activations are converted: act_load fetches one chunk of C
+// activations (fp32 or bf16 source) per thread into registers (every supported
+// row has at most 256 chunks, one per thread: fmt_shape_ok), act_stage writes
+// them into xs as fp16 pairs and, per chunk, the sum of its fp16 values times
+// the code offset 1152 (int8).
 template <int FMT, typename Src>
-__device__ inline void stage_act(const Src* src, int n, uint32_t* xs, float* corr, int32_t* status) {
+struct ActChunk {
+  static constexpr int kWords = Fmt<FMT>::kCols * (int)sizeof(Src) / 16;  // 16-byte words per chunk
+  uint4 v[kWords];
+};
+static_assert(kFThreads == 256, "one activation chunk per thread covers 256 chunks");
+
+template <int FMT, typename Src>
+__device__ inline void act_load(const Src* src, int n, ActChunk<FMT, Src>& ch) {
   constexpr int C = Fmt<FMT>::kCols;
-  const int n_chunks = n / C;
-  bool bad = false;
-  for (int c = threadIdx.x; c < n_chunks; c += kFThreads) {
-    float ca = 0.0f;
+  const int c = (int)threadIdx.x < n / C ? (int)threadIdx.x : 0;  // threads past the row reload chunk 0
+  const uint4* q = reinterpret_cast<const uint4*>(src + (size_t)c * C);
 #pragma unroll
-    for (int j = 0; j < C; j += 2) {
-      float v0, v1;
-      if constexpr (sizeof(Src) == 2) {
-        const uint32_t b = reinterpret_cast<const uint32_t*>(src)[(c * C + j) / 2];
-        v0 = __uint_as_float(b << 16);
-        v1 = __uint_as_float(b & 0xFFFF0000u);
-      } else {
-        v0 = src[c * C + j];
-        v1 = src[c * C + j + 1];
-      }
-      const uint32_t h0 = to_f16_bits(v0, &bad), h1 = to_f16_bits(v1, &bad);
-      xs[(c * C + j) / 2] = h0 | (h1 << 16);
-      ca += f16_lo(h0) + f16_lo(h1);
+  for (int i = 0; i < ActChunk<FMT, Src>::kWords; ++i) ch.v[i] = q[i];
+}
+
+template <int FMT, typename Src>
+__device__ inline void act_stage(const ActChunk<FMT, Src>& ch, int n, uint32_t* xs, float* corr, int32_t* status) {
+  constexpr int C = Fmt<FMT>::kCols;
+  const int c = threadIdx.x;
+  if (c >= n / C) return;
+  const uint32_t* d = reinterpret_cast<const uint32_t*>(ch.v);  // the chunk's dwords, in order
+  bool bad = false;
+  float ca = 0.0f;
+#pragma unroll
+  for (int j = 0; j < C; j += 2) {
+    float v0, v1;
+    if constexpr (sizeof(Src) == 2) {
+      const uint32_t b = d[j / 2];
+      v0 = __uint_as_float(b << 16);
+      v1 = __uint_as_float(b & 0xFFFF0000u);
+    } else {
+      v0 = __uint_as_float(d[j]);
+      v1 = __uint_as_float(d[j + 1]);
     }
-    corr[c] = FMT == MOE_FMT_INT8_G32 ? 1152.0f * ca : 0.0f;
+    const uint32_t h0 = to_f16_bits(v0, &bad), h1 = to_f16_bits(v1, &bad);
+    xs[(c * C + j) / 2] = h0 | (h1 << 16);
+    ca += f16_lo(h0) + f16_lo(h1);
   }
+  corr[c] = FMT == MOE_FMT_INT8_G32 ? 1152.0f * ca : 0.0f;
   if (bad) *status = MOE_EUNSUP;
+}
+
+// Workgroup barrier that orders LDS only: the weight loads still in flight are
+// not waited for (a full fence would wait for every outstanding global load).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // NVFP4: the two groups' sums (columns 0..15 and 16..31 of the chunk). Byte b of
@@ -167,29 +195,44 @@ __host__ __device__ inline size_t row_bytes(int cols) {
   return (size_t)cols / Fmt<FMT>::kCols * 16;
 }
 
-// One wave: S row streams (codes rows, scale rows) over cols columns against the
-// staged activations; lane l takes chunks l, l + 64, ...; returns the full dot
-// products on every lane.
+// One wave: S row streams (codes rows, scale rows) over cols columns; lane l
+// takes chunks l, l + 64, ... rows_load issues every code and scale load of the
+// wave (codes with the non-temporal hint: an expert's weights are read once per
+// token), rows_dot takes the dot products against the staged activations and
+// returns them on every lane.
 // (scales: fp16 [cols / 32] per row for int8, E4M3 bytes [cols / 16] for NVFP4)
+typedef unsigned int FmtU32x4 __attribute__((ext_vector_type(4)));
 template <int FMT, int S, int STEPS>
-__device__ inline void rows_dot(const uint8_t* const (&codes)[S], const uint8_t* const (&scales)[S], int cols,
-                                const uint32_t* xs, const float* corr, float scale_mask, int lane, float (&out)[S]) {
-  constexpr int C = Fmt<FMT>::kCols;
-  const int n_chunks = cols / C;
+struct RowWords {
   uint4 cw[S][STEPS];
   uint32_t sr[S][STEPS];  // int8: the fp16 scale; NVFP4: the chunk's two E4M3 scales
+};
+
+template <int FMT, int S, int STEPS>
+__device__ inline void rows_load(const uint8_t* const (&codes)[S], const uint8_t* const (&scales)[S], int cols,
+                                 int lane, RowWords<FMT, S, STEPS>& rw) {
+  constexpr int C = Fmt<FMT>::kCols;
+  const int n_chunks = cols / C;
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
       int c = i * 64 + lane;
       c = c < n_chunks ? c : n_chunks - 1;  // a real chunk, scaled by 0 below
-      cw[s][i] = *reinterpret_cast<const uint4*>(codes[s] + (size_t)c * 16);
+      const FmtU32x4 v = __builtin_nontemporal_load(reinterpret_cast<const FmtU32x4*>(codes[s] + (size_t)c * 16));
+      rw.cw[s][i] = make_uint4(v.x, v.y, v.z, v.w);
       if (FMT == MOE_FMT_INT8_G32)
-        sr[s][i] = reinterpret_cast<const uint16_t*>(scales[s])[(size_t)c * C / Fmt<FMT>::kG];
+        rw.sr[s][i] = reinterpret_cast<const uint16_t*>(scales[s])[(size_t)c * C / Fmt<FMT>::kG];
       else
-        sr[s][i] = reinterpret_cast<const uint16_t*>(scales[s])[c];  // groups 2c, 2c + 1
+        rw.sr[s][i] = reinterpret_cast<const uint16_t*>(scales[s])[c];  // groups 2c, 2c + 1
     }
+}
+
+template <int FMT, int S, int STEPS>
+__device__ inline void rows_dot(const RowWords<FMT, S, STEPS>& rw, int cols, const uint32_t* xs, const float* corr,
+                                float scale_mask, int lane, float (&out)[S]) {
+  constexpr int C = Fmt<FMT>::kCols;
+  const int n_chunks = cols / C;
 #pragma unroll
   for (int s = 0; s < S; ++s) out[s] = 0.0f;
 #pragma unroll
@@ -203,13 +246,13 @@ __device__ inline void rows_dot(const uint8_t* const (&codes)[S], const uint8_t*
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       if constexpr (FMT == MOE_FMT_INT8_G32) {
-        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[s][i]);
-        out[s] = fmaf(sc * k, chunk_dot<FMT>(cw[s][i], xp) - cr, out[s]);
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)rw.sr[s][i]);
+        out[s] = fmaf(sc * k, chunk_dot<FMT>(rw.cw[s][i], xp) - cr, out[s]);
       } else {
         float d0, d1;
-        chunk_dot_nvfp4(cw[s][i], xp, d0, d1);
-        out[s] = fmaf(e4m3_to_f32<0>(sr[s][i]) * k, d0, out[s]);
-        out[s] = fmaf(e4m3_to_f32<1>(sr[s][i]) * k, d1, out[s]);
+        chunk_dot_nvfp4(rw.cw[s][i], xp, d0, d1);
+        out[s] = fmaf(e4m3_to_f32<0>(rw.sr[s][i]) * k, d0, out[s]);
+        out[s] = fmaf(e4m3_to_f32<1>(rw.sr[s][i]) * k, d1, out[s]);
       }
     }
   }
@@ -226,9 +269,11 @@ __global__ void __launch_bounds__(kFThreads) fmt_gateup_kernel(FfnArgs a) {
   const int n_rb = I / kRowsPerItem;
   const int p = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
   const int t = p < P ? p / K : p - P;
+  // order of the loads: x (its chunk per thread), the pair's slot, every weight
+  // load; x is converted into LDS while the weights stream
+  ActChunk<FMT, uint16_t> xc;
+  act_load<FMT>(a.x + (size_t)t * H, H, xc);
   const uint8_t* blob = fmt_pair_blob(a, p);
-  stage_act<FMT>(a.x + (size_t)t * H, H, xs, corr, a.status);
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const FmtLayout L = fmt_layout(FMT, H, I);
   const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
@@ -239,8 +284,12 @@ __global__ void __launch_bounds__(kFThreads) fmt_gateup_kernel(FfnArgs a) {
                                    src + L.up_codes + n0 * rbytes, src + L.up_codes + (n0 + 1) * rbytes};
   const uint8_t* const scales[4] = {src + L.gate_scales + n0 * sbytes, src + L.gate_scales + (n0 + 1) * sbytes,
                                     src + L.up_scales + n0 * sbytes, src + L.up_scales + (n0 + 1) * sbytes};
+  RowWords<FMT, 4, STEPS> rw;
+  rows_load<FMT, 4, STEPS>(codes, scales, H, lane, rw);
+  act_stage<FMT>(xc, H, xs, corr, a.status);
+  lds_barrier();
   float r[4];
-  rows_dot<FMT, 4, STEPS>(codes, scales, H, xs, corr, blob ? 1.0f : 0.0f, lane, r);
+  rows_dot<FMT, 4, STEPS>(rw, H, xs, corr, blob ? 1.0f : 0.0f, lane, r);
   if (FMT == MOE_FMT_NVFP4) {  // per-tensor global scales of gate and up
     const float* gl = reinterpret_cast<const float*>(src + L.globals);
     const float gg = gl[0], gu = gl[1];
@@ -265,9 +314,9 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
   float* corr = reinterpret_cast<float*>(smem + (size_t)I * 2);
   const int n_rb = H / kRowsPerItem;
   const int p = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  ActChunk<FMT, float> hc;
+  act_load<FMT>(reinterpret_cast<const float*>(a.ws + W.h) + (size_t)p * I, I, hc);
   const uint8_t* blob = fmt_pair_blob(a, p);
-  stage_act<FMT>(reinterpret_cast<const float*>(a.ws + W.h) + (size_t)p * I, I, hs, corr, a.status);
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const FmtLayout L = fmt_layout(FMT, H, I);
   const uint8_t* src = blob ? blob : a.slots;
@@ -276,8 +325,12 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
   const size_t sbytes = (size_t)I / Fmt<FMT>::kG * (FMT == MOE_FMT_INT8_G32 ? 2 : 1);
   const uint8_t* const codes[2] = {src + L.down_codes + n0 * rbytes, src + L.down_codes + (n0 + 1) * rbytes};
   const uint8_t* const scales[2] = {src + L.down_scales + n0 * sbytes, src + L.down_scales + (n0 + 1) * sbytes};
+  RowWords<FMT, 2, STEPS> rw;
+  rows_load<FMT, 2, STEPS>(codes, scales, I, lane, rw);
+  act_stage<FMT>(hc, I, hs, corr, a.status);
+  lds_barrier();
   float r[2];
-  rows_dot<FMT, 2, STEPS>(codes, scales, I, hs, corr, blob ? 1.0f : 0.0f, lane, r);
+  rows_dot<FMT, 2, STEPS>(rw, I, hs, corr, blob ? 1.0f : 0.0f, lane, r);
   if (FMT == MOE_FMT_NVFP4) {
     const float gd = reinterpret_cast<const float*>(src + L.globals)[2];
     r[0] *= gd;
