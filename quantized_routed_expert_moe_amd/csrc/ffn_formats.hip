@@ -72,8 +72,8 @@ struct FmtWs {
 __host__ __device__ inline FmtWs fmt_ws(int T, int H, int I, int K, int has_shared) {
   const size_t PA = (size_t)T * K + (has_shared ? T : 0);
   FmtWs w;
-  w.h = 0;
-  w.o = fmt_al256(PA * I * 4);
+  w.h = 0;  // fp16 h [PA][I]
+  w.o = fmt_al256(PA * I * 2);
   w.bytes = fmt_al256(w.o + PA * H * 4);
   return w;
 }
@@ -97,51 +97,44 @@ __device__ inline const uint8_t* fmt_pair_blob(const FfnArgs& a, int p) {
 
 // Activation staging in two halves, so that a workgroup's weight loads are in
 // flight while its activations are converted: act_load fetches one chunk of C
-// activations (fp32 or bf16 source) per thread into registers (every supported
-// row has at most 256 chunks, one per thread: fmt_shape_ok), act_stage writes
-// them into xs as fp16 pairs and, per chunk, the sum of its fp16 values times
-// the code offset 1152 (int8).
-template <int FMT, typename Src>
+// activations into registers, act_stage writes them into xs as fp16 pairs and,
+// per chunk, the sum of its fp16 values times the code offset 1152 (int8).
+// Sources: bf16 x (converted, a value past the fp16 range sets MOE_EUNSUP) or
+// the fp16 h that the gate/up kernel wrote (copied).
+template <int FMT>
 struct ActChunk {
-  static constexpr int kWords = Fmt<FMT>::kCols * (int)sizeof(Src) / 16;  // 16-byte words per chunk
+  static constexpr int kWords = Fmt<FMT>::kCols * 2 / 16;  // 16-byte words per chunk of 16-bit values
   uint4 v[kWords];
 };
 static_assert(kFThreads == 256, "one activation chunk per thread covers 256 chunks");
 
-template <int FMT, typename Src>
-__device__ inline void act_load(const Src* src, int n, ActChunk<FMT, Src>& ch) {
-  constexpr int C = Fmt<FMT>::kCols;
-  const int c = (int)threadIdx.x < n / C ? (int)threadIdx.x : 0;  // threads past the row reload chunk 0
-  const uint4* q = reinterpret_cast<const uint4*>(src + (size_t)c * C);
+// chunk c of the row at src (c is a real chunk)
+template <int FMT>
+__device__ inline void act_load(const uint16_t* src, int c, ActChunk<FMT>& ch) {
+  const uint4* q = reinterpret_cast<const uint4*>(src + (size_t)c * Fmt<FMT>::kCols);
 #pragma unroll
-  for (int i = 0; i < ActChunk<FMT, Src>::kWords; ++i) ch.v[i] = q[i];
+  for (int i = 0; i < ActChunk<FMT>::kWords; ++i) ch.v[i] = q[i];
 }
 
-template <int FMT, typename Src>
-__device__ inline void act_stage(const ActChunk<FMT, Src>& ch, int n, uint32_t* xs, float* corr, int32_t* status) {
+// chunk c into xs (fp16 pairs of the row) and corr[c]
+template <int FMT, bool F16>
+__device__ inline void act_stage(const ActChunk<FMT>& ch, int c, uint32_t* xs, float* corr, bool* bad) {
   constexpr int C = Fmt<FMT>::kCols;
-  const int c = threadIdx.x;
-  if (c >= n / C) return;
   const uint32_t* d = reinterpret_cast<const uint32_t*>(ch.v);  // the chunk's dwords, in order
-  bool bad = false;
   float ca = 0.0f;
 #pragma unroll
   for (int j = 0; j < C; j += 2) {
-    float v0, v1;
-    if constexpr (sizeof(Src) == 2) {
-      const uint32_t b = d[j / 2];
-      v0 = __uint_as_float(b << 16);
-      v1 = __uint_as_float(b & 0xFFFF0000u);
+    uint32_t hp;
+    if constexpr (F16) {
+      hp = d[j / 2];
     } else {
-      v0 = __uint_as_float(d[j]);
-      v1 = __uint_as_float(d[j + 1]);
+      const uint32_t b = d[j / 2];
+      hp = to_f16_bits(__uint_as_float(b << 16), bad) | (to_f16_bits(__uint_as_float(b & 0xFFFF0000u), bad) << 16);
     }
-    const uint32_t h0 = to_f16_bits(v0, &bad), h1 = to_f16_bits(v1, &bad);
-    xs[(c * C + j) / 2] = h0 | (h1 << 16);
-    ca += f16_lo(h0) + f16_lo(h1);
+    xs[(c * C + j) / 2] = hp;
+    ca += f16_lo(hp) + f16_hi(hp);
   }
   corr[c] = FMT == MOE_FMT_INT8_G32 ? 1152.0f * ca : 0.0f;
-  if (bad) *status = MOE_EUNSUP;
 }
 
 // Workgroup barrier that orders LDS only: the weight loads still in flight are
@@ -271,8 +264,10 @@ __global__ void __launch_bounds__(kFThreads) fmt_gateup_kernel(FfnArgs a) {
   const int t = p < P ? p / K : p - P;
   // order of the loads: x (its chunk per thread), the pair's slot, every weight
   // load; x is converted into LDS while the weights stream
-  ActChunk<FMT, uint16_t> xc;
-  act_load<FMT>(a.x + (size_t)t * H, H, xc);
+  // (every supported row has at most 256 chunks, one per thread: fmt_shape_ok)
+  const int xc_i = (int)threadIdx.x < H / Fmt<FMT>::kCols ? (int)threadIdx.x : 0;
+  ActChunk<FMT> xc;
+  act_load<FMT>(a.x + (size_t)t * H, xc_i, xc);
   const uint8_t* blob = fmt_pair_blob(a, p);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const FmtLayout L = fmt_layout(FMT, H, I);
@@ -286,7 +281,8 @@ __global__ void __launch_bounds__(kFThreads) fmt_gateup_kernel(FfnArgs a) {
                                     src + L.up_scales + n0 * sbytes, src + L.up_scales + (n0 + 1) * sbytes};
   RowWords<FMT, 4, STEPS> rw;
   rows_load<FMT, 4, STEPS>(codes, scales, H, lane, rw);
-  act_stage<FMT>(xc, H, xs, corr, a.status);
+  bool bad = false;
+  if ((int)threadIdx.x < H / Fmt<FMT>::kCols) act_stage<FMT, false>(xc, threadIdx.x, xs, corr, &bad);
   lds_barrier();
   float r[4];
   rows_dot<FMT, 4, STEPS>(rw, H, xs, corr, blob ? 1.0f : 0.0f, lane, r);
@@ -298,10 +294,14 @@ __global__ void __launch_bounds__(kFThreads) fmt_gateup_kernel(FfnArgs a) {
     r[2] *= gu;
     r[3] *= gu;
   }
-  if (lane < 2) {
+  if (lane < 2) {  // h rounded to fp16 from its fp32 value, the operand of the down projection
     const float g = lane ? r[1] : r[0], u = lane ? r[3] : r[2];
-    reinterpret_cast<float*>(a.ws)[(size_t)p * I + n0 + lane] = silu(g) * u;
+    float hv = silu(g) * u;
+    asm volatile("" : "+v"(hv));  // keeps the fp32 rounding of the product (no fused fp32->fp16 multiply)
+    if (!(fabsf(hv) < 65520.0f)) bad = true;  // h does not fit fp16
+    reinterpret_cast<_Float16*>(a.ws)[(size_t)p * I + n0 + lane] = (_Float16)hv;
   }
+  if (bad) *a.status = MOE_EUNSUP;
 }
 
 template <int FMT, int STEPS>
@@ -314,8 +314,9 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
   float* corr = reinterpret_cast<float*>(smem + (size_t)I * 2);
   const int n_rb = H / kRowsPerItem;
   const int p = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
-  ActChunk<FMT, float> hc;
-  act_load<FMT>(reinterpret_cast<const float*>(a.ws + W.h) + (size_t)p * I, I, hc);
+  const int hc_i = (int)threadIdx.x < I / Fmt<FMT>::kCols ? (int)threadIdx.x : 0;
+  ActChunk<FMT> hc;
+  act_load<FMT>(reinterpret_cast<const uint16_t*>(a.ws + W.h) + (size_t)p * I, hc_i, hc);
   const uint8_t* blob = fmt_pair_blob(a, p);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const FmtLayout L = fmt_layout(FMT, H, I);
@@ -327,7 +328,7 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
   const uint8_t* const scales[2] = {src + L.down_scales + n0 * sbytes, src + L.down_scales + (n0 + 1) * sbytes};
   RowWords<FMT, 2, STEPS> rw;
   rows_load<FMT, 2, STEPS>(codes, scales, I, lane, rw);
-  act_stage<FMT>(hc, I, hs, corr, a.status);
+  if ((int)threadIdx.x < I / Fmt<FMT>::kCols) act_stage<FMT, true>(hc, threadIdx.x, hs, corr, nullptr);
   lds_barrier();
   float r[2];
   rows_dot<FMT, 2, STEPS>(rw, I, hs, corr, blob ? 1.0f : 0.0f, lane, r);
@@ -337,6 +338,106 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
     r[1] *= gd;
   }
   if (lane < 2) reinterpret_cast<float*>(a.ws + W.o)[(size_t)p * H + n0 + lane] = lane ? r[1] : r[0];
+}
+
+// Down projection and combine in one kernel for the decode sizes (U = K units,
+// plus the shared expert, of at most kFusedUnits; h rows of at most 128 chunks):
+// one item per (token, 8 rows of H), wave w the rows 2w, 2w + 1 of every unit of
+// the token. The h of all U units goes to LDS; every weight load of the wave is
+// issued first (the units' slots before them). Each unit's sums are those of
+// fmt_down_kernel, and y = o_shared + sum_k w[k] * o_k is added in rank order
+// and rounded once, as fmt_combine_kernel does: the same bits.
+constexpr int kFusedUnits = 9;
+
+template <int FMT, int STEPS, int U>
+__global__ void __launch_bounds__(kFThreads) fmt_down_fused_kernel(FfnArgs a) {
+  constexpr int C = Fmt<FMT>::kCols;
+  constexpr int CH = (U * 64 * STEPS + kFThreads - 1) / kFThreads;  // h chunks per thread, at most
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H, I = a.I, K = a.K, P = a.T * K;
+  const bool has_shared = a.shared_blob != nullptr;
+  const FmtWs W = fmt_ws(a.T, H, I, K, has_shared);
+  const int n_chunks = I / C;
+  uint32_t* hs = reinterpret_cast<uint32_t*>(smem);                   // [U][I / 2] fp16 pairs
+  float* corr = reinterpret_cast<float*>(smem + (size_t)U * I * 2);  // [U][n_chunks]
+  const int n_rb = H / kRowsPerItem;
+  const int t = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // unit u: the shared expert first when present, then ranks 0 .. K-1 (the combine's order)
+  auto pair_of = [&](int u) { return has_shared ? (u == 0 ? P + t : t * K + u - 1) : t * K + u; };
+  const uint16_t* hg = reinterpret_cast<const uint16_t*>(a.ws + W.h);
+  // 1. this thread's h chunks q = tid + 256 j of the U x n_chunks
+  ActChunk<FMT> hc[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int q = (int)threadIdx.x + kFThreads * j;
+    const int qq = q < U * n_chunks ? q : 0;
+    act_load<FMT>(hg + (size_t)pair_of(qq / n_chunks) * I, qq % n_chunks, hc[j]);
+  }
+  // 2. the units' slots (ids, then the slot table), then every weight load
+  int32_t eu[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int pu = pair_of(u);
+    eu[u] = a.ids[pu < P ? pu : 0];
+  }
+  int32_t su[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool ok = eu[u] >= 0 && eu[u] < a.E;
+    su[u] = a.slot_table[ok ? eu[u] : 0];
+  }
+  const FmtLayout L = fmt_layout(FMT, H, I);
+  const int n0 = rb * kRowsPerItem + 2 * wave;
+  const size_t rbytes = row_bytes<FMT>(I);
+  const size_t sbytes = (size_t)I / Fmt<FMT>::kG * (FMT == MOE_FMT_INT8_G32 ? 2 : 1);
+  const uint8_t* src[U];
+  bool live[U];
+  RowWords<FMT, 2, STEPS> rw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool shared_u = has_shared && u == 0;
+    const bool id_ok = eu[u] >= 0 && eu[u] < a.E;
+    live[u] = shared_u || (id_ok && su[u] >= 0);
+    if (!shared_u && !live[u]) *a.status = id_ok ? MOE_ENOTRES : MOE_EINVAL;
+    src[u] = shared_u ? a.shared_blob : (live[u] ? a.slots + (size_t)su[u] * a.stride : a.slots);
+    const uint8_t* const codes[2] = {src[u] + L.down_codes + n0 * rbytes, src[u] + L.down_codes + (n0 + 1) * rbytes};
+    const uint8_t* const scales[2] = {src[u] + L.down_scales + n0 * sbytes,
+                                      src[u] + L.down_scales + (n0 + 1) * sbytes};
+    rows_load<FMT, 2, STEPS>(codes, scales, I, lane, rw[u]);
+  }
+  // 3. h into LDS while the weights stream
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int q = (int)threadIdx.x + kFThreads * j;
+    if (q < U * n_chunks) {
+      const int u = q / n_chunks;
+      act_stage<FMT, true>(hc[j], q % n_chunks, hs + (size_t)u * (I / 2), corr + (size_t)u * n_chunks, nullptr);
+    }
+  }
+  lds_barrier();
+  // 4. per unit, the sums of fmt_down_kernel; combined in rank order
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float r[2];
+    rows_dot<FMT, 2, STEPS>(rw[u], I, hs + (size_t)u * (I / 2), corr + (size_t)u * n_chunks, live[u] ? 1.0f : 0.0f,
+                            lane, r);
+    if (FMT == MOE_FMT_NVFP4) {
+      const float gd = reinterpret_cast<const float*>(src[u] + L.globals)[2];
+      r[0] *= gd;
+      r[1] *= gd;
+    }
+    if (has_shared && u == 0) {
+      acc0 = r[0];
+      acc1 = r[1];
+    } else {
+      const float wk = a.w[t * K + (has_shared ? u - 1 : u)];
+      acc0 = fmaf(wk, r[0], acc0);
+      acc1 = fmaf(wk, r[1], acc1);
+    }
+  }
+  if (lane < 2) a.y[(size_t)t * H + n0 + lane] = __builtin_bit_cast(uint16_t, (__bf16)(lane ? acc1 : acc0));
 }
 
 __global__ void __launch_bounds__(256) fmt_combine_kernel(FfnArgs a) {
@@ -379,6 +480,27 @@ hipError_t launch_fmt(const FfnArgs& a, hipStream_t s) {
   else return hipErrorNotSupported;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int U = a.K + (has_shared ? 1 : 0);
+  const size_t lds_fused = (size_t)U * a.I * 2 + (size_t)U * (a.I / C) * 4;
+  if (U <= kFusedUnits && steps_dn <= 2 && lds_fused <= 96 * 1024) {
+    const int grid_f = a.T * (a.H / kRowsPerItem);
+#define FU(ST, UU)                                                                                          \
+  case UU:                                                                                                  \
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fmt_down_fused_kernel<FMT, ST, UU>),           \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_fused);                  \
+    hipLaunchKernelGGL((fmt_down_fused_kernel<FMT, ST, UU>), dim3(grid_f), dim3(kFThreads), lds_fused, s, a); \
+    break;
+#define FU_ALL(ST) \
+  switch (U) { FU(ST, 1) FU(ST, 2) FU(ST, 3) FU(ST, 4) FU(ST, 5) FU(ST, 6) FU(ST, 7) FU(ST, 8) FU(ST, 9) }
+    if (steps_dn == 1) {
+      FU_ALL(1)
+    } else {
+      FU_ALL(2)
+    }
+#undef FU_ALL
+#undef FU
+    return hipGetLastError();
+  }
   if (steps_dn == 1) DN(1);
   else if (steps_dn == 2) DN(2);
   else if (steps_dn <= 4) DN(4);
