@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(kThreads) dec_route_gateup_kernel(FfnArgs a, O
   if (selector) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
+      const int e = lane * EPL + i;
       tv[i] = a.slot_table[e < E ? e : E - 1];
     }
   }
@@ -327,20 +327,13 @@ __global__ void __launch_bounds__(kThreads) dec_route_gateup_kernel(FfnArgs a, O
   if (ok) {
     // each rank's slot is published in the round that selects it (kOnepassCopies
     // copies, lane c writes copy c), so the gate/up items of rank k start while
-    // the later ranks are still being selected; the slot of expert e is tv[e / 64]
-    // of lane e % 64
-    auto publish = [&](int k, uint64_t best) {
-      const int e = key_id(best);
-      int32_t sk = 0;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int32_t v = __builtin_amdgcn_readlane(tv[i], e & 63);
-        sk = (e >> 6) == i ? v : sk;
-      }
+    // the later ranks are still being selected; the slots ride with their
+    // experts through the selection (the payload)
+    auto publish = [&](int k, int32_t, int32_t sk) {
       if (lane < kOnepassCopies) ll_store(r.words + onepass_slot_word(E, k, lane), ep, (uint32_t)sk);
       if (lane == k) slot = sk;
     };
-    wave_select_values<EPL>(sel, E, a.K, r.flags, lane, id, wt, publish);
+    wave_select_values<EPL>(sel, tv, E, a.K, r.flags, lane, id, wt, publish);
   } else {
     for (int k = 0; k < a.K; ++k)
       if (lane < kOnepassCopies) ll_store(r.words + onepass_slot_word(E, k, lane), ep, (uint32_t)slot);

@@ -43,7 +43,8 @@ __device__ inline void onepass_publish_logit(const uint16_t* x, const float* wr,
 }
 
 // The selector (one wave, lanes 0..63): waits until all E logit words carry
-// this epoch; lane l gets lg[i] = logit of expert l + 64 i (0 past E). Every poll
+// this epoch; lane l gets lg[i] = logit of expert l * EPL + i (0 past E), the
+// blocked layout of wave_topk. Every poll
 // issues all of its loads before it waits (one round trip per poll). Returns
 // false when the words did not arrive within the spin limit (status set).
 template <int EPL>
@@ -54,7 +55,7 @@ __device__ inline bool onepass_wait_logits(const uint64_t* words, int E, uint32_
     uint64_t v[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
+      const int e = lane * EPL + i;
       v[i] = ll_load(words + 1 + (e < E ? e : E - 1));
     }
     bool fresh = true;
@@ -62,7 +63,7 @@ __device__ inline bool onepass_wait_logits(const uint64_t* words, int E, uint32_
     for (int i = 0; i < EPL; ++i) fresh = fresh && (uint32_t)(v[i] >> 32) == ep;
     if (__ballot(!fresh) == 0) {
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) lg[i] = lane + 64 * i < E ? __uint_as_float((uint32_t)v[i]) : 0.0f;
+      for (int i = 0; i < EPL; ++i) lg[i] = lane * EPL + i < E ? __uint_as_float((uint32_t)v[i]) : 0.0f;
       return true;
     }
     if (spins >= kOnepassSpinLimit) {
@@ -73,14 +74,14 @@ __device__ inline bool onepass_wait_logits(const uint64_t* words, int E, uint32_
   }
 }
 
-// Lane l writes the logits of experts l + 64 i (stores are issued after the
+// Lane l writes the logits of experts l * EPL + i (stores are issued after the
 // selection and the hand-off, so that no wait for them lands on the critical path).
 template <int EPL>
 __device__ inline void onepass_store_logits(const float (&lg)[EPL], int E, float* logits) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i < E) logits[lane + 64 * i] = lg[i];
+    if (lane * EPL + i < E) logits[lane * EPL + i] = lg[i];
 }
 
 // Wait for copy `copy` of rank k's slot word of this epoch (moe_layer's one-pass

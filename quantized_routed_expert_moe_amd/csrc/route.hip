@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(64) route_select_kernel(const float* __restric
   if (slot_table) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
+      const int e = lane * EPL + i;
       tv[i] = slot_table[e < E ? e : E - 1];
     }
   }
@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(64) route_select_kernel(const float* __restric
   }
   if (slot_table) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) tbl[lane + 64 * i] = tv[i];  // entries past E are never read
+    for (int i = 0; i < EPL; ++i) tbl[lane * EPL + i] = tv[i];  // entries past E are never read
     __builtin_amdgcn_wave_barrier();  // one wave: its LDS stores precede its loads
     if (lane < K) slots_out[lane] = tbl[id];
   }
@@ -179,28 +179,32 @@ __global__ void __launch_bounds__(64) route_scored_kernel(const float* __restric
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
   const float* l = logits + (size_t)t * E;
-  uint64_t key[EPL];
   float lv[EPL], bv[EPL];  // loads first, all in flight together (clamped index past E)
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
+    const int e = lane * EPL + i;
     const int ec = e < E ? e : E - 1;
     lv[i] = l[ec];
     bv[i] = bias ? bias[ec] : 0.0f;
   }
+  uint32_t img[EPL];
+  int32_t idv[EPL], pay[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
+    const int e = lane * EPL + i;
+    idv[i] = e;
+    pay[i] = 0;
     if (e < E) {
       const float s = expert_score(lv[i], score);
       const float c = bias ? s + bv[i] : s;
-      key[i] = route_key(c, e);
+      img[i] = sel_image(c);
     } else {
-      key[i] = 0ull;  // real keys are > 0
+      img[i] = 0u;  // absent
     }
   }
-  const uint64_t mine = wave_topk<EPL>(key, K, lane);
-  const int id = key_id(mine);
+  uint32_t mine;
+  int32_t id;
+  wave_topk<EPL>(img, idv, pay, K, lane, mine, id);
   float wt = 0.0f;
   if (lane < K) wt = expert_score(l[id], score);
   if (flags & MOE_ROUTE_RENORM) wt = wt / wave_sum_f32(lane < K ? wt : 0.0f);

@@ -121,61 +121,83 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return max((uint32_t)s32[0], (uint32_t)s32[1]);
 }
 
-// Softmax top-k of one token's E logits l[0..E) by one whole wave (E <= 64 * EPL,
-// K <= 64). Lane k < K gets rank k: its expert id and its weight
-// softmax(l)[id] (divided by the sum of the K weights with MOE_ROUTE_RENORM).
-// Lane l holds the keys of experts l, l+64, ... sorted descending in
-// registers; each of K rounds takes the wave-wide maximum of the lanes' first
-// keys (on the 32-bit logit image; among equal images the full key, i.e. the
-// lowest id, decides) and pops it from its owner lane.
-// The K largest keys of the wave (lane l holds the keys of experts l, l + 64, ...;
-// 0 marks an absent expert): lane k < K returns the key of rank k, the others 0.
-// A rank hook is called as hook(k, key) once per rank k = 0 .. K-1 as soon as
-// that rank's key is known (key is wave-uniform); the default does nothing.
+// Top-k of one token's E experts by one whole wave (E <= 64 * EPL, K <= 64), in
+// the blocked layout: lane l holds experts l * EPL + i, i = 0 .. EPL-1, so a
+// lower lane holds only lower ids. The order is the logit (its 32-bit order
+// image, sel_image), then the lower id. Each lane sorts its EPL entries (a
+// stable odd-even transposition sort: equal images keep id order); each of K
+// rounds takes the wave maximum of the lanes' first images, and the lowest lane
+// holding it wins, which is the lowest id among equal logits, without a
+// tie-break pass. The winner pops its entry; a payload value per entry (a slot,
+// or nothing) travels with it.
+// Out: lane k < K gets img_out = the image and id_out = the expert of rank k.
+// A rank hook is called as hook(k, id, payload) once per rank k = 0 .. K-1 as
+// soon as that rank is known (wave-uniform arguments); the default does nothing.
 struct NoRankHook {
-  __device__ void operator()(int, uint64_t) const {}
+  __device__ void operator()(int, int32_t, int32_t) const {}
 };
 
+// Order image of a logit: larger image = higher logit, -0.0 folded into +0.0.
+// Image 0 marks an absent expert; the one logit that would map to it (the NaN
+// with every bit set) maps to 1 instead.
+__device__ inline uint32_t sel_image(float l) {
+  const uint32_t u = __float_as_uint(l + 0.0f);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ord > 1u ? ord : 1u;
+}
+__device__ inline float image_logit(uint32_t ord) {
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
 template <int EPL, typename Hook = NoRankHook>
-__device__ inline uint64_t wave_topk(uint64_t (&key)[EPL], int K, int lane, const Hook& hook = Hook{}) {
-  // local descending sort (odd-even transposition)
+__device__ inline void wave_topk(uint32_t (&img)[EPL], int32_t (&idv)[EPL], int32_t (&pay)[EPL], int K, int lane,
+                                 uint32_t& img_out, int32_t& id_out, const Hook& hook = Hook{}) {
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
 #pragma unroll
     for (int i = (r & 1); i + 1 < EPL; i += 2) {
-      const uint64_t a = key[i], b = key[i + 1];
-      key[i] = a > b ? a : b;
-      key[i + 1] = a > b ? b : a;
+      const bool sw = img[i + 1] > img[i];
+      const uint32_t a = img[i], b = img[i + 1];
+      const int32_t ia = idv[i], ib = idv[i + 1], pa = pay[i], pb = pay[i + 1];
+      img[i] = sw ? b : a;
+      img[i + 1] = sw ? a : b;
+      idv[i] = sw ? ib : ia;
+      idv[i + 1] = sw ? ia : ib;
+      pay[i] = sw ? pb : pa;
+      pay[i + 1] = sw ? pa : pb;
     }
   }
-  uint64_t mine = 0;  // lane k keeps the winner of rank k
+  img_out = 0u;
+  id_out = 0;
   for (int k = 0; k < K; ++k) {
-    const uint32_t hi = (uint32_t)(key[0] >> 32);
-    const uint32_t m = wave_max_u32(hi);
-    uint64_t owners = __ballot(hi == m);
-    if (__builtin_popcountll(owners) > 1) {  // equal values: the highest full key (lowest id) wins
-      const uint64_t best = wave_max_u64(hi == m ? key[0] : 0ull);
-      owners = __ballot(key[0] == best);
-    }
-    const int src = (int)__builtin_ctzll(owners);
-    const uint64_t best = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(key[0] >> 32), src) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)key[0], src);
+    const uint32_t m = wave_max_u32(img[0]);
+    const int src = (int)__builtin_ctzll(__ballot(img[0] == m));
+    const int32_t idk = __builtin_amdgcn_readlane(idv[0], src);
+    const int32_t pk = __builtin_amdgcn_readlane(pay[0], src);
     if (lane == src) {
 #pragma unroll
-      for (int i = 0; i + 1 < EPL; ++i) key[i] = key[i + 1];
-      key[EPL - 1] = 0;
+      for (int i = 0; i + 1 < EPL; ++i) {
+        img[i] = img[i + 1];
+        idv[i] = idv[i + 1];
+        pay[i] = pay[i + 1];
+      }
+      img[EPL - 1] = 0u;
     }
-    if (lane == k) mine = best;
-    hook(k, best);
+    if (lane == k) {
+      img_out = m;
+      id_out = idk;
+    }
+    hook(k, idk, pk);
   }
-  return mine;
 }
 
-// The same contract as wave_topk by a wave-wide bitonic sort of all 64 * EPL keys
-// (EPL a power of two), descending: element i is key[i / 64] of lane i % 64, so
-// rank k ends in key[0] of lane k. A compare-exchange at distance j < 64 pairs
-// lanes (shuffle), at j >= 64 registers of one lane. The keys are distinct, so
-// the order, and the K selected, equal wave_topk's.
+// The same selection as wave_topk by a wave-wide bitonic sort of all 64 * EPL
+// full keys (route_key: logit image, then the lower id; EPL a power of two),
+// descending: element i is key[i / 64] of lane i % 64 (the order the keys come in
+// does not matter, they carry their ids), so rank k ends in key[0] of lane k. A
+// compare-exchange at distance j < 64 pairs lanes (shuffle), at j >= 64
+// registers of one lane. The keys are distinct, so the K selected and their
+// order equal wave_topk's. The rank hook gets payload 0.
 __device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
   return ((uint64_t)hi << 32) | lo;
@@ -210,43 +232,61 @@ __device__ inline uint64_t wave_topk_bitonic(uint64_t (&key)[EPL], int K, int la
       }
     }
   }
-  for (int k = 0; k < K; ++k) {
-    const uint64_t best = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(key[0] >> 32), k) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)key[0], k);
-    hook(k, best);
-  }
+  for (int k = 0; k < K; ++k) hook(k, key_id(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(key[0] >> 32), k) << 32) |
+                                        (uint32_t)__builtin_amdgcn_readlane((uint32_t)key[0], k)), 0);
   return lane < K ? key[0] : 0ull;
 }
 
-// Softmax + top-k of one token's logits: lane k < K gets the expert of rank k
-// and its weight (the softmax probability over all E, with MOE_ROUTE_RENORM
-// divided by the sum over the K selected).
-// Softmax + top-k of one token's logits held in registers: lane l holds lg[i] =
-// logit of expert l + 64 i (entries past E ignored).
+// Softmax + top-k of one token's logits held in registers in the blocked layout
+// (lane l holds lg[i] = logit of expert l * EPL + i; entries past E ignored):
+// lane k < K gets the expert of rank k and its weight (the softmax probability
+// over all E, with MOE_ROUTE_RENORM divided by the sum over the K selected).
+// pay[i] is a payload per expert (e.g. its slot) handed to the rank hook.
 template <int EPL, bool BITONIC = false, typename Hook = NoRankHook>
-__device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsigned flags, int lane, int32_t& id,
-                                          float& wt, const Hook& hook = Hook{}) {
-  uint64_t key[EPL];
+__device__ inline void wave_select_values(float (&lg)[EPL], int32_t (&pay)[EPL], int E, int K, unsigned flags,
+                                          int lane, int32_t& id, float& wt, const Hook& hook = Hook{}) {
+  float top;  // this lane's rank's logit (lanes < K)
+  if constexpr (BITONIC) {
+    uint64_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    if (e >= E) lg[i] = 0.0f;
-    key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane * EPL + i;
+      if (e >= E) lg[i] = 0.0f;
+      key[i] = e < E ? route_key(lg[i], e) : 0ull;  // real keys are > 0
+    }
+    const uint64_t mine = wave_topk_bitonic<EPL>(key, K, lane, hook);
+    top = key_logit(mine);
+    id = key_id(mine);
+  } else {
+    uint32_t img[EPL];
+    int32_t idv[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane * EPL + i;
+      if (e >= E) lg[i] = 0.0f;
+      img[i] = e < E ? sel_image(lg[i]) : 0u;
+      idv[i] = e;
+    }
+    uint32_t mine;
+    wave_topk<EPL>(img, idv, pay, K, lane, mine, id, hook);
+    top = image_logit(mine);
   }
-  const uint64_t mine = BITONIC ? wave_topk_bitonic<EPL>(key, K, lane, hook) : wave_topk<EPL>(key, K, lane, hook);
-  const uint32_t top_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(mine >> 32));
-  const uint32_t top_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)mine);
-  const float m = key_logit(((uint64_t)top_hi << 32) | top_lo);  // the largest logit (rank 0, lane 0)
+  const float m = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane(__float_as_uint(top)));  // rank 0's
   float part = 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i < E) part += expf(lg[i] - m);
+    if (lane * EPL + i < E) part += expf(lg[i] - m);
   part = wave_sum_f32(part);
   float w = 0.0f;
-  if (lane < K) w = expf(key_logit(mine) - m) / part;
+  if (lane < K) w = expf(top - m) / part;
   if (flags & MOE_ROUTE_RENORM) w = w / wave_sum_f32(lane < K ? w : 0.0f);
-  id = key_id(mine);
   wt = w;
+}
+template <int EPL, bool BITONIC = false>
+__device__ inline void wave_select_values(float (&lg)[EPL], int E, int K, unsigned flags, int lane, int32_t& id,
+                                          float& wt) {
+  int32_t pay[EPL] = {};
+  wave_select_values<EPL, BITONIC>(lg, pay, E, K, flags, lane, id, wt);
 }
 
 template <int EPL, bool BITONIC = false>
@@ -257,7 +297,7 @@ __device__ inline void wave_select(const float* __restrict__ l, int E, int K, un
   // flight at once: a load under a branch is waited for before the branch joins
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
+    const int e = lane * EPL + i;
     lg[i] = l[e < E ? e : E - 1];
   }
   wave_select_values<EPL, BITONIC>(lg, E, K, flags, lane, id, wt);
