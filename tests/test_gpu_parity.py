@@ -744,6 +744,14 @@ def fmt_run(fmt, w, slots, table, shared, stride, xb, logits):
         (gen.FMT_NVFP4, gen.Workload("nvfp4_t7_h256_e8_k2_i96", 7, 256, 8, 2, 96, 1, 8, "normal", 82)),
         (gen.FMT_NVFP4, gen.Workload("nvfp4_t32_h2048_e32_k8_i768_shared", 32, 2048, 32, 8, 768, 1, 32, "zipf", 83,
                                      shared=True)),
+        # more than 9 units per token, and h rows past 128 chunks: the per-pair down kernel and the
+        # separate combine instead of the fused down
+        (gen.FMT_INT8_G32, gen.Workload("fmt8_t3_h256_e16_k10_i128_shared", 3, 256, 16, 10, 128, 1, 16, "normal", 95,
+                                        shared=True)),
+        (gen.FMT_INT8_G32, gen.Workload("fmt8_t2_h256_e4_k2_i2560", 2, 256, 4, 2, 2560, 1, 4, "normal", 96)),
+        (gen.FMT_NVFP4, gen.Workload("nvfp4_t2_h256_e16_k12_i256", 2, 256, 16, 12, 256, 1, 16, "normal", 97)),
+        (gen.FMT_NVFP4, gen.Workload("nvfp4_t2_h256_e4_k2_i4608_shared", 2, 256, 4, 2, 4608, 1, 4, "normal", 98,
+                                     shared=True)),
         # prompts (T > 32): the formats' grouped MFMA GEMMs
         (gen.FMT_INT8_G32, gen.Workload("fmt8_t40_h512_e16_k4_i256_shared", 40, 512, 16, 4, 256, 1, 16, "normal", 84,
                                         shared=True)),
@@ -756,7 +764,8 @@ def fmt_run(fmt, w, slots, table, shared, stride, xb, logits):
 )
 def test_fmt_matches_oracle(fmt, w):
     """INT8 group-32, INT4 group-128 (on every path of moe_expert_ffn, 77 tokens on the
-    grouped one) and NVFP4 experts, one token to prompts of 300 (the formats' own grouped
+    grouped one) and NVFP4 experts (the fused down of up to 9 units and the per-pair down
+    with its combine past that), one token to prompts of 300 (the formats' own grouped
     MFMA GEMMs above 32 tokens, experts over two 128-row tiles, a full and a half one; the
     seeds keep the oracle's bf16 rounding floor below the bar, so the plain bar holds): ids
     bit-exact, y within the oracle's bar, the same bits on a second run and under a
