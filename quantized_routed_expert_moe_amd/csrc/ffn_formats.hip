@@ -342,8 +342,10 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_kernel(FfnArgs a) {
 
 // Down projection and combine in one kernel for the decode sizes (U = K units,
 // plus the shared expert, of at most kFusedUnits; h rows of at most 128 chunks):
-// one item per (token, 8 rows of H), wave w the rows 2w, 2w + 1 of every unit of
-// the token. The h of all U units goes to LDS; every weight load of the wave is
+// one item per (token, 4 RPW rows of H), wave w the rows RPW w .. RPW w + RPW - 1
+// of every unit of the token, RPW = 4 when a row's h is one step of 64 chunks
+// (NVFP4 at the decode shape: each workgroup's h staging then serves 16 rows),
+// else 2 (the registers of two steps' loads for every unit). The h of all U units goes to LDS; every weight load of the wave is
 // issued first (the units' slots before them). Each unit's sums are those of
 // fmt_down_kernel, and y = o_shared + sum_k w[k] * o_k is added in rank order
 // and rounded once, as fmt_combine_kernel does: the same bits.
@@ -353,6 +355,7 @@ template <int FMT, int STEPS, int U>
 __global__ void __launch_bounds__(kFThreads) fmt_down_fused_kernel(FfnArgs a) {
   constexpr int C = Fmt<FMT>::kCols;
   constexpr int CH = (U * 64 * STEPS + kFThreads - 1) / kFThreads;  // h chunks per thread, at most
+  constexpr int RPW = STEPS == 1 ? 4 : 2, RPI = 4 * RPW;  // rows per wave, per item
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H, I = a.I, K = a.K, P = a.T * K;
   const bool has_shared = a.shared_blob != nullptr;
@@ -360,7 +363,7 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_fused_kernel(FfnArgs a) {
   const int n_chunks = I / C;
   uint32_t* hs = reinterpret_cast<uint32_t*>(smem);                   // [U][I / 2] fp16 pairs
   float* corr = reinterpret_cast<float*>(smem + (size_t)U * I * 2);  // [U][n_chunks]
-  const int n_rb = H / kRowsPerItem;
+  const int n_rb = H / RPI;
   const int t = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // unit u: the shared expert first when present, then ranks 0 .. K-1 (the combine's order)
@@ -388,12 +391,12 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_fused_kernel(FfnArgs a) {
     su[u] = a.slot_table[ok ? eu[u] : 0];
   }
   const FmtLayout L = fmt_layout(FMT, H, I);
-  const int n0 = rb * kRowsPerItem + 2 * wave;
+  const int n0 = rb * RPI + RPW * wave;
   const size_t rbytes = row_bytes<FMT>(I);
   const size_t sbytes = (size_t)I / Fmt<FMT>::kG * (FMT == MOE_FMT_INT8_G32 ? 2 : 1);
   const uint8_t* src[U];
   bool live[U];
-  RowWords<FMT, 2, STEPS> rw[U];
+  RowWords<FMT, RPW, STEPS> rw[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool shared_u = has_shared && u == 0;
@@ -401,10 +404,14 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_fused_kernel(FfnArgs a) {
     live[u] = shared_u || (id_ok && su[u] >= 0);
     if (!shared_u && !live[u]) *a.status = id_ok ? MOE_ENOTRES : MOE_EINVAL;
     src[u] = shared_u ? a.shared_blob : (live[u] ? a.slots + (size_t)su[u] * a.stride : a.slots);
-    const uint8_t* const codes[2] = {src[u] + L.down_codes + n0 * rbytes, src[u] + L.down_codes + (n0 + 1) * rbytes};
-    const uint8_t* const scales[2] = {src[u] + L.down_scales + n0 * sbytes,
-                                      src[u] + L.down_scales + (n0 + 1) * sbytes};
-    rows_load<FMT, 2, STEPS>(codes, scales, I, lane, rw[u]);
+    const uint8_t* codes[RPW];
+    const uint8_t* scales[RPW];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      codes[rr] = src[u] + L.down_codes + (n0 + rr) * rbytes;
+      scales[rr] = src[u] + L.down_scales + (n0 + rr) * sbytes;
+    }
+    rows_load<FMT, RPW, STEPS>(codes, scales, I, lane, rw[u]);
   }
   // 3. h into LDS while the weights stream
 #pragma unroll
@@ -417,27 +424,32 @@ __global__ void __launch_bounds__(kFThreads) fmt_down_fused_kernel(FfnArgs a) {
   }
   lds_barrier();
   // 4. per unit, the sums of fmt_down_kernel; combined in rank order
-  float acc0 = 0.0f, acc1 = 0.0f;
+  float acc[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) acc[rr] = 0.0f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    float r[2];
-    rows_dot<FMT, 2, STEPS>(rw[u], I, hs + (size_t)u * (I / 2), corr + (size_t)u * n_chunks, live[u] ? 1.0f : 0.0f,
+    float r[RPW];
+    rows_dot<FMT, RPW, STEPS>(rw[u], I, hs + (size_t)u * (I / 2), corr + (size_t)u * n_chunks, live[u] ? 1.0f : 0.0f,
                             lane, r);
     if (FMT == MOE_FMT_NVFP4) {
       const float gd = reinterpret_cast<const float*>(src[u] + L.globals)[2];
-      r[0] *= gd;
-      r[1] *= gd;
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) r[rr] *= gd;
     }
     if (has_shared && u == 0) {
-      acc0 = r[0];
-      acc1 = r[1];
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) acc[rr] = r[rr];
     } else {
       const float wk = a.w[t * K + (has_shared ? u - 1 : u)];
-      acc0 = fmaf(wk, r[0], acc0);
-      acc1 = fmaf(wk, r[1], acc1);
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) acc[rr] = fmaf(wk, r[rr], acc[rr]);
     }
   }
-  if (lane < 2) a.y[(size_t)t * H + n0 + lane] = __builtin_bit_cast(uint16_t, (__bf16)(lane ? acc1 : acc0));
+  float out = acc[0];
+#pragma unroll
+  for (int rr = 1; rr < RPW; ++rr) out = lane == rr ? acc[rr] : out;
+  if (lane < RPW) a.y[(size_t)t * H + n0 + lane] = __builtin_bit_cast(uint16_t, (__bf16)out);
 }
 
 __global__ void __launch_bounds__(256) fmt_combine_kernel(FfnArgs a) {
@@ -483,7 +495,7 @@ hipError_t launch_fmt(const FfnArgs& a, hipStream_t s) {
   const int U = a.K + (has_shared ? 1 : 0);
   const size_t lds_fused = (size_t)U * a.I * 2 + (size_t)U * (a.I / C) * 4;
   if (U <= kFusedUnits && steps_dn <= 2 && lds_fused <= 96 * 1024) {
-    const int grid_f = a.T * (a.H / kRowsPerItem);
+    const int grid_f = a.T * (a.H / (steps_dn == 1 ? 16 : 8));  // 4 RPW rows per item
 #define FU(ST, UU)                                                                                          \
   case UU:                                                                                                  \
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fmt_down_fused_kernel<FMT, ST, UU>),           \
