@@ -26,13 +26,15 @@
 // h for the down projection) are staged as fp16 (a value past the fp16 range
 // sets MOE_EUNSUP).
 //
-// Work: one item per (token, expert) pair and row block, so an expert's bytes
-// are read once per token that uses it (the single-token decode reads each
-// chosen expert once). Kernel 1: item = (pair, 8 rows of I), wave w the rows
-// 2w, 2w + 1 of gate and up, lanes the chunks of a row; h = silu(g) * u in
-// fp32. Kernel 2: item = (pair, 8 rows of H), o in fp32. Kernel 3: the
-// combine in rank order, one bf16 rounding. No atomics: the reduction order
-// depends only on (T, K, the format).
+// Work: an expert's bytes are read once per token that uses it (the
+// single-token decode reads each chosen expert once). Kernel 1: item = (pair,
+// 8 rows of I), wave w the rows 2w, 2w + 1 of gate and up, lanes the chunks of
+// a row; h = silu(g) * u in fp32, handed on rounded to fp16. Down and combine:
+// for up to 9 units per token and h rows of up to 128 chunks one kernel, item =
+// (token, 8 or 16 rows of H) over all of the token's units, y added in rank
+// order and rounded once to bf16; otherwise item = (pair, 8 rows of H) with o
+// in fp32, then the combine kernel in the same order. No atomics: the
+// reduction order depends only on (T, K, the format).
 #include "moe_internal.h"
 #include "wave_ops.h"
 
