@@ -165,17 +165,13 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
     q = q < G * 4 ? q : G * 4 - 1;
     xv[v] = reinterpret_cast<const uint4*>(a.x)[q];
   }
-  const uint8_t* blob =
-      ONEPASS ? onepass_unit_blob(a, u, has_shared, words, ep, wave) : dec_unit_blob(a, u, has_shared, a.ids, pre);
-  tl_mark(tl, 3);
-  const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
-  const BlobLayout BL = blob_layout(H, I);
-  const int n = hb * 8 + r;
-  // 2. x -> fp16 pairs, group corrections, into LDS (lanes 2m, 2m+1 hold group m).
-  //    Done before the weight loads: x has arrived with the slot lookup (issued
-  //    earlier), and the weights' registers are not live yet (register pressure)
+  // 2. x -> fp16 pairs, group corrections, into LDS (lanes 2m, 2m+1 hold group m),
+  //    before the weight loads, whose registers are not live yet (register
+  //    pressure). The standalone kernel stages x after the slot lookup (x has
+  //    arrived during its two dependent loads); the one-pass items stage it while
+  //    the selection runs, so that their weight loads follow the slot at once.
   bool bad = false;
-  {
+  auto stage_x = [&]() {
     const bool live = lane * 2 < gw_here * 4;
     uint32_t xh[8];
     float sa = 0.0f, sb = 0.0f;
@@ -202,7 +198,19 @@ __device__ __forceinline__ void dec_gateup_body(const FfnArgs& a, int bid, const
       if ((lane & 1) == 0) Cs[lane >> 1] = fmaf(1032.0f, sa_t, 72.0f * sb_t);
     }
     __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
+  };
+  const uint8_t* blob;
+  if constexpr (ONEPASS) {
+    stage_x();
+    blob = onepass_unit_blob(a, u, has_shared, words, ep, wave);
+  } else {
+    blob = dec_unit_blob(a, u, has_shared, a.ids, pre);
   }
+  tl_mark(tl, 3);
+  const uint8_t* src = blob ? blob : a.slots;  // any readable blob; its terms get scale 0
+  const BlobLayout BL = blob_layout(H, I);
+  const int n = hb * 8 + r;
+  if constexpr (!ONEPASS) stage_x();
   // 3. codes and scale dwords of every step, in step order
   uint4 cg[GPL], cu[GPL];
   uint32_t sgw[GPL], suw[GPL];
