@@ -31,10 +31,11 @@
 //   phase p of 8) takes groups w*GW + 8i + p of its row in gate and up: per
 //   step a wave reads eight 128-byte lines per matrix. Phases then waves are
 //   summed in a fixed order; h = silu(g) * u is stored as fp16.
-// dec_down: one workgroup per 4 rows of H for all units at once, so the
-//   combine needs no further kernel. The flattened (unit, group) columns are
+// dec_down: one workgroup per 8 rows of H (two quads of 4) for all units at
+//   once, so the combine needs no further kernel; each wave's staged h slice
+//   and its LDS reads serve both quads. The flattened (unit, group) columns are
 //   split into four contiguous ranges, one per wave; at step i lane (row r of
-//   4, phase p of 16) takes column 16i + p of its wave's range; the 16
+//   4 in each quad, phase p of 16) takes column 16i + p of its wave's range; the 16
 //   columns of a step belong to one unit (groups per unit are a multiple of
 //   16). Per-unit sums go over phases, then waves, in a fixed order, and
 //   y = o_shared + sum_k w[k] * o_k in rank order, rounded once to bf16.
@@ -373,7 +374,11 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kMaxUnits = kMaxK + 1;
   constexpr int CW = 16 * CPL;
-  __shared__ float part[kWaves][kMaxUnits][4];
+  // row quads per workgroup (rows 4 qb .. 4 qb + 4 RQ - 1): two quads share the h
+  // staging and the LDS reads (8.5-8.8 us against 8.9-9.1 with one; four quads
+  // left too few workgroups: 9.8-10.3)
+  constexpr int RQ = 2;
+  __shared__ float part[kWaves][kMaxUnits][4 * RQ];
   __shared__ float wsh[kMaxK];
   // the argument pointers the first loads need, in registers with the others (one
   // batch of argument loads instead of two round trips)
@@ -395,8 +400,8 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   const int c0 = wave * CW;
   const uint4* h4 = reinterpret_cast<const uint4*>(a.ws);  // h: fp16 [pair][I]
   const BlobLayout BL = blob_layout(H, I);
-  const int qb = xcd_item(blockIdx.x, H / 4);
-  const int n = qb * 4 + r;
+  const int qb = xcd_item(blockIdx.x, H / (4 * RQ)) * RQ;
+  const int n = qb * 4 + r;  // quad q's row: n + 4 q
   // the slot of rank kk (lane kk + 1 with a shared expert), every lane's load
   // unconditional (a clamped rank): a load under a lane-dependent branch would be
   // waited for at the branch. PRE: one load; else the id, then its table entry.
@@ -453,12 +458,12 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
     }
   }
   // this wave's entries of the partial sums start at zero (only this wave writes them)
-  for (int q = lane; q < kMaxUnits * 4; q += 64) (&part[wave][0][0])[q] = 0.0f;
+  for (int q = lane; q < kMaxUnits * 4 * RQ; q += 64) (&part[wave][0][0])[q] = 0.0f;
   // 2. codes and scale dwords of every step; a step is one unit for all lanes
   bool uok[CPL];
   int ustep[CPL];  // unit of step i (>= n_units past the last column)
-  uint4 cd[CPL];
-  uint32_t sdw[CPL];
+  uint4 cd[RQ][CPL];
+  uint32_t sdw[RQ][CPL];
   {
     int us = c0 / Gd, js = c0 % Gd;  // unit and group of the step's first column (wave-uniform)
 #pragma unroll
@@ -471,8 +476,11 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
       const uint8_t* src = (has_shared && uc == 0) ? a.shared_blob : a.slots + (size_t)(sl > 0 ? sl : 0) * a.stride;
       const int j = jc + p;
       // 4 rows x 16 groups: 1 KB of contiguous codes per wave
-      cd[i] = stream_u4(src + BL.down_codes + code_off(n, j, Gd, kRowBlockDN));
-      sdw[i] = stream_u32(src + BL.down_scales + (scale_off(n, j, Gd, kRowBlockDN) & ~(size_t)3));
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        cd[q][i] = stream_u4(src + BL.down_codes + code_off(n + 4 * q, j, Gd, kRowBlockDN));
+        sdw[q][i] = stream_u32(src + BL.down_scales + (scale_off(n + 4 * q, j, Gd, kRowBlockDN) & ~(size_t)3));
+      }
       js += 16;
       if (js >= Gd) {
         js -= Gd;
@@ -500,7 +508,9 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
   tl_mark(tl, 1);
   // 4. the steps; the LDS operands of step i+1 are read during step i
   const int sh = (r & 1) * 16;
-  float acc = 0.0f;
+  float acc[RQ];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) acc[q] = 0.0f;
   int cur = -1;
   uint4 hn[4];
   float Cn;
@@ -523,29 +533,40 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
       const int us = ustep[i];
       if (us != cur) {
         if (cur >= 0) {
-          const float t = sum_rows(dpp_add<8>(dpp_add<4>(acc)));  // phases (lane bits 2..5), read from lanes 0..3
-          if (p == 0) part[wave][cur][r] = t;
+#pragma unroll
+          for (int q = 0; q < RQ; ++q) {
+            const float t = sum_rows(dpp_add<8>(dpp_add<4>(acc[q])));  // phases (lane bits 2..5), read from lanes 0..3
+            if (p == 0) part[wave][cur][4 * q + r] = t;
+          }
         }
-        acc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) acc[q] = 0.0f;
         cur = us;
       }
-      float P = 0.0f;
-      P = code_dot(cd[i].x, h0.x, h0.y, h0.z, h0.w, P);
-      P = code_dot(cd[i].y, h1.x, h1.y, h1.z, h1.w, P);
-      P = code_dot(cd[i].z, h2.x, h2.y, h2.z, h2.w, P);
-      P = code_dot(cd[i].w, h3.x, h3.y, h3.z, h3.w, P);
-      const float s = uok[i] ? f16_lo(sdw[i] >> sh) : 0.0f;
-      acc = fmaf(s, P - Ccol, acc);
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        float P = 0.0f;
+        P = code_dot(cd[q][i].x, h0.x, h0.y, h0.z, h0.w, P);
+        P = code_dot(cd[q][i].y, h1.x, h1.y, h1.z, h1.w, P);
+        P = code_dot(cd[q][i].z, h2.x, h2.y, h2.z, h2.w, P);
+        P = code_dot(cd[q][i].w, h3.x, h3.y, h3.z, h3.w, P);
+        const float s = uok[i] ? f16_lo(sdw[q][i] >> sh) : 0.0f;
+        acc[q] = fmaf(s, P - Ccol, acc[q]);
+      }
     }
-    asm volatile("" : "+v"(acc)::"memory");  // as in dec_gateup: one step of operands ahead
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) asm volatile("" : "+v"(acc[q])::"memory");  // as in dec_gateup: one step of operands ahead
   }
   if (cur >= 0) {
-    const float t = sum_rows(dpp_add<8>(dpp_add<4>(acc)));
-    if (p == 0) part[wave][cur][r] = t;
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const float t = sum_rows(dpp_add<8>(dpp_add<4>(acc[q])));
+      if (p == 0) part[wave][cur][4 * q + r] = t;
+    }
   }
   tl_mark(tl, 2);
   __syncthreads();
-  if (tid < 4) {
+  if (tid < 4 * RQ) {
     float y = 0.0f;
     const int base = has_shared ? 1 : 0;
     if (has_shared) {
@@ -560,7 +581,7 @@ __global__ void __launch_bounds__(kThreads) dec_down_kernel(FfnArgs a) {
       for (int w = 0; w < kWaves; ++w) o += part[w][base + k][tid];
       y = fmaf(wsh[k], o, y);
     }
-    a.y[(size_t)qb * 4 + tid] = __builtin_bit_cast(uint16_t, (__bf16)y);
+    a.y[(size_t)qb * 4 + tid] = __builtin_bit_cast(uint16_t, (__bf16)y);  // row 4 qb + tid
   }
   // after a one-pass dispatch: every workgroup of it has read the region's call
   // number (that dispatch has completed), so the call is numbered done here (at the
@@ -588,7 +609,7 @@ bool decode1_supported(int T, int H, int I, int K, bool has_shared) {
   const int n_units = K + (has_shared ? 1 : 0);
   const int G = H / kGroup, Gd = I / kGroup;
   // gate/up: at most 4 groups per lane; down: whole steps of 16 columns per unit, at most 8 per lane
-  return T == 1 && G <= 4 * 8 * 4 && Gd % 16 == 0 && H % 4 == 0 && dec_down_cpl(n_units, Gd) <= 8;
+  return T == 1 && G <= 4 * 8 * 4 && Gd % 16 == 0 && H % 8 == 0 && dec_down_cpl(n_units, Gd) <= 8;
 }
 
 hipError_t launch_ffn_decode1_onepass(const FfnArgs& a, const OnepassRoute& r, hipStream_t s) {
@@ -649,7 +670,7 @@ hipError_t launch_ffn_decode1(const FfnArgs& a, int stage, hipStream_t s) {
     const int Gd = a.I / kGroup;
     const int cpl = round_cpl(dec_down_cpl(n_units, Gd));
     const size_t lds = (size_t)kWaves * 16 * cpl * 17 * 4;
-    const int grid = a.H / 4;
+    const int grid = a.H / 8;  // 8 rows of H per workgroup
 #define DN(N)                                                                                       \
   do {                                                                                              \
     if (a.pre_slots) {                                                                              \
